@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA sparse-attention step on one MI355X.
+
+A step is one decode token through the whole hot path -- pooled-key update,
+block scoring, block top-k, sparse attention -- in each of 12 QSA layers (the
+pages' model has 12 QSA layers; 12 replicas of one layer's caches at distinct
+addresses also keep the ~400 MB working set out of the 256 MB last-level
+cache, so the bytes come from HBM).  The K timed steps are captured in one
+HIP graph and replayed; inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  value = microseconds per token per QSA layer (lower is
+better); roofline = the dominant kernel (block scoring) against HBM peak;
+cpu_baseline = the CPU oracle on a bounded sample of the same steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+N_LAYERS = 12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode250k",
+                    choices=["decode50k", "decode250k", "decode5x250k"])
+    ap.add_argument("--layers", type=int, default=N_LAYERS)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for a profiler: no CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, step):
+    """Bytes one layer-step must move at minimum, by kernel."""
+    from top_sparse_attention_pooled_amd import synth
+    n = w.n_cells0 + (step + 1) * w.n_new
+    nc = n // w.r
+    nb = w.nb_max(step)
+    n_q = w.n_seq * w.n_new
+    tail = n - nc * w.r
+    n_sel = min(nc, w.top_k // w.r) * w.r + tail
+    row = synth.row_bytes(w.kv_type, w.D)
+    score = n_q * (nc * w.d * 4 + nb * 4 + w.d * 4)
+    return {
+        "score": score,
+        "update": w.n_seq * (w.r * w.d * 4 + w.d * 4 + w.d * 2),
+        "select": n_q * (nb * 4 + (w.top_k // w.r + w.ld_cells) * 4),
+        "attn": n_q * (n_sel * w.Hk * row * 2 + 2 * w.H * w.D * 4 + n_sel * 4),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
+              "(the QSA step is not sharded across GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from top_sparse_attention_pooled_amd import qsa, runtime, synth
+
+    qsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    K, W, L = args.steps, args.warmup, args.layers
+    if K + W > w.steps:
+        w = synth.Workload(**{**w.__dict__, "steps": K + W})
+
+    t0 = time.time()
+    kidx = synth.make_kidx(w)
+    k = synth.make_kv(w, synth.T_K)
+    v = synth.make_kv(w, synth.T_V)
+    base = runtime.Layer(w, dev, kidx=kidx, k=k, v=v)
+    n0 = np.full(w.n_seq, w.n_cells0, np.int32)
+    base.rebuild(n0)
+    layers = [base] + [runtime.Layer.clone_of(base) for _ in range(L - 1)]
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s ({args.workload}, {L} layer replicas)",
+          file=sys.stderr, flush=True)
+
+    # per-step inputs for warmup + timed steps, all on the device
+    T = W + K
+    qi, qq, qs, qp, nc_all, dl_all = [], [], [], [], [], []
+    for t in range(T):
+        a, b, c, d = synth.make_queries(w, t)
+        qi.append(a); qq.append(b); qs.append(c); qp.append(d)
+        nc_all.append(synth.n_cells_at(w, t))
+        dl_all.append(synth.dirty_blocks(w, t))
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(np.stack(x))).to(dev)
+    q_idx, q, q_seq, q_pos = to(qi), to(qq), to(qs), to(qp)
+    n_cells, dirty = to(nc_all), to([d.reshape(-1) for d in dl_all])
+    n_dirty = dl_all[0].shape[0]
+    n_q = q_pos.shape[1]
+    nb_max = w.nb_max(T - 1)
+    bufs = [runtime.StepBuffers(layers[0].dims, n_q, nb_max, dev) for _ in range(L)]
+
+    stream = torch.cuda.Stream()
+
+    def enqueue(t, only_score=False):
+        for li, layer in enumerate(layers):
+            layer.n_cells = n_cells[t]
+            bf = bufs[li]
+            if only_score:
+                qsa.score_blocks(layer.dims, layer.seqs(), q_idx[t], q_seq[t], q_pos[t], n_q,
+                                 layer.pooled, layer.pooled_bf16, nb_max, bf.scores, bf.ld)
+            else:
+                runtime.run_step(layer, bf, q_idx[t], q[t], q_seq[t], q_pos[t], dirty[t],
+                                 n_dirty)
+
+    def capture(steps, only_score=False):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in steps:
+                enqueue(t, only_score)
+        return g
+
+    g_warm = capture(range(W)) if W > 0 else None
+    g_main = capture(range(W, T))
+    g_score = capture(range(W, T), only_score=True)
+    torch.cuda.synchronize()
+
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g_main.replay()
+    torch.cuda.synchronize()
+    t_main = time.perf_counter() - t_start
+
+    # live timing of the dominant kernel on its own stream: K*L score launches
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    g_score.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g_score.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    score_us = ev0.elapsed_time(ev1) * 1000.0 / (K * L)
+
+    # correctness guard on the last step of layer 0 (selection sizes)
+    n_sel = bufs[0].n_sel.cpu().numpy()
+    assert np.all(n_sel > 0), "empty selections in the benchmark step"
+
+    ms_per_step = t_main * 1000.0 / K
+    us_per_token_layer = ms_per_step * 1000.0 / L
+    ab = [algorithmic_bytes(w, t) for t in range(W, T)]
+    score_bytes = float(np.mean([a["score"] for a in ab]))
+    step_bytes = float(np.mean([sum(a.values()) for a in ab]))
+    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    result = {
+        "metric": "QSA sparse-attn decode us/token (one QSA layer) at 250k ctx",
+        "value": round(us_per_token_layer, 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (q8_0 KV)" if w.kv_type == synth.KV_Q8_0 else "f32",
+        "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded",
+        "config": {
+            "workload": args.workload,
+            "n_seq": w.n_seq, "n_kv_start": w.n_cells0 + w.n_new, "decode_steps": K,
+            "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
+            "compress_ratio": w.r, "top_k": w.top_k,
+            "layers_per_step": L, "graph_replay": True,
+        },
+        "tokens_per_s_per_layer": round(1e6 / us_per_token_layer, 1),
+        "step_hbm_gbps": round(step_bytes / (us_per_token_layer * 1e-6) / 1e9, 1),
+        "roofline": {
+            "kernel": "k_score_f32",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": round(score_bytes),
+            "avg_launch_us": round(score_us, 3),
+        },
+    }
+
+    if not args.profile and args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all,
+                                              W, K, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all, W, K, budget):
+    """The oracle as it stands, single-threaded, on the first decode steps of
+    the same workload (one layer): update, score, select, attend per step."""
+    import oracle
+    pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
+    n0 = np.full(w.n_seq, w.n_cells0, np.int32)
+    pairs = [(s, b) for s in range(w.n_seq) for b in range(-(-w.n_cells0 // w.r))]
+    oracle.update_pooled(kidx, n0, np.array(pairs, np.int32), pooled, w.r, w.theta, w.eps)
+    done, spent = 0, 0.0
+    for t in range(W + K):
+        t0 = time.perf_counter()
+        oracle.update_pooled(kidx, nc_all[t], dl_all[t], pooled, w.r, w.theta, w.eps)
+        oracle.step(qi[t], qq[t], qs[t], qp[t], pooled, k, v, kv_type=w.kv_type, n_head_kv=w.Hk,
+                    r=w.r, top_k=w.top_k, theta=w.theta, nb_out=w.nb_max(t))
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent > budget:
+            break
+    us = spent / done * 1e6
+    return {"value": round(us, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} decode steps of one layer of {w.name} "
+                      f"({w.n_seq} seq), update+score+select+attend, fp32/fp64 C oracle, "
+                      f"1 thread", "tokens_per_s": round(1e6 / us, 2)}
+
+
+if __name__ == "__main__":
+    main()

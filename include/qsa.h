@@ -1,0 +1,248 @@
+/*
+ * qsa.h -- C ABI of libqsa, the QSA sparse-attention step on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The step has four parts, each one call below:
+ *   1. qsa_update_pooled_keys  -- persistent pooled block-key cache; only the
+ *      dirtied blocks are recomputed.
+ *   2. qsa_score_blocks        -- indexer score of every causal block.
+ *   3. qsa_select_topk_blocks  -- top-k over whole blocks, expanded to cells,
+ *      plus the incomplete tail block's cells.
+ *   4. qsa_sparse_attn_decode / qsa_sparse_attn_prefill -- attention over the
+ *      selected cells only.
+ *
+ * Sources (cited by page title and section):
+ *   [ISSUE] llama.cpp issue #28734, "Eval bug: qwen4exp (Qwen3.8-Flash-Next)
+ *           CUDA: decode slows linearly with context": the fix summary's
+ *           sections lever1, lever3, lever2 and lever2b, and goodbadwolf's
+ *           comment, paragraph "Why the two phases disagree".
+ *   [DISC]  llama.cpp discussion #30071, "Qwen3.8-Flash-Next on 6x3090 and
+ *           6x4090 without NVLink ...", the paragraph that separates the two
+ *           problems (the compact-gather path that keeps q8_0 KV sparse).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers named *_dev are device pointers (hipMalloc'd or equivalent);
+ * the caller owns every buffer, including workspaces.  The library never
+ * allocates, frees or synchronises: each call validates its host-side
+ * arguments, enqueues kernels on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns.  On a validation error nothing is enqueued and no
+ * output is touched.  Device faults surface at the caller's next
+ * synchronisation.  No C++ exception crosses this boundary.  The library
+ * keeps no state between calls; calls on different streams may run
+ * concurrently if their outputs do not overlap.
+ *
+ * Sequences.  n_seq independent sequences each own a region of cap_cells
+ * cells in every per-cell cache (cell index = token position in that
+ * sequence).  n_cells_dev[s] (device, int32) is the number of cells present
+ * in sequence s.  Block b of a sequence is cells b*r .. b*r+r-1.
+ *
+ * Queries.  Query i belongs to sequence q_seq_dev[i] and sits at position
+ * q_pos_dev[i] (both device int32).  A query is valid when
+ * 0 <= q_seq < n_seq and 0 <= q_pos < min(n_cells[q_seq], cap_cells).
+ * An invalid query gets an all -inf score row, an empty selection
+ * (n_sel = 0) and an all-zero attention output; no call reads or writes
+ * outside the buffers on its behalf.
+ *
+ * Per query, nc = floor((q_pos+1)/r) complete blocks are visible; the tail
+ * is the tail_len = q_pos+1 - r*nc (0 .. r-1) cells of the incomplete block
+ * at the query position [ISSUE lever3: fully-future blocks are excluded and
+ * the incomplete tail rides a per-token side input].
+ *
+ * Buffer layouts (all little-endian, row-major unless stated):
+ *   kidx      float32 [n_seq][cap_cells][d_idx]   per-cell indexer keys
+ *   pooled    float32 tiled: [n_seq][cap_blocks/64][d_idx/4][64][4];
+ *             element (s, b, t) is at float offset
+ *               ((s*(cap_blocks/64) + b/64) * (d_idx/4) + t/4) * 256
+ *               + (b%64)*4 + t%4
+ *             (64 blocks side by side per 16-byte dim quad, so 64 lanes read
+ *             64 blocks with one 1 KiB coalesced load).  cap_blocks =
+ *             cap_cells / r.
+ *   pooled_bf16  uint16 (bfloat16 bits) [n_seq][cap_blocks][d_idx]: the same
+ *             keys rounded to nearest even; the MFMA operand at prefill.
+ *   scores    float32 [n_q][ld_scores]
+ *   sel_blocks int32 [n_q][top_k/r]     ascending, padded with -1
+ *   sel_cells  int32 [n_q][top_k+r-1]   ascending cell indices, padded -1;
+ *             top_k + r - 1 is the largest possible set, n_kv_max
+ *             [ISSUE, goodbadwolf: n_kv_max = min(n_kv, top_k + r - 1)]
+ *   n_sel     int32 [n_q]               number of valid entries of sel_cells
+ *   q_idx     float32 [n_q][d_idx]      indexer queries, not yet roped
+ *   q         float32 [n_q][n_head][head_dim]   attention queries (already
+ *             positioned; attention applies no RoPE)
+ *   out       float32 [n_q][n_head][head_dim]
+ *   K, V cache QSA_KV_F32:  float32 [n_seq][cap_cells][n_head_kv][head_dim]
+ *             QSA_KV_Q8_0: bytes [n_seq][cap_cells][n_head_kv][head_dim/32*34];
+ *             each 34-byte q8_0 block is a binary16 scale d followed by 32
+ *             int8 q, value = float(d) * q.
+ *
+ * Supported geometry (else QSA_ENOTSUP): head_dim 256, d_idx 128,
+ * n_head/n_head_kv in {1, 2, 4, 8}, 1 <= r <= 16, top_k % r == 0,
+ * top_k/r <= 4096, cap_cells a multiple of 64*r.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+/* Return codes.  0 is success; errors are negative. */
+#define QSA_OK 0
+#define QSA_EINVAL (-1)  /* bad pointer, size, alignment or geometry       */
+#define QSA_ENOTSUP (-2) /* geometry outside what this build implements    */
+#define QSA_EWS (-3)     /* workspace missing or smaller than required     */
+#define QSA_EHIP (-4)    /* a HIP launch reported an error                 */
+
+/* KV cache element types. */
+#define QSA_KV_F32 0
+#define QSA_KV_Q8_0 1
+
+/* Score modes of qsa_score_blocks. */
+#define QSA_SCORE_F32 0      /* decode: fp32, fixed summation order T      */
+#define QSA_SCORE_BF16 1     /* prefill: bf16 operands, fp32 sum in order T */
+
+/* Workspace owners for qsa_workspace_size. */
+#define QSA_OP_SELECT 0
+#define QSA_OP_ATTN_DECODE 1
+#define QSA_OP_ATTN_PREFILL 2
+#define QSA_OP_SCORE_BF16 3
+
+/* Model geometry and constants.
+ *   kq_scale   attention logit scale; <= 0 means 1/sqrt(head_dim)
+ *   rope_theta RoPE base of the indexer (split-half rotation of pairs
+ *              (t, t + d_idx/2), inverse frequency theta^(-2t/d_idx))
+ *   rms_eps    epsilon of the pooled-key RMS norm
+ *   idx_norm_w_dev  optional device float32 [d_idx] RMS-norm weight (NULL =
+ *              none) */
+typedef struct qsa_dims {
+    int32_t n_head;
+    int32_t n_head_kv;
+    int32_t head_dim;
+    int32_t d_idx;
+    int32_t r;
+    int32_t top_k;
+    int32_t kv_type;
+    float kq_scale;
+    float rope_theta;
+    float rms_eps;
+    const float *idx_norm_w_dev;
+} qsa_dims;
+
+/* Sequence geometry shared by every call. */
+typedef struct qsa_seqs {
+    int32_t n_seq;
+    int64_t cap_cells;
+    const int32_t *n_cells_dev;
+} qsa_seqs;
+
+/* Library version (QSA_ABI_VERSION). */
+int qsa_version(void);
+
+/* Message of the last error returned on the calling thread ("" if none). */
+const char *qsa_last_error(void);
+
+/* Bytes of workspace `op` needs for n_q queries whose scores are nb_max wide
+ * (nb_max is ignored by ops that do not read scores).  Returns 0 and writes
+ * *bytes, or an error code. */
+int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q,
+                       int32_t nb_max, size_t *bytes);
+
+/* 1. Pooled-key update  [ISSUE lever2; lever2b for the device-side block
+ * membership, here the arithmetic members b*r .. b*r+r-1].
+ *
+ * For every entry (seq, block) of dirty_dev (int32 pairs, n_dirty of them;
+ * callers pad the list to a power of two >= 4 with (-1, -1) so a captured
+ * graph keeps its shape): with m = min(r, n_cells[seq] - block*r) present
+ * cells, the block's pooled key is
+ *   a_t   = (kidx[c0][t] + ... + kidx[c0+m-1][t]) / m        (fp32, in order)
+ *   ms    = T(a*a) / d_idx,  inv = 1 / sqrt(ms + rms_eps)   (correctly rounded)
+ *   n_t   = a_t * inv  (* idx_norm_w[t] if given)
+ *   key   = RoPE(n, position block*r)
+ * where T is the stride-halving pairwise fp32 sum (h = d/2, d/4, ..., 1:
+ * v[t] += v[t+h]).  The RoPE angle pos*omega_t and its cosine and sine are
+ * evaluated in fp64 and rounded once to fp32; omega_t = theta^(-2t/d) is
+ * formed in fp64 from nested square roots of theta multiplied over the set
+ * bits of t.  Both `pooled_dev` and, if non-NULL, `pooled_bf16_dev` are
+ * written.  Entries with seq < 0 or seq >= n_seq, or whose block has no
+ * present cell or lies beyond cap_cells/r, are skipped.  The result does not
+ * depend on the order of the list; listing a block twice recomputes it twice.
+ * Listing every block of a sequence rebuilds it from scratch ("resume"). */
+int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs,
+                           const float *kidx_dev, const int32_t *dirty_dev,
+                           int32_t n_dirty, float *pooled_dev,
+                           uint16_t *pooled_bf16_dev, void *stream);
+
+/* 2. Block scores  [ISSUE lever3; the device-side causal bias of the
+ * llama.cpp-multigpu README, section 5, LLAMA_QSA_BIAS_DEVICE].
+ *
+ * For each query: q' = RoPE(q_idx, q_pos) (as above, in fp32);
+ *   scores[i][b] = T(q' * pooled[q_seq][b])   for b < nc,
+ *   scores[i][b] = -inf                       for nc <= b < nb_max.
+ * mode QSA_SCORE_F32 multiplies in fp32 (each product rounded) and sums in
+ * order T: the result is fixed to the last bit.  mode QSA_SCORE_BF16 rounds
+ * q' and the keys to bf16 (pooled_bf16_dev) and contracts them on the matrix
+ * cores with fp32 accumulation: products are exact, the sum order is the
+ * hardware's, so each score is within 2*(d_idx-1)*2^-24*sum|q'_t k_t| of the
+ * T-ordered bf16 score.  ld_scores >= nb_max; nb_max <= cap_cells/r.
+ * Mode QSA_SCORE_BF16 needs the workspace QSA_OP_SCORE_BF16 reports (the
+ * roped bf16 queries); mode QSA_SCORE_F32 needs none (ws may be NULL). */
+int qsa_score_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
+                     const float *q_idx_dev, const int32_t *q_seq_dev,
+                     const int32_t *q_pos_dev, int32_t n_q,
+                     const float *pooled_dev, const uint16_t *pooled_bf16_dev,
+                     int32_t nb_max, float *scores_dev, int64_t ld_scores,
+                     int32_t mode, void *ws_dev, size_t ws_bytes, void *stream);
+
+/* 3. Block top-k and expansion  [ISSUE lever3: blocks are selected first and
+ * only the selected ones are expanded to cells; goodbadwolf's n_kv_max].
+ *
+ * Per query, the candidates are the blocks b < min(nc, nb_max) with a finite
+ * score.  They are ranked by score, descending, ties to the lower block index
+ * (-0 equals +0), and the first min(top_k/r, count) are kept.  Output:
+ * sel_blocks in ascending order; sel_cells = each kept block's r cells,
+ * ascending, then the tail cells r*nc .. q_pos; n_sel = r*kept + tail_len
+ * (<= top_k + r - 1).  Unused entries are -1.  Exact: the set is the one the
+ * ranking defines, bit for bit.  No workspace is needed (ws may be NULL). */
+int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
+                           const float *scores_dev, int64_t ld_scores,
+                           const int32_t *q_seq_dev, const int32_t *q_pos_dev,
+                           int32_t n_q, int32_t nb_max, int32_t *sel_blocks_dev,
+                           int32_t *sel_cells_dev, int32_t *n_sel_dev, void *ws_dev,
+                           size_t ws_bytes, void *stream);
+
+/* 4. Sparse attention  [ISSUE lever1: attention runs over the top-k set
+ * only; DISC: q8_0 rows are dequantised inside the gather, never the whole
+ * cache].
+ *
+ * For query i and head h (KV head h / (n_head/n_head_kv)), over the n_sel[i]
+ * cells c_j listed in sel_cells[i]:
+ *   l_j = kq_scale * <q[i][h], K[c_j]>,  w = softmax(l),
+ *   out[i][h] = sum_j w_j * V[c_j]
+ * with K and V dequantised to fp32 and fp32 accumulation.  Cells outside
+ * 0 .. min(n_cells, cap_cells)-1 are ignored; an empty set gives zeros.
+ * Decode is tuned for few queries (split over cells, then a combine), prefill
+ * for many.  Both need the workspace qsa_workspace_size reports. */
+int qsa_sparse_attn_decode(const qsa_dims *dims, const qsa_seqs *seqs,
+                           const float *q_dev, const int32_t *q_seq_dev,
+                           int32_t n_q, const void *k_cache_dev,
+                           const void *v_cache_dev, const int32_t *sel_cells_dev,
+                           const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
+                           size_t ws_bytes, void *stream);
+
+int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs,
+                            const float *q_dev, const int32_t *q_seq_dev,
+                            int32_t n_q, const void *k_cache_dev,
+                            const void *v_cache_dev, const int32_t *sel_cells_dev,
+                            const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
+                            size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

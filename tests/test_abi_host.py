@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/qsa.h declares, sizes workspaces, and rejects bad arguments before any
+device work (so these run without a GPU: every call below fails validation).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from top_sparse_attention_pooled_amd import qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced here
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "qsa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qsa.load()
+    names = _declared()
+    assert set(names) == set(qsa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_error_string():
+    assert qsa.version() == 1
+    assert isinstance(qsa.load().qsa_last_error(), bytes)
+
+
+def test_workspace_sizes():
+    d = qsa.Dims()
+    assert qsa.workspace_size(d, qsa.OP_SELECT, 5) == 0
+    assert qsa.workspace_size(d, qsa.OP_SCORE_BF16, 512) == 512 * 128 * 2
+    runs = -(-d.ld_cells // 64)
+    assert qsa.workspace_size(d, qsa.OP_ATTN_DECODE, 5) == 5 * runs * 16 * 258 * 4
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.workspace_size(d, 99, 1)
+    assert e.value.code == qsa.QSA_EINVAL
+
+
+def _seqs(cap=4096 * 4, n_cells=FAKE):
+    return qsa.Seqs(1, cap, n_cells)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 128, qsa.QSA_ENOTSUP),
+    ("d_idx", 64, qsa.QSA_ENOTSUP),
+    ("n_head", 12, qsa.QSA_ENOTSUP),     # 12/2 = 6 heads per KV head
+    ("n_head", 3, qsa.QSA_EINVAL),       # not a multiple of 2
+    ("top_k", 2050, qsa.QSA_EINVAL),     # not a multiple of r
+    ("top_k", 4 * 4097, qsa.QSA_ENOTSUP),
+    ("r", 0, qsa.QSA_ENOTSUP),
+    ("kv_type", 7, qsa.QSA_EINVAL),
+    ("rope_theta", 0.5, qsa.QSA_EINVAL),
+])
+def test_bad_dims_rejected(field, value, code):
+    d = qsa.Dims()
+    setattr(d, field, value)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.update_pooled_keys(d, _seqs(), FAKE, FAKE, 4, FAKE, None, stream=0)
+    assert e.value.code == code
+
+
+def test_bad_geometry_and_pointers_rejected():
+    d = qsa.Dims()
+    cases = [
+        # cap_cells not a multiple of 64*r
+        lambda: qsa.update_pooled_keys(d, _seqs(cap=1000), FAKE, FAKE, 4, FAKE, None, stream=0),
+        # pooled not 16-byte aligned
+        lambda: qsa.update_pooled_keys(d, _seqs(), FAKE, FAKE, 4, FAKE + 8, None, stream=0),
+        # null n_cells
+        lambda: qsa.update_pooled_keys(d, qsa.Seqs(1, 4096, None), FAKE, FAKE, 4, FAKE, None,
+                                       stream=0),
+        # nb_max beyond the capacity in blocks
+        lambda: qsa.score_blocks(d, _seqs(), FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4097, FAKE, 5000,
+                                 stream=0),
+        # ld below nb_max
+        lambda: qsa.select_topk_blocks(d, _seqs(), FAKE, 10, FAKE, FAKE, 1, 64, FAKE, FAKE, FAKE,
+                                       stream=0),
+        # unknown score mode
+        lambda: qsa.score_blocks(d, _seqs(), FAKE, FAKE, FAKE, 1, FAKE, FAKE, 64, FAKE, 64,
+                                 mode=5, stream=0),
+        # misaligned attention query
+        lambda: qsa.sparse_attn_decode(d, _seqs(), FAKE + 4, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, 1 << 30, stream=0),
+    ]
+    for fn in cases:
+        with pytest.raises(qsa.QsaError) as e:
+            fn()
+        assert e.value.code == qsa.QSA_EINVAL, qsa.load().qsa_last_error()
+
+
+def test_workspace_too_small_rejected():
+    d = qsa.Dims()
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.sparse_attn_decode(d, _seqs(), FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                               stream=0)
+    assert e.value.code == qsa.QSA_EWS
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.score_blocks(d, _seqs(), FAKE, FAKE, FAKE, 4, FAKE, FAKE, 64, FAKE, 64,
+                         mode=qsa.SCORE_BF16, ws=None, ws_bytes=0, stream=0)
+    assert e.value.code == qsa.QSA_EWS
+
+
+def test_empty_calls_are_noops():
+    d = qsa.Dims()
+    qsa.update_pooled_keys(d, _seqs(), FAKE, FAKE, 0, FAKE, None, stream=0)
+    qsa.score_blocks(d, _seqs(), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, FAKE, 64, stream=0)
+    qsa.select_topk_blocks(d, _seqs(), FAKE, 64, FAKE, FAKE, 0, 64, FAKE, FAKE, FAKE, stream=0)
+    assert qsa.load().qsa_last_error() == b""

@@ -1,0 +1,247 @@
+// api.hip -- the extern "C" boundary of libqsa (declared in include/qsa.h):
+// host-side validation, workspace sizing and dispatch to the kernels.  No
+// call allocates, frees or synchronises; errors are returned before anything
+// is enqueued, with a message kept per thread.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return QSA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_dims(const qsa_dims *d) {
+    if (!d) return fail(QSA_EINVAL, "dims is NULL");
+    if (d->head_dim != qsa::kHeadDim)
+        return fail(QSA_ENOTSUP, "head_dim %d not supported (256 only)", d->head_dim);
+    if (d->d_idx != qsa::kDIdx)
+        return fail(QSA_ENOTSUP, "d_idx %d not supported (128 only)", d->d_idx);
+    if (d->n_head <= 0 || d->n_head_kv <= 0 || d->n_head % d->n_head_kv)
+        return fail(QSA_EINVAL, "n_head %d must be a positive multiple of n_head_kv %d",
+                    d->n_head, d->n_head_kv);
+    const int G = d->n_head / d->n_head_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(QSA_ENOTSUP, "n_head/n_head_kv = %d not in {1,2,4,8}", G);
+    if (d->r < 1 || d->r > 16) return fail(QSA_ENOTSUP, "r = %d outside 1..16", d->r);
+    if (d->top_k < d->r || d->top_k % d->r)
+        return fail(QSA_EINVAL, "top_k %d must be a positive multiple of r %d", d->top_k, d->r);
+    if (d->top_k / d->r > 4096)
+        return fail(QSA_ENOTSUP, "top_k/r = %d above 4096", d->top_k / d->r);
+    if (d->kv_type != QSA_KV_F32 && d->kv_type != QSA_KV_Q8_0)
+        return fail(QSA_EINVAL, "kv_type %d unknown", d->kv_type);
+    if (!(d->rope_theta > 1.0f)) return fail(QSA_EINVAL, "rope_theta must be > 1");
+    if (!(d->rms_eps >= 0.0f)) return fail(QSA_EINVAL, "rms_eps must be >= 0");
+    if (d->idx_norm_w_dev && !aligned(d->idx_norm_w_dev, 4))
+        return fail(QSA_EINVAL, "idx_norm_w_dev misaligned");
+    return QSA_OK;
+}
+
+int check_seqs(const qsa_dims *d, const qsa_seqs *s) {
+    if (!s) return fail(QSA_EINVAL, "seqs is NULL");
+    if (s->n_seq <= 0) return fail(QSA_EINVAL, "n_seq must be positive");
+    if (s->cap_cells <= 0 || s->cap_cells % ((int64_t)qsa::kTile * d->r))
+        return fail(QSA_EINVAL, "cap_cells %lld must be a positive multiple of 64*r",
+                    (long long)s->cap_cells);
+    if (s->cap_cells > ((int64_t)1 << 31) - 1)
+        return fail(QSA_ENOTSUP, "cap_cells above 2^31-1");
+    if (!s->n_cells_dev || !aligned(s->n_cells_dev, 4))
+        return fail(QSA_EINVAL, "n_cells_dev NULL or misaligned");
+    return QSA_OK;
+}
+
+qsa::SeqGeom geom(const qsa_seqs *s) { return {s->n_seq, s->cap_cells, s->n_cells_dev}; }
+
+int check_queries(const int32_t *q_seq, const int32_t *q_pos, int32_t n_q, bool need_pos) {
+    if (n_q < 0) return fail(QSA_EINVAL, "n_q negative");
+    if (n_q > 65535) return fail(QSA_ENOTSUP, "n_q above 65535");
+    if (n_q == 0) return QSA_OK;
+    if (!q_seq || !aligned(q_seq, 4)) return fail(QSA_EINVAL, "q_seq_dev NULL or misaligned");
+    if (need_pos && (!q_pos || !aligned(q_pos, 4)))
+        return fail(QSA_EINVAL, "q_pos_dev NULL or misaligned");
+    return QSA_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(QSA_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_version(void) { return QSA_ABI_VERSION; }
+
+const char *qsa_last_error(void) { return g_err; }
+
+int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q, int32_t nb_max,
+                       size_t *bytes) {
+    (void)nb_max;
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!bytes) return fail(QSA_EINVAL, "bytes is NULL");
+    if (n_q < 0) return fail(QSA_EINVAL, "n_q negative");
+    const int ld_cells = dims->top_k + dims->r - 1;
+    switch (op) {
+        case QSA_OP_SELECT: *bytes = 0; break;
+        case QSA_OP_ATTN_DECODE:
+            *bytes = qsa::attn_decode_ws_bytes(n_q, dims->n_head, ld_cells);
+            break;
+        case QSA_OP_ATTN_PREFILL:
+            *bytes = qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells);
+            break;
+        case QSA_OP_SCORE_BF16: *bytes = (size_t)n_q * qsa::kDIdx * sizeof(uint16_t); break;
+        default: return fail(QSA_EINVAL, "unknown op %d", op);
+    }
+    return ok();
+}
+
+int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+                           const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
+                           uint16_t *pooled_bf16_dev, void *stream) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (rc) return rc;
+    if (n_dirty < 0) return fail(QSA_EINVAL, "n_dirty negative");
+    if (n_dirty == 0) return ok();
+    if (!kidx_dev || !aligned(kidx_dev, 4)) return fail(QSA_EINVAL, "kidx_dev NULL or misaligned");
+    if (!dirty_dev || !aligned(dirty_dev, 4)) return fail(QSA_EINVAL, "dirty_dev NULL or misaligned");
+    if (!pooled_dev || !aligned(pooled_dev, 16))
+        return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
+    if (pooled_bf16_dev && !aligned(pooled_bf16_dev, 16))
+        return fail(QSA_EINVAL, "pooled_bf16_dev not 16-byte aligned");
+    qsa::UpdateArgs a{geom(seqs), kidx_dev, dirty_dev, n_dirty, pooled_dev, pooled_bf16_dev,
+                      dims->r, dims->rope_theta, dims->rms_eps, dims->idx_norm_w_dev};
+    return launched(qsa::launch_update_pooled(a, (hipStream_t)stream), "update_pooled_keys");
+}
+
+int qsa_score_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_idx_dev,
+                     const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                     const float *pooled_dev, const uint16_t *pooled_bf16_dev, int32_t nb_max,
+                     float *scores_dev, int64_t ld_scores, int32_t mode, void *ws_dev,
+                     size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (!rc) rc = check_queries(q_seq_dev, q_pos_dev, n_q, true);
+    if (rc) return rc;
+    const int64_t cap_blocks = seqs->cap_cells / dims->r;
+    if (nb_max < 0 || nb_max > cap_blocks)
+        return fail(QSA_EINVAL, "nb_max %d outside 0..cap_cells/r", nb_max);
+    if (ld_scores < nb_max) return fail(QSA_EINVAL, "ld_scores below nb_max");
+    if (n_q == 0 || nb_max == 0) return ok();
+    if (!q_idx_dev || !aligned(q_idx_dev, 4)) return fail(QSA_EINVAL, "q_idx_dev NULL or misaligned");
+    if (!scores_dev || !aligned(scores_dev, 4))
+        return fail(QSA_EINVAL, "scores_dev NULL or misaligned");
+    qsa::ScoreArgs a{geom(seqs), q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
+                     pooled_bf16_dev, nb_max, scores_dev, ld_scores, dims->r, dims->rope_theta};
+    if (mode == QSA_SCORE_F32) {
+        if (!pooled_dev || !aligned(pooled_dev, 16))
+            return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
+        return launched(qsa::launch_score_f32(a, (hipStream_t)stream), "score_blocks");
+    }
+    if (mode == QSA_SCORE_BF16) {
+        if (!pooled_bf16_dev || !aligned(pooled_bf16_dev, 16))
+            return fail(QSA_EINVAL, "pooled_bf16_dev NULL or not 16-byte aligned");
+        const size_t need = (size_t)n_q * qsa::kDIdx * sizeof(uint16_t);
+        if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 16))
+            return fail(QSA_EWS, "score workspace needs %zu bytes, 16-byte aligned", need);
+        return launched(qsa::launch_score_bf16_ws(a, (uint16_t *)ws_dev, (hipStream_t)stream),
+                        "score_blocks(bf16)");
+    }
+    return fail(QSA_EINVAL, "unknown score mode %d", mode);
+}
+
+int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const float *scores_dev,
+                           int64_t ld_scores, const int32_t *q_seq_dev, const int32_t *q_pos_dev,
+                           int32_t n_q, int32_t nb_max, int32_t *sel_blocks_dev,
+                           int32_t *sel_cells_dev, int32_t *n_sel_dev, void *ws_dev,
+                           size_t ws_bytes, void *stream) {
+    (void)ws_dev;
+    (void)ws_bytes;
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (!rc) rc = check_queries(q_seq_dev, q_pos_dev, n_q, true);
+    if (rc) return rc;
+    const int64_t cap_blocks = seqs->cap_cells / dims->r;
+    if (nb_max < 0 || nb_max > cap_blocks)
+        return fail(QSA_EINVAL, "nb_max %d outside 0..cap_cells/r", nb_max);
+    if (ld_scores < nb_max) return fail(QSA_EINVAL, "ld_scores below nb_max");
+    if (n_q == 0) return ok();
+    if (nb_max > 0 && (!scores_dev || !aligned(scores_dev, 4)))
+        return fail(QSA_EINVAL, "scores_dev NULL or misaligned");
+    if (!sel_blocks_dev || !sel_cells_dev || !n_sel_dev || !aligned(sel_blocks_dev, 4) ||
+        !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
+        return fail(QSA_EINVAL, "selection outputs NULL or misaligned");
+    qsa::SelectArgs a{geom(seqs), scores_dev, ld_scores, q_seq_dev, q_pos_dev, n_q, nb_max,
+                      dims->r, dims->top_k, sel_blocks_dev, sel_cells_dev, n_sel_dev};
+    return launched(qsa::launch_select(a, (hipStream_t)stream), "select_topk_blocks");
+}
+
+static int attn_common(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
+                       const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
+                       const void *v_cache_dev, const int32_t *sel_cells_dev,
+                       const int32_t *n_sel_dev, float *out_dev, void *ws_dev, size_t ws_bytes,
+                       void *stream, bool prefill) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (!rc) rc = check_queries(q_seq_dev, nullptr, n_q, false);
+    if (rc) return rc;
+    if (n_q == 0) return ok();
+    if (!q_dev || !aligned(q_dev, 16)) return fail(QSA_EINVAL, "q_dev NULL or not 16-byte aligned");
+    if (!out_dev || !aligned(out_dev, 4)) return fail(QSA_EINVAL, "out_dev NULL or misaligned");
+    if (!k_cache_dev || !v_cache_dev || !aligned(k_cache_dev, 16) || !aligned(v_cache_dev, 16))
+        return fail(QSA_EINVAL, "K/V cache NULL or not 16-byte aligned");
+    if (!sel_cells_dev || !n_sel_dev || !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
+        return fail(QSA_EINVAL, "selection inputs NULL or misaligned");
+    const int ld_cells = dims->top_k + dims->r - 1;
+    const size_t need = prefill ? qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells)
+                                : qsa::attn_decode_ws_bytes(n_q, dims->n_head, ld_cells);
+    if (need && (!ws_dev || ws_bytes < need || !aligned(ws_dev, 16)))
+        return fail(QSA_EWS, "attention workspace needs %zu bytes, 16-byte aligned", need);
+    const float scale =
+        dims->kq_scale > 0.0f ? dims->kq_scale : 1.0f / sqrtf((float)dims->head_dim);
+    qsa::AttnArgs a{geom(seqs), q_dev,         q_seq_dev,     n_q,           dims->n_head,
+                    dims->n_head_kv, dims->kv_type, k_cache_dev, v_cache_dev, sel_cells_dev,
+                    n_sel_dev,      ld_cells,      scale,         out_dev,       (float *)ws_dev,
+                    ws_bytes};
+    hipError_t e = prefill ? qsa::launch_attn_prefill(a, (hipStream_t)stream)
+                           : qsa::launch_attn_decode(a, (hipStream_t)stream);
+    return launched(e, prefill ? "sparse_attn_prefill" : "sparse_attn_decode");
+}
+
+int qsa_sparse_attn_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
+                           const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
+                           const void *v_cache_dev, const int32_t *sel_cells_dev,
+                           const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
+                           size_t ws_bytes, void *stream) {
+    return attn_common(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
+                       sel_cells_dev, n_sel_dev, out_dev, ws_dev, ws_bytes, stream, false);
+}
+
+int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
+                            const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
+                            const void *v_cache_dev, const int32_t *sel_cells_dev,
+                            const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
+                            size_t ws_bytes, void *stream) {
+    return attn_common(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
+                       sel_cells_dev, n_sel_dev, out_dev, ws_dev, ws_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,261 @@
+// score.hip -- indexer scoring of every causal block against each query
+// (llama.cpp issue #28734, fix summary, "lever3": fully-future blocks get -inf
+// and the incomplete tail block is not scored; the README of
+// llama.cpp-multigpu, section 5, keeps that causal bias on the device).
+//
+// Decode (fp32).  The pooled keys are stored as 64-block tiles with the 64
+// blocks of each 4-dim quad side by side, so lane l of a wavefront owns block
+// 64*tile + l and reads its 128 dims with 32 fully coalesced 1 KiB loads; the
+// whole 128-term dot product then runs in-lane in the fixed order T with no
+// cross-lane traffic.  The kernel is a pure HBM stream: 512 bytes of key per
+// block, 4 bytes of score out.
+//
+// Prefill (bf16).  The same contraction for many queries is a dense
+// [queries x 128] x [128 x blocks] product, done on the matrix cores with
+// v_mfma_f32_16x16x32_bf16 from bf16 copies of the roped queries and keys.
+#include "qsa_internal.h"
+
+namespace qsa {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// Roped query element pair (t, t+64) of query i at position p, fp32.
+__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p, float theta,
+                                                float &lo, float &hi) {
+    const float xl = q[t], xh = q[t + 64];
+    float c, s;
+    rope_cs((double)theta, t, p, c, s);
+    const float lc = xl * c, hs = xh * s;
+    const float hc = xh * c, ls = xl * s;
+    lo = lc - hs;
+    hi = hc + ls;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 decode scoring
+// ---------------------------------------------------------------------------
+
+// grid (ceil(nb_max/256), n_q); 4 wavefronts, one 64-block tile each.
+__global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
+    __shared__ float4 qr4[kQuads];
+    const int i = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    int s;
+    int64_t p;
+    bool valid;
+    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
+                                    a.g.n_cells, a.r, s, p, valid);
+    const int64_t cap_blocks = a.g.cap_cells / a.r;
+    const int64_t wg_b0 = (int64_t)blockIdx.x * 256;
+    const int64_t b0 = wg_b0 + wave * kTile;
+    const int64_t b = b0 + lane;
+
+    // Issue the key loads first; the query rotation below overlaps them.
+    float4 k[kQuads];
+    if (b0 < nc) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+                                a.pooled + ((int64_t)s * (cap_blocks / kTile) + b0 / kTile) *
+                                               kTileFloats) +
+                            lane;
+#pragma unroll
+        for (int q = 0; q < kQuads; ++q) k[q] = src[q * kTile];
+    }
+    if (wg_b0 < nc && wave == 0) {
+        float lo, hi;
+        rope_query_pair(a.q_idx + (int64_t)i * kDIdx, lane, p, a.theta, lo, hi);
+        float *qr = reinterpret_cast<float *>(qr4);
+        qr[lane] = lo;
+        qr[lane + 64] = hi;
+    }
+    __syncthreads();
+
+    float sc = -INFINITY;
+    if (b < nc) {
+        // T: level 64 pairs quad q with q+16, level 32 q with q+8, ... level 4
+        // quad 0 with quad 1, then components (0,2), (1,3), then the pair.
+        float4 acc[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const float4 qa = qr4[q], qb = qr4[q + 16];
+            const float4 ka = k[q], kb = k[q + 16];
+            float4 pa, pb;
+            pa.x = qa.x * ka.x; pa.y = qa.y * ka.y; pa.z = qa.z * ka.z; pa.w = qa.w * ka.w;
+            pb.x = qb.x * kb.x; pb.y = qb.y * kb.y; pb.z = qb.z * kb.z; pb.w = qb.w * kb.w;
+            acc[q].x = pa.x + pb.x; acc[q].y = pa.y + pb.y;
+            acc[q].z = pa.z + pb.z; acc[q].w = pa.w + pb.w;
+        }
+#pragma unroll
+        for (int h = 8; h >= 1; h >>= 1) {
+#pragma unroll
+            for (int q = 0; q < h; ++q) {
+                acc[q].x = acc[q].x + acc[q + h].x;
+                acc[q].y = acc[q].y + acc[q + h].y;
+                acc[q].z = acc[q].z + acc[q + h].z;
+                acc[q].w = acc[q].w + acc[q + h].w;
+            }
+        }
+        const float x0 = acc[0].x + acc[0].z;
+        const float x1 = acc[0].y + acc[0].w;
+        sc = x0 + x1;
+    }
+    if (b < a.nb_max) a.scores[(int64_t)i * a.ld + b] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 prefill scoring on the matrix cores
+// ---------------------------------------------------------------------------
+
+// One wavefront per query: roped query rounded to bf16 (zeros if invalid).
+__global__ __launch_bounds__(256) void k_rope_queries_bf16(ScoreArgs a, uint16_t *qr_bf16) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= a.n_q) return;
+    int s;
+    int64_t p;
+    bool valid;
+    query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells, a.g.n_cells, a.r, s, p, valid);
+    uint16_t lo16 = 0, hi16 = 0;
+    if (valid) {
+        float lo, hi;
+        rope_query_pair(a.q_idx + (int64_t)i * kDIdx, lane, p, a.theta, lo, hi);
+        lo16 = bf16_rne(lo);
+        hi16 = bf16_rne(hi);
+    }
+    qr_bf16[(int64_t)i * kDIdx + lane] = lo16;
+    qr_bf16[(int64_t)i * kDIdx + lane + 64] = hi16;
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// grid (ceil(nb_max/256), ceil(n_q/64)); workgroup tile 64 queries x 256
+// blocks, each wavefront 64 queries x 64 blocks as 4x4 16x16 MFMA tiles.
+// Queries of one tile may belong to different sequences: the tile is swept
+// once per distinct sequence, storing only that sequence's rows.
+__global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs a, const uint16_t *qr_bf16) {
+    __shared__ int s_seq[64];
+    __shared__ int64_t s_nc[64];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q0 = blockIdx.y * 64;
+    const int64_t bw0 = (int64_t)blockIdx.x * 256 + wave * 64;
+    const int64_t cap_blocks = a.g.cap_cells / a.r;
+    if (threadIdx.x < 64) {
+        const int qi = q0 + threadIdx.x;
+        int s = -1;
+        int64_t nc = 0;
+        if (qi < a.n_q) {
+            int64_t p;
+            bool valid;
+            nc = query_blocks(a.q_seq, a.q_pos, qi, a.g.n_seq, a.g.cap_cells, a.g.n_cells, a.r,
+                              s, p, valid);
+            if (!valid) s = -1;
+        }
+        s_seq[threadIdx.x] = qi < a.n_q ? s : -2;
+        s_nc[threadIdx.x] = nc;
+    }
+    __syncthreads();
+
+    const int mrow = lane & 15;        // A row / B column within a 16-tile
+    const int kseg = (lane >> 4) * 8;  // 8 consecutive k per lane
+    bf16x8_t A[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int qi = q0 + rb * 16 + mrow;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (qi < a.n_q)
+                A[rb][ks] = load_bf16x8(qr_bf16 + (int64_t)qi * kDIdx + ks * 32 + kseg);
+            else
+                A[rb][ks] = bf16x8_t{};
+        }
+    }
+
+    // rows with an invalid query: -inf over this wavefront's columns
+    for (int r = 0; r < 64; ++r) {
+        if (s_seq[r] != -1) continue;
+        const int64_t b = bw0 + lane;
+        if (b < a.nb_max) a.scores[(int64_t)(q0 + r) * a.ld + b] = -INFINITY;
+    }
+
+    uint64_t done = 0;  // rows handled (wave-uniform)
+    for (int r = 0; r < 64; ++r)
+        if (s_seq[r] < 0) done |= 1ull << r;
+    while (done != ~0ull) {
+        const int r0 = __builtin_ctzll(~done);
+        const int sq = s_seq[r0];
+        uint64_t rows = 0;
+        int64_t ncmax = 0;
+        for (int r = r0; r < 64; ++r)
+            if (s_seq[r] == sq) {
+                rows |= 1ull << r;
+                ncmax = s_nc[r] > ncmax ? s_nc[r] : ncmax;
+            }
+        done |= rows;
+        const uint16_t *keys = a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx;
+#pragma unroll 1
+        for (int cb = 0; cb < 4; ++cb) {
+            const int64_t bc0 = bw0 + cb * 16;
+            if (bc0 >= a.nb_max) break;
+            const int64_t nb = bc0 + mrow;  // this lane's B column (block)
+            const bool live = bc0 < ncmax;  // any row sees any block here
+            bf16x8_t B[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (live && nb < cap_blocks)
+                    B[ks] = load_bf16x8(keys + nb * kDIdx + ks * 32 + kseg);
+                else
+                    B[ks] = bf16x8_t{};
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                if (live) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb][ks], B[ks], acc, 0, 0,
+                                                                      0);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = rb * 16 + (lane >> 4) * 4 + jj;
+                    if (!((rows >> r) & 1)) continue;
+                    if (nb >= a.nb_max) continue;
+                    const float v = nb < s_nc[r] ? acc[jj] : -INFINITY;
+                    a.scores[(int64_t)(q0 + r) * a.ld + nb] = v;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t st) {
+    if (a.n_q <= 0 || a.nb_max <= 0) return hipSuccess;
+    dim3 grid((a.nb_max + 255) / 256, a.n_q);
+    hipLaunchKernelGGL(k_score_f32, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ws must hold n_q * 128 bf16 values (the roped queries).
+hipError_t launch_score_bf16_ws(const ScoreArgs &a, uint16_t *qr_bf16, hipStream_t st) {
+    if (a.n_q <= 0 || a.nb_max <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rope_queries_bf16, dim3((a.n_q + 3) / 4), dim3(256), 0, st, a,
+                       qr_bf16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid((a.nb_max + 255) / 256, (a.n_q + 63) / 64);
+    hipLaunchKernelGGL(k_score_bf16, grid, dim3(256), 0, st, a,
+                       static_cast<const uint16_t *>(qr_bf16));
+    return hipGetLastError();
+}
+
+}  // namespace qsa
