@@ -111,6 +111,7 @@ extern "C" {
 #define QSA_OP_ATTN_DECODE 1
 #define QSA_OP_ATTN_PREFILL 2
 #define QSA_OP_SCORE_BF16 3
+#define QSA_OP_SCORE_SELECT 4
 
 /* Model geometry and constants.
  *   kq_scale   attention logit scale; <= 0 means 1/sqrt(head_dim)
@@ -214,6 +215,24 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
                            int32_t n_q, int32_t nb_max, int32_t *sel_blocks_dev,
                            int32_t *sel_cells_dev, int32_t *n_sel_dev, void *ws_dev,
                            size_t ws_bytes, void *stream);
+
+/* 2+3 fused, for decode.  Exactly qsa_score_blocks (mode QSA_SCORE_F32)
+ * followed by qsa_select_topk_blocks -- the same scores (written to
+ * scores_dev) and the same selection, bit for bit -- in one launch: every
+ * workgroup scores 256 blocks and keeps its 16 best keys, and the last
+ * workgroup of each query selects from those, re-admitting all keys of any
+ * workgroup whose dropped keys could compete.
+ *
+ * Workspace: qsa_workspace_size(QSA_OP_SCORE_SELECT, n_q, nb_max) bytes,
+ * 256-byte aligned.  Its first n_q 32-bit words are arrival counters that
+ * must be zero before the first call (allocate it zero-filled); every call
+ * leaves them zero.  Calls that share a workspace must not overlap. */
+int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs,
+                            const float *q_idx_dev, const int32_t *q_seq_dev,
+                            const int32_t *q_pos_dev, int32_t n_q, const float *pooled_dev,
+                            int32_t nb_max, float *scores_dev, int64_t ld_scores,
+                            int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                            int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
 /* 4. Sparse attention  [ISSUE lever1: attention runs over the top-k set
  * only; DISC: q8_0 rows are dequantised inside the gather, never the whole

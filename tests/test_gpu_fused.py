@@ -1,0 +1,120 @@
+"""GPU parity of the fused decode score+select call against the oracle and
+against the two-call path, with inputs built to drive every branch of its
+selection: the common case, workgroups whose dropped keys compete (their full
+key sets are re-admitted), so many such workgroups that the scores are
+re-streamed, all-tied scores, and contexts with fewer blocks than the budget.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_sparse_attention_pooled_amd import qsa, runtime, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def aligned_cells(w, q_idx, p, blocks, kidx):
+    """Make the given blocks score near the maximum for a query at position p:
+    each of their cells holds the roped query rotated back to the block's
+    position (numpy complex rotation; the oracle scores whatever results)."""
+    d = w.d
+    omega = w.theta ** (-2.0 * np.arange(d // 2) / d)
+    z = (q_idx[:d // 2] + 1j * q_idx[d // 2:]) * np.exp(1j * p * omega)
+    for b in blocks:
+        zb = z * np.exp(-1j * b * w.r * omega)
+        kidx[b * w.r:(b + 1) * w.r] = np.concatenate([zb.real, zb.imag]).astype(np.float32)
+
+
+def run_case(name, w, n_cells, q_idx, kidx):
+    say(f"fused select: {name}")
+    layer = runtime.Layer(w, DEV, kidx=kidx[None].copy() if kidx.ndim == 2 else kidx)
+    layer.rebuild(np.array([n_cells], np.int32))
+    ref_pooled = np.zeros((1, w.cap_blocks, w.d), np.float32)
+    oracle.update_pooled(layer.kidx.cpu().numpy(), np.array([n_cells], np.int32),
+                         np.array([(0, b) for b in range(-(-n_cells // w.r))], np.int32),
+                         ref_pooled, w.r, w.theta, w.eps)
+    positions = [p for p in (n_cells - 1, n_cells - 2, n_cells - 3) if p >= 0]
+    n_q = len(positions)
+    qi = np.repeat(q_idx[None], n_q, axis=0).astype(np.float32)
+    nb_max = -(-n_cells // w.r)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    q_seq, q_pos = t(np.zeros(n_q, np.int32)), t(np.array(positions, np.int32))
+    fused = runtime.StepBuffers(layer.dims, n_q, nb_max, DEV)
+    qsa.score_select_decode(layer.dims, layer.seqs(), t(qi), q_seq, q_pos, n_q, layer.pooled,
+                            nb_max, fused.scores, fused.ld, fused.sel_blocks, fused.sel_cells,
+                            fused.n_sel, fused.ws_fused, fused.ws_fused_bytes)
+    sep = runtime.StepBuffers(layer.dims, n_q, nb_max, DEV)
+    qsa.score_blocks(layer.dims, layer.seqs(), t(qi), q_seq, q_pos, n_q, layer.pooled, None,
+                     nb_max, sep.scores, sep.ld)
+    qsa.select_topk_blocks(layer.dims, layer.seqs(), sep.scores, sep.ld, q_seq, q_pos, n_q,
+                           nb_max, sep.sel_blocks, sep.sel_cells, sep.n_sel)
+    torch.cuda.synchronize()
+    # counters are back to zero for the next call
+    assert int(fused.ws_fused[:4 * n_q].view(torch.int32).abs().sum().cpu()) == 0
+    for i, p in enumerate(positions):
+        r_scores = oracle.score_query(qi[i], p, ref_pooled[0], nb_max, w.r, w.theta)
+        rb, rc = oracle.select(r_scores, p, w.r, w.top_k)
+        for bufs, label in ((fused, "fused"), (sep, "two-call")):
+            gs = bufs.scores.cpu().numpy()[i, :nb_max]
+            assert np.array_equal(gs.view(np.uint32), r_scores.view(np.uint32)), label
+            gb = bufs.sel_blocks.cpu().numpy()[i]
+            gc = bufs.sel_cells.cpu().numpy()[i]
+            assert int(bufs.n_sel.cpu()[i]) == rc.size, (label, p)
+            assert np.array_equal(gb[:rb.size], rb), (label, p)
+            assert np.all(gb[rb.size:] == -1)
+            assert np.array_equal(gc[:rc.size], rc), (label, p)
+            assert np.all(gc[rc.size:] == -1)
+    return r_scores
+
+
+def workload():
+    return synth.Workload("fz", 95, 1, 40000, n_new=1, steps=1, top_k=2048)
+
+
+def test_fused_common_case():
+    w = workload()
+    kidx = synth.make_kidx(w)[0]
+    q = synth.normal((w.d,), 95, 0, synth.T_QIDX)
+    run_case("i.i.d. keys", w, 40000, q, kidx)
+
+
+def test_fused_expands_clustered_workgroups():
+    w = workload()
+    kidx = synth.make_kidx(w)[0]
+    q = synth.normal((w.d,), 96, 0, synth.T_QIDX)
+    aligned_cells(w, q, 39999, range(3000, 3700), kidx)  # 700 blocks over 4 workgroups
+    s = run_case("contiguous cluster (re-admits 4 workgroups)", w, 40000, q, kidx)
+    assert np.sum(s > np.sort(s[np.isfinite(s)])[-513]) >= 512
+
+
+def test_fused_streams_when_many_workgroups_compete():
+    w = workload()
+    kidx = synth.make_kidx(w)[0]
+    q = synth.normal((w.d,), 97, 0, synth.T_QIDX)
+    blocks = [wg * 256 + 7 * j for wg in range(2, 32) for j in range(20)]  # 20 in 30 workgroups
+    aligned_cells(w, q, 39999, blocks, kidx)
+    run_case("strided cluster (30 workgroups compete: re-stream)", w, 40000, q, kidx)
+
+
+def test_fused_all_tied():
+    w = workload()
+    kidx = np.zeros((w.cap_cells, w.d), np.float32)  # every pooled key is 0: all scores tie
+    q = synth.normal((w.d,), 98, 0, synth.T_QIDX)
+    s = run_case("all scores equal", w, 40000, q, kidx)
+    assert np.all(s[np.isfinite(s)] == 0)
+
+
+def test_fused_fewer_blocks_than_budget():
+    w = workload()
+    kidx = synth.make_kidx(w)[0]
+    q = synth.normal((w.d,), 99, 0, synth.T_QIDX)
+    for n in (1, 3, 5, 1000, 2048, 2049, 8200):
+        run_case(f"n_cells={n}", w, n, q, kidx)

@@ -337,7 +337,7 @@ def test_invalid_queries_are_inert():
     assert np.all(np.isfinite(s[0, :25])) and np.all(np.isneginf(s[0, 25:]))
     assert np.all(np.isneginf(s[1:]))
     n_sel = bufs.n_sel.cpu().numpy()
-    assert n_sel[0] == 25 * 4 and np.all(n_sel[1:] == 0)
+    assert n_sel[0] == 16 * 4 and np.all(n_sel[1:] == 0)  # top_k 64: 16 blocks, no tail
     assert np.all(bufs.sel_cells.cpu().numpy()[1:] == -1)
     assert np.all(bufs.out.cpu().numpy()[1:] == 0.0)
 
@@ -355,7 +355,9 @@ def test_repeat_runs_are_bit_identical():
         bufs = runtime.StepBuffers(layer.dims, n_q, 1000, DEV)
         o = runtime.run_step(layer, bufs, *args, None, 0)
         torch.cuda.synchronize()
-        outs.append([x.cpu().numpy().copy() for x in (o.scores, o.sel_cells, o.n_sel, o.out)])
+        # only columns < nb_max of the score rows are defined
+        outs.append([x.cpu().numpy().copy()
+                     for x in (o.scores[:, :1000], o.sel_cells, o.n_sel, o.out)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 

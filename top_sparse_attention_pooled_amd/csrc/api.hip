@@ -2,6 +2,7 @@
 // host-side validation, workspace sizing and dispatch to the kernels.  No
 // call allocates, frees or synchronises; errors are returned before anything
 // is enqueued, with a message kept per thread.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -68,6 +69,26 @@ int check_seqs(const qsa_dims *d, const qsa_seqs *s) {
 
 qsa::SeqGeom geom(const qsa_seqs *s) { return {s->n_seq, s->cap_cells, s->n_cells_dev}; }
 
+// RoPE inverse frequencies omega_t = theta^(-2t/d) for d = 128, in fp64.
+// With d/2 = 2^6, theta^(-2t/d) = theta^(-t/64) is the product over the set
+// bits k of t of theta^(-1/2^(6-k)), and theta^(1/2^j) is j nested square
+// roots of theta.  Only correctly rounded IEEE operations are used (sqrt,
+// divide, multiply, in ascending k), so every conforming machine gets the
+// same bits; the kernels then form the angles pos * omega_t themselves.
+qsa::RopeTable rope_table(float theta_f) {
+    qsa::RopeTable t;
+    double root[7];
+    root[0] = (double)theta_f;
+    for (int j = 1; j <= 6; ++j) root[j] = sqrt(root[j - 1]);
+    for (int i = 0; i < qsa::kDIdx / 2; ++i) {
+        double w = 1.0;
+        for (int k = 0; k < 6; ++k)
+            if ((i >> k) & 1) w = w * (1.0 / root[6 - k]);
+        t.omega[i] = w;
+    }
+    return t;
+}
+
 int check_queries(const int32_t *q_seq, const int32_t *q_pos, int32_t n_q, bool need_pos) {
     if (n_q < 0) return fail(QSA_EINVAL, "n_q negative");
     if (n_q > 65535) return fail(QSA_ENOTSUP, "n_q above 65535");
@@ -108,6 +129,10 @@ int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q, int32_t nb
             *bytes = qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells);
             break;
         case QSA_OP_SCORE_BF16: *bytes = (size_t)n_q * qsa::kDIdx * sizeof(uint16_t); break;
+        case QSA_OP_SCORE_SELECT:
+            if (nb_max < 0) return fail(QSA_EINVAL, "nb_max negative");
+            *bytes = qsa::fused_select_ws_bytes(n_q, nb_max);
+            break;
         default: return fail(QSA_EINVAL, "unknown op %d", op);
     }
     return ok();
@@ -127,8 +152,9 @@ int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs, const flo
         return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
     if (pooled_bf16_dev && !aligned(pooled_bf16_dev, 16))
         return fail(QSA_EINVAL, "pooled_bf16_dev not 16-byte aligned");
-    qsa::UpdateArgs a{geom(seqs), kidx_dev, dirty_dev, n_dirty, pooled_dev, pooled_bf16_dev,
-                      dims->r, dims->rope_theta, dims->rms_eps, dims->idx_norm_w_dev};
+    qsa::UpdateArgs a{geom(seqs), kidx_dev,     dirty_dev,      n_dirty,
+                      pooled_dev, pooled_bf16_dev, dims->r, dims->rms_eps,
+                      dims->idx_norm_w_dev, rope_table(dims->rope_theta)};
     return launched(qsa::launch_update_pooled(a, (hipStream_t)stream), "update_pooled_keys");
 }
 
@@ -149,8 +175,9 @@ int qsa_score_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_
     if (!q_idx_dev || !aligned(q_idx_dev, 4)) return fail(QSA_EINVAL, "q_idx_dev NULL or misaligned");
     if (!scores_dev || !aligned(scores_dev, 4))
         return fail(QSA_EINVAL, "scores_dev NULL or misaligned");
-    qsa::ScoreArgs a{geom(seqs), q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
-                     pooled_bf16_dev, nb_max, scores_dev, ld_scores, dims->r, dims->rope_theta};
+    qsa::ScoreArgs a{geom(seqs),     q_idx_dev,  q_seq_dev, q_pos_dev, n_q,     pooled_dev,
+                     pooled_bf16_dev, nb_max,     scores_dev, ld_scores, dims->r,
+                     rope_table(dims->rope_theta)};
     if (mode == QSA_SCORE_F32) {
         if (!pooled_dev || !aligned(pooled_dev, 16))
             return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
@@ -192,6 +219,48 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const flo
     qsa::SelectArgs a{geom(seqs), scores_dev, ld_scores, q_seq_dev, q_pos_dev, n_q, nb_max,
                       dims->r, dims->top_k, sel_blocks_dev, sel_cells_dev, n_sel_dev};
     return launched(qsa::launch_select(a, (hipStream_t)stream), "select_topk_blocks");
+}
+
+int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_idx_dev,
+                            const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                            const float *pooled_dev, int32_t nb_max, float *scores_dev,
+                            int64_t ld_scores, int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                            int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (!rc) rc = check_queries(q_seq_dev, q_pos_dev, n_q, true);
+    if (rc) return rc;
+    const int64_t cap_blocks = seqs->cap_cells / dims->r;
+    if (nb_max < 0 || nb_max > cap_blocks)
+        return fail(QSA_EINVAL, "nb_max %d outside 0..cap_cells/r", nb_max);
+    if (ld_scores < nb_max) return fail(QSA_EINVAL, "ld_scores below nb_max");
+    if (n_q == 0) return ok();
+    if (!q_idx_dev || !aligned(q_idx_dev, 4)) return fail(QSA_EINVAL, "q_idx_dev NULL or misaligned");
+    if (!pooled_dev || !aligned(pooled_dev, 16))
+        return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
+    if (!scores_dev || !aligned(scores_dev, 4))
+        return fail(QSA_EINVAL, "scores_dev NULL or misaligned");
+    if (!sel_blocks_dev || !sel_cells_dev || !n_sel_dev || !aligned(sel_blocks_dev, 4) ||
+        !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
+        return fail(QSA_EINVAL, "selection outputs NULL or misaligned");
+    const size_t need = qsa::fused_select_ws_bytes(n_q, nb_max);
+    if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 256))
+        return fail(QSA_EWS, "score/select workspace needs %zu bytes, 256-byte aligned", need);
+    qsa::ScoreArgs a{geom(seqs),     q_idx_dev, q_seq_dev, q_pos_dev, n_q,     pooled_dev,
+                     nullptr,        nb_max,    scores_dev, ld_scores, dims->r,
+                     rope_table(dims->rope_theta)};
+    hipStream_t st = (hipStream_t)stream;
+    if (nb_max > qsa::kFusedMaxBlocks) {
+        // beyond the fused kernel's LDS bitmap: score, then select separately
+        hipError_t e = qsa::launch_score_f32(a, st);
+        if (e != hipSuccess) return launched(e, "score_select_decode(score)");
+        qsa::SelectArgs sa{geom(seqs), scores_dev, ld_scores, q_seq_dev, q_pos_dev, n_q, nb_max,
+                           dims->r,    dims->top_k, sel_blocks_dev, sel_cells_dev, n_sel_dev};
+        return launched(qsa::launch_select(sa, st), "score_select_decode(select)");
+    }
+    return launched(qsa::launch_score_select_f32(a, dims->top_k, sel_blocks_dev, sel_cells_dev,
+                                                 n_sel_dev, ws_dev, st),
+                    "score_select_decode");
 }
 
 static int attn_common(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,

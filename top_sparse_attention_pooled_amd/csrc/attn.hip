@@ -7,7 +7,9 @@
 // Work unit: one workgroup = one (query, KV head, run of cells).  Its 256
 // threads are 8 groups of 32; lane j of a group owns dims 8j .. 8j+7 of the
 // head and all G query heads that share the KV head, so each K/V row is read
-// once from memory and feeds G heads.  Per 64-cell chunk: the groups score
+// once from memory and feeds G heads.  A decode workgroup takes one 32-cell
+// chunk (130 workgroups for a 2051-cell set over 2 KV heads) and issues every
+// index, K and V load before it uses any.  Per chunk: the groups score
 // their cells (G dot products reduced over 32 lanes with a transposing
 // butterfly: 9 shuffles for 8 heads), the chunk's softmax statistics come
 // from one wavefront per head, and the groups accumulate P*V; across chunks
@@ -24,35 +26,55 @@ namespace qsa {
 
 namespace {
 
-constexpr int kChunk = 64;   // cells per chunk (= one wavefront for the softmax)
+constexpr int kChunk = 32;   // cells per chunk; a decode workgroup takes one chunk
 constexpr int kGroups = 8;   // 32-lane groups per workgroup
+constexpr int kCPG = kChunk / kGroups;  // cells per group per chunk
 
-// 8 dequantised values (dims 8j .. 8j+7) of one row.
+// Raw bytes of one lane's slice (dims 8j .. 8j+7) of one K or V row.
 template <int KVT>
-__device__ __forceinline__ void load_row8(const void *base, int64_t row, int j, float (&x)[8]) {
-    if (KVT == QSA_KV_F32) {
-        const float4 *p = reinterpret_cast<const float4 *>(
-            static_cast<const float *>(base) + row * kHeadDim + 8 * j);
-        const float4 u = p[0], v = p[1];
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+struct RawRow;
+template <>
+struct RawRow<QSA_KV_F32> {
+    float4 u, v;
+};
+template <>
+struct RawRow<QSA_KV_Q8_0> {
+    uint32_t w0, w1, w2, sw;
+};
+
+template <int KVT>
+__device__ __forceinline__ RawRow<KVT> load_raw(const void *base, int64_t row, int j) {
+    RawRow<KVT> r;
+    if constexpr (KVT == QSA_KV_F32) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) +
+                                                           row * kHeadDim + 8 * j);
+        r.u = p[0];
+        r.v = p[1];
     } else {
-        const uint8_t *r = static_cast<const uint8_t *>(base) + row * kQ8Row;
+        const uint8_t *b = static_cast<const uint8_t *>(base) + row * kQ8Row;
         const int blk = j >> 2;
         const int start = blk * kQ8Bytes + 2 + 8 * (j & 3);
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(r + (start & ~3));
-        uint32_t lo, hi;
-        if (start & 3) {  // 2 mod 4: three dwords, shift by 2 bytes
-            const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
-            lo = __builtin_amdgcn_alignbyte(w1, w0, 2);
-            hi = __builtin_amdgcn_alignbyte(w2, w1, 2);
-        } else {
-            lo = w[0];
-            hi = w[1];
-        }
-        const int sofs = blk * kQ8Bytes;  // scale: low or high half of a dword
-        const uint32_t sw = *reinterpret_cast<const uint32_t *>(r + (sofs & ~3));
-        const uint16_t sbits = (uint16_t)((sofs & 3) ? (sw >> 16) : (sw & 0xffffu));
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(b + (start & ~3));
+        r.w0 = w[0];
+        r.w1 = w[1];
+        r.w2 = (start & 3) ? w[2] : 0u;  // only rows whose int8 start 2 mod 4 need it
+        r.sw = *reinterpret_cast<const uint32_t *>(b + ((blk * kQ8Bytes) & ~3));
+    }
+    return r;
+}
+
+// Dequantise: q8_0 value = float(binary16 scale) * int8, exact in fp32.
+template <int KVT>
+__device__ __forceinline__ void dequant(const RawRow<KVT> &r, int j, float (&x)[8]) {
+    if constexpr (KVT == QSA_KV_F32) {
+        x[0] = r.u.x; x[1] = r.u.y; x[2] = r.u.z; x[3] = r.u.w;
+        x[4] = r.v.x; x[5] = r.v.y; x[6] = r.v.z; x[7] = r.v.w;
+    } else {
+        const int blk = j >> 2;
+        const bool odd = blk & 1;  // block start 2 mod 4: int8 aligned, scale in high half
+        const uint32_t lo = odd ? r.w0 : __builtin_amdgcn_alignbyte(r.w1, r.w0, 2);
+        const uint32_t hi = odd ? r.w1 : __builtin_amdgcn_alignbyte(r.w2, r.w1, 2);
+        const uint16_t sbits = (uint16_t)(odd ? (r.sw >> 16) : (r.sw & 0xffffu));
         const float d = (float)__builtin_bit_cast(_Float16, sbits);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -63,7 +85,8 @@ __device__ __forceinline__ void load_row8(const void *base, int64_t row, int j, 
 }
 
 // Sum v[0..G) over the 32 lanes of a group.  On return lane j holds the full
-// sum for head head_of_lane<G>(j) in v[0].
+// sum for head head_of_lane<G>(j) in v[0]: each halving step exchanges half
+// of the remaining values, so 8 heads cost 4+2+1+1+1 shuffles, not 8*5.
 template <int G>
 __device__ __forceinline__ void group_reduce(float (&v)[G]) {
     int n = G;
@@ -127,10 +150,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     const int s = a.q_seq[i];
     const bool qvalid = s >= 0 && s < a.g.n_seq;
     int n = qvalid ? a.n_sel[i] : 0;
-    if (n < 0) n = 0;
-    if (n > a.ld_cells) n = a.ld_cells;
-    int64_t n_present = qvalid ? a.g.n_cells[s] : 0;
-    if (n_present > a.g.cap_cells) n_present = a.g.cap_cells;
+    n = n < 0 ? 0 : (n > a.ld_cells ? a.ld_cells : n);
     const int c_begin = run * chunks_per_run * kChunk;
     const int c_end = min(n, c_begin + chunks_per_run * kChunk);
     const int h0 = g * G;
@@ -145,6 +165,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     }
 
     if (c_begin < c_end) {
+        // everything this workgroup reads first is independent: issue it all
+        const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
+        const int64_t row0 = (int64_t)s * a.g.cap_cells;
+        const int64_t n_present_raw = a.g.n_cells[s];
         float qv[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -154,18 +178,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
             qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
             qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
         }
-        const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
-        const int64_t row0 = (int64_t)s * a.g.cap_cells;
+        const int64_t n_present = n_present_raw < a.g.cap_cells ? n_present_raw : a.g.cap_cells;
 
         for (int c0 = c_begin; c0 < c_end; c0 += kChunk) {
             const int c1 = min(c_end, c0 + kChunk);
+            // this group's cells of the chunk: c0 + grp*kCPG + u
+            int cell[kCPG];
+            RawRow<KVT> rk[kCPG], rv[kCPG];
+#pragma unroll
+            for (int u = 0; u < kCPG; ++u) {
+                const int cc = c0 + grp * kCPG + u;
+                cell[u] = cc < c1 ? cells[cc] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kCPG; ++u) {
+                // memory safety needs only 0 <= cell < cap_cells
+                if (cell[u] >= 0 && cell[u] < a.g.cap_cells) {
+                    const int64_t row = (row0 + cell[u]) * a.n_head_kv + g;
+                    rk[u] = load_raw<KVT>(a.k, row, j);
+                    rv[u] = load_raw<KVT>(a.v, row, j);
+                }
+            }
             // scores of this group's cells
-            for (int cc = c0 + grp; c1 > cc; cc += kGroups) {
-                const int cell = cells[cc];
-                const bool ok = cell >= 0 && cell < n_present;
+#pragma unroll
+            for (int u = 0; u < kCPG; ++u) {
+                const int cc = c0 + grp * kCPG + u;
+                const bool ok = cell[u] >= 0 && cell[u] < n_present;
                 float kf[8];
                 if (ok) {
-                    load_row8<KVT>(a.k, (row0 + cell) * a.n_head_kv + g, j, kf);
+                    dequant<KVT>(rk[u], j, kf);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) kf[e] = 0.f;
@@ -179,26 +220,27 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
                     sv[h] = acc;
                 }
                 group_reduce<G>(sv);
-                if (lane_reports<G>(j))
+                if (cc < c1 && lane_reports<G>(j))
                     s_p[head_of_lane<G>(j)][cc - c0] = ok ? sv[0] * a.scale : -INFINITY;
             }
             __syncthreads();
-            // chunk statistics: one wavefront per head, lane = cell
+            // chunk statistics: 32 lanes per head, two heads per wavefront
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                if ((h & 3) != wave) continue;
-                const bool in = c0 + lane < c1;
-                const float x = in ? s_p[h][lane] : -INFINITY;
+                if (((h >> 1) & 3) != wave || ((h & 1) != (lane >> 5))) continue;
+                const int c = lane & 31;
+                const bool in = c0 + c < c1;
+                const float x = in ? s_p[h][c] : -INFINITY;
                 float mx = x;
 #pragma unroll
-                for (int o2 = 32; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
-                const float m_new = fmaxf(m_run[h], mx);  // m_run identical in all threads
+                for (int o2 = 16; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
+                const float m_new = fmaxf(m_run[h], mx);  // m_run equal in every thread
                 const float pe = (in && x != -INFINITY) ? __expf(x - m_new) : 0.f;
                 float sum = pe;
 #pragma unroll
-                for (int o2 = 32; o2 >= 1; o2 >>= 1) sum += __shfl_xor(sum, o2, kWave);
-                s_p[h][lane] = pe;
-                if (lane == 0) {
+                for (int o2 = 16; o2 >= 1; o2 >>= 1) sum += __shfl_xor(sum, o2, kWave);
+                s_p[h][c] = pe;
+                if (c == 0) {
                     s_stat[h][0] = m_new;
                     s_stat[h][1] = sum;
                 }
@@ -214,12 +256,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[h][e] *= corr;
             }
-            for (int cc = c0 + grp; c1 > cc; cc += kGroups) {
-                const int cell = cells[cc];
-                const bool ok = cell >= 0 && cell < n_present;
+#pragma unroll
+            for (int u = 0; u < kCPG; ++u) {
+                const int cc = c0 + grp * kCPG + u;
+                const bool ok = cell[u] >= 0 && cell[u] < n_present && cc < c1;
                 if (!ok) continue;
                 float vf[8];
-                load_row8<KVT>(a.v, (row0 + cell) * a.n_head_kv + g, j, vf);
+                dequant<KVT>(rv[u], j, vf);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const float pw = s_p[h][cc - c0];
@@ -258,29 +301,81 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     }
 }
 
-// grid (n_head, n_q), 256 threads = dims.  Merges the runs' partial states.
+constexpr int kCombNT = 1024;
+constexpr int kCombGroups = kCombNT / 128;  // run groups x 128 dim pairs
+
+// grid (n_head, n_q).  Merges the runs' partial states of one head: thread
+// (rg, dp) sums runs rg, rg+8, ... for dims 2dp, 2dp+1; the 8 partial sums
+// are then added in a fixed order.
 template <int G>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_runs) {
-    const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs) {
+    __shared__ float s_w[1024];
+    __shared__ float s_red[32];
+    __shared__ float2 s_acc[kCombGroups][128];
+    const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
     const int g = h / G, hh = h % G;
-    const float *base = a.ws + ((int64_t)i * a.n_head_kv + g) * n_runs * (G * kHeadDim + 2 * G);
-    float M = -INFINITY;
-    for (int r = 0; r < n_runs; ++r) {
-        const float *part = base + (int64_t)r * (G * kHeadDim + 2 * G);
-        if (part[G * kHeadDim + G + hh] > 0.f) M = fmaxf(M, part[G * kHeadDim + hh]);
+    const int stride = G * kHeadDim + 2 * G;
+    const float *base = a.ws + ((int64_t)i * a.n_head_kv + g) * n_runs * stride;
+    // per-run weights exp(m_r - M), M = max over runs that saw any cell
+    float m = -INFINITY, l = 0.f;
+    if (tid < n_runs) {
+        m = base[(int64_t)tid * stride + G * kHeadDim + hh];
+        l = base[(int64_t)tid * stride + G * kHeadDim + G + hh];
+        if (!(l > 0.f)) m = -INFINITY;
     }
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-        for (int r = 0; r < n_runs; ++r) {
-            const float *part = base + (int64_t)r * (G * kHeadDim + 2 * G);
-            const float l = part[G * kHeadDim + G + hh];
-            if (!(l > 0.f)) continue;
-            const float w = __expf(part[G * kHeadDim + hh] - M);
-            L = fmaf(l, w, L);
-            O = fmaf(part[hh * kHeadDim + t], w, O);
+    float mx = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+    __syncthreads();
+    float M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kCombNT / 64; ++w) M = fmaxf(M, s_red[w]);
+    __syncthreads();
+    const float wgt = (m != -INFINITY) ? __expf(m - M) : 0.f;
+    if (tid < n_runs) s_w[tid] = wgt;
+    float lw = l > 0.f ? l * wgt : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lw += __shfl_xor(lw, o, kWave);
+    if ((tid & 63) == 0) s_red[tid >> 6] = lw;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombNT / 64; ++w) L += s_red[w];
+
+    const int rg = tid >> 7, dp = tid & 127;
+    float2 acc = make_float2(0.f, 0.f);
+    constexpr int U = 8;
+    for (int r0 = rg; r0 < n_runs; r0 += kCombGroups * U) {
+        float2 v[U];
+        float w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u * kCombGroups;
+            w[u] = r < n_runs ? s_w[r] : 0.f;
+            v[u] = (r < n_runs && w[u] != 0.f)
+                       ? *reinterpret_cast<const float2 *>(base + (int64_t)r * stride +
+                                                           hh * kHeadDim + 2 * dp)
+                       : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc.x = fmaf(v[u].x, w[u], acc.x);
+            acc.y = fmaf(v[u].y, w[u], acc.y);
         }
     }
-    a.out[((int64_t)i * a.n_head + h) * kHeadDim + t] = L > 0.f ? O / L : 0.f;
+    s_acc[rg][dp] = acc;
+    __syncthreads();
+    if (rg == 0) {
+        float2 t = s_acc[0][dp];
+#pragma unroll
+        for (int q = 1; q < kCombGroups; ++q) {
+            t.x += s_acc[q][dp].x;
+            t.y += s_acc[q][dp].y;
+        }
+        float2 r = make_float2(L > 0.f ? t.x / L : 0.f, L > 0.f ? t.y / L : 0.f);
+        *reinterpret_cast<float2 *>(a.out + ((int64_t)i * a.n_head + h) * kHeadDim + 2 * dp) = r;
+    }
 }
 
 template <int G, int KVT>
@@ -291,7 +386,8 @@ hipError_t launch_g(const AttnArgs &a, int chunks_per_run, int n_runs, bool dire
                        direct ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head, a.n_q), dim3(256), 0, st, a, n_runs);
+    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head, a.n_q), dim3(kCombNT), 0, st, a,
+                       n_runs);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_update_pooled(UpdateArgs a) {
 
     // RoPE at the block position b*r
     float c, sn;
-    rope_cs((double)a.theta, lane, first, c, sn);
+    rope_cs(a.rope, lane, first, c, sn);
     const float lc = lo * c, hs = hi * sn;
     const float hc = hi * c, ls = lo * sn;
     const float out_lo = lc - hs;

@@ -27,31 +27,22 @@ constexpr int kQ8Row = kHeadDim / 32 * kQ8Bytes;  // 272 bytes
 // Scalar helpers
 // ---------------------------------------------------------------------------
 
-// Inverse frequency theta^(-2t/d) for d = 2^(log2_half+1), in fp64: nested
-// square roots of theta, multiplied over the set bits of t in ascending
-// order.  Only correctly rounded IEEE operations, so the value is the same
-// on every conforming machine.
-__device__ __forceinline__ double inv_freq_f64(double theta, int t, int log2_half) {
-    double root[8];
-    root[0] = theta;
-    // sqrt and '/' stay correctly rounded under hipcc's defaults (no fast
-    // math, fp32/fp64 correctly rounded divide and sqrt); the __*_rn
-    // wrappers may map to native approximations and are not used.
-    for (int j = 1; j <= log2_half; ++j) root[j] = __builtin_sqrt(root[j - 1]);
-    double w = 1.0;
-    for (int k = 0; k < log2_half; ++k)
-        if ((t >> k) & 1) w = w * (1.0 / root[log2_half - k]);
-    return w;
-}
+// RoPE inverse frequencies omega_t = theta^(-2t/d), t < d/2, in fp64.  The
+// table is formed on the host (rope_table() in api.hip) and passed by value
+// in the kernel arguments; see there for how it is evaluated.
+struct RopeTable {
+    double omega[kDIdx / 2];
+};
 
-// cos and sin of pos * omega_t, angle and functions in fp64, rounded once to
-// fp32.
-__device__ __forceinline__ void rope_cs(double theta, int t, int64_t pos, float &c,
+// cos and sin of pos * omega_t: the angle and both functions in fp64, each
+// rounded once to fp32.
+__device__ __forceinline__ void rope_cs(const RopeTable &rt, int t, int64_t pos, float &c,
                                         float &s) {
-    const double w = inv_freq_f64(theta, t, 6);
-    const double phi = (double)pos * w;
-    c = (float)cos(phi);
-    s = (float)sin(phi);
+    const double phi = (double)pos * rt.omega[t];
+    double sd, cd;
+    sincos(phi, &sd, &cd);
+    c = (float)cd;
+    s = (float)sd;
 }
 
 // Order-preserving 32-bit key of a finite fp32 score (-0 maps like +0):
@@ -113,9 +104,9 @@ struct UpdateArgs {
     float *pooled;
     uint16_t *pooled_bf16;
     int32_t r;
-    float theta;
     float eps;
     const float *gamma;
+    RopeTable rope;
 };
 
 struct ScoreArgs {
@@ -130,7 +121,24 @@ struct ScoreArgs {
     float *scores;
     int64_t ld;
     int32_t r;
-    float theta;
+    RopeTable rope;
+};
+
+// Fused decode scoring + selection (score.hip).  Per query, each workgroup of
+// 256 blocks leaves its 16 best keys, the largest key it dropped (0 = none)
+// and its count of finite candidates in the workspace; the last workgroup
+// to arrive selects.
+struct FusedSelectArgs {
+    ScoreArgs s;
+    int32_t top_k;
+    int32_t *sel_blocks;
+    int32_t *sel_cells;
+    int32_t *n_sel;
+    uint32_t *arrive;  // [n_q] arrival counters, zero between launches
+    uint64_t *cand;    // [n_q][n_wg][16]
+    uint64_t *drop;    // [n_q][n_wg]
+    uint32_t *fin;     // [n_q][n_wg]
+    int32_t n_wg;
 };
 
 struct SelectArgs {
@@ -171,6 +179,11 @@ hipError_t launch_update_pooled(const UpdateArgs &a, hipStream_t st);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_score_bf16_ws(const ScoreArgs &a, uint16_t *qr_bf16, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+constexpr int kFusedMaxBlocks = 1 << 17;  // fused score+select handles nb_max up to this
+size_t fused_select_ws_bytes(int n_q, int nb_max);
+hipError_t launch_score_select_f32(const ScoreArgs &s, int32_t top_k, int32_t *sel_blocks,
+                                   int32_t *sel_cells, int32_t *n_sel, void *ws,
+                                   hipStream_t st);
 size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
 size_t attn_prefill_ws_bytes(int n_q, int n_head, int ld_cells);

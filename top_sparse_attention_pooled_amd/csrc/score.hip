@@ -13,7 +13,7 @@
 // Prefill (bf16).  The same contraction for many queries is a dense
 // [queries x 128] x [128 x blocks] product, done on the matrix cores with
 // v_mfma_f32_16x16x32_bf16 from bf16 copies of the roped queries and keys.
-#include "qsa_internal.h"
+#include "topk_engine.h"
 
 namespace qsa {
 
@@ -24,11 +24,11 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 // Roped query element pair (t, t+64) of query i at position p, fp32.
-__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p, float theta,
-                                                float &lo, float &hi) {
+__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p,
+                                                const RopeTable &rt, float &lo, float &hi) {
     const float xl = q[t], xh = q[t + 64];
     float c, s;
-    rope_cs((double)theta, t, p, c, s);
+    rope_cs(rt, t, p, c, s);
     const float lc = xl * c, hs = xh * s;
     const float hc = xh * c, ls = xl * s;
     lo = lc - hs;
@@ -39,41 +39,10 @@ __device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p
 // fp32 decode scoring
 // ---------------------------------------------------------------------------
 
-// grid (ceil(nb_max/256), n_q); 4 wavefronts, one 64-block tile each.
-__global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
-    __shared__ float4 qr4[kQuads];
-    const int i = blockIdx.y;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & (kWave - 1);
-    int s;
-    int64_t p;
-    bool valid;
-    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
-                                    a.g.n_cells, a.r, s, p, valid);
-    const int64_t cap_blocks = a.g.cap_cells / a.r;
-    const int64_t wg_b0 = (int64_t)blockIdx.x * 256;
-    const int64_t b0 = wg_b0 + wave * kTile;
-    const int64_t b = b0 + lane;
-
-    // Issue the key loads first; the query rotation below overlaps them.
-    float4 k[kQuads];
-    if (b0 < nc) {
-        const float4 *src = reinterpret_cast<const float4 *>(
-                                a.pooled + ((int64_t)s * (cap_blocks / kTile) + b0 / kTile) *
-                                               kTileFloats) +
-                            lane;
-#pragma unroll
-        for (int q = 0; q < kQuads; ++q) k[q] = src[q * kTile];
-    }
-    if (wg_b0 < nc && wave == 0) {
-        float lo, hi;
-        rope_query_pair(a.q_idx + (int64_t)i * kDIdx, lane, p, a.theta, lo, hi);
-        float *qr = reinterpret_cast<float *>(qr4);
-        qr[lane] = lo;
-        qr[lane + 64] = hi;
-    }
-    __syncthreads();
-
+// Score of this lane's block b = b0 + lane (wave-uniform tile start b0) for
+// one query, in order T; -inf if b >= nc.  qr4 must hold the roped query.
+__device__ __forceinline__ float tile_score(const float4 (&k)[kQuads], const float4 *qr4,
+                                            int64_t b, int64_t nc) {
     float sc = -INFINITY;
     if (b < nc) {
         // T: level 64 pairs quad q with q+16, level 32 q with q+8, ... level 4
@@ -103,7 +72,249 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
         const float x1 = acc[0].y + acc[0].w;
         sc = x0 + x1;
     }
+    return sc;
+}
+
+// Load the 64-block tile starting at b0 (if any block of it is scored) and
+// rope the query into qr4 (wave 0), then synchronise the workgroup.
+__device__ __forceinline__ void load_tile_and_query(const ScoreArgs &a, int i, int s, int64_t p,
+                                                    int64_t nc, int64_t wg_b0, int64_t b0,
+                                                    float4 (&k)[kQuads], float4 *qr4) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t cap_blocks = a.g.cap_cells / a.r;
+    // issue the key loads first; the query rotation below overlaps them
+    if (b0 < nc) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+                                a.pooled + ((int64_t)s * (cap_blocks / kTile) + b0 / kTile) *
+                                               kTileFloats) +
+                            lane;
+#pragma unroll
+        for (int q = 0; q < kQuads; ++q) k[q] = src[q * kTile];
+    }
+    if (wg_b0 < nc && wave == 0) {
+        float lo, hi;
+        rope_query_pair(a.q_idx + (int64_t)i * kDIdx, lane, p, a.rope, lo, hi);
+        float *qr = reinterpret_cast<float *>(qr4);
+        qr[lane] = lo;
+        qr[lane + 64] = hi;
+    }
+    __syncthreads();
+}
+
+// grid (ceil(nb_max/256), n_q); 4 wavefronts, one 64-block tile each.
+__global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
+    __shared__ float4 qr4[kQuads];
+    const int i = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1);
+    int s;
+    int64_t p;
+    bool valid;
+    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
+                                    a.g.n_cells, a.r, s, p, valid);
+    const int64_t wg_b0 = (int64_t)blockIdx.x * 256;
+    const int64_t b0 = wg_b0 + wave * kTile;
+    const int64_t b = b0 + lane;
+    float4 k[kQuads];
+    load_tile_and_query(a, i, s, p, nc, wg_b0, b0, k, qr4);
+    const float sc = tile_score(k, qr4, b, nc);
     if (b < a.nb_max) a.scores[(int64_t)i * a.ld + b] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// fused fp32 decode scoring + exact block top-k
+// ---------------------------------------------------------------------------
+
+constexpr int kCand = 16;    // keys kept per workgroup of 256 blocks
+constexpr int kSlots = 32;   // register slots per thread at selection: 16 + 16 expansions
+constexpr int kMaxExpand = kSlots - kCand;
+
+// Descending bitonic sort of one 64-bit key per lane across a wavefront.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int kk = 2; kk <= kWave; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            const uint64_t o = shfl_xor64(key, j);
+            const bool take_max = ((lane & j) == 0) == ((lane & kk) == 0);
+            key = take_max ? (o > key ? o : key) : (o < key ? o : key);
+        }
+    }
+    return key;
+}
+
+struct FusedSmem {
+    float4 qr4[kQuads];
+    uint64_t wave_top[4][kCand];
+    uint64_t wave_drop[4];
+    uint32_t wave_fin[4];
+    int last;
+    int n_over;
+    int over[kMaxExpand];
+    TopkSmem<256> tk;
+    uint32_t bitmap[kFusedMaxBlocks / 32];
+};
+
+// grid (n_wg, n_q).  Phase 1 scores 256 blocks and leaves the workgroup's 16
+// best keys, its largest dropped key and its finite count.  The last
+// workgroup of a query then (phase 2) finds the exact top-B: threshold z0
+// over the kept keys; every workgroup whose largest dropped key reaches z0
+// (at most 16, else the scores are re-streamed) has all 256 of its keys added
+// in place of its 16, and the threshold is taken again.  Keys a workgroup
+// dropped without reaching z0 lie below z0 <= the final threshold, so the
+// result equals the top-B of all scores.
+__global__ __launch_bounds__(256) void k_score_select_f32(FusedSelectArgs f) {
+    __shared__ FusedSmem sm;
+    const ScoreArgs &a = f.s;
+    const int i = blockIdx.y;
+    const int wg = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & (kWave - 1);
+    int s;
+    int64_t p;
+    bool valid;
+    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
+                                    a.g.n_cells, a.r, s, p, valid);
+    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
+    const int64_t wg_b0 = (int64_t)wg * 256;
+    const int64_t b0 = wg_b0 + wave * kTile;
+    const int64_t b = b0 + lane;
+    float *srow = a.scores + (int64_t)i * a.ld;
+
+    // ---- phase 1: scores and this workgroup's candidates ----
+    {
+        float4 k[kQuads];
+        load_tile_and_query(a, i, s, p, nc, wg_b0, b0, k, sm.qr4);
+        const float sc = tile_score(k, sm.qr4, b, nc);
+        if (b < a.nb_max) srow[b] = sc;
+        uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
+        const uint32_t fin = (uint32_t)__popcll(__ballot(key != 0));
+        key = wave_sort_desc(key);
+        if (lane < kCand) sm.wave_top[wave][lane] = key;
+        if (lane == kCand) sm.wave_drop[wave] = key;
+        if (lane == 0) sm.wave_fin[wave] = fin;
+        __syncthreads();
+        if (wave == 0) {
+            uint64_t k2 = sm.wave_top[lane >> 4][lane & 15];
+            k2 = wave_sort_desc(k2);
+            const uint64_t d16 = (uint64_t)(uint32_t)__shfl((uint32_t)k2, kCand, kWave) |
+                                 ((uint64_t)(uint32_t)__shfl((uint32_t)(k2 >> 32), kCand, kWave)
+                                  << 32);
+            const int64_t slot = (int64_t)i * f.n_wg + wg;
+            if (lane < kCand) f.cand[slot * kCand + lane] = k2;
+            if (lane == 0) {
+                uint64_t d = d16;
+                for (int w = 0; w < 4; ++w) d = sm.wave_drop[w] > d ? sm.wave_drop[w] : d;
+                f.drop[slot] = d;
+                f.fin[slot] = sm.wave_fin[0] + sm.wave_fin[1] + sm.wave_fin[2] + sm.wave_fin[3];
+            }
+        }
+    }
+    // release this workgroup's results, count arrivals
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sm.last = atomicAdd(&f.arrive[i], 1u) == (uint32_t)(f.n_wg - 1);
+    __syncthreads();
+    if (!sm.last) return;
+    __threadfence();
+
+    // ---- phase 2 (last workgroup of query i): exact selection ----
+    const int B = f.top_k / a.r;
+    const int64_t qbase = (int64_t)i * f.n_wg;
+    uint64_t kk[kSlots];
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+        const int fi = tid + 256 * sl;
+        kk[sl] = (sl < kCand && fi < f.n_wg * kCand) ? f.cand[qbase * kCand + fi] : 0ull;
+    }
+    auto from_regs = [&](auto &&fn) {
+#pragma unroll
+        for (int sl = 0; sl < kSlots; ++sl) fn((uint32_t)(kk[sl] >> 32), (uint32_t)kk[sl]);
+    };
+    const Thresh th0 = topk_threshold<256>(from_regs, (uint32_t)B, sm.tk);
+
+    // workgroups whose largest dropped key would be kept could hide more
+    if (tid == 0) sm.n_over = 0;
+    __syncthreads();
+    for (int w = tid; w < f.n_wg; w += 256) {
+        const uint64_t d = f.drop[qbase + w];
+        if (d != 0 && th0.keep((uint32_t)(d >> 32), (uint32_t)d)) {
+            const int at = atomicAdd(&sm.n_over, 1);
+            if (at < kMaxExpand) sm.over[at] = w;
+        }
+    }
+    __syncthreads();
+    const int n_over = sm.n_over;
+    auto from_memory = [&](auto &&fn) {
+        constexpr int U = 16;
+        for (int64_t base = 0; base < limit; base += 256 * U) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t bb = base + (int64_t)u * 256 + tid;
+                v[u] = bb < limit ? srow[bb] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t bb = base + (int64_t)u * 256 + tid;
+                if (bb < limit) fn(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)bb);
+            }
+        }
+    };
+    Thresh th = th0;
+    const bool stream = n_over > kMaxExpand;
+    if (stream) {
+        th = topk_threshold<256>(from_memory, (uint32_t)B, sm.tk);
+    } else if (n_over > 0) {
+        // replace the kept keys of the expanded workgroups by all 256 of theirs
+#pragma unroll
+        for (int sl = 0; sl < kCand; ++sl) {
+            const int w = (tid + 256 * sl) / kCand;
+            for (int e = 0; e < n_over; ++e)
+                if (sm.over[e] == w) kk[sl] = 0ull;
+        }
+#pragma unroll
+        for (int e = 0; e < kMaxExpand; ++e) {
+            uint64_t key = 0ull;
+            if (e < n_over) {
+                const int64_t bb = (int64_t)sm.over[e] * 256 + tid;
+                if (bb < limit) {
+                    const float sc = srow[bb];
+                    if (finite_f32(sc)) key = block_key(sc, bb);
+                }
+            }
+            kk[kCand + e] = key;
+        }
+        th = topk_threshold<256>(from_regs, (uint32_t)B, sm.tk);
+    }
+
+    // ---- emission: bitmap of kept blocks, ascending ----
+    const int n_words = (int)((limit + 31) / 32);
+    for (int w = tid; w < n_words; w += 256) sm.bitmap[w] = 0;
+    __syncthreads();
+    auto mark = [&](uint32_t k, uint32_t u) {
+        if (th.keep(k, u)) {
+            const uint32_t bb = ~u;
+            atomicOr(&sm.bitmap[bb >> 5], 1u << (bb & 31));
+        }
+    };
+    if (stream)
+        from_memory(mark);
+    else
+        from_regs(mark);
+    __syncthreads();
+    const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
+    const int ld_cells = f.top_k + a.r - 1;
+    const int n_keep =
+        emit_from_bitmap<256>(sm.bitmap, n_words, B, a.r, nc, tail, f.sel_blocks + (int64_t)i * B,
+                              f.sel_cells + (int64_t)i * ld_cells, ld_cells, sm.tk);
+    if (tid == 0) {
+        f.n_sel[i] = n_keep * a.r + tail;
+        f.arrive[i] = 0u;  // ready for the next launch
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -122,7 +333,7 @@ __global__ __launch_bounds__(256) void k_rope_queries_bf16(ScoreArgs a, uint16_t
     uint16_t lo16 = 0, hi16 = 0;
     if (valid) {
         float lo, hi;
-        rope_query_pair(a.q_idx + (int64_t)i * kDIdx, lane, p, a.theta, lo, hi);
+        rope_query_pair(a.q_idx + (int64_t)i * kDIdx, lane, p, a.rope, lo, hi);
         lo16 = bf16_rne(lo);
         hi16 = bf16_rne(hi);
     }
@@ -237,6 +448,35 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs a, const uint16_t 
 }
 
 }  // namespace
+
+size_t fused_select_ws_bytes(int n_q, int nb_max) {
+    const size_t n_wg = (size_t)(nb_max + 255) / 256;
+    // arrival counters first (zero between launches), then per-workgroup data
+    const size_t head = ((size_t)n_q * sizeof(uint32_t) + 255) / 256 * 256;
+    return head + (size_t)n_q * n_wg * (kCand * sizeof(uint64_t) + sizeof(uint64_t) +
+                                        sizeof(uint32_t));
+}
+
+hipError_t launch_score_select_f32(const ScoreArgs &s, int32_t top_k, int32_t *sel_blocks,
+                                   int32_t *sel_cells, int32_t *n_sel, void *ws,
+                                   hipStream_t st) {
+    if (s.n_q <= 0) return hipSuccess;
+    FusedSelectArgs f;
+    f.s = s;
+    f.top_k = top_k;
+    f.sel_blocks = sel_blocks;
+    f.sel_cells = sel_cells;
+    f.n_sel = n_sel;
+    f.n_wg = (s.nb_max + 255) / 256;
+    char *w = static_cast<char *>(ws);
+    const size_t head = ((size_t)s.n_q * sizeof(uint32_t) + 255) / 256 * 256;
+    f.arrive = reinterpret_cast<uint32_t *>(w);
+    f.cand = reinterpret_cast<uint64_t *>(w + head);
+    f.drop = f.cand + (size_t)s.n_q * f.n_wg * kCand;
+    f.fin = reinterpret_cast<uint32_t *>(f.drop + (size_t)s.n_q * f.n_wg);
+    hipLaunchKernelGGL(k_score_select_f32, dim3(f.n_wg, s.n_q), dim3(256), 0, st, f);
+    return hipGetLastError();
+}
 
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t st) {
     if (a.n_q <= 0 || a.nb_max <= 0) return hipSuccess;

@@ -1,0 +1,273 @@
+// topk_engine.h -- exact block-wide top-B selection of blocks by score.
+//
+// Ranking: score descending, ties to the lower block index, -0 == +0.  Each
+// candidate is a pair (k, u): k = order-preserving 32-bit key of its finite
+// score (never 0; 0 marks "no candidate") and u = ~block (so a larger u is a
+// lower block).  The kept set is the B largest pairs (k, u) in lexicographic
+// order, which is unique because blocks are distinct.
+//
+// Phase A selects on k alone: a radix select whose digit window follows the
+// live key range -- each round bins the keys inside [lo, hi] by
+// (k - lo) >> shift, with shift chosen so the range spans 1024..2048 bins, and
+// the bin holding the B-th key becomes the next range.  Offsetting by lo
+// spreads the clustered keys of a top-k over the whole histogram (a fixed
+// digit would put them into a few bins and serialise the LDS atomics).  It
+// stops as soon as the threshold bin is taken whole.  Only if the B-th key
+// value is shared by several blocks (ties) does phase B run the same select
+// on u among the tied blocks.  At most 3 rounds per phase.
+//
+// The element source is a functor for_each(f) that calls f(k, u) for every
+// element the calling thread owns; register-cached and streamed sources use
+// the same code.
+#pragma once
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+constexpr int kBinBits = 11;
+constexpr int kBins = 1 << kBinBits;
+
+template <int NT>
+struct TopkSmem {
+    uint32_t hist[kBins];
+    uint32_t red[NT / 64];
+    uint32_t red2[NT / 64];
+    uint32_t b_lo, b_hi, b_above, b_cnt;
+};
+
+// The kept set: valid (k != 0) and (k > T, or k == T and (!tie or u >= U)).
+struct Thresh {
+    uint32_t T;
+    uint32_t U;
+    bool tie;
+    __device__ __forceinline__ bool keep(uint32_t k, uint32_t u) const {
+        return k != 0 && (k > T || (k == T && (!tie || u >= U)));
+    }
+};
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    if (lane == 0) sm.red[wave] = v;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) t += sm.red[w];
+    __syncthreads();
+    return t;
+}
+
+// Block-wide (min, max) of per-thread values.
+template <int NT>
+__device__ __forceinline__ void block_minmax_u32(uint32_t &mn, uint32_t &mx, TopkSmem<NT> &sm) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor(mn, m, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor(mx, m, kWave));
+    }
+    if (lane == 0) {
+        sm.red[wave] = mn;
+        sm.red2[wave] = mx;
+    }
+    __syncthreads();
+    mn = sm.red[0];
+    mx = sm.red2[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        mn = min(mn, sm.red[w]);
+        mx = max(mx, sm.red2[w]);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t span = hi - lo;
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    return bits > kBinBits ? bits - kBinBits : 0;
+}
+
+// Find the bin holding the krem-th largest value: sets b_lo/b_hi (the bin's
+// value range), b_above (values in higher bins) and b_cnt.
+template <int NT>
+__device__ __forceinline__ void pick_bin(TopkSmem<NT> &sm, uint32_t lo, uint32_t hi, int shift,
+                                         uint32_t krem) {
+    constexpr int PER = kBins / NT;  // consecutive bins per thread
+    const int t = threadIdx.x;
+    uint32_t local = 0;
+    uint32_t h[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        h[q] = sm.hist[t * PER + q];
+        local += h[q];
+    }
+    // suffix sums: values in bins above this thread's bins
+    const int lane = t & (kWave - 1), wave = t >> 6;
+    uint32_t incl = local;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t o = __shfl_down(incl, m, kWave);
+        if (lane + m < kWave) incl += o;
+    }
+    if (lane == 0) sm.red[wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - local;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w)
+        if (w > wave) above += sm.red[w];
+#pragma unroll
+    for (int q = PER - 1; q >= 0; --q) {
+        if (above < krem && above + h[q] >= krem) {
+            const uint32_t blo = lo + ((uint32_t)(t * PER + q) << shift);
+            uint32_t bhi = blo + ((1u << shift) - 1u);
+            if (bhi > hi || bhi < blo) bhi = hi;
+            sm.b_lo = blo;
+            sm.b_hi = bhi;
+            sm.b_above = above;
+            sm.b_cnt = h[q];
+        }
+        above += h[q];
+    }
+    __syncthreads();
+}
+
+// Radix select of the krem-th largest of the values v = VAL(k, u) over the
+// elements with PRED(k, u), starting from their range [lo, hi].  Returns the
+// threshold value; n_above gets the count strictly above it; done tells
+// whether count(v >= threshold) == krem (no tie left at the threshold).
+template <int NT, typename ForEach, typename Pred, typename Val>
+__device__ uint32_t select_u32(ForEach for_each, Pred pred, Val val, uint32_t krem, uint32_t lo,
+                               uint32_t hi, TopkSmem<NT> &sm, uint32_t &n_above, bool &done) {
+    n_above = 0;
+    for (int round = 0; round < 4; ++round) {
+        const int shift = range_shift(lo, hi);
+        for (int j = threadIdx.x; j < kBins; j += NT) sm.hist[j] = 0;
+        __syncthreads();
+        for_each([&](uint32_t k, uint32_t u) {
+            if (!pred(k, u)) return;
+            const uint32_t v = val(k, u);
+            if (v >= lo && v <= hi) atomicAdd(&sm.hist[(v - lo) >> shift], 1u);
+        });
+        __syncthreads();
+        pick_bin<NT>(sm, lo, hi, shift, krem);
+        const uint32_t above = sm.b_above, cnt = sm.b_cnt;
+        lo = sm.b_lo;
+        hi = sm.b_hi;
+        __syncthreads();
+        n_above += above;
+        krem -= above;
+        if (cnt == krem) {
+            done = true;
+            return lo;
+        }
+        if (lo == hi) break;  // a single value shared by more than krem elements
+    }
+    done = false;
+    return lo;
+}
+
+// The exact kept set of the top B (or every valid element if there are at
+// most B).
+template <int NT, typename ForEach>
+__device__ Thresh topk_threshold(ForEach for_each, uint32_t B, TopkSmem<NT> &sm) {
+    Thresh th{0u, 0u, false};
+    uint32_t cnt = 0, mn = ~0u, mx = 0u;
+    for_each([&](uint32_t k, uint32_t) {
+        if (!k) return;
+        ++cnt;
+        mn = min(mn, k);
+        mx = max(mx, k);
+    });
+    const uint32_t n_valid = block_sum_u32<NT>(cnt, sm);
+    if (n_valid <= B) return th;  // T = 0: every valid element
+    block_minmax_u32<NT>(mn, mx, sm);
+    uint32_t n_above;
+    bool done;
+    th.T = select_u32<NT>(
+        for_each, [](uint32_t k, uint32_t) { return k != 0; },
+        [](uint32_t k, uint32_t) { return k; }, B, mn, mx, sm, n_above, done);
+    if (done) return th;
+    // ties at score key T: keep the lowest blocks (largest u) among them
+    const uint32_t T = th.T;
+    uint32_t umn = ~0u, umx = 0u;
+    for_each([&](uint32_t k, uint32_t u) {
+        if (k != T) return;
+        umn = min(umn, u);
+        umx = max(umx, u);
+    });
+    block_minmax_u32<NT>(umn, umx, sm);
+    th.U = select_u32<NT>(
+        for_each, [T](uint32_t k, uint32_t) { return k == T; },
+        [](uint32_t, uint32_t u) { return u; }, B - n_above, umn, umx, sm, n_above, done);
+    th.tie = true;
+    return th;
+}
+
+// Ascending emission of the kept blocks from an LDS bitmap over
+// [0, n_words*32): each thread owns a run of words, counts, scans, emits.
+// Writes sel_blocks[0..B) (-1 padded) and sel_cells[0..ld_cells) (each kept
+// block's r cells, then the tail cells, -1 padded); returns the number of
+// kept blocks (block-uniform).
+template <int NT>
+__device__ int emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, int64_t nc,
+                                int tail, int32_t *sel_blocks, int32_t *sel_cells, int ld_cells,
+                                TopkSmem<NT> &sm) {
+    const int per = (n_words + NT - 1) / NT;
+    const int w0 = threadIdx.x * per;
+    uint32_t local = 0;
+    for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(bm[w]);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    uint32_t incl = local;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t o = __shfl_up(incl, m, kWave);
+        if (lane >= m) incl += o;
+    }
+    if (lane == kWave - 1) sm.red[wave] = incl;
+    __syncthreads();
+    uint32_t pos = incl - local;
+    uint32_t total = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        if (w < wave) pos += sm.red[w];
+        total += sm.red[w];
+    }
+    for (int w = w0; w < w0 + per && w < n_words; ++w) {
+        uint32_t bits = bm[w];
+        while (bits) {
+            const int bit = __builtin_ctz(bits);
+            bits &= bits - 1;
+            const int32_t b = w * 32 + bit;
+            if ((int)pos < B) {
+                sel_blocks[pos] = b;
+                for (int c = 0; c < r; ++c) sel_cells[pos * r + c] = b * r + c;
+            }
+            ++pos;
+        }
+    }
+    const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+    for (int j = n_keep + threadIdx.x; j < B; j += NT) sel_blocks[j] = -1;
+    const int n_full = n_keep * r;
+    for (int j = n_full + threadIdx.x; j < ld_cells; j += NT)
+        sel_cells[j] = (j < n_full + tail) ? (int32_t)(nc * r + (j - n_full)) : -1;
+    __syncthreads();
+    return n_keep;
+}
+
+// 64-bit sortable key of a candidate: (score key, ~block); 0 = none.
+__device__ __forceinline__ uint64_t block_key(float s, int64_t b) {
+    return ((uint64_t)score_key(s) << 32) | (uint64_t)(~(uint32_t)b);
+}
+
+__device__ __forceinline__ int32_t key_block(uint64_t key) { return (int32_t)(~(uint32_t)key); }
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace qsa

@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(HERE, "libqsa.so")
 QSA_OK, QSA_EINVAL, QSA_ENOTSUP, QSA_EWS, QSA_EHIP = 0, -1, -2, -3, -4
 KV_F32, KV_Q8_0 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
-OP_SELECT, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_SCORE_BF16 = 0, 1, 2, 3
+OP_SELECT, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_SCORE_BF16, OP_SCORE_SELECT = 0, 1, 2, 3, 4
 TILE = 64
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_update_pooled_keys", "qsa_score_blocks", "qsa_select_topk_blocks",
-           "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
+           "qsa_score_select_decode", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
 
 
 class QsaError(RuntimeError):
@@ -76,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_score_blocks.argtypes = [D, S, vp, vp, vp, i32, vp, vp, i32, vp, i64, i32, vp, sz, vp]
     lib.qsa_select_topk_blocks.restype = ctypes.c_int
     lib.qsa_select_topk_blocks.argtypes = [D, S, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.qsa_score_select_decode.restype = ctypes.c_int
+    lib.qsa_score_select_decode.argtypes = [D, S, vp, vp, vp, i32, vp, i32, vp, i64, vp, vp, vp,
+                                            vp, sz, vp]
     for name in ("qsa_sparse_attn_decode", "qsa_sparse_attn_prefill"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -175,6 +178,16 @@ def select_topk_blocks(dims: Dims, seqs: Seqs, scores, ld_scores: int, q_seq, q_
                                       _ptr(scores), ld_scores, _ptr(q_seq), _ptr(q_pos), n_q,
                                       nb_max, _ptr(sel_blocks), _ptr(sel_cells), _ptr(n_sel),
                                       _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def score_select_decode(dims: Dims, seqs: Seqs, q_idx, q_seq, q_pos, n_q: int, pooled,
+                        nb_max: int, scores, ld_scores: int, sel_blocks, sel_cells, n_sel, ws,
+                        ws_bytes: int, stream=None) -> None:
+    _rc(load().qsa_score_select_decode(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                       _ptr(q_idx), _ptr(q_seq), _ptr(q_pos), n_q, _ptr(pooled),
+                                       nb_max, _ptr(scores), ld_scores, _ptr(sel_blocks),
+                                       _ptr(sel_cells), _ptr(n_sel), _ptr(ws), ws_bytes,
+                                       _stream(stream)))
 
 
 def sparse_attn_decode(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_cache, sel_cells,
