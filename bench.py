@@ -112,29 +112,38 @@ def main():
 
     stream = torch.cuda.Stream()
 
-    def enqueue(t, only_score=False):
+    def enqueue(t, ev=None, only_score=False):
+        """One decode token through every layer: update + scores + candidates,
+        selection, attention (+ combine).  ev: per-layer (start, end) events
+        around the scoring kernel."""
         for li, layer in enumerate(layers):
             layer.n_cells = n_cells[t]
-            bf = bufs[li]
+            bf, d, sq = bufs[li], layer.dims, layer.seqs()
+            if ev is not None:
+                ev[li][0].record(stream)
+            qsa.decode_score_candidates(d, sq, layer.kidx, dirty[t], n_dirty, layer.pooled,
+                                        layer.pooled_bf16, q_idx[t], q_seq[t], q_pos[t], n_q,
+                                        nb_max, bf.scores, bf.ld, bf.ws_fused, bf.ws_fused_bytes)
+            if ev is not None:
+                ev[li][1].record(stream)
             if only_score:
-                qsa.score_blocks(layer.dims, layer.seqs(), q_idx[t], q_seq[t], q_pos[t], n_q,
-                                 layer.pooled, layer.pooled_bf16, nb_max, bf.scores, bf.ld)
-            else:
-                runtime.run_step(layer, bf, q_idx[t], q[t], q_seq[t], q_pos[t], dirty[t],
-                                 n_dirty)
+                continue
+            qsa.decode_select_candidates(d, sq, q_seq[t], q_pos[t], n_q, nb_max, bf.scores,
+                                         bf.ld, bf.sel_blocks, bf.sel_cells, bf.n_sel,
+                                         bf.ws_fused, bf.ws_fused_bytes)
+            qsa.sparse_attn_decode(d, sq, q[t], q_seq[t], n_q, layer.k, layer.v, bf.sel_cells,
+                                   bf.n_sel, bf.out, bf.ws_attn, bf.ws_attn_bytes)
 
-    def capture(steps, only_score=False):
+    def capture(steps, events=None, only_score=False):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for t in steps:
-                enqueue(t, only_score)
+            for n_t, t in enumerate(steps):
+                enqueue(t, None if events is None else events[n_t], only_score)
         return g
 
     g_warm = capture(range(W)) if W > 0 else None
     g_main = capture(range(W, T))
-    g_score = capture(range(W, T), only_score=True)
     torch.cuda.synchronize()
-
     if g_warm is not None:
         g_warm.replay()
     torch.cuda.synchronize()
@@ -143,17 +152,35 @@ def main():
     torch.cuda.synchronize()
     t_main = time.perf_counter() - t_start
 
-    # live timing of the dominant kernel on its own stream: K*L score launches
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    g_score.replay()  # untimed first replay
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
+    # live timing of the dominant kernel (scoring stream) with HIP events:
+    # event record nodes around every scoring launch of a second replay of
+    # the same K steps
+    score_us, timing = None, "graph event nodes around each scoring launch"
+    try:
+        evs = [[(torch.cuda.Event(enable_timing=True, external=True),
+                 torch.cuda.Event(enable_timing=True, external=True)) for _ in range(L)]
+               for _ in range(K)]
+        g_ev = capture(range(W, T), events=evs)
+        g_ev.replay()
+        torch.cuda.synchronize()
+        durs = [a.elapsed_time(b) for row in evs for (a, b) in row]
+        if min(durs) > 0:
+            score_us = float(np.mean(durs)) * 1000.0
+    except Exception as e:  # runtime without graph event nodes
+        print(f"# graph event timing unavailable: {e}", file=sys.stderr)
+    if score_us is None:
+        timing = "events around a graph of the K*L scoring launches alone"
+        g_score = capture(range(W, T), only_score=True)
         g_score.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    score_us = ev0.elapsed_time(ev1) * 1000.0 / (K * L)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            g_score.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        score_us = ev0.elapsed_time(ev1) * 1000.0 / (K * L)
 
     # correctness guard on the last step of layer 0 (selection sizes)
     n_sel = bufs[0].n_sel.cpu().numpy()
@@ -188,7 +215,8 @@ def main():
         "tokens_per_s_per_layer": round(1e6 / us_per_token_layer, 1),
         "step_hbm_gbps": round(step_bytes / (us_per_token_layer * 1e-6) / 1e9, 1),
         "roofline": {
-            "kernel": "k_score_f32",
+            "kernel": "k_score_cand",
+            "timing": timing,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -216,23 +216,45 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
                            int32_t *sel_cells_dev, int32_t *n_sel_dev, void *ws_dev,
                            size_t ws_bytes, void *stream);
 
-/* 2+3 fused, for decode.  Exactly qsa_score_blocks (mode QSA_SCORE_F32)
- * followed by qsa_select_topk_blocks -- the same scores (written to
- * scores_dev) and the same selection, bit for bit -- in one launch: every
- * workgroup scores 256 blocks and keeps its 16 best keys, and the last
- * workgroup of each query selects from those, re-admitting all keys of any
- * workgroup whose dropped keys could compete.
- *
+/* 1+2+3 for decode: the pooled-key update of the dirty list (n_dirty may be
+ * 0), then exactly qsa_score_blocks (mode QSA_SCORE_F32) and
+ * qsa_select_topk_blocks -- the same pooled keys, the same scores (written
+ * to scores_dev) and the same selection, bit for bit -- in two launches,
+ * also available as two calls:
+ *   qsa_decode_score_candidates writes the dirty blocks and scores every
+ *     block (a workgroup that holds a dirty block recomputes it in registers
+ *     rather than reading it), keeping in the workspace the 16 best keys of
+ *     each 256 blocks and the largest key each dropped;
+ *   qsa_decode_select_candidates selects from those, re-admitting all keys
+ *     of any 256 blocks whose dropped keys could compete (or re-reading the
+ *     score row if more than 16 could), so the selection is exact.
  * Workspace: qsa_workspace_size(QSA_OP_SCORE_SELECT, n_q, nb_max) bytes,
- * 256-byte aligned.  Its first n_q 32-bit words are arrival counters that
- * must be zero before the first call (allocate it zero-filled); every call
- * leaves them zero.  Calls that share a workspace must not overlap. */
-int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs,
-                            const float *q_idx_dev, const int32_t *q_seq_dev,
-                            const int32_t *q_pos_dev, int32_t n_q, const float *pooled_dev,
+ * 16-byte aligned, no initial contents required; the two calls must get the
+ * same workspace, scores and geometry, and calls that share a workspace must
+ * not overlap.  The split calls need nb_max <= 131072 (else QSA_ENOTSUP);
+ * qsa_score_select_decode then falls back to the three general calls. */
+int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+                            const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
+                            uint16_t *pooled_bf16_dev, const float *q_idx_dev,
+                            const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
                             int32_t nb_max, float *scores_dev, int64_t ld_scores,
                             int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
                             int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream);
+
+int qsa_decode_score_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
+                                const float *kidx_dev, const int32_t *dirty_dev,
+                                int32_t n_dirty, float *pooled_dev, uint16_t *pooled_bf16_dev,
+                                const float *q_idx_dev, const int32_t *q_seq_dev,
+                                const int32_t *q_pos_dev, int32_t n_q, int32_t nb_max,
+                                float *scores_dev, int64_t ld_scores, void *ws_dev,
+                                size_t ws_bytes, void *stream);
+
+int qsa_decode_select_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
+                                 const int32_t *q_seq_dev, const int32_t *q_pos_dev,
+                                 int32_t n_q, int32_t nb_max, const float *scores_dev,
+                                 int64_t ld_scores, int32_t *sel_blocks_dev,
+                                 int32_t *sel_cells_dev, int32_t *n_sel_dev,
+                                 const void *ws_dev, size_t ws_bytes, void *stream);
 
 /* 4. Sparse attention  [ISSUE lever1: attention runs over the top-k set
  * only; DISC: q8_0 rows are dequantised inside the gather, never the whole

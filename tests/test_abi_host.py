@@ -40,8 +40,8 @@ def test_workspace_sizes():
     assert qsa.workspace_size(d, qsa.OP_SCORE_BF16, 512) == 512 * 128 * 2
     runs = -(-d.ld_cells // 32)  # 32-cell runs
     assert qsa.workspace_size(d, qsa.OP_ATTN_DECODE, 5) == 5 * runs * 16 * 258 * 4
-    n_wg = -(-62070 // 256)  # fused score+select: counters, then 16 keys + drop + count
-    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 256 + 5 * n_wg * (16 * 8 + 12)
+    n_wg = -(-62070 // 256)  # decode score+select: 16 kept keys + the largest dropped
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 5 * n_wg * 17 * 8
     with pytest.raises(qsa.QsaError) as e:
         qsa.workspace_size(d, 99, 1)
     assert e.value.code == qsa.QSA_EINVAL

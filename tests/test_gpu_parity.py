@@ -253,8 +253,8 @@ def test_attention_matches_oracle_on_shared_cells(kv_type, H, Hk):
 # whole steps on the benchmark workloads
 # --------------------------------------------------------------------------
 
-def _run_workload(name, steps, check_every=1):
-    w = synth.WORKLOADS[name]
+def _run_workload(name, steps, check_every=1, w=None):
+    w = synth.WORKLOADS[name] if w is None else w
     say(f"end-to-end {name}: generating inputs")
     kidx = synth.make_kidx(w)
     k = synth.make_kv(w, synth.T_K)
@@ -312,6 +312,13 @@ def test_end_to_end_decode250k():
 
 def test_end_to_end_decode5x250k():
     _run_workload("decode5x250k", 1)
+
+
+def test_end_to_end_multi_token_decode():
+    """Three new tokens per sequence per step (a short verify batch), two
+    sequences: several queries share each dirty block."""
+    w = synth.Workload("multi", 91, 2, 20001, n_new=3, steps=6)
+    _run_workload("multi", 6, w=w)
 
 
 # --------------------------------------------------------------------------

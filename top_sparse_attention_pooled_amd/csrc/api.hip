@@ -221,11 +221,15 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const flo
     return launched(qsa::launch_select(a, (hipStream_t)stream), "select_topk_blocks");
 }
 
-int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_idx_dev,
-                            const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
-                            const float *pooled_dev, int32_t nb_max, float *scores_dev,
-                            int64_t ld_scores, int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
-                            int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream) {
+// Shared validation of the decode indexer calls; fills *f.
+static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+                           const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
+                           uint16_t *pooled_bf16_dev, const float *q_idx_dev,
+                           const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                           int32_t nb_max, float *scores_dev, int64_t ld_scores,
+                           int32_t *sel_blocks_dev, int32_t *sel_cells_dev, int32_t *n_sel_dev,
+                           void *ws_dev, size_t ws_bytes, bool need_scoring, bool need_select,
+                           qsa::DecodeIdxArgs *f) {
     int rc = check_dims(dims);
     if (!rc) rc = check_seqs(dims, seqs);
     if (!rc) rc = check_queries(q_seq_dev, q_pos_dev, n_q, true);
@@ -233,34 +237,113 @@ int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const fl
     const int64_t cap_blocks = seqs->cap_cells / dims->r;
     if (nb_max < 0 || nb_max > cap_blocks)
         return fail(QSA_EINVAL, "nb_max %d outside 0..cap_cells/r", nb_max);
+    if (nb_max > qsa::kFusedMaxBlocks)
+        return fail(QSA_ENOTSUP, "nb_max %d above %d: use the separate calls", nb_max,
+                    qsa::kFusedMaxBlocks);
     if (ld_scores < nb_max) return fail(QSA_EINVAL, "ld_scores below nb_max");
-    if (n_q == 0) return ok();
-    if (!q_idx_dev || !aligned(q_idx_dev, 4)) return fail(QSA_EINVAL, "q_idx_dev NULL or misaligned");
-    if (!pooled_dev || !aligned(pooled_dev, 16))
-        return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
-    if (!scores_dev || !aligned(scores_dev, 4))
+    if (n_q > 0 && (!scores_dev || !aligned(scores_dev, 4)))
         return fail(QSA_EINVAL, "scores_dev NULL or misaligned");
-    if (!sel_blocks_dev || !sel_cells_dev || !n_sel_dev || !aligned(sel_blocks_dev, 4) ||
-        !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
+    if (need_scoring) {
+        if (n_dirty < 0) return fail(QSA_EINVAL, "n_dirty negative");
+        if (n_dirty > 0 &&
+            (!kidx_dev || !dirty_dev || !aligned(kidx_dev, 4) || !aligned(dirty_dev, 4)))
+            return fail(QSA_EINVAL, "kidx_dev/dirty_dev NULL or misaligned");
+        if (pooled_bf16_dev && !aligned(pooled_bf16_dev, 16))
+            return fail(QSA_EINVAL, "pooled_bf16_dev not 16-byte aligned");
+        if (!pooled_dev || !aligned(pooled_dev, 16))
+            return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
+        if (n_q > 0 && (!q_idx_dev || !aligned(q_idx_dev, 4)))
+            return fail(QSA_EINVAL, "q_idx_dev NULL or misaligned");
+    }
+    if (need_select && n_q > 0 &&
+        (!sel_blocks_dev || !sel_cells_dev || !n_sel_dev || !aligned(sel_blocks_dev, 4) ||
+         !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4)))
         return fail(QSA_EINVAL, "selection outputs NULL or misaligned");
     const size_t need = qsa::fused_select_ws_bytes(n_q, nb_max);
-    if (!ws_dev || ws_bytes < need || !aligned(ws_dev, 256))
-        return fail(QSA_EWS, "score/select workspace needs %zu bytes, 256-byte aligned", need);
-    qsa::ScoreArgs a{geom(seqs),     q_idx_dev, q_seq_dev, q_pos_dev, n_q,     pooled_dev,
-                     nullptr,        nb_max,    scores_dev, ld_scores, dims->r,
-                     rope_table(dims->rope_theta)};
-    hipStream_t st = (hipStream_t)stream;
-    if (nb_max > qsa::kFusedMaxBlocks) {
-        // beyond the fused kernel's LDS bitmap: score, then select separately
-        hipError_t e = qsa::launch_score_f32(a, st);
-        if (e != hipSuccess) return launched(e, "score_select_decode(score)");
-        qsa::SelectArgs sa{geom(seqs), scores_dev, ld_scores, q_seq_dev, q_pos_dev, n_q, nb_max,
-                           dims->r,    dims->top_k, sel_blocks_dev, sel_cells_dev, n_sel_dev};
-        return launched(qsa::launch_select(sa, st), "score_select_decode(select)");
+    if (need && (!ws_dev || ws_bytes < need || !aligned(ws_dev, 16)))
+        return fail(QSA_EWS, "decode indexer workspace needs %zu bytes, 16-byte aligned", need);
+    *f = qsa::DecodeIdxArgs{};
+    f->s = qsa::ScoreArgs{geom(seqs),      q_idx_dev, q_seq_dev,  q_pos_dev, n_q,     pooled_dev,
+                          pooled_bf16_dev, nb_max,    scores_dev, ld_scores, dims->r,
+                          rope_table(dims->rope_theta)};
+    f->pooled_w = pooled_dev;
+    f->pooled_bf16 = pooled_bf16_dev;
+    f->kidx = kidx_dev;
+    f->dirty = dirty_dev;
+    f->n_dirty = need_scoring ? n_dirty : 0;
+    f->eps = dims->rms_eps;
+    f->gamma = dims->idx_norm_w_dev;
+    f->top_k = dims->top_k;
+    f->sel_blocks = sel_blocks_dev;
+    f->sel_cells = sel_cells_dev;
+    f->n_sel = n_sel_dev;
+    return QSA_OK;
+}
+
+int qsa_decode_score_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
+                                const float *kidx_dev, const int32_t *dirty_dev, int32_t n_dirty,
+                                float *pooled_dev, uint16_t *pooled_bf16_dev,
+                                const float *q_idx_dev, const int32_t *q_seq_dev,
+                                const int32_t *q_pos_dev, int32_t n_q, int32_t nb_max,
+                                float *scores_dev, int64_t ld_scores, void *ws_dev,
+                                size_t ws_bytes, void *stream) {
+    qsa::DecodeIdxArgs f;
+    const int rc = decode_idx_args(dims, seqs, kidx_dev, dirty_dev, n_dirty, pooled_dev,
+                                   pooled_bf16_dev, q_idx_dev, q_seq_dev, q_pos_dev, n_q, nb_max,
+                                   scores_dev, ld_scores, nullptr, nullptr, nullptr, ws_dev,
+                                   ws_bytes, true, false, &f);
+    if (rc) return rc;
+    return launched(qsa::launch_decode_candidates(f, ws_dev, (hipStream_t)stream),
+                    "decode_score_candidates");
+}
+
+int qsa_decode_select_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
+                                 const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                                 int32_t nb_max, const float *scores_dev, int64_t ld_scores,
+                                 int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                                 int32_t *n_sel_dev, const void *ws_dev, size_t ws_bytes,
+                                 void *stream) {
+    qsa::DecodeIdxArgs f;
+    const int rc = decode_idx_args(dims, seqs, nullptr, nullptr, 0, nullptr, nullptr, nullptr,
+                                   q_seq_dev, q_pos_dev, n_q, nb_max, (float *)scores_dev,
+                                   ld_scores, sel_blocks_dev, sel_cells_dev, n_sel_dev,
+                                   (void *)ws_dev, ws_bytes, false, true, &f);
+    if (rc) return rc;
+    return launched(qsa::launch_decode_select(f, (void *)ws_dev, (hipStream_t)stream),
+                    "decode_select_candidates");
+}
+
+int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+                            const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
+                            uint16_t *pooled_bf16_dev, const float *q_idx_dev,
+                            const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                            int32_t nb_max, float *scores_dev, int64_t ld_scores,
+                            int32_t *sel_blocks_dev, int32_t *sel_cells_dev, int32_t *n_sel_dev,
+                            void *ws_dev, size_t ws_bytes, void *stream) {
+    if (dims && seqs && dims->r >= 1 && nb_max > qsa::kFusedMaxBlocks &&
+        nb_max <= seqs->cap_cells / dims->r) {
+        // beyond the selection kernel's LDS bitmap: the three general calls
+        int rc = qsa_update_pooled_keys(dims, seqs, kidx_dev, dirty_dev, n_dirty, pooled_dev,
+                                        pooled_bf16_dev, stream);
+        if (!rc)
+            rc = qsa_score_blocks(dims, seqs, q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
+                                  pooled_bf16_dev, nb_max, scores_dev, ld_scores, QSA_SCORE_F32,
+                                  nullptr, 0, stream);
+        if (!rc)
+            rc = qsa_select_topk_blocks(dims, seqs, scores_dev, ld_scores, q_seq_dev, q_pos_dev,
+                                        n_q, nb_max, sel_blocks_dev, sel_cells_dev, n_sel_dev,
+                                        nullptr, 0, stream);
+        return rc;
     }
-    return launched(qsa::launch_score_select_f32(a, dims->top_k, sel_blocks_dev, sel_cells_dev,
-                                                 n_sel_dev, ws_dev, st),
-                    "score_select_decode");
+    qsa::DecodeIdxArgs f;
+    const int rc = decode_idx_args(dims, seqs, kidx_dev, dirty_dev, n_dirty, pooled_dev,
+                                   pooled_bf16_dev, q_idx_dev, q_seq_dev, q_pos_dev, n_q, nb_max,
+                                   scores_dev, ld_scores, sel_blocks_dev, sel_cells_dev,
+                                   n_sel_dev, ws_dev, ws_bytes, true, true, &f);
+    if (rc) return rc;
+    hipError_t e = qsa::launch_decode_candidates(f, ws_dev, (hipStream_t)stream);
+    if (e == hipSuccess) e = qsa::launch_decode_select(f, ws_dev, (hipStream_t)stream);
+    return launched(e, "score_select_decode");
 }
 
 static int attn_common(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,

@@ -147,13 +147,31 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     const int run = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
     const int tid = threadIdx.x, grp = tid >> 5, j = tid & 31, wave = tid >> 6,
               lane = tid & 63;
-    const int s = a.q_seq[i];
-    const bool qvalid = s >= 0 && s < a.g.n_seq;
-    int n = qvalid ? a.n_sel[i] : 0;
-    n = n < 0 ? 0 : (n > a.ld_cells ? a.ld_cells : n);
-    const int c_begin = run * chunks_per_run * kChunk;
-    const int c_end = min(n, c_begin + chunks_per_run * kChunk);
     const int h0 = g * G;
+    const int c_begin = run * chunks_per_run * kChunk;
+    const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
+
+    // first round trip: nothing here depends on another load
+    const int s = a.q_seq[i];
+    const int n_raw = a.n_sel[i];
+    int cell[kCPG];
+#pragma unroll
+    for (int u = 0; u < kCPG; ++u) {
+        const int cc = c_begin + grp * kCPG + u;
+        cell[u] = cc < a.ld_cells ? cells[cc] : -1;
+    }
+    float qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float4 *qp = reinterpret_cast<const float4 *>(
+            a.q + ((int64_t)i * a.n_head + h0 + h) * kHeadDim + 8 * j);
+        const float4 u = qp[0], v = qp[1];
+        qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
+        qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
+    }
+    const bool qvalid = s >= 0 && s < a.g.n_seq;
+    const int n = qvalid ? (n_raw < 0 ? 0 : (n_raw > a.ld_cells ? a.ld_cells : n_raw)) : 0;
+    const int c_end = min(n, c_begin + chunks_per_run * kChunk);
 
     float m_run[G], l_run[G], o[G][8];
 #pragma unroll
@@ -165,45 +183,34 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     }
 
     if (c_begin < c_end) {
-        // everything this workgroup reads first is independent: issue it all
-        const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
         const int64_t row0 = (int64_t)s * a.g.cap_cells;
-        const int64_t n_present_raw = a.g.n_cells[s];
-        float qv[G][8];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float4 *qp = reinterpret_cast<const float4 *>(
-                a.q + ((int64_t)i * a.n_head + h0 + h) * kHeadDim + 8 * j);
-            const float4 u = qp[0], v = qp[1];
-            qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
-            qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
-        }
-        const int64_t n_present = n_present_raw < a.g.cap_cells ? n_present_raw : a.g.cap_cells;
-
         for (int c0 = c_begin; c0 < c_end; c0 += kChunk) {
             const int c1 = min(c_end, c0 + kChunk);
-            // this group's cells of the chunk: c0 + grp*kCPG + u
-            int cell[kCPG];
+            if (c0 != c_begin) {
+#pragma unroll
+                for (int u = 0; u < kCPG; ++u) {
+                    const int cc = c0 + grp * kCPG + u;
+                    cell[u] = cc < a.ld_cells ? cells[cc] : -1;
+                }
+            }
+            // second round trip: K/V rows (memory safety needs only
+            // 0 <= cell < cap_cells) and the present-cell count
             RawRow<KVT> rk[kCPG], rv[kCPG];
 #pragma unroll
             for (int u = 0; u < kCPG; ++u) {
-                const int cc = c0 + grp * kCPG + u;
-                cell[u] = cc < c1 ? cells[cc] : -1;
-            }
-#pragma unroll
-            for (int u = 0; u < kCPG; ++u) {
-                // memory safety needs only 0 <= cell < cap_cells
                 if (cell[u] >= 0 && cell[u] < a.g.cap_cells) {
                     const int64_t row = (row0 + cell[u]) * a.n_head_kv + g;
                     rk[u] = load_raw<KVT>(a.k, row, j);
                     rv[u] = load_raw<KVT>(a.v, row, j);
                 }
             }
+            int64_t n_present = a.g.n_cells[s];
+            n_present = n_present < a.g.cap_cells ? n_present : a.g.cap_cells;
             // scores of this group's cells
 #pragma unroll
             for (int u = 0; u < kCPG; ++u) {
                 const int cc = c0 + grp * kCPG + u;
-                const bool ok = cell[u] >= 0 && cell[u] < n_present;
+                const bool ok = cc < c1 && cell[u] >= 0 && cell[u] < n_present;
                 float kf[8];
                 if (ok) {
                     dequant<KVT>(rk[u], j, kf);
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
 #pragma unroll
             for (int u = 0; u < kCPG; ++u) {
                 const int cc = c0 + grp * kCPG + u;
-                const bool ok = cell[u] >= 0 && cell[u] < n_present && cc < c1;
+                const bool ok = cc < c1 && cell[u] >= 0 && cell[u] < n_present;
                 if (!ok) continue;
                 float vf[8];
                 dequant<KVT>(rv[u], j, vf);

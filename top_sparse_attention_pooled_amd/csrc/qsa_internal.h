@@ -86,6 +86,68 @@ __device__ __forceinline__ int64_t query_blocks(const int32_t *q_seq, const int3
     return (p + 1) / r;
 }
 
+// Pooled key of block b of sequence s, whose first m = min(r, n - b*r) cells
+// are present (n > b*r): mean of the m per-cell keys (left-to-right fp32 sum,
+// one divide), RMS-normed (mean of squares in order T, 1/sqrt(ms + eps)
+// correctly rounded, optional weight gamma), roped at position b*r.  All 64
+// lanes of a wavefront call it together; lane t gets dims t and t + 64 (its
+// split-half RoPE pair).  The first level of T pairs dims (t, t+64) in-lane;
+// the rest is an xor butterfly whose lane-0 value is exactly the
+// stride-halving tree (xor h pairs lane t < h with t + h).
+__device__ __forceinline__ void pooled_key_lane(const float *kidx, int64_t cap_cells, int s,
+                                                int64_t b, int64_t n, int r, float eps,
+                                                const float *gamma, const RopeTable &rt,
+                                                int lane, float &out_lo, float &out_hi) {
+    const int64_t first = b * r;
+    const int m = (int)((n - first) < r ? (n - first) : r);
+    const float *x = kidx + ((int64_t)s * cap_cells + first) * kDIdx;
+    float lo = x[lane];
+    float hi = x[lane + 64];
+    for (int j = 1; j < m; ++j) {
+        lo = lo + x[j * kDIdx + lane];
+        hi = hi + x[j * kDIdx + lane + 64];
+    }
+    const float fm = (float)m;
+    lo = lo / fm;
+    hi = hi / fm;
+    const float plo = lo * lo;
+    const float phi2 = hi * hi;
+    float v = plo + phi2;
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) v = v + __shfl_xor(v, h, kWave);
+    v = __shfl(v, 0, kWave);
+    const float ms = v / (float)kDIdx;
+    const float inv = 1.0f / sqrtf(ms + eps);
+    lo = lo * inv;
+    hi = hi * inv;
+    if (gamma) {
+        lo = lo * gamma[lane];
+        hi = hi * gamma[lane + 64];
+    }
+    float c, sn;
+    rope_cs(rt, lane, first, c, sn);
+    const float lc = lo * c, hs = hi * sn;
+    const float hc = hi * c, ls = lo * sn;
+    out_lo = lc - hs;
+    out_hi = hc + ls;
+}
+
+// Store a pooled key (lane t: dims t, t+64) into the tiled fp32 cache and, if
+// given, the row-major bf16 copy.
+__device__ __forceinline__ void store_pooled_lane(float *pooled, uint16_t *pooled_bf16,
+                                                  int64_t cap_blocks, int s, int64_t b, int lane,
+                                                  float out_lo, float out_hi) {
+    float *tile = pooled + ((int64_t)s * (cap_blocks / kTile) + b / kTile) * kTileFloats;
+    const int col = (int)(b % kTile) * 4;
+    tile[(lane >> 2) * (kTile * 4) + col + (lane & 3)] = out_lo;
+    tile[((lane + 64) >> 2) * (kTile * 4) + col + (lane & 3)] = out_hi;
+    if (pooled_bf16) {
+        uint16_t *row = pooled_bf16 + ((int64_t)s * cap_blocks + b) * kDIdx;
+        row[lane] = bf16_rne(out_lo);
+        row[lane + 64] = bf16_rne(out_hi);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launch interfaces (host side, one per kernel family)
 // ---------------------------------------------------------------------------
@@ -124,20 +186,28 @@ struct ScoreArgs {
     RopeTable rope;
 };
 
-// Fused decode scoring + selection (score.hip).  Per query, each workgroup of
-// 256 blocks leaves its 16 best keys, the largest key it dropped (0 = none)
-// and its count of finite candidates in the workspace; the last workgroup
-// to arrive selects.
-struct FusedSelectArgs {
+// Decode indexer step (score.hip): pooled-key update of the dirty blocks,
+// block scores, and the exact top-k, in two launches.  The first scores every
+// block and leaves, per workgroup of 256 blocks, its 16 best keys and the
+// largest key it dropped; it also writes the dirty blocks (extra workgroups)
+// while any scoring workgroup that holds a dirty block recomputes it in
+// registers, so no ordering between the two is needed.  The second selects
+// from those candidates.
+struct DecodeIdxArgs {
     ScoreArgs s;
+    float *pooled_w;        // same buffer as s.pooled, written by the update part
+    uint16_t *pooled_bf16;  // optional bf16 copy, written by the update part
+    const float *kidx;
+    const int32_t *dirty;
+    int32_t n_dirty;
+    float eps;
+    const float *gamma;
     int32_t top_k;
     int32_t *sel_blocks;
     int32_t *sel_cells;
     int32_t *n_sel;
-    uint32_t *arrive;  // [n_q] arrival counters, zero between launches
-    uint64_t *cand;    // [n_q][n_wg][16]
-    uint64_t *drop;    // [n_q][n_wg]
-    uint32_t *fin;     // [n_q][n_wg]
+    uint64_t *cand;  // [n_q][n_wg][16]
+    uint64_t *drop;  // [n_q][n_wg]
     int32_t n_wg;
 };
 
@@ -181,9 +251,9 @@ hipError_t launch_score_bf16_ws(const ScoreArgs &a, uint16_t *qr_bf16, hipStream
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
 constexpr int kFusedMaxBlocks = 1 << 17;  // fused score+select handles nb_max up to this
 size_t fused_select_ws_bytes(int n_q, int nb_max);
-hipError_t launch_score_select_f32(const ScoreArgs &s, int32_t top_k, int32_t *sel_blocks,
-                                   int32_t *sel_cells, int32_t *n_sel, void *ws,
-                                   hipStream_t st);
+// part 1: update + scores + candidates; part 2: selection from candidates
+hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st);
+hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st);
 size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
 size_t attn_prefill_ws_bytes(int n_q, int n_head, int ld_cells);

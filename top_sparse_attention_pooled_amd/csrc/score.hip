@@ -123,12 +123,15 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fused fp32 decode scoring + exact block top-k
+// decode indexer step: update + scoring + candidates, then exact selection
 // ---------------------------------------------------------------------------
 
-constexpr int kCand = 16;    // keys kept per workgroup of 256 blocks
-constexpr int kSlots = 32;   // register slots per thread at selection: 16 + 16 expansions
-constexpr int kMaxExpand = kSlots - kCand;
+constexpr int kCand = 16;        // keys kept per workgroup of 256 blocks
+constexpr int kSelNT = 1024;     // selection workgroup
+constexpr int kBaseSlots = kFusedMaxBlocks / 256 * kCand / kSelNT;  // 8
+constexpr int kMaxExpand = 16;   // workgroups re-admitted whole
+constexpr int kExpSlots = kMaxExpand * 256 / kSelNT;              // 4
+constexpr int kSlots = kBaseSlots + kExpSlots;
 
 // Descending bitonic sort of one 64-bit key per lane across a wavefront.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
@@ -145,34 +148,34 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
     return key;
 }
 
-struct FusedSmem {
-    float4 qr4[kQuads];
-    uint64_t wave_top[4][kCand];
-    uint64_t wave_drop[4];
-    uint32_t wave_fin[4];
-    int last;
-    int n_over;
-    int over[kMaxExpand];
-    TopkSmem<256> tk;
-    uint32_t bitmap[kFusedMaxBlocks / 32];
-};
-
-// grid (n_wg, n_q).  Phase 1 scores 256 blocks and leaves the workgroup's 16
-// best keys, its largest dropped key and its finite count.  The last
-// workgroup of a query then (phase 2) finds the exact top-B: threshold z0
-// over the kept keys; every workgroup whose largest dropped key reaches z0
-// (at most 16, else the scores are re-streamed) has all 256 of its keys added
-// in place of its 16, and the threshold is taken again.  Keys a workgroup
-// dropped without reaching z0 lie below z0 <= the final threshold, so the
-// result equals the top-B of all scores.
-__global__ __launch_bounds__(256) void k_score_select_f32(FusedSelectArgs f) {
-    __shared__ FusedSmem sm;
+// 1-D grid: n_q * n_wg scoring workgroups, then ceil(n_dirty/4) update
+// workgroups (one wavefront per dirty entry).
+__global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
+    __shared__ float4 qr4[kQuads];
+    __shared__ uint64_t wave_top[4][kCand];
+    __shared__ uint64_t wave_drop[4];
+    __shared__ float4 patch[kQuads];
     const ScoreArgs &a = f.s;
-    const int i = blockIdx.y;
-    const int wg = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & (kWave - 1);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+    const int64_t cap_blocks = a.g.cap_cells / a.r;
+    const int n_score_wg = f.n_wg * a.n_q;
+
+    if ((int)blockIdx.x >= n_score_wg) {  // ---- update role ----
+        const int e = ((int)blockIdx.x - n_score_wg) * 4 + wave;
+        if (e >= f.n_dirty) return;
+        const int s = f.dirty[2 * e], b = f.dirty[2 * e + 1];
+        if (s < 0 || s >= a.g.n_seq || b < 0 || b >= cap_blocks) return;
+        int64_t n = a.g.n_cells[s];
+        if (n > a.g.cap_cells) n = a.g.cap_cells;
+        if ((int64_t)b * a.r >= n) return;
+        float lo, hi;
+        pooled_key_lane(f.kidx, a.g.cap_cells, s, b, n, a.r, f.eps, f.gamma, a.rope, lane, lo, hi);
+        store_pooled_lane(f.pooled_w, f.pooled_bf16, cap_blocks, s, b, lane, lo, hi);
+        return;
+    }
+
+    // ---- scoring role: query i, blocks [wg*256, wg*256 + 256) ----
+    const int i = blockIdx.x / f.n_wg, wg = blockIdx.x % f.n_wg;
     int s;
     int64_t p;
     bool valid;
@@ -182,64 +185,114 @@ __global__ __launch_bounds__(256) void k_score_select_f32(FusedSelectArgs f) {
     const int64_t wg_b0 = (int64_t)wg * 256;
     const int64_t b0 = wg_b0 + wave * kTile;
     const int64_t b = b0 + lane;
-    float *srow = a.scores + (int64_t)i * a.ld;
+    float4 k[kQuads];
+    load_tile_and_query(a, i, s, p, nc, wg_b0, b0, k, qr4);
 
-    // ---- phase 1: scores and this workgroup's candidates ----
-    {
-        float4 k[kQuads];
-        load_tile_and_query(a, i, s, p, nc, wg_b0, b0, k, sm.qr4);
-        const float sc = tile_score(k, sm.qr4, b, nc);
-        if (b < a.nb_max) srow[b] = sc;
-        uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
-        const uint32_t fin = (uint32_t)__popcll(__ballot(key != 0));
-        key = wave_sort_desc(key);
-        if (lane < kCand) sm.wave_top[wave][lane] = key;
-        if (lane == kCand) sm.wave_drop[wave] = key;
-        if (lane == 0) sm.wave_fin[wave] = fin;
-        __syncthreads();
-        if (wave == 0) {
-            uint64_t k2 = sm.wave_top[lane >> 4][lane & 15];
-            k2 = wave_sort_desc(k2);
-            const uint64_t d16 = (uint64_t)(uint32_t)__shfl((uint32_t)k2, kCand, kWave) |
-                                 ((uint64_t)(uint32_t)__shfl((uint32_t)(k2 >> 32), kCand, kWave)
-                                  << 32);
-            const int64_t slot = (int64_t)i * f.n_wg + wg;
-            if (lane < kCand) f.cand[slot * kCand + lane] = k2;
-            if (lane == 0) {
-                uint64_t d = d16;
-                for (int w = 0; w < 4; ++w) d = sm.wave_drop[w] > d ? sm.wave_drop[w] : d;
-                f.drop[slot] = d;
-                f.fin[slot] = sm.wave_fin[0] + sm.wave_fin[1] + sm.wave_fin[2] + sm.wave_fin[3];
+    // a dirty block scored here may not be written yet: recompute it in place
+    if (wg_b0 < nc) {
+        int64_t n = a.g.n_cells[s];
+        if (n > a.g.cap_cells) n = a.g.cap_cells;
+        for (int e = 0; e < f.n_dirty; ++e) {  // workgroup-uniform loop
+            const int ds = f.dirty[2 * e];
+            const int64_t db = f.dirty[2 * e + 1];
+            if (ds != s || db < wg_b0 || db >= wg_b0 + 256 || db >= nc) continue;
+            const int owner_wave = (int)((db - wg_b0) >> 6);
+            if (wave == owner_wave) {
+                float lo, hi;
+                pooled_key_lane(f.kidx, a.g.cap_cells, s, db, n, a.r, f.eps, f.gamma, a.rope,
+                                lane, lo, hi);
+                float *pf = reinterpret_cast<float *>(patch);
+                pf[lane] = lo;
+                pf[lane + 64] = hi;
             }
+            __syncthreads();
+            if (b == db) {
+#pragma unroll
+                for (int q = 0; q < kQuads; ++q) k[q] = patch[q];
+            }
+            __syncthreads();
         }
     }
-    // release this workgroup's results, count arrivals
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sm.last = atomicAdd(&f.arrive[i], 1u) == (uint32_t)(f.n_wg - 1);
-    __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
 
-    // ---- phase 2 (last workgroup of query i): exact selection ----
+    const float sc = tile_score(k, qr4, b, nc);
+    float *srow = a.scores + (int64_t)i * a.ld;
+    if (b < a.nb_max) srow[b] = sc;
+    uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
+    key = wave_sort_desc(key);
+    if (lane < kCand) wave_top[wave][lane] = key;
+    if (lane == kCand) wave_drop[wave] = key;
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t k2 = wave_top[lane >> 4][lane & 15];
+        k2 = wave_sort_desc(k2);
+        const uint64_t d16 = (uint64_t)(uint32_t)__shfl((uint32_t)k2, kCand, kWave) |
+                             ((uint64_t)(uint32_t)__shfl((uint32_t)(k2 >> 32), kCand, kWave)
+                              << 32);
+        const int64_t slot = (int64_t)i * f.n_wg + wg;
+        if (lane < kCand) f.cand[slot * kCand + lane] = k2;
+        if (lane == 0) {
+            uint64_t d = d16;
+            for (int w = 0; w < 4; ++w) d = wave_drop[w] > d ? wave_drop[w] : d;
+            f.drop[slot] = d;
+        }
+    }
+}
+
+struct SelCandSmem {
+    TopkSmem<kSelNT> tk;
+    uint32_t bitmap[kFusedMaxBlocks / 32];
+    int n_over;
+    int over[kMaxExpand];
+};
+
+// grid (n_q), 1024 threads.  Threshold over the kept keys; every workgroup
+// whose largest dropped key would itself be kept is re-admitted with all 256
+// of its keys (or, if more than 16 are, the score row is re-streamed) and the
+// threshold is taken again.  A key a workgroup dropped without qualifying
+// lies below the first threshold, which is <= the final one, so the result
+// is the exact top-B of all scores.
+__global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
+    __shared__ SelCandSmem sm;
+    const ScoreArgs &a = f.s;
+    const int i = blockIdx.x, tid = threadIdx.x;
+    int s;
+    int64_t p;
+    bool valid;
+    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
+                                    a.g.n_cells, a.r, s, p, valid);
+    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
     const int B = f.top_k / a.r;
     const int64_t qbase = (int64_t)i * f.n_wg;
-    uint64_t kk[kSlots];
+    const float *srow = a.scores + (int64_t)i * a.ld;
+
+    RegKeys64<kSlots> from_regs;
+    uint64_t *kk = from_regs.k;
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl) {
-        const int fi = tid + 256 * sl;
-        kk[sl] = (sl < kCand && fi < f.n_wg * kCand) ? f.cand[qbase * kCand + fi] : 0ull;
+        const int fi = tid + kSelNT * sl;
+        kk[sl] = (sl < kBaseSlots && fi < f.n_wg * kCand) ? f.cand[qbase * kCand + fi] : 0ull;
     }
-    auto from_regs = [&](auto &&fn) {
+    auto from_memory = [&](auto &&fn) {
+        constexpr int U = 16;
+        for (int64_t base = 0; base < limit; base += (int64_t)kSelNT * U) {
+            float v[U];
 #pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) fn((uint32_t)(kk[sl] >> 32), (uint32_t)kk[sl]);
+            for (int u = 0; u < U; ++u) {
+                const int64_t bb = base + (int64_t)u * kSelNT + tid;
+                v[u] = bb < limit ? srow[bb] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t bb = base + (int64_t)u * kSelNT + tid;
+                if (bb < limit) fn(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)bb);
+            }
+        }
     };
-    const Thresh th0 = topk_threshold<256>(from_regs, (uint32_t)B, sm.tk);
+    const Thresh th0 = topk_threshold<kSelNT>(from_regs, (uint32_t)B, sm.tk);
 
-    // workgroups whose largest dropped key would be kept could hide more
     if (tid == 0) sm.n_over = 0;
     __syncthreads();
-    for (int w = tid; w < f.n_wg; w += 256) {
+    for (int w = tid; w < f.n_wg; w += kSelNT) {
         const uint64_t d = f.drop[qbase + w];
         if (d != 0 && th0.keep((uint32_t)(d >> 32), (uint32_t)d)) {
             const int at = atomicAdd(&sm.n_over, 1);
@@ -248,52 +301,37 @@ __global__ __launch_bounds__(256) void k_score_select_f32(FusedSelectArgs f) {
     }
     __syncthreads();
     const int n_over = sm.n_over;
-    auto from_memory = [&](auto &&fn) {
-        constexpr int U = 16;
-        for (int64_t base = 0; base < limit; base += 256 * U) {
-            float v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t bb = base + (int64_t)u * 256 + tid;
-                v[u] = bb < limit ? srow[bb] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t bb = base + (int64_t)u * 256 + tid;
-                if (bb < limit) fn(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)bb);
-            }
-        }
-    };
     Thresh th = th0;
     const bool stream = n_over > kMaxExpand;
     if (stream) {
-        th = topk_threshold<256>(from_memory, (uint32_t)B, sm.tk);
+        th = topk_threshold<kSelNT>(from_memory, (uint32_t)B, sm.tk);
     } else if (n_over > 0) {
-        // replace the kept keys of the expanded workgroups by all 256 of theirs
+        // replace the kept keys of the re-admitted workgroups by all of theirs
 #pragma unroll
-        for (int sl = 0; sl < kCand; ++sl) {
-            const int w = (tid + 256 * sl) / kCand;
+        for (int sl = 0; sl < kBaseSlots; ++sl) {
+            const int w = (tid + kSelNT * sl) / kCand;
             for (int e = 0; e < n_over; ++e)
                 if (sm.over[e] == w) kk[sl] = 0ull;
         }
 #pragma unroll
-        for (int e = 0; e < kMaxExpand; ++e) {
+        for (int sl = 0; sl < kExpSlots; ++sl) {
+            const int x = sl * (kSelNT / 256) + (tid >> 8);
             uint64_t key = 0ull;
-            if (e < n_over) {
-                const int64_t bb = (int64_t)sm.over[e] * 256 + tid;
+            if (x < n_over) {
+                const int64_t bb = (int64_t)sm.over[x] * 256 + (tid & 255);
                 if (bb < limit) {
                     const float sc = srow[bb];
                     if (finite_f32(sc)) key = block_key(sc, bb);
                 }
             }
-            kk[kCand + e] = key;
+            kk[kBaseSlots + sl] = key;
         }
-        th = topk_threshold<256>(from_regs, (uint32_t)B, sm.tk);
+        th = topk_threshold<kSelNT>(from_regs, (uint32_t)B, sm.tk);
     }
 
-    // ---- emission: bitmap of kept blocks, ascending ----
+    // emission: bitmap of kept blocks, ascending
     const int n_words = (int)((limit + 31) / 32);
-    for (int w = tid; w < n_words; w += 256) sm.bitmap[w] = 0;
+    for (int w = tid; w < n_words; w += kSelNT) sm.bitmap[w] = 0;
     __syncthreads();
     auto mark = [&](uint32_t k, uint32_t u) {
         if (th.keep(k, u)) {
@@ -308,13 +346,11 @@ __global__ __launch_bounds__(256) void k_score_select_f32(FusedSelectArgs f) {
     __syncthreads();
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = f.top_k + a.r - 1;
-    const int n_keep =
-        emit_from_bitmap<256>(sm.bitmap, n_words, B, a.r, nc, tail, f.sel_blocks + (int64_t)i * B,
-                              f.sel_cells + (int64_t)i * ld_cells, ld_cells, sm.tk);
-    if (tid == 0) {
-        f.n_sel[i] = n_keep * a.r + tail;
-        f.arrive[i] = 0u;  // ready for the next launch
-    }
+    const int n_keep = emit_from_bitmap<kSelNT>(sm.bitmap, n_words, B, a.r, nc, tail,
+                                                f.sel_blocks + (int64_t)i * B,
+                                                f.sel_cells + (int64_t)i * ld_cells, ld_cells,
+                                                sm.tk);
+    if (tid == 0) f.n_sel[i] = n_keep * a.r + tail;
 }
 
 // ---------------------------------------------------------------------------
@@ -451,30 +487,25 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs a, const uint16_t 
 
 size_t fused_select_ws_bytes(int n_q, int nb_max) {
     const size_t n_wg = (size_t)(nb_max + 255) / 256;
-    // arrival counters first (zero between launches), then per-workgroup data
-    const size_t head = ((size_t)n_q * sizeof(uint32_t) + 255) / 256 * 256;
-    return head + (size_t)n_q * n_wg * (kCand * sizeof(uint64_t) + sizeof(uint64_t) +
-                                        sizeof(uint32_t));
+    return (size_t)n_q * n_wg * (kCand + 1) * sizeof(uint64_t);
 }
 
-hipError_t launch_score_select_f32(const ScoreArgs &s, int32_t top_k, int32_t *sel_blocks,
-                                   int32_t *sel_cells, int32_t *n_sel, void *ws,
-                                   hipStream_t st) {
-    if (s.n_q <= 0) return hipSuccess;
-    FusedSelectArgs f;
-    f.s = s;
-    f.top_k = top_k;
-    f.sel_blocks = sel_blocks;
-    f.sel_cells = sel_cells;
-    f.n_sel = n_sel;
-    f.n_wg = (s.nb_max + 255) / 256;
-    char *w = static_cast<char *>(ws);
-    const size_t head = ((size_t)s.n_q * sizeof(uint32_t) + 255) / 256 * 256;
-    f.arrive = reinterpret_cast<uint32_t *>(w);
-    f.cand = reinterpret_cast<uint64_t *>(w + head);
-    f.drop = f.cand + (size_t)s.n_q * f.n_wg * kCand;
-    f.fin = reinterpret_cast<uint32_t *>(f.drop + (size_t)s.n_q * f.n_wg);
-    hipLaunchKernelGGL(k_score_select_f32, dim3(f.n_wg, s.n_q), dim3(256), 0, st, f);
+static void bind_ws(DecodeIdxArgs &f, void *ws) {
+    f.n_wg = (f.s.nb_max + 255) / 256;
+    f.cand = static_cast<uint64_t *>(ws);
+    f.drop = f.cand + (size_t)f.s.n_q * f.n_wg * kCand;
+}
+
+hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st) {
+    bind_ws(f, ws);
+    const int grid = f.n_wg * f.s.n_q + (f.n_dirty + 3) / 4;
+    if (grid > 0) hipLaunchKernelGGL(k_score_cand, dim3(grid), dim3(256), 0, st, f);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st) {
+    bind_ws(f, ws);
+    if (f.s.n_q > 0) hipLaunchKernelGGL(k_select_cand, dim3(f.s.n_q), dim3(kSelNT), 0, st, f);
     return hipGetLastError();
 }
 

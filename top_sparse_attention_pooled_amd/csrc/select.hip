@@ -3,12 +3,12 @@
 // selected ones; goodbadwolf's comment on the same issue gives the set's
 // capacity n_kv_max = top_k + r - 1, the budget plus the tail).
 //
-// One 512-thread workgroup per query.  Candidate block b (finite score,
+// One 1024-thread workgroup per query.  Candidate block b (finite score,
 // b < number of complete blocks) has the unique key
 //     (order-preserving bits of its score) << 32 | ~b,
 // so the kept set is exactly the blocks with the top_k/r largest keys: the
-// ranking's ties go to the lower block index.  Up to 65,536 blocks the keys
-// live in registers (128 per thread, loaded once with every load in flight);
+// ranking's ties go to the lower block index.  Up to 32,768 blocks the keys
+// live in registers (32 per thread, loaded once with every load in flight);
 // beyond that they are re-streamed from memory each round.  The threshold
 // comes from topk_engine.h; the kept blocks are marked in an LDS bitmap and
 // emitted in ascending order, each expanded to its r cells, followed by the
@@ -19,8 +19,8 @@ namespace qsa {
 
 namespace {
 
-constexpr int kNT = 512;
-constexpr int kC = 128;                        // register-cached keys per thread
+constexpr int kNT = 1024;
+constexpr int kC = 32;                        // register-cached keys per thread
 constexpr int kMaxBitmapBlocks = 1 << 19;      // 64 KiB bitmap
 constexpr int kMaxKeep = 4096;
 
@@ -47,20 +47,17 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     const float *row = a.scores + (int64_t)i * a.ld;
 
     // source 1: score keys cached in registers, block = s2*kNT + tid
-    uint32_t k32[kC];
+    RegKeys32<kC, kNT> from_regs;
+    from_regs.tid = tid;
     const bool in_regs = limit <= (int64_t)kNT * kC;
     if (in_regs) {
 #pragma unroll
         for (int s2 = 0; s2 < kC; ++s2) {
             const int64_t b = (int64_t)s2 * kNT + tid;
             const float sc = b < limit ? row[b] : 0.0f;
-            k32[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
+            from_regs.k[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
         }
     }
-    auto from_regs = [&](auto &&f) {
-#pragma unroll
-        for (int s2 = 0; s2 < kC; ++s2) f(k32[s2], ~(uint32_t)(s2 * kNT + tid));
-    };
     // source 2: the score row re-read from memory, 16 loads in flight
     auto from_memory = [&](auto &&f) {
         constexpr int U = 16;

@@ -139,7 +139,7 @@ __device__ __forceinline__ void pick_bin(TopkSmem<NT> &sm, uint32_t lo, uint32_t
 // threshold value; n_above gets the count strictly above it; done tells
 // whether count(v >= threshold) == krem (no tie left at the threshold).
 template <int NT, typename ForEach, typename Pred, typename Val>
-__device__ uint32_t select_u32(ForEach for_each, Pred pred, Val val, uint32_t krem, uint32_t lo,
+__device__ uint32_t select_u32(const ForEach &for_each, Pred pred, Val val, uint32_t krem, uint32_t lo,
                                uint32_t hi, TopkSmem<NT> &sm, uint32_t &n_above, bool &done) {
     n_above = 0;
     for (int round = 0; round < 4; ++round) {
@@ -172,7 +172,7 @@ __device__ uint32_t select_u32(ForEach for_each, Pred pred, Val val, uint32_t kr
 // The exact kept set of the top B (or every valid element if there are at
 // most B).
 template <int NT, typename ForEach>
-__device__ Thresh topk_threshold(ForEach for_each, uint32_t B, TopkSmem<NT> &sm) {
+__device__ Thresh topk_threshold(const ForEach &for_each, uint32_t B, TopkSmem<NT> &sm) {
     Thresh th{0u, 0u, false};
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
     for_each([&](uint32_t k, uint32_t) {
@@ -256,6 +256,30 @@ __device__ int emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, i
     __syncthreads();
     return n_keep;
 }
+
+// Register-resident element sources for topk_threshold.  (A functor object,
+// not a capturing lambda: with the array a member, full unrolling keeps every
+// element in a register.)
+template <int C>
+struct RegKeys64 {  // explicit keys (score key << 32 | ~block), 0 = none
+    uint64_t k[C];
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+#pragma unroll
+        for (int s = 0; s < C; ++s) fn((uint32_t)(k[s] >> 32), (uint32_t)k[s]);
+    }
+};
+
+template <int C, int NT>
+struct RegKeys32 {  // score keys of blocks s*NT + tid, 0 = none
+    uint32_t k[C];
+    int tid;
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+#pragma unroll
+        for (int s = 0; s < C; ++s) fn(k[s], ~(uint32_t)(s * NT + tid));
+    }
+};
 
 // 64-bit sortable key of a candidate: (score key, ~block); 0 = none.
 __device__ __forceinline__ uint64_t block_key(float s, int64_t b) {

@@ -23,7 +23,8 @@ TILE = 64
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_update_pooled_keys", "qsa_score_blocks", "qsa_select_topk_blocks",
-           "qsa_score_select_decode", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
+           "qsa_score_select_decode", "qsa_decode_score_candidates",
+           "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
 
 
 class QsaError(RuntimeError):
@@ -77,8 +78,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_select_topk_blocks.restype = ctypes.c_int
     lib.qsa_select_topk_blocks.argtypes = [D, S, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.qsa_score_select_decode.restype = ctypes.c_int
-    lib.qsa_score_select_decode.argtypes = [D, S, vp, vp, vp, i32, vp, i32, vp, i64, vp, vp, vp,
-                                            vp, sz, vp]
+    lib.qsa_score_select_decode.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32,
+                                            vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.qsa_decode_score_candidates.restype = ctypes.c_int
+    lib.qsa_decode_score_candidates.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32,
+                                                vp, i64, vp, sz, vp]
+    lib.qsa_decode_select_candidates.restype = ctypes.c_int
+    lib.qsa_decode_select_candidates.argtypes = [D, S, vp, vp, i32, i32, vp, i64, vp, vp, vp, vp,
+                                                 sz, vp]
     for name in ("qsa_sparse_attn_decode", "qsa_sparse_attn_prefill"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -180,14 +187,34 @@ def select_topk_blocks(dims: Dims, seqs: Seqs, scores, ld_scores: int, q_seq, q_
                                       _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def score_select_decode(dims: Dims, seqs: Seqs, q_idx, q_seq, q_pos, n_q: int, pooled,
-                        nb_max: int, scores, ld_scores: int, sel_blocks, sel_cells, n_sel, ws,
-                        ws_bytes: int, stream=None) -> None:
+def score_select_decode(dims: Dims, seqs: Seqs, kidx, dirty, n_dirty: int, pooled, pooled_bf16,
+                        q_idx, q_seq, q_pos, n_q: int, nb_max: int, scores, ld_scores: int,
+                        sel_blocks, sel_cells, n_sel, ws, ws_bytes: int, stream=None) -> None:
     _rc(load().qsa_score_select_decode(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
-                                       _ptr(q_idx), _ptr(q_seq), _ptr(q_pos), n_q, _ptr(pooled),
-                                       nb_max, _ptr(scores), ld_scores, _ptr(sel_blocks),
+                                       _ptr(kidx), _ptr(dirty), n_dirty, _ptr(pooled),
+                                       _ptr(pooled_bf16), _ptr(q_idx), _ptr(q_seq), _ptr(q_pos),
+                                       n_q, nb_max, _ptr(scores), ld_scores, _ptr(sel_blocks),
                                        _ptr(sel_cells), _ptr(n_sel), _ptr(ws), ws_bytes,
                                        _stream(stream)))
+
+
+def decode_score_candidates(dims: Dims, seqs: Seqs, kidx, dirty, n_dirty: int, pooled,
+                            pooled_bf16, q_idx, q_seq, q_pos, n_q: int, nb_max: int, scores,
+                            ld_scores: int, ws, ws_bytes: int, stream=None) -> None:
+    _rc(load().qsa_decode_score_candidates(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                           _ptr(kidx), _ptr(dirty), n_dirty, _ptr(pooled),
+                                           _ptr(pooled_bf16), _ptr(q_idx), _ptr(q_seq),
+                                           _ptr(q_pos), n_q, nb_max, _ptr(scores), ld_scores,
+                                           _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def decode_select_candidates(dims: Dims, seqs: Seqs, q_seq, q_pos, n_q: int, nb_max: int,
+                             scores, ld_scores: int, sel_blocks, sel_cells, n_sel, ws,
+                             ws_bytes: int, stream=None) -> None:
+    _rc(load().qsa_decode_select_candidates(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                            _ptr(q_seq), _ptr(q_pos), n_q, nb_max, _ptr(scores),
+                                            ld_scores, _ptr(sel_blocks), _ptr(sel_cells),
+                                            _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def sparse_attn_decode(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_cache, sel_cells,

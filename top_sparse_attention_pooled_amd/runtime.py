@@ -108,10 +108,8 @@ class StepBuffers:
         self.ws_attn = torch.empty(max(self.ws_attn_bytes, 16), dtype=torch.uint8, device=dev)
         self.ws_score_bytes = qsa.workspace_size(dims, qsa.OP_SCORE_BF16, n_q)
         self.ws_score = torch.empty(max(self.ws_score_bytes, 16), dtype=torch.uint8, device=dev)
-        # the fused score+select workspace starts with arrival counters that
-        # must be zero before the first call (the library leaves them zero)
         self.ws_fused_bytes = qsa.workspace_size(dims, qsa.OP_SCORE_SELECT, n_q, nb_max)
-        self.ws_fused = torch.zeros(max(self.ws_fused_bytes, 256), dtype=torch.uint8, device=dev)
+        self.ws_fused = torch.empty(max(self.ws_fused_bytes, 16), dtype=torch.uint8, device=dev)
 
 
 def run_step(layer: Layer, bufs: StepBuffers, q_idx, q, q_seq, q_pos, dirty, n_dirty: int,
@@ -119,18 +117,20 @@ def run_step(layer: Layer, bufs: StepBuffers, q_idx, q, q_seq, q_pos, dirty, n_d
              stream=None) -> StepOut:
     """update -> score -> select -> attend, all enqueued on one stream.
 
-    fused: decode scoring and selection in one launch (qsa_score_select_decode)
-    instead of qsa_score_blocks + qsa_select_topk_blocks; same results."""
+    fused: the decode update, scoring and selection through
+    qsa_score_select_decode instead of the three separate calls; same
+    results."""
     d, sq = layer.dims, layer.seqs()
     n_q = bufs.n_q
-    if n_dirty:
-        qsa.update_pooled_keys(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
-                               layer.pooled_bf16, stream=stream)
     if fused and mode == qsa.SCORE_F32:
-        qsa.score_select_decode(d, sq, q_idx, q_seq, q_pos, n_q, layer.pooled, bufs.nb_max,
+        qsa.score_select_decode(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
+                                layer.pooled_bf16, q_idx, q_seq, q_pos, n_q, bufs.nb_max,
                                 bufs.scores, bufs.ld, bufs.sel_blocks, bufs.sel_cells,
                                 bufs.n_sel, bufs.ws_fused, bufs.ws_fused_bytes, stream=stream)
     else:
+        if n_dirty:
+            qsa.update_pooled_keys(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
+                                   layer.pooled_bf16, stream=stream)
         qsa.score_blocks(d, sq, q_idx, q_seq, q_pos, n_q, layer.pooled, layer.pooled_bf16,
                          bufs.nb_max, bufs.scores, bufs.ld, mode, bufs.ws_score,
                          bufs.ws_score_bytes, stream=stream)
