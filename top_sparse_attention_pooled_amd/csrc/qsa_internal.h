@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "../../include/qsa.h"
+#include "wave_ops.h"
 
 namespace qsa {
 
@@ -113,9 +114,13 @@ __device__ __forceinline__ void pooled_key_lane(const float *kidx, int64_t cap_c
     const float plo = lo * lo;
     const float phi2 = hi * hi;
     float v = plo + phi2;
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) v = v + __shfl_xor(v, h, kWave);
-    v = __shfl(v, 0, kWave);
+    v = v + xor_lane_f<32>(v);
+    v = v + xor_lane_f<16>(v);
+    v = v + xor_lane_f<8>(v);
+    v = v + xor_lane_f<4>(v);
+    v = v + xor_lane_f<2>(v);
+    v = v + xor_lane_f<1>(v);
+    v = __uint_as_float(lane_value(__float_as_uint(v), 0));
     const float ms = v / (float)kDIdx;
     const float inv = 1.0f / sqrtf(ms + eps);
     lo = lo * inv;

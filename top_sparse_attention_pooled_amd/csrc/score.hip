@@ -140,7 +140,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
     for (int kk = 2; kk <= kWave; kk <<= 1) {
 #pragma unroll
         for (int j = kk >> 1; j > 0; j >>= 1) {
-            const uint64_t o = shfl_xor64(key, j);
+            const uint64_t o = shfl_xor64(key, j);  // j is a constant once unrolled
             const bool take_max = ((lane & j) == 0) == ((lane & kk) == 0);
             key = take_max ? (o > key ? o : key) : (o < key ? o : key);
         }
@@ -185,17 +185,39 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     const int64_t wg_b0 = (int64_t)wg * 256;
     const int64_t b0 = wg_b0 + wave * kTile;
     const int64_t b = b0 + lane;
+    // the dirty list: fetched with the keys, one entry per thread
+    __shared__ int s_hit[256];
+    __shared__ int s_n_hit;
+    if (tid == 0) s_n_hit = 0;
+    int my_ds = -1, my_db = -1;
+    if (tid < f.n_dirty) {
+        my_ds = f.dirty[2 * tid];
+        my_db = f.dirty[2 * tid + 1];
+    }
     float4 k[kQuads];
     load_tile_and_query(a, i, s, p, nc, wg_b0, b0, k, qr4);
+    // dirty entries of this workgroup's scored blocks (lists longer than 256
+    // are covered by the loop below reading the rest directly)
+    if (my_ds == s && my_db >= wg_b0 && my_db < wg_b0 + 256 && my_db < nc)
+        s_hit[atomicAdd(&s_n_hit, 1)] = my_db;
+    __syncthreads();
+    const int n_hit = s_n_hit;
 
     // a dirty block scored here may not be written yet: recompute it in place
-    if (wg_b0 < nc) {
+    if (wg_b0 < nc && (n_hit > 0 || f.n_dirty > 256)) {
         int64_t n = a.g.n_cells[s];
         if (n > a.g.cap_cells) n = a.g.cap_cells;
-        for (int e = 0; e < f.n_dirty; ++e) {  // workgroup-uniform loop
-            const int ds = f.dirty[2 * e];
-            const int64_t db = f.dirty[2 * e + 1];
-            if (ds != s || db < wg_b0 || db >= wg_b0 + 256 || db >= nc) continue;
+        const int n_iter = f.n_dirty > 256 ? n_hit + (f.n_dirty - 256) : n_hit;
+        for (int e = 0; e < n_iter; ++e) {  // workgroup-uniform loop
+            int64_t db;
+            if (e < n_hit) {
+                db = s_hit[e];
+            } else {
+                const int de = 256 + (e - n_hit);
+                if (f.dirty[2 * de] != s) continue;
+                db = f.dirty[2 * de + 1];
+                if (db < wg_b0 || db >= wg_b0 + 256 || db >= nc) continue;
+            }
             const int owner_wave = (int)((db - wg_b0) >> 6);
             if (wave == owner_wave) {
                 float lo, hi;
@@ -225,9 +247,8 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     if (wave == 0) {
         uint64_t k2 = wave_top[lane >> 4][lane & 15];
         k2 = wave_sort_desc(k2);
-        const uint64_t d16 = (uint64_t)(uint32_t)__shfl((uint32_t)k2, kCand, kWave) |
-                             ((uint64_t)(uint32_t)__shfl((uint32_t)(k2 >> 32), kCand, kWave)
-                              << 32);
+        const uint64_t d16 = (uint64_t)lane_value((uint32_t)k2, kCand) |
+                             ((uint64_t)lane_value((uint32_t)(k2 >> 32), kCand) << 32);
         const int64_t slot = (int64_t)i * f.n_wg + wg;
         if (lane < kCand) f.cand[slot * kCand + lane] = k2;
         if (lane == 0) {
@@ -288,15 +309,23 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
             }
         }
     };
+    // largest dropped key of each scoring workgroup, fetched with the keys
+    constexpr int kDropSlots = kFusedMaxBlocks / 256 / kSelNT;  // 1 (512 workgroups max)
+    uint64_t drop[kDropSlots > 0 ? kDropSlots : 1];
+#pragma unroll
+    for (int q = 0; q < (kDropSlots > 0 ? kDropSlots : 1); ++q) {
+        const int w = tid + kSelNT * q;
+        drop[q] = w < f.n_wg ? f.drop[qbase + w] : 0ull;
+    }
+    if (tid == 0) sm.n_over = 0;
     const Thresh th0 = topk_threshold<kSelNT>(from_regs, (uint32_t)B, sm.tk);
 
-    if (tid == 0) sm.n_over = 0;
-    __syncthreads();
-    for (int w = tid; w < f.n_wg; w += kSelNT) {
-        const uint64_t d = f.drop[qbase + w];
+#pragma unroll
+    for (int q = 0; q < (kDropSlots > 0 ? kDropSlots : 1); ++q) {
+        const uint64_t d = drop[q];
         if (d != 0 && th0.keep((uint32_t)(d >> 32), (uint32_t)d)) {
             const int at = atomicAdd(&sm.n_over, 1);
-            if (at < kMaxExpand) sm.over[at] = w;
+            if (at < kMaxExpand) sm.over[at] = tid + kSelNT * q;
         }
     }
     __syncthreads();

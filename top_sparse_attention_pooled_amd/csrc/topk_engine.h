@@ -22,6 +22,7 @@
 #pragma once
 
 #include "qsa_internal.h"
+#include "wave_ops.h"
 
 namespace qsa {
 
@@ -49,8 +50,7 @@ struct Thresh {
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    v = wave_sum_u32(v);
     if (lane == 0) sm.red[wave] = v;
     __syncthreads();
     uint32_t t = 0;
@@ -64,11 +64,8 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) 
 template <int NT>
 __device__ __forceinline__ void block_minmax_u32(uint32_t &mn, uint32_t &mx, TopkSmem<NT> &sm) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor(mn, m, kWave));
-        mx = max(mx, (uint32_t)__shfl_xor(mx, m, kWave));
-    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
     if (lane == 0) {
         sm.red[wave] = mn;
         sm.red2[wave] = mx;
@@ -106,15 +103,11 @@ __device__ __forceinline__ void pick_bin(TopkSmem<NT> &sm, uint32_t lo, uint32_t
     }
     // suffix sums: values in bins above this thread's bins
     const int lane = t & (kWave - 1), wave = t >> 6;
-    uint32_t incl = local;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const uint32_t o = __shfl_down(incl, m, kWave);
-        if (lane + m < kWave) incl += o;
-    }
-    if (lane == 0) sm.red[wave] = incl;
+    const uint32_t prefix = wave_incl_scan_u32(local);     // lanes <= this one
+    const uint32_t total = lane_value(prefix, kWave - 1);  // whole wave
+    if (lane == 0) sm.red[wave] = total;
     __syncthreads();
-    uint32_t above = incl - local;
+    uint32_t above = total - prefix;  // higher lanes of this wave
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w)
         if (w > wave) above += sm.red[w];
@@ -220,12 +213,7 @@ __device__ int emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, i
     uint32_t local = 0;
     for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(bm[w]);
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-    uint32_t incl = local;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const uint32_t o = __shfl_up(incl, m, kWave);
-        if (lane >= m) incl += o;
-    }
+    const uint32_t incl = wave_incl_scan_u32(local);
     if (lane == kWave - 1) sm.red[wave] = incl;
     __syncthreads();
     uint32_t pos = incl - local;
@@ -289,8 +277,8 @@ __device__ __forceinline__ uint64_t block_key(float s, int64_t b) {
 __device__ __forceinline__ int32_t key_block(uint64_t key) { return (int32_t)(~(uint32_t)key); }
 
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+    const uint32_t lo = xor_lane_rt((uint32_t)v, m);
+    const uint32_t hi = xor_lane_rt((uint32_t)(v >> 32), m);
     return ((uint64_t)hi << 32) | lo;
 }
 
