@@ -114,8 +114,8 @@ def main():
 
     def enqueue(t, ev=None, only_score=False):
         """One decode token through every layer: update + scores + candidates,
-        selection, attention (+ combine).  ev: per-layer (start, end) events
-        around the scoring kernel."""
+        then selection fused into attention (+ the merge of partial states).
+        ev: per-layer (start, end) events around the scoring kernel."""
         for li, layer in enumerate(layers):
             layer.n_cells = n_cells[t]
             bf, d, sq = bufs[li], layer.dims, layer.seqs()
@@ -128,11 +128,10 @@ def main():
                 ev[li][1].record(stream)
             if only_score:
                 continue
-            qsa.decode_select_candidates(d, sq, q_seq[t], q_pos[t], n_q, nb_max, bf.scores,
-                                         bf.ld, bf.sel_blocks, bf.sel_cells, bf.n_sel,
-                                         bf.ws_fused, bf.ws_fused_bytes)
-            qsa.sparse_attn_decode(d, sq, q[t], q_seq[t], n_q, layer.k, layer.v, bf.sel_cells,
-                                   bf.n_sel, bf.out, bf.ws_attn, bf.ws_attn_bytes)
+            qsa.decode_select_attend(d, sq, q_seq[t], q_pos[t], n_q, nb_max, bf.scores, bf.ld,
+                                     bf.sel_blocks, bf.sel_cells, bf.n_sel, bf.ws_fused,
+                                     bf.ws_fused_bytes, q[t], layer.k, layer.v, bf.out,
+                                     bf.ws_attn, bf.ws_attn_bytes)
 
     def capture(steps, events=None, only_score=False):
         g = torch.cuda.CUDAGraph()

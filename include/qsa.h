@@ -223,11 +223,11 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
  * also available as two calls:
  *   qsa_decode_score_candidates writes the dirty blocks and scores every
  *     block (a workgroup that holds a dirty block recomputes it in registers
- *     rather than reading it), keeping in the workspace the 16 best keys of
- *     each 256 blocks and the largest key each dropped;
+ *     rather than reading it), keeping in the workspace the 4 best keys of
+ *     each group of 64 blocks and the largest key each group dropped;
  *   qsa_decode_select_candidates selects from those, re-admitting all keys
- *     of any 256 blocks whose dropped keys could compete (or re-reading the
- *     score row if more than 16 could), so the selection is exact.
+ *     of any group whose dropped key could compete (or re-reading the score
+ *     row if more than 32 groups could), so the selection is exact.
  * Workspace: qsa_workspace_size(QSA_OP_SCORE_SELECT, n_q, nb_max) bytes,
  * 16-byte aligned, no initial contents required; the two calls must get the
  * same workspace, scores and geometry, and calls that share a workspace must
@@ -281,6 +281,31 @@ int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs,
                             const void *v_cache_dev, const int32_t *sel_cells_dev,
                             const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
                             size_t ws_bytes, void *stream);
+
+/* 3+4 for decode, fused  [ISSUE lever3 then lever1: the block top-k, expanded
+ * to cells, is the set attention visits]: exactly qsa_decode_select_candidates
+ * followed by qsa_sparse_attn_decode over its output, in one workgroup grid
+ * plus the merge of partial states.  Every attention workgroup derives the
+ * query's exact kept set from the candidates that qsa_decode_score_candidates
+ * left in ws_idx (the set is unique, so all derive the same one) and takes
+ * its 32 cells of the ascending cell list straight from on-chip memory; one
+ * workgroup per query also writes sel_blocks, sel_cells and n_sel.  The
+ * selection outputs equal the two calls' bit for bit, and so does out (the
+ * same arithmetic in the same order).
+ *   ws_idx:  the workspace qsa_decode_score_candidates filled (same n_q,
+ *            nb_max, scores and geometry); read only.
+ *   ws_attn: qsa_workspace_size(QSA_OP_ATTN_DECODE, n_q) bytes, 16-byte
+ *            aligned, no initial contents required.
+ * Needs nb_max <= 65536 (contexts up to 262144 cells), else QSA_ENOTSUP: use
+ * the two calls.  Calls sharing a workspace must not overlap. */
+int qsa_decode_select_attend(const qsa_dims *dims, const qsa_seqs *seqs,
+                             const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                             int32_t nb_max, const float *scores_dev, int64_t ld_scores,
+                             int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                             int32_t *n_sel_dev, const void *ws_idx_dev, size_t ws_idx_bytes,
+                             const float *q_dev, const void *k_cache_dev,
+                             const void *v_cache_dev, float *out_dev, void *ws_attn_dev,
+                             size_t ws_attn_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -40,8 +40,8 @@ def test_workspace_sizes():
     assert qsa.workspace_size(d, qsa.OP_SCORE_BF16, 512) == 512 * 128 * 2
     runs = -(-d.ld_cells // 32)  # 32-cell runs
     assert qsa.workspace_size(d, qsa.OP_ATTN_DECODE, 5) == 5 * runs * 16 * 258 * 4
-    n_wg = -(-62070 // 256)  # decode score+select: 16 kept keys + the largest dropped
-    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 5 * n_wg * 17 * 8
+    n_grp = -(-62070 // 256) * 4  # decode score+select: per 64-block group, 4 kept + 1 dropped
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 5 * n_grp * 5 * 8
     with pytest.raises(qsa.QsaError) as e:
         qsa.workspace_size(d, 99, 1)
     assert e.value.code == qsa.QSA_EINVAL
@@ -117,3 +117,38 @@ def test_empty_calls_are_noops():
     qsa.score_blocks(d, _seqs(), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, FAKE, 64, stream=0)
     qsa.select_topk_blocks(d, _seqs(), FAKE, 64, FAKE, FAKE, 0, 64, FAKE, FAKE, FAKE, stream=0)
     assert qsa.load().qsa_last_error() == b""
+
+
+def test_fused_select_attend_limits():
+    d = qsa.Dims()
+    big = 70000  # blocks: above the 65536 the fused selection holds on chip
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.decode_select_attend(d, _seqs(cap=280064), FAKE, FAKE, 1, big, FAKE, big, FAKE, FAKE,
+                                 FAKE, FAKE, 1 << 30, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                 stream=0)
+    assert e.value.code == qsa.QSA_ENOTSUP
+    need = qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 1, 4000)
+    with pytest.raises(qsa.QsaError) as e:  # candidate workspace too small
+        qsa.decode_select_attend(d, _seqs(), FAKE, FAKE, 1, 4000, FAKE, 4000, FAKE, FAKE, FAKE,
+                                 FAKE, need - 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
+    assert e.value.code == qsa.QSA_EWS
+    with pytest.raises(qsa.QsaError) as e:  # attention workspace too small
+        qsa.decode_select_attend(d, _seqs(), FAKE, FAKE, 1, 4000, FAKE, 4000, FAKE, FAKE, FAKE,
+                                 FAKE, need, FAKE, FAKE, FAKE, FAKE, FAKE, 16, stream=0)
+    assert e.value.code == qsa.QSA_EWS
+    qsa.decode_select_attend(d, _seqs(), FAKE, FAKE, 0, 4000, FAKE, 4000, FAKE, FAKE, FAKE,
+                             FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0)  # n_q = 0: no-op
+
+
+def test_no_kernel_spills_to_scratch():
+    """Every kernel keeps its register arrays in registers: a spilled key or
+    tile array would turn the register-resident loops into memory traffic."""
+    import json
+    import os
+    from top_sparse_attention_pooled_amd import build
+    if not os.path.exists(build.RESOURCES):
+        pytest.skip("library not built")
+    res = json.load(open(build.RESOURCES))
+    assert res, "no kernel resource report"
+    spilled = {k: v["scratch"] for k, v in res.items() if v.get("scratch", 0) > 0}
+    assert not spilled, spilled

@@ -1,7 +1,8 @@
-"""GPU parity of the fused decode score+select call against the oracle and
-against the two-call path, with inputs built to drive every branch of its
-selection: the common case, workgroups whose dropped keys compete (their full
-key sets are re-admitted), so many such workgroups that the scores are
+"""GPU parity of the fused decode indexer calls (score+select, and
+candidates then select+attend) against the oracle and against the separate
+calls, with inputs built to drive every branch of its
+selection: the common case, 64-block groups whose dropped keys compete (their
+full key sets are re-admitted), so many such groups that the scores are
 re-streamed, all-tied scores, and contexts with fewer blocks than the budget.
 """
 import sys
@@ -56,11 +57,24 @@ def run_case(name, w, n_cells, q_idx, kidx):
                      nb_max, sep.scores, sep.ld)
     qsa.select_topk_blocks(layer.dims, layer.seqs(), sep.scores, sep.ld, q_seq, q_pos, n_q,
                            nb_max, sep.sel_blocks, sep.sel_cells, sep.n_sel)
+    # attention over the separate calls' selection, and the selection fused
+    # into attention (each attention workgroup selects on its own)
+    q = t(synth.normal((n_q, w.H, w.D), 95, 0, synth.T_Q))
+    qsa.sparse_attn_decode(layer.dims, layer.seqs(), q, q_seq, n_q, layer.k, layer.v,
+                           sep.sel_cells, sep.n_sel, sep.out, sep.ws_attn, sep.ws_attn_bytes)
+    att = runtime.StepBuffers(layer.dims, n_q, nb_max, DEV)
+    qsa.decode_score_candidates(layer.dims, layer.seqs(), None, None, 0, layer.pooled, None,
+                                t(qi), q_seq, q_pos, n_q, nb_max, att.scores, att.ld,
+                                att.ws_fused, att.ws_fused_bytes)
+    qsa.decode_select_attend(layer.dims, layer.seqs(), q_seq, q_pos, n_q, nb_max, att.scores,
+                             att.ld, att.sel_blocks, att.sel_cells, att.n_sel, att.ws_fused,
+                             att.ws_fused_bytes, q, layer.k, layer.v, att.out, att.ws_attn,
+                             att.ws_attn_bytes)
     torch.cuda.synchronize()
     for i, p in enumerate(positions):
         r_scores = oracle.score_query(qi[i], p, ref_pooled[0], nb_max, w.r, w.theta)
         rb, rc = oracle.select(r_scores, p, w.r, w.top_k)
-        for bufs, label in ((fused, "fused"), (sep, "two-call")):
+        for bufs, label in ((fused, "fused"), (sep, "two-call"), (att, "select+attend")):
             gs = bufs.scores.cpu().numpy()[i, :nb_max]
             assert np.array_equal(gs.view(np.uint32), r_scores.view(np.uint32)), label
             gb = bufs.sel_blocks.cpu().numpy()[i]
@@ -70,6 +84,9 @@ def run_case(name, w, n_cells, q_idx, kidx):
             assert np.all(gb[rb.size:] == -1)
             assert np.array_equal(gc[:rc.size], rc), (label, p)
             assert np.all(gc[rc.size:] == -1)
+    # same cells, same arithmetic: the fused attention output is identical
+    assert np.array_equal(att.out.cpu().numpy().view(np.uint32),
+                          sep.out.cpu().numpy().view(np.uint32))
     return r_scores
 
 
@@ -84,23 +101,26 @@ def test_fused_common_case():
     run_case("i.i.d. keys", w, 40000, q, kidx)
 
 
-def test_fused_expands_clustered_workgroups():
+def test_fused_expands_clustered_groups():
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 96, 0, synth.T_QIDX)
-    aligned_cells(w, q, 39999, range(3000, 3700), kidx)  # 700 blocks over 4 workgroups
-    s = run_case("contiguous cluster (re-admits 4 workgroups)", w, 40000, q, kidx)
+    aligned_cells(w, q, 39999, range(3000, 3700), kidx)  # 700 blocks over 12 groups
+    s = run_case("contiguous cluster (re-admits 12 groups)", w, 40000, q, kidx)
     kept, _ = oracle.select(s, 40000 - 3, w.r, w.top_k)
     assert np.sum((kept >= 3000) & (kept < 3700)) >= 500  # the case really is clustered
 
 
-def test_fused_streams_when_many_workgroups_compete():
+def test_fused_streams_when_many_groups_compete():
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 97, 0, synth.T_QIDX)
-    blocks = [wg * 256 + 7 * j for wg in range(2, 32) for j in range(20)]  # 20 in 30 workgroups
+    # 20 blocks at stride 7 in each of 30 spans of 256: 10 and 9 of them fall
+    # into the span's first two 64-block groups (more than the 4 a group
+    # keeps), so 60 groups compete
+    blocks = [wg * 256 + 7 * j for wg in range(2, 32) for j in range(20)]
     aligned_cells(w, q, 39999, blocks, kidx)
-    s = run_case("strided cluster (30 workgroups compete: re-stream)", w, 40000, q, kidx)
+    s = run_case("strided cluster (60 groups compete: re-stream)", w, 40000, q, kidx)
     kept, _ = oracle.select(s, 40000 - 3, w.r, w.top_k)
     assert np.isin(kept, blocks).sum() >= 500
 

@@ -253,7 +253,11 @@ def test_attention_matches_oracle_on_shared_cells(kv_type, H, Hk):
 # whole steps on the benchmark workloads
 # --------------------------------------------------------------------------
 
-def _run_workload(name, steps, check_every=1, w=None):
+def _run_workload(name, steps, check_every=1, w=None, paths=("attend", "general")):
+    """Steps of a workload through every call sequence in `paths` (each
+    recomputes the same dirty blocks, so they can share the layer), each
+    checked against the oracle: scores and selections bit-exact, attention
+    within tolerance."""
     w = synth.WORKLOADS[name] if w is None else w
     say(f"end-to-end {name}: generating inputs")
     kidx = synth.make_kidx(w)
@@ -265,16 +269,18 @@ def _run_workload(name, steps, check_every=1, w=None):
     ref_pooled = oracle_pooled(w, kidx, n0)
     worst = 0.0
     fracs = []
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     for step in range(steps):
         n = synth.n_cells_at(w, step)
         layer.set_n_cells(n)
         dirty = synth.dirty_blocks(w, step)
         q_idx, q, q_seq, q_pos = synth.make_queries(w, step)
         n_q = q_pos.size
-        bufs = runtime.StepBuffers(layer.dims, n_q, w.nb_max(step), DEV)
-        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
-        out = runtime.run_step(layer, bufs, t(q_idx), t(q), t(q_seq), t(q_pos),
-                               t(dirty.reshape(-1)), dirty.shape[0])
+        outs = {}
+        for path in paths:
+            bufs = runtime.StepBuffers(layer.dims, n_q, w.nb_max(step), DEV)
+            outs[path] = runtime.run_step(layer, bufs, t(q_idx), t(q), t(q_seq), t(q_pos),
+                                          t(dirty.reshape(-1)), dirty.shape[0], path=path)
         torch.cuda.synchronize()
         oracle.update_pooled(kidx, n, dirty, ref_pooled, w.r, w.theta, w.eps)
         if step % check_every:
@@ -282,18 +288,27 @@ def _run_workload(name, steps, check_every=1, w=None):
         ref = oracle.step(q_idx, q, q_seq, q_pos, ref_pooled, k, v, kv_type=w.kv_type,
                           n_head_kv=w.Hk, r=w.r, top_k=w.top_k, theta=w.theta,
                           nb_out=w.nb_max(step))
-        gs = out.scores.cpu().numpy()[:, :w.nb_max(step)]
-        gb, gc = out.sel_blocks.cpu().numpy(), out.sel_cells.cpu().numpy()
-        gn, go = out.n_sel.cpu().numpy(), out.out.cpu().numpy()
-        for i in range(n_q):
-            fracs.append(check_scores(gs[i], ref["scores"][i]))
-            rb, rc = ref["blocks"][i], ref["cells"][i]
-            assert gn[i] == rc.size
-            assert np.array_equal(gb[i, :rb.size], rb)
-            assert np.array_equal(gc[i, :rc.size], rc)
-            worst = max(worst, float(np.abs(go[i] - ref["out"][i]).max()))
-        assert worst <= ATTN_TOL
-    say(f"  {name}: scores bit-exact {min(fracs):.6f}, worst attention error {worst:.2e}")
+        for path, out in outs.items():
+            gs = out.scores.cpu().numpy()[:, :w.nb_max(step)]
+            gb, gc = out.sel_blocks.cpu().numpy(), out.sel_cells.cpu().numpy()
+            gn, go = out.n_sel.cpu().numpy(), out.out.cpu().numpy()
+            for i in range(n_q):
+                fracs.append(check_scores(gs[i], ref["scores"][i]))
+                rb, rc = ref["blocks"][i], ref["cells"][i]
+                assert gn[i] == rc.size, path
+                assert np.array_equal(gb[i, :rb.size], rb), path
+                assert np.all(gb[i, rb.size:] == -1), path
+                assert np.array_equal(gc[i, :rc.size], rc), path
+                assert np.all(gc[i, rc.size:] == -1), path
+                worst = max(worst, float(np.abs(go[i] - ref["out"][i]).max()))
+            assert worst <= ATTN_TOL, path
+        # the call sequences run the same arithmetic: identical outputs
+        first = outs[paths[0]]
+        for path in paths[1:]:
+            assert np.array_equal(outs[path].out.cpu().numpy().view(np.uint32),
+                                  first.out.cpu().numpy().view(np.uint32)), path
+    say(f"  {name} ({', '.join(paths)}): scores bit-exact {min(fracs):.6f}, "
+        f"worst attention error {worst:.2e}")
     return w, layer
 
 
@@ -334,19 +349,20 @@ def test_invalid_queries_are_inert():
     q_pos = np.array([99, 10, 10, 50, -3], np.int32)  # 2nd..5th invalid
     n_q = q_seq.size
     t = lambda x: torch.from_numpy(x).to(DEV)
-    bufs = runtime.StepBuffers(layer.dims, n_q, 40, DEV)
-    bufs.out.fill_(7.0)
-    runtime.run_step(layer, bufs, t(synth.normal((n_q, w.d), 80, 0, 1)),
-                     t(synth.normal((n_q, w.H, w.D), 80, 0, 2)), t(q_seq), t(q_pos),
-                     None, 0)
-    torch.cuda.synchronize()
-    s = bufs.scores.cpu().numpy()[:, :40]
-    assert np.all(np.isfinite(s[0, :25])) and np.all(np.isneginf(s[0, 25:]))
-    assert np.all(np.isneginf(s[1:]))
-    n_sel = bufs.n_sel.cpu().numpy()
-    assert n_sel[0] == 16 * 4 and np.all(n_sel[1:] == 0)  # top_k 64: 16 blocks, no tail
-    assert np.all(bufs.sel_cells.cpu().numpy()[1:] == -1)
-    assert np.all(bufs.out.cpu().numpy()[1:] == 0.0)
+    for path in runtime.PATHS:
+        bufs = runtime.StepBuffers(layer.dims, n_q, 40, DEV)
+        bufs.out.fill_(7.0)
+        runtime.run_step(layer, bufs, t(synth.normal((n_q, w.d), 80, 0, 1)),
+                         t(synth.normal((n_q, w.H, w.D), 80, 0, 2)), t(q_seq), t(q_pos),
+                         None, 0, path=path)
+        torch.cuda.synchronize()
+        s = bufs.scores.cpu().numpy()[:, :40]
+        assert np.all(np.isfinite(s[0, :25])) and np.all(np.isneginf(s[0, 25:])), path
+        assert np.all(np.isneginf(s[1:])), path
+        n_sel = bufs.n_sel.cpu().numpy()
+        assert n_sel[0] == 16 * 4 and np.all(n_sel[1:] == 0), path  # top_k 64: 16 blocks
+        assert np.all(bufs.sel_cells.cpu().numpy()[1:] == -1), path
+        assert np.all(bufs.out.cpu().numpy()[1:] == 0.0), path
 
 
 def test_repeat_runs_are_bit_identical():
@@ -358,15 +374,16 @@ def test_repeat_runs_are_bit_identical():
     args = (t(synth.normal((n_q, w.d), 81, 0, 1)), t(synth.normal((n_q, w.H, w.D), 81, 0, 2)),
             t(np.zeros(n_q, np.int32)), t(np.array([3999, 2000, 17], np.int32)))
     outs = []
-    for _ in range(2):
+    for path in ("attend", "attend", "general"):  # twice, then another call sequence
         bufs = runtime.StepBuffers(layer.dims, n_q, 1000, DEV)
-        o = runtime.run_step(layer, bufs, *args, None, 0)
+        o = runtime.run_step(layer, bufs, *args, None, 0, path=path)
         torch.cuda.synchronize()
         # only columns < nb_max of the score rows are defined
         outs.append([x.cpu().numpy().copy()
                      for x in (o.scores[:, :1000], o.sel_cells, o.n_sel, o.out)])
-    for a, b in zip(*outs):
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 # --------------------------------------------------------------------------

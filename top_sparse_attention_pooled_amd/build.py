@@ -7,7 +7,9 @@ fp32 arithmetic must not be fused) and with packed fp32 instructions disabled.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -16,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqsa.so")
+# per-kernel VGPRs / scratch / occupancy reported by the compiler
+RESOURCES = os.path.join(BUILD, "resources.json")
 SOURCES = ["api.hip", "pooled.hip", "score.hip", "select.hip", "attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,20 +35,47 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\S+)")
+
+
+def _resources(stderr: str) -> dict:
+    """Kernel -> {VGPRs, AGPRs, scratch, occupancy, lds} from the compiler's
+    kernel-resource-usage remarks."""
+    out, cur = {}, None
+    keys = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+            "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+    for m in _REMARK.finditer(stderr):
+        k, v = m.group(1), m.group(2)
+        if k == "Function Name":
+            cur = out.setdefault(v, {})
+        elif cur is not None:
+            cur[keys[k]] = int(v)
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(jobs: int = 8) -> str:
     """Compile every source and link libqsa.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in results]
+    res = {k: v for _, r in results for k, v in r.items()}
+    with open(RESOURCES, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    spills = sorted(k for k, v in res.items() if v.get("scratch", 0) > 0)
+    if spills:  # a spilled register array turns a register-resident loop into memory traffic
+        print(f"warning: kernels using scratch memory: {spills}", file=sys.stderr)
     tmp = LIB + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared",
                         "-fPIC", "-o", tmp, *objs],

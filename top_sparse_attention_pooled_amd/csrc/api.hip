@@ -346,22 +346,24 @@ int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const fl
     return launched(e, "score_select_decode");
 }
 
-static int attn_common(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
-                       const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
-                       const void *v_cache_dev, const int32_t *sel_cells_dev,
-                       const int32_t *n_sel_dev, float *out_dev, void *ws_dev, size_t ws_bytes,
-                       void *stream, bool prefill) {
+// Validates the attention arguments and fills *a (sel_cells/n_sel may be
+// outputs of the same launch when check_sel is false).
+static int attn_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
+                     const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
+                     const void *v_cache_dev, const int32_t *sel_cells_dev,
+                     const int32_t *n_sel_dev, float *out_dev, void *ws_dev, size_t ws_bytes,
+                     bool prefill, qsa::AttnArgs *a) {
     int rc = check_dims(dims);
     if (!rc) rc = check_seqs(dims, seqs);
     if (!rc) rc = check_queries(q_seq_dev, nullptr, n_q, false);
     if (rc) return rc;
-    if (n_q == 0) return ok();
+    if (n_q == 0) return QSA_OK;
     if (!q_dev || !aligned(q_dev, 16)) return fail(QSA_EINVAL, "q_dev NULL or not 16-byte aligned");
     if (!out_dev || !aligned(out_dev, 4)) return fail(QSA_EINVAL, "out_dev NULL or misaligned");
     if (!k_cache_dev || !v_cache_dev || !aligned(k_cache_dev, 16) || !aligned(v_cache_dev, 16))
         return fail(QSA_EINVAL, "K/V cache NULL or not 16-byte aligned");
     if (!sel_cells_dev || !n_sel_dev || !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
-        return fail(QSA_EINVAL, "selection inputs NULL or misaligned");
+        return fail(QSA_EINVAL, "selection NULL or misaligned");
     const int ld_cells = dims->top_k + dims->r - 1;
     const size_t need = prefill ? qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells)
                                 : qsa::attn_decode_ws_bytes(n_q, dims->n_head, ld_cells);
@@ -369,10 +371,23 @@ static int attn_common(const qsa_dims *dims, const qsa_seqs *seqs, const float *
         return fail(QSA_EWS, "attention workspace needs %zu bytes, 16-byte aligned", need);
     const float scale =
         dims->kq_scale > 0.0f ? dims->kq_scale : 1.0f / sqrtf((float)dims->head_dim);
-    qsa::AttnArgs a{geom(seqs), q_dev,         q_seq_dev,     n_q,           dims->n_head,
-                    dims->n_head_kv, dims->kv_type, k_cache_dev, v_cache_dev, sel_cells_dev,
-                    n_sel_dev,      ld_cells,      scale,         out_dev,       (float *)ws_dev,
-                    ws_bytes};
+    *a = qsa::AttnArgs{geom(seqs), q_dev,         q_seq_dev,     n_q,           dims->n_head,
+                       dims->n_head_kv, dims->kv_type, k_cache_dev, v_cache_dev, sel_cells_dev,
+                       n_sel_dev,      ld_cells,      scale,         out_dev,       (float *)ws_dev,
+                       ws_bytes};
+    return QSA_OK;
+}
+
+static int attn_common(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
+                       const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
+                       const void *v_cache_dev, const int32_t *sel_cells_dev,
+                       const int32_t *n_sel_dev, float *out_dev, void *ws_dev, size_t ws_bytes,
+                       void *stream, bool prefill) {
+    qsa::AttnArgs a;
+    const int rc = attn_args(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
+                             sel_cells_dev, n_sel_dev, out_dev, ws_dev, ws_bytes, prefill, &a);
+    if (rc) return rc;
+    if (n_q == 0) return ok();
     hipError_t e = prefill ? qsa::launch_attn_prefill(a, (hipStream_t)stream)
                            : qsa::launch_attn_decode(a, (hipStream_t)stream);
     return launched(e, prefill ? "sparse_attn_prefill" : "sparse_attn_decode");
@@ -394,6 +409,32 @@ int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const fl
                             size_t ws_bytes, void *stream) {
     return attn_common(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
                        sel_cells_dev, n_sel_dev, out_dev, ws_dev, ws_bytes, stream, true);
+}
+
+int qsa_decode_select_attend(const qsa_dims *dims, const qsa_seqs *seqs,
+                             const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                             int32_t nb_max, const float *scores_dev, int64_t ld_scores,
+                             int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                             int32_t *n_sel_dev, const void *ws_idx_dev, size_t ws_idx_bytes,
+                             const float *q_dev, const void *k_cache_dev,
+                             const void *v_cache_dev, float *out_dev, void *ws_attn_dev,
+                             size_t ws_attn_bytes, void *stream) {
+    qsa::DecodeIdxArgs f;
+    int rc = decode_idx_args(dims, seqs, nullptr, nullptr, 0, nullptr, nullptr, nullptr,
+                             q_seq_dev, q_pos_dev, n_q, nb_max, (float *)scores_dev, ld_scores,
+                             sel_blocks_dev, sel_cells_dev, n_sel_dev, (void *)ws_idx_dev,
+                             ws_idx_bytes, false, true, &f);
+    if (rc) return rc;
+    if (nb_max > qsa::kSelAttnMaxBlocks)
+        return fail(QSA_ENOTSUP, "nb_max %d above %d: use the separate calls", nb_max,
+                    qsa::kSelAttnMaxBlocks);
+    qsa::AttnArgs a;
+    rc = attn_args(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev, sel_cells_dev,
+                   n_sel_dev, out_dev, ws_attn_dev, ws_attn_bytes, false, &a);
+    if (rc) return rc;
+    if (n_q == 0) return ok();
+    return launched(qsa::launch_select_attn_decode(f, (void *)ws_idx_dev, a, (hipStream_t)stream),
+                    "decode_select_attend");
 }
 
 }  // extern "C"

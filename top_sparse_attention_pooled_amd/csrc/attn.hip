@@ -4,23 +4,26 @@
 // the compact-gather path that keeps a quantised cache on the sparse path,
 // where converting the whole cache first would cost O(n_kv)).
 //
-// Work unit: one workgroup = one (query, KV head, run of cells).  Its 256
-// threads are 8 groups of 32; lane j of a group owns dims 8j .. 8j+7 of the
-// head and all G query heads that share the KV head, so each K/V row is read
-// once from memory and feeds G heads.  A decode workgroup takes one 32-cell
-// chunk (130 workgroups for a 2051-cell set over 2 KV heads) and issues every
-// index, K and V load before it uses any.  Per chunk: the groups score
-// their cells (G dot products reduced over 32 lanes with a transposing
-// butterfly: 9 shuffles for 8 heads), the chunk's softmax statistics come
-// from one wavefront per head, and the groups accumulate P*V; across chunks
-// the running (max, sum, output) are rescaled once per chunk.  Decode splits a
-// query's cells over many workgroups and merges their partial states in a
-// second kernel; prefill gives each workgroup all cells of its query.
+// Work unit: one workgroup = one (query, run of cells, pair of query heads
+// that share a KV head).  Its 256 threads are 8 groups of 32; lane j of a
+// group owns dims 8j .. 8j+7 of both heads.  A decode workgroup takes one
+// 32-cell chunk (a 2051-cell set and 16 query heads make 65 x 8 = 520
+// workgroups, two wavefronts per SIMD) and issues every index, K and V load
+// before it uses any; the workgroups of one chunk run on one XCD, so its K/V
+// rows cross HBM once.  Per chunk: the groups score their cells (dot products
+// reduced over 32 lanes with a transposing butterfly), the chunk's softmax
+// statistics come from one half-wavefront per head, and the groups
+// accumulate P*V; across chunks the running (max, sum, output) are rescaled
+// once per chunk.  Decode splits a query's cells over many workgroups and
+// merges their partial states in a second kernel; prefill gives each
+// workgroup all cells of its query.
 //
 // q8_0 rows: 8 blocks of (binary16 scale, 32 int8) = 272 bytes.  A lane's
 // 8 int8 start at byte 34*(j/4) + 2 + 8*(j%4), which is 2 mod 4 for even
 // blocks: they are read as aligned dwords and realigned with a funnel shift.
+#include "cand_select.h"
 #include "qsa_internal.h"
+#include "wave_ops.h"
 
 namespace qsa {
 
@@ -87,27 +90,51 @@ __device__ __forceinline__ void dequant(const RawRow<KVT> &r, int j, float (&x)[
 // Sum v[0..G) over the 32 lanes of a group.  On return lane j holds the full
 // sum for head head_of_lane<G>(j) in v[0]: each halving step exchanges half
 // of the remaining values, so 8 heads cost 4+2+1+1+1 shuffles, not 8*5.
+template <int G, int O>
+__device__ __forceinline__ void group_reduce_step(float (&v)[G], int &n) {
+    if (n > 1) {
+        const int half = n >> 1;
+        const bool upper = (threadIdx.x & O) != 0;
+#pragma unroll
+        for (int h = 0; h < G / 2; ++h) {
+            if (h < half) {
+                const float keep = upper ? v[h + half] : v[h];
+                const float send = upper ? v[h] : v[h + half];
+                v[h] = keep + xor_lane_f<O>(send);
+            }
+        }
+        n = half;
+    } else {
+        v[0] = v[0] + xor_lane_f<O>(v[0]);
+    }
+}
+
 template <int G>
 __device__ __forceinline__ void group_reduce(float (&v)[G]) {
     int n = G;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-        if (n > 1) {
-            const int half = n >> 1;
-            const bool upper = (threadIdx.x & o) != 0;
-#pragma unroll
-            for (int h = 0; h < G / 2; ++h) {
-                if (h < half) {
-                    const float keep = upper ? v[h + half] : v[h];
-                    const float send = upper ? v[h] : v[h + half];
-                    v[h] = keep + __shfl_xor(send, o, kWave);
-                }
-            }
-            n = half;
-        } else {
-            v[0] = v[0] + __shfl_xor(v[0], o, kWave);
-        }
-    }
+    group_reduce_step<G, 16>(v, n);
+    group_reduce_step<G, 8>(v, n);
+    group_reduce_step<G, 4>(v, n);
+    group_reduce_step<G, 2>(v, n);
+    group_reduce_step<G, 1>(v, n);
+}
+
+// Max / sum over the 32 lanes of a half-wavefront.
+__device__ __forceinline__ float half_max(float v) {
+    v = fmaxf(v, xor_lane_f<16>(v));
+    v = fmaxf(v, xor_lane_f<8>(v));
+    v = fmaxf(v, xor_lane_f<4>(v));
+    v = fmaxf(v, xor_lane_f<2>(v));
+    v = fmaxf(v, xor_lane_f<1>(v));
+    return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+    v += xor_lane_f<16>(v);
+    v += xor_lane_f<8>(v);
+    v += xor_lane_f<4>(v);
+    v += xor_lane_f<2>(v);
+    v += xor_lane_f<1>(v);
+    return v;
 }
 
 template <int G>
@@ -133,34 +160,35 @@ __device__ __forceinline__ bool lane_reports(int j) {
     return (j & ~bits & 31) == 0;
 }
 
-// grid (n_runs, n_head_kv, n_q).  Workgroup x covers chunks
-// [x*chunks_per_run, (x+1)*chunks_per_run) of the query's selected list.
-// direct != 0: one run covers all cells, write the normalised output;
-// otherwise write the partial state (o[G][256], m[G], l[G]) to ws.
-template <int G, int KVT>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, int n_runs,
-                                              int direct) {
-    __shared__ float s_p[G][kChunk];
-    __shared__ float s_red[kGroups][G * kHeadDim];
-    __shared__ float s_stat[G][2];  // chunk max, chunk sum
+template <int G>
+struct AttnSmem {
+    float p[G][kChunk];
+    float red[kGroups][G * kHeadDim];
+    float stat[G][2];  // chunk max, chunk sum
+};
 
-    const int run = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
-    const int tid = threadIdx.x, grp = tid >> 5, j = tid & 31, wave = tid >> 6,
-              lane = tid & 63;
-    const int h0 = g * G;
-    const int c_begin = run * chunks_per_run * kChunk;
-    const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
+// Workgroup -> unit (query i, run of chunks, group hg of G heads), head group
+// fastest; the G heads share one KV head.  The hardware deals workgroup ids
+// to the 8 XCDs round-robin (id mod 8), and each XCD has its own L2, so the
+// 1-D grid gives XCD x the contiguous unit range [x*per, (x+1)*per): the head
+// groups of one (query, run), which read the same K/V rows, then share an L2
+// and the rows come from HBM once.  Returns false for the padding ids.
+__device__ __forceinline__ bool unit_of(int n_q, int n_runs, int n_hg, int &i, int &run,
+                                        int &hg) {
+    const int total = n_q * n_runs * n_hg;
+    const int per = (total + 7) >> 3;  // units per XCD; the grid is 8*per
+    const int unit = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (unit >= total) return false;
+    hg = unit % n_hg;
+    run = (unit / n_hg) % n_runs;
+    i = unit / (n_hg * n_runs);
+    return true;
+}
 
-    // first round trip: nothing here depends on another load
-    const int s = a.q_seq[i];
-    const int n_raw = a.n_sel[i];
-    int cell[kCPG];
-#pragma unroll
-    for (int u = 0; u < kCPG; ++u) {
-        const int cc = c_begin + grp * kCPG + u;
-        cell[u] = cc < a.ld_cells ? cells[cc] : -1;
-    }
-    float qv[G][8];
+// Lane j's slice (dims 8j .. 8j+7) of query i's heads h0 .. h0+G-1.
+template <int G>
+__device__ __forceinline__ void load_q(const AttnArgs &a, int i, int h0, int j,
+                                       float (&qv)[G][8]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const float4 *qp = reinterpret_cast<const float4 *>(
@@ -169,10 +197,24 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
         qv[h][0] = u.x; qv[h][1] = u.y; qv[h][2] = u.z; qv[h][3] = u.w;
         qv[h][4] = v.x; qv[h][5] = v.y; qv[h][6] = v.z; qv[h][7] = v.w;
     }
-    const bool qvalid = s >= 0 && s < a.g.n_seq;
-    const int n = qvalid ? (n_raw < 0 ? 0 : (n_raw > a.ld_cells ? a.ld_cells : n_raw)) : 0;
-    const int c_end = min(n, c_begin + chunks_per_run * kChunk);
+}
 
+// Attention of query i (sequence s), heads h0.. (KV head g), over positions
+// [c_begin, c_end) of its cell list, one 32-cell chunk at a time, by the 256
+// threads of one quarter (threadIdx.x / 256) of the workgroup; every quarter
+// of the workgroup calls it with the same c_begin, c_end (it has workgroup
+// barriers).  cell[] holds this thread's cells of the first chunk (positions
+// c_begin + grp*4 + u); later chunks read theirs from `cells` (global).
+// active: write results (false for an idle quarter).  direct: write the
+// normalised output; else the partial state (o[G][256], m[G], l[G]) to part.
+template <int G, int KVT>
+__device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, int g, int h0,
+                                              int c_begin, int c_end, int (&cell)[kCPG],
+                                              const int32_t *cells, const float (&qv)[G][8],
+                                              AttnSmem<G> &sm, float *part, bool direct,
+                                              bool active) {
+    const int tid = threadIdx.x & 255, grp = tid >> 5, j = tid & 31, wave = tid >> 6,
+              lane = tid & 63;
     float m_run[G], l_run[G], o[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -193,8 +235,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
                     cell[u] = cc < a.ld_cells ? cells[cc] : -1;
                 }
             }
-            // second round trip: K/V rows (memory safety needs only
-            // 0 <= cell < cap_cells) and the present-cell count
+            // K/V rows (memory safety needs only 0 <= cell < cap_cells) and
+            // the present-cell count
             RawRow<KVT> rk[kCPG], rv[kCPG];
 #pragma unroll
             for (int u = 0; u < kCPG; ++u) {
@@ -228,7 +270,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
                 }
                 group_reduce<G>(sv);
                 if (cc < c1 && lane_reports<G>(j))
-                    s_p[head_of_lane<G>(j)][cc - c0] = ok ? sv[0] * a.scale : -INFINITY;
+                    sm.p[head_of_lane<G>(j)][cc - c0] = ok ? sv[0] * a.scale : -INFINITY;
             }
             __syncthreads();
             // chunk statistics: 32 lanes per head, two heads per wavefront
@@ -237,28 +279,24 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
                 if (((h >> 1) & 3) != wave || ((h & 1) != (lane >> 5))) continue;
                 const int c = lane & 31;
                 const bool in = c0 + c < c1;
-                const float x = in ? s_p[h][c] : -INFINITY;
-                float mx = x;
-#pragma unroll
-                for (int o2 = 16; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, kWave));
+                const float x = in ? sm.p[h][c] : -INFINITY;
+                const float mx = half_max(x);
                 const float m_new = fmaxf(m_run[h], mx);  // m_run equal in every thread
                 const float pe = (in && x != -INFINITY) ? __expf(x - m_new) : 0.f;
-                float sum = pe;
-#pragma unroll
-                for (int o2 = 16; o2 >= 1; o2 >>= 1) sum += __shfl_xor(sum, o2, kWave);
-                s_p[h][c] = pe;
+                const float sum = half_sum(pe);
+                sm.p[h][c] = pe;
                 if (c == 0) {
-                    s_stat[h][0] = m_new;
-                    s_stat[h][1] = sum;
+                    sm.stat[h][0] = m_new;
+                    sm.stat[h][1] = sum;
                 }
             }
             __syncthreads();
             // rescale the running state, then accumulate P*V
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float m_new = s_stat[h][0];
+                const float m_new = sm.stat[h][0];
                 const float corr = m_run[h] == -INFINITY ? 0.f : __expf(m_run[h] - m_new);
-                l_run[h] = l_run[h] * corr + s_stat[h][1];
+                l_run[h] = l_run[h] * corr + sm.stat[h][1];
                 m_run[h] = m_new;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[h][e] *= corr;
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
                 dequant<KVT>(rv[u], j, vf);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const float pw = s_p[h][cc - c0];
+                    const float pw = sm.p[h][cc - c0];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pw, vf[e], o[h][e]);
                 }
@@ -285,16 +323,15 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_red[grp][h * kHeadDim + 8 * j + e] = o[h][e];
+        for (int e = 0; e < 8; ++e) sm.red[grp][h * kHeadDim + 8 * j + e] = o[h][e];
     __syncthreads();
-    float *part = a.ws + (((int64_t)i * a.n_head_kv + g) * n_runs + run) *
-                             (G * kHeadDim + 2 * G);
+    if (!active) return;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const int t = h * kHeadDim + tid;  // 256 threads = 256 dims
-        float acc = s_red[0][t];
+        float acc = sm.red[0][t];
 #pragma unroll
-        for (int q = 1; q < kGroups; ++q) acc += s_red[q][t];
+        for (int q = 1; q < kGroups; ++q) acc += sm.red[q][t];
         if (direct) {
             const float l = l_run[h];
             a.out[((int64_t)i * a.n_head + h0 + h) * kHeadDim + tid] = l > 0.f ? acc / l : 0.f;
@@ -308,21 +345,186 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     }
 }
 
+// Partial state of (query i, head group hg, run) in the decode workspace.
+template <int G>
+__device__ __forceinline__ float *partial_of(const AttnArgs &a, int i, int hg, int run,
+                                             int n_runs) {
+    return a.ws + (((int64_t)i * (a.n_head / G) + hg) * n_runs + run) * (G * kHeadDim + 2 * G);
+}
+
+// Attention over a given cell list: one workgroup per unit (see unit_of);
+// a decode run is one chunk, a prefill run all of the query's chunks.
+template <int G, int KVT>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, int n_runs,
+                                              int direct) {
+    __shared__ AttnSmem<G> sm;
+    const int n_hg = a.n_head / G;
+    int i, run, hg;
+    if (!unit_of(a.n_q, n_runs, n_hg, i, run, hg)) return;
+    const int hpk = a.n_head / a.n_head_kv;  // query heads per KV head
+    const int g = (hg * G) / hpk;            // the KV head
+    const int h0 = hg * G;
+    const int grp = threadIdx.x >> 5, j = threadIdx.x & 31;
+    const int c_begin = run * chunks_per_run * kChunk;
+    const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
+
+    // first round trip: nothing here depends on another load
+    const int s = a.q_seq[i];
+    const int n_raw = a.n_sel[i];
+    int cell[kCPG];
+#pragma unroll
+    for (int u = 0; u < kCPG; ++u) {
+        const int cc = c_begin + grp * kCPG + u;
+        cell[u] = cc < a.ld_cells ? cells[cc] : -1;
+    }
+    float qv[G][8];
+    load_q<G>(a, i, h0, j, qv);
+    const bool qvalid = s >= 0 && s < a.g.n_seq;
+    const int n = qvalid ? (n_raw < 0 ? 0 : (n_raw > a.ld_cells ? a.ld_cells : n_raw)) : 0;
+    const int c_end = min(n, c_begin + chunks_per_run * kChunk);
+    attend_chunks<G, KVT>(a, i, s, g, h0, c_begin, c_end, cell, cells, qv, sm,
+                          direct ? nullptr : partial_of<G>(a, i, hg, run, n_runs), direct != 0,
+                          true);
+}
+
+constexpr int kSelAttnNT = 1024;
+constexpr int kQuarters = kSelAttnNT / 256;
+
+// Decode selection fused with attention.  Workgroup = (query i, run of 32
+// cells, set of 4 head groups); quarter q (256 threads) attends for head
+// group 4*set + q, so for 16 heads over 2 KV heads the 4 quarters share one
+// KV head and each K/V row is fetched once per workgroup.  First the whole
+// workgroup derives query i's exact kept set from the candidates (the kept
+// set is unique, so all workgroups derive the same), then finds the cells at
+// positions [32*run, 32*run + 32) of the ascending cell list -- blocks by
+// rank through a prefix count over the bitmap, then the tail cells -- and
+// the quarters attend over them.  The workgroup of (run 0, set 0) also
+// writes the selection outputs.  Cells, outputs and partial states equal
+// those of the selection kernel followed by k_attn.
+template <int G, int KVT>
+__global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnArgs a,
+                                                         int n_runs) {
+    __shared__ CandSelSmem<kSelAttnNT, kSelAttnMaxBlocks> ss;
+    __shared__ AttnSmem<G> sm[kQuarters];
+    __shared__ int s_cells[kChunk];
+    const int n_hg = a.n_head / G;
+    const int n_set = (n_hg + kQuarters - 1) / kQuarters;
+    // workgroup -> (query, run, set), set fastest
+    const int set = blockIdx.x % n_set;
+    const int run = (blockIdx.x / n_set) % n_runs;
+    const int i = blockIdx.x / (n_set * n_runs);
+    const int tid = threadIdx.x, quarter = tid >> 8, lt = tid & 255;
+    const int grp = lt >> 5, j = lt & 31;
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+    const int hg_raw = set * kQuarters + quarter;
+    const bool active = hg_raw < n_hg;
+    const int hg = active ? hg_raw : n_hg - 1;  // an idle quarter mirrors a real one
+    const int hpk = a.n_head / a.n_head_kv;
+    const int g = (hg * G) / hpk;
+    const int h0 = hg * G;
+    float qv[G][8];
+    load_q<G>(a, i, h0, j, qv);
+
+    const ScoreArgs &sa = f.s;
+    int s;
+    int64_t p;
+    bool valid;
+    const int64_t nc = query_blocks(sa.q_seq, sa.q_pos, i, sa.g.n_seq, sa.g.cap_cells,
+                                    sa.g.n_cells, sa.r, s, p, valid);
+    const int64_t limit = nc < sa.nb_max ? nc : sa.nb_max;
+    const int r = sa.r;
+    const int B = f.top_k / r;
+    const int tail = valid ? (int)(p + 1 - nc * r) : 0;
+    select_candidates<kSelAttnNT, kSelAttnMaxBlocks>(f, i, limit, B, ss);
+
+    // ranks of this thread's bitmap words
+    const int n_words = (int)((limit + 31) / 32);
+    const int per = (n_words + kSelAttnNT - 1) / kSelAttnNT;
+    const int w0 = tid * per;
+    uint32_t local = 0;
+    for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(ss.bitmap[w]);
+    const uint32_t incl = wave_incl_scan_u32(local);
+    if (lane == kWave - 1) ss.tk.red[wave] = incl;
+    __syncthreads();
+    uint32_t rank = incl - local, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelAttnNT / kWave; ++w) {
+        if (w < wave) rank += ss.tk.red[w];
+        total += ss.tk.red[w];
+    }
+    const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+    const int n_sel = n_keep * r + tail;
+    const int c_begin = run * kChunk;
+    // list positions [c_begin, c_begin + 32): kept blocks of rank
+    // [c_begin / r, (c_begin + 31) / r], then tail cells, then -1
+    const int k_lo = c_begin / r, k_hi = (c_begin + kChunk - 1) / r;
+    if (local && (int)rank <= k_hi && (int)(rank + local) > k_lo) {
+        uint32_t k = rank;
+        for (int w = w0; w < w0 + per && w < n_words; ++w) {
+            uint32_t bits = ss.bitmap[w];
+            while (bits) {
+                const int bit = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if ((int)k >= k_lo && (int)k <= k_hi && (int)k < n_keep) {
+                    const int b = w * 32 + bit;
+                    for (int c = 0; c < r; ++c) {
+                        const int pos = (int)k * r + c - c_begin;
+                        if (pos >= 0 && pos < kChunk) s_cells[pos] = b * r + c;
+                    }
+                }
+                ++k;
+            }
+        }
+    }
+    if (tid < kChunk) {
+        const int pos = c_begin + tid;
+        if (pos >= n_keep * r)
+            s_cells[tid] = pos < n_sel ? (int)(nc * r + (pos - n_keep * r)) : -1;
+    }
+    __syncthreads();
+    if (run == 0 && set == 0) {
+        const int ld_cells = f.top_k + r - 1;
+        emit_from_bitmap<kSelAttnNT>(ss.bitmap, n_words, B, r, nc, tail,
+                                     f.sel_blocks + (int64_t)i * B,
+                                     f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i,
+                                     ss.tk);
+    }
+    int cell[kCPG];
+#pragma unroll
+    for (int u = 0; u < kCPG; ++u) cell[u] = s_cells[grp * kCPG + u];
+    const int c_end = min(n_sel, c_begin + kChunk);
+    attend_chunks<G, KVT>(a, i, s, g, h0, c_begin, c_end, cell, nullptr, qv, sm[quarter],
+                          partial_of<G>(a, i, hg, run, n_runs), false, active);
+}
+
 constexpr int kCombNT = 1024;
 constexpr int kCombGroups = kCombNT / 128;  // run groups x 128 dim pairs
 
 // grid (n_head, n_q).  Merges the runs' partial states of one head: thread
 // (rg, dp) sums runs rg, rg+8, ... for dims 2dp, 2dp+1; the 8 partial sums
-// are then added in a fixed order.
+// are then added in a fixed order.  The first kPre runs of each thread are
+// loaded together with the (m, l) pairs, before the weights are known (every
+// run's partial is written, zeros for a run that saw no cell), so a decode
+// set of up to 8*kPre runs costs one memory round trip.  n_runs <= 1024.
 template <int G>
 __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs) {
+    constexpr int kPre = 9;
     __shared__ float s_w[1024];
     __shared__ float s_red[32];
     __shared__ float2 s_acc[kCombGroups][128];
     const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
-    const int g = h / G, hh = h % G;
+    const int hg = h / G, hh = h % G;
     const int stride = G * kHeadDim + 2 * G;
-    const float *base = a.ws + ((int64_t)i * a.n_head_kv + g) * n_runs * stride;
+    const float *base = a.ws + ((int64_t)i * (a.n_head / G) + hg) * n_runs * stride;
+    const int rg = tid >> 7, dp = tid & 127;
+    float2 pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int r = rg + u * kCombGroups;
+        pre[u] = r < n_runs ? *reinterpret_cast<const float2 *>(base + (int64_t)r * stride +
+                                                                hh * kHeadDim + 2 * dp)
+                            : make_float2(0.f, 0.f);
+    }
     // per-run weights exp(m_r - M), M = max over runs that saw any cell
     float m = -INFINITY, l = 0.f;
     if (tid < n_runs) {
@@ -330,9 +532,7 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
         l = base[(int64_t)tid * stride + G * kHeadDim + G + hh];
         if (!(l > 0.f)) m = -INFINITY;
     }
-    float mx = m;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float mx = wave_max_f32(m);
     if ((tid & 63) == 0) s_red[tid >> 6] = mx;
     __syncthreads();
     float M = s_red[0];
@@ -342,28 +542,37 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
     const float wgt = (m != -INFINITY) ? __expf(m - M) : 0.f;
     if (tid < n_runs) s_w[tid] = wgt;
     float lw = l > 0.f ? l * wgt : 0.f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lw += __shfl_xor(lw, o, kWave);
+    lw += xor_lane_f<1>(lw);
+    lw += xor_lane_f<2>(lw);
+    lw += xor_lane_f<4>(lw);
+    lw += xor_lane_f<8>(lw);
+    lw += xor_lane_f<16>(lw);
+    lw += xor_lane_f<32>(lw);
     if ((tid & 63) == 0) s_red[tid >> 6] = lw;
     __syncthreads();
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kCombNT / 64; ++w) L += s_red[w];
 
-    const int rg = tid >> 7, dp = tid & 127;
     float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int r = rg + u * kCombGroups;
+        const float w = r < n_runs ? s_w[r] : 0.f;
+        acc.x = fmaf(pre[u].x, w, acc.x);
+        acc.y = fmaf(pre[u].y, w, acc.y);
+    }
     constexpr int U = 8;
-    for (int r0 = rg; r0 < n_runs; r0 += kCombGroups * U) {
+    for (int r0 = rg + kPre * kCombGroups; r0 < n_runs; r0 += kCombGroups * U) {
         float2 v[U];
         float w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * kCombGroups;
             w[u] = r < n_runs ? s_w[r] : 0.f;
-            v[u] = (r < n_runs && w[u] != 0.f)
-                       ? *reinterpret_cast<const float2 *>(base + (int64_t)r * stride +
-                                                           hh * kHeadDim + 2 * dp)
-                       : make_float2(0.f, 0.f);
+            v[u] = r < n_runs ? *reinterpret_cast<const float2 *>(base + (int64_t)r * stride +
+                                                                  hh * kHeadDim + 2 * dp)
+                              : make_float2(0.f, 0.f);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -388,8 +597,10 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
 template <int G, int KVT>
 hipError_t launch_g(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct,
                     hipStream_t st) {
-    dim3 grid(n_runs, a.n_head_kv, a.n_q);
-    hipLaunchKernelGGL((k_attn<G, KVT>), grid, dim3(256), 0, st, a, chunks_per_run, n_runs,
+    // 8 equal unit ranges, one per XCD (k_attn maps ids to units)
+    const int units = a.n_q * (a.n_head / G) * n_runs;
+    const int grid = (units + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_attn<G, KVT>), dim3(grid), dim3(256), 0, st, a, chunks_per_run, n_runs,
                        direct ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
@@ -398,16 +609,15 @@ hipError_t launch_g(const AttnArgs &a, int chunks_per_run, int n_runs, bool dire
     return hipGetLastError();
 }
 
+// Heads per workgroup: 2 (enough workgroups to give every SIMD two
+// wavefronts on a single decode query, and a quarter of the registers of 8);
+// it must divide the query heads per KV head.
 template <int KVT>
 hipError_t launch_kvt(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct,
                       hipStream_t st) {
-    switch (a.n_head / a.n_head_kv) {
-        case 1: return launch_g<1, KVT>(a, chunks_per_run, n_runs, direct, st);
-        case 2: return launch_g<2, KVT>(a, chunks_per_run, n_runs, direct, st);
-        case 4: return launch_g<4, KVT>(a, chunks_per_run, n_runs, direct, st);
-        case 8: return launch_g<8, KVT>(a, chunks_per_run, n_runs, direct, st);
-        default: return hipErrorInvalidValue;
-    }
+    const int hpk = a.n_head / a.n_head_kv;
+    if (hpk % 2 == 0) return launch_g<2, KVT>(a, chunks_per_run, n_runs, direct, st);
+    return launch_g<1, KVT>(a, chunks_per_run, n_runs, direct, st);
 }
 
 hipError_t launch(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct,
@@ -419,16 +629,44 @@ hipError_t launch(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct
 
 int decode_runs(int ld_cells) { return (ld_cells + kChunk - 1) / kChunk; }
 
+template <int G, int KVT>
+hipError_t launch_sel_g(const DecodeIdxArgs &f, const AttnArgs &a, hipStream_t st) {
+    const int n_runs = decode_runs(a.ld_cells);
+    const int n_set = (a.n_head / G + kQuarters - 1) / kQuarters;
+    const int grid = a.n_q * n_runs * n_set;
+    hipLaunchKernelGGL((k_sel_attn<G, KVT>), dim3(grid), dim3(kSelAttnNT), 0, st, f, a, n_runs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head, a.n_q), dim3(kCombNT), 0, st, a,
+                       n_runs);
+    return hipGetLastError();
+}
+
+template <int KVT>
+hipError_t launch_sel_kvt(const DecodeIdxArgs &f, const AttnArgs &a, hipStream_t st) {
+    const int hpk = a.n_head / a.n_head_kv;
+    if (hpk % 2 == 0) return launch_sel_g<2, KVT>(f, a, st);
+    return launch_sel_g<1, KVT>(f, a, st);
+}
+
 }  // namespace
 
 size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells) {
-    // per (query, KV head, run): G*256 + 2G floats; summed over KV heads this
-    // is n_head*(256 + 2) floats per run
+    // per (query, run, head group): G*256 + 2G floats; over the head groups
+    // this is n_head*(256 + 2) floats per run
     return (size_t)n_q * decode_runs(ld_cells) * n_head * (kHeadDim + 2) * sizeof(float);
 }
 
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st) {
     return launch(a, 1, decode_runs(a.ld_cells), false, st);
+}
+
+hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnArgs &a,
+                                     hipStream_t st) {
+    if (a.n_q <= 0) return hipSuccess;
+    bind_candidates(f, ws_idx);
+    return a.kv_type == QSA_KV_F32 ? launch_sel_kvt<QSA_KV_F32>(f, a, st)
+                                   : launch_sel_kvt<QSA_KV_Q8_0>(f, a, st);
 }
 
 size_t attn_prefill_ws_bytes(int, int, int) { return 0; }

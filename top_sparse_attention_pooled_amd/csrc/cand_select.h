@@ -1,0 +1,179 @@
+// cand_select.h -- exact block top-k of one decode query from the scoring
+// kernel's candidates (llama.cpp issue #28734, fix summary, "lever3": whole
+// blocks compete, ranked by score with ties to the lower block).
+//
+// The scoring kernel leaves, for every group of 64 blocks (one wavefront's
+// tile), the group's 4 largest 64-bit keys (score key << 32 | ~block) and the
+// largest key it dropped.  The selection takes the top-B threshold over the
+// candidates; a group whose dropped key would itself be kept under that
+// threshold may hold more winners, so all 64 of its keys are re-admitted (or,
+// past 32 such groups, the whole score row is streamed) and the threshold is
+// taken again.  A dropped key of any other group lies below the first
+// threshold, which can only rise as keys are added, so the final kept set is
+// the exact top-B of all scores.
+//
+// The same routine runs in a 1024-thread selection workgroup and inside each
+// 256-thread attention workgroup; the kept set is unique, so every caller
+// derives the same one.
+#pragma once
+
+#include "topk_engine.h"
+
+namespace qsa {
+
+constexpr int kGroup = kTile;   // blocks per candidate group (one wavefront)
+constexpr int kCand = 4;        // keys kept per group
+constexpr int kMaxExpand = 32;  // groups re-admitted whole before streaming
+
+// Workspace of the decode indexer: cand [n_q][groups][4], then drop
+// [n_q][groups], groups = 4 per 256 blocks of nb_max.
+__host__ __device__ inline int cand_groups(int nb_max) { return (nb_max + 255) / 256 * 4; }
+
+inline size_t cand_ws_bytes(int n_q, int nb_max) {
+    return (size_t)n_q * cand_groups(nb_max) * (kCand + 1) * sizeof(uint64_t);
+}
+
+inline void bind_candidates(DecodeIdxArgs &f, void *ws) {
+    f.n_wg = (f.s.nb_max + 255) / 256;
+    f.cand = static_cast<uint64_t *>(ws);
+    f.drop = f.cand + (size_t)f.s.n_q * cand_groups(f.s.nb_max) * kCand;
+}
+
+// The candidate keys of one query in registers, for up to MAXB blocks: base
+// slot s holds candidate s*NT + tid, expansion slot e holds key e*NT + tid of
+// the re-admitted groups' keys (group over[x] at x = (e*NT + tid) / 64).
+// nb / ne: slots in use (workgroup-uniform), so unused slots cost one scalar
+// branch.
+template <int NT, int MAXB>
+struct CandKeys {
+    static constexpr int kBase = MAXB / kGroup * kCand / NT;
+    static constexpr int kExp = kMaxExpand * kGroup / NT;
+    uint64_t k[kBase + kExp];
+    int nb, ne;
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+        // (a guarded body, not an early exit: an exit would turn the loop
+        // into a runtime-count loop that indexes k[] dynamically)
+#pragma unroll
+        for (int s = 0; s < kBase; ++s)
+            if (s < nb) fn((uint32_t)(k[s] >> 32), (uint32_t)k[s]);
+#pragma unroll
+        for (int s = 0; s < kExp; ++s)
+            if (s < ne) fn((uint32_t)(k[kBase + s] >> 32), (uint32_t)k[kBase + s]);
+    }
+};
+
+template <int NT, int MAXB>
+struct CandSelSmem {
+    TopkSmem<NT> tk;
+    uint32_t bitmap[MAXB / 32];
+    int n_over;
+    int over[kMaxExpand];
+};
+
+// Marks the exact top-B blocks among query i's scored blocks [0, limit) in
+// sm.bitmap (words [0, ceil(limit/32)) all written).  Needs nb_max <= MAXB.
+// Workgroup-uniform; ends with a barrier.
+template <int NT, int MAXB>
+__device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i, int64_t limit,
+                                                  int B, CandSelSmem<NT, MAXB> &sm) {
+    const int tid = threadIdx.x;
+    const int n_grp = cand_groups(f.s.nb_max);
+    const int64_t qbase = (int64_t)i * n_grp;
+    const float *srow = f.s.scores + (int64_t)i * f.s.ld;
+    const int n_words = (int)((limit + 31) / 32);
+    for (int w = tid; w < n_words; w += NT) sm.bitmap[w] = 0;
+
+    using Keys = CandKeys<NT, MAXB>;
+    Keys ck;
+    const int n_cand = n_grp * kCand;
+    ck.nb = (n_cand + NT - 1) / NT;
+    ck.ne = 0;
+#pragma unroll
+    for (int s = 0; s < Keys::kBase; ++s) {
+        const int fi = tid + NT * s;
+        ck.k[s] = (s < ck.nb && fi < n_cand) ? f.cand[qbase * kCand + fi] : 0ull;
+    }
+#pragma unroll
+    for (int s = 0; s < Keys::kExp; ++s) ck.k[Keys::kBase + s] = 0ull;
+    // largest dropped key of each group, fetched with the keys
+    constexpr int kDrop = MAXB / kGroup / NT;
+    static_assert(kDrop >= 1, "drop slots");
+    uint64_t drop[kDrop];
+#pragma unroll
+    for (int q = 0; q < kDrop; ++q) {
+        const int g = tid + NT * q;
+        drop[q] = g < n_grp ? f.drop[qbase + g] : 0ull;
+    }
+    auto from_memory = [&](auto &&fn) {
+        constexpr int U = 16;
+        for (int64_t base = 0; base < limit; base += (int64_t)NT * U) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t bb = base + (int64_t)u * NT + tid;
+                v[u] = bb < limit ? srow[bb] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t bb = base + (int64_t)u * NT + tid;
+                if (bb < limit) fn(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)bb);
+            }
+        }
+    };
+    if (tid == 0) sm.n_over = 0;
+    Thresh th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
+
+#pragma unroll
+    for (int q = 0; q < kDrop; ++q) {
+        const uint64_t d = drop[q];
+        if (d != 0 && th.keep((uint32_t)(d >> 32), (uint32_t)d)) {
+            const int at = atomicAdd(&sm.n_over, 1);
+            if (at < kMaxExpand) sm.over[at] = tid + NT * q;
+        }
+    }
+    __syncthreads();
+    const int n_over = sm.n_over;
+    const bool stream = n_over > kMaxExpand;
+    if (stream) {
+        th = topk_threshold<NT>(from_memory, (uint32_t)B, sm.tk);
+    } else if (n_over > 0) {
+        // replace the kept keys of the re-admitted groups by all of theirs
+#pragma unroll
+        for (int s = 0; s < Keys::kBase; ++s) {
+            const int g = (tid + NT * s) / kCand;
+            for (int e = 0; e < n_over; ++e)
+                if (sm.over[e] == g) ck.k[s] = 0ull;
+        }
+        ck.ne = (n_over * kGroup + NT - 1) / NT;
+#pragma unroll
+        for (int s = 0; s < Keys::kExp; ++s) {
+            const int idx = s * NT + tid;
+            const int x = idx / kGroup;
+            uint64_t key = 0ull;
+            if (x < n_over) {
+                const int64_t bb = (int64_t)sm.over[x] * kGroup + idx % kGroup;
+                if (bb < limit) {
+                    const float sc = srow[bb];
+                    if (finite_f32(sc)) key = block_key(sc, bb);
+                }
+            }
+            ck.k[Keys::kBase + s] = key;
+        }
+        th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
+    }
+
+    auto mark = [&](uint32_t k, uint32_t u) {
+        if (th.keep(k, u)) {
+            const uint32_t bb = ~u;
+            atomicOr(&sm.bitmap[bb >> 5], 1u << (bb & 31));
+        }
+    };
+    if (stream)
+        from_memory(mark);
+    else
+        ck(mark);
+    __syncthreads();
+}
+
+}  // namespace qsa

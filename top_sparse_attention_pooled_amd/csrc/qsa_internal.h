@@ -193,11 +193,11 @@ struct ScoreArgs {
 
 // Decode indexer step (score.hip): pooled-key update of the dirty blocks,
 // block scores, and the exact top-k, in two launches.  The first scores every
-// block and leaves, per workgroup of 256 blocks, its 16 best keys and the
-// largest key it dropped; it also writes the dirty blocks (extra workgroups)
-// while any scoring workgroup that holds a dirty block recomputes it in
-// registers, so no ordering between the two is needed.  The second selects
-// from those candidates.
+// block and leaves, per group of 64 blocks, its 4 best keys and the largest
+// key it dropped; it also writes the dirty blocks (extra workgroups) while
+// any scoring workgroup that holds a dirty block recomputes it in registers,
+// so no ordering between the two is needed.  The second selects from those
+// candidates (a selection kernel, or each attention workgroup).
 struct DecodeIdxArgs {
     ScoreArgs s;
     float *pooled_w;        // same buffer as s.pooled, written by the update part
@@ -211,8 +211,8 @@ struct DecodeIdxArgs {
     int32_t *sel_blocks;
     int32_t *sel_cells;
     int32_t *n_sel;
-    uint64_t *cand;  // [n_q][n_wg][16]
-    uint64_t *drop;  // [n_q][n_wg]
+    uint64_t *cand;  // [n_q][4*n_wg][4]: 4 largest keys of each 64-block group
+    uint64_t *drop;  // [n_q][4*n_wg]: largest key each group dropped
     int32_t n_wg;
 };
 
@@ -255,6 +255,9 @@ hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_score_bf16_ws(const ScoreArgs &a, uint16_t *qr_bf16, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
 constexpr int kFusedMaxBlocks = 1 << 17;  // fused score+select handles nb_max up to this
+// decode selection fused into attention (256-thread workgroups holding the
+// candidates in registers) handles nb_max up to this: 262144-cell contexts
+constexpr int kSelAttnMaxBlocks = 1 << 16;
 size_t fused_select_ws_bytes(int n_q, int nb_max);
 // part 1: update + scores + candidates; part 2: selection from candidates
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st);
@@ -263,5 +266,9 @@ size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
 size_t attn_prefill_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st);
+// decode selection (from the candidates in ws_idx) fused with attention; the
+// attention workspace is the one launch_attn_decode uses
+hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnArgs &a,
+                                     hipStream_t st);
 
 }  // namespace qsa

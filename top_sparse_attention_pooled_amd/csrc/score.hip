@@ -13,7 +13,7 @@
 // Prefill (bf16).  The same contraction for many queries is a dense
 // [queries x 128] x [128 x blocks] product, done on the matrix cores with
 // v_mfma_f32_16x16x32_bf16 from bf16 copies of the roped queries and keys.
-#include "topk_engine.h"
+#include "cand_select.h"
 
 namespace qsa {
 
@@ -126,12 +126,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
 // decode indexer step: update + scoring + candidates, then exact selection
 // ---------------------------------------------------------------------------
 
-constexpr int kCand = 16;        // keys kept per workgroup of 256 blocks
-constexpr int kSelNT = 1024;     // selection workgroup
-constexpr int kBaseSlots = kFusedMaxBlocks / 256 * kCand / kSelNT;  // 8
-constexpr int kMaxExpand = 16;   // workgroups re-admitted whole
-constexpr int kExpSlots = kMaxExpand * 256 / kSelNT;              // 4
-constexpr int kSlots = kBaseSlots + kExpSlots;
+constexpr int kSelNT = 1024;  // selection workgroup
 
 // Descending bitonic sort of one 64-bit key per lane across a wavefront.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
@@ -152,8 +147,6 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
 // workgroups (one wavefront per dirty entry).
 __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     __shared__ float4 qr4[kQuads];
-    __shared__ uint64_t wave_top[4][kCand];
-    __shared__ uint64_t wave_drop[4];
     __shared__ float4 patch[kQuads];
     const ScoreArgs &a = f.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
@@ -241,41 +234,17 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     if (b < a.nb_max) srow[b] = sc;
     uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
     key = wave_sort_desc(key);
-    if (lane < kCand) wave_top[wave][lane] = key;
-    if (lane == kCand) wave_drop[wave] = key;
-    __syncthreads();
-    if (wave == 0) {
-        uint64_t k2 = wave_top[lane >> 4][lane & 15];
-        k2 = wave_sort_desc(k2);
-        const uint64_t d16 = (uint64_t)lane_value((uint32_t)k2, kCand) |
-                             ((uint64_t)lane_value((uint32_t)(k2 >> 32), kCand) << 32);
-        const int64_t slot = (int64_t)i * f.n_wg + wg;
-        if (lane < kCand) f.cand[slot * kCand + lane] = k2;
-        if (lane == 0) {
-            uint64_t d = d16;
-            for (int w = 0; w < 4; ++w) d = wave_drop[w] > d ? wave_drop[w] : d;
-            f.drop[slot] = d;
-        }
-    }
+    const int64_t grp = ((int64_t)i * f.n_wg + wg) * 4 + wave;
+    if (lane < kCand) f.cand[grp * kCand + lane] = key;
+    if (lane == kCand) f.drop[grp] = key;
 }
 
-struct SelCandSmem {
-    TopkSmem<kSelNT> tk;
-    uint32_t bitmap[kFusedMaxBlocks / 32];
-    int n_over;
-    int over[kMaxExpand];
-};
-
-// grid (n_q), 1024 threads.  Threshold over the kept keys; every workgroup
-// whose largest dropped key would itself be kept is re-admitted with all 256
-// of its keys (or, if more than 16 are, the score row is re-streamed) and the
-// threshold is taken again.  A key a workgroup dropped without qualifying
-// lies below the first threshold, which is <= the final one, so the result
-// is the exact top-B of all scores.
+// grid (n_q), 1024 threads: the exact selection from the candidates, then
+// the ascending emission of blocks and cells.
 __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
-    __shared__ SelCandSmem sm;
+    __shared__ CandSelSmem<kSelNT, kFusedMaxBlocks> sm;
     const ScoreArgs &a = f.s;
-    const int i = blockIdx.x, tid = threadIdx.x;
+    const int i = blockIdx.x;
     int s;
     int64_t p;
     bool valid;
@@ -283,103 +252,12 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
                                     a.g.n_cells, a.r, s, p, valid);
     const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
     const int B = f.top_k / a.r;
-    const int64_t qbase = (int64_t)i * f.n_wg;
-    const float *srow = a.scores + (int64_t)i * a.ld;
-
-    RegKeys64<kSlots> from_regs;
-    uint64_t *kk = from_regs.k;
-#pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-        const int fi = tid + kSelNT * sl;
-        kk[sl] = (sl < kBaseSlots && fi < f.n_wg * kCand) ? f.cand[qbase * kCand + fi] : 0ull;
-    }
-    auto from_memory = [&](auto &&fn) {
-        constexpr int U = 16;
-        for (int64_t base = 0; base < limit; base += (int64_t)kSelNT * U) {
-            float v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t bb = base + (int64_t)u * kSelNT + tid;
-                v[u] = bb < limit ? srow[bb] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t bb = base + (int64_t)u * kSelNT + tid;
-                if (bb < limit) fn(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)bb);
-            }
-        }
-    };
-    // largest dropped key of each scoring workgroup, fetched with the keys
-    constexpr int kDropSlots = kFusedMaxBlocks / 256 / kSelNT;  // 1 (512 workgroups max)
-    uint64_t drop[kDropSlots > 0 ? kDropSlots : 1];
-#pragma unroll
-    for (int q = 0; q < (kDropSlots > 0 ? kDropSlots : 1); ++q) {
-        const int w = tid + kSelNT * q;
-        drop[q] = w < f.n_wg ? f.drop[qbase + w] : 0ull;
-    }
-    if (tid == 0) sm.n_over = 0;
-    const Thresh th0 = topk_threshold<kSelNT>(from_regs, (uint32_t)B, sm.tk);
-
-#pragma unroll
-    for (int q = 0; q < (kDropSlots > 0 ? kDropSlots : 1); ++q) {
-        const uint64_t d = drop[q];
-        if (d != 0 && th0.keep((uint32_t)(d >> 32), (uint32_t)d)) {
-            const int at = atomicAdd(&sm.n_over, 1);
-            if (at < kMaxExpand) sm.over[at] = tid + kSelNT * q;
-        }
-    }
-    __syncthreads();
-    const int n_over = sm.n_over;
-    Thresh th = th0;
-    const bool stream = n_over > kMaxExpand;
-    if (stream) {
-        th = topk_threshold<kSelNT>(from_memory, (uint32_t)B, sm.tk);
-    } else if (n_over > 0) {
-        // replace the kept keys of the re-admitted workgroups by all of theirs
-#pragma unroll
-        for (int sl = 0; sl < kBaseSlots; ++sl) {
-            const int w = (tid + kSelNT * sl) / kCand;
-            for (int e = 0; e < n_over; ++e)
-                if (sm.over[e] == w) kk[sl] = 0ull;
-        }
-#pragma unroll
-        for (int sl = 0; sl < kExpSlots; ++sl) {
-            const int x = sl * (kSelNT / 256) + (tid >> 8);
-            uint64_t key = 0ull;
-            if (x < n_over) {
-                const int64_t bb = (int64_t)sm.over[x] * 256 + (tid & 255);
-                if (bb < limit) {
-                    const float sc = srow[bb];
-                    if (finite_f32(sc)) key = block_key(sc, bb);
-                }
-            }
-            kk[kBaseSlots + sl] = key;
-        }
-        th = topk_threshold<kSelNT>(from_regs, (uint32_t)B, sm.tk);
-    }
-
-    // emission: bitmap of kept blocks, ascending
+    select_candidates<kSelNT, kFusedMaxBlocks>(f, i, limit, B, sm);
     const int n_words = (int)((limit + 31) / 32);
-    for (int w = tid; w < n_words; w += kSelNT) sm.bitmap[w] = 0;
-    __syncthreads();
-    auto mark = [&](uint32_t k, uint32_t u) {
-        if (th.keep(k, u)) {
-            const uint32_t bb = ~u;
-            atomicOr(&sm.bitmap[bb >> 5], 1u << (bb & 31));
-        }
-    };
-    if (stream)
-        from_memory(mark);
-    else
-        from_regs(mark);
-    __syncthreads();
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = f.top_k + a.r - 1;
-    const int n_keep = emit_from_bitmap<kSelNT>(sm.bitmap, n_words, B, a.r, nc, tail,
-                                                f.sel_blocks + (int64_t)i * B,
-                                                f.sel_cells + (int64_t)i * ld_cells, ld_cells,
-                                                sm.tk);
-    if (tid == 0) f.n_sel[i] = n_keep * a.r + tail;
+    emit_from_bitmap<kSelNT>(sm.bitmap, n_words, B, a.r, nc, tail, f.sel_blocks + (int64_t)i * B,
+                             f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i, sm.tk);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,26 +392,17 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs a, const uint16_t 
 
 }  // namespace
 
-size_t fused_select_ws_bytes(int n_q, int nb_max) {
-    const size_t n_wg = (size_t)(nb_max + 255) / 256;
-    return (size_t)n_q * n_wg * (kCand + 1) * sizeof(uint64_t);
-}
-
-static void bind_ws(DecodeIdxArgs &f, void *ws) {
-    f.n_wg = (f.s.nb_max + 255) / 256;
-    f.cand = static_cast<uint64_t *>(ws);
-    f.drop = f.cand + (size_t)f.s.n_q * f.n_wg * kCand;
-}
+size_t fused_select_ws_bytes(int n_q, int nb_max) { return cand_ws_bytes(n_q, nb_max); }
 
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st) {
-    bind_ws(f, ws);
+    bind_candidates(f, ws);
     const int grid = f.n_wg * f.s.n_q + (f.n_dirty + 3) / 4;
     if (grid > 0) hipLaunchKernelGGL(k_score_cand, dim3(grid), dim3(256), 0, st, f);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st) {
-    bind_ws(f, ws);
+    bind_candidates(f, ws);
     if (f.s.n_q > 0) hipLaunchKernelGGL(k_select_cand, dim3(f.s.n_q), dim3(kSelNT), 0, st, f);
     return hipGetLastError();
 }

@@ -33,6 +33,30 @@ struct SelSmem {
     uint32_t count;
 };
 
+// Keys of one query's score row re-read from memory, 16 loads in flight.
+struct RowStream {
+    const float *row;
+    int64_t limit;
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+        constexpr int U = 16;
+        const int tid = threadIdx.x;
+        for (int64_t base = 0; base < limit; base += (int64_t)kNT * U) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t b = base + (int64_t)u * kNT + tid;
+                v[u] = b < limit ? row[b] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t b = base + (int64_t)u * kNT + tid;
+                if (b < limit) fn(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)b);
+            }
+        }
+    }
+};
+
 __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     __shared__ SelSmem sm;
     const int i = blockIdx.x;
@@ -46,9 +70,11 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     const int B = a.top_k / a.r;
     const float *row = a.scores + (int64_t)i * a.ld;
 
-    // source 1: score keys cached in registers, block = s2*kNT + tid
+    // score keys cached in registers (block = s2*kNT + tid), or, past
+    // 32768 blocks, the score row re-read from memory on every pass
     RegKeys32<kC, kNT> from_regs;
     from_regs.tid = tid;
+    const RowStream from_memory{row, limit};
     const bool in_regs = limit <= (int64_t)kNT * kC;
     if (in_regs) {
 #pragma unroll
@@ -58,23 +84,6 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
             from_regs.k[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
         }
     }
-    // source 2: the score row re-read from memory, 16 loads in flight
-    auto from_memory = [&](auto &&f) {
-        constexpr int U = 16;
-        for (int64_t base = 0; base < limit; base += (int64_t)kNT * U) {
-            float v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t b = base + (int64_t)u * kNT + tid;
-                v[u] = b < limit ? row[b] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t b = base + (int64_t)u * kNT + tid;
-                if (b < limit) f(finite_f32(v[u]) ? score_key(v[u]) : 0u, ~(uint32_t)b);
-            }
-        }
-    };
     const Thresh th = in_regs ? topk_threshold<kNT>(from_regs, (uint32_t)B, sm.tk)
                               : topk_threshold<kNT>(from_memory, (uint32_t)B, sm.tk);
 
@@ -82,7 +91,6 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     const int ld_cells = a.top_k + a.r - 1;
     int32_t *ob = a.sel_blocks + (int64_t)i * B;
     int32_t *oc = a.sel_cells + (int64_t)i * ld_cells;
-    int n_keep;
     if (limit <= kMaxBitmapBlocks) {
         const int n_words = (int)((limit + 31) / 32);
         for (int w = tid; w < n_words; w += kNT) sm.bitmap[w] = 0;
@@ -98,8 +106,8 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
         else
             from_memory(mark);
         __syncthreads();
-        n_keep = emit_from_bitmap<kNT>(sm.bitmap, n_words, B, a.r, nc, tail, ob, oc, ld_cells,
-                                       sm.tk);
+        emit_from_bitmap<kNT>(sm.bitmap, n_words, B, a.r, nc, tail, ob, oc, ld_cells,
+                              a.n_sel + i, sm.tk);
     } else {
         // very long contexts: collect the <= B kept blocks, bitonic-sort them
         if (tid == 0) sm.count = 0;
@@ -111,7 +119,8 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
             }
         });
         __syncthreads();
-        n_keep = (int)(sm.count < (uint32_t)B ? sm.count : (uint32_t)B);
+        const int n_keep = (int)(sm.count < (uint32_t)B ? sm.count : (uint32_t)B);
+        if (tid == 0) a.n_sel[i] = n_keep * a.r + tail;
         int P = 1;
         while (P < n_keep) P <<= 1;
         for (int j = n_keep + tid; j < P; j += kNT) sm.list[j] = 0x7fffffff;
@@ -141,7 +150,6 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
             oc[j] = c;
         }
     }
-    if (tid == 0) a.n_sel[i] = n_keep * a.r + tail;
 }
 
 }  // namespace

@@ -132,7 +132,7 @@ __device__ __forceinline__ void pick_bin(TopkSmem<NT> &sm, uint32_t lo, uint32_t
 // threshold value; n_above gets the count strictly above it; done tells
 // whether count(v >= threshold) == krem (no tie left at the threshold).
 template <int NT, typename ForEach, typename Pred, typename Val>
-__device__ uint32_t select_u32(const ForEach &for_each, Pred pred, Val val, uint32_t krem, uint32_t lo,
+__device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pred, Val val, uint32_t krem, uint32_t lo,
                                uint32_t hi, TopkSmem<NT> &sm, uint32_t &n_above, bool &done) {
     n_above = 0;
     for (int round = 0; round < 4; ++round) {
@@ -165,7 +165,7 @@ __device__ uint32_t select_u32(const ForEach &for_each, Pred pred, Val val, uint
 // The exact kept set of the top B (or every valid element if there are at
 // most B).
 template <int NT, typename ForEach>
-__device__ Thresh topk_threshold(const ForEach &for_each, uint32_t B, TopkSmem<NT> &sm) {
+__device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32_t B, TopkSmem<NT> &sm) {
     Thresh th{0u, 0u, false};
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
     for_each([&](uint32_t k, uint32_t) {
@@ -201,13 +201,14 @@ __device__ Thresh topk_threshold(const ForEach &for_each, uint32_t B, TopkSmem<N
 
 // Ascending emission of the kept blocks from an LDS bitmap over
 // [0, n_words*32): each thread owns a run of words, counts, scans, emits.
-// Writes sel_blocks[0..B) (-1 padded) and sel_cells[0..ld_cells) (each kept
-// block's r cells, then the tail cells, -1 padded); returns the number of
-// kept blocks (block-uniform).
+// Writes *n_sel = kept blocks * r + tail (first, so its store is not queued
+// behind the list), sel_blocks[0..B) (-1 padded) and sel_cells[0..ld_cells)
+// (each kept block's r cells, then the tail cells, -1 padded).  Ends without
+// a barrier: the caller must not reuse sm or the bitmap afterwards.
 template <int NT>
-__device__ int emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, int64_t nc,
-                                int tail, int32_t *sel_blocks, int32_t *sel_cells, int ld_cells,
-                                TopkSmem<NT> &sm) {
+__device__ void emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, int64_t nc,
+                                 int tail, int32_t *sel_blocks, int32_t *sel_cells, int ld_cells,
+                                 int32_t *n_sel, TopkSmem<NT> &sm) {
     const int per = (n_words + NT - 1) / NT;
     const int w0 = threadIdx.x * per;
     uint32_t local = 0;
@@ -223,6 +224,8 @@ __device__ int emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, i
         if (w < wave) pos += sm.red[w];
         total += sm.red[w];
     }
+    const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+    if (threadIdx.x == 0) *n_sel = n_keep * r + tail;
     for (int w = w0; w < w0 + per && w < n_words; ++w) {
         uint32_t bits = bm[w];
         while (bits) {
@@ -236,28 +239,15 @@ __device__ int emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, i
             ++pos;
         }
     }
-    const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
     for (int j = n_keep + threadIdx.x; j < B; j += NT) sel_blocks[j] = -1;
     const int n_full = n_keep * r;
     for (int j = n_full + threadIdx.x; j < ld_cells; j += NT)
         sel_cells[j] = (j < n_full + tail) ? (int32_t)(nc * r + (j - n_full)) : -1;
-    __syncthreads();
-    return n_keep;
 }
 
-// Register-resident element sources for topk_threshold.  (A functor object,
+// Register-resident element source for topk_threshold.  (A functor object,
 // not a capturing lambda: with the array a member, full unrolling keeps every
 // element in a register.)
-template <int C>
-struct RegKeys64 {  // explicit keys (score key << 32 | ~block), 0 = none
-    uint64_t k[C];
-    template <typename F>
-    __device__ __forceinline__ void operator()(F &&fn) const {
-#pragma unroll
-        for (int s = 0; s < C; ++s) fn((uint32_t)(k[s] >> 32), (uint32_t)k[s]);
-    }
-};
-
 template <int C, int NT>
 struct RegKeys32 {  // score keys of blocks s*NT + tid, 0 = none
     uint32_t k[C];

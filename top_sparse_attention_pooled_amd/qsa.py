@@ -24,7 +24,8 @@ TILE = 64
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_update_pooled_keys", "qsa_score_blocks", "qsa_select_topk_blocks",
            "qsa_score_select_decode", "qsa_decode_score_candidates",
-           "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
+           "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
+           "qsa_decode_select_attend")
 
 
 class QsaError(RuntimeError):
@@ -90,6 +91,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_decode_select_attend.restype = ctypes.c_int
+    lib.qsa_decode_select_attend.argtypes = [D, S, vp, vp, i32, i32, vp, i64, vp, vp, vp, vp, sz,
+                                             vp, vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -215,6 +219,18 @@ def decode_select_candidates(dims: Dims, seqs: Seqs, q_seq, q_pos, n_q: int, nb_
                                             _ptr(q_seq), _ptr(q_pos), n_q, nb_max, _ptr(scores),
                                             ld_scores, _ptr(sel_blocks), _ptr(sel_cells),
                                             _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def decode_select_attend(dims: Dims, seqs: Seqs, q_seq, q_pos, n_q: int, nb_max: int, scores,
+                         ld_scores: int, sel_blocks, sel_cells, n_sel, ws_idx, ws_idx_bytes: int,
+                         q, k_cache, v_cache, out, ws_attn, ws_attn_bytes: int,
+                         stream=None) -> None:
+    _rc(load().qsa_decode_select_attend(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                        _ptr(q_seq), _ptr(q_pos), n_q, nb_max, _ptr(scores),
+                                        ld_scores, _ptr(sel_blocks), _ptr(sel_cells), _ptr(n_sel),
+                                        _ptr(ws_idx), ws_idx_bytes, _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(out), _ptr(ws_attn), ws_attn_bytes,
+                                        _stream(stream)))
 
 
 def sparse_attn_decode(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_cache, sel_cells,

@@ -112,17 +112,35 @@ class StepBuffers:
         self.ws_fused = torch.empty(max(self.ws_fused_bytes, 16), dtype=torch.uint8, device=dev)
 
 
-def run_step(layer: Layer, bufs: StepBuffers, q_idx, q, q_seq, q_pos, dirty, n_dirty: int,
-             mode: int = qsa.SCORE_F32, prefill: bool = False, fused: bool = True,
-             stream=None) -> StepOut:
-    """update -> score -> select -> attend, all enqueued on one stream.
+PATHS = ("attend", "indexer", "general")
+SEL_ATTN_MAX_BLOCKS = 1 << 16  # nb_max limit of qsa_decode_select_attend
 
-    fused: the decode update, scoring and selection through
-    qsa_score_select_decode instead of the three separate calls; same
-    results."""
+
+def run_step(layer: Layer, bufs: StepBuffers, q_idx, q, q_seq, q_pos, dirty, n_dirty: int,
+             mode: int = qsa.SCORE_F32, prefill: bool = False, path: str = "attend",
+             stream=None) -> StepOut:
+    """update -> score -> select -> attend, all enqueued on one stream, by one
+    of three call sequences with the same results:
+      attend:  qsa_decode_score_candidates, then qsa_decode_select_attend
+               (decode, fp32 scores, contexts up to 65536 blocks);
+      indexer: qsa_score_select_decode, then the attention call;
+      general: update, score, select and attention as four calls."""
+    assert path in PATHS, path
     d, sq = layer.dims, layer.seqs()
     n_q = bufs.n_q
-    if fused and mode == qsa.SCORE_F32:
+    if path == "attend" and (prefill or mode != qsa.SCORE_F32 or bufs.nb_max > SEL_ATTN_MAX_BLOCKS):
+        path = "indexer" if mode == qsa.SCORE_F32 else "general"
+    if path == "attend":
+        qsa.decode_score_candidates(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
+                                    layer.pooled_bf16, q_idx, q_seq, q_pos, n_q, bufs.nb_max,
+                                    bufs.scores, bufs.ld, bufs.ws_fused, bufs.ws_fused_bytes,
+                                    stream=stream)
+        qsa.decode_select_attend(d, sq, q_seq, q_pos, n_q, bufs.nb_max, bufs.scores, bufs.ld,
+                                 bufs.sel_blocks, bufs.sel_cells, bufs.n_sel, bufs.ws_fused,
+                                 bufs.ws_fused_bytes, q, layer.k, layer.v, bufs.out,
+                                 bufs.ws_attn, bufs.ws_attn_bytes, stream=stream)
+        return StepOut(bufs.scores, bufs.sel_blocks, bufs.sel_cells, bufs.n_sel, bufs.out)
+    if path == "indexer":
         qsa.score_select_decode(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
                                 layer.pooled_bf16, q_idx, q_seq, q_pos, n_q, bufs.nb_max,
                                 bufs.scores, bufs.ld, bufs.sel_blocks, bufs.sel_cells,
