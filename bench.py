@@ -41,6 +41,12 @@ def parse():
                     help="budget of the CPU-oracle baseline sample (0 = skip)")
     ap.add_argument("--profile", action="store_true",
                     help="short run for a profiler: no CPU baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the steps directly instead of replaying a graph (for "
+                         "hardware-counter runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also copy an MIB-MiB buffer once: a kernel of known traffic "
+                         "that scales the byte counters")
     return ap.parse_args()
 
 
@@ -112,20 +118,15 @@ def main():
 
     stream = torch.cuda.Stream()
 
-    def enqueue(t, ev=None, only_score=False):
+    def enqueue(t, only_score=False):
         """One decode token through every layer: update + scores + candidates,
-        then selection fused into attention (+ the merge of partial states).
-        ev: per-layer (start, end) events around the scoring kernel."""
+        then selection fused into attention (+ the merge of partial states)."""
         for li, layer in enumerate(layers):
             layer.n_cells = n_cells[t]
             bf, d, sq = bufs[li], layer.dims, layer.seqs()
-            if ev is not None:
-                ev[li][0].record(stream)
             qsa.decode_score_candidates(d, sq, layer.kidx, dirty[t], n_dirty, layer.pooled,
                                         layer.pooled_bf16, q_idx[t], q_seq[t], q_pos[t], n_q,
                                         nb_max, bf.scores, bf.ld, bf.ws_fused, bf.ws_fused_bytes)
-            if ev is not None:
-                ev[li][1].record(stream)
             if only_score:
                 continue
             qsa.decode_select_attend(d, sq, q_seq[t], q_pos[t], n_q, nb_max, bf.scores, bf.ld,
@@ -133,41 +134,50 @@ def main():
                                      bf.ws_fused_bytes, q[t], layer.k, layer.v, bf.out,
                                      bf.ws_attn, bf.ws_attn_bytes)
 
-    def capture(steps, events=None, only_score=False):
+    def capture(steps, only_score=False):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for n_t, t in enumerate(steps):
-                enqueue(t, None if events is None else events[n_t], only_score)
+            for t in steps:
+                enqueue(t, only_score)
         return g
 
-    g_warm = capture(range(W)) if W > 0 else None
-    g_main = capture(range(W, T))
-    torch.cuda.synchronize()
-    if g_warm is not None:
-        g_warm.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    g_main.replay()
-    torch.cuda.synchronize()
-    t_main = time.perf_counter() - t_start
-
-    # live timing of the dominant kernel (scoring stream) with HIP events:
-    # event record nodes around every scoring launch of a second replay of
-    # the same K steps
-    score_us, timing = None, "graph event nodes around each scoring launch"
-    try:
-        evs = [[(torch.cuda.Event(enable_timing=True, external=True),
-                 torch.cuda.Event(enable_timing=True, external=True)) for _ in range(L)]
-               for _ in range(K)]
-        g_ev = capture(range(W, T), events=evs)
-        g_ev.replay()
+    if args.copy_calibration:  # one streaming kernel of known traffic
+        n = args.copy_calibration * (1 << 20) // 4
+        src_buf = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
         torch.cuda.synchronize()
-        durs = [a.elapsed_time(b) for row in evs for (a, b) in row]
-        if min(durs) > 0:
-            score_us = float(np.mean(durs)) * 1000.0
-    except Exception as e:  # runtime without graph event nodes
-        print(f"# graph event timing unavailable: {e}", file=sys.stderr)
-    if score_us is None:
+        torch.neg(src_buf, out=dst_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+
+    if args.eager:
+        with torch.cuda.stream(stream):
+            for t in range(W):
+                enqueue(t)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for t in range(W, T):
+                enqueue(t)
+        torch.cuda.synchronize()
+        t_main = time.perf_counter() - t_start
+    else:
+        g_warm = capture(range(W)) if W > 0 else None
+        g_main = capture(range(W, T))
+        torch.cuda.synchronize()
+        if g_warm is not None:
+            g_warm.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        g_main.replay()
+        torch.cuda.synchronize()
+        t_main = time.perf_counter() - t_start
+
+    # live timing of the dominant kernel with HIP events on its stream: a
+    # graph of the same K*L scoring launches alone, replayed between two
+    # events (this runtime does not take event nodes inside a captured graph)
+    score_us, timing = None, "eager run: not timed"
+    if not args.eager:
         timing = "events around a graph of the K*L scoring launches alone"
         g_score = capture(range(W, T), only_score=True)
         g_score.replay()
@@ -190,9 +200,9 @@ def main():
     ab = [algorithmic_bytes(w, t) for t in range(W, T)]
     score_bytes = float(np.mean([a["score"] for a in ab]))
     step_bytes = float(np.mean([sum(a.values()) for a in ab]))
-    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    achieved = score_bytes / (score_us * 1e-6) / 1e9 if score_us else None
     result = {
-        "metric": "QSA sparse-attn decode us/token (one QSA layer) at 250k ctx",
+        "metric": "QSA sparse-attn decode \u00b5s/token and HBM GB/s at 250k ctx; prefill t/s",
         "value": round(us_per_token_layer, 3),
         "unit": "us/token",
         "n_gpus": 1,
@@ -217,13 +227,13 @@ def main():
             "kernel": "k_score_cand",
             "timing": timing,
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+            "traffic": recorded_traffic(args.workload),
             "bytes_per_launch": round(score_bytes),
-            "avg_launch_us": round(score_us, 3),
+            "avg_launch_us": round(score_us, 3) if score_us else None,
         },
     }
 
@@ -231,6 +241,21 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all,
                                               W, K, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def recorded_traffic(workload):
+    """HBM-side bytes per scoring launch from the committed counter summary
+    (two rocprofv3 --pmc runs, scaled by a streaming kernel of known size),
+    or None if there is none or the kernel sources changed since."""
+    from top_sparse_attention_pooled_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"k_score_cand_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != profiling.source_hash():
+        return None
+    return round(rec["traffic_bytes"])
 
 
 def cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all, W, K, budget):

@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 runs: per-kernel durations and the HBM-side byte
+counters (FETCH_SIZE, WRITE_SIZE) of a kernel, scaled by what the same
+counters read for a plain streaming kernel of known size.
+
+    python -m top_sparse_attention_pooled_amd.profiling traffic \\
+        --fetch DIR --write DIR --kernel k_score_cand --workload decode250k \\
+        --copy-mib 256 --out profiles/k_score_cand_decode250k_traffic
+
+writes OUT.json (read by bench.py) and OUT.md.  The JSON carries a hash of
+the kernel sources; bench.py reports the traffic only while the sources
+still hash the same (a changed kernel makes the counters stale).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+from typing import Dict, List
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+# the streaming kernel of known size: torch.neg over a float32 buffer (reads
+# and writes copy_mib MiB each)
+CALIBRATION_KERNEL = "neg"
+
+
+def source_hash() -> str:
+    """sha256 over every kernel source and header, in name order."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if path.endswith((".hip", ".h")):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def _rows(directory: str, suffix: str) -> List[dict]:
+    files = glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
+def counter_values(directory: str, counter: str) -> Dict[str, List[float]]:
+    """Kernel name -> per-dispatch values of one counter (rocprofv3 --pmc CSV)."""
+    out: Dict[str, List[float]] = {}
+    for r in _rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def kernel_durations(directory: str) -> Dict[str, List[float]]:
+    """Kernel name -> per-dispatch durations in microseconds (kernel trace)."""
+    out: Dict[str, List[float]] = {}
+    for r in _rows(directory, "kernel_trace.csv"):
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        out.setdefault(r["Kernel_Name"], []).append(d)
+    return out
+
+
+def _pick(values: Dict[str, List[float]], needle: str) -> List[float]:
+    hits = [v for k, v in values.items() if needle in k]
+    if len(hits) != 1:
+        raise KeyError(f"{len(hits)} kernels match {needle!r}: "
+                       f"{[k for k in values if needle in k]}")
+    return hits[0]
+
+
+def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_mib: int) -> dict:
+    fetch = counter_values(fetch_dir, "FETCH_SIZE")
+    write = counter_values(write_dir, "WRITE_SIZE")
+    known_kib = copy_mib * 1024.0
+    cal_f = _pick(fetch, CALIBRATION_KERNEL)
+    cal_w = _pick(write, CALIBRATION_KERNEL)
+    f_scale = known_kib / statistics.mean(cal_f)
+    w_scale = known_kib / statistics.mean(cal_w)
+    kf = _pick(fetch, kernel)
+    kw = _pick(write, kernel)
+    fetch_b = statistics.mean(kf) * f_scale * 1024.0
+    write_b = statistics.mean(kw) * w_scale * 1024.0
+    return {
+        "kernel": kernel,
+        "dispatches": [len(kf), len(kw)],
+        "fetch_kib_raw_mean": statistics.mean(kf),
+        "write_kib_raw_mean": statistics.mean(kw),
+        "calibration": {"kernel": CALIBRATION_KERNEL, "mib": copy_mib,
+                        "fetch_kib_raw": statistics.mean(cal_f),
+                        "write_kib_raw": statistics.mean(cal_w),
+                        "fetch_scale": f_scale, "write_scale": w_scale},
+        "fetch_bytes": fetch_b,
+        "write_bytes": write_b,
+        "traffic_bytes": fetch_b + write_b,
+        "source_sha256": source_hash(),
+    }
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", default="", help="the profiling commands, for the record")
+    a = ap.parse_args()
+    res = traffic(a.fetch, a.write, a.kernel, a.copy_mib)
+    res["workload"] = a.workload
+    with open(a.out + ".json", "w") as f:
+        json.dump(res, f, indent=1)
+    c = res["calibration"]
+    with open(a.out + ".md", "w") as f:
+        f.write(f"# {a.kernel} HBM-side traffic, {a.workload}\n\n")
+        if a.command:
+            f.write("Commands:\n\n```\n" + a.command.strip() + "\n```\n\n")
+        f.write(f"- dispatches (FETCH, WRITE runs): {res['dispatches']}\n")
+        f.write(f"- raw FETCH_SIZE mean {res['fetch_kib_raw_mean']:.1f} KiB, "
+                f"raw WRITE_SIZE mean {res['write_kib_raw_mean']:.1f} KiB per dispatch\n")
+        f.write(f"- calibration: torch.{c['kernel']} over {c['mib']} MiB reads "
+                f"{c['fetch_kib_raw']:.1f} KiB / writes {c['write_kib_raw']:.1f} KiB raw "
+                f"-> scale {c['fetch_scale']:.4f} (fetch), {c['write_scale']:.4f} (write)\n")
+        f.write(f"- scaled: fetch {res['fetch_bytes'] / 1e6:.3f} MB, write "
+                f"{res['write_bytes'] / 1e6:.3f} MB, total "
+                f"{res['traffic_bytes'] / 1e6:.3f} MB per dispatch\n")
+        f.write(f"- kernel sources sha256 {res['source_sha256']}\n")
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
