@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 N_LAYERS = 12
 
 
@@ -35,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode250k",
-                    choices=["decode50k", "decode250k", "decode5x250k"])
+                    choices=["decode50k", "decode250k", "decode5x250k", "prefill"])
     ap.add_argument("--layers", type=int, default=N_LAYERS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU-oracle baseline sample (0 = skip)")
@@ -69,25 +70,14 @@ def algorithmic_bytes(w, step):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
-              "(the QSA step is not sharded across GPUs)", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    from top_sparse_attention_pooled_amd import qsa, runtime, synth
-
-    qsa.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+def setup(args, torch, dev):
+    """Caches of L layer replicas plus the per-step device inputs."""
+    from top_sparse_attention_pooled_amd import runtime, synth
     w = synth.WORKLOADS[args.workload]
     K, W, L = args.steps, args.warmup, args.layers
-    if K + W > w.steps:
+    prefill = args.workload == "prefill"
+    if not prefill and K + W > w.steps:
         w = synth.Workload(**{**w.__dict__, "steps": K + W})
-
     t0 = time.time()
     kidx = synth.make_kidx(w)
     k = synth.make_kv(w, synth.T_K)
@@ -99,23 +89,117 @@ def main():
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.time() - t0:.1f}s ({args.workload}, {L} layer replicas)",
           file=sys.stderr, flush=True)
-
-    # per-step inputs for warmup + timed steps, all on the device
+    # per-step inputs for warmup + timed steps; a prefill step repeats the
+    # same ubatch (re-dirtying the same blocks), a decode step appends a token
     T = W + K
+    steps = [0] * T if prefill else list(range(T))
     qi, qq, qs, qp, nc_all, dl_all = [], [], [], [], [], []
-    for t in range(T):
+    for t in steps:
         a, b, c, d = synth.make_queries(w, t)
         qi.append(a); qq.append(b); qs.append(c); qp.append(d)
         nc_all.append(synth.n_cells_at(w, t))
         dl_all.append(synth.dirty_blocks(w, t))
     to = lambda x: torch.from_numpy(np.ascontiguousarray(np.stack(x))).to(dev)
-    q_idx, q, q_seq, q_pos = to(qi), to(qq), to(qs), to(qp)
-    n_cells, dirty = to(nc_all), to([d.reshape(-1) for d in dl_all])
-    n_dirty = dl_all[0].shape[0]
-    n_q = q_pos.shape[1]
-    nb_max = w.nb_max(T - 1)
-    bufs = [runtime.StepBuffers(layers[0].dims, n_q, nb_max, dev) for _ in range(L)]
+    inp = {"q_idx": to(qi), "q": to(qq), "q_seq": to(qs), "q_pos": to(qp),
+           "n_cells": to(nc_all), "dirty": to([d.reshape(-1) for d in dl_all]),
+           "n_dirty": dl_all[0].shape[0], "n_q": qp[0].shape[0],
+           "nb_max": w.nb_max(max(steps))}
+    host = dict(kidx=kidx, k=k, v=v, qi=qi, qq=qq, qs=qs, qp=qp, nc_all=nc_all, dl_all=dl_all)
+    return w, layers, inp, host
 
+
+def timed_replay(args, torch, stream, enqueue, T, W):
+    """W warm-up then K timed steps, replayed as one HIP graph (or launched
+    directly with --eager); returns seconds for the K steps and the capture
+    helper."""
+    def capture(steps, **kw):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in steps:
+                enqueue(t, **kw)
+        return g
+
+    if args.eager:
+        with torch.cuda.stream(stream):
+            for t in range(W):
+                enqueue(t)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for t in range(W, T):
+                enqueue(t)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_start, capture
+    g_warm = capture(range(W)) if W > 0 else None
+    g_main = capture(range(W, T))
+    torch.cuda.synchronize()
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g_main.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t_start, capture
+
+
+def time_part(torch, stream, capture, T, W, n_launches, **kw):
+    """Mean device time of one launch of a part of the step: a graph of just
+    those launches over the timed steps, between two events on the stream
+    (this runtime takes no event nodes inside a captured graph)."""
+    g = capture(range(W, T), **kw)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1000.0 / n_launches
+
+
+def calibration_copy(args, torch, dev):
+    if args.copy_calibration:  # one streaming kernel of known traffic
+        n = args.copy_calibration * (1 << 20) // 4
+        src_buf = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        torch.neg(src_buf, out=dst_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
+              "(the QSA step is not sharded across GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from top_sparse_attention_pooled_amd import qsa
+
+    qsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == "prefill":
+        result = run_prefill(args, torch, dev)
+    else:
+        result = run_decode(args, torch, dev)
+    print(json.dumps(result), flush=True)
+
+
+def run_decode(args, torch, dev):
+    from top_sparse_attention_pooled_amd import qsa, runtime, synth
+    w, layers, inp, host = setup(args, torch, dev)
+    K, W, L = args.steps, args.warmup, args.layers
+    T = W + K
+    q_idx, q, q_seq, q_pos = inp["q_idx"], inp["q"], inp["q_seq"], inp["q_pos"]
+    n_cells, dirty, n_dirty = inp["n_cells"], inp["dirty"], inp["n_dirty"]
+    n_q, nb_max = inp["n_q"], inp["nb_max"]
+    bufs = [runtime.StepBuffers(layers[0].dims, n_q, nb_max, dev) for _ in range(L)]
     stream = torch.cuda.Stream()
 
     def enqueue(t, only_score=False):
@@ -134,62 +218,13 @@ def main():
                                      bf.ws_fused_bytes, q[t], layer.k, layer.v, bf.out,
                                      bf.ws_attn, bf.ws_attn_bytes)
 
-    def capture(steps, only_score=False):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for t in steps:
-                enqueue(t, only_score)
-        return g
-
-    if args.copy_calibration:  # one streaming kernel of known traffic
-        n = args.copy_calibration * (1 << 20) // 4
-        src_buf = torch.ones(n, dtype=torch.float32, device=dev)
-        dst_buf = torch.empty_like(src_buf)
-        torch.cuda.synchronize()
-        torch.neg(src_buf, out=dst_buf)
-        torch.cuda.synchronize()
-        del src_buf, dst_buf
-
-    if args.eager:
-        with torch.cuda.stream(stream):
-            for t in range(W):
-                enqueue(t)
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        with torch.cuda.stream(stream):
-            for t in range(W, T):
-                enqueue(t)
-        torch.cuda.synchronize()
-        t_main = time.perf_counter() - t_start
-    else:
-        g_warm = capture(range(W)) if W > 0 else None
-        g_main = capture(range(W, T))
-        torch.cuda.synchronize()
-        if g_warm is not None:
-            g_warm.replay()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        g_main.replay()
-        torch.cuda.synchronize()
-        t_main = time.perf_counter() - t_start
-
-    # live timing of the dominant kernel with HIP events on its stream: a
-    # graph of the same K*L scoring launches alone, replayed between two
-    # events (this runtime does not take event nodes inside a captured graph)
+    calibration_copy(args, torch, dev)
+    t_main, capture = timed_replay(args, torch, stream, enqueue, T, W)
+    # live timing of the dominant kernel with HIP events on its stream
     score_us, timing = None, "eager run: not timed"
     if not args.eager:
         timing = "events around a graph of the K*L scoring launches alone"
-        g_score = capture(range(W, T), only_score=True)
-        g_score.replay()
-        torch.cuda.synchronize()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            g_score.replay()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        score_us = ev0.elapsed_time(ev1) * 1000.0 / (K * L)
+        score_us = time_part(torch, stream, capture, T, W, K * L, only_score=True)
 
     # correctness guard on the last step of layer 0 (selection sizes)
     n_sel = bufs[0].n_sel.cpu().numpy()
@@ -219,7 +254,7 @@ def main():
             "n_seq": w.n_seq, "n_kv_start": w.n_cells0 + w.n_new, "decode_steps": K,
             "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
             "compress_ratio": w.r, "top_k": w.top_k,
-            "layers_per_step": L, "graph_replay": True,
+            "layers_per_step": L, "graph_replay": not args.eager,
         },
         "tokens_per_s_per_layer": round(1e6 / us_per_token_layer, 1),
         "step_hbm_gbps": round(step_bytes / (us_per_token_layer * 1e-6) / 1e9, 1),
@@ -236,11 +271,97 @@ def main():
             "avg_launch_us": round(score_us, 3) if score_us else None,
         },
     }
-
     if not args.profile and args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all,
-                                              W, K, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, host, W, K, args.cpu_seconds)
+    return result
+
+
+def run_prefill(args, torch, dev):
+    """One step = the 512-token ubatch at depth 198,628 through every layer:
+    pooled-key update of its 128 dirty blocks, bf16 MFMA block scores,
+    per-query exact block top-k, sparse attention per query."""
+    from top_sparse_attention_pooled_amd import qsa, runtime, synth
+    w, layers, inp, host = setup(args, torch, dev)
+    K, W, L = args.steps, args.warmup, args.layers
+    T = W + K
+    q_idx, q, q_seq, q_pos = inp["q_idx"], inp["q"], inp["q_seq"], inp["q_pos"]
+    n_cells, dirty, n_dirty = inp["n_cells"], inp["dirty"], inp["n_dirty"]
+    n_q, nb_max = inp["n_q"], inp["nb_max"]
+    bufs = [runtime.StepBuffers(layers[0].dims, n_q, nb_max, dev, prefill=True)
+            for _ in range(L)]
+    stream = torch.cuda.Stream()
+    for layer in layers:
+        layer.n_cells = n_cells[0]
+
+    def enqueue(t, part="all"):
+        for li, layer in enumerate(layers):
+            bf, d, sq = bufs[li], layer.dims, layer.seqs()
+            if part in ("all", "indexer"):
+                qsa.score_select_prefill(d, sq, layer.kidx, dirty[t], n_dirty, layer.pooled,
+                                         layer.pooled_bf16, q_idx[t], q_seq[t], q_pos[t], n_q,
+                                         nb_max, bf.sel_blocks, bf.sel_cells, bf.n_sel,
+                                         bf.ws_pf, bf.ws_pf_bytes)
+            if part in ("all", "attn"):
+                qsa.sparse_attn_prefill(d, sq, q[t], q_seq[t], n_q, layer.k, layer.v,
+                                        bf.sel_cells, bf.n_sel, bf.out, bf.ws_attn,
+                                        bf.ws_attn_bytes)
+
+    calibration_copy(args, torch, dev)
+    t_main, capture = timed_replay(args, torch, stream, enqueue, T, W)
+    parts = {}
+    if not args.eager:
+        for part in ("indexer", "attn"):
+            parts[part] = time_part(torch, stream, capture, T, W, K * L, part=part)
+    n_sel = bufs[0].n_sel.cpu().numpy()
+    assert np.all(n_sel > 0), "empty selections in the benchmark step"
+
+    ms_per_step = t_main * 1000.0 / K
+    us_per_layer = ms_per_step * 1000.0 / L
+    pos = host["qp"][0]
+    nc = (pos.astype(np.int64) + 1) // w.r
+    flops = float(np.sum(nc)) * w.d * 2  # the dense query x block-key contraction
+    score_us = parts.get("indexer")
+    tflops = flops / (score_us * 1e-6) / 1e12 if score_us else None
+    result = {
+        "metric": "QSA sparse-attn decode \u00b5s/token and HBM GB/s at 250k ctx; prefill t/s",
+        "value": round(n_q / (us_per_layer * 1e-6), 1),
+        "unit": "t/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 indexer (fp32 accumulate), f32 attention over q8_0 KV",
+        "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded",
+        "config": {
+            "workload": "prefill", "n_seq": 1, "n_kv_start": w.n_cells0, "ubatch": n_q,
+            "dirty_blocks": int(np.sum(host["dl_all"][0][:, 0] >= 0)),
+            "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
+            "compress_ratio": w.r, "top_k": w.top_k, "layers_per_step": L,
+            "graph_replay": not args.eager,
+        },
+        "us_per_layer": round(us_per_layer, 2),
+        "model_prefill_t_s": round(n_q / (ms_per_step * 1e-3), 1),
+        "parts_us": {k: round(v, 2) for k, v in parts.items()},
+        "roofline": {
+            "kernel": "qsa_score_select_prefill (update, rope, sampled and full MFMA passes, "
+                      "exact selection), priced on the dense contraction alone",
+            "timing": "events around a graph of the K*L indexer calls alone",
+            "bound": "mfma",
+            "achieved": round(tflops, 2) if tflops else None,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if tflops else None,
+            "traffic": None,
+            "flops_per_launch": flops,
+            "avg_launch_us": round(score_us, 3) if score_us else None,
+        },
+    }
+    if not args.profile and args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_prefill(w, host, args.cpu_seconds)
+    return result
 
 
 def recorded_traffic(workload):
@@ -258,10 +379,11 @@ def recorded_traffic(workload):
     return round(rec["traffic_bytes"])
 
 
-def cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all, W, K, budget):
+def cpu_baseline(w, host, W, K, budget):
     """The oracle as it stands, single-threaded, on the first decode steps of
     the same workload (one layer): update, score, select, attend per step."""
     import oracle
+    kidx, k, v = host["kidx"], host["k"], host["v"]
     pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
     n0 = np.full(w.n_seq, w.n_cells0, np.int32)
     pairs = [(s, b) for s in range(w.n_seq) for b in range(-(-w.n_cells0 // w.r))]
@@ -269,9 +391,11 @@ def cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all, W, K, budget):
     done, spent = 0, 0.0
     for t in range(W + K):
         t0 = time.perf_counter()
-        oracle.update_pooled(kidx, nc_all[t], dl_all[t], pooled, w.r, w.theta, w.eps)
-        oracle.step(qi[t], qq[t], qs[t], qp[t], pooled, k, v, kv_type=w.kv_type, n_head_kv=w.Hk,
-                    r=w.r, top_k=w.top_k, theta=w.theta, nb_out=w.nb_max(t))
+        oracle.update_pooled(kidx, host["nc_all"][t], host["dl_all"][t], pooled, w.r, w.theta,
+                             w.eps)
+        oracle.step(host["qi"][t], host["qq"][t], host["qs"][t], host["qp"][t], pooled, k, v,
+                    kv_type=w.kv_type, n_head_kv=w.Hk, r=w.r, top_k=w.top_k, theta=w.theta,
+                    nb_out=w.nb_max(t))
         spent += time.perf_counter() - t0
         done += 1
         if spent > budget:
@@ -281,6 +405,38 @@ def cpu_baseline(w, kidx, k, v, qi, qq, qs, qp, nc_all, dl_all, W, K, budget):
             "sample": f"first {done} decode steps of one layer of {w.name} "
                       f"({w.n_seq} seq), update+score+select+attend, fp32/fp64 C oracle, "
                       f"1 thread", "tokens_per_s": round(1e6 / us, 2)}
+
+
+def cpu_baseline_prefill(w, host, budget):
+    """The oracle, single-threaded, on one layer: the ubatch's pooled-key
+    update, then bf16 scores, selection and attention for as many of its
+    queries as the budget allows; reported per query token."""
+    import oracle
+    kidx, k, v = host["kidx"], host["k"], host["v"]
+    pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
+    n0 = np.full(w.n_seq, w.n_cells0, np.int32)
+    pairs = [(0, b) for b in range(-(-w.n_cells0 // w.r))]
+    oracle.update_pooled(kidx, n0, np.array(pairs, np.int32), pooled, w.r, w.theta, w.eps)
+    t0 = time.perf_counter()
+    oracle.update_pooled(kidx, host["nc_all"][0], host["dl_all"][0], pooled, w.r, w.theta,
+                         w.eps)
+    t_update = time.perf_counter() - t0
+    qi, qq, qs, qp = host["qi"][0], host["qq"][0], host["qs"][0], host["qp"][0]
+    done, spent = 0, 0.0
+    for i in range(qp.shape[0]):
+        t0 = time.perf_counter()
+        oracle.step(qi[i:i + 1], qq[i:i + 1], qs[i:i + 1], qp[i:i + 1], pooled, k, v,
+                    kv_type=w.kv_type, n_head_kv=w.Hk, r=w.r, top_k=w.top_k, theta=w.theta,
+                    nb_out=w.nb_max(0), bf16_scores=True)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent > budget:
+            break
+    per_tok = spent / done + t_update / qp.shape[0]
+    return {"value": round(1.0 / per_tok, 2), "unit": "t/s", "cores": 1, "kind": "oracle",
+            "sample": f"one layer of the prefill ubatch: its 128-block update, then {done} of "
+                      f"{qp.shape[0]} queries (bf16 scores, selection, attention), fp32/fp64 C "
+                      f"oracle, 1 thread"}
 
 
 if __name__ == "__main__":

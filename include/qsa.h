@@ -112,6 +112,7 @@ extern "C" {
 #define QSA_OP_ATTN_PREFILL 2
 #define QSA_OP_SCORE_BF16 3
 #define QSA_OP_SCORE_SELECT 4
+#define QSA_OP_SCORE_SELECT_PREFILL 5
 
 /* Model geometry and constants.
  *   kq_scale   attention logit scale; <= 0 means 1/sqrt(head_dim)
@@ -215,6 +216,30 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
                            int32_t n_q, int32_t nb_max, int32_t *sel_blocks_dev,
                            int32_t *sel_cells_dev, int32_t *n_sel_dev, void *ws_dev,
                            size_t ws_bytes, void *stream);
+
+/* 1+2+3 for prefill  [ISSUE lever2 and lever3]: the pooled-key update of the
+ * dirty list (n_dirty may be 0), then for each query the exact top-k of
+ * qsa_select_topk_blocks over the scores of mode QSA_SCORE_BF16 taken in the
+ * canonical order T -- the bf16-rounded q' and keys, exact products, the T
+ * sum -- without writing a score matrix.  The contraction runs on the matrix
+ * cores; their sums differ from T's by at most Delta_i (a bound from |q'_i|
+ * and the RMS-normed keys' norm), so a sampled pass (every 8th group of 64
+ * blocks) gives each query a threshold below which no block of its exact
+ * top-k can score, the full pass marks the blocks above it, and only those
+ * are rescored in order T for the exact selection: sel_blocks, sel_cells
+ * and n_sel equal those of qsa_select_topk_blocks over T-ordered bf16 scores
+ * bit for bit (ties to the lower block).  If a query marks more than 8192
+ * blocks it rescores every causal block (correct, slower).
+ *   pooled_bf16_dev: required (the update writes it; the scores read it).
+ *   Workspace: qsa_workspace_size(QSA_OP_SCORE_SELECT_PREFILL, n_q, nb_max)
+ *   bytes, 16-byte aligned, no initial contents required.
+ * Needs nb_max <= 131072 (else QSA_ENOTSUP). */
+int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+                             const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
+                             uint16_t *pooled_bf16_dev, const float *q_idx_dev,
+                             const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                             int32_t nb_max, int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                             int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
 /* 1+2+3 for decode: the pooled-key update of the dirty list (n_dirty may be
  * 0), then exactly qsa_score_blocks (mode QSA_SCORE_F32) and

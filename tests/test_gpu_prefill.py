@@ -1,0 +1,142 @@
+"""GPU parity of the prefill indexer (qsa_score_select_prefill): the exact
+block top-k of many queries under the canonical order T over bf16-rounded
+operands, computed from matrix-core scores plus exact rescoring, against the
+oracle's T-ordered bf16 scores and full-sort selection -- bit for bit, on
+mixed-sequence query tiles, small and early contexts, all-tied scores (the
+path that rescores every block) and the 512-token ubatch at depth 198,628.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_sparse_attention_pooled_amd import qsa, runtime, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def oracle_pooled(w, kidx, n_cells):
+    pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
+    pairs = [(s, b) for s in range(w.n_seq) for b in range(-(-int(n_cells[s]) // w.r))]
+    oracle.update_pooled(kidx, np.asarray(n_cells, np.int32), np.array(pairs, np.int32),
+                         pooled, w.r, w.theta, w.eps)
+    return pooled
+
+
+def run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max, dirty=None):
+    n_q = q_pos.size
+    bufs = runtime.StepBuffers(layer.dims, n_q, nb_max, DEV, prefill=True)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    nd = 0 if dirty is None else dirty.shape[0]
+    qsa.score_select_prefill(layer.dims, layer.seqs(), layer.kidx,
+                             None if dirty is None else t(dirty.reshape(-1)), nd, layer.pooled,
+                             layer.pooled_bf16, t(q_idx), t(q_seq), t(q_pos), n_q, nb_max,
+                             bufs.sel_blocks, bufs.sel_cells, bufs.n_sel, bufs.ws_pf,
+                             bufs.ws_pf_bytes)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, which):
+    gb = bufs.sel_blocks.cpu().numpy()
+    gc = bufs.sel_cells.cpu().numpy()
+    gn = bufs.n_sel.cpu().numpy()
+    for i in which:
+        p = int(q_pos[i])
+        if q_seq[i] < 0 or p < 0:
+            assert gn[i] == 0
+            continue
+        r = oracle.score_query(q_idx[i], p, ref_pooled[q_seq[i]], nb_max, w.r, w.theta,
+                               bf16=True)
+        rb, rc = oracle.select(r, p, w.r, w.top_k)
+        assert gn[i] == rc.size, (i, gn[i], rc.size)
+        assert np.array_equal(gb[i, :rb.size], rb), i
+        assert np.all(gb[i, rb.size:] == -1), i
+        assert np.array_equal(gc[i, :rc.size], rc), i
+        assert np.all(gc[i, rc.size:] == -1), i
+
+
+def test_prefill_selection_exact_mixed_sequences():
+    """140 queries of two sequences (query tiles mix them), the ubatch's dirty
+    blocks updated by the same call."""
+    w = synth.Workload("pfx", 90, 2, 5000, n_new=70, steps=1, top_k=256)
+    say("prefill select: 2 seqs x 70 new tokens at depth 5000")
+    layer = runtime.Layer(w, DEV)
+    kidx = layer.kidx.cpu().numpy()
+    layer.rebuild(np.full(w.n_seq, w.n_cells0, np.int32))
+    n = synth.n_cells_at(w, 0)
+    layer.set_n_cells(n)
+    dirty = synth.dirty_blocks(w, 0)
+    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    nb_max = w.nb_max(0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max, dirty)
+    ref_pooled = oracle_pooled(w, kidx, n)
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, range(q_pos.size))
+
+
+def test_prefill_selection_small_and_early_contexts():
+    """Contexts shorter than the sample needs (every block is a candidate),
+    positions before the first complete block (tail only), invalid queries."""
+    w = synth.Workload("pfs", 91, 1, 3000, n_new=1, steps=1, top_k=256)
+    layer = runtime.Layer(w, DEV)
+    kidx = layer.kidx.cpu().numpy()
+    layer.rebuild(np.array([3001], np.int32))
+    q_pos = np.array([0, 1, 2, 3, 4, 7, 100, 255, 256, 257, 1000, 2047, 2048, 3000, -1, 5000],
+                     np.int32)
+    q_seq = np.zeros(q_pos.size, np.int32)
+    q_idx = synth.normal((q_pos.size, w.d), 91, 0, synth.T_QIDX)
+    nb_max = w.nb_max(0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max)
+    ref_pooled = oracle_pooled(w, kidx, np.array([3001]))
+    gn = bufs.n_sel.cpu().numpy()
+    assert gn[-1] == 0 and gn[-2] == 0  # p = -1 and p past the present cells
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max,
+                         range(q_pos.size - 2))
+
+
+def test_prefill_selection_all_tied_rescoring_every_block():
+    """Every pooled key zero: all scores tie at 0, every causal block passes
+    the candidate threshold, more than the candidate list holds, so every
+    block is rescored on each pass; ties go to the lower blocks."""
+    w = synth.Workload("pft", 92, 1, 40000, n_new=8, steps=1, top_k=2048)
+    kidx = np.zeros((1, w.cap_cells, w.d), np.float32)
+    layer = runtime.Layer(w, DEV, kidx=kidx)
+    n = synth.n_cells_at(w, 0)
+    layer.rebuild(n)
+    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    nb_max = w.nb_max(0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max)
+    ref_pooled = oracle_pooled(w, kidx, n)
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, range(q_pos.size))
+    gb = bufs.sel_blocks.cpu().numpy()
+    assert np.array_equal(gb[0], np.arange(512))  # the lowest blocks win every tie
+
+
+def test_prefill_selection_ubatch_at_depth():
+    """The 512-token ubatch at depth 198,628 (128 dirty blocks), oracle-checked
+    on queries spread over the ubatch."""
+    w = synth.WORKLOADS["prefill"]
+    say("prefill select: 512-token ubatch at 198,628 (oracle on 24 queries)")
+    kidx = synth.make_kidx(w)
+    layer = runtime.Layer(w, DEV, kidx=kidx, k=np.zeros((1, 1, 1, 1), np.uint8),
+                          v=np.zeros((1, 1, 1, 1), np.uint8))
+    layer.rebuild(np.full(1, w.n_cells0, np.int32))
+    n = synth.n_cells_at(w, 0)
+    layer.set_n_cells(n)
+    dirty = synth.dirty_blocks(w, 0)
+    assert int((dirty[:, 0] >= 0).sum()) == 128
+    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    nb_max = w.nb_max(0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max, dirty)
+    ref_pooled = oracle_pooled(w, kidx, n)
+    which = list(range(0, 512, 23)) + [511]
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, which)
+    gn = bufs.n_sel.cpu().numpy()
+    assert np.all(gn <= w.top_k + w.r - 1)

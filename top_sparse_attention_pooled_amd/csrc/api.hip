@@ -133,6 +133,10 @@ int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q, int32_t nb
             if (nb_max < 0) return fail(QSA_EINVAL, "nb_max negative");
             *bytes = qsa::fused_select_ws_bytes(n_q, nb_max);
             break;
+        case QSA_OP_SCORE_SELECT_PREFILL:
+            if (nb_max < 0) return fail(QSA_EINVAL, "nb_max negative");
+            *bytes = qsa::prefill_ws_bytes(n_q, nb_max);
+            break;
         default: return fail(QSA_EINVAL, "unknown op %d", op);
     }
     return ok();
@@ -278,6 +282,54 @@ static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const flo
     f->sel_cells = sel_cells_dev;
     f->n_sel = n_sel_dev;
     return QSA_OK;
+}
+
+int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+                             const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
+                             uint16_t *pooled_bf16_dev, const float *q_idx_dev,
+                             const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
+                             int32_t nb_max, int32_t *sel_blocks_dev, int32_t *sel_cells_dev,
+                             int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (!rc) rc = check_queries(q_seq_dev, q_pos_dev, n_q, true);
+    if (rc) return rc;
+    const int64_t cap_blocks = seqs->cap_cells / dims->r;
+    if (nb_max < 0 || nb_max > cap_blocks)
+        return fail(QSA_EINVAL, "nb_max %d outside 0..cap_cells/r", nb_max);
+    if (nb_max > qsa::kFusedMaxBlocks)
+        return fail(QSA_ENOTSUP, "nb_max %d above %d", nb_max, qsa::kFusedMaxBlocks);
+    if (n_dirty < 0) return fail(QSA_EINVAL, "n_dirty negative");
+    if (n_dirty > 0 && (!kidx_dev || !dirty_dev || !aligned(kidx_dev, 4) || !aligned(dirty_dev, 4)))
+        return fail(QSA_EINVAL, "kidx_dev/dirty_dev NULL or misaligned");
+    if (!pooled_dev || !aligned(pooled_dev, 16))
+        return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
+    if (!pooled_bf16_dev || !aligned(pooled_bf16_dev, 16))
+        return fail(QSA_EINVAL, "pooled_bf16_dev NULL or not 16-byte aligned");
+    if (n_q > 0 && (!q_idx_dev || !aligned(q_idx_dev, 4)))
+        return fail(QSA_EINVAL, "q_idx_dev NULL or misaligned");
+    if (n_q > 0 && (!sel_blocks_dev || !sel_cells_dev || !n_sel_dev || !aligned(sel_blocks_dev, 4) ||
+                    !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4)))
+        return fail(QSA_EINVAL, "selection outputs NULL or misaligned");
+    const size_t need = qsa::prefill_ws_bytes(n_q, nb_max);
+    if (need && (!ws_dev || ws_bytes < need || !aligned(ws_dev, 16)))
+        return fail(QSA_EWS, "prefill indexer workspace needs %zu bytes, 16-byte aligned", need);
+    const qsa::RopeTable rope = rope_table(dims->rope_theta);
+    hipError_t e = hipSuccess;
+    if (n_dirty > 0) {
+        qsa::UpdateArgs u{geom(seqs), kidx_dev,        dirty_dev, n_dirty,
+                          pooled_dev, pooled_bf16_dev, dims->r,   dims->rms_eps,
+                          dims->idx_norm_w_dev, rope};
+        e = qsa::launch_update_pooled(u, (hipStream_t)stream);
+    }
+    if (e == hipSuccess && n_q > 0 && nb_max > 0) {
+        qsa::ScoreArgs a{geom(seqs),      q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
+                         pooled_bf16_dev, nb_max,    nullptr,   0,         dims->r, rope};
+        e = qsa::launch_score_select_prefill(a, dims->idx_norm_w_dev, ws_dev, dims->top_k,
+                                             sel_blocks_dev, sel_cells_dev, n_sel_dev,
+                                             (hipStream_t)stream);
+    }
+    return launched(e, "score_select_prefill");
 }
 
 int qsa_decode_score_candidates(const qsa_dims *dims, const qsa_seqs *seqs,

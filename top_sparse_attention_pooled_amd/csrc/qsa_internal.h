@@ -87,6 +87,18 @@ __device__ __forceinline__ int64_t query_blocks(const int32_t *q_seq, const int3
     return (p + 1) / r;
 }
 
+// Roped query element pair (t, t+64) of a query at position p, fp32.
+__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p,
+                                                const RopeTable &rt, float &lo, float &hi) {
+    const float xl = q[t], xh = q[t + 64];
+    float c, s;
+    rope_cs(rt, t, p, c, s);
+    const float lc = xl * c, hs = xh * s;
+    const float hc = xh * c, ls = xl * s;
+    lo = lc - hs;
+    hi = hc + ls;
+}
+
 // Pooled key of block b of sequence s, whose first m = min(r, n - b*r) cells
 // are present (n > b*r): mean of the m per-cell keys (left-to-right fp32 sum,
 // one divide), RMS-normed (mean of squares in order T, 1/sqrt(ms + eps)
@@ -262,6 +274,21 @@ size_t fused_select_ws_bytes(int n_q, int nb_max);
 // part 1: update + scores + candidates; part 2: selection from candidates
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st);
 hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st);
+// Prefill indexer (prefill.hip): MFMA scores, a sampled lower bound of each
+// query's threshold, candidate masks, exact rescoring and selection.
+struct PrefillWs {
+    uint64_t *mask;   // [n_q][n_grp] candidate bits per 64-block group
+    float *sample;    // [n_q][ld_s] MFMA scores of every 8th group
+    uint16_t *qr;     // [n_q][128] roped queries, bf16
+    float *delta;     // [n_q] bound on |MFMA score - T score|
+    float *theta;     // [n_q] candidate threshold
+    int64_t ld_s;
+    int32_t n_grp, n_sgrp;
+};
+size_t prefill_ws_bytes(int n_q, int nb_max);
+hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, void *ws,
+                                       int top_k, int32_t *sel_blocks, int32_t *sel_cells,
+                                       int32_t *n_sel, hipStream_t st);
 size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
 size_t attn_prefill_ws_bytes(int n_q, int n_head, int ld_cells);

@@ -14,26 +14,11 @@
 // [queries x 128] x [128 x blocks] product, done on the matrix cores with
 // v_mfma_f32_16x16x32_bf16 from bf16 copies of the roped queries and keys.
 #include "cand_select.h"
+#include "mfma_tile.h"
 
 namespace qsa {
 
 namespace {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-
-// Roped query element pair (t, t+64) of query i at position p, fp32.
-__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p,
-                                                const RopeTable &rt, float &lo, float &hi) {
-    const float xl = q[t], xh = q[t + 64];
-    float c, s;
-    rope_cs(rt, t, p, c, s);
-    const float lc = xl * c, hs = xh * s;
-    const float hc = xh * c, ls = xl * s;
-    lo = lc - hs;
-    hi = hc + ls;
-}
 
 // ---------------------------------------------------------------------------
 // fp32 decode scoring
@@ -282,11 +267,6 @@ __global__ __launch_bounds__(256) void k_rope_queries_bf16(ScoreArgs a, uint16_t
     }
     qr_bf16[(int64_t)i * kDIdx + lane] = lo16;
     qr_bf16[(int64_t)i * kDIdx + lane + 64] = hi16;
-}
-
-__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
-    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // grid (ceil(nb_max/256), ceil(n_q/64)); workgroup tile 64 queries x 256

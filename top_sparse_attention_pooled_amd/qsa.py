@@ -19,13 +19,14 @@ QSA_OK, QSA_EINVAL, QSA_ENOTSUP, QSA_EWS, QSA_EHIP = 0, -1, -2, -3, -4
 KV_F32, KV_Q8_0 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
 OP_SELECT, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_SCORE_BF16, OP_SCORE_SELECT = 0, 1, 2, 3, 4
+OP_SCORE_SELECT_PREFILL = 5
 TILE = 64
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_update_pooled_keys", "qsa_score_blocks", "qsa_select_topk_blocks",
            "qsa_score_select_decode", "qsa_decode_score_candidates",
            "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
-           "qsa_decode_select_attend")
+           "qsa_decode_select_attend", "qsa_score_select_prefill")
 
 
 class QsaError(RuntimeError):
@@ -91,6 +92,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_score_select_prefill.restype = ctypes.c_int
+    lib.qsa_score_select_prefill.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, vp,
+                                             vp, vp, vp, sz, vp]
     lib.qsa_decode_select_attend.restype = ctypes.c_int
     lib.qsa_decode_select_attend.argtypes = [D, S, vp, vp, i32, i32, vp, i64, vp, vp, vp, vp, sz,
                                              vp, vp, vp, vp, vp, sz, vp]
@@ -219,6 +223,16 @@ def decode_select_candidates(dims: Dims, seqs: Seqs, q_seq, q_pos, n_q: int, nb_
                                             _ptr(q_seq), _ptr(q_pos), n_q, nb_max, _ptr(scores),
                                             ld_scores, _ptr(sel_blocks), _ptr(sel_cells),
                                             _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def score_select_prefill(dims: Dims, seqs: Seqs, kidx, dirty, n_dirty: int, pooled, pooled_bf16,
+                         q_idx, q_seq, q_pos, n_q: int, nb_max: int, sel_blocks, sel_cells,
+                         n_sel, ws, ws_bytes: int, stream=None) -> None:
+    _rc(load().qsa_score_select_prefill(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                        _ptr(kidx), _ptr(dirty), n_dirty, _ptr(pooled),
+                                        _ptr(pooled_bf16), _ptr(q_idx), _ptr(q_seq), _ptr(q_pos),
+                                        n_q, nb_max, _ptr(sel_blocks), _ptr(sel_cells),
+                                        _ptr(n_sel), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def decode_select_attend(dims: Dims, seqs: Seqs, q_seq, q_pos, n_q: int, nb_max: int, scores,

@@ -110,6 +110,9 @@ class StepBuffers:
         self.ws_score = torch.empty(max(self.ws_score_bytes, 16), dtype=torch.uint8, device=dev)
         self.ws_fused_bytes = qsa.workspace_size(dims, qsa.OP_SCORE_SELECT, n_q, nb_max)
         self.ws_fused = torch.empty(max(self.ws_fused_bytes, 16), dtype=torch.uint8, device=dev)
+        self.ws_pf_bytes = (qsa.workspace_size(dims, qsa.OP_SCORE_SELECT_PREFILL, n_q, nb_max)
+                            if prefill else 0)
+        self.ws_pf = torch.empty(max(self.ws_pf_bytes, 16), dtype=torch.uint8, device=dev)
 
 
 PATHS = ("attend", "indexer", "general")
@@ -123,13 +126,26 @@ def run_step(layer: Layer, bufs: StepBuffers, q_idx, q, q_seq, q_pos, dirty, n_d
     of three call sequences with the same results:
       attend:  qsa_decode_score_candidates, then qsa_decode_select_attend
                (decode, fp32 scores, contexts up to 65536 blocks);
-      indexer: qsa_score_select_decode, then the attention call;
-      general: update, score, select and attention as four calls."""
+      indexer: qsa_score_select_decode (fp32 scores) or, for bf16 scores,
+               qsa_score_select_prefill (exact in order T; bufs built with
+               prefill=True), then the attention call;
+      general: update, score, select and attention as four calls (with bf16
+               scores the selection follows the matrix-core sums, which match
+               T's to within a bound, not bit for bit)."""
     assert path in PATHS, path
     d, sq = layer.dims, layer.seqs()
     n_q = bufs.n_q
     if path == "attend" and (prefill or mode != qsa.SCORE_F32 or bufs.nb_max > SEL_ATTN_MAX_BLOCKS):
-        path = "indexer" if mode == qsa.SCORE_F32 else "general"
+        path = "indexer"
+    if path == "indexer" and mode == qsa.SCORE_BF16:
+        qsa.score_select_prefill(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
+                                 layer.pooled_bf16, q_idx, q_seq, q_pos, n_q, bufs.nb_max,
+                                 bufs.sel_blocks, bufs.sel_cells, bufs.n_sel, bufs.ws_pf,
+                                 bufs.ws_pf_bytes, stream=stream)
+        attn = qsa.sparse_attn_prefill if prefill else qsa.sparse_attn_decode
+        attn(d, sq, q, q_seq, n_q, layer.k, layer.v, bufs.sel_cells, bufs.n_sel, bufs.out,
+             bufs.ws_attn, bufs.ws_attn_bytes, stream=stream)
+        return StepOut(None, bufs.sel_blocks, bufs.sel_cells, bufs.n_sel, bufs.out)
     if path == "attend":
         qsa.decode_score_candidates(d, sq, layer.kidx, dirty, n_dirty, layer.pooled,
                                     layer.pooled_bf16, q_idx, q_seq, q_pos, n_q, bufs.nb_max,
