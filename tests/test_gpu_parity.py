@@ -246,7 +246,11 @@ def test_attention_matches_oracle_on_shared_cells(kv_type, H, Hk):
             worst = max(worst, err)
             assert err <= ATTN_TOL, (entry.__name__, n, err)
         say(f"  {entry.__name__}: worst max-abs error {worst:.2e}")
-        assert worst < 1e-4  # fp32 accumulation leaves far more margin than the bar
+        # decode: fp32 operands and sums leave far more margin than the bar.
+        # Prefill rounds Q*scale, K, V and P to fp16 for the matrix cores
+        # (relative 2^-11 each): a one-cell set returns its V row rounded to
+        # fp16, about 2.4e-4 * |v| off, so the bar itself applies.
+        assert worst < (ATTN_TOL if prefill else 1e-4)
 
 
 # --------------------------------------------------------------------------

@@ -140,3 +140,42 @@ def test_prefill_selection_ubatch_at_depth():
     check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, which)
     gn = bufs.n_sel.cpu().numpy()
     assert np.all(gn <= w.top_k + w.r - 1)
+
+
+def test_prefill_step_end_to_end():
+    """A whole prefill step through the ABI (exact indexer, then attention on
+    the matrix cores) against the oracle's step with T-ordered bf16 scores:
+    selections bit for bit, outputs within the attention tolerance."""
+    w = synth.Workload("pfe", 93, 2, 6000, n_new=40, steps=1, top_k=512)
+    say("prefill step: 2 seqs x 40 new tokens at depth 6000, q8_0 KV")
+    kidx = synth.make_kidx(w)
+    k = synth.make_kv(w, synth.T_K)
+    v = synth.make_kv(w, synth.T_V)
+    layer = runtime.Layer(w, DEV, kidx=kidx, k=k, v=v)
+    layer.rebuild(np.full(w.n_seq, w.n_cells0, np.int32))
+    n = synth.n_cells_at(w, 0)
+    layer.set_n_cells(n)
+    dirty = synth.dirty_blocks(w, 0)
+    q_idx, q, q_seq, q_pos = synth.make_queries(w, 0)
+    nb_max = w.nb_max(0)
+    bufs = runtime.StepBuffers(layer.dims, q_pos.size, nb_max, DEV, prefill=True)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    out = runtime.run_step(layer, bufs, t(q_idx), t(q), t(q_seq), t(q_pos),
+                           t(dirty.reshape(-1)), dirty.shape[0], mode=qsa.SCORE_BF16,
+                           prefill=True, path="indexer")
+    torch.cuda.synchronize()
+    ref_pooled = oracle_pooled(w, kidx, n)
+    ref = oracle.step(q_idx, q, q_seq, q_pos, ref_pooled, k, v, kv_type=w.kv_type,
+                      n_head_kv=w.Hk, r=w.r, top_k=w.top_k, theta=w.theta, nb_out=nb_max,
+                      bf16_scores=True)
+    gb, gc = out.sel_blocks.cpu().numpy(), out.sel_cells.cpu().numpy()
+    gn, go = out.n_sel.cpu().numpy(), out.out.cpu().numpy()
+    worst = 0.0
+    for i in range(q_pos.size):
+        rb, rc = ref["blocks"][i], ref["cells"][i]
+        assert gn[i] == rc.size
+        assert np.array_equal(gb[i, :rb.size], rb)
+        assert np.array_equal(gc[i, :rc.size], rc)
+        worst = max(worst, float(np.abs(go[i] - ref["out"][i]).max()))
+    say(f"  worst attention error {worst:.2e} (fp16 operands, fp32 sums)")
+    assert worst <= 2e-3

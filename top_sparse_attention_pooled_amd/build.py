@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqsa.so")
 # per-kernel VGPRs / scratch / occupancy reported by the compiler
 RESOURCES = os.path.join(BUILD, "resources.json")
-SOURCES = ["api.hip", "pooled.hip", "score.hip", "select.hip", "attn.hip", "prefill.hip"]
+SOURCES = ["api.hip", "pooled.hip", "score.hip", "select.hip", "attn.hip", "attn_prefill.hip",
+           "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -22,6 +22,7 @@
 // 8 int8 start at byte 34*(j/4) + 2 + 8*(j%4), which is 2 mod 4 for even
 // blocks: they are read as aligned dwords and realigned with a funnel shift.
 #include "cand_select.h"
+#include "kv_rows.h"
 #include "qsa_internal.h"
 #include "wave_ops.h"
 
@@ -32,60 +33,6 @@ namespace {
 constexpr int kChunk = 32;   // cells per chunk; a decode workgroup takes one chunk
 constexpr int kGroups = 8;   // 32-lane groups per workgroup
 constexpr int kCPG = kChunk / kGroups;  // cells per group per chunk
-
-// Raw bytes of one lane's slice (dims 8j .. 8j+7) of one K or V row.
-template <int KVT>
-struct RawRow;
-template <>
-struct RawRow<QSA_KV_F32> {
-    float4 u, v;
-};
-template <>
-struct RawRow<QSA_KV_Q8_0> {
-    uint32_t w0, w1, w2, sw;
-};
-
-template <int KVT>
-__device__ __forceinline__ RawRow<KVT> load_raw(const void *base, int64_t row, int j) {
-    RawRow<KVT> r;
-    if constexpr (KVT == QSA_KV_F32) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) +
-                                                           row * kHeadDim + 8 * j);
-        r.u = p[0];
-        r.v = p[1];
-    } else {
-        const uint8_t *b = static_cast<const uint8_t *>(base) + row * kQ8Row;
-        const int blk = j >> 2;
-        const int start = blk * kQ8Bytes + 2 + 8 * (j & 3);
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(b + (start & ~3));
-        r.w0 = w[0];
-        r.w1 = w[1];
-        r.w2 = (start & 3) ? w[2] : 0u;  // only rows whose int8 start 2 mod 4 need it
-        r.sw = *reinterpret_cast<const uint32_t *>(b + ((blk * kQ8Bytes) & ~3));
-    }
-    return r;
-}
-
-// Dequantise: q8_0 value = float(binary16 scale) * int8, exact in fp32.
-template <int KVT>
-__device__ __forceinline__ void dequant(const RawRow<KVT> &r, int j, float (&x)[8]) {
-    if constexpr (KVT == QSA_KV_F32) {
-        x[0] = r.u.x; x[1] = r.u.y; x[2] = r.u.z; x[3] = r.u.w;
-        x[4] = r.v.x; x[5] = r.v.y; x[6] = r.v.z; x[7] = r.v.w;
-    } else {
-        const int blk = j >> 2;
-        const bool odd = blk & 1;  // block start 2 mod 4: int8 aligned, scale in high half
-        const uint32_t lo = odd ? r.w0 : __builtin_amdgcn_alignbyte(r.w1, r.w0, 2);
-        const uint32_t hi = odd ? r.w1 : __builtin_amdgcn_alignbyte(r.w2, r.w1, 2);
-        const uint16_t sbits = (uint16_t)(odd ? (r.sw >> 16) : (r.sw & 0xffffu));
-        const float d = (float)__builtin_bit_cast(_Float16, sbits);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = d * (float)((int32_t)(lo << (24 - 8 * e)) >> 24);
-            x[e + 4] = d * (float)((int32_t)(hi << (24 - 8 * e)) >> 24);
-        }
-    }
-}
 
 // Sum v[0..G) over the 32 lanes of a group.  On return lane j holds the full
 // sum for head head_of_lane<G>(j) in v[0]: each halving step exchanges half
@@ -669,11 +616,5 @@ hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnAr
                                    : launch_sel_kvt<QSA_KV_Q8_0>(f, a, st);
 }
 
-size_t attn_prefill_ws_bytes(int, int, int) { return 0; }
-
-hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
-    const int chunks = decode_runs(a.ld_cells);
-    return launch(a, chunks, 1, true, st);
-}
 
 }  // namespace qsa
