@@ -346,8 +346,8 @@ def run_prefill(args, torch, dev):
         "model_prefill_t_s": round(n_q / (ms_per_step * 1e-3), 1),
         "parts_us": {k: round(v, 2) for k, v in parts.items()},
         "roofline": {
-            "kernel": "qsa_score_select_prefill (update, rope, sampled and full MFMA passes, "
-                      "exact selection), priced on the dense contraction alone",
+            "kernel": "qsa_score_select_prefill (update, rope, MFMA score matrix, radix cut "
+                      "and exact rescoring of the band at the cut), priced on the dense contraction alone",
             "timing": "events around a graph of the K*L indexer calls alone",
             "bound": "mfma",
             "achieved": round(tflops, 2) if tflops else None,

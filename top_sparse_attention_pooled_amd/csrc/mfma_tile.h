@@ -37,15 +37,13 @@ __device__ __forceinline__ void load_query_tile(const uint16_t *qr_bf16, int q0,
     }
 }
 
-// acc[rb][cb][jj] = <query row rb*16 + 4*(lane/16) + jj, block gb0 + cb*16 +
-// lane%16> over the bf16 keys of one sequence (zero columns past cap_blocks
-// or when !live).  All B operands are loaded before the first product.
-__device__ __forceinline__ void wave_tile_mfma(const bf16x8_t (&A)[4][4], const uint16_t *keys,
-                                               int64_t gb0, int64_t cap_blocks, bool live,
-                                               f32x4_t (&acc)[4][4]) {
+// B operands of blocks gb0 .. gb0+63 of one sequence's bf16 keys (zero
+// columns past cap_blocks or when !live).
+__device__ __forceinline__ void load_key_tile(const uint16_t *keys, int64_t gb0,
+                                              int64_t cap_blocks, bool live,
+                                              bf16x8_t (&B)[4][4]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int mrow = lane & 15, kseg = (lane >> 4) * 8;
-    bf16x8_t B[4][4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const int64_t nb = gb0 + cb * 16 + mrow;
@@ -55,6 +53,12 @@ __device__ __forceinline__ void wave_tile_mfma(const bf16x8_t (&A)[4][4], const 
                             ? load_bf16x8(keys + nb * kDIdx + ks * 32 + kseg)
                             : bf16x8_t{};
     }
+}
+
+// acc[rb][cb][jj] = <query row rb*16 + 4*(lane/16) + jj, block col cb*16 +
+// lane%16 of the B tile>.
+__device__ __forceinline__ void mfma_tile(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4][4],
+                                          f32x4_t (&acc)[4][4]) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -65,6 +69,15 @@ __device__ __forceinline__ void wave_tile_mfma(const bf16x8_t (&A)[4][4], const 
                 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb][ks], B[cb][ks], c, 0, 0, 0);
             acc[rb][cb] = c;
         }
+}
+
+// Both: the tile of blocks gb0 .. gb0+63.
+__device__ __forceinline__ void wave_tile_mfma(const bf16x8_t (&A)[4][4], const uint16_t *keys,
+                                               int64_t gb0, int64_t cap_blocks, bool live,
+                                               f32x4_t (&acc)[4][4]) {
+    bf16x8_t B[4][4];
+    load_key_tile(keys, gb0, cap_blocks, live, B);
+    mfma_tile(A, B, acc);
 }
 
 }  // namespace qsa

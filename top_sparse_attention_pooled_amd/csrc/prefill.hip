@@ -4,22 +4,22 @@
 // the canonical order T over bf16-rounded operands.
 //
 // The bf16 contraction runs on MFMA, whose fp32 sums differ from T only in
-// order: |s_mfma - s_T| <= Delta_i = 2^-15 * |q_i| * K_max bounds it (twice
-// (d - 1) * 2^-24 * sum |q_t k_t|, with room for the 6 key bits used as a
-// tie-break below).  The full score matrix (512 x ~50k floats at depth) is
-// never written:
+// the order of the additions: each order is within (d - 1) * 2^-24 * sum
+// |q_t k_t| of the true sum, and sum |q_t k_t| <= |q_i| * |k| with |k| <=
+// sqrt(d) * max(1, |gamma|) for an RMS-normed key, so |s_mfma - s_T| <=
+// Delta_i = 2^-15 * |q_i| * sqrt(d) * max(1, |gamma|) * (1 + 2^-8), rounded
+// up.  Selection then needs exact scores only near the cut:
 //   1. k_rope_queries_delta: roped bf16 queries and Delta_i;
-//   2. k_prefill_tiles<kSample>: MFMA over every 8th 64-block group, scores
-//      to a small matrix;
-//   3. k_sample_threshold: per query the B-th largest sampled score s_B;
-//      since at least B blocks score >= s_B - Delta exactly, every block of
-//      the exact top-B has an MFMA score >= theta_lo = s_B - 2 Delta;
-//   4. k_prefill_tiles<kFilter>: MFMA over all groups; each score is
-//      compared with theta_lo and a 64-bit mask per (query, group) marks the
-//      candidates (one compare per score; the masks are assembled from the
-//      compare results on the scalar unit);
-//   5. k_select_prefill: per query the candidates are rescored exactly in
-//      order T and the exact top-B taken, then emitted like every selection.
+//   2. k_prefill_scores: the MFMA score matrix, written densely;
+//   3. k_select_prefill, per query: a_B = the B-th largest MFMA score
+//      (radix select on the row).  Since at least B blocks have MFMA score
+//      >= a_B, the exact B-th largest S_B is >= a_B - Delta; and S_B <= a_B
+//      + Delta.  So a block with MFMA score > a_B + 2 Delta scores exactly
+//      above S_B (kept), one below a_B - 2 Delta exactly below S_B (dropped),
+//      and only the band in between is rescored in order T; the exact top
+//      (B - kept) of the band completes the set.  If the band overflows its
+//      LDS list, or Delta is outside the range where no partial sum can
+//      overflow or underflow, every causal block is rescored instead.
 #include "mfma_tile.h"
 #include "topk_engine.h"
 #include "wave_ops.h"
@@ -28,13 +28,11 @@ namespace qsa {
 
 namespace {
 
-constexpr int kSampleStride = 8;  // every 8th 64-block group is sampled
-constexpr int kSampNT = 1024;     // sample-threshold workgroup
 constexpr int kSelPNT = 512;      // selection workgroup (256 registers per lane)
-constexpr int kPrefCandCap = 8192;   // candidates per query before the slow path
+constexpr int kApproxVec = 26;    // score vectors of 4 blocks held in registers per thread
+constexpr int kBandCap = 4096;    // band blocks rescored from the LDS list
 constexpr int kPrefMaxBlocks = kFusedMaxBlocks;
-
-enum { kSample = 0, kFilter = 1 };
+constexpr float kDeltaMin = 0x1p-100f, kDeltaMax = 0x1p100f;
 
 __device__ __forceinline__ float key_value(uint32_t k) {
     const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -86,34 +84,32 @@ __global__ __launch_bounds__(256) void k_rope_queries_delta(ScoreArgs a, const f
     }
 }
 
-// 1-D grid over (group tile gt of 4 groups, query tile qt of 64 queries):
-// the hardware deals workgroup ids to the 8 XCDs round-robin, so ids are
-// laid out to put the query tiles of one group tile on one XCD, where its
-// keys are read from HBM once and then hit that XCD's L2.  Wavefront w takes
-// 64-block group (4*gt + w) * stride (sample: stride 8) for 64 queries.
-// kSample: the scores (-inf where not causal) go to w.sample[q][(4gt+w)*64 +
-// col].  kFilter: bit col of w.mask[q][group] is set if the block is causal
-// and its MFMA score >= w.theta[q].  Queries of one tile may belong to
-// different sequences: the tile is swept once per distinct sequence.
-template <int MODE>
-__global__ __launch_bounds__(256) void k_prefill_tiles(ScoreArgs a, PrefillWs w, int n_gt,
-                                                      int n_qt) {
+// 1-D grid over (slab sb of `slab` group tiles, query tile qt of 64
+// queries); a group tile is 4 groups of 64 blocks, one per wavefront.  The
+// hardware deals workgroup ids to the 8 XCDs round-robin, so ids are laid out
+// to put the query tiles of one slab on one XCD, where its keys are read
+// from HBM once and then hit that XCD's L2.  A workgroup loads its queries
+// once and sweeps its slab, writing w.approx[q][b] for every causal block of
+// its rows (other entries are left as they are: the selection never reads
+// them).  When all valid queries of the tile belong to one sequence (the
+// usual ubatch) the next group's keys are in flight while the current group
+// is on the matrix cores; otherwise each group is swept once per distinct
+// sequence.
+__global__ __launch_bounds__(256) void k_prefill_scores(ScoreArgs a, PrefillWs w, int n_gt,
+                                                       int n_qt, int slab) {
     const int id = blockIdx.x;
-    const int gt = (id / (8 * n_qt)) * 8 + (id & 7);
+    const int n_slab = (n_gt + slab - 1) / slab;
+    const int sb = (id / (8 * n_qt)) * 8 + (id & 7);
     const int qt = (id / 8) % n_qt;
-    if (gt >= n_gt) return;
+    if (sb >= n_slab) return;
+    const int gt0 = sb * slab, gt1 = min(n_gt, gt0 + slab);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
     const int q0 = qt * 64;
-    const int slot = gt * 4 + wave;  // sample column group, or group
-    const int64_t grp = MODE == kSample ? (int64_t)slot * kSampleStride : slot;
-    const int64_t gb0 = grp * 64;
     const int64_t cap_blocks = a.g.cap_cells / a.r;
-    const bool group_ok = MODE == kSample ? slot < w.n_sgrp : grp < w.n_grp;
-    if (!group_ok) return;
-    // lane r: the query of row r (sequence, causal blocks, threshold)
-    int my_seq = -2, my_nc = 0;
-    float my_th = 0.0f;
+    auto grp_of = [&](int gt) { return (int64_t)(gt * 4 + wave); };
+    // lane r: the query of row r (sequence, -1 if invalid or past n_q)
+    int my_seq = -1, my_nc = 0;
     {
         const int qi = q0 + lane;
         if (qi < a.n_q) {
@@ -123,110 +119,70 @@ __global__ __launch_bounds__(256) void k_prefill_tiles(ScoreArgs a, PrefillWs w,
                                             a.g.n_cells, a.r, my_seq, p, valid);
             if (!valid) my_seq = -1;
             my_nc = (int)(nc < a.nb_max ? nc : a.nb_max);
-            if (MODE == kFilter) my_th = w.theta[qi];
         }
     }
-
+    const uint64_t valid_rows = __ballot(my_seq >= 0);
+    if (!valid_rows) return;
     bf16x8_t A[4][4];
     load_query_tile(w.qr, q0, a.n_q, A);
-    // per-lane row constants: row rb*16 + 4*(lane/16) + jj
-    int nc_r[4][4];
-    float th_r[4][4];
+    // result lane l holds rows rb*16 + 4*(l/16) + jj of column l % 16
+    const int rsub = (lane >> 4) * 4;
+    float *const out = w.approx + (int64_t)q0 * w.ld + (lane & 15);
+    f32x4_t acc[4][4];
+    auto store_rows = [&](int64_t gb0, uint64_t rows) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = rb * 16 + (lane >> 4) * 4 + jj;
-            nc_r[rb][jj] = __shfl(my_nc, r);
-            th_r[rb][jj] = __shfl(my_th, r);
-        }
-    const int mrow = lane & 15;
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = rb * 16 + rsub + jj;
+                if (!((rows >> r) & 1)) continue;
+                float *const p = out + (int64_t)r * w.ld + gb0;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) p[cb * 16] = acc[rb][cb][jj];
+            }
+    };
 
-    uint64_t done = __ballot(my_seq == -2);  // rows past n_q: nothing to write
-    while (done != ~0ull) {
-        const int r0 = __builtin_ctzll(~done);
-        const int sq = __shfl(my_seq, r0);
-        const uint64_t rows = __ballot(my_seq == sq);
-        const int ncmax = (int)wave_max_u32((my_seq == sq) ? (uint32_t)my_nc : 0u);
-        done |= rows;
-        const bool live = sq >= 0 && gb0 < ncmax;
-        f32x4_t acc[4][4];
-        if (live) {
-            const uint16_t *keys = a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx;
-            wave_tile_mfma(A, keys, gb0, cap_blocks, true, acc);
+    const int sq0 = __shfl(my_seq, __builtin_ctzll(valid_rows));
+    if (__ballot(my_seq >= 0 && my_seq != sq0) == 0) {
+        const int ncmax = (int)wave_max_u32(my_seq >= 0 ? (uint32_t)my_nc : 0u);
+        const uint16_t *keys = a.pooled_bf16 + (int64_t)sq0 * cap_blocks * kDIdx;
+        auto live_of = [&](int gt) {
+            return grp_of(gt) < w.n_grp && grp_of(gt) * 64 < ncmax;
+        };
+        auto sweep = [&](int gt, const bf16x8_t (&B)[4][4]) {
+            if (!live_of(gt)) return;
+            mfma_tile(A, B, acc);
+            store_rows(grp_of(gt) * 64, valid_rows);
+        };
+        // two key buffers: the next group's keys are in flight while the
+        // current group is on the matrix cores
+        bf16x8_t B0[4][4], B1[4][4];
+        load_key_tile(keys, grp_of(gt0) * 64, cap_blocks, live_of(gt0), B0);
+        for (int gt = gt0; gt < gt1; gt += 2) {
+            if (gt + 1 < gt1)
+                load_key_tile(keys, grp_of(gt + 1) * 64, cap_blocks, live_of(gt + 1), B1);
+            sweep(gt, B0);
+            if (gt + 1 >= gt1) break;
+            if (gt + 2 < gt1)
+                load_key_tile(keys, grp_of(gt + 2) * 64, cap_blocks, live_of(gt + 2), B0);
+            sweep(gt + 1, B1);
         }
-        if (MODE == kSample) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int r = rb * 16 + (lane >> 4) * 4 + jj;
-                        if (!((rows >> r) & 1)) continue;
-                        const int64_t b = gb0 + cb * 16 + mrow;
-                        const float v = (live && b < nc_r[rb][jj]) ? acc[rb][cb][jj] : -INFINITY;
-                        w.sample[(int64_t)(q0 + r) * w.ld_s + slot * 64 + cb * 16 + mrow] = v;
-                    }
-        } else {
-            // lane r collects the mask of row r
-            uint32_t m_lo = 0, m_hi = 0;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    uint64_t mc[4];
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) {
-                        const int64_t b = gb0 + cb * 16 + mrow;
-                        const bool pass = live && b < nc_r[rb][jj] &&
-                                          acc[rb][cb][jj] >= th_r[rb][jj];
-                        mc[cb] = __ballot(pass);
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t lo = (uint32_t)((mc[0] >> (16 * k)) & 0xffffu) |
-                                            (uint32_t)(((mc[1] >> (16 * k)) & 0xffffu) << 16);
-                        const uint32_t hi = (uint32_t)((mc[2] >> (16 * k)) & 0xffffu) |
-                                            (uint32_t)(((mc[3] >> (16 * k)) & 0xffffu) << 16);
-                        const int r = rb * 16 + k * 4 + jj;
-                        if (lane == r) {
-                            m_lo = lo;
-                            m_hi = hi;
-                        }
-                    }
-                }
-            if ((rows >> lane) & 1)
-                w.mask[(int64_t)(q0 + lane) * w.n_grp + grp] =
-                    ((uint64_t)m_hi << 32) | (uint64_t)m_lo;
-        }
+        return;
     }
-}
-
-// grid (n_q), 1024 threads: theta_lo = s_B - 2 Delta rounded down, s_B the
-// B-th largest sampled MFMA score (-inf if the sample holds at most B).
-__global__ __launch_bounds__(kSampNT) void k_sample_threshold(ScoreArgs a, PrefillWs w, int B) {
-    __shared__ TopkSmem<kSampNT> sm;
-    const int i = blockIdx.x, tid = threadIdx.x;
-    constexpr int C = kPrefMaxBlocks / kSampleStride / kSampNT;  // 16
-    RegKeys32<C, kSampNT> keys;
-    keys.tid = tid;
-    const float *row = w.sample + (int64_t)i * w.ld_s;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int x = c * kSampNT + tid;
-        const float v = x < w.ld_s ? row[x] : -INFINITY;
-        keys.k[c] = finite_f32(v) ? score_key(v) : 0u;
-    }
-    const Thresh th = topk_threshold<kSampNT>(keys, (uint32_t)B, sm);
-    if (tid == 0) {
-        float lo = -INFINITY;
-        if (th.T != 0) {
-            const double t = (double)key_value(th.T) - 2.0 * (double)w.delta[i];
-            lo = (float)t;
-            if ((double)lo > t) lo = nextafterf(lo, -INFINITY);
+    for (int gt = gt0; gt < gt1; ++gt) {
+        if (grp_of(gt) >= w.n_grp) continue;
+        const int64_t gb0 = grp_of(gt) * 64;
+        uint64_t done = ~valid_rows;
+        while (done != ~0ull) {
+            const int sq = __shfl(my_seq, __builtin_ctzll(~done));
+            const uint64_t rows = __ballot(my_seq == sq);
+            const int ncmax = (int)wave_max_u32((my_seq == sq) ? (uint32_t)my_nc : 0u);
+            done |= rows;
+            if (gb0 >= ncmax) continue;
+            wave_tile_mfma(A, a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx, gb0, cap_blocks,
+                           true, acc);
+            store_rows(gb0, rows);
         }
-        w.theta[i] = lo;
     }
 }
 
@@ -274,26 +230,59 @@ struct PrefSelSmem {
     TopkSmem<kSelPNT> tk;
     float q[kDIdx];
     uint32_t bitmap[kPrefMaxBlocks / 32];
-    uint64_t list[kPrefCandCap];  // candidate blocks, then their exact keys
+    uint64_t band[kBandCap];  // band blocks, then their exact keys
+    uint32_t n_band;
 };
 
-// Candidate keys, exact, in registers (slot c holds list entry c*NT + tid);
-// or, if the candidates overflowed the list, every causal block rescored on
-// each pass.
-struct PrefSource {
-    uint64_t k[kPrefCandCap / kSelPNT];
-    bool stream;
+__device__ __forceinline__ uint32_t approx_key(float v, int64_t b, int64_t limit) {
+    return (b < limit && finite_f32(v)) ? score_key(v) : 0u;
+}
+
+// Keys of the MFMA scores of one query's causal blocks, as (k, ~block):
+// blocks 4x .. 4x+3 for x = c * kSelPNT + tid, in registers for c <
+// kApproxVec and re-read from the row beyond.
+struct ApproxKeys {
+    uint32_t k[kApproxVec][4];
+    const float *row;
+    int64_t limit;
+    int n_vec;
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int c = 0; c < kApproxVec; ++c) {
+            const uint32_t b0 = (uint32_t)(c * kSelPNT + tid) * 4u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fn(k[c][e], ~(b0 + e));
+        }
+        for (int x = kApproxVec * kSelPNT + tid; x < n_vec; x += kSelPNT) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(row + 4 * (int64_t)x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t b = 4 * (int64_t)x + e;
+                fn(approx_key(v[e], b, limit), ~(uint32_t)b);
+            }
+        }
+    }
+};
+
+// Exact keys of the band list (slot c holds entry c * kSelPNT + tid).
+struct BandKeys {
+    uint64_t k[kBandCap / kSelPNT];
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+#pragma unroll
+        for (int c = 0; c < kBandCap / kSelPNT; ++c) fn((uint32_t)(k[c] >> 32), (uint32_t)k[c]);
+    }
+};
+
+// Every causal block rescored exactly, on each pass.
+struct ExactStream {
     int64_t limit;
     const uint16_t *keys;
     const float *q;
     template <typename F>
     __device__ __forceinline__ void operator()(F &&fn) const {
-        if (!stream) {
-#pragma unroll
-            for (int c = 0; c < kPrefCandCap / kSelPNT; ++c)
-                fn((uint32_t)(k[c] >> 32), (uint32_t)k[c]);
-            return;
-        }
         for (int64_t b = threadIdx.x; b < limit; b += kSelPNT) {
             const float sc = exact_score(keys + b * kDIdx, q);
             fn(finite_f32(sc) ? score_key(sc) : 0u, ~(uint32_t)b);
@@ -301,7 +290,12 @@ struct PrefSource {
     }
 };
 
-// grid (n_q), 1024 threads.
+__device__ __forceinline__ void mark(uint32_t *bm, uint32_t b) {
+    atomicOr(&bm[b >> 5], 1u << (b & 31));
+}
+
+// grid (n_q), kSelPNT threads: the exact top-B of query i from its row of
+// MFMA scores plus exact rescoring of the band around the cut.
 __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, PrefillWs w, int top_k,
                                                             int32_t *sel_blocks,
                                                             int32_t *sel_cells, int32_t *n_sel) {
@@ -317,75 +311,107 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
     const int64_t cap_blocks = a.g.cap_cells / a.r;
     const uint16_t *keys = a.pooled_bf16 + (valid ? (int64_t)s * cap_blocks * kDIdx : 0);
     if (tid < kDIdx) sm.q[tid] = bf16_value(w.qr[(int64_t)i * kDIdx + tid]);
+    if (tid == 0) sm.n_band = 0;
     const int n_words = (int)((limit + 31) / 32);
     for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
+    const float delta = w.delta[i];
+    const bool safe = delta >= kDeltaMin && delta <= kDeltaMax;  // false for NaN
+    bool exact_all = limit > 0 && !safe;
 
-    // candidate masks of this query's groups: count, scan, list
-    constexpr int kMW = kPrefMaxBlocks / 64 / kSelPNT;  // mask words per thread
-    const int n_g = (int)((limit + 63) / 64);
-    uint64_t m[kMW];
-    uint32_t local = 0;
+    if (limit > 0 && safe) {
+        ApproxKeys ak;
+        ak.row = w.approx + (int64_t)i * w.ld;
+        ak.limit = limit;
+        ak.n_vec = (int)((limit + 3) / 4);
 #pragma unroll
-    for (int c = 0; c < kMW; ++c) {
-        const int g = tid * kMW + c;  // consecutive groups per thread
-        m[c] = g < n_g ? w.mask[(int64_t)i * w.n_grp + g] : 0ull;
-        local += __popcll(m[c]);
-    }
-    const int lane = tid & (kWave - 1), wave = tid >> 6;
-    const uint32_t incl = wave_incl_scan_u32(local);
-    if (lane == kWave - 1) sm.tk.red[wave] = incl;
-    __syncthreads();
-    uint32_t pos = incl - local, total = 0;
+        for (int c = 0; c < kApproxVec; ++c) {
+            const int x = c * kSelPNT + tid;
+            f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+            if (x < ak.n_vec) v = *reinterpret_cast<const f32x4_t *>(ak.row + 4 * (int64_t)x);
 #pragma unroll
-    for (int x = 0; x < kSelPNT / kWave; ++x) {
-        if (x < wave) pos += sm.tk.red[x];
-        total += sm.tk.red[x];
-    }
-    const bool stream = total > (uint32_t)kPrefCandCap;
-    if (!stream) {
+            for (int e = 0; e < 4; ++e) ak.k[c][e] = approx_key(v[e], 4 * (int64_t)x + e, limit);
+        }
+        // with Delta in range no sum overflows, so every causal block has a
+        // finite score under both orders
+        uint32_t cnt = 0, mn = ~0u, mx = 0u;
+        ak([&](uint32_t k, uint32_t) {
+            if (!k) return;
+            ++cnt;
+            mn = min(mn, k);
+            mx = max(mx, k);
+        });
+        // low 18 bits: valid keys (<= 2^17); above: threads holding one
+        const uint32_t packed = block_sum_u32<kSelPNT>(cnt + (cnt ? 1u << 18 : 0u), sm.tk);
+        const uint32_t n_valid = packed & ((1u << 18) - 1u), n_holders = packed >> 18;
+        if (n_valid <= (uint32_t)B) {
+            ak([&](uint32_t k, uint32_t u) {
+                if (k) mark(sm.bitmap, ~u);
+            });
+        } else {
+            // Every holder has a key >= its own largest, so at least
+            // n_holders keys are >= the smallest of those maxima: if that is
+            // B or more, the B-th largest lies above it, and the first
+            // radix round bins only the top of the distribution (not the
+            // bulk, whose keys would crowd a few bins).
+            uint32_t lo = cnt ? mx : ~0u, hi = mx;
+            block_minmax_u32<kSelPNT>(lo, hi, sm.tk);
+            if (n_holders < (uint32_t)B) {
+                uint32_t unused = 0u;
+                block_minmax_u32<kSelPNT>(mn, unused, sm.tk);
+                lo = mn;
+            }
+            const float a_B = key_value(kth_largest_u32<kSelPNT>(ak, (uint32_t)B, lo, hi, sm.tk));
+            const double tlo = (double)a_B - 2.0 * (double)delta;
+            const double thi = (double)a_B + 2.0 * (double)delta;
+            float flo = (float)tlo, fhi = (float)thi;
+            if ((double)flo > tlo) flo = nextafterf(flo, -INFINITY);
+            if ((double)fhi < thi) fhi = nextafterf(fhi, INFINITY);
+            const uint32_t k_lo = score_key(flo), k_hi = score_key(fhi);
+            uint32_t n_keep = 0;
+            ak([&](uint32_t k, uint32_t u) {
+                if (k > k_hi) {
+                    mark(sm.bitmap, ~u);
+                    ++n_keep;
+                } else if (k >= k_lo) {
+                    const uint32_t at = atomicAdd(&sm.n_band, 1u);
+                    if (at < (uint32_t)kBandCap) sm.band[at] = (uint64_t)(~u);
+                }
+            });
+            n_keep = block_sum_u32<kSelPNT>(n_keep, sm.tk);  // ends with a barrier
+            const uint32_t n_band = sm.n_band;
+            if (n_band > (uint32_t)kBandCap) {
+                exact_all = true;
+                for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
+                __syncthreads();
+            } else {
+                for (int x = tid; x < (int)n_band; x += kSelPNT) {
+                    const int64_t b = (int64_t)sm.band[x];
+                    sm.band[x] = block_key(exact_score(keys + b * kDIdx, sm.q), b);
+                }
+                __syncthreads();
+                BandKeys bk;
 #pragma unroll
-        for (int c = 0; c < kMW; ++c) {
-            uint64_t bits = m[c];
-            const int g = tid * kMW + c;
-            while (bits) {
-                const int bit = __builtin_ctzll(bits);
-                bits &= bits - 1;
-                sm.list[pos++] = (uint64_t)(g * 64 + bit);
+                for (int c = 0; c < kBandCap / kSelPNT; ++c) {
+                    const int x = c * kSelPNT + tid;
+                    bk.k[c] = x < (int)n_band ? sm.band[x] : 0ull;
+                }
+                const Thresh th = topk_threshold<kSelPNT>(bk, (uint32_t)B - n_keep, sm.tk);
+                bk([&](uint32_t k, uint32_t u) {
+                    if (th.keep(k, u)) mark(sm.bitmap, ~u);
+                });
             }
         }
     }
-    __syncthreads();
-    // exact keys in place, two candidates per thread at a time (their key
-    // rows in flight together)
-    if (!stream) {
-        for (int x = tid; x < (int)total; x += 2 * kSelPNT) {
-            const int x2 = x + kSelPNT;
-            const int64_t b = (int64_t)sm.list[x];
-            const int64_t b2 = x2 < (int)total ? (int64_t)sm.list[x2] : b;
-            const float sc = exact_score(keys + b * kDIdx, sm.q);
-            const float sc2 = exact_score(keys + b2 * kDIdx, sm.q);
-            sm.list[x] = finite_f32(sc) ? block_key(sc, b) : 0ull;
-            if (x2 < (int)total) sm.list[x2] = finite_f32(sc2) ? block_key(sc2, b2) : 0ull;
-        }
+    if (exact_all) {
+        ExactStream src;
+        src.limit = limit;
+        src.keys = keys;
+        src.q = sm.q;
+        const Thresh th = topk_threshold<kSelPNT>(src, (uint32_t)B, sm.tk);
+        src([&](uint32_t k, uint32_t u) {
+            if (th.keep(k, u)) mark(sm.bitmap, ~u);
+        });
     }
-    __syncthreads();
-    PrefSource src;
-    src.stream = stream;
-    src.limit = limit;
-    src.keys = keys;
-    src.q = sm.q;
-#pragma unroll
-    for (int c = 0; c < kPrefCandCap / kSelPNT; ++c) {
-        const int x = c * kSelPNT + tid;
-        src.k[c] = (!stream && x < (int)total) ? sm.list[x] : 0ull;
-    }
-    const Thresh th = topk_threshold<kSelPNT>(src, (uint32_t)B, sm.tk);
-    src([&](uint32_t k, uint32_t u) {
-        if (th.keep(k, u)) {
-            const uint32_t bb = ~u;
-            atomicOr(&sm.bitmap[bb >> 5], 1u << (bb & 31));
-        }
-    });
     __syncthreads();
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = top_k + a.r - 1;
@@ -401,20 +427,16 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
 static size_t prefill_layout(char *base, int n_q, int nb_max, PrefillWs *w) {
     PrefillWs d{};
     d.n_grp = (nb_max + 255) / 256 * 4;
-    d.n_sgrp = (d.n_grp + kSampleStride - 1) / kSampleStride;
-    d.n_sgrp = (d.n_sgrp + 3) / 4 * 4;
-    d.ld_s = (int64_t)d.n_sgrp * 64;
+    d.ld = (int64_t)d.n_grp * 64;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
         off += (bytes + 255) / 256 * 256;
         return base ? base + at : nullptr;
     };
-    d.mask = reinterpret_cast<uint64_t *>(take((size_t)n_q * d.n_grp * 8));
-    d.sample = reinterpret_cast<float *>(take((size_t)n_q * d.ld_s * 4));
+    d.approx = reinterpret_cast<float *>(take((size_t)n_q * d.ld * 4));
     d.qr = reinterpret_cast<uint16_t *>(take((size_t)n_q * kDIdx * 2));
     d.delta = reinterpret_cast<float *>(take((size_t)n_q * 4));
-    d.theta = reinterpret_cast<float *>(take((size_t)n_q * 4));
     if (w) *w = d;
     return off;
 }
@@ -432,14 +454,13 @@ hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, v
     hipLaunchKernelGGL(k_rope_queries_delta, dim3((a.n_q + 3) / 4), dim3(256), 0, st, a, gamma,
                        w);
     const int qt = (a.n_q + 63) / 64;
-    // group tiles padded to whole rounds of the 8 XCDs (k_prefill_tiles maps ids)
-    auto tiles = [&](int n_gt) { return (n_gt + 7) / 8 * 8 * qt; };
-    hipLaunchKernelGGL(k_prefill_tiles<kSample>, dim3(tiles(w.n_sgrp / 4)), dim3(256), 0, st, a,
-                       w, w.n_sgrp / 4, qt);
-    hipLaunchKernelGGL(k_sample_threshold, dim3(a.n_q), dim3(kSampNT), 0, st, a, w,
-                       top_k / a.r);
-    hipLaunchKernelGGL(k_prefill_tiles<kFilter>, dim3(tiles(w.n_grp / 4)), dim3(256), 0, st, a, w,
-                       w.n_grp / 4, qt);
+    // slabs of group tiles: about 512 workgroups (two per CU); the grid is
+    // padded to whole rounds of the 8 XCDs (k_prefill_scores maps ids)
+    const int n_gt = w.n_grp / 4;
+    const int n_slab = max(1, min(n_gt, 512 / qt));
+    const int slab = (n_gt + n_slab - 1) / n_slab;
+    const int grid = ((n_gt + slab - 1) / slab + 7) / 8 * 8 * qt;
+    hipLaunchKernelGGL(k_prefill_scores, dim3(grid), dim3(256), 0, st, a, w, n_gt, qt, slab);
     hipLaunchKernelGGL(k_select_prefill, dim3(a.n_q), dim3(kSelPNT), 0, st, a, w, top_k,
                        sel_blocks, sel_cells, n_sel);
     return hipGetLastError();

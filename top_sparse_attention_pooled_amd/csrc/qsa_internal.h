@@ -16,6 +16,11 @@
 namespace qsa {
 
 constexpr int kWave = 64;
+
+// Index of the calling wavefront in its workgroup, as a scalar (uniform).
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 constexpr int kDIdx = 128;   // indexer dim this build implements
 constexpr int kHeadDim = 256;
 constexpr int kTile = 64;    // blocks per pooled-key tile
@@ -274,16 +279,14 @@ size_t fused_select_ws_bytes(int n_q, int nb_max);
 // part 1: update + scores + candidates; part 2: selection from candidates
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st);
 hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st);
-// Prefill indexer (prefill.hip): MFMA scores, a sampled lower bound of each
-// query's threshold, candidate masks, exact rescoring and selection.
+// Prefill indexer (prefill.hip): MFMA scores, then per query the exact top-B
+// with exact rescoring of the blocks near the cut.
 struct PrefillWs {
-    uint64_t *mask;   // [n_q][n_grp] candidate bits per 64-block group
-    float *sample;    // [n_q][ld_s] MFMA scores of every 8th group
+    float *approx;    // [n_q][ld] MFMA scores (entries of causal blocks only)
     uint16_t *qr;     // [n_q][128] roped queries, bf16
     float *delta;     // [n_q] bound on |MFMA score - T score|
-    float *theta;     // [n_q] candidate threshold
-    int64_t ld_s;
-    int32_t n_grp, n_sgrp;
+    int64_t ld;
+    int32_t n_grp;
 };
 size_t prefill_ws_bytes(int n_q, int nb_max);
 hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, void *ws,

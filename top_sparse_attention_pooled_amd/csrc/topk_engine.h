@@ -49,7 +49,7 @@ struct Thresh {
 
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     v = wave_sum_u32(v);
     if (lane == 0) sm.red[wave] = v;
     __syncthreads();
@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) 
 // Block-wide (min, max) of per-thread values.
 template <int NT>
 __device__ __forceinline__ void block_minmax_u32(uint32_t &mn, uint32_t &mx, TopkSmem<NT> &sm) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
     if (lane == 0) {
@@ -162,6 +162,30 @@ __device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pre
     return lo;
 }
 
+// The krem-th largest value among the keys k in [lo, hi] (k = 0 never
+// counts when lo > 0): the same binning, continued until the bin is a single
+// value (at most 3 rounds of 11 bits).  The caller guarantees that [lo, hi]
+// holds at least krem keys.
+template <int NT, typename ForEach>
+__device__ __forceinline__ uint32_t kth_largest_u32(const ForEach &for_each, uint32_t krem,
+                                                    uint32_t lo, uint32_t hi, TopkSmem<NT> &sm) {
+    while (lo != hi) {
+        const int shift = range_shift(lo, hi);
+        for (int j = threadIdx.x; j < kBins; j += NT) sm.hist[j] = 0;
+        __syncthreads();
+        for_each([&](uint32_t k, uint32_t) {
+            if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> shift], 1u);
+        });
+        __syncthreads();
+        pick_bin<NT>(sm, lo, hi, shift, krem);
+        krem -= sm.b_above;
+        lo = sm.b_lo;
+        hi = sm.b_hi;
+        __syncthreads();
+    }
+    return lo;
+}
+
 // The exact kept set of the top B (or every valid element if there are at
 // most B).
 template <int NT, typename ForEach>
@@ -213,7 +237,7 @@ __device__ void emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, 
     const int w0 = threadIdx.x * per;
     uint32_t local = 0;
     for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(bm[w]);
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     const uint32_t incl = wave_incl_scan_u32(local);
     if (lane == kWave - 1) sm.red[wave] = incl;
     __syncthreads();
