@@ -289,10 +289,16 @@ int qsa_decode_select_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
  * cells c_j listed in sel_cells[i]:
  *   l_j = kq_scale * <q[i][h], K[c_j]>,  w = softmax(l),
  *   out[i][h] = sum_j w_j * V[c_j]
- * with K and V dequantised to fp32 and fp32 accumulation.  Cells outside
- * 0 .. min(n_cells, cap_cells)-1 are ignored; an empty set gives zeros.
- * Decode is tuned for few queries (split over cells, then a combine), prefill
- * for many.  Both need the workspace qsa_workspace_size reports. */
+ * Decode dequantises K and V to fp32 and accumulates in fp32.  Prefill runs
+ * both products on the matrix cores with fp16 operands and fp32 sums (q *
+ * kq_scale, P and V -- q8_0 V as int8 times its scale -- rounded to fp16;
+ * q8_0 K enters as exact integers with its block scale applied to the fp32
+ * partial sum; f32 K rounded to fp16), so it agrees with decode to about
+ * 1e-3 absolute for unit-scale inputs.  Cells outside 0 ..
+ * min(n_cells, cap_cells)-1 are ignored; an empty set gives zeros.  Decode is
+ * tuned for few queries (split over cells, then a combine), prefill for many.
+ * Both need the workspace qsa_workspace_size reports.  QSA_EINVAL if the
+ * cache has 2^31 rows (n_seq * cap_cells * n_head_kv) or more. */
 int qsa_sparse_attn_decode(const qsa_dims *dims, const qsa_seqs *seqs,
                            const float *q_dev, const int32_t *q_seq_dev,
                            int32_t n_q, const void *k_cache_dev,

@@ -416,6 +416,8 @@ static int attn_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_
         return fail(QSA_EINVAL, "K/V cache NULL or not 16-byte aligned");
     if (!sel_cells_dev || !n_sel_dev || !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
         return fail(QSA_EINVAL, "selection NULL or misaligned");
+    if ((int64_t)seqs->n_seq * seqs->cap_cells * dims->n_head_kv >= ((int64_t)1 << 31))
+        return fail(QSA_EINVAL, "K/V cache of 2^31 rows or more");
     const int ld_cells = dims->top_k + dims->r - 1;
     const size_t need = prefill ? qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells)
                                 : qsa::attn_decode_ws_bytes(n_q, dims->n_head, ld_cells);

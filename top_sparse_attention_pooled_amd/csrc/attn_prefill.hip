@@ -9,14 +9,21 @@
 // the hpk <= 8 query heads of the KV head as the 16 M-rows of the tiles
 // (rows past hpk are zero):
 //   S  = (scale * Q) K^T  : 2 tiles of 16 cells x 8 k-steps of 32 dims with
-//        v_mfma_f32_16x16x32_f16; a k-step is one q8_0 block, dequantised to
-//        fp16 in registers straight into the B operand (8 dims per lane);
+//        v_mfma_f32_16x16x32_f16.  For q8_0 a k-step is one block: its int8
+//        go into the B operand as exact fp16 integers (byte | 0x6400 is 1024
+//        + byte) and the block scale multiplies the k-step's fp32 result;
 //   online softmax on S in the accumulator layout (a head row's 16 columns
 //        sit in one 16-lane DPP row);
 //   O += P V : P goes through LDS to the A layout, V is staged transposed in
-//        LDS as fp16 [dim][cell] so each B operand is one 16-byte read.
-// Operands are rounded to fp16 (Q * scale, K, V, P); sums and the softmax
-// state are fp32.
+//        LDS as fp16 [dim][cell] (q8_0: int8 times its scale, one fp16
+//        rounding) so each B operand is one 16-byte read.
+// q8_0 rows reach the wavefront as whole 16-byte pieces: the chunk's 64 rows
+// (K and V, 272 bytes each) are 17 coalesced loads per lane, prefetched one
+// chunk ahead in registers and written to an LDS stage, from which the
+// operands are read.  f32 rows (the small configuration) are gathered per
+// lane straight into the operand layout.
+// Operands are rounded to fp16 (Q * scale, P, V; f32 K); sums and the
+// softmax state are fp32.
 #include "kv_rows.h"
 #include "qsa_internal.h"
 #include "wave_ops.h"
@@ -26,13 +33,20 @@ namespace qsa {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPChunk = 32;  // cells per chunk
 constexpr int kPWaves = 4;
-constexpr int kCellCap = 4096;  // cell indices held in LDS; the rest are read directly
+constexpr int kStride = kPWaves * kPChunk;
+constexpr int kCellCap = 4096;  // f32 kernel: cell indices held in LDS; the rest read directly
+constexpr int kStageWords = 2 * kPChunk * kQ8Row / 4;  // raw K rows, then V rows
+constexpr int kPieces = 2 * kPChunk * kQ8Row / 16;     // 16-byte pieces per chunk
+static_assert(kPieces == 17 * kWave, "a chunk is 17 loads of 16 bytes per lane");
 
-struct PrefAttnWave {
+// Per-wavefront LDS shared by both kernels.
+struct WaveTail {
     union {
         _Float16 vt[kHeadDim][kPChunk];  // V of the chunk, transposed
         float o[16][kHeadDim / 4];       // merge: a quarter of the dims at a time
@@ -40,12 +54,58 @@ struct PrefAttnWave {
     _Float16 p[16][kPChunk];  // probabilities, [head row][cell]
     float m[16], l[16];
 };
+struct F32Wave {
+    WaveTail t;
+};
+struct Q8Wave {
+    uint32_t stage[kStageWords];  // [K, V][cell slot][272 bytes], as loaded
+    WaveTail t;
+};
 
 __device__ __forceinline__ half8_t to_half8(const float (&x)[8]) {
     half8_t h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
     return h;
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Bytes 0, 1 (sel kLowPair) or 2, 3 (kHighPair) of x, each as the fp16 1024 + byte.
+constexpr uint32_t kLowPair = 0x04010400u, kHighPair = 0x04030402u;
+__device__ __forceinline__ half2_t byte_pair_1024(uint32_t x, uint32_t sel) {
+    return as_half2(__builtin_amdgcn_perm(0x64646464u, x, sel));
+}
+
+// Four int8 of w (two's complement) as exact fp16: (b ^ 0x80) is b + 128 as
+// an unsigned byte, so 1024 + (b ^ 0x80) - 1152 = b.
+__device__ __forceinline__ void int8x4_to_half(uint32_t w, half2_t &h01, half2_t &h23) {
+    const half2_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    w ^= 0x80808080u;
+    h01 = byte_pair_1024(w, kLowPair) + off;
+    h23 = byte_pair_1024(w, kHighPair) + off;
+}
+
+// Dims 8j .. 8j+7 of a staged q8_0 row (block j/4 at byte 34*(j/4), its
+// int8 from byte 2): the 8 int8, realigned when the block is even (its int8
+// then start 2 mod 4).  The alignment depends on j/4 only.
+__device__ __forceinline__ void staged_slice(const uint8_t *row, int j, uint32_t &lo,
+                                             uint32_t &hi) {
+    const int blk = j >> 2, off = blk * kQ8Bytes + 2 + 8 * (j & 3);
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(row + (off & ~3));
+    if (blk & 1) {
+        lo = w[0];
+        hi = w[1];
+    } else {
+        const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+        lo = __builtin_amdgcn_alignbyte(w1, w0, 2);
+        hi = __builtin_amdgcn_alignbyte(w2, w1, 2);
+    }
+}
+// binary16 bits of the scale of block blk of a staged q8_0 row.
+__device__ __forceinline__ uint32_t staged_scale(const uint8_t *row, int blk) {
+    return *reinterpret_cast<const uint16_t *>(row + blk * kQ8Bytes);
 }
 
 // Max / sum over the 16 lanes of a DPP row.
@@ -64,42 +124,173 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Query state common to both kernels.
+struct QueryCtx {
+    int n;              // cells in the list
+    int64_t n_present;  // cells of the sequence
+    const int32_t *cells;
+    int64_t row0;  // first cell row of the sequence
+};
+
+__device__ __forceinline__ QueryCtx query_ctx(const AttnArgs &a, int i) {
+    QueryCtx c;
+    const int s = a.q_seq[i];
+    const bool qvalid = s >= 0 && s < a.g.n_seq;
+    const int n = qvalid ? a.n_sel[i] : 0;
+    c.n = n < 0 ? 0 : (n > a.ld_cells ? a.ld_cells : n);
+    const int64_t np = qvalid ? a.g.n_cells[s] : 0;
+    c.n_present = np < a.g.cap_cells ? np : a.g.cap_cells;
+    c.cells = a.sel_cells + (int64_t)i * a.ld_cells;
+    c.row0 = (int64_t)(qvalid ? s : 0) * a.g.cap_cells;
+    return c;
+}
+
+// A operand of S: row col = head g*hpk + col (zero past hpk), dims 32*kb +
+// 8*quad .. +7, scaled, fp16.
+__device__ __forceinline__ void load_q_operand(const AttnArgs &a, int i, int g, int hpk, int col,
+                                               int quad, half8_t (&qa)[8]) {
+    const bool live = col < hpk;
+    // every load is issued (a dead row reads head g*hpk), then selected
+    const float4 *qp = reinterpret_cast<const float4 *>(
+        a.q + ((int64_t)i * a.n_head + g * hpk + (live ? col : 0)) * kHeadDim + 8 * quad);
+    float4 raw[16];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        raw[2 * kb] = qp[8 * kb];
+        raw[2 * kb + 1] = qp[8 * kb + 1];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const float4 u = raw[2 * kb], v = raw[2 * kb + 1];
+        const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = live ? x[e] * a.scale : 0.0f;
+        qa[kb] = to_half8(y);
+    }
+}
+
+// Online softmax of a chunk's two S tiles (column col of tile t is chunk
+// cell 16t + col; -inf where there is no cell) into the running state, and
+// P to LDS.
+__device__ __forceinline__ void softmax_chunk(const f32x4 (&sacc)[2], int col, int quad,
+                                              float (&m_run)[4], float (&l_run)[4],
+                                              f32x4 (&o)[16], WaveTail &t) {
+    float corr[4];
+    bool moved = false;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const float mx = row16_max(fmaxf(sacc[0][jj], sacc[1][jj]));
+        const float m_new = fmaxf(m_run[jj], mx);
+        const float p0 = m_new == -INFINITY ? 0.f : __expf(sacc[0][jj] - m_new);
+        const float p1 = m_new == -INFINITY ? 0.f : __expf(sacc[1][jj] - m_new);
+        corr[jj] = m_run[jj] == -INFINITY ? 0.f : __expf(m_run[jj] - m_new);
+        moved |= m_new != m_run[jj];
+        l_run[jj] = l_run[jj] * corr[jj] + row16_sum(p0 + p1);
+        m_run[jj] = m_new;
+        t.p[4 * quad + jj][col] = (_Float16)p0;
+        t.p[4 * quad + jj][16 + col] = (_Float16)p1;
+    }
+    // a row whose max did not move has corr 1 (or o still 0): the rescale
+    // is skipped when no row of the wavefront moved
+    if (__ballot(moved)) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) o[tt][jj] *= corr[jj];
+    }
+}
+
+// O += P V from LDS: A = P[row col][cells 8*quad ..], B = V[cells 8*quad ..][dim].
+__device__ __forceinline__ void pv_chunk(const WaveTail &t, int col, int quad, f32x4 (&o)[16]) {
+    const half8_t pa = *reinterpret_cast<const half8_t *>(&t.p[col][8 * quad]);
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+        const half8_t vb = *reinterpret_cast<const half8_t *>(&t.vt[16 * tt + col][8 * quad]);
+        o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[tt], 0, 0, 0);
+    }
+}
+
+// Merge the four wavefronts' states, a quarter of the dims at a time, and
+// write the heads of KV head g.
+template <typename W>
+__device__ __forceinline__ void merge_store(const AttnArgs &a, int i, int g, int hpk,
+                                            W (&sw)[kPWaves], const f32x4 (&o)[16],
+                                            const float (&m_run)[4], const float (&l_run)[4]) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int col = lane & 15, quad = lane >> 4;
+    WaveTail &t = sw[tid >> 6].t;
+    if (col == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            t.m[4 * quad + jj] = m_run[jj];
+            t.l[4 * quad + jj] = l_run[jj];
+        }
+    }
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+        __syncthreads();
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int tt = part * 4 + t4;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) t.o[4 * quad + jj][16 * t4 + col] = o[tt][jj];
+        }
+        __syncthreads();
+        // thread: head row r = tid / 16 (16 rows), dims 4*(tid%16) .. +3 of the quarter
+        const int r = tid >> 4, d0 = (tid & 15) * 4;
+        if (r < hpk) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kPWaves; ++w) M = fmaxf(M, sw[w].t.m[r]);
+            float L = 0.f, wt[kPWaves];
+#pragma unroll
+            for (int w = 0; w < kPWaves; ++w) {
+                wt[w] = sw[w].t.m[r] == -INFINITY ? 0.f : __expf(sw[w].t.m[r] - M);
+                L += sw[w].t.l[r] * wt[w];
+            }
+            float *outp = a.out + ((int64_t)i * a.n_head + g * hpk + r) * kHeadDim + part * 64 + d0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float acc = 0.f;
+#pragma unroll
+                for (int w = 0; w < kPWaves; ++w) acc += sw[w].t.o[r][d0 + e] * wt[w];
+                outp[e] = L > 0.f ? acc / L : 0.f;
+            }
+        }
+    }
+}
+
+// ---- q8_0 rows, staged through LDS ----
+
+// Load k (0..16) of a chunk: loads 0..7 are K rows of slots 4k .. 4k+3 (16
+// lanes a row, bytes 0..255), loads 8..15 the same for V, load 16 the last
+// 16 bytes of the K row (lanes < 32) or V row (lanes >= 32) of slot lane%32.
+__device__ __forceinline__ int piece_slot(int k, int lane) {
+    return k < 16 ? 4 * (k & 7) + (lane >> 4) : (lane & 31);
+}
+__device__ __forceinline__ int piece_kv(int k, int lane) { return k < 16 ? (k >> 3) : (lane >> 5); }
+__device__ __forceinline__ int piece_part(int k, int lane) { return k < 16 ? (lane & 15) : 16; }
+
 // grid (n_head_kv, n_q), 256 threads.
-template <int KVT>
-__global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
-    __shared__ PrefAttnWave sw[kPWaves];
-    __shared__ int32_t s_cells[kCellCap];  // the query's cell list (its first kCellCap)
+__global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
+    __shared__ Q8Wave sw[kPWaves];
     const int g = blockIdx.x, i = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;  // MFMA column / k-quarter
     const int hpk = a.n_head / a.n_head_kv;
-    PrefAttnWave &ws = sw[wave];
+    Q8Wave &ws = sw[wave];
+    const QueryCtx qc = query_ctx(a, i);
+    const uint8_t *stage = reinterpret_cast<const uint8_t *>(ws.stage);
 
-    const int s = a.q_seq[i];
-    const bool qvalid = s >= 0 && s < a.g.n_seq;
-    int n = qvalid ? a.n_sel[i] : 0;
-    n = n < 0 ? 0 : (n > a.ld_cells ? a.ld_cells : n);
-    int64_t n_present = qvalid ? a.g.n_cells[s] : 0;
-    n_present = n_present < a.g.cap_cells ? n_present : a.g.cap_cells;
-    const int32_t *cells = a.sel_cells + (int64_t)i * a.ld_cells;
-    const int64_t row0 = (int64_t)(qvalid ? s : 0) * a.g.cap_cells;
-
-    // A operand of S: row col = head g*hpk + col (zero past hpk), dims
-    // 32*kb + 8*quad .. +7, scaled
     half8_t qa[8];
-    {
-        const bool live = col < hpk;
-        const float *qp = a.q + ((int64_t)i * a.n_head + g * hpk + (live ? col : 0)) * kHeadDim;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                x[e] = live ? qp[32 * kb + 8 * quad + e] * a.scale : 0.0f;
-            qa[kb] = to_half8(x);
-        }
-    }
-
+    load_q_operand(a, i, g, hpk, col, quad, qa);
     f32x4 o[16];  // O[row 4*quad + jj][dim 16*tt + col]
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -110,190 +301,195 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
         l_run[jj] = 0.f;
     }
 
-    // the query's cell list, once, for every wavefront
-    for (int x = tid; x < n && x < kCellCap; x += 256) s_cells[x] = cells[x];
-    __syncthreads();
-    auto cell_at = [&](int cc) { return cc < kCellCap ? s_cells[cc] : cells[cc]; };
-    // cells of this lane for a chunk: the two S-tile columns (16t + col) and
-    // the two V-staging cells (2*col, 2*col + 1)
-    auto chunk_cells = [&](int c0, int (&kc)[2], int (&vc)[2]) {
-        const int c1 = min(n, c0 + kPChunk);
+    // Lane l (and l + 32) holds the cell of chunk slot l % 32, -1 past the
+    // list; the index is clamped so that every load is issued.
+    auto chunk_cell = [&](int c0) {
+        const int cc = c0 + (lane & 31);
+        const int v = qc.cells[min(cc, a.ld_cells - 1)];
+        return cc < qc.n ? v : -1;
+    };
+    // The chunk's rows; a cell that is not present loads the sequence's cell 0.
+    auto issue = [&](int cell, u32x4 (&R)[17]) {
+        const bool ok = cell >= 0 && cell < qc.n_present;
+        // the row index fits 32 bits: the host rejects caches of 2^31 rows
+        const uint32_t row = (uint32_t)((qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int cc = c0 + 16 * t + col;
-            kc[t] = cc < c1 ? cell_at(cc) : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int cc = c0 + 2 * col + u;
-            vc[u] = cc < c1 ? cell_at(cc) : -1;
+        for (int k = 0; k < 17; ++k) {
+            const uint32_t r = (uint32_t)__shfl((int)row, piece_slot(k, lane));
+            const uint8_t *base = static_cast<const uint8_t *>(piece_kv(k, lane) ? a.v : a.k);
+            R[k] = *reinterpret_cast<const u32x4 *>(base + (uint64_t)r * kQ8Row +
+                                                    piece_part(k, lane) * 16);
         }
     };
-    // raw K and V rows of a chunk (memory safety needs only 0 <= cell < cap)
-    auto issue_rows = [&](const int (&kc)[2], const int (&vc)[2], RawRow<KVT> (&rk)[2][8],
-                          RawRow<KVT> (&rv)[2][8]) {
+
+    u32x4 R[17];
+    int c0 = wave * kPChunk;
+    int cur = -1, nxt = -1;
+    if (c0 < qc.n) {
+        cur = chunk_cell(c0);
+        nxt = chunk_cell(c0 + kStride);
+        issue(cur, R);
+    }
+    for (; c0 < qc.n; c0 += kStride) {
+        // chunk c0's rows to the stage (the previous chunk's reads are done)
+        wave_sync_lds();
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bool ok = kc[t] >= 0 && kc[t] < a.g.cap_cells;
-            const int64_t row = ((row0 + (ok ? kc[t] : 0)) * a.n_head_kv + g);
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
-                if (ok) rk[t][kb] = load_raw<KVT>(a.k, row, kb * 4 + quad);
+        for (int k = 0; k < 17; ++k) {
+            const int at = piece_kv(k, lane) * (kPChunk * kQ8Row) +
+                           piece_slot(k, lane) * kQ8Row + piece_part(k, lane) * 16;
+            *reinterpret_cast<u32x4 *>(ws.stage + at / 4) = R[k];
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const bool ok = vc[u] >= 0 && vc[u] < a.g.cap_cells;
-            const int64_t row = ((row0 + (ok ? vc[u] : 0)) * a.n_head_kv + g);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (ok) rv[u][q] = load_raw<KVT>(a.v, row, quad * 8 + q);
+        const uint64_t okmask =
+            __ballot(lane < 32 && cur >= 0 && cur < qc.n_present) & 0xffffffffull;
+        // the next chunk's rows in flight while this one is computed
+        const int c1 = c0 + kStride;
+        int nxt2 = -1;
+        if (c1 < qc.n) {
+            issue(nxt, R);
+            nxt2 = chunk_cell(c1 + kStride);
         }
-    };
-    auto process = [&](const int (&kc)[2], const int (&vc)[2], const RawRow<KVT> (&rk)[2][8],
-                       const RawRow<KVT> (&rv)[2][8]) {
-        // S tiles: column col of tile t is cell kc[t]
+        wave_sync_lds();
+
+        // S tiles: column col of tile t is chunk slot 16t + col
         f32x4 sacc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const bool ok = kc[t] >= 0 && kc[t] < n_present;
+            const uint8_t *krow = stage + (16 * t + col) * kQ8Row;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                uint32_t lo, hi;
+                staged_slice(krow, kb * 4 + quad, lo, hi);
+                half2_t h[4];
+                int8x4_to_half(lo, h[0], h[1]);
+                int8x4_to_half(hi, h[2], h[3]);
+                const half8_t kop = {h[0][0], h[0][1], h[1][0], h[1][1],
+                                     h[2][0], h[2][1], h[3][0], h[3][1]};
+                const f32x4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    qa[kb], kop, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                const float d =
+                    (float)__builtin_bit_cast(_Float16, (uint16_t)staged_scale(krow, kb));
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(d, r[jj], acc[jj]);
+            }
+            if (!((okmask >> (16 * t + col)) & 1))
+                acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            sacc[t] = acc;
+        }
+        softmax_chunk(sacc, col, quad, m_run, l_run, o, ws.t);
+
+        // V to LDS, transposed: vt[dim][cell], the lane's two cells (2*col,
+        // 2*col + 1) as one fp16 pair per dim; a cell that is not present
+        // gets scale 0 (its int8 are finite)
+        {
+            const uint8_t *v0 = stage + (kPChunk + 2 * col) * kQ8Row;
+            const uint8_t *v1 = v0 + kQ8Row;
+            const bool ok0 = (okmask >> (2 * col)) & 1, ok1 = (okmask >> (2 * col + 1)) & 1;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int j = quad * 8 + q;  // dims 8j .. 8j+7, block j / 4
+                uint32_t lo0, hi0, lo1, hi1;
+                staged_slice(v0, j, lo0, hi0);
+                staged_slice(v1, j, lo1, hi1);
+                const uint32_t s0 = ok0 ? staged_scale(v0, j >> 2) : 0u;
+                const uint32_t s1 = ok1 ? staged_scale(v1, j >> 2) : 0u;
+                const half2_t dd = as_half2(s0 | (s1 << 16));
+                // interleave the two cells' bytes: (c0 e, c1 e, c0 e+1, c1 e+1)
+                const uint32_t w[4] = {__builtin_amdgcn_perm(lo1, lo0, 0x05010400u),
+                                       __builtin_amdgcn_perm(lo1, lo0, 0x07030602u),
+                                       __builtin_amdgcn_perm(hi1, hi0, 0x05010400u),
+                                       __builtin_amdgcn_perm(hi1, hi0, 0x07030602u)};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    half2_t h0, h1;
+                    int8x4_to_half(w[c], h0, h1);
+                    *reinterpret_cast<uint32_t *>(&ws.t.vt[8 * j + 2 * c][2 * col]) =
+                        as_u32(h0 * dd);
+                    *reinterpret_cast<uint32_t *>(&ws.t.vt[8 * j + 2 * c + 1][2 * col]) =
+                        as_u32(h1 * dd);
+                }
+            }
+        }
+        wave_sync_lds();
+        pv_chunk(ws.t, col, quad, o);
+        cur = nxt;
+        nxt = nxt2;
+    }
+    merge_store(a, i, g, hpk, sw, o, m_run, l_run);
+}
+
+// ---- f32 rows, gathered per lane ----
+
+// grid (n_head_kv, n_q), 256 threads.
+__global__ __launch_bounds__(256) void k_attn_prefill_f32(AttnArgs a) {
+    constexpr int KVT = QSA_KV_F32;
+    __shared__ F32Wave sw[kPWaves];
+    __shared__ int32_t s_cells[kCellCap];  // the query's cell list (its first kCellCap)
+    const int g = blockIdx.x, i = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+    const int col = lane & 15, quad = lane >> 4;
+    const int hpk = a.n_head / a.n_head_kv;
+    WaveTail &ws = sw[wave].t;
+    const QueryCtx qc = query_ctx(a, i);
+
+    half8_t qa[8];
+    load_q_operand(a, i, g, hpk, col, quad, qa);
+    f32x4 o[16];
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        m_run[jj] = -INFINITY;
+        l_run[jj] = 0.f;
+    }
+
+    for (int x = tid; x < qc.n && x < kCellCap; x += 256) s_cells[x] = qc.cells[x];
+    __syncthreads();
+    auto cell_at = [&](int cc) { return cc < kCellCap ? s_cells[cc] : qc.cells[cc]; };
+    for (int c0 = wave * kPChunk; c0 < qc.n; c0 += kStride) {
+        const int c1 = min(qc.n, c0 + kPChunk);
+        // S tiles: column col of tile t is cell c0 + 16t + col
+        f32x4 sacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int cc = c0 + 16 * t + col;
+            const int cell = cc < c1 ? cell_at(cc) : -1;
+            const bool ok = cell >= 0 && cell < qc.n_present;
+            const int64_t row = (qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
                 float x[8];
-                if (ok) {
-                    dequant<KVT>(rk[t][kb], kb * 4 + quad, x);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = 0.f;
-                }
+                dequant<KVT>(load_raw<KVT>(a.k, row, kb * 4 + quad), kb * 4 + quad, x);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], to_half8(x), acc, 0, 0, 0);
             }
             if (!ok) acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             sacc[t] = acc;
         }
-        // online softmax over the chunk, per head row 4*quad + jj
+        softmax_chunk(sacc, col, quad, m_run, l_run, o, ws);
+        // V to LDS, transposed; zeros for cells that are not present
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const float mx = row16_max(fmaxf(sacc[0][jj], sacc[1][jj]));
-            const float m_new = fmaxf(m_run[jj], mx);
-            const float p0 = m_new == -INFINITY ? 0.f : __expf(sacc[0][jj] - m_new);
-            const float p1 = m_new == -INFINITY ? 0.f : __expf(sacc[1][jj] - m_new);
-            const float corr = m_run[jj] == -INFINITY ? 0.f : __expf(m_run[jj] - m_new);
-            l_run[jj] = l_run[jj] * corr + row16_sum(p0 + p1);
-            m_run[jj] = m_new;
+        for (int u = 0; u < 2; ++u) {
+            const int cc = c0 + 2 * col + u;
+            const int cell = cc < c1 ? cell_at(cc) : -1;
+            const bool ok = cell >= 0 && cell < qc.n_present;
+            const int64_t row = (qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) o[tt][jj] *= corr;
-            ws.p[4 * quad + jj][col] = (_Float16)p0;
-            ws.p[4 * quad + jj][16 + col] = (_Float16)p1;
-        }
-        // V to LDS, transposed: vt[dim][cell]
+            for (int q = 0; q < 8; ++q) {
+                float x[8];
+                dequant<KVT>(load_raw<KVT>(a.v, row, quad * 8 + q), quad * 8 + q, x);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            float x0[8], x1[8];
-            const bool ok0 = vc[0] >= 0 && vc[0] < n_present;
-            const bool ok1 = vc[1] >= 0 && vc[1] < n_present;
-            if (ok0) dequant<KVT>(rv[0][q], quad * 8 + q, x0);
-            if (ok1) dequant<KVT>(rv[1][q], quad * 8 + q, x1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int dim = 64 * quad + 8 * q + e;
-                ws.vt[dim][2 * col] = ok0 ? (_Float16)x0[e] : (_Float16)0.0f;
-                ws.vt[dim][2 * col + 1] = ok1 ? (_Float16)x1[e] : (_Float16)0.0f;
+                for (int e = 0; e < 8; ++e)
+                    ws.vt[64 * quad + 8 * q + e][2 * col + u] =
+                        ok ? (_Float16)x[e] : (_Float16)0.f;
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // O += P V: A = P[row col][cells 8*quad ..], B = V[cells 8*quad ..][dim]
-        const half8_t pa = *reinterpret_cast<const half8_t *>(&ws.p[col][8 * quad]);
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-            const half8_t vb = *reinterpret_cast<const half8_t *>(&ws.vt[16 * tt + col][8 * quad]);
-            o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[tt], 0, 0, 0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-    constexpr int kStride = kPWaves * kPChunk;
-    if constexpr (KVT == QSA_KV_Q8_0) {
-        // two row buffers: the next chunk's rows are in flight while this
-        // one is computed
-        RawRow<KVT> rkA[2][8], rvA[2][8], rkB[2][8], rvB[2][8];
-        int kcA[2], vcA[2], kcB[2], vcB[2];
-        int c0 = wave * kPChunk;
-        if (c0 < n) {
-            chunk_cells(c0, kcA, vcA);
-            issue_rows(kcA, vcA, rkA, rvA);
-        }
-        while (c0 < n) {
-            const int c1 = c0 + kStride;
-            if (c1 < n) {
-                chunk_cells(c1, kcB, vcB);
-                issue_rows(kcB, vcB, rkB, rvB);
-            }
-            process(kcA, vcA, rkA, rvA);
-            if (c1 >= n) break;
-            const int c2 = c1 + kStride;
-            if (c2 < n) {
-                chunk_cells(c2, kcA, vcA);
-                issue_rows(kcA, vcA, rkA, rvA);
-            }
-            process(kcB, vcB, rkB, rvB);
-            c0 = c2;
-        }
-    } else {
-        // f32 rows are twice the registers: one buffer
-        for (int c0 = wave * kPChunk; c0 < n; c0 += kStride) {
-            RawRow<KVT> rk[2][8], rv[2][8];
-            int kc[2], vc[2];
-            chunk_cells(c0, kc, vc);
-            issue_rows(kc, vc, rk, rv);
-            process(kc, vc, rk, rv);
-        }
+        wave_sync_lds();
+        pv_chunk(ws, col, quad, o);
+        wave_sync_lds();
     }
-
-    // merge the four wavefronts' states, a quarter of the dims at a time
-    if (col == 0) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            ws.m[4 * quad + jj] = m_run[jj];
-            ws.l[4 * quad + jj] = l_run[jj];
-        }
-    }
-#pragma unroll
-    for (int part = 0; part < 4; ++part) {
-        __syncthreads();
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-            const int tt = part * 4 + t4;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) ws.o[4 * quad + jj][16 * t4 + col] = o[tt][jj];
-        }
-        __syncthreads();
-        // thread: head row r = tid / 16 (16 rows), dims 4*(tid%16) .. +3 of the quarter
-        const int r = tid >> 4, d0 = (tid & 15) * 4;
-        if (r < hpk) {
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < kPWaves; ++w) M = fmaxf(M, sw[w].m[r]);
-            float L = 0.f, wt[kPWaves];
-#pragma unroll
-            for (int w = 0; w < kPWaves; ++w) {
-                wt[w] = sw[w].m[r] == -INFINITY ? 0.f : __expf(sw[w].m[r] - M);
-                L += sw[w].l[r] * wt[w];
-            }
-            float *outp = a.out + ((int64_t)i * a.n_head + g * hpk + r) * kHeadDim + part * 64 + d0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float acc = 0.f;
-#pragma unroll
-                for (int w = 0; w < kPWaves; ++w) acc += sw[w].o[r][d0 + e] * wt[w];
-                outp[e] = L > 0.f ? acc / L : 0.f;
-            }
-        }
-    }
+    merge_store(a, i, g, hpk, sw, o, m_run, l_run);
 }
 
 }  // namespace
@@ -304,9 +500,9 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;
     const dim3 grid(a.n_head_kv, a.n_q);
     if (a.kv_type == QSA_KV_F32)
-        hipLaunchKernelGGL(k_attn_prefill<QSA_KV_F32>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_attn_prefill_f32, grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(k_attn_prefill<QSA_KV_Q8_0>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_attn_prefill_q8, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -64,4 +64,17 @@ __device__ __forceinline__ void dequant(const RawRow<KVT> &r, int j, float (&x)[
     }
 }
 
+// The 8 int8 of a q8_0 slice (dims 8j .. 8j+7, block j/4), realigned.
+__device__ __forceinline__ void q8_ints(const RawRow<QSA_KV_Q8_0> &r, int j, uint32_t &lo,
+                                        uint32_t &hi) {
+    const bool odd = (j >> 2) & 1;
+    lo = odd ? r.w0 : __builtin_amdgcn_alignbyte(r.w1, r.w0, 2);
+    hi = odd ? r.w1 : __builtin_amdgcn_alignbyte(r.w2, r.w1, 2);
+}
+
+// binary16 bits of the slice's block scale.
+__device__ __forceinline__ uint32_t q8_scale_bits(const RawRow<QSA_KV_Q8_0> &r, int j) {
+    return ((j >> 2) & 1) ? (r.sw >> 16) : (r.sw & 0xffffu);
+}
+
 }  // namespace qsa
