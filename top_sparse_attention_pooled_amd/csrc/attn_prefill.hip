@@ -46,10 +46,11 @@ constexpr int kPieces = 2 * kPChunk * kQ8Row / 16;     // 16-byte pieces per chu
 static_assert(kPieces == 17 * kWave, "a chunk is 17 loads of 16 bytes per lane");
 
 // Per-wavefront LDS shared by both kernels.
+constexpr int kVtPitch = kPChunk + 4;  // fp16 per vt row: 18 dwords, so rows 8 apart differ in bank
 struct WaveTail {
     union {
-        _Float16 vt[kHeadDim][kPChunk];  // V of the chunk, transposed
-        float o[16][kHeadDim / 4];       // merge: a quarter of the dims at a time
+        _Float16 vt[kHeadDim][kVtPitch];  // V of the chunk, transposed (cells 0..31 used)
+        float o[16][kHeadDim / 4];        // merge: a quarter of the dims at a time
     };
     _Float16 p[16][kPChunk];  // probabilities, [head row][cell]
     float m[16], l[16];
@@ -212,7 +213,10 @@ __device__ __forceinline__ void pv_chunk(const WaveTail &t, int col, int quad, f
     const half8_t pa = *reinterpret_cast<const half8_t *>(&t.p[col][8 * quad]);
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
-        const half8_t vb = *reinterpret_cast<const half8_t *>(&t.vt[16 * tt + col][8 * quad]);
+        // vt rows are 8-byte aligned: two 8-byte reads
+        const uint2 *vp = reinterpret_cast<const uint2 *>(&t.vt[16 * tt + col][8 * quad]);
+        const uint2 lo = vp[0], hi = vp[1];
+        const half8_t vb = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
         o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[tt], 0, 0, 0);
     }
 }
@@ -278,10 +282,23 @@ __device__ __forceinline__ int piece_slot(int k, int lane) {
 __device__ __forceinline__ int piece_kv(int k, int lane) { return k < 16 ? (k >> 3) : (lane >> 5); }
 __device__ __forceinline__ int piece_part(int k, int lane) { return k < 16 ? (lane & 15) : 16; }
 
-// grid (n_head_kv, n_q), 256 threads.
+// Workgroup id -> (query, KV head): ids are dealt to the 8 XCDs
+// round-robin, so the KV heads of one query get ids 8 apart, on one XCD at
+// about the same time, where the cache line their adjacent rows share is
+// read once.  False for the padding of the grid.
+__device__ __forceinline__ bool unit_of(const AttnArgs &a, int &i, int &g) {
+    const int id = blockIdx.x, per = 8 * a.n_head_kv;
+    const int r = id % per;
+    g = r >> 3;
+    i = (id / per) * 8 + (r & 7);
+    return i < a.n_q;
+}
+
+// 1-D grid of ceil(n_q / 8) * 8 * n_head_kv, 256 threads.
 __global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
     __shared__ Q8Wave sw[kPWaves];
-    const int g = blockIdx.x, i = blockIdx.y;
+    int i, g;
+    if (!unit_of(a, i, g)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;  // MFMA column / k-quarter
     const int hpk = a.n_head / a.n_head_kv;
@@ -380,14 +397,15 @@ __global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
 
         // V to LDS, transposed: vt[dim][cell], the lane's two cells (2*col,
         // 2*col + 1) as one fp16 pair per dim; a cell that is not present
-        // gets scale 0 (its int8 are finite)
+        // gets scale 0 (its int8 are finite).  The four quarter-waves write
+        // rows 8 apart at once, in different banks.
         {
             const uint8_t *v0 = stage + (kPChunk + 2 * col) * kQ8Row;
             const uint8_t *v1 = v0 + kQ8Row;
             const bool ok0 = (okmask >> (2 * col)) & 1, ok1 = (okmask >> (2 * col + 1)) & 1;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int j = quad * 8 + q;  // dims 8j .. 8j+7, block j / 4
+                const int j = q * 4 + quad;  // dims 8j .. 8j+7, block q
                 uint32_t lo0, hi0, lo1, hi1;
                 staged_slice(v0, j, lo0, hi0);
                 staged_slice(v1, j, lo1, hi1);
@@ -420,12 +438,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
 
 // ---- f32 rows, gathered per lane ----
 
-// grid (n_head_kv, n_q), 256 threads.
+// Same grid as k_attn_prefill_q8.
 __global__ __launch_bounds__(256) void k_attn_prefill_f32(AttnArgs a) {
     constexpr int KVT = QSA_KV_F32;
     __shared__ F32Wave sw[kPWaves];
     __shared__ int32_t s_cells[kCellCap];  // the query's cell list (its first kCellCap)
-    const int g = blockIdx.x, i = blockIdx.y;
+    int i, g;
+    if (!unit_of(a, i, g)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;
     const int hpk = a.n_head / a.n_head_kv;
@@ -477,12 +496,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(AttnArgs a) {
             const int64_t row = (qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
+                const int j = q * 4 + quad;
                 float x[8];
-                dequant<KVT>(load_raw<KVT>(a.v, row, quad * 8 + q), quad * 8 + q, x);
+                dequant<KVT>(load_raw<KVT>(a.v, row, j), j, x);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    ws.vt[64 * quad + 8 * q + e][2 * col + u] =
-                        ok ? (_Float16)x[e] : (_Float16)0.f;
+                    ws.vt[8 * j + e][2 * col + u] = ok ? (_Float16)x[e] : (_Float16)0.f;
             }
         }
         wave_sync_lds();
@@ -498,7 +517,7 @@ size_t attn_prefill_ws_bytes(int, int, int) { return 0; }
 
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;
-    const dim3 grid(a.n_head_kv, a.n_q);
+    const dim3 grid((a.n_q + 7) / 8 * 8 * a.n_head_kv);
     if (a.kv_type == QSA_KV_F32)
         hipLaunchKernelGGL(k_attn_prefill_f32, grid, dim3(256), 0, st, a);
     else

@@ -42,13 +42,16 @@ struct RopeTable {
 
 // cos and sin of pos * omega_t: the angle and both functions in fp64, each
 // rounded once to fp32.
-__device__ __forceinline__ void rope_cs(const RopeTable &rt, int t, int64_t pos, float &c,
-                                        float &s) {
-    const double phi = (double)pos * rt.omega[t];
+__device__ __forceinline__ void rope_cs_omega(double omega, int64_t pos, float &c, float &s) {
+    const double phi = (double)pos * omega;
     double sd, cd;
     sincos(phi, &sd, &cd);
     c = (float)cd;
     s = (float)sd;
+}
+__device__ __forceinline__ void rope_cs(const RopeTable &rt, int t, int64_t pos, float &c,
+                                        float &s) {
+    rope_cs_omega(rt.omega[t], pos, c, s);
 }
 
 // Order-preserving 32-bit key of a finite fp32 score (-0 maps like +0):
@@ -93,15 +96,19 @@ __device__ __forceinline__ int64_t query_blocks(const int32_t *q_seq, const int3
 }
 
 // Roped query element pair (t, t+64) of a query at position p, fp32.
-__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p,
-                                                const RopeTable &rt, float &lo, float &hi) {
-    const float xl = q[t], xh = q[t + 64];
+// Roped pair (t, t+64) from the two values and omega_t.
+__device__ __forceinline__ void rope_pair_omega(float xl, float xh, double omega, int64_t p,
+                                                float &lo, float &hi) {
     float c, s;
-    rope_cs(rt, t, p, c, s);
+    rope_cs_omega(omega, p, c, s);
     const float lc = xl * c, hs = xh * s;
     const float hc = xh * c, ls = xl * s;
     lo = lc - hs;
     hi = hc + ls;
+}
+__device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p,
+                                                const RopeTable &rt, float &lo, float &hi) {
+    rope_pair_omega(q[t], q[t + 64], rt.omega[t], p, lo, hi);
 }
 
 // Pooled key of block b of sequence s, whose first m = min(r, n - b*r) cells

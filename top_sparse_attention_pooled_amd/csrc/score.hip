@@ -128,15 +128,28 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
     return key;
 }
 
-// 1-D grid: n_q * n_wg scoring workgroups, then ceil(n_dirty/4) update
-// workgroups (one wavefront per dirty entry).
+// 1-D grid: n_q * 4*n_wg scoring workgroups (one per query and 64-block
+// group), then ceil(n_dirty/4) update workgroups (one wavefront per dirty
+// entry).
+//
+// Scoring: lane l of wavefront w owns block 64*g + l and the quads (4 dims)
+// q = w, w + 4, ..., w + 28 of it, so each load is 1 KiB contiguous and a
+// lane makes 8 of them (many workgroups, few loads each: the shape that
+// streams fastest from HBM).  Order T in this split: levels 64, 32 and 16
+// pair quads q, q + 16, q + 8 and q + 4, all within the wavefront; the
+// wavefront's quad-w partial then meets the others in LDS for level 8 (quad
+// w with w + 2), level 4 (0 with 1) and the two levels inside the quad.
 __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     __shared__ float4 qr4[kQuads];
     __shared__ float4 patch[kQuads];
+    __shared__ float4 part[4][kTile];  // quad-w partial of each block
+    __shared__ int s_hit[256];
+    __shared__ int s_n_hit;
     const ScoreArgs &a = f.s;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int64_t cap_blocks = a.g.cap_cells / a.r;
-    const int n_score_wg = f.n_wg * a.n_q;
+    const int n_grp = f.n_wg * 4;
+    const int n_score_wg = n_grp * a.n_q;
 
     if ((int)blockIdx.x >= n_score_wg) {  // ---- update role ----
         const int e = ((int)blockIdx.x - n_score_wg) * 4 + wave;
@@ -152,37 +165,58 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
         return;
     }
 
-    // ---- scoring role: query i, blocks [wg*256, wg*256 + 256) ----
-    const int i = blockIdx.x / f.n_wg, wg = blockIdx.x % f.n_wg;
+    // ---- scoring role: query i, blocks [64*gg, 64*gg + 64) ----
+    // Loads are issued before anything waits: the query (no dependence),
+    // the key tile (needs only the sequence), then the dirty list; the
+    // causal count comes from scalar loads, which wait on their own counter.
+    const int i = blockIdx.x / n_grp, gg = blockIdx.x % n_grp;
+    const int64_t b0 = (int64_t)gg * kTile;
+    const int64_t b = b0 + lane;
+    const float qxl = a.q_idx[(int64_t)i * kDIdx + lane];
+    const float qxh = a.q_idx[(int64_t)i * kDIdx + lane + 64];
+    const double omega = a.rope.omega[lane];
+    const int s_in = a.q_seq[i];
+    // (issued unconditionally, from tile 0 if the tile does not exist, so the
+    // wait counts below stay exact)
+    const bool tile_ok = s_in >= 0 && s_in < a.g.n_seq && b0 < cap_blocks;
+    const float4 *src = reinterpret_cast<const float4 *>(
+                            a.pooled + (tile_ok ? ((int64_t)s_in * (cap_blocks / kTile) + gg) *
+                                                      kTileFloats
+                                                : 0)) + lane;
+    float4 k[8];  // quads wave + 4m of block b
+#pragma unroll
+    for (int m = 0; m < 8; ++m) k[m] = src[(wave + 4 * m) * kTile];
+    // (unconditional, clamped loads: a load under a lane condition would be
+    // waited for, with the keys, right after it)
+    const int32_t *dl = f.n_dirty > 0 ? f.dirty : a.q_seq;
+    const int nd2 = f.n_dirty > 0 ? 2 * f.n_dirty : 1;
+    int my_ds = dl[min(2 * tid, nd2 - 1)], my_db = dl[min(2 * tid + 1, nd2 - 1)];
+    if (tid >= f.n_dirty) my_ds = -1;
     int s;
     int64_t p;
     bool valid;
     const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
                                     a.g.n_cells, a.r, s, p, valid);
     const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
-    const int64_t wg_b0 = (int64_t)wg * 256;
-    const int64_t b0 = wg_b0 + wave * kTile;
-    const int64_t b = b0 + lane;
-    // the dirty list: fetched with the keys, one entry per thread
-    __shared__ int s_hit[256];
-    __shared__ int s_n_hit;
+    const bool live = b0 < nc;  // implies a valid sequence and b0 < cap_blocks
     if (tid == 0) s_n_hit = 0;
-    int my_ds = -1, my_db = -1;
-    if (tid < f.n_dirty) {
-        my_ds = f.dirty[2 * tid];
-        my_db = f.dirty[2 * tid + 1];
+    if (live && wave == 0) {
+        float lo, hi;
+        rope_pair_omega(qxl, qxh, omega, p, lo, hi);
+        float *qr = reinterpret_cast<float *>(qr4);
+        qr[lane] = lo;
+        qr[lane + 64] = hi;
     }
-    float4 k[kQuads];
-    load_tile_and_query(a, i, s, p, nc, wg_b0, b0, k, qr4);
-    // dirty entries of this workgroup's scored blocks (lists longer than 256
+    __syncthreads();
+    // dirty entries among this group's scored blocks (lists longer than 256
     // are covered by the loop below reading the rest directly)
-    if (my_ds == s && my_db >= wg_b0 && my_db < wg_b0 + 256 && my_db < nc)
+    if (my_ds == s && my_db >= b0 && my_db < b0 + kTile && my_db < nc)
         s_hit[atomicAdd(&s_n_hit, 1)] = my_db;
     __syncthreads();
     const int n_hit = s_n_hit;
 
     // a dirty block scored here may not be written yet: recompute it in place
-    if (wg_b0 < nc && (n_hit > 0 || f.n_dirty > 256)) {
+    if (live && (n_hit > 0 || f.n_dirty > 256)) {
         int64_t n = a.g.n_cells[s];
         if (n > a.g.cap_cells) n = a.g.cap_cells;
         const int n_iter = f.n_dirty > 256 ? n_hit + (f.n_dirty - 256) : n_hit;
@@ -194,10 +228,9 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
                 const int de = 256 + (e - n_hit);
                 if (f.dirty[2 * de] != s) continue;
                 db = f.dirty[2 * de + 1];
-                if (db < wg_b0 || db >= wg_b0 + 256 || db >= nc) continue;
+                if (db < b0 || db >= b0 + kTile || db >= nc) continue;
             }
-            const int owner_wave = (int)((db - wg_b0) >> 6);
-            if (wave == owner_wave) {
+            if (wave == 0) {
                 float lo, hi;
                 pooled_key_lane(f.kidx, a.g.cap_cells, s, db, n, a.r, f.eps, f.gamma, a.rope,
                                 lane, lo, hi);
@@ -208,18 +241,55 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
             __syncthreads();
             if (b == db) {
 #pragma unroll
-                for (int q = 0; q < kQuads; ++q) k[q] = patch[q];
+                for (int m = 0; m < 8; ++m) k[m] = patch[wave + 4 * m];
             }
             __syncthreads();
         }
     }
 
-    const float sc = tile_score(k, qr4, b, nc);
+    // levels 64, 32, 16 within the wavefront
+    if (live) {
+        float4 v[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float4 qq = qr4[wave + 4 * m];
+            v[m].x = qq.x * k[m].x;
+            v[m].y = qq.y * k[m].y;
+            v[m].z = qq.z * k[m].z;
+            v[m].w = qq.w * k[m].w;
+        }
+        // slot m is quad wave + 4m: level 64 pairs m with m + 4, 32 m with
+        // m + 2, 16 m with m + 1
+#pragma unroll
+        for (int h = 4; h >= 1; h >>= 1)
+#pragma unroll
+            for (int m = 0; m < h; ++m) {
+                v[m].x = v[m].x + v[m + h].x;
+                v[m].y = v[m].y + v[m + h].y;
+                v[m].z = v[m].z + v[m + h].z;
+                v[m].w = v[m].w + v[m + h].w;
+            }
+        part[wave][lane] = v[0];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float sc = -INFINITY;
+    if (live && b < nc) {
+        const float4 p0 = part[0][lane], p1 = part[1][lane];
+        const float4 p2 = part[2][lane], p3 = part[3][lane];
+        float4 u0, u1;  // level 8: quad 0 with 2, quad 1 with 3
+        u0.x = p0.x + p2.x; u0.y = p0.y + p2.y; u0.z = p0.z + p2.z; u0.w = p0.w + p2.w;
+        u1.x = p1.x + p3.x; u1.y = p1.y + p3.y; u1.z = p1.z + p3.z; u1.w = p1.w + p3.w;
+        float4 t;  // level 4
+        t.x = u0.x + u1.x; t.y = u0.y + u1.y; t.z = u0.z + u1.z; t.w = u0.w + u1.w;
+        const float x0 = t.x + t.z, x1 = t.y + t.w;  // level 2
+        sc = x0 + x1;                                 // level 1
+    }
     float *srow = a.scores + (int64_t)i * a.ld;
     if (b < a.nb_max) srow[b] = sc;
     uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
     key = wave_sort_desc(key);
-    const int64_t grp = ((int64_t)i * f.n_wg + wg) * 4 + wave;
+    const int64_t grp = (int64_t)i * n_grp + gg;
     if (lane < kCand) f.cand[grp * kCand + lane] = key;
     if (lane == kCand) f.drop[grp] = key;
 }
@@ -376,7 +446,7 @@ size_t fused_select_ws_bytes(int n_q, int nb_max) { return cand_ws_bytes(n_q, nb
 
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st) {
     bind_candidates(f, ws);
-    const int grid = f.n_wg * f.s.n_q + (f.n_dirty + 3) / 4;
+    const int grid = f.n_wg * 4 * f.s.n_q + (f.n_dirty + 3) / 4;
     if (grid > 0) hipLaunchKernelGGL(k_score_cand, dim3(grid), dim3(256), 0, st, f);
     return hipGetLastError();
 }
