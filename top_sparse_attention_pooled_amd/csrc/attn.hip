@@ -182,16 +182,17 @@ __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, i
                     cell[u] = cc < a.ld_cells ? cells[cc] : -1;
                 }
             }
-            // K/V rows (memory safety needs only 0 <= cell < cap_cells) and
-            // the present-cell count
+            // K/V rows and the present-cell count.  Every load is issued (a
+            // cell outside 0 .. cap_cells-1 reads cell 0 and is not used):
+            // a load under a lane condition is waited for right after it,
+            // which would serialise the cells' round trips.
             RawRow<KVT> rk[kCPG], rv[kCPG];
 #pragma unroll
             for (int u = 0; u < kCPG; ++u) {
-                if (cell[u] >= 0 && cell[u] < a.g.cap_cells) {
-                    const int64_t row = (row0 + cell[u]) * a.n_head_kv + g;
-                    rk[u] = load_raw<KVT>(a.k, row, j);
-                    rv[u] = load_raw<KVT>(a.v, row, j);
-                }
+                const bool in_cap = cell[u] >= 0 && cell[u] < a.g.cap_cells;
+                const int64_t row = (row0 + (in_cap ? cell[u] : 0)) * a.n_head_kv + g;
+                rk[u] = load_raw<KVT>(a.k, row, j);
+                rv[u] = load_raw<KVT>(a.v, row, j);
             }
             int64_t n_present = a.g.n_cells[s];
             n_present = n_present < a.g.cap_cells ? n_present : a.g.cap_cells;

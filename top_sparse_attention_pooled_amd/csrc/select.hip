@@ -7,8 +7,8 @@
 // b < number of complete blocks) has the unique key
 //     (order-preserving bits of its score) << 32 | ~b,
 // so the kept set is exactly the blocks with the top_k/r largest keys: the
-// ranking's ties go to the lower block index.  Up to 32,768 blocks the keys
-// live in registers (32 per thread, loaded once with every load in flight);
+// ranking's ties go to the lower block index.  Up to 24,576 blocks the keys
+// live in registers (24 per thread, loaded once with every load in flight);
 // beyond that they are re-streamed from memory each round.  The threshold
 // comes from topk_engine.h; the kept blocks are marked in an LDS bitmap and
 // emitted in ascending order, each expanded to its r cells, followed by the
@@ -20,7 +20,7 @@ namespace qsa {
 namespace {
 
 constexpr int kNT = 1024;
-constexpr int kC = 32;                        // register-cached keys per thread
+constexpr int kC = 24;                        // register-cached keys per thread
 constexpr int kMaxBitmapBlocks = 1 << 19;      // 64 KiB bitmap
 constexpr int kMaxKeep = 4096;
 
@@ -57,6 +57,19 @@ struct RowStream {
     }
 };
 
+struct SelSource {
+    RegKeys32<kC, kNT> regs;
+    RowStream mem;
+    bool in_regs;
+    template <typename F>
+    __device__ __forceinline__ void operator()(F &&fn) const {
+        if (in_regs)
+            regs(fn);
+        else
+            mem(fn);
+    }
+};
+
 __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     __shared__ SelSmem sm;
     const int i = blockIdx.x;
@@ -71,21 +84,22 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     const float *row = a.scores + (int64_t)i * a.ld;
 
     // score keys cached in registers (block = s2*kNT + tid), or, past
-    // 32768 blocks, the score row re-read from memory on every pass
-    RegKeys32<kC, kNT> from_regs;
-    from_regs.tid = tid;
-    const RowStream from_memory{row, limit};
-    const bool in_regs = limit <= (int64_t)kNT * kC;
-    if (in_regs) {
+    // 24576 blocks, the score row re-read from memory on every pass (one
+    // source type, so the engine is instantiated once)
+    SelSource src;
+    src.regs.tid = tid;
+    src.mem = RowStream{row, limit};
+    src.in_regs = limit <= (int64_t)kNT * kC;
+    if (src.in_regs) {
 #pragma unroll
         for (int s2 = 0; s2 < kC; ++s2) {
             const int64_t b = (int64_t)s2 * kNT + tid;
-            const float sc = b < limit ? row[b] : 0.0f;
-            from_regs.k[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
+            const float sc = row[b < limit ? b : 0];  // unconditional: no wait per load
+            src.regs.k[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
         }
     }
-    const Thresh th = in_regs ? topk_threshold<kNT>(from_regs, (uint32_t)B, sm.tk)
-                              : topk_threshold<kNT>(from_memory, (uint32_t)B, sm.tk);
+    const Thresh th = topk_threshold<kNT>(src, (uint32_t)B, sm.tk);
+    const RowStream &from_memory = src.mem;
 
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = a.top_k + a.r - 1;
@@ -101,10 +115,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
                 atomicOr(&sm.bitmap[b >> 5], 1u << (b & 31));
             }
         };
-        if (in_regs)
-            from_regs(mark);
-        else
-            from_memory(mark);
+        src(mark);
         __syncthreads();
         emit_from_bitmap<kNT>(sm.bitmap, n_words, B, a.r, nc, tail, ob, oc, ld_cells,
                               a.n_sel + i, sm.tk);

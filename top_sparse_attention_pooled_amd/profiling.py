@@ -28,14 +28,34 @@ CSRC = os.path.join(HERE, "csrc")
 CALIBRATION_KERNEL = "neg"
 
 
-def source_hash() -> str:
-    """sha256 over every kernel source and header, in name order."""
+# the source file that defines each profiled kernel
+KERNEL_SOURCE = {"k_score_cand": "score.hip"}
+
+
+def _sources_of(name: str) -> List[str]:
+    """The file and every local header it includes, transitively, in name order."""
+    seen, todo = set(), [name]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.add(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            for line in fh:
+                line = line.strip()
+                if line.startswith('#include "') and not line.startswith('#include "../'):
+                    todo.append(line.split('"')[1])
+    return sorted(seen)
+
+
+def source_hash(kernel: str = "k_score_cand") -> str:
+    """sha256 over the sources the kernel is built from (its file and the
+    local headers it includes), in name order."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if path.endswith((".hip", ".h")):
-            h.update(os.path.basename(path).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+    for f in _sources_of(KERNEL_SOURCE.get(kernel, "score.hip")):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -101,7 +121,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_mib: int) -> dict:
         "fetch_bytes": fetch_b,
         "write_bytes": write_b,
         "traffic_bytes": fetch_b + write_b,
-        "source_sha256": source_hash(),
+        "source_sha256": source_hash(kernel),
     }
 
 
