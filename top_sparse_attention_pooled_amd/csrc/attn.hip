@@ -465,20 +465,22 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
     const int stride = G * kHeadDim + 2 * G;
     const float *base = a.ws + ((int64_t)i * (a.n_head / G) + hg) * n_runs * stride;
     const int rg = tid >> 7, dp = tid & 127;
+    // every load is issued (clamped to the last run; a run past n_runs gets
+    // weight 0): a load under a lane condition is waited for right after it
     float2 pre[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-        const int r = rg + u * kCombGroups;
-        pre[u] = r < n_runs ? *reinterpret_cast<const float2 *>(base + (int64_t)r * stride +
-                                                                hh * kHeadDim + 2 * dp)
-                            : make_float2(0.f, 0.f);
+        const int r = min(rg + u * kCombGroups, n_runs - 1);
+        pre[u] = *reinterpret_cast<const float2 *>(base + (int64_t)r * stride + hh * kHeadDim +
+                                                   2 * dp);
     }
     // per-run weights exp(m_r - M), M = max over runs that saw any cell
-    float m = -INFINITY, l = 0.f;
-    if (tid < n_runs) {
-        m = base[(int64_t)tid * stride + G * kHeadDim + hh];
-        l = base[(int64_t)tid * stride + G * kHeadDim + G + hh];
-        if (!(l > 0.f)) m = -INFINITY;
+    const int tr = min(tid, n_runs - 1);
+    float m = base[(int64_t)tr * stride + G * kHeadDim + hh];
+    float l = base[(int64_t)tr * stride + G * kHeadDim + G + hh];
+    if (tid >= n_runs || !(l > 0.f)) {
+        m = -INFINITY;
+        l = 0.f;
     }
     const float mx = wave_max_f32(m);
     if ((tid & 63) == 0) s_red[tid >> 6] = mx;
@@ -518,9 +520,8 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * kCombGroups;
             w[u] = r < n_runs ? s_w[r] : 0.f;
-            v[u] = r < n_runs ? *reinterpret_cast<const float2 *>(base + (int64_t)r * stride +
-                                                                  hh * kHeadDim + 2 * dp)
-                              : make_float2(0.f, 0.f);
+            v[u] = *reinterpret_cast<const float2 *>(base + (int64_t)min(r, n_runs - 1) * stride +
+                                                     hh * kHeadDim + 2 * dp);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
