@@ -140,6 +140,32 @@ def test_fused_select_attend_limits():
                              FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0)  # n_q = 0: no-op
 
 
+def test_prefill_indexer_workspace_and_limits():
+    d = qsa.Dims()
+    a256 = lambda x: -(-x // 256) * 256
+    ld = -(-49785 // 256) * 256  # MFMA score row: whole 64-block groups, 4 per 256 blocks
+    want = a256(512 * ld * 4) + a256(512 * 128 * 2) + a256(512 * 4)
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 512, 49785) == want
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 0, 49785) == 0
+    big = 131073  # blocks: above what the selection's bitmap holds
+    seqs = _seqs(cap=4 * 131328)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.score_select_prefill(d, seqs, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1, big,
+                                 FAKE, FAKE, FAKE, FAKE, 1 << 40, stream=0)
+    assert e.value.code == qsa.QSA_ENOTSUP
+    need = qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 8, 4000)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.score_select_prefill(d, _seqs(), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4000,
+                                 FAKE, FAKE, FAKE, FAKE, need - 16, stream=0)
+    assert e.value.code == qsa.QSA_EWS
+    with pytest.raises(qsa.QsaError) as e:  # the bf16 key copy is required here
+        qsa.score_select_prefill(d, _seqs(), FAKE, FAKE, 4, FAKE, None, FAKE, FAKE, FAKE, 8, 4000,
+                                 FAKE, FAKE, FAKE, FAKE, need, stream=0)
+    assert e.value.code == qsa.QSA_EINVAL
+    qsa.score_select_prefill(d, _seqs(), FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4000,
+                             FAKE, FAKE, FAKE, FAKE, 0, stream=0)  # nothing to do: no-op
+
+
 def test_no_kernel_spills_to_scratch():
     """Every kernel keeps its register arrays in registers: a spilled key or
     tile array would turn the register-resident loops into memory traffic."""

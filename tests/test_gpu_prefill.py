@@ -142,6 +142,47 @@ def test_prefill_selection_ubatch_at_depth():
     assert np.all(gn <= w.top_k + w.r - 1)
 
 
+def test_prefill_selection_extreme_query_norms():
+    """Queries scaled far up and far down: their error bound Delta leaves the
+    range where no partial sum can overflow or underflow, so every causal
+    block is rescored in order T; ordinary queries beside them take the
+    band path."""
+    w = synth.Workload("pfn", 94, 1, 20000, n_new=12, steps=1, top_k=512)
+    kidx = synth.make_kidx(w)
+    layer = runtime.Layer(w, DEV, kidx=kidx)
+    n = synth.n_cells_at(w, 0)
+    layer.rebuild(n)
+    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    q_idx = q_idx.copy()
+    q_idx[0] *= 1e33
+    q_idx[1] *= 1e-33
+    q_idx[2] *= 1e30
+    nb_max = w.nb_max(0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max)
+    ref_pooled = oracle_pooled(w, kidx, n)
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, range(q_pos.size))
+
+
+def test_prefill_selection_no_scored_blocks():
+    """nb_max = 0: no block competes, every query keeps only its tail."""
+    w = synth.Workload("pfz", 95, 1, 3000, n_new=6, steps=1, top_k=256)
+    layer = runtime.Layer(w, DEV)
+    n = synth.n_cells_at(w, 0)
+    layer.rebuild(n)
+    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, 0)
+    gb = bufs.sel_blocks.cpu().numpy()
+    gc = bufs.sel_cells.cpu().numpy()
+    gn = bufs.n_sel.cpu().numpy()
+    for i, p in enumerate(q_pos):
+        nc = (int(p) + 1) // w.r
+        tail = np.arange(nc * w.r, int(p) + 1, dtype=np.int32)
+        assert gn[i] == tail.size
+        assert np.all(gb[i] == -1)
+        assert np.array_equal(gc[i, :tail.size], tail)
+        assert np.all(gc[i, tail.size:] == -1)
+
+
 def test_prefill_step_end_to_end():
     """A whole prefill step through the ABI (exact indexer, then attention on
     the matrix cores) against the oracle's step with T-ordered bf16 scores:

@@ -322,7 +322,7 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const f
                           dims->idx_norm_w_dev, rope};
         e = qsa::launch_update_pooled(u, (hipStream_t)stream);
     }
-    if (e == hipSuccess && n_q > 0 && nb_max > 0) {
+    if (e == hipSuccess && n_q > 0) {  // (nb_max 0: every query keeps its tail only)
         qsa::ScoreArgs a{geom(seqs),      q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
                          pooled_bf16_dev, nb_max,    nullptr,   0,         dims->r, rope};
         e = qsa::launch_score_select_prefill(a, dims->idx_norm_w_dev, ws_dev, dims->top_k,

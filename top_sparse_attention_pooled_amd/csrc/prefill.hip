@@ -458,9 +458,10 @@ hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, v
     // padded to whole rounds of the 8 XCDs (k_prefill_scores maps ids)
     const int n_gt = w.n_grp / 4;
     const int n_slab = max(1, min(n_gt, 512 / qt));
-    const int slab = (n_gt + n_slab - 1) / n_slab;
+    const int slab = max(1, (n_gt + n_slab - 1) / n_slab);
     const int grid = ((n_gt + slab - 1) / slab + 7) / 8 * 8 * qt;
-    hipLaunchKernelGGL(k_prefill_scores, dim3(grid), dim3(256), 0, st, a, w, n_gt, qt, slab);
+    if (n_gt > 0)
+        hipLaunchKernelGGL(k_prefill_scores, dim3(grid), dim3(256), 0, st, a, w, n_gt, qt, slab);
     hipLaunchKernelGGL(k_select_prefill, dim3(a.n_q), dim3(kSelPNT), 0, st, a, w, top_k,
                        sel_blocks, sel_cells, n_sel);
     return hipGetLastError();
