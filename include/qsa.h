@@ -248,8 +248,9 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const f
  * also available as two calls:
  *   qsa_decode_score_candidates writes the dirty blocks and scores every
  *     block (a workgroup that holds a dirty block recomputes it in registers
- *     rather than reading it), keeping in the workspace the 4 best keys of
- *     each group of 64 blocks and the largest key each group dropped;
+ *     rather than reading it), keeping in the workspace the best keys of
+ *     each group of 64 blocks (16 while nb_max <= 16384, 8 up to 32768, else
+ *     4) and the largest key each group dropped;
  *   qsa_decode_select_candidates selects from those, re-admitting all keys
  *     of any group whose dropped key could compete (or re-reading the score
  *     row if more than 32 groups could), so the selection is exact.

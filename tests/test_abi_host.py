@@ -42,6 +42,11 @@ def test_workspace_sizes():
     assert qsa.workspace_size(d, qsa.OP_ATTN_DECODE, 5) == 5 * runs * 16 * 258 * 4
     n_grp = -(-62070 // 256) * 4  # decode score+select: per 64-block group, 4 kept + 1 dropped
     assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 5 * n_grp * 5 * 8
+    # shorter contexts keep more keys per group: 16 for 196 groups (12,420 blocks)
+    n_grp = -(-12420 // 256) * 4
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 1, 12420) == n_grp * 17 * 8
+    n_grp = -(-30000 // 256) * 4  # 472 groups: 8 kept
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 1, 30000) == n_grp * 9 * 8
     with pytest.raises(qsa.QsaError) as e:
         qsa.workspace_size(d, 99, 1)
     assert e.value.code == qsa.QSA_EINVAL

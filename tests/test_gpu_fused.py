@@ -105,7 +105,7 @@ def test_fused_expands_clustered_groups():
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 96, 0, synth.T_QIDX)
-    aligned_cells(w, q, 39999, range(3000, 3700), kidx)  # 700 blocks over 12 groups
+    aligned_cells(w, q, 39999, range(3000, 3700), kidx)  # 700 blocks over 12 groups of 64
     s = run_case("contiguous cluster (re-admits 12 groups)", w, 40000, q, kidx)
     kept, _ = oracle.select(s, 40000 - 3, w.r, w.top_k)
     assert np.sum((kept >= 3000) & (kept < 3700)) >= 500  # the case really is clustered
@@ -115,12 +115,12 @@ def test_fused_streams_when_many_groups_compete():
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 97, 0, synth.T_QIDX)
-    # 20 blocks at stride 7 in each of 30 spans of 256: 10 and 9 of them fall
-    # into the span's first two 64-block groups (more than the 4 a group
-    # keeps), so 60 groups compete
-    blocks = [wg * 256 + 7 * j for wg in range(2, 32) for j in range(20)]
+    # 20 blocks at stride 3 in the first 64-block group of each of 36 spans
+    # of 256: more than the 16 keys a group keeps at this context length, so
+    # 36 groups (over the 32 re-admitted whole) compete
+    blocks = [wg * 256 + 3 * j for wg in range(2, 38) for j in range(20)]
     aligned_cells(w, q, 39999, blocks, kidx)
-    s = run_case("strided cluster (60 groups compete: re-stream)", w, 40000, q, kidx)
+    s = run_case("strided cluster (36 groups compete: re-stream)", w, 40000, q, kidx)
     kept, _ = oracle.select(s, 40000 - 3, w.r, w.top_k)
     assert np.isin(kept, blocks).sum() >= 500
 

@@ -22,21 +22,32 @@
 namespace qsa {
 
 constexpr int kGroup = kTile;   // blocks per candidate group (one wavefront)
-constexpr int kCand = 4;        // keys kept per group
+constexpr int kCand = 4;        // fewest keys kept per group
+constexpr int kCandSlots = 4096;  // candidates the selection holds on chip for nb_max <= 65536
 constexpr int kMaxExpand = 32;  // groups re-admitted whole before streaming
 
-// Workspace of the decode indexer: cand [n_q][groups][4], then drop
+// Workspace of the decode indexer: cand [n_q][groups][n_cand], then drop
 // [n_q][groups], groups = 4 per 256 blocks of nb_max.
 __host__ __device__ inline int cand_groups(int nb_max) { return (nb_max + 255) / 256 * 4; }
 
+// Keys kept per group: as many (16, 8, then 4) as the on-chip candidate
+// slots allow.  B winners spread over fewer groups in a shorter context (512
+// of ~12,400 blocks at 50k cells is 2.6 per group on average), and a group
+// with more winners than it kept must be re-admitted whole.
+__host__ __device__ inline int cand_per_group(int nb_max) {
+    const int g = cand_groups(nb_max);
+    return g * 16 <= kCandSlots ? 16 : (g * 8 <= kCandSlots ? 8 : kCand);
+}
+
 inline size_t cand_ws_bytes(int n_q, int nb_max) {
-    return (size_t)n_q * cand_groups(nb_max) * (kCand + 1) * sizeof(uint64_t);
+    return (size_t)n_q * cand_groups(nb_max) * (cand_per_group(nb_max) + 1) * sizeof(uint64_t);
 }
 
 inline void bind_candidates(DecodeIdxArgs &f, void *ws) {
     f.n_wg = (f.s.nb_max + 255) / 256;
+    f.n_cand = cand_per_group(f.s.nb_max);
     f.cand = static_cast<uint64_t *>(ws);
-    f.drop = f.cand + (size_t)f.s.n_q * cand_groups(f.s.nb_max) * kCand;
+    f.drop = f.cand + (size_t)f.s.n_q * cand_groups(f.s.nb_max) * f.n_cand;
 }
 
 // The candidate keys of one query in registers, for up to MAXB blocks: base
@@ -86,13 +97,14 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
 
     using Keys = CandKeys<NT, MAXB>;
     Keys ck;
-    const int n_cand = n_grp * kCand;
+    const int kc = f.n_cand;
+    const int n_cand = n_grp * kc;
     ck.nb = (n_cand + NT - 1) / NT;
     ck.ne = 0;
 #pragma unroll
     for (int s = 0; s < Keys::kBase; ++s) {
         const int fi = tid + NT * s;
-        ck.k[s] = (s < ck.nb && fi < n_cand) ? f.cand[qbase * kCand + fi] : 0ull;
+        ck.k[s] = (s < ck.nb && fi < n_cand) ? f.cand[qbase * kc + fi] : 0ull;
     }
 #pragma unroll
     for (int s = 0; s < Keys::kExp; ++s) ck.k[Keys::kBase + s] = 0ull;
@@ -141,7 +153,7 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
         // replace the kept keys of the re-admitted groups by all of theirs
 #pragma unroll
         for (int s = 0; s < Keys::kBase; ++s) {
-            const int g = (tid + NT * s) / kCand;
+            const int g = (tid + NT * s) / kc;
             for (int e = 0; e < n_over; ++e)
                 if (sm.over[e] == g) ck.k[s] = 0ull;
         }

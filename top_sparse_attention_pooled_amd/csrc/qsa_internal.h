@@ -235,9 +235,10 @@ struct DecodeIdxArgs {
     int32_t *sel_blocks;
     int32_t *sel_cells;
     int32_t *n_sel;
-    uint64_t *cand;  // [n_q][4*n_wg][4]: 4 largest keys of each 64-block group
+    uint64_t *cand;  // [n_q][4*n_wg][n_cand]: largest keys of each 64-block group
     uint64_t *drop;  // [n_q][4*n_wg]: largest key each group dropped
     int32_t n_wg;
+    int32_t n_cand;  // keys kept per group (16, 8 or 4: see cand_per_group)
 };
 
 struct SelectArgs {

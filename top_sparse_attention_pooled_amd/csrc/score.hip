@@ -290,8 +290,8 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
     key = wave_sort_desc(key);
     const int64_t grp = (int64_t)i * n_grp + gg;
-    if (lane < kCand) f.cand[grp * kCand + lane] = key;
-    if (lane == kCand) f.drop[grp] = key;
+    if (lane < f.n_cand) f.cand[grp * f.n_cand + lane] = key;
+    if (lane == f.n_cand) f.drop[grp] = key;
 }
 
 // grid (n_q), 1024 threads: the exact selection from the candidates, then
