@@ -613,6 +613,17 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st) {
 hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnArgs &a,
                                      hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;
+    // Every fused workgroup derives the selection itself: free while the
+    // grid fits the chip in one round, wasteful beyond (several queries).
+    // Then select once per query and attend over the lists instead; the
+    // selection and the attention arithmetic are the same, so are the results.
+    const int hpk = a.n_head / a.n_head_kv;
+    const int n_set = (a.n_head / (hpk % 2 == 0 ? 2 : 1) + kQuarters - 1) / kQuarters;
+    if ((int64_t)a.n_q * decode_runs(a.ld_cells) * n_set > 256) {
+        hipError_t e = launch_decode_select(f, ws_idx, st);
+        if (e != hipSuccess) return e;
+        return launch_attn_decode(a, st);
+    }
     bind_candidates(f, ws_idx);
     return a.kv_type == QSA_KV_F32 ? launch_sel_kvt<QSA_KV_F32>(f, a, st)
                                    : launch_sel_kvt<QSA_KV_Q8_0>(f, a, st);

@@ -296,8 +296,9 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
 
 // grid (n_q), 1024 threads: the exact selection from the candidates, then
 // the ascending emission of blocks and cells.
+template <int MAXB>
 __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
-    __shared__ CandSelSmem<kSelNT, kFusedMaxBlocks> sm;
+    __shared__ CandSelSmem<kSelNT, MAXB> sm;
     const ScoreArgs &a = f.s;
     const int i = blockIdx.x;
     int s;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
                                     a.g.n_cells, a.r, s, p, valid);
     const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
     const int B = f.top_k / a.r;
-    select_candidates<kSelNT, kFusedMaxBlocks>(f, i, limit, B, sm);
+    select_candidates<kSelNT, MAXB>(f, i, limit, B, sm);
     const int n_words = (int)((limit + 31) / 32);
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = f.top_k + a.r - 1;
@@ -453,7 +454,12 @@ hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st) {
 
 hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st) {
     bind_candidates(f, ws);
-    if (f.s.n_q > 0) hipLaunchKernelGGL(k_select_cand, dim3(f.s.n_q), dim3(kSelNT), 0, st, f);
+    if (f.s.n_q <= 0) return hipSuccess;
+    // the smaller instance (half the bitmap and register slots) up to 65536 blocks
+    if (f.s.nb_max <= kSelAttnMaxBlocks)
+        hipLaunchKernelGGL(k_select_cand<kSelAttnMaxBlocks>, dim3(f.s.n_q), dim3(kSelNT), 0, st, f);
+    else
+        hipLaunchKernelGGL(k_select_cand<kFusedMaxBlocks>, dim3(f.s.n_q), dim3(kSelNT), 0, st, f);
     return hipGetLastError();
 }
 
