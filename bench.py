@@ -231,7 +231,8 @@ def run_decode(args, torch, dev):
     assert np.all(n_sel > 0), "empty selections in the benchmark step"
 
     ms_per_step = t_main * 1000.0 / K
-    us_per_token_layer = ms_per_step * 1000.0 / L
+    us_per_step_layer = ms_per_step * 1000.0 / L
+    us_per_token_layer = us_per_step_layer / n_q  # n_q tokens per step (one per session)
     ab = [algorithmic_bytes(w, t) for t in range(W, T)]
     score_bytes = float(np.mean([a["score"] for a in ab]))
     step_bytes = float(np.mean([sum(a.values()) for a in ab]))
@@ -257,7 +258,8 @@ def run_decode(args, torch, dev):
             "layers_per_step": L, "graph_replay": not args.eager,
         },
         "tokens_per_s_per_layer": round(1e6 / us_per_token_layer, 1),
-        "step_hbm_gbps": round(step_bytes / (us_per_token_layer * 1e-6) / 1e9, 1),
+        "us_per_step_layer": round(us_per_step_layer, 3),
+        "step_hbm_gbps": round(step_bytes / (us_per_step_layer * 1e-6) / 1e9, 1),
         "roofline": {
             "kernel": "k_score_cand",
             "timing": timing,

@@ -169,7 +169,9 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     // Loads are issued before anything waits: the query (no dependence),
     // the key tile (needs only the sequence), then the dirty list; the
     // causal count comes from scalar loads, which wait on their own counter.
-    const int i = blockIdx.x / n_grp, gg = blockIdx.x % n_grp;
+    // groups in reverse: the tail group, which usually holds the dirty block
+    // and recomputes it, is dispatched first instead of last
+    const int i = blockIdx.x / n_grp, gg = n_grp - 1 - (int)(blockIdx.x % n_grp);
     const int64_t b0 = (int64_t)gg * kTile;
     const int64_t b = b0 + lane;
     const float qxl = a.q_idx[(int64_t)i * kDIdx + lane];
