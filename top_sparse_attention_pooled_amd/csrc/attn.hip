@@ -148,11 +148,11 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int i, int h0, int j,
 
 // Attention of query i (sequence s), heads h0.. (KV head g), over positions
 // [c_begin, c_end) of its cell list, one 32-cell chunk at a time, by the 256
-// threads of one quarter (threadIdx.x / 256) of the workgroup; every quarter
+// threads of one part (threadIdx.x / 256) of the workgroup; every part
 // of the workgroup calls it with the same c_begin, c_end (it has workgroup
 // barriers).  cell[] holds this thread's cells of the first chunk (positions
 // c_begin + grp*4 + u); later chunks read theirs from `cells` (global).
-// active: write results (false for an idle quarter).  direct: write the
+// active: write results (false for an idle part).  direct: write the
 // normalised output; else the partial state (o[G][256], m[G], l[G]) to part.
 template <int G, int KVT>
 __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, int g, int h0,
@@ -335,38 +335,40 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
                           true);
 }
 
-constexpr int kSelAttnNT = 1024;
-constexpr int kQuarters = kSelAttnNT / 256;
+constexpr int kSelAttnNT = 512;
+constexpr int kParts = kSelAttnNT / 256;  // 256-thread attention parts per workgroup
+constexpr int kSelAttnOnChip = 512;       // fused workgroups resident at once (2 per CU)
 
 // Decode selection fused with attention.  Workgroup = (query i, run of 32
-// cells, set of 4 head groups); quarter q (256 threads) attends for head
-// group 4*set + q, so for 16 heads over 2 KV heads the 4 quarters share one
-// KV head and each K/V row is fetched once per workgroup.  First the whole
+// cells, set of 2 head groups); part q (256 threads) attends for head group
+// 2*set + q, so both parts share one KV head whenever the query heads per KV
+// head are a multiple of 4 (16 heads over 2 KV heads: 4 sets per run, 260
+// workgroups for a 2051-cell set, about one per CU).  First the whole
 // workgroup derives query i's exact kept set from the candidates (the kept
 // set is unique, so all workgroups derive the same), then finds the cells at
 // positions [32*run, 32*run + 32) of the ascending cell list -- blocks by
 // rank through a prefix count over the bitmap, then the tail cells -- and
-// the quarters attend over them.  The workgroup of (run 0, set 0) also
-// writes the selection outputs.  Cells, outputs and partial states equal
-// those of the selection kernel followed by k_attn.
+// the parts attend over them.  The workgroup of (run 0, set 0) also writes
+// the selection outputs.  Cells, outputs and partial states equal those of
+// the selection kernel followed by k_attn.
 template <int G, int KVT>
 __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnArgs a,
                                                          int n_runs) {
     __shared__ CandSelSmem<kSelAttnNT, kSelAttnMaxBlocks> ss;
-    __shared__ AttnSmem<G> sm[kQuarters];
+    __shared__ AttnSmem<G> sm[kParts];
     __shared__ int s_cells[kChunk];
     const int n_hg = a.n_head / G;
-    const int n_set = (n_hg + kQuarters - 1) / kQuarters;
+    const int n_set = (n_hg + kParts - 1) / kParts;
     // workgroup -> (query, run, set), set fastest
     const int set = blockIdx.x % n_set;
     const int run = (blockIdx.x / n_set) % n_runs;
     const int i = blockIdx.x / (n_set * n_runs);
-    const int tid = threadIdx.x, quarter = tid >> 8, lt = tid & 255;
+    const int tid = threadIdx.x, part = tid >> 8, lt = tid & 255;
     const int grp = lt >> 5, j = lt & 31;
-    const int lane = tid & (kWave - 1), wave = tid >> 6;
-    const int hg_raw = set * kQuarters + quarter;
+    const int lane = tid & (kWave - 1), wave = wave_id();
+    const int hg_raw = set * kParts + part;
     const bool active = hg_raw < n_hg;
-    const int hg = active ? hg_raw : n_hg - 1;  // an idle quarter mirrors a real one
+    const int hg = active ? hg_raw : n_hg - 1;  // an idle part mirrors a real one
     const int hpk = a.n_head / a.n_head_kv;
     const int g = (hg * G) / hpk;
     const int h0 = hg * G;
@@ -394,12 +396,9 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const uint32_t incl = wave_incl_scan_u32(local);
     if (lane == kWave - 1) ss.tk.red[wave] = incl;
     __syncthreads();
-    uint32_t rank = incl - local, total = 0;
-#pragma unroll
-    for (int w = 0; w < kSelAttnNT / kWave; ++w) {
-        if (w < wave) rank += ss.tk.red[w];
-        total += ss.tk.red[w];
-    }
+    uint32_t before, total;
+    waves_prefix<kSelAttnNT / kWave>(ss.tk.red, wave, before, total);
+    const uint32_t rank = before + incl - local;
     const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
     const int n_sel = n_keep * r + tail;
     const int c_begin = run * kChunk;
@@ -441,7 +440,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
 #pragma unroll
     for (int u = 0; u < kCPG; ++u) cell[u] = s_cells[grp * kCPG + u];
     const int c_end = min(n_sel, c_begin + kChunk);
-    attend_chunks<G, KVT>(a, i, s, g, h0, c_begin, c_end, cell, nullptr, qv, sm[quarter],
+    attend_chunks<G, KVT>(a, i, s, g, h0, c_begin, c_end, cell, nullptr, qv, sm[part],
                           partial_of<G>(a, i, hg, run, n_runs), false, active);
 }
 
@@ -485,24 +484,18 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
     const float mx = wave_max_f32(m);
     if ((tid & 63) == 0) s_red[tid >> 6] = mx;
     __syncthreads();
-    float M = s_red[0];
-#pragma unroll
-    for (int w = 1; w < kCombNT / 64; ++w) M = fmaxf(M, s_red[w]);
+    // lane w holds wavefront w's value (one LDS load, then DPP)
+    constexpr int kNW = kCombNT / 64;
+    const int lane = tid & 63;
+    const float M = wave_max_f32(lane < kNW ? s_red[lane] : -INFINITY);
     __syncthreads();
     const float wgt = (m != -INFINITY) ? __expf(m - M) : 0.f;
     if (tid < n_runs) s_w[tid] = wgt;
     float lw = l > 0.f ? l * wgt : 0.f;
-    lw += xor_lane_f<1>(lw);
-    lw += xor_lane_f<2>(lw);
-    lw += xor_lane_f<4>(lw);
-    lw += xor_lane_f<8>(lw);
-    lw += xor_lane_f<16>(lw);
-    lw += xor_lane_f<32>(lw);
+    lw = wave_sum_f32(lw);
     if ((tid & 63) == 0) s_red[tid >> 6] = lw;
     __syncthreads();
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kCombNT / 64; ++w) L += s_red[w];
+    const float L = wave_sum_f32(lane < kNW ? s_red[lane] : 0.f);
 
     float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
@@ -581,7 +574,7 @@ int decode_runs(int ld_cells) { return (ld_cells + kChunk - 1) / kChunk; }
 template <int G, int KVT>
 hipError_t launch_sel_g(const DecodeIdxArgs &f, const AttnArgs &a, hipStream_t st) {
     const int n_runs = decode_runs(a.ld_cells);
-    const int n_set = (a.n_head / G + kQuarters - 1) / kQuarters;
+    const int n_set = (a.n_head / G + kParts - 1) / kParts;
     const int grid = a.n_q * n_runs * n_set;
     hipLaunchKernelGGL((k_sel_attn<G, KVT>), dim3(grid), dim3(kSelAttnNT), 0, st, f, a, n_runs);
     hipError_t e = hipGetLastError();
@@ -618,8 +611,8 @@ hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnAr
     // Then select once per query and attend over the lists instead; the
     // selection and the attention arithmetic are the same, so are the results.
     const int hpk = a.n_head / a.n_head_kv;
-    const int n_set = (a.n_head / (hpk % 2 == 0 ? 2 : 1) + kQuarters - 1) / kQuarters;
-    if ((int64_t)a.n_q * decode_runs(a.ld_cells) * n_set > 256) {
+    const int n_set = (a.n_head / (hpk % 2 == 0 ? 2 : 1) + kParts - 1) / kParts;
+    if ((int64_t)a.n_q * decode_runs(a.ld_cells) * n_set > kSelAttnOnChip) {
         hipError_t e = launch_decode_select(f, ws_idx, st);
         if (e != hipSuccess) return e;
         return launch_attn_decode(a, st);

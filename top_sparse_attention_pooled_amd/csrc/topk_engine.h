@@ -47,15 +47,33 @@ struct Thresh {
     }
 };
 
+// Cross-wave combination of one value per wavefront, red[0 .. NW) (read
+// after a barrier): lane l loads red[l] once and the wavefront combines the
+// values with DPP.  (A loop over the array in every thread pays one LDS
+// round trip per step: the loads reuse registers and wait one by one.)
+template <int NW>
+__device__ __forceinline__ uint32_t waves_sum(const uint32_t *red) {
+    const int lane = threadIdx.x & (kWave - 1);
+    return wave_sum_u32(lane < NW ? red[lane] : 0u);
+}
+
+// before = sum over wavefronts w < wave, total = sum over all (wave uniform).
+template <int NW>
+__device__ __forceinline__ void waves_prefix(const uint32_t *red, int wave, uint32_t &before,
+                                             uint32_t &total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t incl = wave_incl_scan_u32(lane < NW ? red[lane] : 0u);
+    total = lane_value(incl, kWave - 1);
+    before = wave > 0 ? lane_value(incl, wave - 1) : 0u;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) {
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     v = wave_sum_u32(v);
     if (lane == 0) sm.red[wave] = v;
     __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) t += sm.red[w];
+    const uint32_t t = waves_sum<NT / 64>(sm.red);
     __syncthreads();
     return t;
 }
@@ -71,13 +89,9 @@ __device__ __forceinline__ void block_minmax_u32(uint32_t &mn, uint32_t &mx, Top
         sm.red2[wave] = mx;
     }
     __syncthreads();
-    mn = sm.red[0];
-    mx = sm.red2[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) {
-        mn = min(mn, sm.red[w]);
-        mx = max(mx, sm.red2[w]);
-    }
+    constexpr int NW = NT / 64;
+    mn = wave_min_u32(lane < NW ? sm.red[lane] : ~0u);
+    mx = wave_max_u32(lane < NW ? sm.red2[lane] : 0u);
     __syncthreads();
 }
 
@@ -102,15 +116,14 @@ __device__ __forceinline__ void pick_bin(TopkSmem<NT> &sm, uint32_t lo, uint32_t
         local += h[q];
     }
     // suffix sums: values in bins above this thread's bins
-    const int lane = t & (kWave - 1), wave = t >> 6;
+    const int lane = t & (kWave - 1), wave = wave_id();
     const uint32_t prefix = wave_incl_scan_u32(local);     // lanes <= this one
     const uint32_t total = lane_value(prefix, kWave - 1);  // whole wave
     if (lane == 0) sm.red[wave] = total;
     __syncthreads();
-    uint32_t above = total - prefix;  // higher lanes of this wave
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w)
-        if (w > wave) above += sm.red[w];
+    uint32_t before, all;
+    waves_prefix<NT / 64>(sm.red, wave, before, all);
+    uint32_t above = all - before - prefix;  // higher lanes and higher wavefronts
 #pragma unroll
     for (int q = PER - 1; q >= 0; --q) {
         if (above < krem && above + h[q] >= krem) {
@@ -241,13 +254,9 @@ __device__ void emit_from_bitmap(const uint32_t *bm, int n_words, int B, int r, 
     const uint32_t incl = wave_incl_scan_u32(local);
     if (lane == kWave - 1) sm.red[wave] = incl;
     __syncthreads();
-    uint32_t pos = incl - local;
-    uint32_t total = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        if (w < wave) pos += sm.red[w];
-        total += sm.red[w];
-    }
+    uint32_t before, total;
+    waves_prefix<NT / 64>(sm.red, wave, before, total);
+    uint32_t pos = before + incl - local;
     const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
     if (threadIdx.x == 0) *n_sel = n_keep * r + tail;
     for (int w = w0; w < w0 + per && w < n_words; ++w) {

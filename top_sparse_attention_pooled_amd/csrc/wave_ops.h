@@ -109,6 +109,18 @@ __device__ __forceinline__ float wave_max_f32(float v) {
     return v;
 }
 
+// Every lane gets the same sum: partners add the same two values at each
+// level, and addition is commutative.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += xor_lane_f<1>(v);
+    v += xor_lane_f<2>(v);
+    v += xor_lane_f<4>(v);
+    v += xor_lane_f<8>(v);
+    v += xor_lane_f<16>(v);
+    v += xor_lane_f<32>(v);
+    return v;
+}
+
 // Inclusive prefix sum over the 64 lanes in lane order.
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
     int x = (int)v;
