@@ -24,6 +24,8 @@
 // lane straight into the operand layout.
 // Operands are rounded to fp16 (Q * scale, P, V; f32 K); sums and the
 // softmax state are fp32.
+#include <type_traits>
+
 #include "kv_rows.h"
 #include "qsa_internal.h"
 #include "wave_ops.h"
@@ -41,26 +43,33 @@ constexpr int kPChunk = 32;  // cells per chunk
 constexpr int kPWaves = 4;
 constexpr int kStride = kPWaves * kPChunk;
 constexpr int kCellCap = 4096;  // f32 kernel: cell indices held in LDS; the rest read directly
-constexpr int kStageWords = 2 * kPChunk * kQ8Row / 4;  // raw K rows, then V rows
+constexpr int kStageWords = kPChunk * kQ8Row / 4;  // raw rows of one chunk (K or V)
 constexpr int kPieces = 2 * kPChunk * kQ8Row / 16;     // 16-byte pieces per chunk
 static_assert(kPieces == 17 * kWave, "a chunk is 17 loads of 16 bytes per lane");
 
-// Per-wavefront LDS shared by both kernels.
+// Per-wavefront LDS.  The q8_0 kernel transposes V in two halves of 128
+// dims so that a wavefront's LDS (the stage plus this tail, about 19 KB)
+// lets two workgroups share a CU.
 constexpr int kVtPitch = kPChunk + 4;  // fp16 per vt row: 18 dwords, so rows 8 apart differ in bank
-struct WaveTail {
+template <int VROWS>
+struct WaveTailT {
     union {
-        _Float16 vt[kHeadDim][kVtPitch];  // V of the chunk, transposed (cells 0..31 used)
-        float o[16][kHeadDim / 4];        // merge: a quarter of the dims at a time
+        _Float16 vt[VROWS][kVtPitch];  // V of the chunk, transposed (cells 0..31 used)
+        float o[16][kHeadDim / 4];     // merge: a quarter of the dims at a time
     };
     _Float16 p[16][kPChunk];  // probabilities, [head row][cell]
     float m[16], l[16];
 };
+using WaveTail = WaveTailT<kHeadDim>;      // f32 rows: all dims at once
+using HalfTail = WaveTailT<kHeadDim / 2>;  // q8_0 rows: V in two halves
+static_assert(sizeof(_Float16[kHeadDim / 2][kVtPitch]) >= sizeof(float[16][kHeadDim / 4]),
+              "the merge buffer fits the half transpose");
 struct F32Wave {
     WaveTail t;
 };
 struct Q8Wave {
-    uint32_t stage[kStageWords];  // [K, V][cell slot][272 bytes], as loaded
-    WaveTail t;
+    uint32_t stage[kStageWords];  // the chunk's K rows, later its V rows, as loaded
+    HalfTail t;
 };
 
 __device__ __forceinline__ half8_t to_half8(const float (&x)[8]) {
@@ -180,9 +189,10 @@ __device__ __forceinline__ void load_q_operand(const AttnArgs &a, int i, int g, 
 // Online softmax of a chunk's two S tiles (column col of tile t is chunk
 // cell 16t + col; -inf where there is no cell) into the running state, and
 // P to LDS.
+template <typename Tail>
 __device__ __forceinline__ void softmax_chunk(const f32x4 (&sacc)[2], int col, int quad,
                                               float (&m_run)[4], float (&l_run)[4],
-                                              f32x4 (&o)[16], WaveTail &t) {
+                                              f32x4 (&o)[16], Tail &t) {
     float corr[4];
     bool moved = false;
 #pragma unroll
@@ -208,13 +218,16 @@ __device__ __forceinline__ void softmax_chunk(const f32x4 (&sacc)[2], int col, i
     }
 }
 
-// O += P V from LDS: A = P[row col][cells 8*quad ..], B = V[cells 8*quad ..][dim].
-__device__ __forceinline__ void pv_chunk(const WaveTail &t, int col, int quad, f32x4 (&o)[16]) {
+// O += P V from LDS for the output tiles TT0 .. TT0 + NTT - 1 (dims 16*tt ..),
+// whose V rows are vt[16*(tt - TT0) ..]: A = P[row col][cells 8*quad ..],
+// B = V[cells 8*quad ..][dim].
+template <int TT0, int NTT, typename Tail>
+__device__ __forceinline__ void pv_tiles(const Tail &t, int col, int quad, f32x4 (&o)[16]) {
     const half8_t pa = *reinterpret_cast<const half8_t *>(&t.p[col][8 * quad]);
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
+    for (int tt = TT0; tt < TT0 + NTT; ++tt) {
         // vt rows are 8-byte aligned: two 8-byte reads
-        const uint2 *vp = reinterpret_cast<const uint2 *>(&t.vt[16 * tt + col][8 * quad]);
+        const uint2 *vp = reinterpret_cast<const uint2 *>(&t.vt[16 * (tt - TT0) + col][8 * quad]);
         const uint2 lo = vp[0], hi = vp[1];
         const half8_t vb = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
         o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[tt], 0, 0, 0);
@@ -229,7 +242,7 @@ __device__ __forceinline__ void merge_store(const AttnArgs &a, int i, int g, int
                                             const float (&m_run)[4], const float (&l_run)[4]) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;
-    WaveTail &t = sw[tid >> 6].t;
+    auto &t = sw[tid >> 6].t;
     if (col == 0) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -276,6 +289,7 @@ __device__ __forceinline__ void merge_store(const AttnArgs &a, int i, int g, int
 // Load k (0..16) of a chunk: loads 0..7 are K rows of slots 4k .. 4k+3 (16
 // lanes a row, bytes 0..255), loads 8..15 the same for V, load 16 the last
 // 16 bytes of the K row (lanes < 32) or V row (lanes >= 32) of slot lane%32.
+// K and V pass through the same stage, at byte slot*272 + part*16.
 __device__ __forceinline__ int piece_slot(int k, int lane) {
     return k < 16 ? 4 * (k & 7) + (lane >> 4) : (lane & 31);
 }
@@ -294,8 +308,10 @@ __device__ __forceinline__ bool unit_of(const AttnArgs &a, int &i, int &g) {
     return i < a.n_q;
 }
 
-// 1-D grid of ceil(n_q / 8) * 8 * n_head_kv, 256 threads.
-__global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
+// 1-D grid of ceil(n_q / 8) * 8 * n_head_kv, 256 threads, two workgroups
+// per CU (LDS and registers are sized for two wavefronts per SIMD).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_q8(
+    AttnArgs a) {
     __shared__ Q8Wave sw[kPWaves];
     int i, g;
     if (!unit_of(a, i, g)) return;
@@ -325,19 +341,29 @@ __global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
         const int v = qc.cells[min(cc, a.ld_cells - 1)];
         return cc < qc.n ? v : -1;
     };
-    // The chunk's rows; a cell that is not present loads the sequence's cell 0.
-    auto issue = [&](int cell, u32x4 (&R)[17]) {
+    // Row of a cell; a cell that is not present reads the sequence's cell 0.
+    // (The row index fits 32 bits: the host rejects caches of 2^31 rows.)
+    auto row_of = [&](int cell) {
         const bool ok = cell >= 0 && cell < qc.n_present;
-        // the row index fits 32 bits: the host rejects caches of 2^31 rows
-        const uint32_t row = (uint32_t)((qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g);
+        return (uint32_t)((qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g);
+    };
+    // Loads K0 .. K1-1 of the chunk whose slot rows the lanes hold.
+    auto issue = [&](uint32_t row, u32x4(&R)[17], auto k0, auto k1) {
 #pragma unroll
-        for (int k = 0; k < 17; ++k) {
+        for (int k = decltype(k0)::value; k < decltype(k1)::value; ++k) {
             const uint32_t r = (uint32_t)__shfl((int)row, piece_slot(k, lane));
             const uint8_t *base = static_cast<const uint8_t *>(piece_kv(k, lane) ? a.v : a.k);
             R[k] = *reinterpret_cast<const u32x4 *>(base + (uint64_t)r * kQ8Row +
                                                     piece_part(k, lane) * 16);
         }
     };
+    auto put = [&](int k, const u32x4 &v) {
+        const int at = piece_slot(k, lane) * kQ8Row + piece_part(k, lane) * 16;
+        *reinterpret_cast<u32x4 *>(ws.stage + at / 4) = v;
+    };
+    using K0 = std::integral_constant<int, 0>;
+    using K8 = std::integral_constant<int, 8>;
+    using K17 = std::integral_constant<int, 17>;
 
     u32x4 R[17];
     int c0 = wave * kPChunk;
@@ -345,26 +371,20 @@ __global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
     if (c0 < qc.n) {
         cur = chunk_cell(c0);
         nxt = chunk_cell(c0 + kStride);
-        issue(cur, R);
+        issue(row_of(cur), R, K0{}, K17{});
     }
     for (; c0 < qc.n; c0 += kStride) {
-        // chunk c0's rows to the stage (the previous chunk's reads are done)
+        const bool more = c0 + kStride < qc.n;
+        const uint32_t nrow = row_of(nxt);
+        // K rows of chunk c0 to the stage (the previous chunk's V reads are
+        // done), then the next chunk's K in flight
         wave_sync_lds();
 #pragma unroll
-        for (int k = 0; k < 17; ++k) {
-            const int at = piece_kv(k, lane) * (kPChunk * kQ8Row) +
-                           piece_slot(k, lane) * kQ8Row + piece_part(k, lane) * 16;
-            *reinterpret_cast<u32x4 *>(ws.stage + at / 4) = R[k];
-        }
+        for (int k = 0; k < 8; ++k) put(k, R[k]);
+        if (lane < 32) put(16, R[16]);
         const uint64_t okmask =
             __ballot(lane < 32 && cur >= 0 && cur < qc.n_present) & 0xffffffffull;
-        // the next chunk's rows in flight while this one is computed
-        const int c1 = c0 + kStride;
-        int nxt2 = -1;
-        if (c1 < qc.n) {
-            issue(nxt, R);
-            nxt2 = chunk_cell(c1 + kStride);
-        }
+        if (more) issue(nrow, R, K0{}, K8{});
         wave_sync_lds();
 
         // S tiles: column col of tile t is chunk slot 16t + col
@@ -395,41 +415,61 @@ __global__ __launch_bounds__(256) void k_attn_prefill_q8(AttnArgs a) {
         }
         softmax_chunk(sacc, col, quad, m_run, l_run, o, ws.t);
 
-        // V to LDS, transposed: vt[dim][cell], the lane's two cells (2*col,
-        // 2*col + 1) as one fp16 pair per dim; a cell that is not present
-        // gets scale 0 (its int8 are finite).  The four quarter-waves write
-        // rows 8 apart at once, in different banks.
-        {
-            const uint8_t *v0 = stage + (kPChunk + 2 * col) * kQ8Row;
-            const uint8_t *v1 = v0 + kQ8Row;
-            const bool ok0 = (okmask >> (2 * col)) & 1, ok1 = (okmask >> (2 * col + 1)) & 1;
+        // V rows to the stage (S has read the K rows), then the next chunk's
+        // V and both 16-byte tails in flight
+        wave_sync_lds();
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+        for (int k = 8; k < 16; ++k) put(k, R[k]);
+        if (lane >= 32) put(16, R[16]);
+        int nxt2 = -1;
+        if (more) {
+            issue(nrow, R, K8{}, K17{});
+            nxt2 = chunk_cell(c0 + 2 * kStride);
+        }
+        wave_sync_lds();
+
+        // V to LDS transposed, 128 dims at a time: vt[dim - 128h][cell], the
+        // lane's two cells (2*col, 2*col + 1) as one fp16 pair per dim; a cell
+        // that is not present gets scale 0 (its int8 are finite).  The four
+        // quarter-waves write rows 8 apart at once, in different banks.
+        const uint8_t *v0 = stage + (2 * col) * kQ8Row;
+        const uint8_t *v1 = v0 + kQ8Row;
+        const bool ok0 = (okmask >> (2 * col)) & 1, ok1 = (okmask >> (2 * col + 1)) & 1;
+        auto transpose_half = [&](auto hh) {
+            constexpr int h = decltype(hh)::value;
+#pragma unroll
+            for (int q = 4 * h; q < 4 * h + 4; ++q) {
                 const int j = q * 4 + quad;  // dims 8j .. 8j+7, block q
                 uint32_t lo0, hi0, lo1, hi1;
                 staged_slice(v0, j, lo0, hi0);
                 staged_slice(v1, j, lo1, hi1);
-                const uint32_t s0 = ok0 ? staged_scale(v0, j >> 2) : 0u;
-                const uint32_t s1 = ok1 ? staged_scale(v1, j >> 2) : 0u;
+                const uint32_t s0 = ok0 ? staged_scale(v0, q) : 0u;
+                const uint32_t s1 = ok1 ? staged_scale(v1, q) : 0u;
                 const half2_t dd = as_half2(s0 | (s1 << 16));
                 // interleave the two cells' bytes: (c0 e, c1 e, c0 e+1, c1 e+1)
                 const uint32_t w[4] = {__builtin_amdgcn_perm(lo1, lo0, 0x05010400u),
                                        __builtin_amdgcn_perm(lo1, lo0, 0x07030602u),
                                        __builtin_amdgcn_perm(hi1, hi0, 0x05010400u),
                                        __builtin_amdgcn_perm(hi1, hi0, 0x07030602u)};
+                const int row = 8 * j - 128 * h;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     half2_t h0, h1;
                     int8x4_to_half(w[c], h0, h1);
-                    *reinterpret_cast<uint32_t *>(&ws.t.vt[8 * j + 2 * c][2 * col]) =
+                    *reinterpret_cast<uint32_t *>(&ws.t.vt[row + 2 * c][2 * col]) =
                         as_u32(h0 * dd);
-                    *reinterpret_cast<uint32_t *>(&ws.t.vt[8 * j + 2 * c + 1][2 * col]) =
+                    *reinterpret_cast<uint32_t *>(&ws.t.vt[row + 2 * c + 1][2 * col]) =
                         as_u32(h1 * dd);
                 }
             }
-        }
+        };
+        transpose_half(std::integral_constant<int, 0>{});
         wave_sync_lds();
-        pv_chunk(ws.t, col, quad, o);
+        pv_tiles<0, 8>(ws.t, col, quad, o);
+        wave_sync_lds();
+        transpose_half(std::integral_constant<int, 1>{});
+        wave_sync_lds();
+        pv_tiles<8, 8>(ws.t, col, quad, o);
         cur = nxt;
         nxt = nxt2;
     }
@@ -505,7 +545,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(AttnArgs a) {
             }
         }
         wave_sync_lds();
-        pv_chunk(ws, col, quad, o);
+        pv_tiles<0, 16>(ws, col, quad, o);
         wave_sync_lds();
     }
     merge_store(a, i, g, hpk, sw, o, m_run, l_run);
