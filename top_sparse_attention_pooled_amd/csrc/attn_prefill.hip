@@ -242,7 +242,7 @@ __device__ __forceinline__ void merge_store(const AttnArgs &a, int i, int g, int
                                             const float (&m_run)[4], const float (&l_run)[4]) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;
-    auto &t = sw[tid >> 6].t;
+    auto &t = sw[wave_id()].t;
     if (col == 0) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ Q8Wave sw[kPWaves];
     int i, g;
     if (!unit_of(a, i, g)) return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;  // MFMA column / k-quarter
     const int hpk = a.n_head / a.n_head_kv;
     Q8Wave &ws = sw[wave];
@@ -375,7 +375,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     for (; c0 < qc.n; c0 += kStride) {
         const bool more = c0 + kStride < qc.n;
-        const uint32_t nrow = row_of(nxt);
         // K rows of chunk c0 to the stage (the previous chunk's V reads are
         // done), then the next chunk's K in flight
         wave_sync_lds();
@@ -384,7 +383,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (lane < 32) put(16, R[16]);
         const uint64_t okmask =
             __ballot(lane < 32 && cur >= 0 && cur < qc.n_present) & 0xffffffffull;
-        if (more) issue(nrow, R, K0{}, K8{});
+        if (more) issue(row_of(nxt), R, K0{}, K8{});
         wave_sync_lds();
 
         // S tiles: column col of tile t is chunk slot 16t + col
@@ -423,7 +422,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (lane >= 32) put(16, R[16]);
         int nxt2 = -1;
         if (more) {
-            issue(nrow, R, K8{}, K17{});
+            issue(row_of(nxt), R, K8{}, K17{});
             nxt2 = chunk_cell(c0 + 2 * kStride);
         }
         wave_sync_lds();
@@ -485,7 +484,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_f32(AttnArgs a) {
     __shared__ int32_t s_cells[kCellCap];  // the query's cell list (its first kCellCap)
     int i, g;
     if (!unit_of(a, i, g)) return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & (kWave - 1);
     const int col = lane & 15, quad = lane >> 4;
     const int hpk = a.n_head / a.n_head_kv;
     WaveTail &ws = sw[wave].t;

@@ -9,6 +9,12 @@ counters read for a plain streaming kernel of known size.
 writes OUT.json (read by bench.py) and OUT.md.  The JSON carries a hash of
 the kernel sources; bench.py reports the traffic only while the sources
 still hash the same (a changed kernel makes the counters stale).
+
+    python -m top_sparse_attention_pooled_amd.profiling kernels \
+        --trace DIR --title "..." --command "..." --out profiles/NAME.md
+
+writes a table of per-kernel device durations (min, median, p90, mean) from
+a rocprofv3 --kernel-trace --stats run, followed by its kernel_stats.csv.
 """
 from __future__ import annotations
 
@@ -125,9 +131,47 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_mib: int) -> dict:
     }
 
 
+def _quantile(v: List[float], q: float) -> float:
+    s = sorted(v)
+    return s[min(len(s) - 1, int(q * (len(s) - 1) + 0.5))]
+
+
+def kernels_md(trace_dir: str, title: str, command: str, notes: str = "") -> str:
+    """Markdown: per-kernel durations of a kernel trace, then the stats CSV."""
+    dur = kernel_durations(trace_dir)
+    lines = [f"# {title}", ""]
+    if command:
+        lines += ["Command:", "", "```", command.strip(), "```", ""]
+    lines += ["Per-kernel device durations from the kernel trace (microseconds):", "",
+              "| kernel | launches | min | median | p90 | mean |", "|---|---|---|---|---|---|"]
+    order = sorted(dur.items(), key=lambda kv: -sum(kv[1]))
+    for name, v in order:
+        if "FillFunctor" in name or "copyBuffer" in name:
+            continue
+        short = name.replace("qsa::(anonymous namespace)::", "").replace("void ", "")
+        short = short.split("(")[0]
+        lines.append(f"| {short} | {len(v)} | {min(v):.2f} | {statistics.median(v):.2f} | "
+                     f"{_quantile(v, 0.9):.2f} | {statistics.mean(v):.2f} |")
+    lines.append("")
+    if notes:
+        lines += [notes.strip(), ""]
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        with open(stats[0]) as f:
+            raw = f.read().strip().splitlines()
+        lines += ["rocprofv3 --stats (kernel_stats.csv):", "", "```"] + raw[:12] + ["```", ""]
+    return "\n".join(lines)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("--trace", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", default="")
+    k.add_argument("--notes", default="")
+    k.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -137,6 +181,10 @@ def main() -> None:
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="", help="the profiling commands, for the record")
     a = ap.parse_args()
+    if a.cmd == "kernels":
+        with open(a.out, "w") as f:
+            f.write(kernels_md(a.trace, a.title, a.command, a.notes))
+        return
     res = traffic(a.fetch, a.write, a.kernel, a.copy_mib)
     res["workload"] = a.workload
     with open(a.out + ".json", "w") as f:
