@@ -71,6 +71,10 @@
  *             positioned; attention applies no RoPE)
  *   out       float32 [n_q][n_head][head_dim]
  *   K, V cache QSA_KV_F32:  float32 [n_seq][cap_cells][n_head_kv][head_dim]
+ *             QSA_KV_F16:  binary16 [n_seq][cap_cells][n_head_kv][head_dim],
+ *             value = float(h), exact (the KV type the fix of llama.cpp issue
+ *             #28734 requires: its fix summary and the comment that times
+ *             q8_0 KV against it)
  *             QSA_KV_Q8_0: bytes [n_seq][cap_cells][n_head_kv][head_dim/32*34];
  *             each 34-byte q8_0 block is a binary16 scale d followed by 32
  *             int8 q, value = float(d) * q.
@@ -101,6 +105,7 @@ extern "C" {
 /* KV cache element types. */
 #define QSA_KV_F32 0
 #define QSA_KV_Q8_0 1
+#define QSA_KV_F16 2
 
 /* Score modes of qsa_score_blocks. */
 #define QSA_SCORE_F32 0      /* decode: fp32, fixed summation order T      */

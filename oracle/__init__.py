@@ -254,8 +254,8 @@ def attend(q, k_seq, v_seq, kv_type: int, cells, n_head_kv: int,
            scale: float = 0.0) -> np.ndarray:
     """fp64 attention of one query ([H][D]) over one sequence's listed cells.
 
-    k_seq / v_seq: that sequence's cache rows, fp32 [cap][Hk][D] or q8_0 uint8
-    [cap][Hk][D/32*34]."""
+    k_seq / v_seq: that sequence's cache rows, fp32 [cap][Hk][D], q8_0 uint8
+    [cap][Hk][D/32*34] (kv_type 1) or binary16 [cap][Hk][D] (kv_type 2)."""
     q = _c(q, np.float32)
     H, D = q.shape
     cells = _c(cells, np.int32)

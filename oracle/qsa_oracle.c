@@ -393,11 +393,17 @@ int qo_select_dense_cells(const float *scores, int64_t pos, int r, int top_k,
 /* One KV row (one cell, one KV head) of D values, dequantised to fp32.
  * kv_type 0: fp32 row.  kv_type 1: q8_0 row, D/32 blocks of 34 bytes, each a
  * little-endian binary16 scale d followed by 32 int8 q; value = float(d)*q
- * (exact in fp32). */
+ * (exact in fp32).  kv_type 2: D binary16 values, the KV type of the fix of
+ * llama.cpp issue #28734 (fix summary); value = float(h), exact. */
 static void qo_row(const void *cache, int kv_type, int64_t row, int D, float *out)
 {
     if (kv_type == 0) {
         memcpy(out, (const float *)cache + (size_t)row * D, sizeof(float) * D);
+        return;
+    }
+    if (kv_type == 2) {
+        const uint16_t *h = (const uint16_t *)cache + (size_t)row * D;
+        for (int i = 0; i < D; i++) out[i] = qo_half_to_float(h[i]);
         return;
     }
     const uint8_t *p = (const uint8_t *)cache + (size_t)row * (D / 32) * 34;
@@ -418,8 +424,8 @@ int qo_attend(const float *q, int H, int Hk, int D, const void *k_cache,
               const void *v_cache, int kv_type, const int32_t *cells, int n,
               float scale, float *out)
 {
-    if (H <= 0 || Hk <= 0 || H % Hk || D <= 0 || D > QO_MAX_D ||
-        (kv_type == 1 && D % 32))
+    if (H <= 0 || Hk <= 0 || H % Hk || D <= 0 || D > QO_MAX_D || kv_type < 0 ||
+        kv_type > 2 || (kv_type == 1 && D % 32))
         return -1;
     int G = H / Hk;
     double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)D);
@@ -467,7 +473,8 @@ int qo_attend_dense_masked(const float *q, int H, int Hk, int D,
                            int kv_type, const uint8_t *sel_mask, int64_t pos,
                            float scale, float *out)
 {
-    if (H <= 0 || Hk <= 0 || H % Hk || D <= 0 || D > QO_MAX_D || pos < 0)
+    if (H <= 0 || Hk <= 0 || H % Hk || D <= 0 || D > QO_MAX_D || pos < 0 || kv_type < 0 ||
+        kv_type > 2 || (kv_type == 1 && D % 32))
         return -1;
     int G = H / Hk;
     double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)D);

@@ -211,7 +211,8 @@ def test_select_matches_oracle_on_shared_scores():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kv_type,H,Hk", [(synth.KV_F32, 4, 1), (synth.KV_Q8_0, 16, 2),
-                                          (synth.KV_Q8_0, 8, 4), (synth.KV_F32, 2, 2)])
+                                          (synth.KV_Q8_0, 8, 4), (synth.KV_F32, 2, 2),
+                                          (synth.KV_F16, 16, 2), (synth.KV_F16, 4, 1)])
 def test_attention_matches_oracle_on_shared_cells(kv_type, H, Hk):
     w = synth.Workload("att", 70 + H, 2, 3000, n_new=1, steps=1, H=H, Hk=Hk, top_k=2048,
                        kv_type=kv_type)
@@ -338,6 +339,13 @@ def test_end_to_end_multi_token_decode():
     sequences: several queries share each dirty block."""
     w = synth.Workload("multi", 91, 2, 20001, n_new=3, steps=6)
     _run_workload("multi", 6, w=w)
+
+
+def test_end_to_end_f16_kv_decode():
+    """f16 KV, the type of the pages' first fix: two sequences, one token each
+    per step, through both decode paths."""
+    w = synth.Workload("f16", 93, 2, 30001, n_new=1, steps=3, kv_type=synth.KV_F16)
+    _run_workload("f16", 3, w=w)
 
 
 # --------------------------------------------------------------------------

@@ -466,7 +466,7 @@ def test_select_early_positions_tail_only():
 # --------------------------------------------------------------------------
 
 def _deq(rows, kv_type, D):
-    if kv_type == synth.KV_F32:
+    if kv_type in (synth.KV_F32, synth.KV_F16):
         return rows.astype(np.float64)
     blk = rows.reshape(*rows.shape[:-1], D // 32, 34)
     scale = blk[..., :2].copy().view(np.float16)[..., 0].astype(np.float64)
@@ -486,14 +486,22 @@ def _sdpa_ref(q, k_rows, v_rows, kv_type, Hk, scale=None):
     return o[:, 0, :].numpy()
 
 
-@pytest.mark.parametrize("kv_type", [synth.KV_F32, synth.KV_Q8_0])
+def _store(x, kv_type):
+    if kv_type == synth.KV_F32:
+        return x
+    if kv_type == synth.KV_F16:
+        return x.astype(np.float16)
+    return synth.quantize_q8_0(x)
+
+
+@pytest.mark.parametrize("kv_type", [synth.KV_F32, synth.KV_Q8_0, synth.KV_F16])
 def test_attend_vs_torch_sdpa(kv_type):
     rng = np.random.default_rng(40 + kv_type)
     H, Hk, D, n = 8, 2, 256, 300
     x_k = rng.standard_normal((n, Hk, D)).astype(np.float32)
     x_v = rng.standard_normal((n, Hk, D)).astype(np.float32)
-    kc = x_k if kv_type == synth.KV_F32 else synth.quantize_q8_0(x_k)
-    vc = x_v if kv_type == synth.KV_F32 else synth.quantize_q8_0(x_v)
+    kc = _store(x_k, kv_type)
+    vc = _store(x_v, kv_type)
     q = rng.standard_normal((H, D)).astype(np.float32)
     cells = np.sort(rng.choice(n, size=77, replace=False)).astype(np.int32)
     got = oracle.attend(q, kc, vc, kv_type, cells, Hk)
@@ -515,6 +523,37 @@ def test_attend_q8_dequant_exact_on_grid():
     qv = rng.standard_normal((2, D)).astype(np.float32)
     out = oracle.attend(qv, rows, rows, 1, np.array([0], np.int32), 1)
     assert np.array_equal(out[0], x[0, 0]) and np.array_equal(out[1], x[0, 0])
+
+
+def test_attend_f16_rows_equal_their_f32_widening():
+    """binary16 -> binary32 is exact, so attention over an f16 cache equals,
+    bit for bit, attention over the same values stored as f32 (the widening
+    here is numpy's, not the oracle's)."""
+    rng = np.random.default_rng(44)
+    H, Hk, D, n = 8, 2, 256, 120
+    kh = (rng.standard_normal((n, Hk, D)) * 3).astype(np.float16)
+    vh = (rng.standard_normal((n, Hk, D)) * 3).astype(np.float16)
+    q = rng.standard_normal((H, D)).astype(np.float32)
+    cells = np.sort(rng.choice(n, size=41, replace=False)).astype(np.int32)
+    got = oracle.attend(q, kh, vh, synth.KV_F16, cells, Hk)
+    ref = oracle.attend(q, kh.astype(np.float32), vh.astype(np.float32), synth.KV_F32, cells, Hk)
+    assert np.array_equal(got, ref)
+
+
+def test_attend_f16_one_cell_returns_the_row_exactly():
+    """Over a one-cell set the output is that V row; binary16 edge values
+    (subnormals, -0, the largest finite 65504) come through unchanged."""
+    D = 256
+    v = np.zeros((1, 1, D), dtype=np.float16)
+    specials = np.array([65504.0, -65504.0, 2.0 ** -24, -(2.0 ** -24), 2.0 ** -14, -0.0, 1.0,
+                         -2.5, 0.1, 1000.0], dtype=np.float16)
+    v[0, 0, :specials.size] = specials
+    v[0, 0, specials.size:] = np.arange(D - specials.size, dtype=np.float16) / np.float16(7)
+    k = np.ones((1, 1, D), dtype=np.float16)
+    q = np.random.default_rng(45).standard_normal((2, D)).astype(np.float32)
+    out = oracle.attend(q, k, v, synth.KV_F16, np.array([0], np.int32), 1)
+    want = v[0, 0].astype(np.float32)
+    assert np.array_equal(out[0], want) and np.array_equal(out[1], want)
 
 
 def test_attend_identical_keys_gives_mean_of_values():

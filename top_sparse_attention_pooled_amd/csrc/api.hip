@@ -45,7 +45,7 @@ int check_dims(const qsa_dims *d) {
         return fail(QSA_EINVAL, "top_k %d must be a positive multiple of r %d", d->top_k, d->r);
     if (d->top_k / d->r > 4096)
         return fail(QSA_ENOTSUP, "top_k/r = %d above 4096", d->top_k / d->r);
-    if (d->kv_type != QSA_KV_F32 && d->kv_type != QSA_KV_Q8_0)
+    if (d->kv_type != QSA_KV_F32 && d->kv_type != QSA_KV_Q8_0 && d->kv_type != QSA_KV_F16)
         return fail(QSA_EINVAL, "kv_type %d unknown", d->kv_type);
     if (!(d->rope_theta > 1.0f)) return fail(QSA_EINVAL, "rope_theta must be > 1");
     if (!(d->rms_eps >= 0.0f)) return fail(QSA_EINVAL, "rms_eps must be >= 0");

@@ -565,8 +565,9 @@ hipError_t launch_kvt(const AttnArgs &a, int chunks_per_run, int n_runs, bool di
 hipError_t launch(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct,
                   hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;
-    return a.kv_type == QSA_KV_F32 ? launch_kvt<QSA_KV_F32>(a, chunks_per_run, n_runs, direct, st)
-                                   : launch_kvt<QSA_KV_Q8_0>(a, chunks_per_run, n_runs, direct, st);
+    if (a.kv_type == QSA_KV_F32) return launch_kvt<QSA_KV_F32>(a, chunks_per_run, n_runs, direct, st);
+    if (a.kv_type == QSA_KV_F16) return launch_kvt<QSA_KV_F16>(a, chunks_per_run, n_runs, direct, st);
+    return launch_kvt<QSA_KV_Q8_0>(a, chunks_per_run, n_runs, direct, st);
 }
 
 int decode_runs(int ld_cells) { return (ld_cells + kChunk - 1) / kChunk; }
@@ -618,8 +619,9 @@ hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnAr
         return launch_attn_decode(a, st);
     }
     bind_candidates(f, ws_idx);
-    return a.kv_type == QSA_KV_F32 ? launch_sel_kvt<QSA_KV_F32>(f, a, st)
-                                   : launch_sel_kvt<QSA_KV_Q8_0>(f, a, st);
+    if (a.kv_type == QSA_KV_F32) return launch_sel_kvt<QSA_KV_F32>(f, a, st);
+    if (a.kv_type == QSA_KV_F16) return launch_sel_kvt<QSA_KV_F16>(f, a, st);
+    return launch_sel_kvt<QSA_KV_Q8_0>(f, a, st);
 }
 
 

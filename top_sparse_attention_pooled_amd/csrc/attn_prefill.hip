@@ -20,8 +20,8 @@
 // q8_0 rows reach the wavefront as whole 16-byte pieces: the chunk's 64 rows
 // (K and V, 272 bytes each) are 17 coalesced loads per lane, prefetched one
 // chunk ahead in registers and written to an LDS stage, from which the
-// operands are read.  f32 rows (the small configuration) are gathered per
-// lane straight into the operand layout.
+// operands are read.  f32 and f16 rows are gathered per lane straight into
+// the operand layout.
 // Operands are rounded to fp16 (Q * scale, P, V; f32 K); sums and the
 // softmax state are fp32.
 #include <type_traits>
@@ -42,7 +42,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPChunk = 32;  // cells per chunk
 constexpr int kPWaves = 4;
 constexpr int kStride = kPWaves * kPChunk;
-constexpr int kCellCap = 4096;  // f32 kernel: cell indices held in LDS; the rest read directly
+constexpr int kCellCap = 4096;  // per-lane kernel: cell indices held in LDS; the rest read directly
 constexpr int kStageWords = kPChunk * kQ8Row / 4;  // raw rows of one chunk (K or V)
 constexpr int kPieces = 2 * kPChunk * kQ8Row / 16;     // 16-byte pieces per chunk
 static_assert(kPieces == 17 * kWave, "a chunk is 17 loads of 16 bytes per lane");
@@ -60,11 +60,11 @@ struct WaveTailT {
     _Float16 p[16][kPChunk];  // probabilities, [head row][cell]
     float m[16], l[16];
 };
-using WaveTail = WaveTailT<kHeadDim>;      // f32 rows: all dims at once
+using WaveTail = WaveTailT<kHeadDim>;      // f32 and f16 rows: all dims at once
 using HalfTail = WaveTailT<kHeadDim / 2>;  // q8_0 rows: V in two halves
 static_assert(sizeof(_Float16[kHeadDim / 2][kVtPitch]) >= sizeof(float[16][kHeadDim / 4]),
               "the merge buffer fits the half transpose");
-struct F32Wave {
+struct RowWave {
     WaveTail t;
 };
 struct Q8Wave {
@@ -475,12 +475,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     merge_store(a, i, g, hpk, sw, o, m_run, l_run);
 }
 
-// ---- f32 rows, gathered per lane ----
+// ---- f32 and f16 rows, gathered per lane ----
 
 // Same grid as k_attn_prefill_q8.
-__global__ __launch_bounds__(256) void k_attn_prefill_f32(AttnArgs a) {
-    constexpr int KVT = QSA_KV_F32;
-    __shared__ F32Wave sw[kPWaves];
+template <int KVT>
+__global__ __launch_bounds__(256) void k_attn_prefill_rows(AttnArgs a) {
+    __shared__ RowWave sw[kPWaves];
     __shared__ int32_t s_cells[kCellCap];  // the query's cell list (its first kCellCap)
     int i, g;
     if (!unit_of(a, i, g)) return;
@@ -558,7 +558,9 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;
     const dim3 grid((a.n_q + 7) / 8 * 8 * a.n_head_kv);
     if (a.kv_type == QSA_KV_F32)
-        hipLaunchKernelGGL(k_attn_prefill_f32, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_attn_prefill_rows<QSA_KV_F32>, grid, dim3(256), 0, st, a);
+    else if (a.kv_type == QSA_KV_F16)
+        hipLaunchKernelGGL(k_attn_prefill_rows<QSA_KV_F16>, grid, dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL(k_attn_prefill_q8, grid, dim3(256), 0, st, a);
     return hipGetLastError();

@@ -3,7 +3,8 @@
 // q8_0 rows: 8 blocks of (binary16 scale, 32 int8) = 272 bytes.  The slice
 // of dims 8j .. 8j+7 lies in block j/4 at byte 34*(j/4) + 2 + 8*(j%4), which
 // is 2 mod 4 for even blocks: it is read as aligned dwords and realigned with
-// a funnel shift.  f32 rows: 256 floats.
+// a funnel shift.  f32 rows: 256 floats.  f16 rows: 256 binary16 values, the
+// slice one 16-byte load, widened exactly.
 #pragma once
 
 #include "qsa_internal.h"
@@ -21,6 +22,10 @@ template <>
 struct RawRow<QSA_KV_Q8_0> {
     uint32_t w0, w1, w2, sw;
 };
+template <>
+struct RawRow<QSA_KV_F16> {
+    uint4 h;  // 8 binary16 values
+};
 
 template <int KVT>
 __device__ __forceinline__ RawRow<KVT> load_raw(const void *base, int64_t row, int j) {
@@ -30,6 +35,9 @@ __device__ __forceinline__ RawRow<KVT> load_raw(const void *base, int64_t row, i
                                                            row * kHeadDim + 8 * j);
         r.u = p[0];
         r.v = p[1];
+    } else if constexpr (KVT == QSA_KV_F16) {
+        r.h = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) +
+                                               row * kHeadDim + 8 * j);
     } else {
         const uint8_t *b = static_cast<const uint8_t *>(base) + row * kQ8Row;
         const int blk = j >> 2;
@@ -49,6 +57,13 @@ __device__ __forceinline__ void dequant(const RawRow<KVT> &r, int j, float (&x)[
     if constexpr (KVT == QSA_KV_F32) {
         x[0] = r.u.x; x[1] = r.u.y; x[2] = r.u.z; x[3] = r.u.w;
         x[4] = r.v.x; x[5] = r.v.y; x[6] = r.v.z; x[7] = r.v.w;
+    } else if constexpr (KVT == QSA_KV_F16) {
+        const uint32_t w[4] = {r.h.x, r.h.y, r.h.z, r.h.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xffffu));
+            x[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+        }
     } else {
         const int blk = j >> 2;
         const bool odd = blk & 1;  // block start 2 mod 4: int8 aligned, scale in high half

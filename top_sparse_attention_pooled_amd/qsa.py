@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqsa.so")
 
 QSA_OK, QSA_EINVAL, QSA_ENOTSUP, QSA_EWS, QSA_EHIP = 0, -1, -2, -3, -4
-KV_F32, KV_Q8_0 = 0, 1
+KV_F32, KV_Q8_0, KV_F16 = 0, 1, 2
 SCORE_F32, SCORE_BF16 = 0, 1
 OP_SELECT, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_SCORE_BF16, OP_SCORE_SELECT = 0, 1, 2, 3, 4
 OP_SCORE_SELECT_PREFILL = 5

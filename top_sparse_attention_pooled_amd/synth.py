@@ -23,6 +23,7 @@ T_KIDX, T_QIDX, T_Q, T_K, T_V = 0, 1, 2, 3, 4
 
 KV_F32 = 0
 KV_Q8_0 = 1
+KV_F16 = 2
 Q8_BLOCK = 32
 Q8_BYTES = 34  # binary16 scale + 32 int8
 TILE = 64      # pooled-key tile width in blocks (capacity granularity)
@@ -61,7 +62,11 @@ def quantize_q8_0(x: np.ndarray) -> np.ndarray:
 
 
 def row_bytes(kv_type: int, D: int) -> int:
-    return D * 4 if kv_type == KV_F32 else D // Q8_BLOCK * Q8_BYTES
+    if kv_type == KV_F32:
+        return D * 4
+    if kv_type == KV_F16:
+        return D * 2
+    return D // Q8_BLOCK * Q8_BYTES
 
 
 def round_up(x: int, m: int) -> int:
@@ -133,12 +138,15 @@ def make_kidx(w: Workload) -> np.ndarray:
 
 
 def make_kv(w: Workload, tensor_id: int) -> np.ndarray:
-    """K (tensor_id T_K) or V (T_V) cache for every sequence:
-    f32 [n_seq][cap][Hk][D] or q8_0 uint8 [n_seq][cap][Hk][D/32*34]."""
+    """K (tensor_id T_K) or V (T_V) cache for every sequence: f32 [n_seq][cap]
+    [Hk][D], f16 [n_seq][cap][Hk][D] (values rounded to nearest binary16) or
+    q8_0 uint8 [n_seq][cap][Hk][D/32*34]."""
     n_fill = w.n_cells0 + w.n_new * w.steps
     rb = row_bytes(w.kv_type, w.D)
     if w.kv_type == KV_F32:
         out = np.zeros((w.n_seq, w.cap_cells, w.Hk, w.D), dtype=np.float32)
+    elif w.kv_type == KV_F16:
+        out = np.zeros((w.n_seq, w.cap_cells, w.Hk, w.D), dtype=np.float16)
     else:
         out = np.zeros((w.n_seq, w.cap_cells, w.Hk, rb), dtype=np.uint8)
     chunk = 1 << 16
@@ -147,7 +155,12 @@ def make_kv(w: Workload, tensor_id: int) -> np.ndarray:
         for c0 in range(0, n_fill, chunk):
             c1 = min(n_fill, c0 + chunk)
             x = g.standard_normal(size=(c1 - c0, w.Hk, w.D), dtype=np.float32)
-            out[s, c0:c1] = x if w.kv_type == KV_F32 else quantize_q8_0(x)
+            if w.kv_type == KV_F32:
+                out[s, c0:c1] = x
+            elif w.kv_type == KV_F16:
+                out[s, c0:c1] = x.astype(np.float16)
+            else:
+                out[s, c0:c1] = quantize_q8_0(x)
     return out
 
 
