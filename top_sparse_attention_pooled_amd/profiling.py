@@ -180,6 +180,7 @@ def main() -> None:
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="", help="the profiling commands, for the record")
+    t.add_argument("--notes", default="", help="lines appended to OUT.md")
     a = ap.parse_args()
     if a.cmd == "kernels":
         with open(a.out, "w") as f:
@@ -204,6 +205,8 @@ def main() -> None:
                 f"{res['write_bytes'] / 1e6:.3f} MB, total "
                 f"{res['traffic_bytes'] / 1e6:.3f} MB per dispatch\n")
         f.write(f"- kernel sources sha256 {res['source_sha256']}\n")
+        if a.notes:
+            f.write(a.notes.strip() + "\n")
     print(json.dumps(res))
 
 
