@@ -220,3 +220,55 @@ def test_prefill_step_end_to_end():
         worst = max(worst, float(np.abs(go[i] - ref["out"][i]).max()))
     say(f"  worst attention error {worst:.2e} (fp16 operands, fp32 sums)")
     assert worst <= 2e-3
+
+
+def test_mixed_step_prefill_chunk_beside_decode_tokens():
+    """One launch sequence serving a 256-token prefill chunk of one session
+    next to a decode token of each of three other sessions at other depths
+    (the llama.cpp-multigpu README, on mixed prefill and generation: prompts
+    are prefilled in 256-token chunks beside the decoding slots).  Every query
+    is scored against its own session's blocks only.  Each query's selection
+    bit for bit, outputs within the attention tolerance."""
+    w = synth.Workload("mix", 95, 4, 7000, n_new=256, steps=1, top_k=512)
+    say("mixed step: 256-token chunk of seq 0 + one decode token of seqs 1-3, q8_0 KV")
+    kidx = synth.make_kidx(w)
+    k = synth.make_kv(w, synth.T_K)
+    v = synth.make_kv(w, synth.T_V)
+    layer = runtime.Layer(w, DEV, kidx=kidx, k=k, v=v)
+    n0 = np.array([7000, 6001, 4502, 6999], np.int32)
+    layer.rebuild(n0)
+    n = n0 + np.array([256, 1, 1, 1], np.int32)
+    layer.set_n_cells(n)
+    q_seq = np.concatenate([np.zeros(256, np.int32), np.arange(1, 4, dtype=np.int32)])
+    q_pos = np.concatenate([np.arange(7000, 7256, dtype=np.int32), n0[1:]]).astype(np.int32)
+    n_q = q_pos.size
+    q_idx = synth.normal((n_q, w.d), 95, 0, synth.T_QIDX)
+    q = synth.normal((n_q, w.H, w.D), 95, 0, synth.T_Q)
+    pairs = [(0, b) for b in range(7000 // w.r, 7255 // w.r + 1)]
+    pairs += [(s, int(n0[s]) // w.r) for s in range(1, 4)]
+    m = 4
+    while m < len(pairs):
+        m *= 2
+    dirty = np.asarray(pairs + [(-1, -1)] * (m - len(pairs)), np.int32)
+    nb_max = int(-(-int(n.max()) // w.r))
+    bufs = runtime.StepBuffers(layer.dims, n_q, nb_max, DEV, prefill=True)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    out = runtime.run_step(layer, bufs, t(q_idx), t(q), t(q_seq), t(q_pos),
+                           t(dirty.reshape(-1)), dirty.shape[0], mode=qsa.SCORE_BF16,
+                           prefill=True, path="indexer")
+    torch.cuda.synchronize()
+    ref_pooled = oracle_pooled(w, kidx, n)
+    ref = oracle.step(q_idx, q, q_seq, q_pos, ref_pooled, k, v, kv_type=w.kv_type,
+                      n_head_kv=w.Hk, r=w.r, top_k=w.top_k, theta=w.theta, nb_out=nb_max,
+                      bf16_scores=True)
+    gb, gc = out.sel_blocks.cpu().numpy(), out.sel_cells.cpu().numpy()
+    gn, go = out.n_sel.cpu().numpy(), out.out.cpu().numpy()
+    worst = 0.0
+    for i in range(n_q):
+        rb, rc = ref["blocks"][i], ref["cells"][i]
+        assert gn[i] == rc.size, i
+        assert np.array_equal(gb[i, :rb.size], rb), i
+        assert np.array_equal(gc[i, :rc.size], rc), i
+        worst = max(worst, float(np.abs(go[i] - ref["out"][i]).max()))
+    say(f"  worst attention error {worst:.2e}")
+    assert worst <= 2e-3
