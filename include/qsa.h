@@ -50,7 +50,9 @@
  * the incomplete tail rides a per-token side input].
  *
  * Buffer layouts (all little-endian, row-major unless stated):
- *   kidx      float32 [n_seq][cap_cells][d_idx]   per-cell indexer keys
+ *   kidx      float32, or bfloat16 bits when dims->kidx_type is QSA_KIDX_BF16
+ *             (widened exactly before the mean), [n_seq][cap_cells][d_idx]:
+ *             per-cell indexer keys
  *   pooled    float32 tiled: [n_seq][cap_blocks/64][d_idx/4][64][4];
  *             element (s, b, t) is at float offset
  *               ((s*(cap_blocks/64) + b/64) * (d_idx/4) + t/4) * 256
@@ -93,7 +95,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 /* Return codes.  0 is success; errors are negative. */
 #define QSA_OK 0
@@ -106,6 +108,10 @@ extern "C" {
 #define QSA_KV_F32 0
 #define QSA_KV_Q8_0 1
 #define QSA_KV_F16 2
+
+/* Per-cell indexer key storage (qsa_dims.kidx_type). */
+#define QSA_KIDX_F32 0
+#define QSA_KIDX_BF16 1
 
 /* Score modes of qsa_score_blocks. */
 #define QSA_SCORE_F32 0      /* decode: fp32, fixed summation order T      */
@@ -125,7 +131,12 @@ extern "C" {
  *              (t, t + d_idx/2), inverse frequency theta^(-2t/d_idx))
  *   rms_eps    epsilon of the pooled-key RMS norm
  *   idx_norm_w_dev  optional device float32 [d_idx] RMS-norm weight (NULL =
- *              none) */
+ *              none)
+ *   kidx_type  storage of the per-cell indexer keys: QSA_KIDX_F32 or
+ *              QSA_KIDX_BF16 (the pages do not fix their dtype; bf16 halves
+ *              the cache).  The pooled key is computed from the exactly
+ *              widened values, so a bf16 cache gives the pooled keys of its
+ *              f32 widening bit for bit. */
 typedef struct qsa_dims {
     int32_t n_head;
     int32_t n_head_kv;
@@ -138,6 +149,7 @@ typedef struct qsa_dims {
     float rope_theta;
     float rms_eps;
     const float *idx_norm_w_dev;
+    int32_t kidx_type;
 } qsa_dims;
 
 /* Sequence geometry shared by every call. */
@@ -180,7 +192,7 @@ int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q,
  * depend on the order of the list; listing a block twice recomputes it twice.
  * Listing every block of a sequence rebuilds it from scratch ("resume"). */
 int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs,
-                           const float *kidx_dev, const int32_t *dirty_dev,
+                           const void *kidx_dev, const int32_t *dirty_dev,
                            int32_t n_dirty, float *pooled_dev,
                            uint16_t *pooled_bf16_dev, void *stream);
 
@@ -239,7 +251,7 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
  *   Workspace: qsa_workspace_size(QSA_OP_SCORE_SELECT_PREFILL, n_q, nb_max)
  *   bytes, 16-byte aligned, no initial contents required.
  * Needs nb_max <= 131072 (else QSA_ENOTSUP). */
-int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const void *kidx_dev,
                              const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
                              uint16_t *pooled_bf16_dev, const float *q_idx_dev,
                              const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
@@ -264,7 +276,7 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const f
  * same workspace, scores and geometry, and calls that share a workspace must
  * not overlap.  The split calls need nb_max <= 131072 (else QSA_ENOTSUP);
  * qsa_score_select_decode then falls back to the three general calls. */
-int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const void *kidx_dev,
                             const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
                             uint16_t *pooled_bf16_dev, const float *q_idx_dev,
                             const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
@@ -273,7 +285,7 @@ int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const fl
                             int32_t *n_sel_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
 int qsa_decode_score_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
-                                const float *kidx_dev, const int32_t *dirty_dev,
+                                const void *kidx_dev, const int32_t *dirty_dev,
                                 int32_t n_dirty, float *pooled_dev, uint16_t *pooled_bf16_dev,
                                 const float *q_idx_dev, const int32_t *q_seq_dev,
                                 const int32_t *q_pos_dev, int32_t n_q, int32_t nb_max,

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_error_string():
-    assert qsa.version() == 1
+    assert qsa.version() == 2
     assert isinstance(qsa.load().qsa_last_error(), bytes)
 
 
@@ -65,6 +65,7 @@ def _seqs(cap=4096 * 4, n_cells=FAKE):
     ("top_k", 4 * 4097, qsa.QSA_ENOTSUP),
     ("r", 0, qsa.QSA_ENOTSUP),
     ("kv_type", 7, qsa.QSA_EINVAL),
+    ("kidx_type", 2, qsa.QSA_EINVAL),
     ("rope_theta", 0.5, qsa.QSA_EINVAL),
 ])
 def test_bad_dims_rejected(field, value, code):
@@ -73,6 +74,20 @@ def test_bad_dims_rejected(field, value, code):
     with pytest.raises(qsa.QsaError) as e:
         qsa.update_pooled_keys(d, _seqs(), FAKE, FAKE, 4, FAKE, None, stream=0)
     assert e.value.code == code
+
+
+def test_kidx_alignment_follows_its_type():
+    """f32 keys need 4-byte alignment, bf16 keys 2 (a 2-byte offset is
+    rejected for f32 only)."""
+    d = qsa.Dims()
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.update_pooled_keys(d, _seqs(), FAKE + 2, FAKE, 4, FAKE, None, stream=0)
+    assert e.value.code == qsa.QSA_EINVAL
+    assert "kidx" in str(e.value)
+    d.kidx_type = qsa.KIDX_BF16
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.update_pooled_keys(d, _seqs(), FAKE + 1, FAKE, 4, FAKE, None, stream=0)
+    assert "kidx" in str(e.value)
 
 
 def test_bad_geometry_and_pointers_rejected():
@@ -183,3 +198,18 @@ def test_no_kernel_spills_to_scratch():
     assert res, "no kernel resource report"
     spilled = {k: v["scratch"] for k, v in res.items() if v.get("scratch", 0) > 0}
     assert not spilled, spilled
+
+
+def test_bf16_key_storage_helpers():
+    """The bf16 per-cell key storage used by the tests: round to nearest even
+    (as torch rounds) and an exact widening back."""
+    import numpy as np
+    import torch
+    from top_sparse_attention_pooled_amd import synth
+    x = np.random.default_rng(3).standard_normal(50000).astype(np.float32) * 7
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]  # ties go to even
+    bits = synth.to_bf16_bits(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, want)
+    assert np.array_equal(synth.widen_kidx(bits),
+                          torch.from_numpy(x).to(torch.bfloat16).float().numpy())

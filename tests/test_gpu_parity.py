@@ -26,7 +26,13 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def f32_keys(kidx):
+    """The oracle's input: per-cell keys as float32 (bf16 bits widened exactly)."""
+    return synth.widen_kidx(kidx.view(np.uint16) if kidx.dtype == np.int16 else kidx)
+
+
 def oracle_pooled(w, kidx, n_cells):
+    kidx = f32_keys(kidx)
     pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
     pairs = [(s, b) for s in range(w.n_seq) for b in range(-(-int(n_cells[s]) // w.r))]
     oracle.update_pooled(kidx, np.asarray(n_cells, np.int32), np.array(pairs, np.int32),
@@ -88,6 +94,24 @@ def test_pooled_keys_match_oracle_ragged():
         nb = -(-int(n_cells[s]) // w.r)
         want = oracle.round_bf16(g32[s, :nb]).view(np.uint32) >> 16
         assert np.array_equal(gb[s, :nb].astype(np.uint32), want)
+
+
+def test_pooled_keys_from_bf16_storage():
+    """bf16 per-cell keys: the pooled keys are those of their exact f32
+    widening, bit for bit like the f32 case, on ragged lengths."""
+    w = synth.Workload("small_bf16", 52, 3, 4000, n_new=1, steps=200, top_k=64,
+                       kidx_type=synth.KIDX_BF16)
+    say("pooled: bf16 per-cell keys, 3 seqs, ragged lengths")
+    layer = runtime.Layer(w, DEV)
+    assert layer.kidx.dtype == torch.int16
+    kidx = layer.kidx.cpu().numpy()
+    n_cells = np.array([4001, 3, 2046], np.int32)
+    layer.rebuild(n_cells)
+    torch.cuda.synchronize()
+    ref = oracle_pooled(w, kidx, n_cells)
+    frac = check_pooled(layer.pooled_rows().cpu().numpy(), ref, w, n_cells)
+    say(f"  pooled bit-exact fraction {frac:.6f}")
+    assert frac >= 0.999
 
 
 def test_incremental_update_equals_full_rebuild():
@@ -287,7 +311,7 @@ def _run_workload(name, steps, check_every=1, w=None, paths=("attend", "general"
             outs[path] = runtime.run_step(layer, bufs, t(q_idx), t(q), t(q_seq), t(q_pos),
                                           t(dirty.reshape(-1)), dirty.shape[0], path=path)
         torch.cuda.synchronize()
-        oracle.update_pooled(kidx, n, dirty, ref_pooled, w.r, w.theta, w.eps)
+        oracle.update_pooled(f32_keys(kidx), n, dirty, ref_pooled, w.r, w.theta, w.eps)
         if step % check_every:
             continue
         ref = oracle.step(q_idx, q, q_seq, q_pos, ref_pooled, k, v, kv_type=w.kv_type,
@@ -339,6 +363,14 @@ def test_end_to_end_multi_token_decode():
     sequences: several queries share each dirty block."""
     w = synth.Workload("multi", 91, 2, 20001, n_new=3, steps=6)
     _run_workload("multi", 6, w=w)
+
+
+def test_end_to_end_bf16_keys_decode():
+    """bf16 per-cell indexer keys: the dirty block recomputed inside the
+    scoring kernel and by the update call, both decode paths."""
+    w = synth.Workload("bf16keys", 94, 2, 30001, n_new=1, steps=3,
+                       kidx_type=synth.KIDX_BF16)
+    _run_workload("bf16keys", 3, w=w)
 
 
 def test_end_to_end_f16_kv_decode():

@@ -47,6 +47,8 @@ int check_dims(const qsa_dims *d) {
         return fail(QSA_ENOTSUP, "top_k/r = %d above 4096", d->top_k / d->r);
     if (d->kv_type != QSA_KV_F32 && d->kv_type != QSA_KV_Q8_0 && d->kv_type != QSA_KV_F16)
         return fail(QSA_EINVAL, "kv_type %d unknown", d->kv_type);
+    if (d->kidx_type != QSA_KIDX_F32 && d->kidx_type != QSA_KIDX_BF16)
+        return fail(QSA_EINVAL, "kidx_type %d unknown", d->kidx_type);
     if (!(d->rope_theta > 1.0f)) return fail(QSA_EINVAL, "rope_theta must be > 1");
     if (!(d->rms_eps >= 0.0f)) return fail(QSA_EINVAL, "rms_eps must be >= 0");
     if (d->idx_norm_w_dev && !aligned(d->idx_norm_w_dev, 4))
@@ -68,6 +70,11 @@ int check_seqs(const qsa_dims *d, const qsa_seqs *s) {
 }
 
 qsa::SeqGeom geom(const qsa_seqs *s) { return {s->n_seq, s->cap_cells, s->n_cells_dev}; }
+
+size_t kidx_align(const qsa_dims *d) { return d->kidx_type == QSA_KIDX_BF16 ? 2 : 4; }
+qsa::KidxRef kidx_ref(const qsa_dims *d, const void *kidx) {
+    return {kidx, d->kidx_type == QSA_KIDX_BF16 ? 1 : 0};
+}
 
 // RoPE inverse frequencies omega_t = theta^(-2t/d) for d = 128, in fp64.
 // With d/2 = 2^6, theta^(-2t/d) = theta^(-t/64) is the product over the set
@@ -142,7 +149,7 @@ int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q, int32_t nb
     return ok();
 }
 
-int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs, const void *kidx_dev,
                            const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
                            uint16_t *pooled_bf16_dev, void *stream) {
     int rc = check_dims(dims);
@@ -150,13 +157,14 @@ int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs, const flo
     if (rc) return rc;
     if (n_dirty < 0) return fail(QSA_EINVAL, "n_dirty negative");
     if (n_dirty == 0) return ok();
-    if (!kidx_dev || !aligned(kidx_dev, 4)) return fail(QSA_EINVAL, "kidx_dev NULL or misaligned");
+    if (!kidx_dev || !aligned(kidx_dev, kidx_align(dims)))
+        return fail(QSA_EINVAL, "kidx_dev NULL or misaligned");
     if (!dirty_dev || !aligned(dirty_dev, 4)) return fail(QSA_EINVAL, "dirty_dev NULL or misaligned");
     if (!pooled_dev || !aligned(pooled_dev, 16))
         return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
     if (pooled_bf16_dev && !aligned(pooled_bf16_dev, 16))
         return fail(QSA_EINVAL, "pooled_bf16_dev not 16-byte aligned");
-    qsa::UpdateArgs a{geom(seqs), kidx_dev,     dirty_dev,      n_dirty,
+    qsa::UpdateArgs a{geom(seqs), kidx_ref(dims, kidx_dev), dirty_dev, n_dirty,
                       pooled_dev, pooled_bf16_dev, dims->r, dims->rms_eps,
                       dims->idx_norm_w_dev, rope_table(dims->rope_theta)};
     return launched(qsa::launch_update_pooled(a, (hipStream_t)stream), "update_pooled_keys");
@@ -226,7 +234,7 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const flo
 }
 
 // Shared validation of the decode indexer calls; fills *f.
-static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const void *kidx_dev,
                            const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
                            uint16_t *pooled_bf16_dev, const float *q_idx_dev,
                            const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
@@ -250,7 +258,8 @@ static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const flo
     if (need_scoring) {
         if (n_dirty < 0) return fail(QSA_EINVAL, "n_dirty negative");
         if (n_dirty > 0 &&
-            (!kidx_dev || !dirty_dev || !aligned(kidx_dev, 4) || !aligned(dirty_dev, 4)))
+            (!kidx_dev || !dirty_dev || !aligned(kidx_dev, kidx_align(dims)) ||
+             !aligned(dirty_dev, 4)))
             return fail(QSA_EINVAL, "kidx_dev/dirty_dev NULL or misaligned");
         if (pooled_bf16_dev && !aligned(pooled_bf16_dev, 16))
             return fail(QSA_EINVAL, "pooled_bf16_dev not 16-byte aligned");
@@ -272,7 +281,7 @@ static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const flo
                           rope_table(dims->rope_theta)};
     f->pooled_w = pooled_dev;
     f->pooled_bf16 = pooled_bf16_dev;
-    f->kidx = kidx_dev;
+    f->kidx = kidx_ref(dims, kidx_dev);
     f->dirty = dirty_dev;
     f->n_dirty = need_scoring ? n_dirty : 0;
     f->eps = dims->rms_eps;
@@ -284,7 +293,7 @@ static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const flo
     return QSA_OK;
 }
 
-int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const void *kidx_dev,
                              const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
                              uint16_t *pooled_bf16_dev, const float *q_idx_dev,
                              const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,
@@ -300,7 +309,8 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const f
     if (nb_max > qsa::kFusedMaxBlocks)
         return fail(QSA_ENOTSUP, "nb_max %d above %d", nb_max, qsa::kFusedMaxBlocks);
     if (n_dirty < 0) return fail(QSA_EINVAL, "n_dirty negative");
-    if (n_dirty > 0 && (!kidx_dev || !dirty_dev || !aligned(kidx_dev, 4) || !aligned(dirty_dev, 4)))
+    if (n_dirty > 0 && (!kidx_dev || !dirty_dev || !aligned(kidx_dev, kidx_align(dims)) ||
+                        !aligned(dirty_dev, 4)))
         return fail(QSA_EINVAL, "kidx_dev/dirty_dev NULL or misaligned");
     if (!pooled_dev || !aligned(pooled_dev, 16))
         return fail(QSA_EINVAL, "pooled_dev NULL or not 16-byte aligned");
@@ -317,7 +327,7 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const f
     const qsa::RopeTable rope = rope_table(dims->rope_theta);
     hipError_t e = hipSuccess;
     if (n_dirty > 0) {
-        qsa::UpdateArgs u{geom(seqs), kidx_dev,        dirty_dev, n_dirty,
+        qsa::UpdateArgs u{geom(seqs), kidx_ref(dims, kidx_dev), dirty_dev, n_dirty,
                           pooled_dev, pooled_bf16_dev, dims->r,   dims->rms_eps,
                           dims->idx_norm_w_dev, rope};
         e = qsa::launch_update_pooled(u, (hipStream_t)stream);
@@ -333,7 +343,7 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const f
 }
 
 int qsa_decode_score_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
-                                const float *kidx_dev, const int32_t *dirty_dev, int32_t n_dirty,
+                                const void *kidx_dev, const int32_t *dirty_dev, int32_t n_dirty,
                                 float *pooled_dev, uint16_t *pooled_bf16_dev,
                                 const float *q_idx_dev, const int32_t *q_seq_dev,
                                 const int32_t *q_pos_dev, int32_t n_q, int32_t nb_max,
@@ -365,7 +375,7 @@ int qsa_decode_select_candidates(const qsa_dims *dims, const qsa_seqs *seqs,
                     "decode_select_candidates");
 }
 
-int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const float *kidx_dev,
+int qsa_score_select_decode(const qsa_dims *dims, const qsa_seqs *seqs, const void *kidx_dev,
                             const int32_t *dirty_dev, int32_t n_dirty, float *pooled_dev,
                             uint16_t *pooled_bf16_dev, const float *q_idx_dev,
                             const int32_t *q_seq_dev, const int32_t *q_pos_dev, int32_t n_q,

@@ -7,6 +7,8 @@
 // call fmaf explicitly.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -119,19 +121,41 @@ __device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p
 // split-half RoPE pair).  The first level of T pairs dims (t, t+64) in-lane;
 // the rest is an xor butterfly whose lane-0 value is exactly the
 // stride-halving tree (xor h pairs lane t < h with t + h).
-__device__ __forceinline__ void pooled_key_lane(const float *kidx, int64_t cap_cells, int s,
+// Per-cell indexer keys: float32, or bfloat16 bits widened exactly to fp32.
+struct KidxRef {
+    const void *p;
+    int32_t bf16;
+};
+
+template <bool BF16>
+__device__ __forceinline__ float kidx_value(const void *p, int64_t i) {
+    if constexpr (BF16)
+        return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+    else
+        return static_cast<const float *>(p)[i];
+}
+
+__device__ __forceinline__ void pooled_key_lane(KidxRef kidx, int64_t cap_cells, int s,
                                                 int64_t b, int64_t n, int r, float eps,
                                                 const float *gamma, const RopeTable &rt,
                                                 int lane, float &out_lo, float &out_hi) {
     const int64_t first = b * r;
     const int m = (int)((n - first) < r ? (n - first) : r);
-    const float *x = kidx + ((int64_t)s * cap_cells + first) * kDIdx;
-    float lo = x[lane];
-    float hi = x[lane + 64];
-    for (int j = 1; j < m; ++j) {
-        lo = lo + x[j * kDIdx + lane];
-        hi = hi + x[j * kDIdx + lane + 64];
-    }
+    const int64_t x = ((int64_t)s * cap_cells + first) * kDIdx;
+    float lo, hi;
+    auto cell_sum = [&](auto bf16) {
+        constexpr bool BF = decltype(bf16)::value;
+        lo = kidx_value<BF>(kidx.p, x + lane);
+        hi = kidx_value<BF>(kidx.p, x + lane + 64);
+        for (int j = 1; j < m; ++j) {
+            lo = lo + kidx_value<BF>(kidx.p, x + j * kDIdx + lane);
+            hi = hi + kidx_value<BF>(kidx.p, x + j * kDIdx + lane + 64);
+        }
+    };
+    if (kidx.bf16)
+        cell_sum(std::true_type{});
+    else
+        cell_sum(std::false_type{});
     const float fm = (float)m;
     lo = lo / fm;
     hi = hi / fm;
@@ -189,7 +213,7 @@ struct SeqGeom {
 
 struct UpdateArgs {
     SeqGeom g;
-    const float *kidx;
+    KidxRef kidx;
     const int32_t *dirty;
     int32_t n_dirty;
     float *pooled;
@@ -226,7 +250,7 @@ struct DecodeIdxArgs {
     ScoreArgs s;
     float *pooled_w;        // same buffer as s.pooled, written by the update part
     uint16_t *pooled_bf16;  // optional bf16 copy, written by the update part
-    const float *kidx;
+    KidxRef kidx;
     const int32_t *dirty;
     int32_t n_dirty;
     float eps;

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libqsa.so")
 
 QSA_OK, QSA_EINVAL, QSA_ENOTSUP, QSA_EWS, QSA_EHIP = 0, -1, -2, -3, -4
 KV_F32, KV_Q8_0, KV_F16 = 0, 1, 2
+KIDX_F32, KIDX_BF16 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
 OP_SELECT, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_SCORE_BF16, OP_SCORE_SELECT = 0, 1, 2, 3, 4
 OP_SCORE_SELECT_PREFILL = 5
@@ -41,7 +42,7 @@ class _Dims(ctypes.Structure):
                 ("r", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("kv_type", ctypes.c_int32), ("kq_scale", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("idx_norm_w_dev", ctypes.c_void_p)]
+                ("idx_norm_w_dev", ctypes.c_void_p), ("kidx_type", ctypes.c_int32)]
 
 
 class _Seqs(ctypes.Structure):
@@ -115,11 +116,12 @@ class Dims:
     rope_theta: float = 1.0e4
     rms_eps: float = 1.0e-6
     idx_norm_w: Optional[object] = None  # device float32 tensor [d_idx] or None
+    kidx_type: int = KIDX_F32
 
     def c(self) -> _Dims:
         return _Dims(self.n_head, self.n_head_kv, self.head_dim, self.d_idx, self.r,
                      self.top_k, self.kv_type, self.kq_scale, self.rope_theta,
-                     self.rms_eps, _ptr(self.idx_norm_w))
+                     self.rms_eps, _ptr(self.idx_norm_w), self.kidx_type)
 
     @property
     def ld_cells(self) -> int:

@@ -18,7 +18,7 @@ from . import synth
 def dims_of(w: synth.Workload) -> qsa.Dims:
     return qsa.Dims(n_head=w.H, n_head_kv=w.Hk, head_dim=w.D, d_idx=w.d, r=w.r,
                     top_k=w.top_k, kv_type=w.kv_type, kq_scale=0.0,
-                    rope_theta=w.theta, rms_eps=w.eps)
+                    rope_theta=w.theta, rms_eps=w.eps, kidx_type=w.kidx_type)
 
 
 def untile_pooled(flat: torch.Tensor, n_seq: int, cap_blocks: int, d: int = 128) -> torch.Tensor:
@@ -50,6 +50,8 @@ class Layer:
         kidx = synth.make_kidx(w) if kidx is None else kidx
         k = synth.make_kv(w, synth.T_K) if k is None else k
         v = synth.make_kv(w, synth.T_V) if v is None else v
+        # bf16 keys travel as int16 (torch's uint16 lacks device copies here)
+        kidx = kidx.view(np.int16) if kidx.dtype == np.uint16 else kidx
         self.kidx = torch.from_numpy(kidx).to(self.device)
         self.k = torch.from_numpy(k).to(self.device)
         self.v = torch.from_numpy(v).to(self.device)

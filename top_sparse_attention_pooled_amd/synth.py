@@ -24,6 +24,8 @@ T_KIDX, T_QIDX, T_Q, T_K, T_V = 0, 1, 2, 3, 4
 KV_F32 = 0
 KV_Q8_0 = 1
 KV_F16 = 2
+KIDX_F32 = 0
+KIDX_BF16 = 1
 Q8_BLOCK = 32
 Q8_BYTES = 34  # binary16 scale + 32 int8
 TILE = 64      # pooled-key tile width in blocks (capacity granularity)
@@ -89,6 +91,7 @@ class Workload:
     r: int = 4
     top_k: int = 2048
     kv_type: int = KV_Q8_0
+    kidx_type: int = KIDX_F32
     theta: float = 1.0e4
     eps: float = 1.0e-6
     note: str = ""
@@ -129,12 +132,27 @@ WORKLOADS = {
 
 def make_kidx(w: Workload) -> np.ndarray:
     """Per-cell indexer keys [n_seq][cap_cells][d] (cells past the last step are
-    zero)."""
+    zero): float32, or for kidx_type KIDX_BF16 their bfloat16 bits (uint16,
+    rounded to nearest even)."""
     n_fill = w.n_cells0 + w.n_new * w.steps
     out = np.zeros((w.n_seq, w.cap_cells, w.d), dtype=np.float32)
     for s in range(w.n_seq):
         out[s, :n_fill] = normal((n_fill, w.d), w.cfg_id, s, T_KIDX)
-    return out
+    return to_bf16_bits(out) if w.kidx_type == KIDX_BF16 else out
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits (uint16), round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def widen_kidx(kidx: np.ndarray) -> np.ndarray:
+    """Per-cell keys as float32: bfloat16 bits widened exactly, float32 as is."""
+    if kidx.dtype == np.uint16:
+        return (kidx.astype(np.uint32) << 16).view(np.float32)
+    return kidx
 
 
 def make_kv(w: Workload, tensor_id: int) -> np.ndarray:
