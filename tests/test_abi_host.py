@@ -163,8 +163,10 @@ def test_fused_select_attend_limits():
 def test_prefill_indexer_workspace_and_limits():
     d = qsa.Dims()
     a256 = lambda x: -(-x // 256) * 256
-    ld = -(-49785 // 256) * 256  # MFMA score row: whole 64-block groups, 4 per 256 blocks
-    want = a256(512 * ld * 4) + a256(512 * 128 * 2) + a256(512 * 4)
+    n_grp = -(-49785 // 256) * 4  # 64-block groups, 4 per 256 blocks
+    # subgroup maxima (4 per group), thresholds, group masks, roped queries, Delta
+    want = (a256(512 * n_grp * 4 * 4) + a256(512 * 4) + a256(512 * n_grp * 8)
+            + a256(512 * 128 * 2) + a256(512 * 4))
     assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 512, 49785) == want
     assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 0, 49785) == 0
     big = 131073  # blocks: above what the selection's bitmap holds

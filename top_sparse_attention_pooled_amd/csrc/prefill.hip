@@ -8,18 +8,23 @@
 // |q_t k_t| of the true sum, and sum |q_t k_t| <= |q_i| * |k| with |k| <=
 // sqrt(d) * max(1, |gamma|) for an RMS-normed key, so |s_mfma - s_T| <=
 // Delta_i = 2^-15 * |q_i| * sqrt(d) * max(1, |gamma|) * (1 + 2^-8), rounded
-// up.  Selection then needs exact scores only near the cut:
+// up.  The MFMA scores are never stored:
 //   1. k_rope_queries_delta: roped bf16 queries and Delta_i;
-//   2. k_prefill_scores: the MFMA score matrix, written densely;
-//   3. k_select_prefill, per query: a_B = the B-th largest MFMA score
-//      (radix select on the row).  Since at least B blocks have MFMA score
-//      >= a_B, the exact B-th largest S_B is >= a_B - Delta; and S_B <= a_B
-//      + Delta.  So a block with MFMA score > a_B + 2 Delta scores exactly
-//      above S_B (kept), one below a_B - 2 Delta exactly below S_B (dropped),
-//      and only the band in between is rescored in order T; the exact top
-//      (B - kept) of the band completes the set.  If the band overflows its
-//      LDS list, or Delta is outside the range where no partial sum can
-//      overflow or underflow, every causal block is rescored instead.
+//   2. k_prefill_scores<kSubMax>: per query, the largest MFMA score of each
+//      16-block subgroup of its causal blocks;
+//   3. k_prefill_tau: tau_i = the B-th largest of those maxima.  B distinct
+//      blocks then have MFMA score >= tau_i, so the exact B-th largest score
+//      S_B is >= tau_i - Delta, and every block of the exact top-B has MFMA
+//      score >= S_B - Delta >= tau_i - 2 Delta.  The filter threshold is
+//      tau_i - 2 Delta rounded down (-inf, every causal block, when there are
+//      fewer than B subgroups);
+//   4. k_prefill_scores<kMask>: per (query, 64-block group), a bit mask of
+//      the blocks whose MFMA score reaches the threshold;
+//   5. k_select_prefill: the masked blocks rescored in order T; their exact
+//      top-B is the exact top-B of all blocks, which lies among them.  If
+//      more blocks pass than the LDS list holds, or Delta is outside the
+//      range where no partial sum can overflow or underflow, every causal
+//      block is rescored instead.
 #include "mfma_tile.h"
 #include "topk_engine.h"
 #include "wave_ops.h"
@@ -28,9 +33,9 @@ namespace qsa {
 
 namespace {
 
-constexpr int kSelPNT = 512;      // selection workgroup (256 registers per lane)
-constexpr int kApproxVec = 26;    // score vectors of 4 blocks held in registers per thread
-constexpr int kBandCap = 4096;    // band blocks rescored from the LDS list
+constexpr int kSelPNT = 512;      // selection workgroup
+constexpr int kBandCap = 8192;    // masked blocks rescored from the LDS list (16 x B)
+constexpr int kTauNT = 256;       // threshold workgroup
 constexpr int kPrefMaxBlocks = kFusedMaxBlocks;
 constexpr float kDeltaMin = 0x1p-100f, kDeltaMax = 0x1p100f;
 
@@ -84,18 +89,46 @@ __global__ __launch_bounds__(256) void k_rope_queries_delta(ScoreArgs a, const f
     }
 }
 
+// What a k_prefill_scores pass leaves per query row and group of 64 blocks.
+constexpr int kSubMax = 0;  // the largest MFMA score of each 16-block subgroup
+constexpr int kMask = 1;    // the bit mask of blocks whose score reaches the threshold
+
+// Max of v[0..3] (the four 16-block subgroups of a group, cb) over the 16
+// lanes of a DPP row: exchange-halving steps, so lane col ends with the
+// maximum of subgroup 2*bit3(col) + bit2(col).
+__device__ __forceinline__ float row16_max4(float (&v)[4], int col) {
+    const bool hi8 = col & 8, hi4 = col & 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float keep = hi8 ? v[h + 2] : v[h];
+        const float send = hi8 ? v[h] : v[h + 2];
+        v[h] = fmaxf(keep, xor_lane_f<8>(send));
+    }
+    const float keep = hi4 ? v[1] : v[0];
+    const float send = hi4 ? v[0] : v[1];
+    float m = fmaxf(keep, xor_lane_f<4>(send));
+    m = fmaxf(m, xor_lane_f<2>(m));
+    m = fmaxf(m, xor_lane_f<1>(m));
+    return m;
+}
+
 // 1-D grid over (slab sb of `slab` group tiles, query tile qt of 64
 // queries); a group tile is 4 groups of 64 blocks, one per wavefront.  The
 // hardware deals workgroup ids to the 8 XCDs round-robin, so ids are laid out
 // to put the query tiles of one slab on one XCD, where its keys are read
 // from HBM once and then hit that XCD's L2.  A workgroup loads its queries
-// once and sweeps its slab, writing w.approx[q][b] for every causal block of
-// its rows (other entries are left as they are: the selection never reads
-// them).  When all valid queries of the tile belong to one sequence (the
-// usual ubatch) the next group's keys are in flight while the current group
-// is on the matrix cores; otherwise each group is swept once per distinct
-// sequence.
-__global__ __launch_bounds__(256) void k_prefill_scores(ScoreArgs a, PrefillWs w, int n_gt,
+// once and sweeps its slab.  Per query row and group it writes, for every
+// group any row of its sequence needs (blocks past a row's causal limit never
+// count):
+//   kSubMax: w.smax[q][4*grp + c], the largest score of subgroup c (-inf if
+//            none of its blocks is causal);
+//   kMask:   w.mask[q][grp], bit j set when block 64*grp + j is causal and
+//            its score is >= w.thr[q].
+// When all valid queries of the tile belong to one sequence (the usual
+// ubatch) the next group's keys are in flight while the current group is on
+// the matrix cores; otherwise each group is swept once per distinct sequence.
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_scores(ScoreArgs a, PrefillWs w, int n_gt,
                                                        int n_qt, int slab) {
     const int id = blockIdx.x;
     const int n_slab = (n_gt + slab - 1) / slab;
@@ -122,24 +155,78 @@ __global__ __launch_bounds__(256) void k_prefill_scores(ScoreArgs a, PrefillWs w
         }
     }
     const uint64_t valid_rows = __ballot(my_seq >= 0);
-    if (!valid_rows) return;
-    bf16x8_t A[4][4];
-    load_query_tile(w.qr, q0, a.n_q, A);
-    // result lane l holds rows rb*16 + 4*(l/16) + jj of column l % 16
-    const int rsub = (lane >> 4) * 4;
-    float *const out = w.approx + (int64_t)q0 * w.ld + (lane & 15);
-    f32x4_t acc[4][4];
-    auto store_rows = [&](int64_t gb0, uint64_t rows) {
+    if (!valid_rows) return;  // (the same for every wavefront of the workgroup)
+    // the 64 rows' causal limits and thresholds, for the result layout: lane
+    // l holds rows rb*16 + 4*(l/16) + jj of column l % 16
+    __shared__ int s_nc[64];
+    __shared__ float s_thr[64];
+    // the 64 roped queries (A operands), rows padded to 272 bytes so the 16
+    // rows one MFMA operand read touches fall in different banks
+    constexpr int kQPitch = kDIdx + 8;
+    __shared__ __align__(16) uint16_t s_q[64][kQPitch];
+    if (wave == 0) {
+        s_nc[lane] = my_nc;
+        if constexpr (MODE == kMask) s_thr[lane] = q0 + lane < a.n_q ? w.thr[q0 + lane] : 0.f;
+    }
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+    for (int u = 0; u < 4; ++u) {
+        const int x = u * 256 + (int)threadIdx.x;  // 16-byte piece: row x / 16, part x % 16
+        const int rr = x >> 4, part = x & 15;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (q0 + rr < a.n_q)
+            v = *reinterpret_cast<const u32x4_t *>(w.qr + (int64_t)(q0 + rr) * kDIdx + part * 8);
+        *reinterpret_cast<u32x4_t *>(&s_q[rr][part * 8]) = v;
+    }
+    __syncthreads();
+    const int col = lane & 15, quad = lane >> 4;
+    const int64_t n_sub = 4 * (int64_t)w.n_grp;
+    // One 16-row band rb of the 64 x 64 tile on the matrix cores, then its
+    // epilogue (the band's accumulators are all that is live).
+    auto tile = [&](const bf16x8_t (&B)[4][4], int64_t grp, uint64_t rows) {
+        const int64_t gb0 = grp * 64;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            bf16x8_t A[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                A[ks] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t *>(&s_q[rb * 16 + col][ks * 32 + quad * 8]));
+            f32x4_t acc[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], B[cb][ks], c, 0, 0, 0);
+                acc[cb] = c;
+            }
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int r = rb * 16 + rsub + jj;
-                if (!((rows >> r) & 1)) continue;
-                float *const p = out + (int64_t)r * w.ld + gb0;
+                const int r = rb * 16 + quad * 4 + jj;
+                const int lim = s_nc[r];
+                if constexpr (MODE == kSubMax) {
+                    float v[4];
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) p[cb * 16] = acc[rb][cb][jj];
+                    for (int cb = 0; cb < 4; ++cb)
+                        v[cb] = gb0 + cb * 16 + col < lim ? acc[cb][jj] : -INFINITY;
+                    const float m = row16_max4(v, col);
+                    // lanes 0, 4, 8, 12 of the row hold subgroups 0, 1, 2, 3
+                    if ((col & 3) == 0 && ((rows >> r) & 1))
+                        w.smax[(int64_t)(q0 + r) * n_sub + 4 * grp + (col >> 2)] = m;
+                } else {
+                    const float t = s_thr[r];
+                    uint64_t mk = 0;
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) {
+                        const bool pass = gb0 + cb * 16 + col < lim && acc[cb][jj] >= t;
+                        const uint64_t bal = __ballot(pass);
+                        mk |= ((bal >> (16 * quad)) & 0xffffull) << (16 * cb);
+                    }
+                    if (col == 0 && ((rows >> r) & 1))
+                        w.mask[(int64_t)(q0 + r) * w.n_grp + grp] = mk;
+                }
             }
+        }
     };
 
     const int sq0 = __shfl(my_seq, __builtin_ctzll(valid_rows));
@@ -149,23 +236,12 @@ __global__ __launch_bounds__(256) void k_prefill_scores(ScoreArgs a, PrefillWs w
         auto live_of = [&](int gt) {
             return grp_of(gt) < w.n_grp && grp_of(gt) * 64 < ncmax;
         };
-        auto sweep = [&](int gt, const bf16x8_t (&B)[4][4]) {
-            if (!live_of(gt)) return;
-            mfma_tile(A, B, acc);
-            store_rows(grp_of(gt) * 64, valid_rows);
-        };
-        // two key buffers: the next group's keys are in flight while the
-        // current group is on the matrix cores
-        bf16x8_t B0[4][4], B1[4][4];
-        load_key_tile(keys, grp_of(gt0) * 64, cap_blocks, live_of(gt0), B0);
-        for (int gt = gt0; gt < gt1; gt += 2) {
-            if (gt + 1 < gt1)
-                load_key_tile(keys, grp_of(gt + 1) * 64, cap_blocks, live_of(gt + 1), B1);
-            sweep(gt, B0);
-            if (gt + 1 >= gt1) break;
-            if (gt + 2 < gt1)
-                load_key_tile(keys, grp_of(gt + 2) * 64, cap_blocks, live_of(gt + 2), B0);
-            sweep(gt + 1, B1);
+        // one key buffer: the other wavefront on the SIMD covers the wait
+        for (int gt = gt0; gt < gt1; ++gt) {
+            if (!live_of(gt)) continue;
+            bf16x8_t B[4][4];
+            load_key_tile(keys, grp_of(gt) * 64, cap_blocks, true, B);
+            tile(B, grp_of(gt), valid_rows);
         }
         return;
     }
@@ -179,9 +255,9 @@ __global__ __launch_bounds__(256) void k_prefill_scores(ScoreArgs a, PrefillWs w
             const int ncmax = (int)wave_max_u32((my_seq == sq) ? (uint32_t)my_nc : 0u);
             done |= rows;
             if (gb0 >= ncmax) continue;
-            wave_tile_mfma(A, a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx, gb0, cap_blocks,
-                           true, acc);
-            store_rows(gb0, rows);
+            bf16x8_t B[4][4];
+            load_key_tile(a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx, gb0, cap_blocks, true, B);
+            tile(B, grp_of(gt), rows);
         }
     }
 }
@@ -230,43 +306,14 @@ struct PrefSelSmem {
     TopkSmem<kSelPNT> tk;
     float q[kDIdx];
     uint32_t bitmap[kPrefMaxBlocks / 32];
-    uint64_t band[kBandCap];  // band blocks, then their exact keys
-    uint32_t n_band;
+    uint64_t band[kBandCap];  // masked blocks, then their exact keys
 };
 
-__device__ __forceinline__ uint32_t approx_key(float v, int64_t b, int64_t limit) {
-    return (b < limit && finite_f32(v)) ? score_key(v) : 0u;
+__device__ __forceinline__ uint32_t approx_key(float v) {
+    return finite_f32(v) ? score_key(v) : 0u;
 }
 
-// Keys of the MFMA scores of one query's causal blocks, as (k, ~block):
-// blocks 4x .. 4x+3 for x = c * kSelPNT + tid, in registers for c <
-// kApproxVec and re-read from the row beyond.
-struct ApproxKeys {
-    uint32_t k[kApproxVec][4];
-    const float *row;
-    int64_t limit;
-    int n_vec;
-    template <typename F>
-    __device__ __forceinline__ void operator()(F &&fn) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int c = 0; c < kApproxVec; ++c) {
-            const uint32_t b0 = (uint32_t)(c * kSelPNT + tid) * 4u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fn(k[c][e], ~(b0 + e));
-        }
-        for (int x = kApproxVec * kSelPNT + tid; x < n_vec; x += kSelPNT) {
-            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(row + 4 * (int64_t)x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t b = 4 * (int64_t)x + e;
-                fn(approx_key(v[e], b, limit), ~(uint32_t)b);
-            }
-        }
-    }
-};
-
-// Exact keys of the band list (slot c holds entry c * kSelPNT + tid).
+// Exact keys of the masked blocks (slot c holds entry c * kSelPNT + tid).
 struct BandKeys {
     uint64_t k[kBandCap / kSelPNT];
     template <typename F>
@@ -294,13 +341,63 @@ __device__ __forceinline__ void mark(uint32_t *bm, uint32_t b) {
     atomicOr(&bm[b >> 5], 1u << (b & 31));
 }
 
-// grid (n_q), kSelPNT threads: the exact top-B of query i from its row of
-// MFMA scores plus exact rescoring of the band around the cut.
+__device__ __forceinline__ bool delta_in_range(float delta) {
+    return delta >= kDeltaMin && delta <= kDeltaMax;  // false for NaN
+}
+
+// grid (n_q), kTauNT threads: w.thr[i] = tau_i - 2 Delta_i rounded down,
+// tau_i the B-th largest subgroup maximum of query i; -inf when fewer than B
+// subgroups hold a causal block or Delta_i is out of range (every causal
+// block then passes the filter).
+constexpr int kTauPer = kPrefMaxBlocks / 16 / kTauNT;  // subgroup maxima per thread
+__global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w, int top_k) {
+    __shared__ TopkSmem<kTauNT> sm;
+    const int i = blockIdx.x, tid = threadIdx.x;
+    int s;
+    int64_t p;
+    bool valid;
+    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells, a.g.n_cells,
+                                    a.r, s, p, valid);
+    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
+    const int n_sub = (int)((limit + 15) / 16);
+    const int B = top_k / a.r;
+    const float delta = w.delta[i];
+    const float *row = w.smax + (int64_t)i * 4 * w.n_grp;
+    RegKeys32<kTauPer, kTauNT> keys;
+    keys.tid = tid;
+    uint32_t cnt = 0, mn = ~0u, mx = 0u;
+#pragma unroll
+    for (int c = 0; c < kTauPer; ++c) {
+        const int x = c * kTauNT + tid;
+        const uint32_t k = x < n_sub ? approx_key(row[x]) : 0u;
+        keys.k[c] = k;
+        if (k) {
+            ++cnt;
+            mn = min(mn, k);
+            mx = max(mx, k);
+        }
+    }
+    const uint32_t n_valid = block_sum_u32<kTauNT>(cnt, sm);
+    float thr = -INFINITY;
+    if (n_valid >= (uint32_t)B && delta_in_range(delta)) {
+        block_minmax_u32<kTauNT>(mn, mx, sm);
+        const float tau = key_value(kth_largest_u32<kTauNT>(keys, (uint32_t)B, mn, mx, sm));
+        const double t = (double)tau - 2.0 * (double)delta;
+        thr = (float)t;
+        if ((double)thr > t) thr = nextafterf(thr, -INFINITY);
+    }
+    if (tid == 0) w.thr[i] = thr;
+}
+
+// grid (n_q), kSelPNT threads: the exact top-B of query i among its masked
+// blocks, rescored in order T.
+constexpr int kMaskPer = kPrefMaxBlocks / 64 / kSelPNT;  // group masks per thread
 __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, PrefillWs w, int top_k,
                                                             int32_t *sel_blocks,
                                                             int32_t *sel_cells, int32_t *n_sel) {
     __shared__ PrefSelSmem sm;
     const int i = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = wave_id();
     int s;
     int64_t p;
     bool valid;
@@ -311,95 +408,55 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
     const int64_t cap_blocks = a.g.cap_cells / a.r;
     const uint16_t *keys = a.pooled_bf16 + (valid ? (int64_t)s * cap_blocks * kDIdx : 0);
     if (tid < kDIdx) sm.q[tid] = bf16_value(w.qr[(int64_t)i * kDIdx + tid]);
-    if (tid == 0) sm.n_band = 0;
     const int n_words = (int)((limit + 31) / 32);
     for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
-    const float delta = w.delta[i];
-    const bool safe = delta >= kDeltaMin && delta <= kDeltaMax;  // false for NaN
-    bool exact_all = limit > 0 && !safe;
+    bool exact_all = limit > 0 && !delta_in_range(w.delta[i]);
 
-    if (limit > 0 && safe) {
-        ApproxKeys ak;
-        ak.row = w.approx + (int64_t)i * w.ld;
-        ak.limit = limit;
-        ak.n_vec = (int)((limit + 3) / 4);
+    if (limit > 0 && !exact_all) {
+        // the masked blocks, listed by a prefix count over the masks
+        const int n_g = (int)((limit + 63) / 64);
+        uint64_t mk[kMaskPer];
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int c = 0; c < kApproxVec; ++c) {
-            const int x = c * kSelPNT + tid;
-            f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-            if (x < ak.n_vec) v = *reinterpret_cast<const f32x4_t *>(ak.row + 4 * (int64_t)x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ak.k[c][e] = approx_key(v[e], 4 * (int64_t)x + e, limit);
+        for (int c = 0; c < kMaskPer; ++c) {
+            const int g = tid * kMaskPer + c;
+            mk[c] = g < n_g ? w.mask[(int64_t)i * w.n_grp + g] : 0ull;
+            cnt += (uint32_t)__popcll(mk[c]);
         }
-        // with Delta in range no sum overflows, so every causal block has a
-        // finite score under both orders
-        uint32_t cnt = 0, mn = ~0u, mx = 0u;
-        ak([&](uint32_t k, uint32_t) {
-            if (!k) return;
-            ++cnt;
-            mn = min(mn, k);
-            mx = max(mx, k);
-        });
-        // low 18 bits: valid keys (<= 2^17); above: threads holding one
-        const uint32_t packed = block_sum_u32<kSelPNT>(cnt + (cnt ? 1u << 18 : 0u), sm.tk);
-        const uint32_t n_valid = packed & ((1u << 18) - 1u), n_holders = packed >> 18;
-        if (n_valid <= (uint32_t)B) {
-            ak([&](uint32_t k, uint32_t u) {
-                if (k) mark(sm.bitmap, ~u);
-            });
+        const uint32_t incl = wave_incl_scan_u32(cnt);
+        if (lane == kWave - 1) sm.tk.red[wave] = incl;
+        __syncthreads();
+        uint32_t before, total;
+        waves_prefix<kSelPNT / kWave>(sm.tk.red, wave, before, total);
+        if (total > (uint32_t)kBandCap) {
+            exact_all = true;
         } else {
-            // Every holder has a key >= its own largest, so at least
-            // n_holders keys are >= the smallest of those maxima: if that is
-            // B or more, the B-th largest lies above it, and the first
-            // radix round bins only the top of the distribution (not the
-            // bulk, whose keys would crowd a few bins).
-            uint32_t lo = cnt ? mx : ~0u, hi = mx;
-            block_minmax_u32<kSelPNT>(lo, hi, sm.tk);
-            if (n_holders < (uint32_t)B) {
-                uint32_t unused = 0u;
-                block_minmax_u32<kSelPNT>(mn, unused, sm.tk);
-                lo = mn;
-            }
-            const float a_B = key_value(kth_largest_u32<kSelPNT>(ak, (uint32_t)B, lo, hi, sm.tk));
-            const double tlo = (double)a_B - 2.0 * (double)delta;
-            const double thi = (double)a_B + 2.0 * (double)delta;
-            float flo = (float)tlo, fhi = (float)thi;
-            if ((double)flo > tlo) flo = nextafterf(flo, -INFINITY);
-            if ((double)fhi < thi) fhi = nextafterf(fhi, INFINITY);
-            const uint32_t k_lo = score_key(flo), k_hi = score_key(fhi);
-            uint32_t n_keep = 0;
-            ak([&](uint32_t k, uint32_t u) {
-                if (k > k_hi) {
-                    mark(sm.bitmap, ~u);
-                    ++n_keep;
-                } else if (k >= k_lo) {
-                    const uint32_t at = atomicAdd(&sm.n_band, 1u);
-                    if (at < (uint32_t)kBandCap) sm.band[at] = (uint64_t)(~u);
-                }
-            });
-            n_keep = block_sum_u32<kSelPNT>(n_keep, sm.tk);  // ends with a barrier
-            const uint32_t n_band = sm.n_band;
-            if (n_band > (uint32_t)kBandCap) {
-                exact_all = true;
-                for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
-                __syncthreads();
-            } else {
-                for (int x = tid; x < (int)n_band; x += kSelPNT) {
-                    const int64_t b = (int64_t)sm.band[x];
-                    sm.band[x] = block_key(exact_score(keys + b * kDIdx, sm.q), b);
-                }
-                __syncthreads();
-                BandKeys bk;
+            uint32_t at = before + incl - cnt;
 #pragma unroll
-                for (int c = 0; c < kBandCap / kSelPNT; ++c) {
-                    const int x = c * kSelPNT + tid;
-                    bk.k[c] = x < (int)n_band ? sm.band[x] : 0ull;
+            for (int c = 0; c < kMaskPer; ++c) {
+                uint64_t bits = mk[c];
+                const int64_t g0 = (int64_t)(tid * kMaskPer + c) * 64;
+                while (bits) {
+                    sm.band[at++] = (uint64_t)(g0 + __builtin_ctzll(bits));
+                    bits &= bits - 1;
                 }
-                const Thresh th = topk_threshold<kSelPNT>(bk, (uint32_t)B - n_keep, sm.tk);
-                bk([&](uint32_t k, uint32_t u) {
-                    if (th.keep(k, u)) mark(sm.bitmap, ~u);
-                });
             }
+            __syncthreads();
+            for (int x = tid; x < (int)total; x += kSelPNT) {
+                const int64_t b = (int64_t)sm.band[x];
+                sm.band[x] = block_key(exact_score(keys + b * kDIdx, sm.q), b);
+            }
+            __syncthreads();
+            BandKeys bk;
+#pragma unroll
+            for (int c = 0; c < kBandCap / kSelPNT; ++c) {
+                const int x = c * kSelPNT + tid;
+                bk.k[c] = x < (int)total ? sm.band[x] : 0ull;
+            }
+            const Thresh th = topk_threshold<kSelPNT>(bk, (uint32_t)B, sm.tk);
+            bk([&](uint32_t k, uint32_t u) {
+                if (th.keep(k, u)) mark(sm.bitmap, ~u);
+            });
         }
     }
     if (exact_all) {
@@ -427,14 +484,15 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
 static size_t prefill_layout(char *base, int n_q, int nb_max, PrefillWs *w) {
     PrefillWs d{};
     d.n_grp = (nb_max + 255) / 256 * 4;
-    d.ld = (int64_t)d.n_grp * 64;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
         off += (bytes + 255) / 256 * 256;
         return base ? base + at : nullptr;
     };
-    d.approx = reinterpret_cast<float *>(take((size_t)n_q * d.ld * 4));
+    d.smax = reinterpret_cast<float *>(take((size_t)n_q * d.n_grp * 4 * 4));
+    d.thr = reinterpret_cast<float *>(take((size_t)n_q * 4));
+    d.mask = reinterpret_cast<uint64_t *>(take((size_t)n_q * d.n_grp * 8));
     d.qr = reinterpret_cast<uint16_t *>(take((size_t)n_q * kDIdx * 2));
     d.delta = reinterpret_cast<float *>(take((size_t)n_q * 4));
     if (w) *w = d;
@@ -461,7 +519,12 @@ hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, v
     const int slab = max(1, (n_gt + n_slab - 1) / n_slab);
     const int grid = ((n_gt + slab - 1) / slab + 7) / 8 * 8 * qt;
     if (n_gt > 0)
-        hipLaunchKernelGGL(k_prefill_scores, dim3(grid), dim3(256), 0, st, a, w, n_gt, qt, slab);
+        hipLaunchKernelGGL(k_prefill_scores<kSubMax>, dim3(grid), dim3(256), 0, st, a, w, n_gt,
+                           qt, slab);
+    hipLaunchKernelGGL(k_prefill_tau, dim3(a.n_q), dim3(kTauNT), 0, st, a, w, top_k);
+    if (n_gt > 0)
+        hipLaunchKernelGGL(k_prefill_scores<kMask>, dim3(grid), dim3(256), 0, st, a, w, n_gt, qt,
+                           slab);
     hipLaunchKernelGGL(k_select_prefill, dim3(a.n_q), dim3(kSelPNT), 0, st, a, w, top_k,
                        sel_blocks, sel_cells, n_sel);
     return hipGetLastError();

@@ -314,10 +314,11 @@ hipError_t launch_decode_select(DecodeIdxArgs f, void *ws, hipStream_t st);
 // Prefill indexer (prefill.hip): MFMA scores, then per query the exact top-B
 // with exact rescoring of the blocks near the cut.
 struct PrefillWs {
-    float *approx;    // [n_q][ld] MFMA scores (entries of causal blocks only)
+    float *smax;      // [n_q][4*n_grp] largest MFMA score of each causal 16-block subgroup
+    float *thr;       // [n_q] filter threshold: tau - 2*Delta rounded down (-inf: all causal)
+    uint64_t *mask;   // [n_q][n_grp] blocks of each 64-block group with MFMA score >= thr
     uint16_t *qr;     // [n_q][128] roped queries, bf16
     float *delta;     // [n_q] bound on |MFMA score - T score|
-    int64_t ld;
     int32_t n_grp;
 };
 size_t prefill_ws_bytes(int n_q, int nb_max);
