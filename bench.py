@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode250k",
                     choices=["decode50k", "decode250k", "decode5x250k", "prefill"])
+    ap.add_argument("--kv", default="q8_0", choices=["q8_0", "f16"],
+                    help="K/V cache type of a decode workload (the workloads are defined "
+                         "with q8_0; f16 is the type the pages' first fix required)")
     ap.add_argument("--layers", type=int, default=N_LAYERS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU-oracle baseline sample (0 = skip)")
@@ -78,6 +81,8 @@ def setup(args, torch, dev):
     prefill = args.workload == "prefill"
     if not prefill and K + W > w.steps:
         w = synth.Workload(**{**w.__dict__, "steps": K + W})
+    if not prefill and args.kv == "f16":
+        w = synth.Workload(**{**w.__dict__, "kv_type": synth.KV_F16})
     t0 = time.time()
     kidx = synth.make_kidx(w)
     k = synth.make_kv(w, synth.T_K)
@@ -248,10 +253,11 @@ def run_decode(args, torch, dev):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (q8_0 KV)" if w.kv_type == synth.KV_Q8_0 else "f32",
-        "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded",
+        "dtype": {synth.KV_Q8_0: "f32 (q8_0 KV)", synth.KV_F16: "f32 (f16 KV)"}.get(w.kv_type, "f32"),
+        "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (%s), seeded"
+                % {synth.KV_Q8_0: "q8_0-packed", synth.KV_F16: "rounded to f16"}.get(w.kv_type, "f32"),
         "config": {
-            "workload": args.workload,
+            "workload": args.workload if args.kv == "q8_0" else f"{args.workload} (f16 KV)",
             "n_seq": w.n_seq, "n_kv_start": w.n_cells0 + w.n_new, "decode_steps": K,
             "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
             "compress_ratio": w.r, "top_k": w.top_k,
@@ -348,8 +354,9 @@ def run_prefill(args, torch, dev):
         "model_prefill_t_s": round(n_q / (ms_per_step * 1e-3), 1),
         "parts_us": {k: round(v, 2) for k, v in parts.items()},
         "roofline": {
-            "kernel": "qsa_score_select_prefill (update, rope, MFMA score matrix, radix cut "
-                      "and exact rescoring of the band at the cut), priced on the dense contraction alone",
+            "kernel": "qsa_score_select_prefill (update, rope, two MFMA passes: subgroup maxima, "
+                      "then masks at tau - 2 Delta; exact rescoring of the masked blocks), priced "
+                      "on the dense contraction once",
             "timing": "events around a graph of the K*L indexer calls alone",
             "bound": "mfma",
             "achieved": round(tflops, 2) if tflops else None,
