@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 /* Return codes.  0 is success; errors are negative. */
 #define QSA_OK 0
@@ -152,11 +152,22 @@ typedef struct qsa_dims {
     int32_t kidx_type;
 } qsa_dims;
 
-/* Sequence geometry shared by every call. */
+/* Sequence geometry shared by every call.
+ *   n_cells_dev      device int32 [n_seq]: cells (positions 0 .. n-1) present
+ *   cell_rows_dev    optional device int32 [n_seq][cap_cells]: the row of
+ *                    position p of sequence s in the per-cell arrays (kidx, K,
+ *                    V), which then hold n_rows rows shared by all sequences
+ *                    (a unified cache whose cells move under defrag and
+ *                    sequence edits).  NULL: position p of sequence s is row
+ *                    s*cap_cells + p.  Entries of present positions must lie in
+ *                    [0, n_rows); others are read as row 0 and not used.
+ *   n_rows           rows of the per-cell arrays when cell_rows_dev is given */
 typedef struct qsa_seqs {
     int32_t n_seq;
     int64_t cap_cells;
     const int32_t *n_cells_dev;
+    const int32_t *cell_rows_dev;
+    int64_t n_rows;
 } qsa_seqs;
 
 /* Library version (QSA_ABI_VERSION). */
@@ -171,8 +182,32 @@ const char *qsa_last_error(void);
 int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q,
                        int32_t nb_max, size_t *bytes);
 
+/* 0. Dirty blocks by structural compare  [ISSUE fix summary, lever2: a block
+ * is recomputed when its member cells changed, found by comparing them with
+ * the cells it was built from -- defrag, rollback and sequence edits need no
+ * invalidation hooks].
+ *
+ * A block's members are the rows (through seqs->cell_rows_dev when given) of
+ * its present positions block*r .. block*r+m-1, m = min(r, n_cells - block*r).
+ * snapshot_dev: int32 [n_seq][cap_cells/r][r+1], owned by the caller and
+ * zero-filled before the first call (every block empty), then kept by this
+ * call: per block the member count and rows last reported.  Writes
+ * dirty_dev[max_dirty][2]: the (seq, block) pairs of the changed non-empty
+ * blocks, then (-1, -1) padding -- the list qsa_update_pooled_keys takes with
+ * n_dirty = max_dirty, a fixed size a captured graph can keep -- and
+ * *n_found_dev, the number of changed non-empty blocks found.  If that
+ * exceeds max_dirty, the blocks the list has no room for keep their old
+ * snapshot and are found again by the next call.  Blocks that became empty
+ * are recorded, not listed.  Changes of a cell's contents in place are not
+ * structural and are not seen (the caller lists such blocks itself).  Order
+ * of the listed pairs is unspecified. */
+int qsa_detect_dirty_blocks(const qsa_dims *dims, const qsa_seqs *seqs, int32_t *snapshot_dev,
+                            int32_t *dirty_dev, int32_t max_dirty, uint32_t *n_found_dev,
+                            void *stream);
+
 /* 1. Pooled-key update  [ISSUE lever2; lever2b for the device-side block
- * membership, here the arithmetic members b*r .. b*r+r-1].
+ * membership: the members of block b are positions b*r .. b*r+r-1, read
+ * through the cell table when the caller gives one].
  *
  * For every entry (seq, block) of dirty_dev (int32 pairs, n_dirty of them;
  * callers pad the list to a power of two >= 4 with (-1, -1) so a captured

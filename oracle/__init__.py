@@ -22,6 +22,12 @@ What each function follows (pages cited by title and section):
   dequantised before use (discussion #30071, the two-problems paragraph).
 * ``select_dense_cells`` / ``attend_dense_masked`` / full re-pooling -- the
   pages' own slow forms, kept as cross-checks.
+* ``dirty_blocks`` -- which blocks to recompute: those whose member cells
+  changed since they were built, found by comparing the members with a
+  snapshot (issue #28734, fix summary, "lever2": the structural compare that
+  also catches defrag, rollback and sequence edits).  With a cell table the
+  method itself reads positions' contents; callers gather each sequence's
+  rows into a contiguous view for the other functions.
 
 Pins: every function here is checked against something other than itself in
 ``tests/test_oracle_pins.py`` (closed forms, library routines, brute force,
@@ -308,3 +314,33 @@ def step(q_idx, q, q_seq, q_pos, pooled, k_cache, v_cache, *, kv_type: int,
         cells.append(c)
         out[i] = attend(q[i], k_cache[s], v_cache[s], kv_type, c, n_head_kv, scale)
     return {"scores": scores, "blocks": blocks, "cells": cells, "out": out}
+
+
+def dirty_blocks(cell_rows, n_cells, snapshot, r: int):
+    """Structural dirty detection.
+
+    cell_rows: [n_seq][cap_cells] int, the row of each position of each
+    sequence; n_cells: [n_seq] present positions; snapshot: [n_seq][cap_blocks]
+    [r + 1] int, per block the member count and member rows it was last built
+    from.  A block's members are the rows of its present positions b*r ..
+    b*r + m - 1, m = min(r, n - b*r).  Returns (the (seq, block) pairs whose
+    non-empty member list changed, in (seq, block) order; the updated
+    snapshot, in which emptied blocks are recorded as empty)."""
+    rows = np.asarray(cell_rows)
+    snap = np.array(snapshot, copy=True)
+    n_seq, cap_blocks = snap.shape[0], snap.shape[1]
+    out = []
+    for s in range(n_seq):
+        n = int(n_cells[s])
+        for b in range(cap_blocks):
+            m = max(0, min(r, n - b * r))
+            members = [int(rows[s][b * r + j]) for j in range(m)]
+            old_m = int(snap[s][b][0])
+            if old_m == m and [int(x) for x in snap[s][b][1:1 + m]] == members:
+                continue
+            snap[s][b][0] = m
+            if m == 0:
+                continue
+            snap[s][b][1:1 + m] = members
+            out.append((s, b))
+    return out, snap

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_error_string():
-    assert qsa.version() == 2
+    assert qsa.version() == 3
     assert isinstance(qsa.load().qsa_last_error(), bytes)
 
 

@@ -605,3 +605,50 @@ def test_step_on_tiny_workload_runs():
                       nb_out=w.nb_max())
     assert res["blocks"][0].size == 64 and res["cells"][0].size == 256
     assert np.all(np.isfinite(res["out"]))
+
+
+# --------------------------------------------------------------------------
+# structural dirty detection
+# --------------------------------------------------------------------------
+
+def _contig_rows(n_seq, cap):
+    return np.arange(n_seq * cap, dtype=np.int64).reshape(n_seq, cap)
+
+
+def test_dirty_blocks_first_call_lists_every_present_block():
+    r, cap = 4, 64
+    rows = _contig_rows(2, cap)
+    snap = np.zeros((2, cap // r, r + 1), np.int64)
+    d, snap = oracle.dirty_blocks(rows, [10, 17], snap, r)
+    assert d == [(0, b) for b in range(3)] + [(1, b) for b in range(5)]
+    assert oracle.dirty_blocks(rows, [10, 17], snap, r)[0] == []  # nothing changed
+
+
+def test_dirty_blocks_append_and_rollback():
+    r, cap = 4, 64
+    rows = _contig_rows(1, cap)
+    _, snap = oracle.dirty_blocks(rows, [10], np.zeros((1, cap // r, r + 1), np.int64), r)
+    # one appended cell touches only the tail block (positions 8..10 -> 8..11)
+    d, snap = oracle.dirty_blocks(rows, [11], snap, r)
+    assert d == [(0, 2)]
+    # positions 11 and 12: block 2 fills up, block 3 starts
+    d, snap = oracle.dirty_blocks(rows, [13], snap, r)
+    assert d == [(0, 2), (0, 3)]
+    # rollback to 6 cells: block 1 loses members, blocks 2, 3 empty (recorded, not listed)
+    d, snap = oracle.dirty_blocks(rows, [6], snap, r)
+    assert d == [(0, 1)]
+    assert snap[0][2][0] == 0 and snap[0][3][0] == 0
+    # growing back over the emptied blocks lists them again
+    d, snap = oracle.dirty_blocks(rows, [13], snap, r)
+    assert d == [(0, 1), (0, 2), (0, 3)]
+
+
+def test_dirty_blocks_moved_cell_marks_its_block_only():
+    """Defrag: a cell moved to another row dirties the one block holding it."""
+    r, cap = 4, 64
+    rows = _contig_rows(2, cap).copy()
+    _, snap = oracle.dirty_blocks(rows, [40, 40], np.zeros((2, cap // r, r + 1), np.int64), r)
+    rows[1][21] = 1000  # position 21 of sequence 1 now lives in row 1000
+    rows[0][3], rows[0][2] = rows[0][2], rows[0][3]  # two cells of block 0 swap rows
+    d, _ = oracle.dirty_blocks(rows, [40, 40], snap, r)
+    assert d == [(0, 0), (1, 5)]

@@ -66,10 +66,24 @@ int check_seqs(const qsa_dims *d, const qsa_seqs *s) {
         return fail(QSA_ENOTSUP, "cap_cells above 2^31-1");
     if (!s->n_cells_dev || !aligned(s->n_cells_dev, 4))
         return fail(QSA_EINVAL, "n_cells_dev NULL or misaligned");
+    if (s->cell_rows_dev) {
+        if (!aligned(s->cell_rows_dev, 4)) return fail(QSA_EINVAL, "cell_rows_dev misaligned");
+        if (s->n_rows <= 0 || s->n_rows > ((int64_t)1 << 31) - 1)
+            return fail(QSA_EINVAL, "n_rows %lld outside 1 .. 2^31-1 with a cell table",
+                        (long long)s->n_rows);
+    }
     return QSA_OK;
 }
 
-qsa::SeqGeom geom(const qsa_seqs *s) { return {s->n_seq, s->cap_cells, s->n_cells_dev}; }
+qsa::SeqGeom geom(const qsa_seqs *s) {
+    return {s->n_seq, s->cap_cells, s->n_cells_dev, s->cell_rows_dev,
+            s->cell_rows_dev ? s->n_rows : 0};
+}
+
+// Rows of the per-cell arrays (kidx, K, V).
+int64_t cell_rows(const qsa_seqs *s) {
+    return s->cell_rows_dev ? s->n_rows : (int64_t)s->n_seq * s->cap_cells;
+}
 
 size_t kidx_align(const qsa_dims *d) { return d->kidx_type == QSA_KIDX_BF16 ? 2 : 4; }
 qsa::KidxRef kidx_ref(const qsa_dims *d, const void *kidx) {
@@ -168,6 +182,22 @@ int qsa_update_pooled_keys(const qsa_dims *dims, const qsa_seqs *seqs, const voi
                       pooled_dev, pooled_bf16_dev, dims->r, dims->rms_eps,
                       dims->idx_norm_w_dev, rope_table(dims->rope_theta)};
     return launched(qsa::launch_update_pooled(a, (hipStream_t)stream), "update_pooled_keys");
+}
+
+int qsa_detect_dirty_blocks(const qsa_dims *dims, const qsa_seqs *seqs, int32_t *snapshot_dev,
+                            int32_t *dirty_dev, int32_t max_dirty, uint32_t *n_found_dev,
+                            void *stream) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (rc) return rc;
+    if (max_dirty < 0) return fail(QSA_EINVAL, "max_dirty negative");
+    if (!snapshot_dev || !aligned(snapshot_dev, 4))
+        return fail(QSA_EINVAL, "snapshot_dev NULL or misaligned");
+    if ((max_dirty > 0 && (!dirty_dev || !aligned(dirty_dev, 4))) || !n_found_dev ||
+        !aligned(n_found_dev, 4))
+        return fail(QSA_EINVAL, "dirty_dev/n_found_dev NULL or misaligned");
+    qsa::DirtyArgs a{geom(seqs), dims->r, snapshot_dev, dirty_dev, max_dirty, n_found_dev};
+    return launched(qsa::launch_detect_dirty(a, (hipStream_t)stream), "detect_dirty_blocks");
 }
 
 int qsa_score_blocks(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_idx_dev,
@@ -426,7 +456,7 @@ static int attn_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_
         return fail(QSA_EINVAL, "K/V cache NULL or not 16-byte aligned");
     if (!sel_cells_dev || !n_sel_dev || !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
         return fail(QSA_EINVAL, "selection NULL or misaligned");
-    if ((int64_t)seqs->n_seq * seqs->cap_cells * dims->n_head_kv >= ((int64_t)1 << 31))
+    if (cell_rows(seqs) * dims->n_head_kv >= ((int64_t)1 << 31))
         return fail(QSA_EINVAL, "K/V cache of 2^31 rows or more");
     const int ld_cells = dims->top_k + dims->r - 1;
     const size_t need = prefill ? qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells)

@@ -172,7 +172,6 @@ __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, i
     }
 
     if (c_begin < c_end) {
-        const int64_t row0 = (int64_t)s * a.g.cap_cells;
         for (int c0 = c_begin; c0 < c_end; c0 += kChunk) {
             const int c1 = min(c_end, c0 + kChunk);
             if (c0 != c_begin) {
@@ -190,7 +189,7 @@ __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, i
 #pragma unroll
             for (int u = 0; u < kCPG; ++u) {
                 const bool in_cap = cell[u] >= 0 && cell[u] < a.g.cap_cells;
-                const int64_t row = (row0 + (in_cap ? cell[u] : 0)) * a.n_head_kv + g;
+                const int64_t row = cell_row(a.g, s, in_cap ? cell[u] : 0) * a.n_head_kv + g;
                 rk[u] = load_raw<KVT>(a.k, row, j);
                 rv[u] = load_raw<KVT>(a.v, row, j);
             }

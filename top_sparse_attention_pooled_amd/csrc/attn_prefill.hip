@@ -20,8 +20,8 @@
 // q8_0 rows reach the wavefront as whole 16-byte pieces: the chunk's 64 rows
 // (K and V, 272 bytes each) are 17 coalesced loads per lane, prefetched one
 // chunk ahead in registers and written to an LDS stage, from which the
-// operands are read.  f32 and f16 rows are gathered per lane straight into
-// the operand layout.
+// operands are read.  f32 and f16 rows, and q8_0 rows reached through a cell
+// table, are gathered per lane straight into the operand layout.
 // Operands are rounded to fp16 (Q * scale, P, V; f32 K); sums and the
 // softmax state are fp32.
 #include <type_traits>
@@ -145,7 +145,7 @@ struct QueryCtx {
     int n;              // cells in the list
     int64_t n_present;  // cells of the sequence
     const int32_t *cells;
-    int64_t row0;  // first cell row of the sequence
+    int64_t row0;  // s * cap_cells: position p of the sequence is entry row0 + p
 };
 
 __device__ __forceinline__ QueryCtx query_ctx(const AttnArgs &a, int i) {
@@ -342,9 +342,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         return cc < qc.n ? v : -1;
     };
     // Row of a cell; a cell that is not present reads the sequence's cell 0.
-    // (The row index fits 32 bits: the host rejects caches of 2^31 rows.)
     auto row_of = [&](int cell) {
         const bool ok = cell >= 0 && cell < qc.n_present;
+        // (the row index fits 32 bits: the host rejects caches of 2^31 rows)
         return (uint32_t)((qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g);
     };
     // Loads K0 .. K1-1 of the chunk whose slot rows the lanes hold.
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     merge_store(a, i, g, hpk, sw, o, m_run, l_run);
 }
 
-// ---- f32 and f16 rows, gathered per lane ----
+// ---- rows gathered per lane: f32 and f16 caches, and q8_0 through a cell table ----
 
 // Same grid as k_attn_prefill_q8.
 template <int KVT>
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_rows(AttnArgs a) {
             const int cc = c0 + 16 * t + col;
             const int cell = cc < c1 ? cell_at(cc) : -1;
             const bool ok = cell >= 0 && cell < qc.n_present;
-            const int64_t row = (qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
+            const int64_t row = cell_row_at(a.g, qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_rows(AttnArgs a) {
             const int cc = c0 + 2 * col + u;
             const int cell = cc < c1 ? cell_at(cc) : -1;
             const bool ok = cell >= 0 && cell < qc.n_present;
-            const int64_t row = (qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
+            const int64_t row = cell_row_at(a.g, qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int j = q * 4 + quad;
@@ -561,6 +561,8 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(k_attn_prefill_rows<QSA_KV_F32>, grid, dim3(256), 0, st, a);
     else if (a.kv_type == QSA_KV_F16)
         hipLaunchKernelGGL(k_attn_prefill_rows<QSA_KV_F16>, grid, dim3(256), 0, st, a);
+    else if (a.g.rows)  // a cell table: rows gathered per lane through it
+        hipLaunchKernelGGL(k_attn_prefill_rows<QSA_KV_Q8_0>, grid, dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL(k_attn_prefill_q8, grid, dim3(256), 0, st, a);
     return hipGetLastError();

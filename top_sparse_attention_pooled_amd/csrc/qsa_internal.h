@@ -121,6 +121,26 @@ __device__ __forceinline__ void rope_query_pair(const float *q, int t, int64_t p
 // split-half RoPE pair).  The first level of T pairs dims (t, t+64) in-lane;
 // the rest is an xor butterfly whose lane-0 value is exactly the
 // stride-halving tree (xor h pairs lane t < h with t + h).
+struct SeqGeom {
+    int32_t n_seq;
+    int64_t cap_cells;
+    const int32_t *n_cells;
+    const int32_t *rows;  // optional cell table [n_seq][cap_cells]
+    int64_t n_rows;
+};
+
+// Row of position p of sequence s in the per-cell arrays (kidx, K, V): the
+// cell table's entry at = s*cap_cells + p (out-of-range entries read row 0),
+// else at itself.
+__device__ __forceinline__ int64_t cell_row_at(const SeqGeom &g, int64_t at) {
+    if (!g.rows) return at;
+    const int32_t r = g.rows[at];
+    return (r >= 0 && r < g.n_rows) ? r : 0;
+}
+__device__ __forceinline__ int64_t cell_row(const SeqGeom &g, int s, int64_t p) {
+    return cell_row_at(g, (int64_t)s * g.cap_cells + p);
+}
+
 // Per-cell indexer keys: float32, or bfloat16 bits widened exactly to fp32.
 struct KidxRef {
     const void *p;
@@ -135,21 +155,22 @@ __device__ __forceinline__ float kidx_value(const void *p, int64_t i) {
         return static_cast<const float *>(p)[i];
 }
 
-__device__ __forceinline__ void pooled_key_lane(KidxRef kidx, int64_t cap_cells, int s,
+__device__ __forceinline__ void pooled_key_lane(KidxRef kidx, const SeqGeom &g, int s,
                                                 int64_t b, int64_t n, int r, float eps,
                                                 const float *gamma, const RopeTable &rt,
                                                 int lane, float &out_lo, float &out_hi) {
     const int64_t first = b * r;
     const int m = (int)((n - first) < r ? (n - first) : r);
-    const int64_t x = ((int64_t)s * cap_cells + first) * kDIdx;
     float lo, hi;
     auto cell_sum = [&](auto bf16) {
         constexpr bool BF = decltype(bf16)::value;
-        lo = kidx_value<BF>(kidx.p, x + lane);
-        hi = kidx_value<BF>(kidx.p, x + lane + 64);
+        const int64_t x0 = cell_row(g, s, first) * kDIdx;
+        lo = kidx_value<BF>(kidx.p, x0 + lane);
+        hi = kidx_value<BF>(kidx.p, x0 + lane + 64);
         for (int j = 1; j < m; ++j) {
-            lo = lo + kidx_value<BF>(kidx.p, x + j * kDIdx + lane);
-            hi = hi + kidx_value<BF>(kidx.p, x + j * kDIdx + lane + 64);
+            const int64_t x = cell_row(g, s, first + j) * kDIdx;
+            lo = lo + kidx_value<BF>(kidx.p, x + lane);
+            hi = hi + kidx_value<BF>(kidx.p, x + lane + 64);
         }
     };
     if (kidx.bf16)
@@ -204,12 +225,6 @@ __device__ __forceinline__ void store_pooled_lane(float *pooled, uint16_t *poole
 // ---------------------------------------------------------------------------
 // Launch interfaces (host side, one per kernel family)
 // ---------------------------------------------------------------------------
-
-struct SeqGeom {
-    int32_t n_seq;
-    int64_t cap_cells;
-    const int32_t *n_cells;
-};
 
 struct UpdateArgs {
     SeqGeom g;
@@ -300,6 +315,17 @@ struct AttnArgs {
 };
 
 hipError_t launch_update_pooled(const UpdateArgs &a, hipStream_t st);
+
+// Structural dirty detection (pooled.hip).
+struct DirtyArgs {
+    SeqGeom g;
+    int32_t r;
+    int32_t *snap;      // [n_seq][cap_blocks][r + 1]: member count, then member rows
+    int32_t *dirty;     // [max_dirty][2] (seq, block), (-1, -1) padded
+    int32_t max_dirty;
+    uint32_t *n_found;  // changed blocks found (may exceed max_dirty)
+};
+hipError_t launch_detect_dirty(const DirtyArgs &a, hipStream_t st);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_score_bf16_ws(const ScoreArgs &a, uint16_t *qr_bf16, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);

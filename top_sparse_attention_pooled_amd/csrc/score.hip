@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
         if (n > a.g.cap_cells) n = a.g.cap_cells;
         if ((int64_t)b * a.r >= n) return;
         float lo, hi;
-        pooled_key_lane(f.kidx, a.g.cap_cells, s, b, n, a.r, f.eps, f.gamma, a.rope, lane, lo, hi);
+        pooled_key_lane(f.kidx, a.g, s, b, n, a.r, f.eps, f.gamma, a.rope, lane, lo, hi);
         store_pooled_lane(f.pooled_w, f.pooled_bf16, cap_blocks, s, b, lane, lo, hi);
         return;
     }
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
             }
             if (wave == 0) {
                 float lo, hi;
-                pooled_key_lane(f.kidx, a.g.cap_cells, s, db, n, a.r, f.eps, f.gamma, a.rope,
+                pooled_key_lane(f.kidx, a.g, s, db, n, a.r, f.eps, f.gamma, a.rope,
                                 lane, lo, hi);
                 float *pf = reinterpret_cast<float *>(patch);
                 pf[lane] = lo;

@@ -27,7 +27,7 @@ EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_update_pooled_keys", "qsa_score_blocks", "qsa_select_topk_blocks",
            "qsa_score_select_decode", "qsa_decode_score_candidates",
            "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
-           "qsa_decode_select_attend", "qsa_score_select_prefill")
+           "qsa_decode_select_attend", "qsa_score_select_prefill", "qsa_detect_dirty_blocks")
 
 
 class QsaError(RuntimeError):
@@ -47,7 +47,8 @@ class _Dims(ctypes.Structure):
 
 class _Seqs(ctypes.Structure):
     _fields_ = [("n_seq", ctypes.c_int32), ("cap_cells", ctypes.c_int64),
-                ("n_cells_dev", ctypes.c_void_p)]
+                ("n_cells_dev", ctypes.c_void_p), ("cell_rows_dev", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int64)]
 
 
 _lib = None
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_workspace_size.argtypes = [D, i32, i32, i32, ctypes.POINTER(sz)]
     lib.qsa_update_pooled_keys.restype = ctypes.c_int
     lib.qsa_update_pooled_keys.argtypes = [D, S, vp, vp, i32, vp, vp, vp]
+    lib.qsa_detect_dirty_blocks.restype = ctypes.c_int
+    lib.qsa_detect_dirty_blocks.argtypes = [D, S, vp, vp, i32, vp, vp]
     lib.qsa_score_blocks.restype = ctypes.c_int
     lib.qsa_score_blocks.argtypes = [D, S, vp, vp, vp, i32, vp, vp, i32, vp, i64, i32, vp, sz, vp]
     lib.qsa_select_topk_blocks.restype = ctypes.c_int
@@ -137,9 +140,12 @@ class Seqs:
     n_seq: int
     cap_cells: int
     n_cells: object  # device int32 tensor [n_seq]
+    cell_rows: Optional[object] = None  # device int32 [n_seq][cap_cells] or None
+    n_rows: int = 0
 
     def c(self) -> _Seqs:
-        return _Seqs(self.n_seq, self.cap_cells, _ptr(self.n_cells))
+        return _Seqs(self.n_seq, self.cap_cells, _ptr(self.n_cells), _ptr(self.cell_rows),
+                     self.n_rows)
 
 
 def _ptr(t) -> Optional[int]:
@@ -170,6 +176,13 @@ def workspace_size(dims: Dims, op: int, n_q: int, nb_max: int = 0) -> int:
     out = ctypes.c_size_t(0)
     _rc(load().qsa_workspace_size(ctypes.byref(dims.c()), op, n_q, nb_max, ctypes.byref(out)))
     return out.value
+
+
+def detect_dirty_blocks(dims: Dims, seqs: Seqs, snapshot, dirty, max_dirty: int, n_found,
+                        stream=None) -> None:
+    _rc(load().qsa_detect_dirty_blocks(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                       _ptr(snapshot), _ptr(dirty), max_dirty, _ptr(n_found),
+                                       _stream(stream)))
 
 
 def update_pooled_keys(dims: Dims, seqs: Seqs, kidx, dirty, n_dirty: int, pooled,
