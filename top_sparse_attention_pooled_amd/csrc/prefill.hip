@@ -25,6 +25,8 @@
 //      more blocks pass than the LDS list holds, or Delta is outside the
 //      range where no partial sum can overflow or underflow, every causal
 //      block is rescored instead.
+#include <type_traits>
+
 #include "mfma_tile.h"
 #include "topk_engine.h"
 #include "wave_ops.h"
@@ -182,7 +184,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int64_t n_sub = 4 * (int64_t)w.n_grp;
     // One 16-row band rb of the 64 x 64 tile on the matrix cores, then its
     // epilogue (the band's accumulators are all that is live).
-    auto tile = [&](const bf16x8_t (&B)[4][4], int64_t grp, uint64_t rows) {
+    // FULL: every block of the group is causal for every stored row, so no
+    // per-element limit test
+    auto tile_as = [&](auto full, const bf16x8_t (&B)[4][4], int64_t grp, uint64_t rows) {
+        constexpr bool FULL = decltype(full)::value;
         const int64_t gb0 = grp * 64;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
@@ -203,12 +208,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int r = rb * 16 + quad * 4 + jj;
-                const int lim = s_nc[r];
+                const int lim = FULL ? 0 : s_nc[r];
                 if constexpr (MODE == kSubMax) {
                     float v[4];
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb)
-                        v[cb] = gb0 + cb * 16 + col < lim ? acc[cb][jj] : -INFINITY;
+                        v[cb] = (FULL || gb0 + cb * 16 + col < lim) ? acc[cb][jj] : -INFINITY;
                     const float m = row16_max4(v, col);
                     // lanes 0, 4, 8, 12 of the row hold subgroups 0, 1, 2, 3
                     if ((col & 3) == 0 && ((rows >> r) & 1))
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     uint64_t mk = 0;
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb) {
-                        const bool pass = gb0 + cb * 16 + col < lim && acc[cb][jj] >= t;
+                        const bool pass = (FULL || gb0 + cb * 16 + col < lim) && acc[cb][jj] >= t;
                         const uint64_t bal = __ballot(pass);
                         mk |= ((bal >> (16 * quad)) & 0xffffull) << (16 * cb);
                     }
@@ -227,6 +232,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 }
             }
         }
+    };
+    auto tile = [&](const bf16x8_t (&B)[4][4], int64_t grp, uint64_t rows) {
+        // smallest causal limit of the stored rows (lane r holds row r's)
+        const uint32_t ncmin = wave_min_u32(((rows >> lane) & 1) ? (uint32_t)my_nc : ~0u);
+        if ((uint64_t)grp * 64 + 64 <= ncmin)
+            tile_as(std::true_type{}, B, grp, rows);
+        else
+            tile_as(std::false_type{}, B, grp, rows);
     };
 
     const int sq0 = __shfl(my_seq, __builtin_ctzll(valid_rows));
