@@ -87,6 +87,16 @@ def run_case(name, w, n_cells, q_idx, kidx):
     # same cells, same arithmetic: the fused attention output is identical
     assert np.array_equal(att.out.cpu().numpy().view(np.uint32),
                           sep.out.cpu().numpy().view(np.uint32))
+    # the call only reads the candidate workspace: a second call over the
+    # same candidates (no scoring call between) gives the same output
+    att.out.fill_(float("nan"))
+    qsa.decode_select_attend(layer.dims, layer.seqs(), q_seq, q_pos, n_q, nb_max, att.scores,
+                             att.ld, att.sel_blocks, att.sel_cells, att.n_sel, att.ws_fused,
+                             att.ws_fused_bytes, q, layer.k, layer.v, att.out, att.ws_attn,
+                             att.ws_attn_bytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(att.out.cpu().numpy().view(np.uint32),
+                          sep.out.cpu().numpy().view(np.uint32))
     return r_scores
 
 
