@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode250k",
-                    choices=["decode50k", "decode250k", "decode5x250k", "prefill"])
+                    choices=["decode50k", "decode250k", "decode5x250k", "prefill", "prefill_ar1"])
     ap.add_argument("--kv", default="q8_0", choices=["q8_0", "f16"],
                     help="K/V cache type of a decode workload (the workloads are defined "
                          "with q8_0; f16 is the type the pages' first fix required)")
@@ -78,7 +78,7 @@ def setup(args, torch, dev):
     from top_sparse_attention_pooled_amd import runtime, synth
     w = synth.WORKLOADS[args.workload]
     K, W, L = args.steps, args.warmup, args.layers
-    prefill = args.workload == "prefill"
+    prefill = args.workload.startswith("prefill")
     if not prefill and K + W > w.steps:
         w = synth.Workload(**{**w.__dict__, "steps": K + W})
     if not prefill and args.kv == "f16":
@@ -189,7 +189,7 @@ def main():
     qsa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload == "prefill":
+    if args.workload.startswith("prefill"):
         result = run_prefill(args, torch, dev)
     else:
         result = run_decode(args, torch, dev)
@@ -342,9 +342,11 @@ def run_prefill(args, torch, dev):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 indexer (fp32 accumulate), f32 attention over q8_0 KV",
-        "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded",
+        "data": ("synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded"
+                 + ("; indexer queries AR(1) along the tokens, rho %g" % w.extra["qidx_ar1"]
+                    if w.extra.get("qidx_ar1") else "")),
         "config": {
-            "workload": "prefill", "n_seq": 1, "n_kv_start": w.n_cells0, "ubatch": n_q,
+            "workload": args.workload, "n_seq": 1, "n_kv_start": w.n_cells0, "ubatch": n_q,
             "dirty_blocks": int(np.sum(host["dl_all"][0][:, 0] >= 0)),
             "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
             "compress_ratio": w.r, "top_k": w.top_k, "layers_per_step": L,

@@ -119,11 +119,13 @@ def test_prefill_selection_all_tied_rescoring_every_block():
     assert np.array_equal(gb[0], np.arange(512))  # the lowest blocks win every tie
 
 
-def test_prefill_selection_ubatch_at_depth():
+@pytest.mark.parametrize("name", ["prefill", "prefill_ar1"])
+def test_prefill_selection_ubatch_at_depth(name):
     """The 512-token ubatch at depth 198,628 (128 dirty blocks), oracle-checked
-    on queries spread over the ubatch."""
-    w = synth.WORKLOADS["prefill"]
-    say("prefill select: 512-token ubatch at 198,628 (oracle on 24 queries)")
+    on queries spread over the ubatch; also with AR(1) indexer queries (rho
+    0.9), whose neighbouring tokens select overlapping blocks."""
+    w = synth.WORKLOADS[name]
+    say(f"{name} select: 512-token ubatch at 198,628 (oracle on 24 queries)")
     kidx = synth.make_kidx(w)
     layer = runtime.Layer(w, DEV, kidx=kidx, k=np.zeros((1, 1, 1, 1), np.uint8),
                           v=np.zeros((1, 1, 1, 1), np.uint8))

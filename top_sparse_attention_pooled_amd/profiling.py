@@ -15,6 +15,13 @@ still hash the same (a changed kernel makes the counters stale).
 
 writes a table of per-kernel device durations (min, median, p90, mean) from
 a rocprofv3 --kernel-trace --stats run, followed by its kernel_stats.csv.
+
+    python -m top_sparse_attention_pooled_amd.profiling counters \
+        --pmc DIR [DIR ...] --match k_prefill --title "..." --command "..." \
+        --out profiles/NAME.md
+
+writes the per-dispatch mean of every counter collected in one or more
+rocprofv3 --pmc runs, one row per kernel whose name contains --match.
 """
 from __future__ import annotations
 
@@ -163,6 +170,36 @@ def kernels_md(trace_dir: str, title: str, command: str, notes: str = "") -> str
     return "\n".join(lines)
 
 
+def counters_md(dirs: List[str], match: str, title: str, command: str, notes: str = "") -> str:
+    """Markdown: per kernel (name containing match), the mean of each counter
+    per dispatch over the --pmc runs in dirs."""
+    per: Dict[str, Dict[str, List[float]]] = {}
+    for d in dirs:
+        for r in _rows(d, "counter_collection.csv"):
+            name = r["Kernel_Name"]
+            if match not in name:
+                continue
+            short = name.replace("qsa::(anonymous namespace)::", "").replace("void ", "")
+            short = short.split("(")[0]
+            per.setdefault(short, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    lines = [f"# {title}", ""]
+    if command:
+        lines += ["Commands:", "", "```", command.strip(), "```", ""]
+    lines += ["Mean per dispatch:", "", "| kernel | dispatches | " + " | ".join(names) + " |",
+              "|---|---|" + "---|" * len(names)]
+    for k in sorted(per):
+        v = per[k]
+        n = max(len(x) for x in v.values())
+        cells = [f"{statistics.mean(v[c]):.4g}" if c in v else "" for c in names]
+        lines.append(f"| {k} | {n} | " + " | ".join(cells) + " |")
+    lines.append("")
+    if notes:
+        lines += [notes.strip(), ""]
+    return "\n".join(lines)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -172,6 +209,13 @@ def main() -> None:
     k.add_argument("--command", default="")
     k.add_argument("--notes", default="")
     k.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--match", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", default="")
+    c.add_argument("--notes", default="")
+    c.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -185,6 +229,10 @@ def main() -> None:
     if a.cmd == "kernels":
         with open(a.out, "w") as f:
             f.write(kernels_md(a.trace, a.title, a.command, a.notes))
+        return
+    if a.cmd == "counters":
+        with open(a.out, "w") as f:
+            f.write(counters_md(a.pmc, a.match, a.title, a.command, a.notes))
         return
     res = traffic(a.fetch, a.write, a.kernel, a.copy_mib)
     res["workload"] = a.workload

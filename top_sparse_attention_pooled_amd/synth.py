@@ -127,7 +127,23 @@ WORKLOADS = {
                              note="5 independent seqs at n_kv=248,278, one token each"),
     "prefill": Workload("prefill", 4, 1, 198628, n_new=512, steps=1,
                         note="512-token ubatch appended at depth 198,628"),
+    "prefill_ar1": Workload("prefill_ar1", 4, 1, 198628, n_new=512, steps=1,
+                            note="the prefill ubatch with AR(1) indexer queries (rho 0.9) "
+                                 "along the tokens",
+                            extra={"qidx_ar1": 0.9}),
 }
+
+
+def ar1_rows(x: np.ndarray, rho: float) -> np.ndarray:
+    """Rows of i.i.d. N(0,1) draws turned into an AR(1) series along axis 0
+    with unit variance: y_0 = x_0, y_t = rho y_{t-1} + sqrt(1 - rho^2) x_t
+    (float64 recursion, rounded to float32)."""
+    y = np.empty(x.shape, np.float64)
+    c = np.sqrt(1.0 - rho * rho)
+    y[0] = x[0]
+    for t in range(1, x.shape[0]):
+        y[t] = rho * y[t - 1] + c * x[t]
+    return y.astype(np.float32)
 
 
 def make_kidx(w: Workload) -> np.ndarray:
@@ -188,7 +204,9 @@ def make_queries(w: Workload, step: int):
     each new cell is one query at its own position."""
     q_idx, q, seqs, pos = [], [], [], []
     for s in range(w.n_seq):
-        q_idx.append(normal((w.n_new, w.d), w.cfg_id, s, T_QIDX, step))
+        qi = normal((w.n_new, w.d), w.cfg_id, s, T_QIDX, step)
+        rho = w.extra.get("qidx_ar1")
+        q_idx.append(ar1_rows(qi, rho) if rho else qi)
         q.append(normal((w.n_new, w.H, w.D), w.cfg_id, s, T_Q, step))
         base = w.n_cells0 + step * w.n_new
         seqs.append(np.full(w.n_new, s, dtype=np.int32))
