@@ -278,6 +278,43 @@ def test_attention_matches_oracle_on_shared_cells(kv_type, H, Hk):
         assert worst < (ATTN_TOL if prefill else 1e-4)
 
 
+def test_decode_attention_on_the_longest_cell_lists():
+    """The longest lists the ABI accepts: top_k/r = 4096 blocks of r = 16 cells
+    (65,551 list positions, 2,049 runs of 32 cells, more runs than threads in
+    a merge workgroup).  Sets of 40,000 and 33,001 cells (more than 32,768)
+    and a one-cell set, q8_0 rows, against the oracle."""
+    H, Hk = 4, 1
+    w = synth.Workload("long", 75, 1, 40000, n_new=1, steps=1, H=H, Hk=Hk, r=16,
+                       top_k=65536, kv_type=synth.KV_Q8_0)
+    say(f"attention on long lists: ld_cells={w.ld_cells}")
+    layer = runtime.Layer(w, DEV, kidx=np.zeros((w.n_seq, w.cap_cells, w.d), np.float32))
+    n_cells = np.array([40000], np.int32)
+    layer.set_n_cells(n_cells)
+    rng = np.random.default_rng(75)
+    sizes = [40000, 33001, 1]
+    n_q, ld = len(sizes), w.ld_cells
+    cells = np.full((n_q, ld), -1, np.int32)
+    for i, n in enumerate(sizes):
+        cells[i, :n] = np.sort(rng.choice(40000, size=n, replace=False))
+    q_seq = np.zeros(n_q, np.int32)
+    q = synth.normal((n_q, H, w.D), 75, 0, synth.T_Q)
+    bufs = runtime.StepBuffers(layer.dims, n_q, 64, DEV)
+    qsa.sparse_attn_decode(layer.dims, layer.seqs(), torch.from_numpy(q).to(DEV),
+                           torch.from_numpy(q_seq).to(DEV), n_q, layer.k, layer.v,
+                           torch.from_numpy(cells).to(DEV),
+                           torch.tensor(sizes, dtype=torch.int32, device=DEV),
+                           bufs.out, bufs.ws_attn, bufs.ws_attn_bytes)
+    torch.cuda.synchronize()
+    g = bufs.out.cpu().numpy()
+    k_np, v_np = layer.k.cpu().numpy(), layer.v.cpu().numpy()
+    worst = 0.0
+    for i, n in enumerate(sizes):
+        r = oracle.attend(q[i], k_np[0], v_np[0], w.kv_type, cells[i, :n], Hk)
+        worst = max(worst, float(np.abs(g[i] - r).max()))
+    say(f"  worst max-abs error {worst:.2e}")
+    assert worst < 1e-4
+
+
 # --------------------------------------------------------------------------
 # whole steps on the benchmark workloads
 # --------------------------------------------------------------------------

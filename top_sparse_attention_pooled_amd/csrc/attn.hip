@@ -443,95 +443,91 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
                           partial_of<G>(a, i, hg, run, n_runs), false, active);
 }
 
-constexpr int kCombNT = 1024;
-constexpr int kCombGroups = kCombNT / 128;  // run groups x 128 dim pairs
+constexpr int kCombNT = 256;
+constexpr int kCombWaves = kCombNT / kWave;
+constexpr int kCombSlices = kHeadDim / kWave;  // workgroups per head: 64 output dims each
+constexpr int kCombPre = 17;                    // runs per wavefront loaded up front
+// longest cell list: top_k/r <= 4096 blocks of r <= 16 cells plus r-1 tail
+// cells, 65,551 positions in runs of 32
+constexpr int kCombMaxRuns = (4096 * 16 + 15 + kChunk - 1) / kChunk;
+static_assert(kCombWaves == 4, "the merge adds its wavefronts' values two by two");
 
-// grid (n_head, n_q).  Merges the runs' partial states of one head: thread
-// (rg, dp) sums runs rg, rg+8, ... for dims 2dp, 2dp+1; the 8 partial sums
-// are then added in a fixed order.  The first kPre runs of each thread are
-// loaded together with the (m, l) pairs, before the weights are known (every
-// run's partial is written, zeros for a run that saw no cell), so a decode
-// set of up to 8*kPre runs costs one memory round trip.  n_runs <= 1024.
+// grid (n_head * 4, n_q).  Workgroup (head h, 64-dim slice) merges the runs'
+// partial states of that head for its 64 output dims: wavefront w sums runs
+// w, w+4, ... with lane = output dim.  Its first kCombPre runs are loaded
+// together with the (m, l) pairs, before the weights are known (every run's
+// partial is written, zeros for a run that saw no cell), so a decode set of up
+// to 4*kCombPre = 68 runs (2,176 cells) costs one memory round trip.  The
+// wavefronts' sums are added in a fixed order.
 template <int G>
 __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs) {
-    constexpr int kPre = 9;
-    __shared__ float s_w[1024];
-    __shared__ float s_red[32];
-    __shared__ float2 s_acc[kCombGroups][128];
-    const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+    __shared__ float s_w[kCombMaxRuns];  // m of run r, then its weight exp(m_r - M)
+    __shared__ float s_l[kCombMaxRuns];
+    __shared__ float s_red[kCombWaves];
+    __shared__ float s_acc[kCombWaves][kWave];
+    const int h = blockIdx.x / kCombSlices, slice = blockIdx.x % kCombSlices;
+    const int i = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int hg = h / G, hh = h % G;
     const int stride = G * kHeadDim + 2 * G;
     const float *base = a.ws + ((int64_t)i * (a.n_head / G) + hg) * n_runs * stride;
-    const int rg = tid >> 7, dp = tid & 127;
+    const int col = hh * kHeadDim + slice * kWave + lane;
     // every load is issued (clamped to the last run; a run past n_runs gets
     // weight 0): a load under a lane condition is waited for right after it
-    float2 pre[kPre];
+    float pre[kCombPre];
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-        const int r = min(rg + u * kCombGroups, n_runs - 1);
-        pre[u] = *reinterpret_cast<const float2 *>(base + (int64_t)r * stride + hh * kHeadDim +
-                                                   2 * dp);
+    for (int u = 0; u < kCombPre; ++u)
+        pre[u] = base[(int64_t)min(wave + kCombWaves * u, n_runs - 1) * stride + col];
+    // (m, l) of runs tid, tid + 256, ...; a run that saw no cell has l = 0
+    float mloc = -INFINITY;
+    for (int r = tid; r < n_runs; r += kCombNT) {
+        const float m = base[(int64_t)r * stride + G * kHeadDim + hh];
+        const float l = base[(int64_t)r * stride + G * kHeadDim + G + hh];
+        const bool seen = l > 0.f;
+        s_w[r] = seen ? m : -INFINITY;
+        s_l[r] = seen ? l : 0.f;
+        mloc = fmaxf(mloc, seen ? m : -INFINITY);
     }
-    // per-run weights exp(m_r - M), M = max over runs that saw any cell
-    const int tr = min(tid, n_runs - 1);
-    float m = base[(int64_t)tr * stride + G * kHeadDim + hh];
-    float l = base[(int64_t)tr * stride + G * kHeadDim + G + hh];
-    if (tid >= n_runs || !(l > 0.f)) {
-        m = -INFINITY;
-        l = 0.f;
+    mloc = wave_max_f32(mloc);
+    if (lane == 0) s_red[wave] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    // weights exp(m_r - M) of this thread's own runs (no barrier needed)
+    float lw = 0.f;
+    for (int r = tid; r < n_runs; r += kCombNT) {
+        const float m = s_w[r];
+        const float w = m != -INFINITY ? __expf(m - M) : 0.f;
+        s_w[r] = w;
+        lw += s_l[r] * w;
     }
-    const float mx = wave_max_f32(m);
-    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-    __syncthreads();
-    // lane w holds wavefront w's value (one LDS load, then DPP)
-    constexpr int kNW = kCombNT / 64;
-    const int lane = tid & 63;
-    const float M = wave_max_f32(lane < kNW ? s_red[lane] : -INFINITY);
-    __syncthreads();
-    const float wgt = (m != -INFINITY) ? __expf(m - M) : 0.f;
-    if (tid < n_runs) s_w[tid] = wgt;
-    float lw = l > 0.f ? l * wgt : 0.f;
     lw = wave_sum_f32(lw);
-    if ((tid & 63) == 0) s_red[tid >> 6] = lw;
+    __syncthreads();  // every M read before s_red is reused; every weight written
+    if (lane == 0) s_red[wave] = lw;
     __syncthreads();
-    const float L = wave_sum_f32(lane < kNW ? s_red[lane] : 0.f);
+    const float L = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
 
-    float2 acc = make_float2(0.f, 0.f);
+    float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-        const int r = rg + u * kCombGroups;
-        const float w = r < n_runs ? s_w[r] : 0.f;
-        acc.x = fmaf(pre[u].x, w, acc.x);
-        acc.y = fmaf(pre[u].y, w, acc.y);
+    for (int u = 0; u < kCombPre; ++u) {
+        const int r = wave + kCombWaves * u;
+        acc = fmaf(pre[u], r < n_runs ? s_w[r] : 0.f, acc);
     }
     constexpr int U = 8;
-    for (int r0 = rg + kPre * kCombGroups; r0 < n_runs; r0 += kCombGroups * U) {
-        float2 v[U];
-        float w[U];
+    for (int r0 = wave + kCombWaves * kCombPre; r0 < n_runs; r0 += kCombWaves * U) {
+        float v[U], w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * kCombGroups;
+            const int r = r0 + kCombWaves * u;
             w[u] = r < n_runs ? s_w[r] : 0.f;
-            v[u] = *reinterpret_cast<const float2 *>(base + (int64_t)min(r, n_runs - 1) * stride +
-                                                     hh * kHeadDim + 2 * dp);
+            v[u] = base[(int64_t)min(r, n_runs - 1) * stride + col];
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            acc.x = fmaf(v[u].x, w[u], acc.x);
-            acc.y = fmaf(v[u].y, w[u], acc.y);
-        }
+        for (int u = 0; u < U; ++u) acc = fmaf(v[u], w[u], acc);
     }
-    s_acc[rg][dp] = acc;
+    s_acc[wave][lane] = acc;
     __syncthreads();
-    if (rg == 0) {
-        float2 t = s_acc[0][dp];
-#pragma unroll
-        for (int q = 1; q < kCombGroups; ++q) {
-            t.x += s_acc[q][dp].x;
-            t.y += s_acc[q][dp].y;
-        }
-        float2 r = make_float2(L > 0.f ? t.x / L : 0.f, L > 0.f ? t.y / L : 0.f);
-        *reinterpret_cast<float2 *>(a.out + ((int64_t)i * a.n_head + h) * kHeadDim + 2 * dp) = r;
+    if (wave == 0) {
+        const float t = (s_acc[0][lane] + s_acc[1][lane]) + (s_acc[2][lane] + s_acc[3][lane]);
+        a.out[((int64_t)i * a.n_head + h) * kHeadDim + slice * kWave + lane] = L > 0.f ? t / L : 0.f;
     }
 }
 
@@ -545,8 +541,8 @@ hipError_t launch_g(const AttnArgs &a, int chunks_per_run, int n_runs, bool dire
                        direct ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head, a.n_q), dim3(kCombNT), 0, st, a,
-                       n_runs);
+    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head * kCombSlices, a.n_q), dim3(kCombNT),
+                       0, st, a, n_runs);
     return hipGetLastError();
 }
 
@@ -579,8 +575,8 @@ hipError_t launch_sel_g(const DecodeIdxArgs &f, const AttnArgs &a, hipStream_t s
     hipLaunchKernelGGL((k_sel_attn<G, KVT>), dim3(grid), dim3(kSelAttnNT), 0, st, f, a, n_runs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head, a.n_q), dim3(kCombNT), 0, st, a,
-                       n_runs);
+    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_head * kCombSlices, a.n_q), dim3(kCombNT),
+                       0, st, a, n_runs);
     return hipGetLastError();
 }
 
