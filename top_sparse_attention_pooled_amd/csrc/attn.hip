@@ -384,57 +384,114 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int r = sa.r;
     const int B = f.top_k / r;
     const int tail = valid ? (int)(p + 1 - nc * r) : 0;
-    select_candidates<kSelAttnNT, kSelAttnMaxBlocks>(f, i, limit, B, ss);
+    CandKeys<kSelAttnNT, kSelAttnMaxBlocks> ck;
+    Thresh th;
+    const bool fast =
+        select_candidates<kSelAttnNT, kSelAttnMaxBlocks, true>(f, i, limit, B, ss, ck, th);
 
-    // ranks of this thread's bitmap words
-    const int n_words = (int)((limit + 31) / 32);
-    const int per = (n_words + kSelAttnNT - 1) / kSelAttnNT;
-    const int w0 = tid * per;
-    uint32_t local = 0;
-    for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(ss.bitmap[w]);
-    const uint32_t incl = wave_incl_scan_u32(local);
-    if (lane == kWave - 1) ss.tk.red[wave] = incl;
-    __syncthreads();
-    uint32_t before, total;
-    waves_prefix<kSelAttnNT / kWave>(ss.tk.red, wave, before, total);
-    const uint32_t rank = before + incl - local;
-    const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
-    const int n_sel = n_keep * r + tail;
+    // List positions [c_begin, c_begin + 32): the kept blocks of ascending
+    // rank [k_lo, k_hi] (block k covers positions k*r .. k*r + r-1), then
+    // the tail cells, then -1.
     const int c_begin = run * kChunk;
-    // list positions [c_begin, c_begin + 32): kept blocks of rank
-    // [c_begin / r, (c_begin + 31) / r], then tail cells, then -1
     const int k_lo = c_begin / r, k_hi = (c_begin + kChunk - 1) / r;
-    if (local && (int)rank <= k_hi && (int)(rank + local) > k_lo) {
-        uint32_t k = rank;
-        for (int w = w0; w < w0 + per && w < n_words; ++w) {
-            uint32_t bits = ss.bitmap[w];
-            while (bits) {
-                const int bit = __builtin_ctz(bits);
-                bits &= bits - 1;
+    const int ld_cells = f.top_k + r - 1;
+    int32_t *sel_blocks = f.sel_blocks + (int64_t)i * B;
+    auto place = [&](int k, int b) {
+        for (int c = 0; c < r; ++c) {
+            const int pos = k * r + c - c_begin;
+            if (pos >= 0 && pos < kChunk) s_cells[pos] = b * r + c;
+        }
+    };
+    uint32_t local = 0, incl;
+    int n_keep_all;
+    if (fast) {
+        // the kept set is the base candidates th keeps; they ascend by block
+        // thread by thread, so a scan of the kept counts gives the ranks
+        uint32_t kept = 0;
+#pragma unroll
+        for (int x = 0; x < decltype(ck)::kBase; ++x)
+            if (x < ck.nb && th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]))
+                kept |= 1u << x;
+        local = __popc(kept);
+        incl = wave_incl_scan_u32(local);
+        if (lane == kWave - 1) ss.tk.red[wave] = incl;
+        __syncthreads();
+        uint32_t before, total;
+        waves_prefix<kSelAttnNT / kWave>(ss.tk.red, wave, before, total);
+        uint32_t k = before + incl - local;
+        const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+        if (local && (int)k <= k_hi && (int)(k + local) > k_lo) {
+#pragma unroll
+            for (int x = 0; x < decltype(ck)::kBase; ++x) {
+                if (!((kept >> x) & 1)) continue;
                 if ((int)k >= k_lo && (int)k <= k_hi && (int)k < n_keep) {
-                    const int b = w * 32 + bit;
-                    for (int c = 0; c < r; ++c) {
-                        const int pos = (int)k * r + c - c_begin;
-                        if (pos >= 0 && pos < kChunk) s_cells[pos] = b * r + c;
-                    }
+                    const int b = key_block(ck.k[x]);
+                    place((int)k, b);
+                    if (set == 0) sel_blocks[k] = b;
                 }
                 ++k;
             }
         }
+        // this run's share of the selection outputs: -1 past the kept blocks
+        // (the runs' block ranks cover [0, B)), the count from run 0
+        if (set == 0) {
+            const int k0 = max(k_lo, n_keep), k1 = min(k_hi, B - 1);
+            if (tid <= k1 - k0) sel_blocks[k0 + tid] = -1;
+            if (run == 0 && tid == 0) f.n_sel[i] = n_keep * r + tail;
+        }
+        if (tid < kChunk) {
+            const int pos = c_begin + tid;
+            if (pos >= n_keep * r) {
+                const int n_sel = n_keep * r + tail;
+                s_cells[tid] = pos < n_sel ? (int)(nc * r + (pos - n_keep * r)) : -1;
+            }
+        }
+        __syncthreads();
+        if (set == 0 && tid < kChunk && c_begin + tid < ld_cells)
+            f.sel_cells[(int64_t)i * ld_cells + c_begin + tid] = s_cells[tid];
+        n_keep_all = n_keep;
+    } else {
+        // ranks of this thread's bitmap words
+        const int n_words = (int)((limit + 31) / 32);
+        const int per = (n_words + kSelAttnNT - 1) / kSelAttnNT;
+        const int w0 = tid * per;
+        for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(ss.bitmap[w]);
+        incl = wave_incl_scan_u32(local);
+        if (lane == kWave - 1) ss.tk.red[wave] = incl;
+        __syncthreads();
+        uint32_t before, total;
+        waves_prefix<kSelAttnNT / kWave>(ss.tk.red, wave, before, total);
+        const uint32_t rank = before + incl - local;
+        const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+        if (local && (int)rank <= k_hi && (int)(rank + local) > k_lo) {
+            uint32_t k = rank;
+            for (int w = w0; w < w0 + per && w < n_words; ++w) {
+                uint32_t bits = ss.bitmap[w];
+                while (bits) {
+                    const int bit = __builtin_ctz(bits);
+                    bits &= bits - 1;
+                    if ((int)k >= k_lo && (int)k <= k_hi && (int)k < n_keep)
+                        place((int)k, w * 32 + bit);
+                    ++k;
+                }
+            }
+        }
+        if (tid < kChunk) {
+            const int pos = c_begin + tid;
+            if (pos >= n_keep * r) {
+                const int n_sel = n_keep * r + tail;
+                s_cells[tid] = pos < n_sel ? (int)(nc * r + (pos - n_keep * r)) : -1;
+            }
+        }
+        __syncthreads();
+        if (run == 0 && set == 0) {
+            emit_from_bitmap<kSelAttnNT>(ss.bitmap, n_words, B, r, nc, tail, sel_blocks,
+                                         f.sel_cells + (int64_t)i * ld_cells, ld_cells,
+                                         f.n_sel + i, ss.tk);
+        }
+        n_keep_all = n_keep;
     }
-    if (tid < kChunk) {
-        const int pos = c_begin + tid;
-        if (pos >= n_keep * r)
-            s_cells[tid] = pos < n_sel ? (int)(nc * r + (pos - n_keep * r)) : -1;
-    }
-    __syncthreads();
-    if (run == 0 && set == 0) {
-        const int ld_cells = f.top_k + r - 1;
-        emit_from_bitmap<kSelAttnNT>(ss.bitmap, n_words, B, r, nc, tail,
-                                     f.sel_blocks + (int64_t)i * B,
-                                     f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i,
-                                     ss.tk);
-    }
+    const int n_sel = n_keep_all * r + tail;
     int cell[kCPG];
 #pragma unroll
     for (int u = 0; u < kCPG; ++u) cell[u] = s_cells[grp * kCPG + u];

@@ -3,14 +3,17 @@
 // blocks compete, ranked by score with ties to the lower block).
 //
 // The scoring kernel leaves, for every group of 64 blocks (one wavefront's
-// tile), the group's 4 largest 64-bit keys (score key << 32 | ~block) and the
-// largest key it dropped.  The selection takes the top-B threshold over the
-// candidates; a group whose dropped key would itself be kept under that
-// threshold may hold more winners, so all 64 of its keys are re-admitted (or,
-// past 32 such groups, the whole score row is streamed) and the threshold is
-// taken again.  A dropped key of any other group lies below the first
-// threshold, which can only rise as keys are added, so the final kept set is
-// the exact top-B of all scores.
+// tile), the group's 4 largest 64-bit keys (score key << 32 | ~block), in
+// ascending block order, and the largest key it dropped.  The selection
+// takes the top-B threshold over the candidates; a group whose dropped key
+// would itself be kept under that threshold may hold more winners, so all 64
+// of its keys are re-admitted (or, past 32 such groups, the whole score row
+// is streamed) and the threshold is taken again.  A dropped key of any other
+// group lies below the first threshold, which can only rise as keys are
+// added, so the final kept set is the exact top-B of all scores.  Without a
+// re-admission the kept set lies among the candidates, and since they ascend
+// by block, a kept candidate's place in the ascending output is the number
+// of kept candidates before it.
 //
 // The same routine runs in a 1024-thread selection workgroup and inside each
 // 256-thread attention workgroup; the kept set is unique, so every caller
@@ -51,10 +54,11 @@ inline void bind_candidates(DecodeIdxArgs &f, void *ws) {
 }
 
 // The candidate keys of one query in registers, for up to MAXB blocks: base
-// slot s holds candidate s*NT + tid, expansion slot e holds key e*NT + tid of
-// the re-admitted groups' keys (group over[x] at x = (e*NT + tid) / 64).
-// nb / ne: slots in use (workgroup-uniform), so unused slots cost one scalar
-// branch.
+// slot s holds candidate tid*nb + s (each thread a run of consecutive
+// candidates, so the base slots read thread by thread ascend by block),
+// expansion slot e holds key e*NT + tid of the re-admitted groups' keys
+// (group over[x] at x = (e*NT + tid) / 64).  nb / ne: slots in use
+// (workgroup-uniform), so unused slots cost one scalar branch.
 template <int NT, int MAXB>
 struct CandKeys {
     static constexpr int kBase = MAXB / kGroup * kCand / NT;
@@ -82,12 +86,17 @@ struct CandSelSmem {
     int over[kMaxExpand];
 };
 
-// Marks the exact top-B blocks among query i's scored blocks [0, limit) in
-// sm.bitmap (words [0, ceil(limit/32)) all written).  Needs nb_max <= MAXB.
-// Workgroup-uniform; ends with a barrier.
-template <int NT, int MAXB>
-__device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i, int64_t limit,
-                                                  int B, CandSelSmem<NT, MAXB> &sm) {
+// The exact top-B blocks among query i's scored blocks [0, limit): the
+// threshold th over the candidates ck (both returned).  Returns true when no
+// group was re-admitted and the score row was not streamed: the kept set is
+// then exactly the base slots of ck that th keeps.  The kept blocks are also
+// marked in sm.bitmap (words [0, ceil(limit/32)) all written), except in that
+// case when SKIP_FAST_MARK.  Needs nb_max <= MAXB.  Workgroup-uniform; ends
+// with a barrier.
+template <int NT, int MAXB, bool SKIP_FAST_MARK = false>
+__device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i, int64_t limit,
+                                                  int B, CandSelSmem<NT, MAXB> &sm,
+                                                  CandKeys<NT, MAXB> &ck, Thresh &th) {
     const int tid = threadIdx.x;
     const int n_grp = cand_groups(f.s.nb_max);
     const int64_t qbase = (int64_t)i * n_grp;
@@ -96,14 +105,14 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
     for (int w = tid; w < n_words; w += NT) sm.bitmap[w] = 0;
 
     using Keys = CandKeys<NT, MAXB>;
-    Keys ck;
     const int kc = f.n_cand;
     const int n_cand = n_grp * kc;
     ck.nb = (n_cand + NT - 1) / NT;
     ck.ne = 0;
+    const int fi0 = tid * ck.nb;
 #pragma unroll
     for (int s = 0; s < Keys::kBase; ++s) {
-        const int fi = tid + NT * s;
+        const int fi = fi0 + s;
         ck.k[s] = (s < ck.nb && fi < n_cand) ? f.cand[qbase * kc + fi] : 0ull;
     }
 #pragma unroll
@@ -134,7 +143,7 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
         }
     };
     if (tid == 0) sm.n_over = 0;
-    Thresh th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
+    th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
 
 #pragma unroll
     for (int q = 0; q < kDrop; ++q) {
@@ -153,7 +162,7 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
         // replace the kept keys of the re-admitted groups by all of theirs
 #pragma unroll
         for (int s = 0; s < Keys::kBase; ++s) {
-            const int g = (tid + NT * s) / kc;
+            const int g = (fi0 + s) / kc;
             for (int e = 0; e < n_over; ++e)
                 if (sm.over[e] == g) ck.k[s] = 0ull;
         }
@@ -174,6 +183,8 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
         }
         th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
     }
+    const bool fast = n_over == 0;
+    if (SKIP_FAST_MARK && fast) return true;
 
     auto mark = [&](uint32_t k, uint32_t u) {
         if (th.keep(k, u)) {
@@ -186,6 +197,7 @@ __device__ __forceinline__ void select_candidates(const DecodeIdxArgs &f, int i,
     else
         ck(mark);
     __syncthreads();
+    return fast;
 }
 
 }  // namespace qsa

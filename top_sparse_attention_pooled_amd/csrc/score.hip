@@ -128,6 +128,39 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
     return key;
 }
 
+// One compare-exchange of a bitonic network (stage KK, partner lane ^ J).
+template <int KK, int J>
+__device__ __forceinline__ void bitonic_step(uint64_t &k, int lane) {
+    const uint64_t o = xor_lane64<J>(k);
+    const bool take_max = ((lane & J) == 0) == ((lane & KK) == 0);
+    k = take_max ? (o > k ? o : k) : (o < k ? o : k);
+}
+
+// Lanes [0, n) (n = 4, 8 or 16, wave-uniform) hold keys (score key << 32 |
+// ~block); on return they hold the same keys by descending ~block, that is
+// ascending block, with zero keys last.  A bitonic network over groups of n
+// lanes on the swapped halves; lanes from n on end up with other keys of
+// their own groups.
+__device__ __forceinline__ uint64_t group_sort_by_block(uint64_t key, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t k = (key << 32) | (key >> 32);
+    bitonic_step<2, 1>(k, lane);
+    bitonic_step<4, 2>(k, lane);
+    bitonic_step<4, 1>(k, lane);
+    if (n >= 8) {
+        bitonic_step<8, 4>(k, lane);
+        bitonic_step<8, 2>(k, lane);
+        bitonic_step<8, 1>(k, lane);
+    }
+    if (n >= 16) {
+        bitonic_step<16, 8>(k, lane);
+        bitonic_step<16, 4>(k, lane);
+        bitonic_step<16, 2>(k, lane);
+        bitonic_step<16, 1>(k, lane);
+    }
+    return (k << 32) | (k >> 32);
+}
+
 // 1-D grid: n_q * 4*n_wg scoring workgroups (one per query and 64-block
 // group), then ceil(n_dirty/4) update workgroups (one wavefront per dirty
 // entry).
@@ -292,8 +325,11 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     uint64_t key = (b < limit && finite_f32(sc)) ? block_key(sc, b) : 0ull;
     key = wave_sort_desc(key);
     const int64_t grp = (int64_t)i * n_grp + gg;
-    if (lane < f.n_cand) f.cand[grp * f.n_cand + lane] = key;
     if (lane == f.n_cand) f.drop[grp] = key;
+    // the kept keys in ascending block order (zeros last), so that the
+    // candidates of all groups, read in order, ascend by block
+    key = group_sort_by_block(key, f.n_cand);
+    if (lane < f.n_cand) f.cand[grp * f.n_cand + lane] = key;
 }
 
 // grid (n_q), 1024 threads: the exact selection from the candidates, then
@@ -310,7 +346,9 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
                                     a.g.n_cells, a.r, s, p, valid);
     const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
     const int B = f.top_k / a.r;
-    select_candidates<kSelNT, MAXB>(f, i, limit, B, sm);
+    CandKeys<kSelNT, MAXB> ck;
+    Thresh th;
+    select_candidates<kSelNT, MAXB>(f, i, limit, B, sm, ck, th);
     const int n_words = (int)((limit + 31) / 32);
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = f.top_k + a.r - 1;
