@@ -356,6 +356,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     __shared__ CandSelSmem<kSelAttnNT, kSelAttnMaxBlocks> ss;
     __shared__ AttnSmem<G> sm[kParts];
     __shared__ int s_cells[kChunk];
+    __shared__ int s_blk[kChunk + 1];  // kept blocks of ranks k_lo .. k_hi
     const int n_hg = a.n_head / G;
     const int n_set = (n_hg + kParts - 1) / kParts;
     // workgroup -> (query, run, set), set fastest
@@ -406,38 +407,39 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     int n_keep_all;
     if (fast) {
         // the kept set is the base candidates th keeps; they ascend by block
-        // thread by thread, so a scan of the kept counts gives the ranks
-        uint32_t kept = 0;
+        // in the order (wavefront, slot, lane), so a kept one's rank is the
+        // kept count of the earlier wavefronts, then of the wavefront's
+        // earlier slots, then of its slot's lower lanes (ballots)
+        uint32_t in_wave = 0;
 #pragma unroll
         for (int x = 0; x < decltype(ck)::kBase; ++x)
-            if (x < ck.nb && th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]))
-                kept |= 1u << x;
-        local = __popc(kept);
-        incl = wave_incl_scan_u32(local);
-        if (lane == kWave - 1) ss.tk.red[wave] = incl;
+            if (x < ck.nb)
+                in_wave += __popcll(
+                    __ballot(th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x])));
+        if (lane == 0) ss.tk.red[wave] = in_wave;
         __syncthreads();
         uint32_t before, total;
-        waves_prefix<kSelAttnNT / kWave>(ss.tk.red, wave, before, total);
-        uint32_t k = before + incl - local;
-        const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
-        if (local && (int)k <= k_hi && (int)(k + local) > k_lo) {
-#pragma unroll
-            for (int x = 0; x < decltype(ck)::kBase; ++x) {
-                if (!((kept >> x) & 1)) continue;
-                if ((int)k >= k_lo && (int)k <= k_hi && (int)k < n_keep) {
-                    const int b = key_block(ck.k[x]);
-                    place((int)k, b);
-                    if (set == 0) sel_blocks[k] = b;
-                }
-                ++k;
-            }
+        {
+            constexpr int NW = kSelAttnNT / kWave;
+            const uint32_t incl = wave_incl_scan_u32(lane < NW ? ss.tk.red[lane] : 0u);
+            total = lane_value(incl, kWave - 1);
+            before = wave > 0 ? lane_value(incl, wave - 1) : 0u;
         }
-        // this run's share of the selection outputs: -1 past the kept blocks
-        // (the runs' block ranks cover [0, B)), the count from run 0
-        if (set == 0) {
-            const int k0 = max(k_lo, n_keep), k1 = min(k_hi, B - 1);
-            if (tid <= k1 - k0) sel_blocks[k0 + tid] = -1;
-            if (run == 0 && tid == 0) f.n_sel[i] = n_keep * r + tail;
+        const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+        const uint64_t below = (1ull << lane) - 1ull;
+        uint32_t k0 = before;  // rank of this wavefront's next kept slot
+#pragma unroll
+        for (int x = 0; x < decltype(ck)::kBase; ++x) {
+            if (x >= ck.nb) continue;
+            const bool kp = th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]);
+            const uint64_t bal = __ballot(kp);
+            const int k = (int)(k0 + __popcll(bal & below));
+            if (kp && k >= k_lo && k <= k_hi && k < n_keep) {
+                const int b = key_block(ck.k[x]);
+                place(k, b);
+                s_blk[k - k_lo] = b;
+            }
+            k0 += __popcll(bal);
         }
         if (tid < kChunk) {
             const int pos = c_begin + tid;
@@ -447,8 +449,6 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
             }
         }
         __syncthreads();
-        if (set == 0 && tid < kChunk && c_begin + tid < ld_cells)
-            f.sel_cells[(int64_t)i * ld_cells + c_begin + tid] = s_cells[tid];
         n_keep_all = n_keep;
     } else {
         // ranks of this thread's bitmap words
@@ -484,11 +484,6 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
             }
         }
         __syncthreads();
-        if (run == 0 && set == 0) {
-            emit_from_bitmap<kSelAttnNT>(ss.bitmap, n_words, B, r, nc, tail, sel_blocks,
-                                         f.sel_cells + (int64_t)i * ld_cells, ld_cells,
-                                         f.n_sel + i, ss.tk);
-        }
         n_keep_all = n_keep;
     }
     const int n_sel = n_keep_all * r + tail;
@@ -498,6 +493,27 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int c_end = min(n_sel, c_begin + kChunk);
     attend_chunks<G, KVT>(a, i, s, g, h0, c_begin, c_end, cell, nullptr, qv, sm[part],
                           partial_of<G>(a, i, hg, run, n_runs), false, active);
+
+    // The selection outputs, after the attention: a barrier waits for every
+    // store issued before it, so stores issued earlier would delay the
+    // gather.  attend_chunks leaves s_cells, s_blk and ss untouched.
+    if (fast) {
+        // this run's share (set 0): its blocks, -1 past the kept blocks (the
+        // runs' block ranks cover [0, B)), its list positions; the count
+        // from run 0
+        if (set == 0) {
+            const int k = k_lo + tid;
+            if (k <= k_hi && k < B) sel_blocks[k] = k < n_keep_all ? s_blk[tid] : -1;
+            if (tid < kChunk && c_begin + tid < ld_cells)
+                f.sel_cells[(int64_t)i * ld_cells + c_begin + tid] = s_cells[tid];
+            if (run == 0 && tid == 0) f.n_sel[i] = n_sel;
+        }
+    } else if (run == 0 && set == 0) {
+        const int n_words = (int)((limit + 31) / 32);
+        emit_from_bitmap<kSelAttnNT>(ss.bitmap, n_words, B, r, nc, tail, sel_blocks,
+                                     f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i,
+                                     ss.tk);
+    }
 }
 
 constexpr int kCombNT = 256;

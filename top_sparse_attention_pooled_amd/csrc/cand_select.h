@@ -26,7 +26,11 @@ namespace qsa {
 
 constexpr int kGroup = kTile;   // blocks per candidate group (one wavefront)
 constexpr int kCand = 4;        // fewest keys kept per group
-constexpr int kCandSlots = 4096;  // candidates the selection holds on chip for nb_max <= 65536
+// candidates a selection workgroup holds in registers: 4 per group up to
+// nb_max 65536, 8 up to 32768, 16 up to 16384 blocks (more slots would cost
+// the fused decode kernel the registers that let two of its workgroups
+// share a CU)
+constexpr int kCandSlots = 4096;
 constexpr int kMaxExpand = 32;  // groups re-admitted whole before streaming
 
 // Workspace of the decode indexer: cand [n_q][groups][n_cand], then drop
@@ -34,9 +38,12 @@ constexpr int kMaxExpand = 32;  // groups re-admitted whole before streaming
 __host__ __device__ inline int cand_groups(int nb_max) { return (nb_max + 255) / 256 * 4; }
 
 // Keys kept per group: as many (16, 8, then 4) as the on-chip candidate
-// slots allow.  B winners spread over fewer groups in a shorter context (512
-// of ~12,400 blocks at 50k cells is 2.6 per group on average), and a group
-// with more winners than it kept must be re-admitted whole.
+// slots allow.  A group with more winners than it kept must be re-admitted
+// whole, which costs the selection a second pass: with B = 512 of ~62,000
+// blocks (250k cells) a group of 64 holds 0.53 winners on average, and with
+// 4 kept keys about one step in five has a group of 5 or more.  Winners
+// spread over fewer groups in a shorter context (512 of ~12,400 blocks at
+// 50k cells is 2.6 per group on average).
 __host__ __device__ inline int cand_per_group(int nb_max) {
     const int g = cand_groups(nb_max);
     return g * 16 <= kCandSlots ? 16 : (g * 8 <= kCandSlots ? 8 : kCand);
@@ -54,11 +61,17 @@ inline void bind_candidates(DecodeIdxArgs &f, void *ws) {
 }
 
 // The candidate keys of one query in registers, for up to MAXB blocks: base
-// slot s holds candidate tid*nb + s (each thread a run of consecutive
-// candidates, so the base slots read thread by thread ascend by block),
-// expansion slot e holds key e*NT + tid of the re-admitted groups' keys
-// (group over[x] at x = (e*NT + tid) / 64).  nb / ne: slots in use
-// (workgroup-uniform), so unused slots cost one scalar branch.
+// slot s of lane l of wavefront w holds candidate cand_index(nb, s) =
+// (w*nb + s)*64 + l -- each wavefront a run of consecutive candidates, slot
+// by slot, so every load is 512 contiguous bytes and the candidates ascend
+// by block in the order (wavefront, slot, lane).  Expansion slot e holds key
+// e*NT + tid of the re-admitted groups' keys (group over[x] at x = (e*NT +
+// tid) / 64).  nb / ne: slots in use (workgroup-uniform), so unused slots
+// cost one scalar branch.
+__device__ __forceinline__ int cand_index(int nb, int s) {
+    return ((int)(threadIdx.x >> 6) * nb + s) * kWave + (int)(threadIdx.x & (kWave - 1));
+}
+
 template <int NT, int MAXB>
 struct CandKeys {
     static constexpr int kBase = MAXB / kGroup * kCand / NT;
@@ -109,10 +122,9 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
     const int n_cand = n_grp * kc;
     ck.nb = (n_cand + NT - 1) / NT;
     ck.ne = 0;
-    const int fi0 = tid * ck.nb;
 #pragma unroll
     for (int s = 0; s < Keys::kBase; ++s) {
-        const int fi = fi0 + s;
+        const int fi = cand_index(ck.nb, s);
         ck.k[s] = (s < ck.nb && fi < n_cand) ? f.cand[qbase * kc + fi] : 0ull;
     }
 #pragma unroll
@@ -162,7 +174,7 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
         // replace the kept keys of the re-admitted groups by all of theirs
 #pragma unroll
         for (int s = 0; s < Keys::kBase; ++s) {
-            const int g = (fi0 + s) / kc;
+            const int g = cand_index(ck.nb, s) / kc;
             for (int e = 0; e < n_over; ++e)
                 if (sm.over[e] == g) ck.k[s] = 0ull;
         }
