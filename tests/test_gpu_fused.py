@@ -34,15 +34,19 @@ def aligned_cells(w, q_idx, p, blocks, kidx):
         kidx[b * w.r:(b + 1) * w.r] = np.concatenate([zb.real, zb.imag]).astype(np.float32)
 
 
-def run_case(name, w, n_cells, q_idx, kidx):
-    say(f"fused select: {name}")
+def run_case(name, w, n_cells, q_idx, kidx, n_q=3):
+    """n_q queries at the last positions.  Three queries make the fused
+    select+attend grid larger than the chip holds at once, so that call
+    selects once per query and attends over the lists; one query runs the
+    fused kernel, where every attention workgroup selects on its own."""
+    say(f"fused select: {name} ({n_q} queries)")
     layer = runtime.Layer(w, DEV, kidx=kidx[None].copy() if kidx.ndim == 2 else kidx)
     layer.rebuild(np.array([n_cells], np.int32))
     ref_pooled = np.zeros((1, w.cap_blocks, w.d), np.float32)
     oracle.update_pooled(layer.kidx.cpu().numpy(), np.array([n_cells], np.int32),
                          np.array([(0, b) for b in range(-(-n_cells // w.r))], np.int32),
                          ref_pooled, w.r, w.theta, w.eps)
-    positions = [p for p in (n_cells - 1, n_cells - 2, n_cells - 3) if p >= 0]
+    positions = [p for p in range(n_cells - 1, n_cells - 1 - n_q, -1) if p >= 0]
     n_q = len(positions)
     qi = np.repeat(q_idx[None], n_q, axis=0).astype(np.float32)
     nb_max = -(-n_cells // w.r)
@@ -104,24 +108,27 @@ def workload():
     return synth.Workload("fz", 95, 1, 40000, n_new=1, steps=1, top_k=2048)
 
 
-def test_fused_common_case():
+@pytest.mark.parametrize("n_q", [3, 1])
+def test_fused_common_case(n_q):
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 95, 0, synth.T_QIDX)
-    run_case("i.i.d. keys", w, 40000, q, kidx)
+    run_case("i.i.d. keys", w, 40000, q, kidx, n_q)
 
 
-def test_fused_expands_clustered_groups():
+@pytest.mark.parametrize("n_q", [3, 1])
+def test_fused_expands_clustered_groups(n_q):
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 96, 0, synth.T_QIDX)
     aligned_cells(w, q, 39999, range(3000, 3700), kidx)  # 700 blocks over 12 groups of 64
-    s = run_case("contiguous cluster (re-admits 12 groups)", w, 40000, q, kidx)
-    kept, _ = oracle.select(s, 40000 - 3, w.r, w.top_k)
+    s = run_case("contiguous cluster (re-admits 12 groups)", w, 40000, q, kidx, n_q)
+    kept, _ = oracle.select(s, 40000 - n_q, w.r, w.top_k)
     assert np.sum((kept >= 3000) & (kept < 3700)) >= 500  # the case really is clustered
 
 
-def test_fused_streams_when_many_groups_compete():
+@pytest.mark.parametrize("n_q", [3, 1])
+def test_fused_streams_when_many_groups_compete(n_q):
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 97, 0, synth.T_QIDX)
@@ -130,22 +137,42 @@ def test_fused_streams_when_many_groups_compete():
     # 36 groups (over the 32 re-admitted whole) compete
     blocks = [wg * 256 + 3 * j for wg in range(2, 38) for j in range(20)]
     aligned_cells(w, q, 39999, blocks, kidx)
-    s = run_case("strided cluster (36 groups compete: re-stream)", w, 40000, q, kidx)
-    kept, _ = oracle.select(s, 40000 - 3, w.r, w.top_k)
+    s = run_case("strided cluster (36 groups compete: re-stream)", w, 40000, q, kidx, n_q)
+    kept, _ = oracle.select(s, 40000 - n_q, w.r, w.top_k)
     assert np.isin(kept, blocks).sum() >= 500
 
 
-def test_fused_all_tied():
+@pytest.mark.parametrize("n_q", [3, 1])
+def test_fused_all_tied(n_q):
     w = workload()
     kidx = np.zeros((w.cap_cells, w.d), np.float32)  # every pooled key is 0: all scores tie
     q = synth.normal((w.d,), 98, 0, synth.T_QIDX)
-    s = run_case("all scores equal", w, 40000, q, kidx)
+    s = run_case("all scores equal", w, 40000, q, kidx, n_q)
     assert np.all(s[np.isfinite(s)] == 0)
 
 
-def test_fused_fewer_blocks_than_budget():
+@pytest.mark.parametrize("n_q", [3, 1])
+def test_fused_fewer_blocks_than_budget(n_q):
     w = workload()
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 99, 0, synth.T_QIDX)
     for n in (1, 3, 5, 1000, 2048, 2049, 8200):
-        run_case(f"n_cells={n}", w, n, q, kidx)
+        run_case(f"n_cells={n}", w, n, q, kidx, n_q)
+
+
+def test_fused_readmits_a_group_at_250k():
+    """248,278 cells (62,069 scored blocks): groups keep only their 4 best
+    keys at this length.  Six blocks of one group aligned with the query
+    beat every other block, so that group's dropped key competes and its
+    keys are re-admitted; one query runs the fused kernel (the bitmap path),
+    three the per-query selection."""
+    w = synth.Workload("fz250", 94, 1, 248278, n_new=1, steps=1, top_k=2048)
+    kidx = synth.make_kidx(w)[0]
+    q = synth.normal((w.d,), 94, 0, synth.T_QIDX)
+    planted = [40000 + 5 * j for j in range(6)]  # one 64-block group (block 40000 // 64 * 64 on)
+    assert len({b // 64 for b in planted}) == 1
+    aligned_cells(w, q, 248277, planted, kidx)
+    for n_q in (1, 3):
+        s = run_case("one group with 6 winners at 250k", w, 248278, q, kidx, n_q)
+        kept, _ = oracle.select(s, 248278 - n_q, w.r, w.top_k)
+        assert np.isin(planted, kept).all()
