@@ -178,7 +178,7 @@ def calibration_copy(args, torch, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               "(the QSA step is not sharded across GPUs)", file=sys.stderr)
         sys.exit(2)
 

@@ -100,7 +100,7 @@ extern "C" {
 /* Return codes.  0 is success; errors are negative. */
 #define QSA_OK 0
 #define QSA_EINVAL (-1)  /* bad pointer, size, alignment or geometry       */
-#define QSA_ENOTSUP (-2) /* geometry outside what this build implements    */
+#define QSA_ENOTSUP (-2) /* geometry outside what the library implements  */
 #define QSA_EWS (-3)     /* workspace missing or smaller than required     */
 #define QSA_EHIP (-4)    /* a HIP launch reported an error                 */
 

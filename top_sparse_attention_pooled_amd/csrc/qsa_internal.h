@@ -23,7 +23,7 @@ constexpr int kWave = 64;
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
-constexpr int kDIdx = 128;   // indexer dim this build implements
+constexpr int kDIdx = 128;   // indexer dim the library implements
 constexpr int kHeadDim = 256;
 constexpr int kTile = 64;    // blocks per pooled-key tile
 constexpr int kQuads = kDIdx / 4;
