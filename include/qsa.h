@@ -275,13 +275,15 @@ int qsa_select_topk_blocks(const qsa_dims *dims, const qsa_seqs *seqs,
  * canonical order T -- the bf16-rounded q' and keys, exact products, the T
  * sum -- without writing a score matrix.  The contraction runs on the matrix
  * cores; their sums differ from T's by at most Delta_i (a bound from |q'_i|
- * and the RMS-normed keys' norm), so a sampled pass (every 8th group of 64
- * blocks) gives each query a threshold below which no block of its exact
- * top-k can score, the full pass marks the blocks above it, and only those
- * are rescored in order T for the exact selection: sel_blocks, sel_cells
- * and n_sel equal those of qsa_select_topk_blocks over T-ordered bf16 scores
- * bit for bit (ties to the lower block).  If a query marks more than 8192
- * blocks it rescores every causal block (correct, slower).
+ * and the RMS-normed keys' norm), so a first pass keeps each query's
+ * largest matrix-core score of every 16-block subgroup; tau_i, the
+ * (top_k/r)-th largest of those, less 2 Delta_i is a threshold below which
+ * no block of the exact top-k can score; a second pass marks the blocks
+ * above it, and only those are rescored in order T for the exact selection:
+ * sel_blocks, sel_cells and n_sel equal those of qsa_select_topk_blocks over
+ * T-ordered bf16 scores bit for bit (ties to the lower block).  If a query
+ * marks more than 4096 blocks it rescores every causal block (correct,
+ * slower).
  *   pooled_bf16_dev: required (the update writes it; the scores read it).
  *   Workspace: qsa_workspace_size(QSA_OP_SCORE_SELECT_PREFILL, n_q, nb_max)
  *   bytes, 16-byte aligned, no initial contents required.

@@ -35,8 +35,8 @@ namespace qsa {
 
 namespace {
 
-constexpr int kSelPNT = 512;      // selection workgroup
-constexpr int kBandCap = 8192;    // masked blocks rescored from the LDS list (16 x B)
+constexpr int kSelPNT = 256;      // selection workgroup (two share a CU)
+constexpr int kBandCap = 4096;    // masked blocks rescored from the LDS list (8 x B)
 constexpr int kTauNT = 256;       // threshold workgroup
 constexpr int kPrefMaxBlocks = kFusedMaxBlocks;
 constexpr float kDeltaMin = 0x1p-100f, kDeltaMax = 0x1p100f;
