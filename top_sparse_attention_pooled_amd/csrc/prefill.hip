@@ -12,12 +12,17 @@
 //   1. k_rope_queries_delta: roped bf16 queries and Delta_i;
 //   2. k_prefill_scores<kSubMax>: per query, the largest MFMA score of each
 //      16-block subgroup of its causal blocks;
-//   3. k_prefill_tau: tau_i = the B-th largest of those maxima.  B distinct
-//      blocks then have MFMA score >= tau_i, so the exact B-th largest score
-//      S_B is >= tau_i - Delta, and every block of the exact top-B has MFMA
-//      score >= S_B - Delta >= tau_i - 2 Delta.  The filter threshold is
-//      tau_i - 2 Delta rounded down (-inf, every causal block, when there are
-//      fewer than B subgroups);
+//   3. k_prefill_tau: tau_i = a value that at least B of those maxima reach:
+//      the lower edge of the bin that holds the B-th largest after two radix
+//      rounds over the maxima's keys, at most 2^10 units in the last place
+//      (about 2^-13 of the score) below the B-th largest itself, which a
+//      third round would pin.  One round is too coarse: its range spans the
+//      negative and the positive keys, and its bin lets far more blocks
+//      through to the rescoring.  B distinct blocks then have MFMA score >=
+//      tau_i, so the exact B-th largest score S_B is >= tau_i - Delta, and
+//      every block of the exact top-B has MFMA score >= S_B - Delta >= tau_i
+//      - 2 Delta.  The filter threshold is tau_i - 2 Delta rounded down
+//      (-inf, every causal block, when there are fewer than B subgroups);
 //   4. k_prefill_scores<kMask>: per (query, 64-block group), a bit mask of
 //      the blocks whose MFMA score reaches the threshold;
 //   5. k_select_prefill: the masked blocks rescored in order T; their exact
@@ -394,7 +399,25 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     float thr = -INFINITY;
     if (n_valid >= (uint32_t)B && delta_in_range(delta)) {
         block_minmax_u32<kTauNT>(mn, mx, sm);
-        const float tau = key_value(kth_largest_u32<kTauNT>(keys, (uint32_t)B, mn, mx, sm));
+        // two rounds: the bin holding the B-th largest key, then the sub-bin
+        // within it; every key at or above the sub-bin's lower edge is >= it,
+        // and there are at least B of them
+        uint32_t lo = mn, hi = mx, krem = (uint32_t)B;
+        for (int round = 0; round < 2 && lo != hi; ++round) {
+            const int shift = range_shift(lo, hi);
+            for (int j = tid; j < kBins; j += kTauNT) sm.hist[j] = 0;
+            __syncthreads();
+            keys([&](uint32_t k, uint32_t) {
+                if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> shift], 1u);
+            });
+            __syncthreads();
+            pick_bin<kTauNT>(sm, lo, hi, shift, krem);
+            krem -= sm.b_above;
+            lo = sm.b_lo;
+            hi = sm.b_hi;
+            __syncthreads();
+        }
+        const float tau = key_value(lo);
         const double t = (double)tau - 2.0 * (double)delta;
         thr = (float)t;
         if ((double)thr > t) thr = nextafterf(thr, -INFINITY);
