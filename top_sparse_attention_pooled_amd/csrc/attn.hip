@@ -345,11 +345,15 @@ constexpr int kSelAttnOnChip = 512;       // fused workgroups resident at once (
 // workgroups for a 2051-cell set, about one per CU).  First the whole
 // workgroup derives query i's exact kept set from the candidates (the kept
 // set is unique, so all workgroups derive the same), then finds the cells at
-// positions [32*run, 32*run + 32) of the ascending cell list -- blocks by
-// rank through a prefix count over the bitmap, then the tail cells -- and
-// the parts attend over them.  The workgroup of (run 0, set 0) also writes
-// the selection outputs.  Cells, outputs and partial states equal those of
-// the selection kernel followed by k_attn.
+// positions [32*run, 32*run + 32) of the ascending cell list -- kept blocks
+// by rank, then the tail cells -- and the parts attend over them.  Without
+// a re-admitted group the ranks come from ballots over the candidates, which
+// ascend by block, and each run's set-0 workgroup writes its own share of
+// the selection outputs; after a re-admission the kept blocks are marked in
+// a bitmap, ranked by a prefix count over it, and the workgroup of (run 0,
+// set 0) writes all the outputs.  The outputs are written after the
+// attention.  Cells, outputs and partial states equal those of the selection
+// kernel followed by k_attn.
 template <int G, int KVT>
 __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnArgs a,
                                                          int n_runs) {
