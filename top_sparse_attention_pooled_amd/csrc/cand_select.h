@@ -16,7 +16,7 @@
 // of kept candidates before it.
 //
 // The same routine runs in a 1024-thread selection workgroup and inside each
-// 256-thread attention workgroup; the kept set is unique, so every caller
+// 512-thread fused attention workgroup; the kept set is unique, so every caller
 // derives the same one.
 #pragma once
 
