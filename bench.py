@@ -1,16 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the QSA sparse-attention step on one MI355X.
 
-A step is one decode token through the whole hot path -- pooled-key update,
+A decode step is one token through the whole hot path -- pooled-key update,
 block scoring, block top-k, sparse attention -- in each of 12 QSA layers (the
 pages' model has 12 QSA layers; 12 replicas of one layer's caches at distinct
 addresses also keep the ~400 MB working set out of the 256 MB last-level
 cache, so the bytes come from HBM).  The K timed steps are captured in one
 HIP graph and replayed; inputs are resident in HBM before timing starts.
 
+The default run (no --workload) measures the 250k-context decode step and,
+in the same JSON line, the 512-token prefill ubatch at depth 198,628
+("prefill"): the metric names both.  --workload picks one workload alone.
+
 Prints one JSON line.  value = microseconds per token per QSA layer (lower is
-better); roofline = the dominant kernel (block scoring) against HBM peak;
-cpu_baseline = the CPU oracle on a bounded sample of the same steps.
+better); step_device_us = per-step device time quantiles (events around
+one-step graph replays); roofline = the kernel that takes the most time in the
+step, against HBM peak, with every kernel's own fraction in roofline.kernels
+and the whole step's in roofline.step; cpu_baseline = the CPU oracle on a
+bounded sample of the same steps, on all host cores (OpenMP over independent
+blocks and heads) and on one.
 """
 from __future__ import annotations
 
@@ -27,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
 N_LAYERS = 12
+METRIC = "QSA sparse-attn decode µs/token and HBM GB/s at 250k ctx; prefill t/s"
 
 
 def parse():
@@ -35,16 +45,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode250k",
-                    choices=["decode50k", "decode250k", "decode5x250k", "prefill", "prefill_ar1"])
+    ap.add_argument("--workload", default=None,
+                    choices=["decode50k", "decode250k", "decode5x250k", "prefill", "prefill_ar1"],
+                    help="one workload alone (default: decode250k plus the prefill ubatch)")
     ap.add_argument("--kv", default="q8_0", choices=["q8_0", "f16"],
                     help="K/V cache type of a decode workload (the workloads are defined "
                          "with q8_0; f16 is the type the pages' first fix required)")
     ap.add_argument("--layers", type=int, default=N_LAYERS)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="budget of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--prefill-steps", type=int, default=16,
+                    help="timed prefill ubatch steps in the default run")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="budget of each CPU-oracle baseline leg (0 = skip)")
     ap.add_argument("--profile", action="store_true",
-                    help="short run for a profiler: no CPU baseline")
+                    help="short run for a profiler: no CPU baseline, no per-step replays")
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of replaying a graph (for "
                          "hardware-counter runs)")
@@ -54,8 +67,42 @@ def parse():
     return ap.parse_args()
 
 
+# ---------------------------------------------------------------------------
+# host and oracle threads
+# ---------------------------------------------------------------------------
+
+def host_info():
+    """CPU model, sockets and the cores this process may use."""
+    model, sockets = None, set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name") and model is None:
+                    model = line.split(":", 1)[1].strip()
+                elif line.startswith("physical id"):
+                    sockets.add(line.split(":", 1)[1].strip())
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cores": aff, "cpu_model": model,
+            "sockets": max(1, len(sockets))}
+
+
+def oracle_threads(host):
+    """All the cores this process may use, within OMP_NUM_THREADS if set."""
+    n = host["usable_cores"] or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+
 def algorithmic_bytes(w, step):
-    """Bytes one layer-step must move at minimum, by kernel."""
+    """Bytes one layer-step must move at minimum, by part of the step."""
     from top_sparse_attention_pooled_amd import synth
     n = w.n_cells0 + (step + 1) * w.n_new
     nc = n // w.r
@@ -64,24 +111,26 @@ def algorithmic_bytes(w, step):
     tail = n - nc * w.r
     n_sel = min(nc, w.top_k // w.r) * w.r + tail
     row = synth.row_bytes(w.kv_type, w.D)
-    score = n_q * (nc * w.d * 4 + nb * 4 + w.d * 4)
     return {
-        "score": score,
+        # pooled keys of the complete blocks, the score row, the query
+        "score": n_q * (nc * w.d * 4 + nb * 4 + w.d * 4),
+        # the dirty block's r per-cell keys in, its f32 and bf16 key out
         "update": w.n_seq * (w.r * w.d * 4 + w.d * 4 + w.d * 2),
-        "select": n_q * (nb * 4 + (w.top_k // w.r + w.ld_cells) * 4),
+        # selection outputs (the candidates it reads are the score kernel's)
+        "select": n_q * ((w.top_k // w.r + w.ld_cells) * 4),
+        # K and V rows of the selected cells, Q in, O out, the cell list
         "attn": n_q * (n_sel * w.Hk * row * 2 + 2 * w.H * w.D * 4 + n_sel * 4),
     }
 
 
-def setup(args, torch, dev):
+def setup(torch, dev, name, K, W, L, kv="q8_0"):
     """Caches of L layer replicas plus the per-step device inputs."""
     from top_sparse_attention_pooled_amd import runtime, synth
-    w = synth.WORKLOADS[args.workload]
-    K, W, L = args.steps, args.warmup, args.layers
-    prefill = args.workload.startswith("prefill")
+    w = synth.WORKLOADS[name]
+    prefill = name.startswith("prefill")
     if not prefill and K + W > w.steps:
         w = synth.Workload(**{**w.__dict__, "steps": K + W})
-    if not prefill and args.kv == "f16":
+    if not prefill and kv == "f16":
         w = synth.Workload(**{**w.__dict__, "kv_type": synth.KV_F16})
     t0 = time.time()
     kidx = synth.make_kidx(w)
@@ -92,7 +141,7 @@ def setup(args, torch, dev):
     base.rebuild(n0)
     layers = [base] + [runtime.Layer.clone_of(base) for _ in range(L - 1)]
     torch.cuda.synchronize()
-    print(f"# inputs ready in {time.time() - t0:.1f}s ({args.workload}, {L} layer replicas)",
+    print(f"# inputs ready in {time.time() - t0:.1f}s ({name}, {L} layer replicas)",
           file=sys.stderr, flush=True)
     # per-step inputs for warmup + timed steps; a prefill step repeats the
     # same ubatch (re-dirtying the same blocks), a decode step appends a token
@@ -113,55 +162,90 @@ def setup(args, torch, dev):
     return w, layers, inp, host
 
 
-def timed_replay(args, torch, stream, enqueue, T, W):
-    """W warm-up then K timed steps, replayed as one HIP graph (or launched
-    directly with --eager); returns seconds for the K steps and the capture
-    helper."""
-    def capture(steps, **kw):
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+class Timer:
+    """HIP-graph capture and replay of a step function on one stream, with
+    HIP events recorded on that stream around the replays (this runtime takes
+    no event nodes inside a captured graph)."""
+
+    def __init__(self, torch, stream, enqueue, eager=False):
+        self.torch, self.stream, self.enqueue, self.eager = torch, stream, enqueue, eager
+
+    def capture(self, steps, **kw):
+        torch = self.torch
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
+        with torch.cuda.graph(g, stream=self.stream):
             for t in steps:
-                enqueue(t, **kw)
+                self.enqueue(t, **kw)
         return g
 
-    if args.eager:
-        with torch.cuda.stream(stream):
-            for t in range(W):
-                enqueue(t)
+    def run(self, W, T):
+        """W warm-up steps, then steps W..T-1 timed as one graph replay (or
+        launched directly when eager).  Returns seconds."""
+        torch = self.torch
+        if self.eager:
+            with torch.cuda.stream(self.stream):
+                for t in range(W):
+                    self.enqueue(t)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(self.stream):
+                for t in range(W, T):
+                    self.enqueue(t)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+        g_warm = self.capture(range(W)) if W > 0 else None
+        g_main = self.capture(range(W, T))
         torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        with torch.cuda.stream(stream):
-            for t in range(W, T):
-                enqueue(t)
+        with torch.cuda.stream(self.stream):
+            if g_warm is not None:
+                g_warm.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g_main.replay()
+            torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def part(self, W, T, n_launches, **kw):
+        """Mean device time of one launch of a part of the step: a graph of
+        just those launches over the timed steps, between two events."""
+        torch = self.torch
+        g = self.capture(range(W, T), **kw)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):  # a graph replays on the current stream
+            g.replay()
+            torch.cuda.synchronize()
+            ev0.record(self.stream)
+            g.replay()
+            ev1.record(self.stream)
         torch.cuda.synchronize()
-        return time.perf_counter() - t_start, capture
-    g_warm = capture(range(W)) if W > 0 else None
-    g_main = capture(range(W, T))
-    torch.cuda.synchronize()
-    if g_warm is not None:
-        g_warm.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    g_main.replay()
-    torch.cuda.synchronize()
-    return time.perf_counter() - t_start, capture
+        return ev0.elapsed_time(ev1) * 1000.0 / n_launches
+
+    def per_step(self, W, T):
+        """Device time of each timed step: one graph per step, replayed back
+        to back with an event between consecutive replays.  Microseconds."""
+        torch = self.torch
+        graphs = [self.capture([t]) for t in range(W, T)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+        with torch.cuda.stream(self.stream):  # a graph replays on the current stream
+            for g in graphs:  # warm every graph once
+                g.replay()
+            torch.cuda.synchronize()
+            evs[0].record(self.stream)
+            for g, e in zip(graphs, evs[1:]):
+                g.replay()
+                e.record(self.stream)
+        torch.cuda.synchronize()
+        return np.array([evs[i].elapsed_time(evs[i + 1]) * 1000.0 for i in range(len(graphs))])
 
 
-def time_part(torch, stream, capture, T, W, n_launches, **kw):
-    """Mean device time of one launch of a part of the step: a graph of just
-    those launches over the timed steps, between two events on the stream
-    (this runtime takes no event nodes inside a captured graph)."""
-    g = capture(range(W, T), **kw)
-    g.replay()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) * 1000.0 / n_launches
+def quantiles(us):
+    return {"median": round(float(np.median(us)), 3), "p10": round(float(np.percentile(us, 10)), 3),
+            "p90": round(float(np.percentile(us, 90)), 3), "n": int(len(us))}
 
 
 def calibration_copy(args, torch, dev):
@@ -175,31 +259,20 @@ def calibration_copy(args, torch, dev):
         del src_buf, dst_buf
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(the QSA step is not sharded across GPUs)", file=sys.stderr)
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
 
-    import torch
-
-    from top_sparse_attention_pooled_amd import qsa
-
-    qsa.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.workload.startswith("prefill"):
-        result = run_prefill(args, torch, dev)
-    else:
-        result = run_decode(args, torch, dev)
-    print(json.dumps(result), flush=True)
+# The decode step's kernels, in launch order, with the part of the step whose
+# algorithmic bytes each one moves.
+DECODE_KERNELS = [("k_score_cand", "score"), ("k_sel_attn", "attn"),
+                  ("k_attn_combine", None)]
 
 
-def run_decode(args, torch, dev):
+def run_decode(args, torch, dev, name):
     from top_sparse_attention_pooled_amd import qsa, runtime, synth
-    w, layers, inp, host = setup(args, torch, dev)
     K, W, L = args.steps, args.warmup, args.layers
+    w, layers, inp, host = setup(torch, dev, name, K, W, L, args.kv)
     T = W + K
     q_idx, q, q_seq, q_pos = inp["q_idx"], inp["q"], inp["q_seq"], inp["q_pos"]
     n_cells, dirty, n_dirty = inp["n_cells"], inp["dirty"], inp["n_dirty"]
@@ -207,29 +280,32 @@ def run_decode(args, torch, dev):
     bufs = [runtime.StepBuffers(layers[0].dims, n_q, nb_max, dev) for _ in range(L)]
     stream = torch.cuda.Stream()
 
-    def enqueue(t, only_score=False):
+    def enqueue(t, part="all"):
         """One decode token through every layer: update + scores + candidates,
         then selection fused into attention (+ the merge of partial states)."""
         for li, layer in enumerate(layers):
             layer.n_cells = n_cells[t]
             bf, d, sq = bufs[li], layer.dims, layer.seqs()
-            qsa.decode_score_candidates(d, sq, layer.kidx, dirty[t], n_dirty, layer.pooled,
-                                        layer.pooled_bf16, q_idx[t], q_seq[t], q_pos[t], n_q,
-                                        nb_max, bf.scores, bf.ld, bf.ws_fused, bf.ws_fused_bytes)
-            if only_score:
-                continue
-            qsa.decode_select_attend(d, sq, q_seq[t], q_pos[t], n_q, nb_max, bf.scores, bf.ld,
-                                     bf.sel_blocks, bf.sel_cells, bf.n_sel, bf.ws_fused,
-                                     bf.ws_fused_bytes, q[t], layer.k, layer.v, bf.out,
-                                     bf.ws_attn, bf.ws_attn_bytes)
+            if part in ("all", "score"):
+                qsa.decode_score_candidates(d, sq, layer.kidx, dirty[t], n_dirty, layer.pooled,
+                                            layer.pooled_bf16, q_idx[t], q_seq[t], q_pos[t],
+                                            n_q, nb_max, bf.scores, bf.ld, bf.ws_fused,
+                                            bf.ws_fused_bytes)
+            if part in ("all", "select_attend"):
+                qsa.decode_select_attend(d, sq, q_seq[t], q_pos[t], n_q, nb_max, bf.scores,
+                                         bf.ld, bf.sel_blocks, bf.sel_cells, bf.n_sel,
+                                         bf.ws_fused, bf.ws_fused_bytes, q[t], layer.k, layer.v,
+                                         bf.out, bf.ws_attn, bf.ws_attn_bytes)
 
     calibration_copy(args, torch, dev)
-    t_main, capture = timed_replay(args, torch, stream, enqueue, T, W)
-    # live timing of the dominant kernel with HIP events on its stream
-    score_us, timing = None, "eager run: not timed"
+    timer = Timer(torch, stream, enqueue, args.eager)
+    t_main = timer.run(W, T)
+    parts, steps_us = {}, None
     if not args.eager:
-        timing = "events around a graph of the K*L scoring launches alone"
-        score_us = time_part(torch, stream, capture, T, W, K * L, only_score=True)
+        for part in ("score", "select_attend"):
+            parts[part] = timer.part(W, T, K * L, part=part)
+        if not args.profile:
+            steps_us = timer.per_step(W, T) / L
 
     # correctness guard on the last step of layer 0 (selection sizes)
     n_sel = bufs[0].n_sel.cpu().numpy()
@@ -239,11 +315,27 @@ def run_decode(args, torch, dev):
     us_per_step_layer = ms_per_step * 1000.0 / L
     us_per_token_layer = us_per_step_layer / n_q  # n_q tokens per step (one per session)
     ab = [algorithmic_bytes(w, t) for t in range(W, T)]
-    score_bytes = float(np.mean([a["score"] for a in ab]))
-    step_bytes = float(np.mean([sum(a.values()) for a in ab]))
-    achieved = score_bytes / (score_us * 1e-6) / 1e9 if score_us else None
+    mean_b = {k: float(np.mean([a[k] for a in ab])) for k in ab[0]}
+    step_bytes = sum(mean_b.values())
+
+    # per-kernel fractions: the scoring launch timed alone; the selection +
+    # attention call holds two launches whose split comes from the kernel
+    # trace, so its fraction is that of the call
+    kernels = []
+    if parts:
+        kernels.append({"kernel": "k_score_cand", "avg_launch_us": round(parts["score"], 3),
+                        "bytes_per_launch": round(mean_b["score"] + mean_b["update"]),
+                        "frac": round((mean_b["score"] + mean_b["update"]) /
+                                      (parts["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        kernels.append({"kernel": "k_sel_attn + k_attn_combine (one call)",
+                        "avg_launch_us": round(parts["select_attend"], 3),
+                        "bytes_per_launch": round(mean_b["attn"] + mean_b["select"]),
+                        "frac": round((mean_b["attn"] + mean_b["select"]) /
+                                      (parts["select_attend"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    dom = max(kernels, key=lambda k: k["avg_launch_us"]) if kernels else None
+    step_frac = step_bytes / (us_per_step_layer * 1e-6) / 1e9 / HBM_PEAK_GBS
     result = {
-        "metric": "QSA sparse-attn decode \u00b5s/token and HBM GB/s at 250k ctx; prefill t/s",
+        "metric": METRIC,
         "value": round(us_per_token_layer, 3),
         "unit": "us/token",
         "n_gpus": 1,
@@ -257,7 +349,7 @@ def run_decode(args, torch, dev):
         "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (%s), seeded"
                 % {synth.KV_Q8_0: "q8_0-packed", synth.KV_F16: "rounded to f16"}.get(w.kv_type, "f32"),
         "config": {
-            "workload": args.workload if args.kv == "q8_0" else f"{args.workload} (f16 KV)",
+            "workload": name if args.kv == "q8_0" else f"{name} (f16 KV)",
             "n_seq": w.n_seq, "n_kv_start": w.n_cells0 + w.n_new, "decode_steps": K,
             "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
             "compress_ratio": w.r, "top_k": w.top_k,
@@ -265,32 +357,43 @@ def run_decode(args, torch, dev):
         },
         "tokens_per_s_per_layer": round(1e6 / us_per_token_layer, 1),
         "us_per_step_layer": round(us_per_step_layer, 3),
+        "step_device_us": quantiles(steps_us) if steps_us is not None else None,
         "step_hbm_gbps": round(step_bytes / (us_per_step_layer * 1e-6) / 1e9, 1),
         "roofline": {
-            "kernel": "k_score_cand",
-            "timing": timing,
+            "kernel": dom["kernel"] if dom else None,
+            "timing": "events around a graph of the K*L launches of that part alone",
             "bound": "hbm",
-            "achieved": round(achieved, 1) if achieved else None,
+            "achieved": round(dom["bytes_per_launch"] / (dom["avg_launch_us"] * 1e-6) / 1e9, 1)
+            if dom else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-            "traffic": recorded_traffic(args.workload),
-            "bytes_per_launch": round(score_bytes),
-            "avg_launch_us": round(score_us, 3) if score_us else None,
+            "frac": dom["frac"] if dom else None,
+            "traffic": recorded_traffic(name) if dom and dom["kernel"] == "k_score_cand" else None,
+            "bytes_per_launch": dom["bytes_per_launch"] if dom else None,
+            "avg_launch_us": dom["avg_launch_us"] if dom else None,
+            "kernels": kernels,
+            "step": {"bytes": round(step_bytes), "us": round(us_per_step_layer, 3),
+                     "achieved": round(step_bytes / (us_per_step_layer * 1e-6) / 1e9, 1),
+                     "frac": round(step_frac, 4)},
         },
     }
     if not args.profile and args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, host, W, K, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_decode(w, host, W, K, args.cpu_seconds)
+    del layers, bufs, inp
     return result
 
 
-def run_prefill(args, torch, dev):
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def run_prefill(args, torch, dev, name, K, W):
     """One step = the 512-token ubatch at depth 198,628 through every layer:
     pooled-key update of its 128 dirty blocks, bf16 MFMA block scores,
     per-query exact block top-k, sparse attention per query."""
     from top_sparse_attention_pooled_amd import qsa, runtime, synth
-    w, layers, inp, host = setup(args, torch, dev)
-    K, W, L = args.steps, args.warmup, args.layers
+    L = args.layers
+    w, layers, inp, host = setup(torch, dev, name, K, W, L)
     T = W + K
     q_idx, q, q_seq, q_pos = inp["q_idx"], inp["q"], inp["q_seq"], inp["q_pos"]
     n_cells, dirty, n_dirty = inp["n_cells"], inp["dirty"], inp["n_dirty"]
@@ -315,11 +418,14 @@ def run_prefill(args, torch, dev):
                                         bf.ws_attn_bytes)
 
     calibration_copy(args, torch, dev)
-    t_main, capture = timed_replay(args, torch, stream, enqueue, T, W)
-    parts = {}
+    timer = Timer(torch, stream, enqueue, args.eager)
+    t_main = timer.run(W, T)
+    parts, steps_us = {}, None
     if not args.eager:
         for part in ("indexer", "attn"):
-            parts[part] = time_part(torch, stream, capture, T, W, K * L, part=part)
+            parts[part] = timer.part(W, T, K * L, part=part)
+        if not args.profile:
+            steps_us = timer.per_step(W, T) / L
     n_sel = bufs[0].n_sel.cpu().numpy()
     assert np.all(n_sel > 0), "empty selections in the benchmark step"
 
@@ -328,52 +434,46 @@ def run_prefill(args, torch, dev):
     pos = host["qp"][0]
     nc = (pos.astype(np.int64) + 1) // w.r
     flops = float(np.sum(nc)) * w.d * 2  # the dense query x block-key contraction
-    score_us = parts.get("indexer")
+    n_sel_np = n_sel.astype(np.int64)
+    attn_flops = float(np.sum(n_sel_np)) * w.H * w.D * 4  # QK and PV over the lists
+    score_us, attn_us = parts.get("indexer"), parts.get("attn")
     tflops = flops / (score_us * 1e-6) / 1e12 if score_us else None
-    result = {
-        "metric": "QSA sparse-attn decode \u00b5s/token and HBM GB/s at 250k ctx; prefill t/s",
-        "value": round(n_q / (us_per_layer * 1e-6), 1),
-        "unit": "t/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16 indexer (fp32 accumulate), f32 attention over q8_0 KV",
-        "data": ("synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded"
-                 + ("; indexer queries AR(1) along the tokens, rho %g" % w.extra["qidx_ar1"]
-                    if w.extra.get("qidx_ar1") else "")),
+    attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12 if attn_us else None
+    res = {
+        "t_s_per_layer": round(n_q / (us_per_layer * 1e-6), 1),
+        "us_per_layer": round(us_per_layer, 2),
+        "model_prefill_t_s": round(n_q / (ms_per_step * 1e-3), 1),
+        "steps": K, "warmup": W,
+        "step_device_us": quantiles(steps_us) if steps_us is not None else None,
+        "parts_us": {k: round(v, 2) for k, v in parts.items()},
+        "indexer_mfma": {"flops_per_launch": flops,
+                         "achieved_tflops": round(tflops, 2) if tflops else None,
+                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if tflops else None},
+        "attn_mfma": {"flops_per_launch": attn_flops,
+                      "achieved_tflops": round(attn_tflops, 2) if attn_tflops else None,
+                      "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
+                      "frac": round(attn_tflops / MFMA_FP16_PEAK_TFLOPS, 4) if attn_tflops else None},
         "config": {
-            "workload": args.workload, "n_seq": 1, "n_kv_start": w.n_cells0, "ubatch": n_q,
+            "workload": name, "n_seq": 1, "n_kv_start": w.n_cells0, "ubatch": n_q,
             "dirty_blocks": int(np.sum(host["dl_all"][0][:, 0] >= 0)),
             "q_heads": w.H, "kv_heads": w.Hk, "head_dim": w.D, "indexer_dim": w.d,
             "compress_ratio": w.r, "top_k": w.top_k, "layers_per_step": L,
             "graph_replay": not args.eager,
         },
-        "us_per_layer": round(us_per_layer, 2),
-        "model_prefill_t_s": round(n_q / (ms_per_step * 1e-3), 1),
-        "parts_us": {k: round(v, 2) for k, v in parts.items()},
-        "roofline": {
-            "kernel": "qsa_score_select_prefill (update, rope, two MFMA passes: subgroup maxima, "
-                      "then masks at tau - 2 Delta; exact rescoring of the masked blocks), priced "
-                      "on the dense contraction once",
-            "timing": "events around a graph of the K*L indexer calls alone",
-            "bound": "mfma",
-            "achieved": round(tflops, 2) if tflops else None,
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if tflops else None,
-            "traffic": None,
-            "flops_per_launch": flops,
-            "avg_launch_us": round(score_us, 3) if score_us else None,
-        },
+        "data": ("synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded"
+                 + ("; indexer queries AR(1) along the tokens, rho %g" % w.extra["qidx_ar1"]
+                    if w.extra.get("qidx_ar1") else "")),
     }
     if not args.profile and args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline_prefill(w, host, args.cpu_seconds)
-    return result
+        res["cpu_baseline"] = cpu_baseline_prefill(w, host, args.cpu_seconds)
+    del layers, bufs, inp
+    return res, ms_per_step, w
 
+
+# ---------------------------------------------------------------------------
+# counters and the CPU baseline
+# ---------------------------------------------------------------------------
 
 def recorded_traffic(workload):
     """HBM-side bytes per scoring launch from the committed counter summary
@@ -390,10 +490,12 @@ def recorded_traffic(workload):
     return round(rec["traffic_bytes"])
 
 
-def cpu_baseline(w, host, W, K, budget):
-    """The oracle as it stands, single-threaded, on the first decode steps of
-    the same workload (one layer): update, score, select, attend per step."""
+def _decode_oracle_leg(w, host, W, K, budget, threads):
+    """The oracle's decode steps (one layer): per step the pooled-key update,
+    then scores, full-sort selection and fp64 attention.  Returns (us per
+    token, steps done)."""
     import oracle
+    oracle.set_threads(threads)
     kidx, k, v = host["kidx"], host["k"], host["v"]
     pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
     n0 = np.full(w.n_seq, w.n_cells0, np.int32)
@@ -411,18 +513,37 @@ def cpu_baseline(w, host, W, K, budget):
         done += 1
         if spent > budget:
             break
-    us = spent / done * 1e6
-    return {"value": round(us, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} decode steps of one layer of {w.name} "
-                      f"({w.n_seq} seq), update+score+select+attend, fp32/fp64 C oracle, "
-                      f"1 thread", "tokens_per_s": round(1e6 / us, 2)}
+    oracle.set_threads(1)
+    n_q = w.n_seq * w.n_new
+    return spent / done / n_q * 1e6, done
+
+
+def cpu_baseline_decode(w, host, W, K, budget):
+    """The oracle as it stands on the first decode steps of the same workload
+    (one layer): on all usable host cores (OpenMP over the blocks of a score
+    row, the heads of an attention call and the dirty entries of an update;
+    each iteration's arithmetic and order unchanged), then on one thread."""
+    hi = host_info()
+    n = oracle_threads(hi)
+    us_n, done_n = _decode_oracle_leg(w, host, W, K, budget, n)
+    us_1, done_1 = _decode_oracle_leg(w, host, W, K, budget, 1)
+    return {"value": round(us_n, 1), "unit": "us/token", "cores": n, "kind": "oracle",
+            "sample": f"first {done_n} decode steps of one layer of {w.name} ({w.n_seq} seq), "
+                      f"update+score+select+attend, fp32/fp64 C oracle, {n} OpenMP threads",
+            "tokens_per_s": round(1e6 / us_n, 2),
+            "single_thread": {"value": round(us_1, 1), "unit": "us/token", "cores": 1,
+                              "sample": f"first {done_1} decode steps, 1 thread"},
+            "host": hi}
 
 
 def cpu_baseline_prefill(w, host, budget):
-    """The oracle, single-threaded, on one layer: the ubatch's pooled-key
-    update, then bf16 scores, selection and attention for as many of its
-    queries as the budget allows; reported per query token."""
+    """The oracle on one layer: the ubatch's pooled-key update, then bf16
+    scores, selection and attention for as many of its queries as the budget
+    allows, on all usable host cores; reported per query token."""
     import oracle
+    hi = host_info()
+    n = oracle_threads(hi)
+    oracle.set_threads(n)
     kidx, k, v = host["kidx"], host["k"], host["v"]
     pooled = np.zeros((w.n_seq, w.cap_blocks, w.d), np.float32)
     n0 = np.full(w.n_seq, w.n_cells0, np.int32)
@@ -443,11 +564,64 @@ def cpu_baseline_prefill(w, host, budget):
         done += 1
         if spent > budget:
             break
+    oracle.set_threads(1)
     per_tok = spent / done + t_update / qp.shape[0]
-    return {"value": round(1.0 / per_tok, 2), "unit": "t/s", "cores": 1, "kind": "oracle",
+    return {"value": round(1.0 / per_tok, 2), "unit": "t/s", "cores": n, "kind": "oracle",
             "sample": f"one layer of the prefill ubatch: its 128-block update, then {done} of "
                       f"{qp.shape[0]} queries (bf16 scores, selection, attention), fp32/fp64 C "
-                      f"oracle, 1 thread"}
+                      f"oracle, {n} OpenMP threads", "host": hi}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the QSA step is not sharded across GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from top_sparse_attention_pooled_amd import qsa
+
+    qsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    if name is None:  # the headline decode line, with the prefill ubatch in it
+        result = run_decode(args, torch, dev, "decode250k")
+        torch.cuda.empty_cache()
+        pf, _, _ = run_prefill(args, torch, dev, "prefill", args.prefill_steps, 2)
+        result["prefill_t_s"] = pf["t_s_per_layer"]
+        result["prefill"] = pf
+    elif name.startswith("prefill"):
+        pf, ms_per_step, w = run_prefill(args, torch, dev, name, args.steps, args.warmup)
+        result = {
+            "metric": METRIC, "value": pf["t_s_per_layer"], "unit": "t/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16 indexer (fp32 accumulate), fp16 attention operands over q8_0 KV "
+                     "(fp32 accumulate)",
+            "data": pf.pop("data"), "config": pf.pop("config"),
+            "roofline": {
+                "kernel": "qsa_score_select_prefill (its launches together), priced on the "
+                          "dense query x block-key contraction",
+                "timing": "events around a graph of the K*L indexer calls alone",
+                "bound": "mfma",
+                "achieved": pf["indexer_mfma"]["achieved_tflops"],
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": pf["indexer_mfma"]["frac"], "traffic": None,
+                "flops_per_launch": pf["indexer_mfma"]["flops_per_launch"],
+                "avg_launch_us": pf["parts_us"].get("indexer"),
+            },
+            "prefill": pf,
+        }
+        if "cpu_baseline" in pf:
+            result["cpu_baseline"] = pf.pop("cpu_baseline")
+    else:
+        result = run_decode(args, torch, dev, name)
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

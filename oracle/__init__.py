@@ -48,7 +48,7 @@ _SRC = os.path.join(_HERE, "qsa_oracle.c")
 _LIB = os.path.join(_HERE, "libqsa_oracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-          "-fno-fast-math", "-fno-unsafe-math-optimizations", "-Wall"]
+          "-fno-fast-math", "-fno-unsafe-math-optimizations", "-fopenmp", "-Wall"]
 
 
 def build() -> str:
@@ -77,6 +77,7 @@ def _load():
     i64, i32, f32, f64, vp = (ctypes.c_int64, ctypes.c_int, ctypes.c_float,
                               ctypes.c_double, ctypes.c_void_p)
     sig = {
+        "qo_set_threads": (i32, [i32]),
         "qo_half_to_float": (f32, [ctypes.c_uint16]),
         "qo_round_bf16": (f32, [f32]),
         "qo_tree_sum": (f32, [_f32p, i32]),
@@ -123,6 +124,13 @@ def _check(rc, what):
 # --------------------------------------------------------------------------
 # scalars and building blocks
 # --------------------------------------------------------------------------
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops (update entries, score blocks,
+    attention heads); returns the count in force.  Results do not depend on
+    it: each iteration runs the single-threaded arithmetic in its order."""
+    return int(_load().qo_set_threads(int(n)))
+
 
 def half_to_float(bits: int) -> float:
     return float(_load().qo_half_to_float(int(bits)))

@@ -28,13 +28,44 @@
  *   - The score is a plain dot product of the roped query and the pooled key.
  *   - The incomplete tail block is never scored; its cells are always kept.
  *   - Ties in the block ranking go to the lower block index; -0 equals +0.
+ *
+ * Threads.  Built with OpenMP, three loops run their independent iterations
+ * on several threads: the dirty entries of a pooled-key update, the blocks of
+ * a score row and the heads of an attention call.  Each iteration computes
+ * what it computes single-threaded, in the same order, so results do not
+ * depend on the thread count (qo_set_threads; 1 by default).
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define QO_MAX_D 1024
+
+/* ------------------------------------------------------------------------ */
+/* Threads                                                                   */
+/* ------------------------------------------------------------------------ */
+
+static int qo_threads = 1;
+
+/* Threads the parallel loops use (n >= 1; capped by what OpenMP offers).
+ * Returns the count now in force: 1 when built without OpenMP. */
+int qo_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n < 1)
+        n = 1;
+    int mx = omp_get_num_procs();
+    qo_threads = n < mx ? n : mx;
+#else
+    (void)n;
+    qo_threads = 1;
+#endif
+    return qo_threads;
+}
 
 /* ------------------------------------------------------------------------ */
 /* Scalars                                                                   */
@@ -218,6 +249,9 @@ int qo_update_pooled(const float *kidx, int64_t cap_cells, const int32_t *n_cell
                      double theta, const int32_t *dirty, int n_dirty,
                      float *pooled, int64_t cap_blocks)
 {
+    int err = 0;
+    /* (a block listed twice is written twice with the same value) */
+#pragma omp parallel for num_threads(qo_threads) schedule(static) reduction(| : err)
     for (int i = 0; i < n_dirty; i++) {
         int32_t s = dirty[2 * i], b = dirty[2 * i + 1];
         if (s < 0 || s >= n_seq || b < 0 || b >= cap_blocks)
@@ -225,13 +259,11 @@ int qo_update_pooled(const float *kidx, int64_t cap_cells, const int32_t *n_cell
         int64_t nc = n_cells[s];
         if ((int64_t)b * r >= nc)
             continue;
-        int rc = qo_block_key(kidx + (size_t)s * cap_cells * d, nc, d, r, eps,
-                              gamma, theta, b,
-                              pooled + ((size_t)s * cap_blocks + b) * d);
-        if (rc)
-            return rc;
+        if (qo_block_key(kidx + (size_t)s * cap_cells * d, nc, d, r, eps, gamma,
+                         theta, b, pooled + ((size_t)s * cap_blocks + b) * d))
+            err = 1;
     }
-    return 0;
+    return err ? -1 : 0;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -249,7 +281,7 @@ int qo_score_query(const float *q_idx, int d, int64_t pos, double theta, int r,
                    const float *pooled, int64_t nb_avail, int64_t nb_out,
                    int bf16, float *scores)
 {
-    float qr[QO_MAX_D], k[QO_MAX_D];
+    float qr[QO_MAX_D];
     if (qo_rope(q_idx, d, pos, theta, qr))
         return -1;
     if (bf16)
@@ -258,7 +290,9 @@ int qo_score_query(const float *q_idx, int d, int64_t pos, double theta, int r,
     int64_t nc = qo_complete_blocks(pos, r);
     if (nc > nb_avail)
         return -1;
+#pragma omp parallel for num_threads(qo_threads) schedule(static)
     for (int64_t b = 0; b < nb_out; b++) {
+        float k[QO_MAX_D];
         if (b >= nc) {
             scores[b] = -INFINITY;
             continue;
@@ -429,12 +463,16 @@ int qo_attend(const float *q, int H, int Hk, int D, const void *k_cache,
         return -1;
     int G = H / Hk;
     double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)D);
-    double *lg = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-    double acc[QO_MAX_D];
-    float kr[QO_MAX_D], vr[QO_MAX_D];
-    if (!lg)
-        return -1;
+    int err = 0;
+#pragma omp parallel for num_threads(qo_threads) schedule(static) reduction(| : err)
     for (int h = 0; h < H; h++) {
+        double acc[QO_MAX_D];
+        float kr[QO_MAX_D], vr[QO_MAX_D];
+        double *lg = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        if (!lg) {
+            err = 1;
+            continue;
+        }
         int kvh = h / G;
         const float *qh = q + (size_t)h * D;
         double mx = -INFINITY;
@@ -459,9 +497,9 @@ int qo_attend(const float *q, int H, int Hk, int D, const void *k_cache,
         }
         for (int t = 0; t < D; t++)
             out[(size_t)h * D + t] = n > 0 ? (float)(acc[t] / den) : 0.0f;
+        free(lg);
     }
-    free(lg);
-    return 0;
+    return err ? -1 : 0;
 }
 
 /* The pages' slow form: dense causal attention over every cell 0..pos with

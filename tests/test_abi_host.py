@@ -106,6 +106,10 @@ def test_bad_geometry_and_pointers_rejected():
         # ld below nb_max
         lambda: qsa.select_topk_blocks(d, _seqs(), FAKE, 10, FAKE, FAKE, 1, 64, FAKE, FAKE, FAKE,
                                        stream=0),
+        # a score row is required whenever blocks compete (nb_max > 0); with
+        # nb_max = 0 the row is never read and may be NULL (GPU test)
+        lambda: qsa.select_topk_blocks(d, _seqs(), None, 64, FAKE, FAKE, 1, 64, FAKE, FAKE,
+                                       FAKE, stream=0),
         # unknown score mode
         lambda: qsa.score_blocks(d, _seqs(), FAKE, FAKE, FAKE, 1, FAKE, FAKE, 64, FAKE, 64,
                                  mode=5, stream=0),

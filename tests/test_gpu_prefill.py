@@ -120,28 +120,51 @@ def test_prefill_selection_all_tied_rescoring_every_block():
 
 
 @pytest.mark.parametrize("name", ["prefill", "prefill_ar1"])
-def test_prefill_selection_ubatch_at_depth(name):
-    """The 512-token ubatch at depth 198,628 (128 dirty blocks), oracle-checked
-    on queries spread over the ubatch; also with AR(1) indexer queries (rho
-    0.9), whose neighbouring tokens select overlapping blocks."""
+def test_prefill_ubatch_at_depth(name):
+    """The benchmarked prefill step: the 512-token ubatch at depth 198,628
+    (128 dirty blocks), top_k 2048, q8_0 K/V.  All 512 selections against the
+    oracle bit for bit; then qsa_sparse_attn_prefill over those lists, its
+    outputs against the oracle's fp64 attention for 65 queries spread over the
+    ubatch.  Also with AR(1) indexer queries (rho 0.9, selections only),
+    whose neighbouring tokens select overlapping blocks."""
     w = synth.WORKLOADS[name]
-    say(f"{name} select: 512-token ubatch at 198,628 (oracle on 24 queries)")
+    full = name == "prefill"
+    say(f"{name}: 512-token ubatch at 198,628, all selections"
+        + (", attention on 65 queries" if full else ""))
     kidx = synth.make_kidx(w)
-    layer = runtime.Layer(w, DEV, kidx=kidx, k=np.zeros((1, 1, 1, 1), np.uint8),
-                          v=np.zeros((1, 1, 1, 1), np.uint8))
+    if full:
+        k, v = synth.make_kv(w, synth.T_K), synth.make_kv(w, synth.T_V)
+    else:
+        k = v = np.zeros((1, 1, 1, 1), np.uint8)
+    layer = runtime.Layer(w, DEV, kidx=kidx, k=k, v=v)
     layer.rebuild(np.full(1, w.n_cells0, np.int32))
     n = synth.n_cells_at(w, 0)
     layer.set_n_cells(n)
     dirty = synth.dirty_blocks(w, 0)
     assert int((dirty[:, 0] >= 0).sum()) == 128
-    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    q_idx, q, q_seq, q_pos = synth.make_queries(w, 0)
     nb_max = w.nb_max(0)
     bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max, dirty)
     ref_pooled = oracle_pooled(w, kidx, n)
-    which = list(range(0, 512, 23)) + [511]
-    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, which)
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, range(q_pos.size))
     gn = bufs.n_sel.cpu().numpy()
     assert np.all(gn <= w.top_k + w.r - 1)
+    assert np.all(gn >= w.top_k)  # every query sees more than top_k complete cells
+    if not full:
+        return
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    qsa.sparse_attn_prefill(layer.dims, layer.seqs(), t(q), t(q_seq), q_pos.size, layer.k,
+                            layer.v, bufs.sel_cells, bufs.n_sel, bufs.out, bufs.ws_attn,
+                            bufs.ws_attn_bytes)
+    torch.cuda.synchronize()
+    go = bufs.out.cpu().numpy()
+    gc = bufs.sel_cells.cpu().numpy()
+    worst = 0.0
+    for i in list(range(0, 512, 8)) + [511]:
+        r = oracle.attend(q[i], k[0], v[0], w.kv_type, gc[i, :gn[i]], w.Hk)
+        worst = max(worst, float(np.abs(go[i] - r).max()))
+    say(f"  attention on 65 queries: worst max-abs error {worst:.2e}")
+    assert worst <= 2e-3
 
 
 def test_prefill_selection_extreme_query_norms():

@@ -652,3 +652,37 @@ def test_dirty_blocks_moved_cell_marks_its_block_only():
     rows[0][3], rows[0][2] = rows[0][2], rows[0][3]  # two cells of block 0 swap rows
     d, _ = oracle.dirty_blocks(rows, [40, 40], snap, r)
     assert d == [(0, 0), (1, 5)]
+
+
+# --------------------------------------------------------------------------
+# threads
+# --------------------------------------------------------------------------
+
+def test_threaded_oracle_is_bit_identical_to_one_thread():
+    """The parallel loops (update entries, score blocks, attention heads) give
+    the single-threaded results bit for bit: each iteration keeps its order."""
+    rng = np.random.default_rng(41)
+    d, r, cap, H, Hk = 128, 4, 4096, 16, 2
+    kidx = rng.standard_normal((2, cap, d)).astype(np.float32)
+    n_cells = np.array([4000, 3001], np.int32)
+    pairs = np.array([(s, b) for s in range(2) for b in range(-(-int(n_cells[s]) // r))],
+                     np.int32)
+    w = synth.Workload("thr", 41, 1, 3000, H=H, Hk=Hk)
+    k = synth.make_kv(w, synth.T_K)[0]
+    v = synth.make_kv(w, synth.T_V)[0]
+    q = rng.standard_normal((H, 256)).astype(np.float32)
+    q_idx = rng.standard_normal(d).astype(np.float32)
+    cells = np.sort(rng.choice(3001, size=2051, replace=False)).astype(np.int32)
+    outs = []
+    for n_threads in (1, 8):
+        got = oracle.set_threads(n_threads)
+        assert got >= 1 and (n_threads == 1) == (got == 1) or os.cpu_count() == 1
+        pooled = np.zeros((2, cap // r, d), np.float32)
+        oracle.update_pooled(kidx, n_cells, pairs, pooled, r, THETA, EPS)
+        sc = oracle.score_query(q_idx, 3999, pooled[0], 1000, r, THETA)
+        sb = oracle.score_query(q_idx, 3999, pooled[0], 1000, r, THETA, bf16=True)
+        at = oracle.attend(q, k, v, synth.KV_Q8_0, cells, Hk)
+        outs.append((pooled, sc, sb, at))
+    oracle.set_threads(1)
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

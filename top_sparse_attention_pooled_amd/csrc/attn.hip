@@ -376,6 +376,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int hpk = a.n_head / a.n_head_kv;
     const int g = (hg * G) / hpk;
     const int h0 = hg * G;
+    QSA_STAMP(0);
     float qv[G][8];
     load_q<G>(a, i, h0, j, qv);
 
@@ -393,6 +394,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     Thresh th;
     const bool fast =
         select_candidates<kSelAttnNT, kSelAttnMaxBlocks, true>(f, i, limit, B, ss, ck, th);
+    QSA_STAMP(2);
 
     // List positions [c_begin, c_begin + 32): the kept blocks of ascending
     // rank [k_lo, k_hi] (block k covers positions k*r .. k*r + r-1), then
@@ -491,6 +493,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
         n_keep_all = n_keep;
     }
     const int n_sel = n_keep_all * r + tail;
+    QSA_STAMP(3);
     int cell[kCPG];
 #pragma unroll
     for (int u = 0; u < kCPG; ++u) cell[u] = s_cells[grp * kCPG + u];
@@ -518,6 +521,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
                                      f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i,
                                      ss.tk);
     }
+    QSA_STAMP(4);
 }
 
 constexpr int kCombNT = 256;
@@ -542,6 +546,7 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
     __shared__ float s_l[kCombMaxRuns];
     __shared__ float s_red[kCombWaves];
     __shared__ float s_acc[kCombWaves][kWave];
+    QSA_STAMP(5);
     const int h = blockIdx.x / kCombSlices, slice = blockIdx.x % kCombSlices;
     const int i = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int hg = h / G, hh = h % G;
@@ -606,6 +611,7 @@ __global__ __launch_bounds__(kCombNT) void k_attn_combine(AttnArgs a, int n_runs
         const float t = (s_acc[0][lane] + s_acc[1][lane]) + (s_acc[2][lane] + s_acc[3][lane]);
         a.out[((int64_t)i * a.n_head + h) * kHeadDim + slice * kWave + lane] = L > 0.f ? t / L : 0.f;
     }
+    QSA_STAMP(6);
 }
 
 template <int G, int KVT>
@@ -665,6 +671,8 @@ hipError_t launch_sel_kvt(const DecodeIdxArgs &f, const AttnArgs &a, hipStream_t
 }
 
 }  // namespace
+
+QSA_STAMP_READER(attn)
 
 size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells) {
     // per (query, run, head group): G*256 + 2G floats; over the head groups

@@ -32,6 +32,47 @@ constexpr int kQ8Bytes = 34;
 constexpr int kQ8Row = kHeadDim / 32 * kQ8Bytes;  // 272 bytes
 
 // ---------------------------------------------------------------------------
+// Phase stamps: a measurement build option (QSA_STAMPS, off by default).
+// Thread 0 of a workgroup records the 100 MHz real-time clock at numbered
+// points of a kernel; the last slot holds the XCD the workgroup ran on.  Each
+// translation unit keeps its own table, read and cleared through
+// qsa_stamps_<unit> (exported by stamp builds only).  Without the option the
+// macros expand to nothing.
+// ---------------------------------------------------------------------------
+#ifdef QSA_STAMPS
+constexpr int kStampWgs = 4096;
+constexpr int kStampSlots = 8;
+static __device__ uint64_t g_stamps[kStampWgs][kStampSlots];
+__device__ __forceinline__ void stamp_at(int slot) {
+    const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if (threadIdx.x == 0 && wg < (uint32_t)kStampWgs) {
+        g_stamps[wg][slot] = __builtin_amdgcn_s_memrealtime();
+        if (slot == 0) {
+            uint32_t xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            g_stamps[wg][kStampSlots - 1] = xcc;
+        }
+    }
+}
+#define QSA_STAMP(slot) ::qsa::stamp_at(slot)
+#define QSA_STAMP_READER(unit)                                                            \
+    extern "C" int qsa_stamps_##unit(void *dst, int clear) {                              \
+        hipError_t e = hipSuccess;                                                        \
+        if (dst)                                                                          \
+            e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(::qsa::g_stamps),                     \
+                                    sizeof(::qsa::g_stamps));                             \
+        if (e == hipSuccess && clear) {                                                   \
+            static uint64_t zero[::qsa::kStampWgs][::qsa::kStampSlots];                   \
+            e = hipMemcpyToSymbol(HIP_SYMBOL(::qsa::g_stamps), zero, sizeof(zero));       \
+        }                                                                                 \
+        return (int)e;                                                                    \
+    }
+#else
+#define QSA_STAMP(slot) ((void)0)
+#define QSA_STAMP_READER(unit)
+#endif
+
+// ---------------------------------------------------------------------------
 // Scalar helpers
 // ---------------------------------------------------------------------------
 

@@ -111,6 +111,16 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a) {
 // decode indexer step: update + scoring + candidates, then exact selection
 // ---------------------------------------------------------------------------
 
+// A 16-byte load of data read exactly once (the pooled-key stream): marked
+// non-temporal so it does not displace what the L2 holds for the next
+// kernels -- the candidates, and the selection kernel's instructions, which
+// would otherwise come back from memory one cache line at a time.
+__device__ __forceinline__ float4 load_stream(const float4 *p) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 constexpr int kSelNT = 1024;  // selection workgroup
 
 // Descending bitonic sort of one 64-bit key per lane across a wavefront.
@@ -173,6 +183,7 @@ __device__ __forceinline__ uint64_t group_sort_by_block(uint64_t key, int n) {
 // wavefront's quad-w partial then meets the others in LDS for level 8 (quad
 // w with w + 2), level 4 (0 with 1) and the two levels inside the quad.
 __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
+    QSA_STAMP(0);
     __shared__ float4 qr4[kQuads];
     __shared__ float4 patch[kQuads];
     __shared__ float4 part[4][kTile];  // quad-w partial of each block
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
                                                 : 0)) + lane;
     float4 k[8];  // quads wave + 4m of block b
 #pragma unroll
-    for (int m = 0; m < 8; ++m) k[m] = src[(wave + 4 * m) * kTile];
+    for (int m = 0; m < 8; ++m) k[m] = load_stream(src + (wave + 4 * m) * kTile);
     // (unconditional, clamped loads: a load under a lane condition would be
     // waited for, with the keys, right after it)
     const int32_t *dl = f.n_dirty > 0 ? f.dirty : a.q_seq;
@@ -307,6 +318,7 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
         part[wave][lane] = v[0];
     }
     __syncthreads();
+    QSA_STAMP(2);  // (slot 1 is the selection engine's)
     if (wave != 0) return;
     float sc = -INFINITY;
     if (live && b < nc) {
@@ -330,6 +342,7 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     // candidates of all groups, read in order, ascend by block
     key = group_sort_by_block(key, f.n_cand);
     if (lane < f.n_cand) f.cand[grp * f.n_cand + lane] = key;
+    QSA_STAMP(3);
 }
 
 // grid (n_q), 1024 threads: the exact selection from the candidates, then
@@ -482,6 +495,8 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs a, const uint16_t 
 }
 
 }  // namespace
+
+QSA_STAMP_READER(score)
 
 size_t fused_select_ws_bytes(int n_q, int nb_max) { return cand_ws_bytes(n_q, nb_max); }
 

@@ -91,11 +91,16 @@ __global__ __launch_bounds__(kNT) void k_select(SelectArgs a) {
     src.mem = RowStream{row, limit};
     src.in_regs = limit <= (int64_t)kNT * kC;
     if (src.in_regs) {
+        // (limit == 0 reads nothing: the score row may then be absent, NULL)
 #pragma unroll
-        for (int s2 = 0; s2 < kC; ++s2) {
-            const int64_t b = (int64_t)s2 * kNT + tid;
-            const float sc = row[b < limit ? b : 0];  // unconditional: no wait per load
-            src.regs.k[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
+        for (int s2 = 0; s2 < kC; ++s2) src.regs.k[s2] = 0u;
+        if (limit > 0) {  // workgroup-uniform
+#pragma unroll
+            for (int s2 = 0; s2 < kC; ++s2) {
+                const int64_t b = (int64_t)s2 * kNT + tid;
+                const float sc = row[b < limit ? b : 0];  // unconditional: no wait per load
+                src.regs.k[s2] = (b < limit && finite_f32(sc)) ? score_key(sc) : 0u;
+            }
         }
     }
     const Thresh th = topk_threshold<kNT>(src, (uint32_t)B, sm.tk);
