@@ -29,8 +29,9 @@
  * stream) and returns.  On a validation error nothing is enqueued and no
  * output is touched.  Device faults surface at the caller's next
  * synchronisation.  No C++ exception crosses this boundary.  The library
- * keeps no state between calls; calls on different streams may run
- * concurrently if their outputs do not overlap.
+ * keeps no state between calls (qsa_sparse_attn_decode_noalloc aside, which
+ * uses a scratch array the library holds on each GPU); calls on different
+ * streams may run concurrently if their outputs do not overlap.
  *
  * Sequences.  n_seq independent sequences each own a region of cap_cells
  * cells in every per-cell cache (cell index = token position in that
@@ -367,6 +368,23 @@ int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs,
                             const void *v_cache_dev, const int32_t *sel_cells_dev,
                             const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
                             size_t ws_bytes, void *stream);
+
+/* 4 for decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): exactly qsa_sparse_attn_decode -- the same
+ * kernels, the same results bit for bit -- with the partial attention states
+ * kept in a scratch array the library holds on each GPU (8 MiB: 65 runs x
+ * n_head x 258 floats per query at top_k 2048, r 4 -- 7 queries of 16 heads).
+ * Calls needing more return QSA_EWS.  The call allocates nothing; its first
+ * call on a device looks up that device's scratch address (the current
+ * device).  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller.  The scratch needs no initial contents. */
+int qsa_sparse_attn_decode_noalloc(const qsa_dims *dims, const qsa_seqs *seqs,
+                                   const float *q_dev, const int32_t *q_seq_dev, int32_t n_q,
+                                   const void *k_cache_dev, const void *v_cache_dev,
+                                   const int32_t *sel_cells_dev, const int32_t *n_sel_dev,
+                                   float *out_dev, void *stream);
 
 /* 3+4 for decode, fused  [ISSUE lever3 then lever1: the block top-k, expanded
  * to cells, is the set attention visits]: exactly qsa_decode_select_candidates

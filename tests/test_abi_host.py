@@ -219,3 +219,15 @@ def test_bf16_key_storage_helpers():
     assert np.array_equal(bits, want)
     assert np.array_equal(synth.widen_kidx(bits),
                           torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_noalloc_decode_attention_rejects_oversize_before_any_device_work():
+    """The allocation-free entry point holds 8 MiB of partial states per GPU:
+    64 queries of 16 heads over 2051-cell lists need more, and the call says
+    so before touching the device (no GPU needed for this check)."""
+    d = qsa.Dims()
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.sparse_attn_decode_noalloc(d, _seqs(), FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       stream=0)
+    assert e.value.code == qsa.QSA_EWS
+    assert "scratch" in str(e.value)

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qsa_internal.h"
 
 namespace {
@@ -123,6 +125,38 @@ int check_queries(const int32_t *q_seq, const int32_t *q_pos, int32_t n_q, bool 
 int launched(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(QSA_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+// Scratch of qsa_sparse_attn_decode_noalloc (the attention's partial states),
+// a file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept here.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, or an error code.
+int scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QSA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QSA_ENOTSUP, "device %d beyond the %d the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(QSA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return QSA_OK;
 }
 
 }  // namespace
@@ -494,6 +528,30 @@ int qsa_sparse_attn_decode(const qsa_dims *dims, const qsa_seqs *seqs, const flo
                            size_t ws_bytes, void *stream) {
     return attn_common(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
                        sel_cells_dev, n_sel_dev, out_dev, ws_dev, ws_bytes, stream, false);
+}
+
+int qsa_sparse_attn_decode_noalloc(const qsa_dims *dims, const qsa_seqs *seqs,
+                                   const float *q_dev, const int32_t *q_seq_dev, int32_t n_q,
+                                   const void *k_cache_dev, const void *v_cache_dev,
+                                   const int32_t *sel_cells_dev, const int32_t *n_sel_dev,
+                                   float *out_dev, void *stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (n_q < 0) return fail(QSA_EINVAL, "n_q negative");
+    const size_t need =
+        qsa::attn_decode_ws_bytes(n_q, dims->n_head, dims->top_k + dims->r - 1);
+    if (need > kNoAllocScratchBytes)
+        return fail(QSA_EWS,
+                    "decode attention of %d queries needs %zu bytes of partial states; the "
+                    "library's scratch holds %zu",
+                    n_q, need, kNoAllocScratchBytes);
+    if (n_q == 0) return ok();
+    void *ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc) return rc;
+    return attn_common(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
+                       sel_cells_dev, n_sel_dev, out_dev, ws, kNoAllocScratchBytes, stream,
+                       false);
 }
 
 int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,

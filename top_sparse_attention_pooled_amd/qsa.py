@@ -27,7 +27,8 @@ EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_update_pooled_keys", "qsa_score_blocks", "qsa_select_topk_blocks",
            "qsa_score_select_decode", "qsa_decode_score_candidates",
            "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
-           "qsa_decode_select_attend", "qsa_score_select_prefill", "qsa_detect_dirty_blocks")
+           "qsa_decode_select_attend", "qsa_score_select_prefill", "qsa_detect_dirty_blocks",
+           "qsa_sparse_attn_decode_noalloc")
 
 
 class QsaError(RuntimeError):
@@ -96,6 +97,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
+    lib.qsa_sparse_attn_decode_noalloc.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.qsa_score_select_prefill.restype = ctypes.c_int
     lib.qsa_score_select_prefill.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, vp,
                                              vp, vp, vp, sz, vp]
@@ -268,6 +271,14 @@ def sparse_attn_decode(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_ca
                                       _ptr(q_seq), n_q, _ptr(k_cache), _ptr(v_cache),
                                       _ptr(sel_cells), _ptr(n_sel), _ptr(out), _ptr(ws),
                                       ws_bytes, _stream(stream)))
+
+
+def sparse_attn_decode_noalloc(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_cache,
+                               sel_cells, n_sel, out, stream=None) -> None:
+    _rc(load().qsa_sparse_attn_decode_noalloc(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                              _ptr(q), _ptr(q_seq), n_q, _ptr(k_cache),
+                                              _ptr(v_cache), _ptr(sel_cells), _ptr(n_sel),
+                                              _ptr(out), _stream(stream)))
 
 
 def sparse_attn_prefill(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_cache, sel_cells,
