@@ -44,10 +44,77 @@ def run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max, dirty=None):
     return bufs
 
 
+def indexer_workspace(bufs, nb_max):
+    """The indexer's intermediate arrays, as the library lays them out in the
+    workspace (each 256-byte aligned, in this order): per query the
+    largest matrix-core score of each 16-block subgroup [n_q][4 n_grp], the
+    band threshold [n_q], the band mask of each 64-block group [n_q][n_grp],
+    then the roped bf16 queries and the error bounds."""
+    n_q = bufs.n_q
+    n_grp = (nb_max + 255) // 256 * 4
+    ws = bufs.ws_pf.cpu().numpy()
+    off, views = 0, []
+    for nbytes in (n_q * n_grp * 16, n_q * 4, n_q * n_grp * 8):
+        views.append(ws[off:off + nbytes])
+        off += (nbytes + 255) // 256 * 256
+    smax = views[0].view(np.float32).reshape(n_q, 4 * n_grp)
+    thr = views[1].view(np.float32)
+    mask = views[2].view(np.uint64).reshape(n_q, n_grp)
+    return smax, thr, mask
+
+
+def check_workspace(w, ws, i, t_scores, q_idx_i, p, nb_max):
+    """The band of query i against the oracle's T-order scores.  The
+    matrix-core sums lie within Delta = 2^-15 |q| sqrt(d) (1 + 2^-8) of T's
+    (the bound the band rests on, |q| of the roped bf16 query, gamma = 1), so:
+    each causal subgroup's maximum is within Delta of T's and the others are
+    -inf; the threshold lies between the B-th largest T maximum M_B less
+    3 Delta and the two radix rounds' bin width (2^-12 |M_B|), and M_B less
+    Delta (-inf with fewer than B subgroups); a block at least Delta above
+    the threshold is in the mask, one more than Delta below it is not, and
+    no block past the causal limit is.  The threshold is the library's own,
+    bounded by the second check before the third uses it."""
+    smax, thr, mask = ws
+    nc = min(oracle.complete_blocks(p, w.r), nb_max)
+    qr = oracle.round_bf16(oracle.rope(q_idx_i, p, w.theta)).astype(np.float64)
+    delta = 2.0 ** -15 * np.sqrt((qr * qr).sum()) * np.sqrt(w.d) * (1 + 2.0 ** -8) * 1.001
+    n_sub = -(-nc // 16)
+    tpad = np.full(-(-max(nc, 1) // 64) * 64, -np.inf)
+    tpad[:nc] = t_scores[:nc]
+    tmax = tpad.reshape(-1, 16).max(axis=1)
+    gm = smax[i, :tmax.size].astype(np.float64)
+    assert np.all(np.isneginf(gm[n_sub:])), (i, "maxima past the causal limit")
+    err = np.abs(gm[:n_sub] - tmax[:n_sub])
+    assert np.all(err <= delta), (i, "subgroup maxima", float(err.max()), delta)
+    B = w.top_k // w.r
+    th = float(thr[i])
+    if n_sub < B:
+        assert th == -np.inf, (i, th)
+    else:
+        # out of range (the fp32 norm of q overflows or underflows, or Delta
+        # leaves [2^-100, 2^100]): every causal block passes, threshold -inf
+        qn = np.sqrt((qr * qr).sum())
+        sure = 2.0 ** -60 < qn < 2.0 ** 60 and 2.0 ** -99 < delta < 2.0 ** 99
+        if sure or th != -np.inf:
+            m_b = float(np.sort(tmax[:n_sub])[::-1][B - 1])
+            lo = m_b - 3.01 * delta - 2.0 ** -12 * abs(m_b)
+            assert lo <= th <= m_b - 0.99 * delta, (i, "threshold", th, m_b, delta)
+    n_g = -(-nc // 64)
+    bits = (mask[i, :n_g, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)
+    bits = bits.reshape(-1).astype(bool)
+    blk = np.arange(bits.size)
+    assert not np.any(bits[blk >= nc]), (i, "mask past the causal limit")
+    must = (blk < nc) & (tpad[:bits.size] >= th + delta)
+    never = (blk < nc) & (tpad[:bits.size] < th - delta)
+    assert np.all(bits[must]), (i, "mask misses", int((must & ~bits).sum()))
+    assert not np.any(bits[never]), (i, "mask extra", int((never & bits).sum()))
+
+
 def check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, which):
     gb = bufs.sel_blocks.cpu().numpy()
     gc = bufs.sel_cells.cpu().numpy()
     gn = bufs.n_sel.cpu().numpy()
+    ws = indexer_workspace(bufs, nb_max)
     for i in which:
         p = int(q_pos[i])
         if q_seq[i] < 0 or p < 0:
@@ -55,6 +122,8 @@ def check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, which
             continue
         r = oracle.score_query(q_idx[i], p, ref_pooled[q_seq[i]], nb_max, w.r, w.theta,
                                bf16=True)
+        if oracle.complete_blocks(p, w.r) > 0:
+            check_workspace(w, ws, i, r, q_idx[i], p, nb_max)
         rb, rc = oracle.select(r, p, w.r, w.top_k)
         assert gn[i] == rc.size, (i, gn[i], rc.size)
         assert np.array_equal(gb[i, :rb.size], rb), i

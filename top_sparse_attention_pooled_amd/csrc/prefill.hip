@@ -100,59 +100,200 @@ __global__ __launch_bounds__(256) void k_rope_queries_delta(ScoreArgs a, const f
 constexpr int kSubMax = 0;  // the largest MFMA score of each 16-block subgroup
 constexpr int kMask = 1;    // the bit mask of blocks whose score reaches the threshold
 
-// Max of v[0..3] (the four 16-block subgroups of a group, cb) over the 16
-// lanes of a DPP row: exchange-halving steps, so lane col ends with the
-// maximum of subgroup 2*bit3(col) + bit2(col).
-__device__ __forceinline__ float row16_max4(float (&v)[4], int col) {
-    const bool hi8 = col & 8, hi4 = col & 4;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const float keep = hi8 ? v[h + 2] : v[h];
-        const float send = hi8 ? v[h] : v[h + 2];
-        v[h] = fmaxf(keep, xor_lane_f<8>(send));
-    }
-    const float keep = hi4 ? v[1] : v[0];
-    const float send = hi4 ? v[0] : v[1];
-    float m = fmaxf(keep, xor_lane_f<4>(send));
-    m = fmaxf(m, xor_lane_f<2>(m));
-    m = fmaxf(m, xor_lane_f<1>(m));
-    return m;
+// Maximum of two and of three floats.  The scores are MFMA results or lane
+// exchanges of them, never NaN, so the NaN-propagating maximum (one
+// v_maximum3_f32 for three operands) gives the same value as fmaxf without
+// the quieting instructions fmaxf adds around a value it cannot prove
+// canonical.  Builtins, not inline asm: the compiler then keeps the wait
+// states an MFMA result needs before a vector instruction may read it.
+__device__ __forceinline__ float max2f(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// 1-D grid over (slab sb of `slab` group tiles, query tile qt of 64
-// queries); a group tile is 4 groups of 64 blocks, one per wavefront.  The
-// hardware deals workgroup ids to the 8 XCDs round-robin, so ids are laid out
-// to put the query tiles of one slab on one XCD, where its keys are read
-// from HBM once and then hit that XCD's L2.  A workgroup loads its queries
-// once and sweeps its slab.  Per query row and group it writes, for every
-// group any row of its sequence needs (blocks past a row's causal limit never
-// count):
+// The contraction: a panel of up to 512 queries against key groups of 64
+// blocks, in work units of (group, half panel of 256 queries) with one
+// wavefront per unit.  A workgroup = 8 wavefronts (one per CU) keeps one
+// half panel's roped bf16 queries in LDS (68 KiB) and takes units of one set
+// of 8 groups at a time, a group per wavefront; the two halves of a set go
+// to workgroups on the same XCD (workgroups are dealt to the 8 XCDs round
+// robin), so a group's second key load comes from that XCD's L2.  The
+// wavefront loads its group's 16 KiB of keys straight into registers, then
+// runs the half panel's queries through the matrix cores 16 at a time with
+// the keys as the A operand and the queries, read from LDS, as the B
+// operand.  The result tile is blocks x queries: lane (R, col) = (lane / 16,
+// lane % 16) holds blocks 16*c + 4*R + jj (c, jj < 4) of query col, so the
+// 16 blocks of a subgroup c lie in one register of the four lanes of a
+// column, and a subgroup's maximum or a group's mask is an in-lane step and
+// two permlane-swap steps across the rows.  Per query row and group of 64
+// blocks a pass writes, for every group any row of its sequence needs
+// (blocks past a row's causal limit never count):
 //   kSubMax: w.smax[q][4*grp + c], the largest score of subgroup c (-inf if
 //            none of its blocks is causal);
 //   kMask:   w.mask[q][grp], bit j set when block 64*grp + j is causal and
 //            its score is >= w.thr[q].
-// When all valid queries of the tile belong to one sequence (the usual
-// ubatch) the next group's keys are in flight while the current group is on
-// the matrix cores; otherwise each group is swept once per distinct sequence.
+// The panel's rows usually belong to one sequence; otherwise the units are
+// swept once per distinct sequence, storing only that sequence's rows.
+constexpr int kPanelNT = 512;
+constexpr int kPanelQ = 512;          // queries per panel
+constexpr int kHalfQ = kPanelQ / 2;   // queries a workgroup holds
+constexpr int kHalfTiles = kHalfQ / 64;
+constexpr int kSetGroups = kPanelNT / kWave;  // groups per set: one per wavefront
+constexpr int kXcds = 8;
+constexpr int kQPitch = kDIdx + 8;  // LDS query row, padded: 16 rows of one read hit distinct banks
+
+// Workgroups per panel for n_grp groups: both halves of every set, a
+// multiple of 2 * kXcds so that a workgroup keeps its half in every round,
+// at most the chip's CUs over the panels (but at least one round).
+__host__ __device__ inline int panel_wgs(int n_grp, int n_panel) {
+    const int n_sets = (n_grp + kSetGroups - 1) / kSetGroups;
+    const int need = (2 * n_sets + 2 * kXcds - 1) / (2 * kXcds) * (2 * kXcds);
+    const int room = max(2 * kXcds, 256 / max(n_panel, 1) / (2 * kXcds) * (2 * kXcds));
+    return max(2 * kXcds, min(need, room));
+}
+
+// Workgroup slot v of a panel -> (half, set): v = 16*m + 8*h + x takes half
+// h of set 8*m + x, and v + 8 the other half of the same set on the same XCD.
+__device__ __forceinline__ void slot_unit(int v, int &half, int &set) {
+    const int x = v % kXcds, k = v / kXcds;
+    half = k & 1;
+    set = (k >> 1) * kXcds + x;
+}
+
+// One group's 16 queries: 16 MFMA with the keys K as A and the queries of
+// LDS rows rl (this lane's column) as B.
+__device__ __forceinline__ void group_x_queries(const bf16x8_t (&K)[4][4],
+                                                const uint16_t *qrow, int quad,
+                                                f32x4_t (&acc)[4]) {
+    bf16x8_t Q[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        Q[ks] = __builtin_bit_cast(bf16x8_t,
+                                   *reinterpret_cast<const u32x4_t *>(qrow + ks * 32 + quad * 8));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K[c][ks], Q[ks], z, 0, 0, 0);
+        acc[c] = z;
+    }
+}
+
+// Subgroup maxima of the tile (avail = causal blocks of the lane's query in
+// the group, 64 when all are): lane (R, col) returns subgroup R of query col.
+template <bool FULL>
+__device__ __forceinline__ float tile_submax(const f32x4_t (&acc)[4], int avail, int quad) {
+    float x[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            v[jj] = (FULL || 16 * c + 4 * quad + jj < avail) ? acc[c][jj] : -INFINITY;
+        x[c] = max2f(max3f(v[0], v[1], v[2]), v[3]);
+    }
+    // rows R, R+2 of subgroups (0, 2) and (1, 3), then rows R, R+1
+    const auto p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]),
+                                                      __float_as_uint(x[2]), false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]),
+                                                      __float_as_uint(x[3]), false, false);
+    const float y02 = max2f(__uint_as_float(p02[0]), __uint_as_float(p02[1]));
+    const float y13 = max2f(__uint_as_float(p13[0]), __uint_as_float(p13[1]));
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(y02), __float_as_uint(y13),
+                                                     false, false);
+    return max2f(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+// Mask word of the tile: rows 0-1 return the low word (blocks 0-31) of
+// query col, rows 2-3 the high word.
+template <bool FULL>
+__device__ __forceinline__ uint32_t tile_mask(const f32x4_t (&acc)[4], float t, int avail,
+                                              int quad) {
+    uint32_t nib[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) b |= (acc[c][jj] >= t ? 1u : 0u) << jj;
+        nib[c] = b;
+    }
+    const uint32_t lo = (nib[0] | nib[1] << 16) << (4 * quad);
+    const uint32_t hi = (nib[2] | nib[3] << 16) << (4 * quad);
+    // rows R, R+2 of the low and the high word, then rows R, R+1
+    const auto p = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+    const uint32_t z = p[0] | p[1];
+    const auto pz = __builtin_amdgcn_permlane16_swap(z, z, false, false);
+    uint32_t m = pz[0] | pz[1];
+    if (!FULL) {
+        const int ab = avail - (quad >= 2 ? 32 : 0);  // causal blocks in this word
+        if (ab < 32) m &= ab <= 0 ? 0u : (1u << ab) - 1u;
+    }
+    return m;
+}
+
 template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_scores(ScoreArgs a, PrefillWs w, int n_gt,
-                                                       int n_qt, int slab) {
-    const int id = blockIdx.x;
-    const int n_slab = (n_gt + slab - 1) / slab;
-    const int sb = (id / (8 * n_qt)) * 8 + (id & 7);
-    const int qt = (id / 8) % n_qt;
-    if (sb >= n_slab) return;
-    const int gt0 = sb * slab, gt1 = min(n_gt, gt0 + slab);
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int q0 = qt * 64;
+__global__ __launch_bounds__(kPanelNT) void k_prefill_scores(ScoreArgs a, PrefillWs w,
+                                                             int wg_per_panel) {
+    constexpr int kSt = MODE == kSubMax ? 0 : 4;  // stamp slots of this pass
+    QSA_STAMP(kSt);
+    __shared__ __align__(16) uint16_t s_q[kHalfQ][kQPitch];
+    __shared__ int s_seq[kHalfQ];
+    __shared__ int s_nc[kHalfQ];
+    __shared__ float s_thr[kHalfQ];
+    __shared__ uint64_t s_trows[kHalfTiles];  // per query tile: its rows of the swept sequence
+    __shared__ int s_tmin[kHalfTiles], s_tmax[kHalfTiles];  // and their causal limits
+    __shared__ int s_next;
+    const int panel = blockIdx.x / wg_per_panel, wc = blockIdx.x % wg_per_panel;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+    const int col = lane & 15, quad = lane >> 4;
+    int half, set0;
+    slot_unit(wc, half, set0);
+    const int qh0 = panel * kPanelQ + half * kHalfQ;  // first query of the half
+    const int n_rows = max(0, min(kHalfQ, a.n_q - qh0));
+    const int n_qt = (n_rows + 63) / 64;
     const int64_t cap_blocks = a.g.cap_cells / a.r;
-    auto grp_of = [&](int gt) { return (int64_t)(gt * 4 + wave); };
-    // lane r: the query of row r (sequence, -1 if invalid or past n_q)
+    const int64_t n_sub = 4 * (int64_t)w.n_grp;
+
+    // the first unit's keys, requested before the query load so that the two
+    // overlap: the first sweep is almost always over the half's first row's
+    // sequence; a wrong guess is reloaded
+    bf16x8_t K[4][4];
+    int k_seq = -1, k_grp = set0 * kSetGroups + wave;
+    if (n_rows > 0) {
+        const int s0 = a.q_seq[qh0];
+        if (s0 >= 0 && s0 < a.g.n_seq && k_grp < w.n_grp) {
+            k_seq = s0;
+            load_key_tile(a.pooled_bf16 + (int64_t)s0 * cap_blocks * kDIdx, (int64_t)k_grp * 64,
+                          cap_blocks, true, K);
+        }
+    }
+    // the half's queries into LDS: 16-byte pieces, row x / 16, part x % 16,
+    // all of a thread's in flight at once.  Rows past the last query repeat
+    // it: a column of the B operand only reaches its own column of results,
+    // and those are never stored.
+    if (n_rows > 0) {
+        constexpr int kPer = kHalfQ * 16 / kPanelNT;
+        u32x4_t v[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int x = tid + i * kPanelNT, rr = min(x >> 4, n_rows - 1), part = x & 15;
+            v[i] = *reinterpret_cast<const u32x4_t *>(w.qr + (int64_t)(qh0 + rr) * kDIdx +
+                                                      part * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int x = tid + i * kPanelNT, rr = x >> 4, part = x & 15;
+            *reinterpret_cast<u32x4_t *>(&s_q[rr][part * 8]) = v[i];
+        }
+    }
+    // row tid of the half (wavefronts 0-3): sequence, causal limit, threshold
     int my_seq = -1, my_nc = 0;
-    {
-        const int qi = q0 + lane;
-        if (qi < a.n_q) {
+    if (tid < kHalfQ) {
+        const int qi = qh0 + tid;
+        if (tid < n_rows) {
             int64_t p;
             bool valid;
             const int64_t nc = query_blocks(a.q_seq, a.q_pos, qi, a.g.n_seq, a.g.cap_cells,
@@ -160,124 +301,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             if (!valid) my_seq = -1;
             my_nc = (int)(nc < a.nb_max ? nc : a.nb_max);
         }
+        s_seq[tid] = my_seq;
+        s_nc[tid] = my_nc;
+        if constexpr (MODE == kMask) s_thr[tid] = tid < n_rows ? w.thr[qi] : 0.f;
     }
-    const uint64_t valid_rows = __ballot(my_seq >= 0);
-    if (!valid_rows) return;  // (the same for every wavefront of the workgroup)
-    // the 64 rows' causal limits and thresholds, for the result layout: lane
-    // l holds rows rb*16 + 4*(l/16) + jj of column l % 16
-    __shared__ int s_nc[64];
-    __shared__ float s_thr[64];
-    // the 64 roped queries (A operands), rows padded to 272 bytes so the 16
-    // rows one MFMA operand read touches fall in different banks
-    constexpr int kQPitch = kDIdx + 8;
-    __shared__ __align__(16) uint16_t s_q[64][kQPitch];
-    if (wave == 0) {
-        s_nc[lane] = my_nc;
-        if constexpr (MODE == kMask) s_thr[lane] = q0 + lane < a.n_q ? w.thr[q0 + lane] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int x = u * 256 + (int)threadIdx.x;  // 16-byte piece: row x / 16, part x % 16
-        const int rr = x >> 4, part = x & 15;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (q0 + rr < a.n_q)
-            v = *reinterpret_cast<const u32x4_t *>(w.qr + (int64_t)(q0 + rr) * kDIdx + part * 8);
-        *reinterpret_cast<u32x4_t *>(&s_q[rr][part * 8]) = v;
-    }
-    __syncthreads();
-    const int col = lane & 15, quad = lane >> 4;
-    const int64_t n_sub = 4 * (int64_t)w.n_grp;
-    // One 16-row band rb of the 64 x 64 tile on the matrix cores, then its
-    // epilogue (the band's accumulators are all that is live).
-    // FULL: every block of the group is causal for every stored row, so no
-    // per-element limit test
-    auto tile_as = [&](auto full, const bf16x8_t (&B)[4][4], int64_t grp, uint64_t rows) {
-        constexpr bool FULL = decltype(full)::value;
-        const int64_t gb0 = grp * 64;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            bf16x8_t A[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                A[ks] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t *>(&s_q[rb * 16 + col][ks * 32 + quad * 8]));
-            f32x4_t acc[4];
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks], B[cb][ks], c, 0, 0, 0);
-                acc[cb] = c;
+
+    int sq = -1;  // the sequence being swept; rows of others are not stored
+    bool first = true;
+    for (;;) {
+        // next sequence: the smallest valid one above sq among the half's rows
+        if (tid == 0) s_next = 0x7fffffff;
+        __syncthreads();
+        {
+            const int cand = my_seq > sq ? my_seq : 0x7fffffff;
+            const int m = (int)wave_min_u32((uint32_t)cand);
+            if (lane == 0 && m != 0x7fffffff) atomicMin(&s_next, m);
+        }
+        __syncthreads();
+        const int nsq = s_next;
+        if (nsq == 0x7fffffff) break;
+        sq = nsq;
+        if (wave < kHalfTiles) {  // wavefront t describes query tile t for this sweep
+            const bool mine = my_seq == sq;
+            const uint64_t rows = __ballot(mine);
+            const uint32_t mx = wave_max_u32(mine ? (uint32_t)my_nc : 0u);
+            const uint32_t mn = wave_min_u32(mine ? (uint32_t)my_nc : 0x7fffffffu);
+            if (lane == 0) {
+                s_trows[wave] = rows;
+                s_tmax[wave] = (int)mx;
+                s_tmin[wave] = (int)mn;
             }
+        }
+        __syncthreads();
+        if (first) {
+            QSA_STAMP(kSt + 1);
+            first = false;
+        }
+        int ncmax = 0;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = rb * 16 + quad * 4 + jj;
-                const int lim = FULL ? 0 : s_nc[r];
-                if constexpr (MODE == kSubMax) {
-                    float v[4];
+        for (int t = 0; t < kHalfTiles; ++t) ncmax = max(ncmax, s_tmax[t]);
+        const int n_g = min((ncmax + 63) / 64, w.n_grp);
+        const uint16_t *keys = a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx;
+        for (int v = wc; ; v += wg_per_panel) {
+            int h, set;
+            slot_unit(v, h, set);
+            if (set * kSetGroups >= n_g) break;  // sets grow with v
+            const int grp = set * kSetGroups + wave;
+            if (grp >= n_g) continue;
+            const int gb0 = grp * 64;
+            if (k_seq != sq || k_grp != grp) {
+                load_key_tile(keys, gb0, cap_blocks, true, K);
+                k_seq = sq;
+                k_grp = grp;
+            }
+            for (int qt = 0; qt < n_qt; ++qt) {
+                const uint64_t rows = s_trows[qt];
+                if (!rows || gb0 >= s_tmax[qt]) continue;
+                const int64_t q0 = qh0 + qt * 64;
+                if (rows == ~0ull && gb0 + 64 <= s_tmin[qt]) {
+                    // every row of the tile is the sweep's and sees every block:
+                    // straight-line code, every lane stores
 #pragma unroll
-                    for (int cb = 0; cb < 4; ++cb)
-                        v[cb] = (FULL || gb0 + cb * 16 + col < lim) ? acc[cb][jj] : -INFINITY;
-                    const float m = row16_max4(v, col);
-                    // lanes 0, 4, 8, 12 of the row hold subgroups 0, 1, 2, 3
-                    if ((col & 3) == 0 && ((rows >> r) & 1))
-                        w.smax[(int64_t)(q0 + r) * n_sub + 4 * grp + (col >> 2)] = m;
-                } else {
-                    const float t = s_thr[r];
-                    uint64_t mk = 0;
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) {
-                        const bool pass = (FULL || gb0 + cb * 16 + col < lim) && acc[cb][jj] >= t;
-                        const uint64_t bal = __ballot(pass);
-                        mk |= ((bal >> (16 * quad)) & 0xffffull) << (16 * cb);
+                    for (int st = 0; st < 4; ++st) {
+                        f32x4_t acc[4];
+                        group_x_queries(K, &s_q[qt * 64 + st * 16 + col][0], quad, acc);
+                        const int64_t qg = q0 + st * 16 + col;
+                        if constexpr (MODE == kSubMax) {
+                            w.smax[qg * n_sub + 4 * grp + quad] = tile_submax<true>(acc, 64, quad);
+                        } else {
+                            const uint32_t m = tile_mask<true>(acc, s_thr[qt * 64 + st * 16 + col],
+                                                               64, quad);
+                            // rows 0 and 1 (2 and 3) hold the same word
+                            reinterpret_cast<uint32_t *>(w.mask)[(qg * w.n_grp + grp) * 2 +
+                                                                 (quad >> 1)] = m;
+                        }
                     }
-                    if (col == 0 && ((rows >> r) & 1))
-                        w.mask[(int64_t)(q0 + r) * w.n_grp + grp] = mk;
+                } else {
+                    for (int st = 0; st < 4; ++st) {
+                        const int rl = qt * 64 + st * 16 + col;  // this lane's query row
+                        f32x4_t acc[4];
+                        group_x_queries(K, &s_q[rl][0], quad, acc);
+                        const bool store = (rows >> (st * 16 + col)) & 1;
+                        const int64_t qg = q0 + st * 16 + col;
+                        const int avail = s_nc[rl] - gb0;
+                        if constexpr (MODE == kSubMax) {
+                            const float m = tile_submax<false>(acc, avail, quad);
+                            if (store) w.smax[qg * n_sub + 4 * grp + quad] = m;
+                        } else {
+                            const uint32_t m = tile_mask<false>(acc, s_thr[rl], avail, quad);
+                            if (store && (quad & 1) == 0)
+                                reinterpret_cast<uint32_t *>(w.mask)[(qg * w.n_grp + grp) * 2 +
+                                                                     (quad >> 1)] = m;
+                        }
+                    }
                 }
             }
-        }
-    };
-    auto tile = [&](const bf16x8_t (&B)[4][4], int64_t grp, uint64_t rows) {
-        // smallest causal limit of the stored rows (lane r holds row r's)
-        const uint32_t ncmin = wave_min_u32(((rows >> lane) & 1) ? (uint32_t)my_nc : ~0u);
-        if ((uint64_t)grp * 64 + 64 <= ncmin)
-            tile_as(std::true_type{}, B, grp, rows);
-        else
-            tile_as(std::false_type{}, B, grp, rows);
-    };
-
-    const int sq0 = __shfl(my_seq, __builtin_ctzll(valid_rows));
-    if (__ballot(my_seq >= 0 && my_seq != sq0) == 0) {
-        const int ncmax = (int)wave_max_u32(my_seq >= 0 ? (uint32_t)my_nc : 0u);
-        const uint16_t *keys = a.pooled_bf16 + (int64_t)sq0 * cap_blocks * kDIdx;
-        auto live_of = [&](int gt) {
-            return grp_of(gt) < w.n_grp && grp_of(gt) * 64 < ncmax;
-        };
-        // one key buffer: the other wavefront on the SIMD covers the wait
-        for (int gt = gt0; gt < gt1; ++gt) {
-            if (!live_of(gt)) continue;
-            bf16x8_t B[4][4];
-            load_key_tile(keys, grp_of(gt) * 64, cap_blocks, true, B);
-            tile(B, grp_of(gt), valid_rows);
-        }
-        return;
-    }
-    for (int gt = gt0; gt < gt1; ++gt) {
-        if (grp_of(gt) >= w.n_grp) continue;
-        const int64_t gb0 = grp_of(gt) * 64;
-        uint64_t done = ~valid_rows;
-        while (done != ~0ull) {
-            const int sq = __shfl(my_seq, __builtin_ctzll(~done));
-            const uint64_t rows = __ballot(my_seq == sq);
-            const int ncmax = (int)wave_max_u32((my_seq == sq) ? (uint32_t)my_nc : 0u);
-            done |= rows;
-            if (gb0 >= ncmax) continue;
-            bf16x8_t B[4][4];
-            load_key_tile(a.pooled_bf16 + (int64_t)sq * cap_blocks * kDIdx, gb0, cap_blocks, true, B);
-            tile(B, grp_of(gt), rows);
+            if (v == wc) QSA_STAMP(kSt + 2);
         }
     }
+    QSA_STAMP(kSt + 3);
 }
 
 // Exact score of block b under order T: bf16 key row against the query held
@@ -369,6 +491,7 @@ __device__ __forceinline__ bool delta_in_range(float delta) {
 // block then passes the filter).
 constexpr int kTauPer = kPrefMaxBlocks / 16 / kTauNT;  // subgroup maxima per thread
 __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w, int top_k) {
+    QSA_STAMP(8);
     __shared__ TopkSmem<kTauNT> sm;
     const int i = blockIdx.x, tid = threadIdx.x;
     int s;
@@ -423,6 +546,7 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
         if ((double)thr > t) thr = nextafterf(thr, -INFINITY);
     }
     if (tid == 0) w.thr[i] = thr;
+    QSA_STAMP(9);
 }
 
 // grid (n_q), kSelPNT threads: the exact top-B of query i among its masked
@@ -432,6 +556,7 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
                                                             int32_t *sel_blocks,
                                                             int32_t *sel_cells, int32_t *n_sel) {
     __shared__ PrefSelSmem sm;
+    QSA_STAMP(10);
     const int i = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = wave_id();
     int s;
@@ -478,11 +603,13 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
                 }
             }
             __syncthreads();
+            QSA_STAMP(11);
             for (int x = tid; x < (int)total; x += kSelPNT) {
                 const int64_t b = (int64_t)sm.band[x];
                 sm.band[x] = block_key(exact_score(keys + b * kDIdx, sm.q), b);
             }
             __syncthreads();
+            QSA_STAMP(12);
             BandKeys bk;
 #pragma unroll
             for (int c = 0; c < kBandCap / kSelPNT; ++c) {
@@ -490,6 +617,7 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
                 bk.k[c] = x < (int)total ? sm.band[x] : 0ull;
             }
             const Thresh th = topk_threshold<kSelPNT>(bk, (uint32_t)B, sm.tk);
+            QSA_STAMP(13);
             bk([&](uint32_t k, uint32_t u) {
                 if (th.keep(k, u)) mark(sm.bitmap, ~u);
             });
@@ -511,6 +639,7 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
     emit_from_bitmap<kSelPNT>(sm.bitmap, n_words, B, a.r, nc, tail,
                               sel_blocks + (int64_t)i * B, sel_cells + (int64_t)i * ld_cells,
                               ld_cells, n_sel + i, sm.tk);
+    QSA_STAMP(14);
 }
 
 }  // namespace
@@ -535,6 +664,8 @@ static size_t prefill_layout(char *base, int n_q, int nb_max, PrefillWs *w) {
     return off;
 }
 
+QSA_STAMP_READER(prefill)
+
 size_t prefill_ws_bytes(int n_q, int nb_max) {
     return n_q > 0 ? prefill_layout(nullptr, n_q, nb_max, nullptr) : 0;
 }
@@ -547,20 +678,18 @@ hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, v
     prefill_layout(static_cast<char *>(ws), a.n_q, a.nb_max, &w);
     hipLaunchKernelGGL(k_rope_queries_delta, dim3((a.n_q + 3) / 4), dim3(256), 0, st, a, gamma,
                        w);
-    const int qt = (a.n_q + 63) / 64;
-    // slabs of group tiles: about 512 workgroups (two per CU); the grid is
-    // padded to whole rounds of the 8 XCDs (k_prefill_scores maps ids)
-    const int n_gt = w.n_grp / 4;
-    const int n_slab = max(1, min(n_gt, 512 / qt));
-    const int slab = max(1, (n_gt + n_slab - 1) / n_slab);
-    const int grid = ((n_gt + slab - 1) / slab + 7) / 8 * 8 * qt;
-    if (n_gt > 0)
-        hipLaunchKernelGGL(k_prefill_scores<kSubMax>, dim3(grid), dim3(256), 0, st, a, w, n_gt,
-                           qt, slab);
+    // per panel of 512 queries, workgroups for both halves of its sets of
+    // groups, XCD-paired (one per CU, at most the chip's 256 CUs in all)
+    const int n_panel = (a.n_q + kPanelQ - 1) / kPanelQ;
+    const int wg_per_panel = panel_wgs(w.n_grp, n_panel);
+    const int grid = n_panel * wg_per_panel;
+    if (w.n_grp > 0)
+        hipLaunchKernelGGL(k_prefill_scores<kSubMax>, dim3(grid), dim3(kPanelNT), 0, st, a, w,
+                           wg_per_panel);
     hipLaunchKernelGGL(k_prefill_tau, dim3(a.n_q), dim3(kTauNT), 0, st, a, w, top_k);
-    if (n_gt > 0)
-        hipLaunchKernelGGL(k_prefill_scores<kMask>, dim3(grid), dim3(256), 0, st, a, w, n_gt, qt,
-                           slab);
+    if (w.n_grp > 0)
+        hipLaunchKernelGGL(k_prefill_scores<kMask>, dim3(grid), dim3(kPanelNT), 0, st, a, w,
+                           wg_per_panel);
     hipLaunchKernelGGL(k_select_prefill, dim3(a.n_q), dim3(kSelPNT), 0, st, a, w, top_k,
                        sel_blocks, sel_cells, n_sel);
     return hipGetLastError();

@@ -41,7 +41,7 @@ constexpr int kQ8Row = kHeadDim / 32 * kQ8Bytes;  // 272 bytes
 // ---------------------------------------------------------------------------
 #ifdef QSA_STAMPS
 constexpr int kStampWgs = 4096;
-constexpr int kStampSlots = 8;
+constexpr int kStampSlots = 16;
 static __device__ uint64_t g_stamps[kStampWgs][kStampSlots];
 __device__ __forceinline__ void stamp_at(int slot) {
     const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);

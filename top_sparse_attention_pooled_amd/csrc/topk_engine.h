@@ -212,7 +212,6 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
         mx = max(mx, k);
     });
     const uint32_t n_valid = block_sum_u32<NT>(cnt, sm);
-    QSA_STAMP(1);  // the elements are in (their first use)
     if (n_valid <= B) return th;  // T = 0: every valid element
     block_minmax_u32<NT>(mn, mx, sm);
     uint32_t n_above;

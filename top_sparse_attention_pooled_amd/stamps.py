@@ -21,16 +21,24 @@ import sys
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SLOTS = 8
+SLOTS = 16
 STAMP_WGS = 4096
 
-# (translation unit, kernel, workgroups of one launch for n_q = 1 as a
-# function of the step's geometry, {slot: point name})
+# kernel -> (translation unit, {slot: point name}), for the decode step and
+# for the prefill indexer
 POINTS = {
     "k_score_cand": ("score", {0: "start", 2: "tile scored", 3: "end"}),
-    "k_sel_attn": ("attn", {0: "start", 1: "candidates in", 2: "threshold",
-                            3: "cells placed", 4: "end"}),
+    "k_sel_attn": ("attn", {0: "start", 2: "threshold", 3: "cells placed", 4: "end"}),
     "k_attn_combine": ("attn", {5: "start", 6: "end"}),
+}
+PREFILL_POINTS = {
+    "k_prefill_scores (maxima)": ("prefill", {0: "start", 1: "operands in",
+                                              2: "first group", 3: "end"}),
+    "k_prefill_scores (masks)": ("prefill", {4: "start", 5: "operands in",
+                                             6: "first group", 7: "end"}),
+    "k_prefill_tau": ("prefill", {8: "start", 9: "end"}),
+    "k_select_prefill": ("prefill", {10: "start", 11: "band listed", 12: "rescored",
+                                     13: "threshold", 14: "end"}),
 }
 
 
@@ -64,6 +72,8 @@ def main():
 
     from . import qsa, runtime, synth
     lib = qsa.load(os.path.join(HERE, "libqsa_stamps.so"))
+    if args.workload.startswith("prefill"):
+        return prefill_main(args, lib, torch, qsa, runtime, synth)
     dev = "cuda:0"
     w = synth.WORKLOADS[args.workload]
     w = synth.Workload(**{**w.__dict__, "steps": max(w.steps, args.steps)})
@@ -134,6 +144,64 @@ def main():
     if args.json:
         with open(args.json, "w") as f:
             json.dump(out, f, indent=1)
+
+
+def prefill_main(args, lib, torch, qsa, runtime, synth):
+    """The prefill indexer (qsa_score_select_prefill) on the 512-token ubatch,
+    repeated --steps times over the same blocks; per kernel, the quantiles
+    over workgroups and repeats of each point's time from the kernel's first
+    start, and of its phases."""
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.workload]
+    kidx = synth.make_kidx(w)
+    z = np.zeros((1, 1, 1, 1), np.uint8)
+    layer = runtime.Layer(w, dev, kidx=kidx, k=z, v=z)
+    layer.rebuild(np.full(1, w.n_cells0, np.int32))
+    layer.set_n_cells(synth.n_cells_at(w, 0))
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q_idx, _, q_seq, q_pos = (t(x) for x in synth.make_queries(w, 0))
+    dirty = synth.dirty_blocks(w, 0)
+    dl = t(dirty.reshape(-1))
+    nb = w.nb_max(0)
+    bufs = runtime.StepBuffers(layer.dims, q_pos.numel(), nb, dev, prefill=True)
+    torch.cuda.synchronize()
+    read(lib, "prefill")
+    times = {k: {p: [] for p in v[1].values()} for k, v in PREFILL_POINTS.items()}
+    durs = {}
+    for step in range(args.steps):
+        qsa.score_select_prefill(layer.dims, layer.seqs(), layer.kidx, dl, dirty.shape[0],
+                                 layer.pooled, layer.pooled_bf16, q_idx, q_seq, q_pos,
+                                 q_pos.numel(), nb, bufs.sel_blocks, bufs.sel_cells, bufs.n_sel,
+                                 bufs.ws_pf, bufs.ws_pf_bytes)
+        torch.cuda.synchronize()
+        tab = read(lib, "prefill")
+        if step < args.skip:
+            continue
+        for name, (_, pts) in PREFILL_POINTS.items():
+            first = min(pts)
+            rows = tab[tab[:, first] > 0]
+            if not len(rows):
+                continue
+            t0 = rows[:, first].min()
+            for slot, pname in pts.items():
+                vals = rows[:, slot]
+                times[name][pname] += list((vals[vals > 0] - t0) * 0.01)
+            sl = list(pts)
+            for a_, b_ in zip(sl, sl[1:]):
+                ok = (rows[:, a_] > 0) & (rows[:, b_] > 0)
+                key = f"{name}: {pts[a_]} -> {pts[b_]}"
+                durs.setdefault(key, []).extend(list((rows[ok, b_] - rows[ok, a_]) * 0.01))
+    print(f"# {args.workload} indexer: {args.steps - args.skip} repeats; microseconds, "
+          "quantiles p0 p10 p50 p90 p100 over workgroups and repeats")
+    print("## time of each point from the kernel's first workgroup start")
+    for name, pts in times.items():
+        for pname, vals in pts.items():
+            if vals:
+                print(f"{name:28s} {pname:16s} {q(vals)}")
+    print("## phase durations within a workgroup")
+    for key, vals in durs.items():
+        if vals:
+            print(f"{key:60s} {q(vals)}")
 
 
 if __name__ == "__main__":
