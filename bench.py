@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of replaying a graph (for "
                          "hardware-counter runs)")
+    ap.add_argument("--probe", action="store_true",
+                    help="memory-traffic floors instead of the step: HBM, last-level-cache and "
+                         "L2 streaming reads, and the prefill attention's K/V row gather alone "
+                         "beside the attention kernel itself")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also copy an MIB-MiB buffer once: a kernel of known traffic "
                          "that scales the byte counters")
@@ -574,6 +578,76 @@ def cpu_baseline_prefill(w, host, budget):
 
 # ---------------------------------------------------------------------------
 
+def run_probe(args, torch, dev):
+    """Floors for the kernels' access patterns: qsa_probe_stream_read over 4
+    GiB (HBM, streaming loads), over 64 MiB re-read (resident in the 256 MB
+    last-level cache) and over 16 MiB re-read (each XCD re-reads the same 2
+    MiB, resident in its L2); then qsa_probe_gather_prefill -- the prefill
+    attention's K/V row gather without its arithmetic -- and
+    qsa_sparse_attn_prefill itself on the 512-token ubatch's selections.
+    Each figure: events around n back-to-back launches on one stream."""
+    from top_sparse_attention_pooled_amd import qsa, runtime
+    stream = torch.cuda.Stream()
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+
+    def timed(fn, n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            fn()
+            fn()
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(n):
+                fn()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1000.0 / n  # us per launch
+
+    out = {"probe": "memory-traffic floors", "unit": "GB/s and us per launch"}
+    for name, mib, nt, n in (("hbm_stream_read", 4096, True, 20),
+                             ("llc_reread", 64, False, 200), ("l2_reread", 16, False, 400)):
+        buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+        nb = buf.numel()
+        us = timed(lambda: qsa.probe_stream_read(buf, nb, sink, 64, nontemporal=nt,
+                                                 stream=stream), n)
+        out[name] = {"bytes": nb, "us": round(us, 2), "GBps": round(nb / us / 1e3, 1)}
+        del buf
+        torch.cuda.empty_cache()
+    # the prefill ubatch's selections, then the gather alone and the kernel
+    w, layers, inp, host = setup(torch, dev, "prefill", 1, 0, 1)
+    layer = layers[0]
+    n_q, nb_max = inp["n_q"], inp["nb_max"]
+    bf = runtime.StepBuffers(layer.dims, n_q, nb_max, dev, prefill=True)
+    layer.n_cells = inp["n_cells"][0]
+    d, sq = layer.dims, layer.seqs()
+    qsa.score_select_prefill(d, sq, layer.kidx, inp["dirty"][0], inp["n_dirty"], layer.pooled,
+                             layer.pooled_bf16, inp["q_idx"][0], inp["q_seq"][0],
+                             inp["q_pos"][0], n_q, nb_max, bf.sel_blocks, bf.sel_cells,
+                             bf.n_sel, bf.ws_pf, bf.ws_pf_bytes)
+    torch.cuda.synchronize()
+    n_sel = bf.n_sel.cpu().numpy().astype(np.int64)
+    # rows loaded: every slot of every 32-cell chunk, K and V, per KV head
+    rows = int(np.sum(-(-n_sel // 32) * 32)) * w.Hk * 2
+    gbytes = rows * 272
+    g_us = timed(lambda: qsa.probe_gather_prefill(d, sq, inp["q_seq"][0], n_q, layer.k, layer.v,
+                                                  bf.sel_cells, bf.n_sel, sink, 64,
+                                                  stream=stream), 20)
+    a_us = timed(lambda: qsa.sparse_attn_prefill(d, sq, inp["q"][0], inp["q_seq"][0], n_q,
+                                                 layer.k, layer.v, bf.sel_cells, bf.n_sel,
+                                                 bf.out, bf.ws_attn, bf.ws_attn_bytes,
+                                                 stream=stream), 20)
+    distinct = int(np.unique(bf.sel_cells.cpu().numpy()[bf.sel_cells.cpu().numpy() >= 0]).size)
+    out["prefill_gather"] = {"rows_loaded": rows, "bytes": gbytes, "us": round(g_us, 2),
+                             "GBps": round(gbytes / g_us / 1e3, 1),
+                             "distinct_cells": distinct,
+                             "distinct_bytes": distinct * w.Hk * 2 * 272}
+    out["prefill_attn"] = {"us": round(a_us, 2), "GBps_of_gather": round(gbytes / a_us / 1e3, 1)}
+    out["config"] = {"workload": "prefill", "ubatch": n_q, "n_kv": int(w.n_cells0),
+                     "top_k": w.top_k, "kv_heads": w.Hk, "kv_type": "q8_0"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -589,6 +663,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = args.workload
+    if args.probe:
+        print(json.dumps(run_probe(args, torch, dev)), flush=True)
+        return
     if name is None:  # the headline decode line, with the prefill ubatch in it
         result = run_decode(args, torch, dev, "decode250k")
         torch.cuda.empty_cache()

@@ -125,6 +125,7 @@ extern "C" {
 #define QSA_OP_SCORE_BF16 3
 #define QSA_OP_SCORE_SELECT 4
 #define QSA_OP_SCORE_SELECT_PREFILL 5
+#define QSA_OP_ATTN_DECODE_UNION 6 /* nb_max argument: tokens per group */
 
 /* Model geometry and constants.
  *   kq_scale   attention logit scale; <= 0 means 1/sqrt(head_dim)
@@ -368,6 +369,39 @@ int qsa_sparse_attn_prefill(const qsa_dims *dims, const qsa_seqs *seqs,
                             const void *v_cache_dev, const int32_t *sel_cells_dev,
                             const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
                             size_t ws_bytes, void *stream);
+
+/* 4 for several decode tokens per sequence over the union of their lists
+ * [ISSUE goodbadwolf's comment, "Why the two phases disagree": with a few
+ * query tokens per sequence -- a speculative verify step, the end of a chunk
+ * -- each token has its own top-k set, and a gather per token reads the rows
+ * their sets share once per token].  The same attention as
+ * qsa_sparse_attn_prefill, per query, but each K/V row is loaded once for
+ * every token of its group that lists it.
+ *
+ * Queries are taken t_group (1 .. 8) at a time in order (the last group may
+ * be shorter).  Per group, the rows of every token's listed cells (cells in
+ * 0 .. min(n_cells, cap_cells)-1 of its own sequence, first n_sel entries)
+ * form one ascending list with a bit per token that holds the row; each row
+ * is staged once per run of 128 and scored for every query head of the group,
+ * a token's softmax skipping the rows it does not hold.  When the group's
+ * tokens are in one sequence and each list strictly ascends (as the
+ * selection calls produce them), equal cells fold into one entry; otherwise
+ * the lists are concatenated (the same result, without the sharing).
+ * Arithmetic as in prefill: fp16 operands on the matrix cores, fp32 sums.
+ *
+ *   t_group    tokens per group, 1 .. 8
+ *   ws_dev     qsa_workspace_size(QSA_OP_ATTN_DECODE_UNION, n_q, t_group)
+ *              bytes, 16-byte aligned
+ * Other arguments as qsa_sparse_attn_decode.  QSA_EINVAL for t_group outside
+ * 1 .. 8; QSA_ENOTSUP unless kv_type is QSA_KV_Q8_0, the sequences have no
+ * cell table, cap_cells < 2^28, n_head / n_head_kv is 4, 8 or 16, and
+ * t_group * (top_k + r - 1) <= 16448 (8 tokens of top_k 2048, r <= 9). */
+int qsa_sparse_attn_decode_union(const qsa_dims *dims, const qsa_seqs *seqs,
+                                 const float *q_dev, const int32_t *q_seq_dev, int32_t n_q,
+                                 int32_t t_group, const void *k_cache_dev,
+                                 const void *v_cache_dev, const int32_t *sel_cells_dev,
+                                 const int32_t *n_sel_dev, float *out_dev, void *ws_dev,
+                                 size_t ws_bytes, void *stream);
 
 /* 4 for decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

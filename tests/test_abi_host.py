@@ -15,10 +15,15 @@ FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced here
 
 
 def _declared():
-    with open(os.path.join(ROOT, "include", "qsa.h")) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
+    """Every qsa_* function the headers under include/ declare."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            with open(os.path.join(inc, h)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            names |= set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -231,3 +236,50 @@ def test_noalloc_decode_attention_rejects_oversize_before_any_device_work():
                                        stream=0)
     assert e.value.code == qsa.QSA_EWS
     assert "scratch" in str(e.value)
+
+
+def test_probes_reject_bad_arguments_before_any_device_work():
+    """The memory-traffic probes validate like the other calls: a source that
+    is not whole 16-byte words, a misaligned source, an empty sink, and the
+    gather probe on a cache type its q8_0 kernel does not read."""
+    for src, n, n_sink in ((FAKE, 24, 1), (FAKE + 8, 32, 1), (FAKE, 32, 0), (None, 32, 1)):
+        with pytest.raises(qsa.QsaError) as e:
+            qsa.probe_stream_read(src, n, FAKE, n_sink, stream=0)
+        assert e.value.code == qsa.QSA_EINVAL
+    d = qsa.Dims(kv_type=qsa.KV_F16)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.probe_gather_prefill(d, _seqs(), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1, stream=0)
+    assert e.value.code == qsa.QSA_ENOTSUP
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.probe_gather_prefill(qsa.Dims(), _seqs(), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                 stream=0)
+    assert e.value.code == qsa.QSA_EINVAL
+
+
+def test_union_decode_attention_validates_before_any_device_work():
+    """qsa_sparse_attn_decode_union: t_group outside 1..8, a cache type or
+    head layout it does not read, too many entries per group, a short
+    workspace -- all rejected on the host; its workspace is the union lists
+    plus the per-run partial states."""
+    d = qsa.Dims()
+    ld = d.ld_cells
+    args = (FAKE, FAKE, 5)
+    for t, code in ((0, qsa.QSA_EINVAL), (9, qsa.QSA_EINVAL)):
+        with pytest.raises(qsa.QsaError) as e:
+            qsa.sparse_attn_decode_union(d, _seqs(), *args, t, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         1 << 30, stream=0)
+        assert e.value.code == code
+    for dd in (qsa.Dims(kv_type=qsa.KV_F16), qsa.Dims(n_head_kv=8), qsa.Dims(top_k=4096)):
+        with pytest.raises(qsa.QsaError) as e:
+            qsa.sparse_attn_decode_union(dd, _seqs(), *args, 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, 1 << 30, stream=0)
+        assert e.value.code == qsa.QSA_ENOTSUP
+    need = qsa.workspace_size(d, qsa.OP_ATTN_DECODE_UNION, 5, 5)
+    cap = 5 * ld
+    runs = -(-cap // 128)
+    rnd = lambda x: -(-x // 256) * 256
+    assert need == rnd(cap * 4) + rnd(cap) + rnd(4) + rnd(2 * runs * 5 * 8 * 258 * 4)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.sparse_attn_decode_union(d, _seqs(), *args, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     need - 16, stream=0)
+    assert e.value.code == qsa.QSA_EWS

@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "libqsa.so")
 # per-kernel VGPRs / scratch / occupancy reported by the compiler
 RESOURCES = os.path.join(BUILD, "resources.json")
 SOURCES = ["api.hip", "pooled.hip", "score.hip", "select.hip", "attn.hip", "attn_prefill.hip",
-           "prefill.hip"]
+           "prefill.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

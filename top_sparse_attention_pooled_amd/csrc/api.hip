@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "qsa_internal.h"
+#include "../../include/qsa_probe.h"
 
 namespace {
 
@@ -191,6 +192,11 @@ int qsa_workspace_size(const qsa_dims *dims, int32_t op, int32_t n_q, int32_t nb
         case QSA_OP_SCORE_SELECT_PREFILL:
             if (nb_max < 0) return fail(QSA_EINVAL, "nb_max negative");
             *bytes = qsa::prefill_ws_bytes(n_q, nb_max);
+            break;
+        case QSA_OP_ATTN_DECODE_UNION:  // nb_max carries t_group
+            if (nb_max < 1 || nb_max > qsa::kUnionMaxTokens)
+                return fail(QSA_EINVAL, "t_group %d outside 1..%d", nb_max, qsa::kUnionMaxTokens);
+            *bytes = qsa::union_ws_bytes(n_q, nb_max, dims->n_head, dims->n_head_kv, ld_cells);
             break;
         default: return fail(QSA_EINVAL, "unknown op %d", op);
     }
@@ -478,14 +484,17 @@ static int attn_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_
                      const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
                      const void *v_cache_dev, const int32_t *sel_cells_dev,
                      const int32_t *n_sel_dev, float *out_dev, void *ws_dev, size_t ws_bytes,
-                     bool prefill, qsa::AttnArgs *a) {
+                     bool prefill, qsa::AttnArgs *a, bool gather_only = false,
+                     int64_t ws_need = -1) {
     int rc = check_dims(dims);
     if (!rc) rc = check_seqs(dims, seqs);
     if (!rc) rc = check_queries(q_seq_dev, nullptr, n_q, false);
     if (rc) return rc;
     if (n_q == 0) return QSA_OK;
-    if (!q_dev || !aligned(q_dev, 16)) return fail(QSA_EINVAL, "q_dev NULL or not 16-byte aligned");
-    if (!out_dev || !aligned(out_dev, 4)) return fail(QSA_EINVAL, "out_dev NULL or misaligned");
+    if (!gather_only && (!q_dev || !aligned(q_dev, 16)))
+        return fail(QSA_EINVAL, "q_dev NULL or not 16-byte aligned");
+    if (!gather_only && (!out_dev || !aligned(out_dev, 4)))
+        return fail(QSA_EINVAL, "out_dev NULL or misaligned");
     if (!k_cache_dev || !v_cache_dev || !aligned(k_cache_dev, 16) || !aligned(v_cache_dev, 16))
         return fail(QSA_EINVAL, "K/V cache NULL or not 16-byte aligned");
     if (!sel_cells_dev || !n_sel_dev || !aligned(sel_cells_dev, 4) || !aligned(n_sel_dev, 4))
@@ -493,8 +502,10 @@ static int attn_args(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_
     if (cell_rows(seqs) * dims->n_head_kv >= ((int64_t)1 << 31))
         return fail(QSA_EINVAL, "K/V cache of 2^31 rows or more");
     const int ld_cells = dims->top_k + dims->r - 1;
-    const size_t need = prefill ? qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells)
-                                : qsa::attn_decode_ws_bytes(n_q, dims->n_head, ld_cells);
+    const size_t need = ws_need >= 0 ? (size_t)ws_need
+                        : gather_only ? 0
+                        : prefill     ? qsa::attn_prefill_ws_bytes(n_q, dims->n_head, ld_cells)
+                                      : qsa::attn_decode_ws_bytes(n_q, dims->n_head, ld_cells);
     if (need && (!ws_dev || ws_bytes < need || !aligned(ws_dev, 16)))
         return fail(QSA_EWS, "attention workspace needs %zu bytes, 16-byte aligned", need);
     const float scale =
@@ -528,6 +539,39 @@ int qsa_sparse_attn_decode(const qsa_dims *dims, const qsa_seqs *seqs, const flo
                            size_t ws_bytes, void *stream) {
     return attn_common(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
                        sel_cells_dev, n_sel_dev, out_dev, ws_dev, ws_bytes, stream, false);
+}
+
+int qsa_sparse_attn_decode_union(const qsa_dims *dims, const qsa_seqs *seqs, const float *q_dev,
+                                 const int32_t *q_seq_dev, int32_t n_q, int32_t t_group,
+                                 const void *k_cache_dev, const void *v_cache_dev,
+                                 const int32_t *sel_cells_dev, const int32_t *n_sel_dev,
+                                 float *out_dev, void *ws_dev, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims);
+    if (!rc) rc = check_seqs(dims, seqs);
+    if (rc) return rc;
+    if (t_group < 1 || t_group > qsa::kUnionMaxTokens)
+        return fail(QSA_EINVAL, "t_group %d outside 1..%d", t_group, qsa::kUnionMaxTokens);
+    if (dims->kv_type != QSA_KV_Q8_0)
+        return fail(QSA_ENOTSUP, "the union path reads q8_0 caches");
+    const int hpk = dims->n_head / dims->n_head_kv;
+    if (hpk < 4 || 16 % hpk)
+        return fail(QSA_ENOTSUP, "query heads per KV head %d: the union path takes 4, 8 or 16", hpk);
+    const int ld_cells = dims->top_k + dims->r - 1;
+    if ((int64_t)t_group * ld_cells > qsa::kUnionMaxEntries)
+        return fail(QSA_ENOTSUP, "t_group * (top_k + r - 1) = %lld above %d",
+                    (long long)t_group * ld_cells, qsa::kUnionMaxEntries);
+    if (seqs->cell_rows_dev) return fail(QSA_ENOTSUP, "the union path takes no cell table");
+    if (seqs->cap_cells >= ((int64_t)1 << 28))
+        return fail(QSA_ENOTSUP, "cap_cells of 2^28 or more");
+    const size_t need =
+        qsa::union_ws_bytes(n_q, t_group, dims->n_head, dims->n_head_kv, ld_cells);
+    qsa::AttnArgs a;
+    rc = attn_args(dims, seqs, q_dev, q_seq_dev, n_q, k_cache_dev, v_cache_dev, sel_cells_dev,
+                   n_sel_dev, out_dev, ws_dev, ws_bytes, false, &a, false, (int64_t)need);
+    if (rc) return rc;
+    if (n_q == 0) return ok();
+    return launched(qsa::launch_attn_decode_union(a, t_group, (hipStream_t)stream),
+                    "sparse_attn_decode_union");
 }
 
 int qsa_sparse_attn_decode_noalloc(const qsa_dims *dims, const qsa_seqs *seqs,
@@ -587,6 +631,38 @@ int qsa_decode_select_attend(const qsa_dims *dims, const qsa_seqs *seqs,
     if (n_q == 0) return ok();
     return launched(qsa::launch_select_attn_decode(f, (void *)ws_idx_dev, a, (hipStream_t)stream),
                     "decode_select_attend");
+}
+
+// ---- memory-traffic probes (include/qsa_probe.h) ----
+
+int qsa_probe_stream_read(const void *src_dev, size_t n_bytes, int32_t nontemporal,
+                          uint32_t *sink_dev, int32_t n_sink, void *stream) {
+    if (!src_dev || !aligned(src_dev, 16) || n_bytes % 16)
+        return fail(QSA_EINVAL, "probe source NULL, not 16-byte aligned, or not whole 16-byte words");
+    if (!sink_dev || !aligned(sink_dev, 4) || n_sink < 1)
+        return fail(QSA_EINVAL, "probe sink NULL, misaligned or empty");
+    if (n_bytes == 0) return ok();
+    return launched(qsa::launch_probe_read(src_dev, n_bytes, nontemporal != 0, sink_dev, n_sink,
+                                           (hipStream_t)stream),
+                    "probe_stream_read");
+}
+
+int qsa_probe_gather_prefill(const qsa_dims *dims, const qsa_seqs *seqs,
+                             const int32_t *q_seq_dev, int32_t n_q, const void *k_cache_dev,
+                             const void *v_cache_dev, const int32_t *sel_cells_dev,
+                             const int32_t *n_sel_dev, uint32_t *sink_dev, int32_t n_sink,
+                             void *stream) {
+    qsa::AttnArgs a;
+    int rc = attn_args(dims, seqs, nullptr, q_seq_dev, n_q, k_cache_dev, v_cache_dev,
+                       sel_cells_dev, n_sel_dev, nullptr, nullptr, 0, true, &a, true);
+    if (rc) return rc;
+    if (dims->kv_type != QSA_KV_Q8_0 || seqs->cell_rows_dev)
+        return fail(QSA_ENOTSUP, "the gather probe follows the q8_0 kernel without a cell table");
+    if (!sink_dev || !aligned(sink_dev, 4) || n_sink < 1)
+        return fail(QSA_EINVAL, "probe sink NULL, misaligned or empty");
+    if (n_q == 0) return ok();
+    return launched(qsa::launch_probe_gather_prefill(a, sink_dev, n_sink, (hipStream_t)stream),
+                    "probe_gather_prefill");
 }
 
 }  // extern "C"

@@ -308,54 +308,49 @@ __device__ __forceinline__ bool unit_of(const AttnArgs &a, int &i, int &g) {
     return i < a.n_q;
 }
 
-// 1-D grid of ceil(n_q / 8) * 8 * n_head_kv, 256 threads, two workgroups
-// per CU (LDS and registers are sized for two wavefronts per SIMD).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_q8(
-    AttnArgs a) {
-    __shared__ Q8Wave sw[kPWaves];
-    int i, g;
-    if (!unit_of(a, i, g)) return;
-    const int tid = threadIdx.x, wave = wave_id(), lane = tid & (kWave - 1);
-    const int col = lane & 15, quad = lane >> 4;  // MFMA column / k-quarter
-    const int hpk = a.n_head / a.n_head_kv;
-    Q8Wave &ws = sw[wave];
-    const QueryCtx qc = query_ctx(a, i);
-    const uint8_t *stage = reinterpret_cast<const uint8_t *>(ws.stage);
-
-    half8_t qa[8];
-    load_q_operand(a, i, g, hpk, col, quad, qa);
-    f32x4 o[16];  // O[row 4*quad + jj][dim 16*tt + col]
+// Lane l (and l + 32) holds the cell of chunk slot l % 32, -1 past the
+// list; the index is clamped so that every load is issued.
+__device__ __forceinline__ int chunk_cell_of(const AttnArgs &a, const QueryCtx &qc, int lane,
+                                             int c0) {
+    const int cc = c0 + (lane & 31);
+    const int v = qc.cells[min(cc, a.ld_cells - 1)];
+    return cc < qc.n ? v : -1;
+}
+// Row of a cell; a cell that is not present reads the sequence's cell 0.
+// (The row index fits 32 bits: the host rejects caches of 2^31 rows.)
+__device__ __forceinline__ uint32_t row_of_cell(const AttnArgs &a, const QueryCtx &qc, int g,
+                                                int cell) {
+    const bool ok = cell >= 0 && cell < qc.n_present;
+    return (uint32_t)((qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g);
+}
+// Loads K0 .. K1-1 of the chunk whose slot rows the lanes hold.
+template <typename K0, typename K1>
+__device__ __forceinline__ void issue_pieces(const AttnArgs &a, uint32_t row, int lane,
+                                             u32x4 (&R)[17], K0, K1) {
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        m_run[jj] = -INFINITY;
-        l_run[jj] = 0.f;
+    for (int k = K0::value; k < K1::value; ++k) {
+        const uint32_t r = (uint32_t)__shfl((int)row, piece_slot(k, lane));
+        const uint8_t *base = static_cast<const uint8_t *>(piece_kv(k, lane) ? a.v : a.k);
+        R[k] = *reinterpret_cast<const u32x4 *>(base + (uint64_t)r * kQ8Row +
+                                                piece_part(k, lane) * 16);
     }
+}
 
-    // Lane l (and l + 32) holds the cell of chunk slot l % 32, -1 past the
-    // list; the index is clamped so that every load is issued.
-    auto chunk_cell = [&](int c0) {
-        const int cc = c0 + (lane & 31);
-        const int v = qc.cells[min(cc, a.ld_cells - 1)];
-        return cc < qc.n ? v : -1;
-    };
-    // Row of a cell; a cell that is not present reads the sequence's cell 0.
-    auto row_of = [&](int cell) {
-        const bool ok = cell >= 0 && cell < qc.n_present;
-        // (the row index fits 32 bits: the host rejects caches of 2^31 rows)
-        return (uint32_t)((qc.row0 + (ok ? cell : 0)) * a.n_head_kv + g);
-    };
-    // Loads K0 .. K1-1 of the chunk whose slot rows the lanes hold.
+// One wavefront's walk over chunks c0 = first, first + step, ... < end of a
+// cell source, with its 16 A rows qa, into the online-softmax state (m_run,
+// l_run, o).  Src supplies, for lane l: at(c0), the handle of chunk slot
+// l % 32 (prefetched two chunks ahead); row(h), its K/V row; ok(h), whether
+// it is a cell to attend; and visible(cur, okmask, col, quad, c0), bit t set
+// when the lane's S rows may see slot 16t + col (okmask: the chunk's ok slots).
+template <class Src>
+__device__ __forceinline__ void q8_walk(const AttnArgs &a, Q8Wave &ws, const half8_t (&qa)[8],
+                                        int c0, int step, int end, const Src &src,
+                                        f32x4 (&o)[16], float (&m_run)[4], float (&l_run)[4]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15, quad = lane >> 4;  // MFMA column / k-quarter
+    const uint8_t *stage = reinterpret_cast<const uint8_t *>(ws.stage);
     auto issue = [&](uint32_t row, u32x4(&R)[17], auto k0, auto k1) {
-#pragma unroll
-        for (int k = decltype(k0)::value; k < decltype(k1)::value; ++k) {
-            const uint32_t r = (uint32_t)__shfl((int)row, piece_slot(k, lane));
-            const uint8_t *base = static_cast<const uint8_t *>(piece_kv(k, lane) ? a.v : a.k);
-            R[k] = *reinterpret_cast<const u32x4 *>(base + (uint64_t)r * kQ8Row +
-                                                    piece_part(k, lane) * 16);
-        }
+        issue_pieces(a, row, lane, R, k0, k1);
     };
     auto put = [&](int k, const u32x4 &v) {
         const int at = piece_slot(k, lane) * kQ8Row + piece_part(k, lane) * 16;
@@ -366,24 +361,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     using K17 = std::integral_constant<int, 17>;
 
     u32x4 R[17];
-    int c0 = wave * kPChunk;
-    int cur = -1, nxt = -1;
-    if (c0 < qc.n) {
-        cur = chunk_cell(c0);
-        nxt = chunk_cell(c0 + kStride);
-        issue(row_of(cur), R, K0{}, K17{});
+    typename Src::Handle cur = src.none(), nxt = src.none();
+    if (c0 < end) {
+        cur = src.at(c0);
+        nxt = src.at(c0 + step);
+        issue(src.row(cur), R, K0{}, K17{});
     }
-    for (; c0 < qc.n; c0 += kStride) {
-        const bool more = c0 + kStride < qc.n;
+    for (; c0 < end; c0 += step) {
+        const bool more = c0 + step < end;
         // K rows of chunk c0 to the stage (the previous chunk's V reads are
         // done), then the next chunk's K in flight
         wave_sync_lds();
 #pragma unroll
         for (int k = 0; k < 8; ++k) put(k, R[k]);
         if (lane < 32) put(16, R[16]);
-        const uint64_t okmask =
-            __ballot(lane < 32 && cur >= 0 && cur < qc.n_present) & 0xffffffffull;
-        if (more) issue(row_of(nxt), R, K0{}, K8{});
+        const uint64_t okmask = __ballot(lane < 32 && src.ok(cur)) & 0xffffffffull;
+        const uint32_t vis = src.visible(cur, okmask, col, quad, c0);
+        if (more) issue(src.row(nxt), R, K0{}, K8{});
         wave_sync_lds();
 
         // S tiles: column col of tile t is chunk slot 16t + col
@@ -408,8 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(d, r[jj], acc[jj]);
             }
-            if (!((okmask >> (16 * t + col)) & 1))
-                acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (!((vis >> t) & 1)) acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             sacc[t] = acc;
         }
         softmax_chunk(sacc, col, quad, m_run, l_run, o, ws.t);
@@ -420,16 +413,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int k = 8; k < 16; ++k) put(k, R[k]);
         if (lane >= 32) put(16, R[16]);
-        int nxt2 = -1;
+        typename Src::Handle nxt2 = src.none();
         if (more) {
-            issue(row_of(nxt), R, K8{}, K17{});
-            nxt2 = chunk_cell(c0 + 2 * kStride);
+            issue(src.row(nxt), R, K8{}, K17{});
+            nxt2 = src.at(c0 + 2 * step);
         }
         wave_sync_lds();
 
         // V to LDS transposed, 128 dims at a time: vt[dim - 128h][cell], the
         // lane's two cells (2*col, 2*col + 1) as one fp16 pair per dim; a cell
-        // that is not present gets scale 0 (its int8 are finite).  The four
+        // that is not attended gets scale 0 (its int8 are finite).  The four
         // quarter-waves write rows 8 apart at once, in different banks.
         const uint8_t *v0 = stage + (2 * col) * kQ8Row;
         const uint8_t *v1 = v0 + kQ8Row;
@@ -472,7 +465,422 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         cur = nxt;
         nxt = nxt2;
     }
+}
+
+// A query's own cell list: handles are cells (-1 past the list).
+struct ListSrc {
+    typedef int Handle;
+    const AttnArgs &a;
+    const QueryCtx &qc;
+    int g, lane;
+    __device__ Handle none() const { return -1; }
+    __device__ Handle at(int c0) const { return chunk_cell_of(a, qc, lane, c0); }
+    __device__ uint32_t row(Handle h) const { return row_of_cell(a, qc, g, h); }
+    __device__ bool ok(Handle h) const { return h >= 0 && h < qc.n_present; }
+    __device__ uint32_t visible(Handle, uint64_t okm, int col, int, int) const {
+        return (uint32_t)((okm >> col) & 1) | (uint32_t)(((okm >> (16 + col)) & 1) << 1);
+    }
+};
+
+__device__ __forceinline__ void init_state(f32x4 (&o)[16], float (&m_run)[4], float (&l_run)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        m_run[jj] = -INFINITY;
+        l_run[jj] = 0.f;
+    }
+}
+
+// 1-D grid of ceil(n_q / 8) * 8 * n_head_kv, 256 threads, two workgroups
+// per CU (LDS and registers are sized for two wavefronts per SIMD).  The
+// four wavefronts take the chunks of the query's list in turn.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_prefill_q8(
+    AttnArgs a) {
+    __shared__ Q8Wave sw[kPWaves];
+    int i, g;
+    if (!unit_of(a, i, g)) return;
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+    const int col = lane & 15, quad = lane >> 4;
+    const int hpk = a.n_head / a.n_head_kv;
+    const QueryCtx qc = query_ctx(a, i);
+    half8_t qa[8];
+    load_q_operand(a, i, g, hpk, col, quad, qa);
+    f32x4 o[16];  // O[row 4*quad + jj][dim 16*tt + col]
+    float m_run[4], l_run[4];
+    init_state(o, m_run, l_run);
+    const ListSrc src{a, qc, g, lane};
+    q8_walk(a, sw[wave], qa, wave * kPChunk, kStride, qc.n, src, o, m_run, l_run);
     merge_store(a, i, g, hpk, sw, o, m_run, l_run);
+}
+
+// ---- several decode tokens of a sequence over the union of their lists ----
+//
+// Tokens are taken t_group at a time (the last group may be shorter).  Per
+// group, k_union_build lists every K/V row any token of the group attends
+// (ascending) with a bit per token that holds it; k_attn_union_q8 walks that
+// union in runs of kURun rows, each workgroup staging a run's rows once for
+// all tokens of the group: wavefront w takes the query heads of KV head g of
+// 16 / hpk tokens as its 16 A rows (8 heads of 2 tokens for 16 heads over 2
+// KV heads), scores every staged row, and a row a token does not hold gets
+// -inf before that token's softmax.  Each (token, head) keeps its own online
+// softmax; its per-run partial states are merged by k_union_combine.
+
+constexpr int kUnionNT = 1024;
+constexpr int kUnionMaxT = 8;
+constexpr int kUnionCap = kUnionMaxEntries;  // union entries per group: t_group * ld_cells at most
+constexpr int kURun = 4 * kPChunk;  // union rows per attention workgroup
+
+// Exclusive prefix sum over the workgroup (kUnionNT threads) and the total.
+__device__ __forceinline__ uint32_t union_scan(uint32_t v, uint32_t *s_w, uint32_t &total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_incl_scan_u32(v);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kUnionNT / kWave; ++w) {
+        const uint32_t x = s_w[w];
+        before += w < wave ? x : 0u;
+        all += x;
+    }
+    __syncthreads();  // s_w may be reused
+    total = all;
+    return before + inc - v;
+}
+
+// grid (n_groups), kUnionNT threads.  Token t's valid cells (in 0 ..
+// n_present-1 of its sequence, the first n_sel entries of its list) are
+// keyed (cell << 3) | t.  If every valid token of the group is in one
+// sequence and every list strictly ascends, the lists are merged (pairs of
+// adjacent runs by merge path, log2 t_group rounds) and equal cells fold into
+// one entry with the OR of their token bits; otherwise the lists are
+// concatenated, one entry and one bit per (token, cell), which attends
+// exactly the same cells.
+__global__ __launch_bounds__(kUnionNT) void k_union_build(AttnArgs a, UnionArgs u) {
+    __shared__ uint32_t s_buf[2][kUnionCap];
+    __shared__ int s_off[kUnionMaxT + 1];  // start of token t's entries; s_off[T] = total
+    __shared__ int s_seq[kUnionMaxT];
+    __shared__ uint32_t s_w[kUnionNT / kWave];
+    __shared__ int s_bad;
+    const int gi = blockIdx.x, tid = threadIdx.x;
+    const int q0 = gi * u.t_group;
+    const int T = min(u.t_group, a.n_q - q0);
+    const int ld = a.ld_cells;
+    if (tid == 0) {
+        s_off[0] = 0;
+        s_bad = 0;
+    }
+    __syncthreads();
+    // 1. each token's valid entries, compacted in order
+    for (int t = 0; t < T; ++t) {  // workgroup-uniform
+        const int q = q0 + t;
+        const int s = a.q_seq[q];
+        const bool qvalid = s >= 0 && s < a.g.n_seq;
+        const int n_raw = qvalid ? a.n_sel[q] : 0;
+        const int n = n_raw < 0 ? 0 : (n_raw > ld ? ld : n_raw);
+        int64_t np = qvalid ? a.g.n_cells[s] : 0;
+        np = np < a.g.cap_cells ? np : a.g.cap_cells;
+        const int32_t *cells = a.sel_cells + (int64_t)q * ld;
+        // thread tid takes entries [tid*per, tid*per + per): contiguous, in order
+        const int per = (n + kUnionNT - 1) / kUnionNT;
+        uint32_t cnt = 0;
+        for (int k = tid * per; k < min(n, tid * per + per); ++k) {
+            const int c = cells[k];
+            cnt += (c >= 0 && c < np) ? 1u : 0u;
+        }
+        uint32_t total;
+        uint32_t at = union_scan(cnt, s_w, total) + (uint32_t)s_off[t];
+        for (int k = tid * per; k < min(n, tid * per + per); ++k) {
+            const int c = cells[k];
+            if (c >= 0 && c < np) s_buf[0][at++] = ((uint32_t)c << 3) | (uint32_t)t;
+        }
+        if (tid == 0) {
+            s_off[t + 1] = s_off[t] + (int)total;
+            s_seq[t] = total > 0 ? s : -1;
+        }
+        __syncthreads();
+    }
+    const int E = s_off[T];
+    int32_t *urow = u.urow + (int64_t)gi * u.cap;
+    uint8_t *umask = u.umask + (int64_t)gi * u.cap;
+    // 2. merge only lists of one sequence that strictly ascend
+    int s0 = -1;
+    for (int t = 0; t < T; ++t) {
+        const int st = s_seq[t];
+        if (st >= 0) {
+            if (s0 < 0) s0 = st;
+            else if (st != s0) s_bad = 1;  // (benign race: every writer writes 1)
+        }
+    }
+    for (int e = tid; e < E; e += kUnionNT) {
+        const uint32_t k = s_buf[0][e];
+        const int t = (int)(k & 7u);
+        if (e > s_off[t] && (s_buf[0][e - 1] >> 3) >= (k >> 3)) s_bad = 1;
+    }
+    __syncthreads();
+    if (s_bad) {
+        for (int e = tid; e < E; e += kUnionNT) {
+            const uint32_t k = s_buf[0][e];
+            const int t = (int)(k & 7u);
+            urow[e] = (int32_t)((int64_t)s_seq[t] * a.g.cap_cells + (k >> 3));
+            umask[e] = (uint8_t)(1u << t);
+        }
+        if (tid == 0) u.n_union[gi] = E;
+        return;
+    }
+    // 3. merge path: runs [s_off[t], s_off[t+1]) merged two by two; a merged
+    // pair keeps the place of the pair, so the run bounds just halve
+    int src = 0;
+    for (int width = 1; width < T; width *= 2) {
+        const int per = (E + kUnionNT - 1) / kUnionNT;
+        for (int p = tid * per; p < min(E, tid * per + per);) {
+            // the pair holding output position p: runs r0 = 2*width*k .. +width, then the next width
+            int r0 = 0;
+            while (r0 + 2 * width <= T && s_off[min(r0 + 2 * width, T)] <= p) r0 += 2 * width;
+            const int a0 = s_off[r0], a1 = s_off[min(r0 + width, T)], b1 = s_off[min(r0 + 2 * width, T)];
+            const uint32_t *A = s_buf[src] + a0, *B = s_buf[src] + a1;
+            const int na = a1 - a0, nb = b1 - a1;
+            const int d = p - a0;
+            int lo = max(0, d - nb), hi = min(d, na);
+            while (lo < hi) {  // A elements among the first d outputs (keys are distinct)
+                const int mid = (lo + hi) >> 1;
+                if (A[mid] < B[d - mid - 1]) lo = mid + 1;
+                else hi = mid;
+            }
+            int i = lo, j = d - lo;
+            const int stop = min(min(E, tid * per + per), b1);
+            for (; p < stop; ++p) {
+                const bool take_a = i < na && (j >= nb || A[i] < B[j]);
+                s_buf[src ^ 1][p] = take_a ? A[i++] : B[j++];
+            }
+        }
+        __syncthreads();
+        src ^= 1;
+    }
+    // 4. fold equal cells: a first occurrence gathers the bits of its run
+    const uint32_t *M = s_buf[src];
+    const int per = (E + kUnionNT - 1) / kUnionNT;
+    const int e0 = min(E, tid * per), e1 = min(E, tid * per + per);
+    uint32_t cnt = 0;
+    for (int e = e0; e < e1; ++e) cnt += (e == 0 || (M[e] >> 3) != (M[e - 1] >> 3)) ? 1u : 0u;
+    uint32_t total;
+    uint32_t at = union_scan(cnt, s_w, total);
+    for (int e = e0; e < e1; ++e) {
+        const uint32_t cell = M[e] >> 3;
+        if (e > 0 && (M[e - 1] >> 3) == cell) continue;
+        uint32_t bits = 0;
+        for (int f = e; f < E && (M[f] >> 3) == cell; ++f) bits |= 1u << (M[f] & 7u);
+        urow[at] = (int32_t)((int64_t)s0 * a.g.cap_cells + cell);
+        umask[at] = (uint8_t)bits;
+        ++at;
+    }
+    if (tid == 0) u.n_union[gi] = (int32_t)total;
+}
+
+// The union's rows as a cell source: handles are rows (-1 past the run); the
+// token bits of the run's rows sit in LDS (bits[e - c_begin]).
+struct UnionSrc {
+    typedef int Handle;
+    const int32_t *urow;
+    const uint8_t *bits;
+    int c_begin, end, g, n_head_kv, tok0, hpk;  // (all wavefront-uniform)
+    __device__ Handle none() const { return -1; }
+    __device__ Handle at(int c0) const {
+        // (a clamped, unconditional load; end >= 1 whenever a chunk is walked)
+        const int e = c0 + (int)(threadIdx.x & 31);
+        const int r = urow[min(e, max(end - 1, 0))];
+        return e < end ? r : -1;
+    }
+    __device__ uint32_t row(Handle h) const {
+        return (uint32_t)(h < 0 ? 0 : h) * (uint32_t)n_head_kv + (uint32_t)g;
+    }
+    __device__ bool ok(Handle h) const { return h >= 0; }
+    __device__ uint32_t visible(Handle, uint64_t okm, int col, int quad, int c0) const {
+        // the lane's S rows 4*quad .. +3 belong to one token (hpk >= 4)
+        const int tok = tok0 + 4 * quad / hpk;
+        const int e0 = c0 - c_begin + col;  // (slots past the run are not ok)
+        const uint32_t b0 = (uint32_t)(okm >> col) & ((uint32_t)bits[e0] >> tok) & 1u;
+        const uint32_t b1 =
+            (uint32_t)(okm >> (16 + col)) & ((uint32_t)bits[e0 + 16] >> tok) & 1u;
+        return b0 | (b1 << 1);
+    }
+};
+
+// grid (n_groups * n_head_kv * n_runs * n_slices), 256 threads: workgroup
+// (group gi, KV head g, run, token slice); wavefront w of slice sl takes
+// tokens (4*sl + w) * tpw .. + tpw - 1 (tpw = 16 / hpk), its row col being
+// head col % hpk of token col / hpk.  Each wavefront walks every chunk of the
+// run and writes its rows' partial states (o[256], m, l) for the combine.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_union_q8(
+    AttnArgs a, UnionArgs u) {
+    __shared__ Q8Wave sw[kPWaves];
+    __shared__ uint8_t s_bits[kURun + kPChunk];  // token bits of the run's rows (zero past it)
+    const int hpk = a.n_head / a.n_head_kv, tpw = 16 / hpk;
+    const int n_slices = (u.t_group + kPWaves * tpw - 1) / (kPWaves * tpw);
+    int id = blockIdx.x;
+    const int sl = id % n_slices;
+    id /= n_slices;
+    const int run = id % u.n_runs;
+    id /= u.n_runs;
+    const int g = id % a.n_head_kv, gi = id / a.n_head_kv;
+    const int n = u.n_union[gi];
+    const int c_begin = run * kURun, c_end = min(n, c_begin + kURun);
+    if (c_begin >= c_end) return;
+    const int wave = wave_id();
+    int col = threadIdx.x & 15, quad = (threadIdx.x >> 4) & 3;
+    const int q0 = gi * u.t_group;
+    const int T = min(u.t_group, a.n_q - q0);
+    const int tok0 = (sl * kPWaves + wave) * tpw;
+    const uint8_t *umask = u.umask + (int64_t)gi * u.cap;
+    if (threadIdx.x < kURun + kPChunk) {
+        const int e = c_begin + (int)threadIdx.x;
+        s_bits[threadIdx.x] = e < c_end ? umask[e] : (uint8_t)0;
+    }
+    __syncthreads();
+    if (tok0 >= T) return;  // (no workgroup barrier follows)
+    // A rows: row col = head g*hpk + col % hpk of token tok0 + col / hpk
+    half8_t qa[8];
+    {
+        const int t = tok0 + col / hpk;
+        const bool live = t < T;
+        const int qi = q0 + (live ? t : 0);
+        const float4 *qp = reinterpret_cast<const float4 *>(
+            a.q + ((int64_t)qi * a.n_head + g * hpk + col % hpk) * kHeadDim + 8 * quad);
+        float4 raw[16];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            raw[2 * kb] = qp[8 * kb];
+            raw[2 * kb + 1] = qp[8 * kb + 1];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            const float4 p0 = raw[2 * kb], p1 = raw[2 * kb + 1];
+            const float x[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = live ? x[e] * a.scale : 0.0f;
+            qa[kb] = to_half8(y);
+        }
+    }
+    f32x4 o[16];
+    float m_run[4], l_run[4];
+    init_state(o, m_run, l_run);
+    const UnionSrc src{u.urow + (int64_t)gi * u.cap, s_bits, c_begin, c_end, g,
+                       a.n_head_kv, tok0, hpk};
+    q8_walk(a, sw[wave], qa, c_begin, kPChunk, c_end, src, o, m_run, l_run);
+    // partial states of the wavefront's rows that are tokens of the group
+    // (the lane index is taken afresh: nothing per lane stays live across the walk)
+    {
+        const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        col = ln & 15;
+        quad = ln >> 4;
+    }
+    const int rows = u.t_group * hpk;
+    float *base = u.part + (((int64_t)gi * a.n_head_kv + g) * u.n_runs + run) * rows * kUPartStride;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int r = 4 * quad + jj;
+        const int t = tok0 + r / hpk;
+        if (t >= T) continue;
+        float *pr = base + (int64_t)(t * hpk + r % hpk) * kUPartStride;
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) pr[16 * tt + col] = o[tt][jj];
+        if (col == 0) {
+            pr[kHeadDim] = m_run[jj];
+            pr[kHeadDim + 1] = l_run[jj];
+        }
+    }
+}
+
+// grid (n_q * n_head), 256 threads: out[q][h] from the partial states of its
+// group's runs (every run below ceil(n_union / kURun) was written for every
+// token of the group: o = 0, m = -inf, l = 0 where the token saw no row).
+__global__ __launch_bounds__(256) void k_union_combine(AttnArgs a, UnionArgs u) {
+    __shared__ float s_m[(kUnionCap + kURun - 1) / kURun];
+    __shared__ float s_red[4];
+    const int q = blockIdx.x / a.n_head, h = blockIdx.x % a.n_head;
+    const int tid = threadIdx.x;
+    const int hpk = a.n_head / a.n_head_kv, g = h / hpk;
+    const int gi = q / u.t_group, t = q % u.t_group;
+    const int runs = (u.n_union[gi] + kURun - 1) / kURun;
+    const int rows = u.t_group * hpk;
+    const float *base = u.part + ((int64_t)gi * a.n_head_kv + g) * u.n_runs * rows * kUPartStride +
+                        (int64_t)(t * hpk + h % hpk) * kUPartStride;
+    const int64_t stride = (int64_t)rows * kUPartStride;
+    float mloc = -INFINITY;
+    for (int r = tid; r < runs; r += 256) {
+        const float m = base[r * stride + kHeadDim], l = base[r * stride + kHeadDim + 1];
+        const float mm = l > 0.f ? m : -INFINITY;
+        s_m[r] = mm;
+        mloc = fmaxf(mloc, mm);
+    }
+    mloc = wave_max_f32(mloc);
+    if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    // thread tid = output dim: sum over runs in order, 8 runs' loads at once
+    // (clamped to the last run; a run past the end, or one where the token
+    // saw no row, weighs 0)
+    float acc = 0.f, L = 0.f;
+    for (int r0 = 0; r0 < runs; r0 += 8) {
+        float v[8], lv[8], w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t rr = min(r0 + k, runs - 1);
+            v[k] = base[rr * stride + tid];
+            lv[k] = base[rr * stride + kHeadDim + 1];
+            const float m = r0 + k < runs ? s_m[r0 + k] : -INFINITY;
+            w[k] = m == -INFINITY ? 0.f : __expf(m - M);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            acc = fmaf(v[k], w[k], acc);
+            L = fmaf(lv[k], w[k], L);
+        }
+    }
+    a.out[((int64_t)q * a.n_head + h) * kHeadDim + tid] = L > 0.f ? acc / L : 0.f;
+}
+
+// ---- the gather alone ----
+
+// The row gather of k_attn_prefill_q8 without its arithmetic: the same
+// grid, units and chunk walk, the same 17 loads of 16 bytes per lane and
+// chunk (padding slots of a last chunk read the sequence's cell 0, as
+// there), two chunks in flight.  The loaded words are XOR-folded into
+// sink[workgroup % n_sink], so that the loads cannot be dropped; the fold of
+// every sink word is the XOR of every 32-bit word the kernel loaded.
+__global__ __launch_bounds__(256) void k_probe_gather_q8(AttnArgs a, uint32_t *sink, int n_sink) {
+    int i, g;
+    if (!unit_of(a, i, g)) return;
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+    const QueryCtx qc = query_ctx(a, i);
+    using K0 = std::integral_constant<int, 0>;
+    using K17 = std::integral_constant<int, 17>;
+    uint32_t acc = 0;
+    for (int c0 = wave * kPChunk; c0 < qc.n; c0 += 2 * kStride) {
+        u32x4 R[2][17];
+        const bool two = c0 + kStride < qc.n;
+        issue_pieces(a, row_of_cell(a, qc, g, chunk_cell_of(a, qc, lane, c0)), lane, R[0], K0{},
+                     K17{});
+        if (two)
+            issue_pieces(a, row_of_cell(a, qc, g, chunk_cell_of(a, qc, lane, c0 + kStride)),
+                         lane, R[1], K0{}, K17{});
+#pragma unroll
+        for (int k = 0; k < 17; ++k) {
+            // the tail load (k = 16) is the K row's for lanes < 32, V's above;
+            // both are loaded, as in the kernel above
+            acc ^= R[0][k][0] ^ R[0][k][1] ^ R[0][k][2] ^ R[0][k][3];
+            if (two) acc ^= R[1][k][0] ^ R[1][k][1] ^ R[1][k][2] ^ R[1][k][3];
+        }
+    }
+    acc ^= xor_lane<1>(acc);
+    acc ^= xor_lane<2>(acc);
+    acc ^= xor_lane<4>(acc);
+    acc ^= xor_lane<8>(acc);
+    acc ^= xor_lane<16>(acc);
+    acc ^= xor_lane<32>(acc);
+    if (lane == 0) atomicXor(&sink[blockIdx.x % n_sink], acc);
 }
 
 // ---- rows gathered per lane: f32 and f16 caches, and q8_0 through a cell table ----
@@ -553,6 +961,54 @@ __global__ __launch_bounds__(256) void k_attn_prefill_rows(AttnArgs a) {
 }  // namespace
 
 size_t attn_prefill_ws_bytes(int, int, int) { return 0; }
+
+size_t union_ws_bytes(int n_q, int t_group, int n_head, int n_head_kv, int ld_cells) {
+    return union_layout(nullptr, n_q, t_group, n_head, n_head_kv, ld_cells, nullptr);
+}
+
+size_t union_layout(char *base, int n_q, int t_group, int n_head, int n_head_kv, int ld_cells,
+                    UnionArgs *u) {
+    UnionArgs d{};
+    d.t_group = t_group;
+    d.n_groups = t_group > 0 ? (n_q + t_group - 1) / t_group : 0;
+    d.cap = t_group * ld_cells;
+    d.n_runs = (d.cap + kURun - 1) / kURun;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return base ? base + at : nullptr;
+    };
+    d.urow = reinterpret_cast<int32_t *>(take((size_t)d.n_groups * d.cap * 4));
+    d.umask = reinterpret_cast<uint8_t *>(take((size_t)d.n_groups * d.cap));
+    d.n_union = reinterpret_cast<int32_t *>(take((size_t)d.n_groups * 4));
+    d.part = reinterpret_cast<float *>(take((size_t)d.n_groups * n_head_kv * d.n_runs *
+                                            (t_group * (n_head / n_head_kv)) * kUPartStride * 4));
+    if (u) *u = d;
+    return n_q > 0 ? off : 0;
+}
+
+hipError_t launch_attn_decode_union(const AttnArgs &a, int t_group, hipStream_t st) {
+    if (a.n_q <= 0) return hipSuccess;
+    UnionArgs u;
+    union_layout(reinterpret_cast<char *>(a.ws), a.n_q, t_group, a.n_head, a.n_head_kv,
+                 a.ld_cells, &u);
+    hipLaunchKernelGGL(k_union_build, dim3(u.n_groups), dim3(kUnionNT), 0, st, a, u);
+    const int hpk = a.n_head / a.n_head_kv, tpw = 16 / hpk;
+    const int n_slices = (t_group + kPWaves * tpw - 1) / (kPWaves * tpw);
+    const int grid = u.n_groups * a.n_head_kv * u.n_runs * n_slices;
+    hipLaunchKernelGGL(k_attn_union_q8, dim3(grid), dim3(256), 0, st, a, u);
+    hipLaunchKernelGGL(k_union_combine, dim3(a.n_q * a.n_head), dim3(256), 0, st, a, u);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_gather_prefill(const AttnArgs &a, uint32_t *sink, int n_sink,
+                                       hipStream_t st) {
+    if (a.n_q <= 0) return hipSuccess;
+    const dim3 grid((a.n_q + 7) / 8 * 8 * a.n_head_kv);
+    hipLaunchKernelGGL(k_probe_gather_q8, grid, dim3(256), 0, st, a, sink, n_sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;

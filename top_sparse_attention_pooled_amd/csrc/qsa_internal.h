@@ -396,6 +396,34 @@ size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
 size_t attn_prefill_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st);
+
+// Decode tokens in groups over the union of their cell lists
+// (attn_prefill.hip).  Workspace: the union rows and token bits per group,
+// the union sizes, then the per-run partial states of every (token, head).
+constexpr int kUPartStride = kHeadDim + 2;  // o[256], m, l
+struct UnionArgs {
+    int32_t t_group;   // tokens per group
+    int32_t n_groups;
+    int32_t cap;       // union entries per group: t_group * ld_cells
+    int32_t n_runs;    // attention runs per (group, KV head): ceil(cap / run length)
+    int32_t *urow;     // [n_groups][cap] K/V cell rows (s * cap_cells + cell), ascending
+    uint8_t *umask;    // [n_groups][cap] bit t: token t of the group holds the row
+    int32_t *n_union;  // [n_groups]
+    float *part;       // [n_groups][n_head_kv][n_runs][t_group * hpk][kUPartStride]
+};
+size_t union_layout(char *base, int n_q, int t_group, int n_head, int n_head_kv, int ld_cells,
+                    UnionArgs *u);
+size_t union_ws_bytes(int n_q, int t_group, int n_head, int n_head_kv, int ld_cells);
+hipError_t launch_attn_decode_union(const AttnArgs &a, int t_group, hipStream_t st);
+constexpr int kUnionMaxTokens = 8;
+constexpr int kUnionMaxEntries = 16448;  // 8 tokens of top_k + r - 1 = 2056 cells
+
+// Memory-traffic probes (probe.hip, attn_prefill.hip): loads only, folded
+// into sink[workgroup % n_sink] by XOR.
+hipError_t launch_probe_read(const void *src, size_t n_bytes, bool nontemporal, uint32_t *sink,
+                             int n_sink, hipStream_t st);
+hipError_t launch_probe_gather_prefill(const AttnArgs &a, uint32_t *sink, int n_sink,
+                                       hipStream_t st);
 // decode selection (from the candidates in ws_idx) fused with attention; the
 // attention workspace is the one launch_attn_decode uses
 hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnArgs &a,

@@ -21,6 +21,7 @@ KIDX_F32, KIDX_BF16 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
 OP_SELECT, OP_ATTN_DECODE, OP_ATTN_PREFILL, OP_SCORE_BF16, OP_SCORE_SELECT = 0, 1, 2, 3, 4
 OP_SCORE_SELECT_PREFILL = 5
+OP_ATTN_DECODE_UNION = 6  # the nb_max argument of workspace_size carries t_group
 TILE = 64
 
 EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
@@ -28,7 +29,9 @@ EXPORTS = ("qsa_version", "qsa_last_error", "qsa_workspace_size",
            "qsa_score_select_decode", "qsa_decode_score_candidates",
            "qsa_decode_select_candidates", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill",
            "qsa_decode_select_attend", "qsa_score_select_prefill", "qsa_detect_dirty_blocks",
-           "qsa_sparse_attn_decode_noalloc")
+           "qsa_sparse_attn_decode_noalloc", "qsa_sparse_attn_decode_union",
+           # memory-traffic probes (include/qsa_probe.h)
+           "qsa_probe_stream_read", "qsa_probe_gather_prefill")
 
 
 class QsaError(RuntimeError):
@@ -97,6 +100,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_sparse_attn_decode_union.restype = ctypes.c_int
+    lib.qsa_sparse_attn_decode_union.argtypes = [D, S, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                                 sz, vp]
     lib.qsa_sparse_attn_decode_noalloc.restype = ctypes.c_int
     lib.qsa_sparse_attn_decode_noalloc.argtypes = [D, S, vp, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.qsa_score_select_prefill.restype = ctypes.c_int
@@ -105,6 +111,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_decode_select_attend.restype = ctypes.c_int
     lib.qsa_decode_select_attend.argtypes = [D, S, vp, vp, i32, i32, vp, i64, vp, vp, vp, vp, sz,
                                              vp, vp, vp, vp, vp, sz, vp]
+    lib.qsa_probe_stream_read.restype = ctypes.c_int
+    lib.qsa_probe_stream_read.argtypes = [vp, sz, i32, vp, i32, vp]
+    lib.qsa_probe_gather_prefill.restype = ctypes.c_int
+    lib.qsa_probe_gather_prefill.argtypes = [D, S, vp, i32, vp, vp, vp, vp, vp, i32, vp]
     _lib = lib
     return lib
 
@@ -287,6 +297,33 @@ def sparse_attn_prefill(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, k_cache, v_c
                                        _ptr(q_seq), n_q, _ptr(k_cache), _ptr(v_cache),
                                        _ptr(sel_cells), _ptr(n_sel), _ptr(out), _ptr(ws),
                                        ws_bytes, _stream(stream)))
+
+
+def sparse_attn_decode_union(dims: Dims, seqs: Seqs, q, q_seq, n_q: int, t_group: int,
+                             k_cache, v_cache, sel_cells, n_sel, out, ws=None, ws_bytes: int = 0,
+                             stream=None) -> None:
+    """Decode attention of queries in groups of t_group over the union of
+    each group's cell lists (include/qsa.h)."""
+    _rc(load().qsa_sparse_attn_decode_union(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                            _ptr(q), _ptr(q_seq), n_q, t_group, _ptr(k_cache),
+                                            _ptr(v_cache), _ptr(sel_cells), _ptr(n_sel),
+                                            _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def probe_stream_read(src, n_bytes: int, sink, n_sink: int, nontemporal: bool = True,
+                      stream=None) -> None:
+    """Memory-traffic probe: read n_bytes of src once (include/qsa_probe.h)."""
+    _rc(load().qsa_probe_stream_read(_ptr(src), n_bytes, int(nontemporal), _ptr(sink), n_sink,
+                                     _stream(stream)))
+
+
+def probe_gather_prefill(dims: Dims, seqs: Seqs, q_seq, n_q: int, k_cache, v_cache, sel_cells,
+                         n_sel, sink, n_sink: int, stream=None) -> None:
+    """Memory-traffic probe: the K/V row gather of sparse_attn_prefill alone."""
+    _rc(load().qsa_probe_gather_prefill(ctypes.byref(dims.c()), ctypes.byref(seqs.c()),
+                                        _ptr(q_seq), n_q, _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(sel_cells), _ptr(n_sel), _ptr(sink), n_sink,
+                                        _stream(stream)))
 
 
 def pooled_numel(n_seq: int, cap_cells: int, r: int, d_idx: int = 128) -> int:
