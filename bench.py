@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None,
-                    choices=["decode50k", "decode250k", "decode5x250k", "prefill", "prefill_ar1"],
+                    choices=["decode50k", "decode250k", "decode5x250k", "verify5x250k",
+                             "verify5x250k_ar1", "prefill", "prefill_ar1"],
                     help="one workload alone (default: decode250k plus the prefill ubatch)")
     ap.add_argument("--kv", default="q8_0", choices=["q8_0", "f16"],
                     help="K/V cache type of a decode workload (the workloads are defined "
@@ -388,6 +389,105 @@ def run_decode(args, torch, dev, name):
 
 
 # ---------------------------------------------------------------------------
+# several tokens per sequence (a verify step)
+# ---------------------------------------------------------------------------
+
+def run_verify(args, torch, dev, name):
+    """A step = the sequence's 5 new tokens through every layer: update,
+    scores and candidates of all 5 (one call), the exact selection of each,
+    then attention (a) over the union of the 5 lists, each K/V row staged once
+    for the tokens that list it (qsa_sparse_attn_decode_union), or (b) per
+    token (qsa_decode_select_attend, which selects and attends per query);
+    and (c) the first token alone through the 1-token path.  value = us per
+    token per layer of (a)."""
+    from top_sparse_attention_pooled_amd import qsa, runtime, synth
+    K, W, L = args.steps, args.warmup, args.layers
+    w, layers, inp, host = setup(torch, dev, name, K, W, L)
+    T = W + K
+    q_idx, q, q_seq, q_pos = inp["q_idx"], inp["q"], inp["q_seq"], inp["q_pos"]
+    n_cells, dirty, n_dirty = inp["n_cells"], inp["dirty"], inp["n_dirty"]
+    n_q, nb_max = inp["n_q"], inp["nb_max"]
+    d0 = layers[0].dims
+    bufs = [runtime.StepBuffers(d0, n_q, nb_max, dev) for _ in range(L)]
+    bufs1 = [runtime.StepBuffers(d0, 1, nb_max, dev) for _ in range(L)]
+    u_bytes = qsa.workspace_size(d0, qsa.OP_ATTN_DECODE_UNION, n_q, n_q)
+    u_ws = [torch.empty(max(u_bytes, 16), dtype=torch.uint8, device=dev) for _ in range(L)]
+    stream = torch.cuda.Stream()
+
+    def enqueue(t, part="union"):
+        for li, layer in enumerate(layers):
+            layer.n_cells = n_cells[t]
+            d, sq = layer.dims, layer.seqs()
+            bf = bufs[li] if part != "one" else bufs1[li]
+            m = n_q if part != "one" else 1
+            qsa.decode_score_candidates(d, sq, layer.kidx, dirty[t], n_dirty, layer.pooled,
+                                        layer.pooled_bf16, q_idx[t], q_seq[t], q_pos[t], m,
+                                        nb_max, bf.scores, bf.ld, bf.ws_fused, bf.ws_fused_bytes)
+            if part == "union":
+                qsa.decode_select_candidates(d, sq, q_seq[t], q_pos[t], m, nb_max, bf.scores,
+                                             bf.ld, bf.sel_blocks, bf.sel_cells, bf.n_sel,
+                                             bf.ws_fused, bf.ws_fused_bytes)
+                qsa.sparse_attn_decode_union(d, sq, q[t], q_seq[t], m, m, layer.k, layer.v,
+                                             bf.sel_cells, bf.n_sel, bf.out, u_ws[li], u_bytes)
+            else:
+                qsa.decode_select_attend(d, sq, q_seq[t], q_pos[t], m, nb_max, bf.scores,
+                                         bf.ld, bf.sel_blocks, bf.sel_cells, bf.n_sel,
+                                         bf.ws_fused, bf.ws_fused_bytes, q[t], layer.k, layer.v,
+                                         bf.out, bf.ws_attn, bf.ws_attn_bytes)
+
+    timer = Timer(torch, stream, enqueue, args.eager)
+    t_main = timer.run(W, T)
+    res_us = {"union": t_main * 1e6 / (K * L)}
+    if not args.eager:
+        for part in ("per_token", "one"):
+            res_us[part] = timer.part(W, T, K * L, part=part)
+    n_sel = bufs[0].n_sel.cpu().numpy()
+    assert np.all(n_sel > 0), "empty selections in the benchmark step"
+    # union size of the last step, layer 0 (the union workspace's n_union)
+    ld = d0.ld_cells
+    cap = n_q * ld
+    rnd = lambda x: -(-x // 256) * 256
+    n_union = int(u_ws[0][rnd(cap * 4) + rnd(cap):][:4].view(torch.int32).item())
+    listed = int(n_sel.sum())
+    per_tok = {k: round(v / (n_q if k != "one" else 1), 3) for k, v in res_us.items()}
+    # algorithmic bytes per step: the pooled keys once, the union's K/V rows once
+    nb = w.nb_max(K + W - 1)
+    kv_row = w.Hk * synth.row_bytes(w.kv_type, w.D) * 2
+    step_bytes = nb * w.d * 4 + n_union * kv_row
+    result = {
+        "metric": METRIC, "value": per_tok["union"], "unit": "us/token", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(t_main * 1000.0 / K, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 scores and selection; fp16 attention operands over q8_0 KV (fp32 sums)",
+        "data": "synthetic: i.i.d. N(0,1) indexer keys, queries and K/V (q8_0-packed), seeded"
+                + ("; indexer queries AR(1) along the step's tokens, rho %g" % w.extra["qidx_ar1"]
+                   if w.extra.get("qidx_ar1") else ""),
+        "config": {"workload": name, "n_seq": 1, "tokens_per_step": n_q,
+                   "n_kv_start": w.n_cells0 + w.n_new, "decode_steps": K, "q_heads": w.H,
+                   "kv_heads": w.Hk, "head_dim": w.D, "top_k": w.top_k, "layers_per_step": L,
+                   "graph_replay": not args.eager},
+        "us_per_token_layer": {"union_attention": per_tok["union"],
+                               "per_token_attention": per_tok.get("per_token"),
+                               "one_token_step": per_tok.get("one")},
+        "us_per_step_layer": {k: round(v, 3) for k, v in res_us.items()},
+        "union": {"rows": n_union, "listed_cells": listed,
+                  "rows_per_listed": round(n_union / max(listed, 1), 3)},
+        "roofline": {
+            "kernel": "the whole verify step (update, scores, selection, union attention)",
+            "timing": "graph replay of K steps x L layers",
+            "bound": "hbm",
+            "bytes_per_step": int(step_bytes),
+            "achieved": round(step_bytes / (res_us["union"] * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(step_bytes / (res_us["union"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    del layers, bufs, bufs1, inp
+    return result
+
+
+# ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
 
@@ -672,6 +772,8 @@ def main():
         pf, _, _ = run_prefill(args, torch, dev, "prefill", args.prefill_steps, 2)
         result["prefill_t_s"] = pf["t_s_per_layer"]
         result["prefill"] = pf
+    elif name.startswith("verify"):
+        result = run_verify(args, torch, dev, name)
     elif name.startswith("prefill"):
         pf, ms_per_step, w = run_prefill(args, torch, dev, name, args.steps, args.warmup)
         result = {

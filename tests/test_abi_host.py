@@ -276,7 +276,7 @@ def test_union_decode_attention_validates_before_any_device_work():
         assert e.value.code == qsa.QSA_ENOTSUP
     need = qsa.workspace_size(d, qsa.OP_ATTN_DECODE_UNION, 5, 5)
     cap = 5 * ld
-    runs = -(-cap // 128)
+    runs = -(-cap // 64)
     rnd = lambda x: -(-x // 256) * 256
     assert need == rnd(cap * 4) + rnd(cap) + rnd(4) + rnd(2 * runs * 5 * 8 * 258 * 4)
     with pytest.raises(qsa.QsaError) as e:

@@ -529,7 +529,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 constexpr int kUnionNT = 1024;
 constexpr int kUnionMaxT = 8;
 constexpr int kUnionCap = kUnionMaxEntries;  // union entries per group: t_group * ld_cells at most
-constexpr int kURun = 4 * kPChunk;  // union rows per attention workgroup
+constexpr int kURun = 2 * kPChunk;  // union rows per attention workgroup
 
 // Exclusive prefix sum over the workgroup (kUnionNT threads) and the total.
 __device__ __forceinline__ uint32_t union_scan(uint32_t v, uint32_t *s_w, uint32_t &total) {
@@ -560,47 +560,76 @@ __device__ __forceinline__ uint32_t union_scan(uint32_t v, uint32_t *s_w, uint32
 __global__ __launch_bounds__(kUnionNT) void k_union_build(AttnArgs a, UnionArgs u) {
     __shared__ uint32_t s_buf[2][kUnionCap];
     __shared__ int s_off[kUnionMaxT + 1];  // start of token t's entries; s_off[T] = total
-    __shared__ int s_seq[kUnionMaxT];
+    __shared__ int s_seq[kUnionMaxT];      // token t's sequence (-1: none, or no valid cell)
+    __shared__ int s_n[kUnionMaxT];
+    __shared__ int s_np[kUnionMaxT];
     __shared__ uint32_t s_w[kUnionNT / kWave];
     __shared__ int s_bad;
+    QSA_STAMP(0);
     const int gi = blockIdx.x, tid = threadIdx.x;
     const int q0 = gi * u.t_group;
     const int T = min(u.t_group, a.n_q - q0);
     const int ld = a.ld_cells;
-    if (tid == 0) {
-        s_off[0] = 0;
-        s_bad = 0;
-    }
-    __syncthreads();
-    // 1. each token's valid entries, compacted in order
-    for (int t = 0; t < T; ++t) {  // workgroup-uniform
-        const int q = q0 + t;
-        const int s = a.q_seq[q];
+    // 1. the group's lists as one flat range of T*ld entries (token-major),
+    // staged in LDS with coalesced loads while threads 0 .. T-1 fetch their
+    // token's sequence and sizes; thread tid then takes the kUPer
+    // consecutive entries from tid*kUPer (an odd stride: no bank conflicts)
+    constexpr int kUPer = kUnionCap / kUnionNT + 1;
+    const int flat = T * ld;
+    for (int e = tid; e < flat; e += kUnionNT)
+        s_buf[1][e] = (uint32_t)a.sel_cells[(int64_t)q0 * ld + e];
+    if (tid < T) {
+        const int s = a.q_seq[q0 + tid];
         const bool qvalid = s >= 0 && s < a.g.n_seq;
-        const int n_raw = qvalid ? a.n_sel[q] : 0;
-        const int n = n_raw < 0 ? 0 : (n_raw > ld ? ld : n_raw);
+        const int n_raw = qvalid ? a.n_sel[q0 + tid] : 0;
         int64_t np = qvalid ? a.g.n_cells[s] : 0;
         np = np < a.g.cap_cells ? np : a.g.cap_cells;
-        const int32_t *cells = a.sel_cells + (int64_t)q * ld;
-        // thread tid takes entries [tid*per, tid*per + per): contiguous, in order
-        const int per = (n + kUnionNT - 1) / kUnionNT;
-        uint32_t cnt = 0;
-        for (int k = tid * per; k < min(n, tid * per + per); ++k) {
-            const int c = cells[k];
-            cnt += (c >= 0 && c < np) ? 1u : 0u;
-        }
-        uint32_t total;
-        uint32_t at = union_scan(cnt, s_w, total) + (uint32_t)s_off[t];
-        for (int k = tid * per; k < min(n, tid * per + per); ++k) {
-            const int c = cells[k];
-            if (c >= 0 && c < np) s_buf[0][at++] = ((uint32_t)c << 3) | (uint32_t)t;
-        }
-        if (tid == 0) {
-            s_off[t + 1] = s_off[t] + (int)total;
-            s_seq[t] = total > 0 ? s : -1;
-        }
-        __syncthreads();
+        s_seq[tid] = qvalid ? s : -1;
+        s_n[tid] = n_raw < 0 ? 0 : (n_raw > ld ? ld : n_raw);
+        s_np[tid] = (int)np;
     }
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    QSA_STAMP(1);  // lists staged
+    const int e_first = tid * kUPer;
+    int t_first = e_first / ld;  // token of the first entry; 17 < ld, so one step at most
+    const int j_first = e_first - t_first * ld;
+    uint32_t valid = 0, cnt = 0;  // bit k: entry tid*kUPer + k is a valid cell
+#pragma unroll
+    for (int k = 0; k < kUPer; ++k) {
+        const int e = e_first + k;
+        const bool wrap = j_first + k >= ld;
+        const int t = t_first + (wrap ? 1 : 0), j = j_first + k - (wrap ? ld : 0);
+        if (e < flat) {
+            const int cell = (int)s_buf[1][e];
+            if (j < s_n[t] && cell >= 0 && cell < s_np[t]) {
+                valid |= 1u << k;
+                ++cnt;
+            }
+        }
+    }
+    uint32_t total;
+    uint32_t at = union_scan(cnt, s_w, total);
+    // token t's entries start at the compacted index of flat position t*ld:
+    // the thread whose range holds that position records it
+    for (int t = 1; t < T; ++t) {
+        const int d = t * ld - tid * kUPer;
+        if (d >= 0 && d < kUPer) s_off[t] = (int)(at + __popc(valid & ((1u << d) - 1u)));
+    }
+    if (tid == 0) {
+        s_off[0] = 0;
+        s_off[T] = (int)total;
+    }
+    __syncthreads();
+    if (tid < T && s_off[tid + 1] == s_off[tid]) s_seq[tid] = -1;  // no valid cell
+#pragma unroll
+    for (int k = 0; k < kUPer; ++k) {
+        if (!((valid >> k) & 1u)) continue;
+        const int t = t_first + (j_first + k >= ld ? 1 : 0);
+        s_buf[0][at++] = (s_buf[1][e_first + k] << 3) | (uint32_t)t;
+    }
+    __syncthreads();
+    QSA_STAMP(2);  // compacted
     const int E = s_off[T];
     int32_t *urow = u.urow + (int64_t)gi * u.cap;
     uint8_t *umask = u.umask + (int64_t)gi * u.cap;
@@ -629,6 +658,7 @@ __global__ __launch_bounds__(kUnionNT) void k_union_build(AttnArgs a, UnionArgs 
         if (tid == 0) u.n_union[gi] = E;
         return;
     }
+    QSA_STAMP(3);  // checked
     // 3. merge path: runs [s_off[t], s_off[t+1]) merged two by two; a merged
     // pair keeps the place of the pair, so the run bounds just halve
     int src = 0;
@@ -658,24 +688,26 @@ __global__ __launch_bounds__(kUnionNT) void k_union_build(AttnArgs a, UnionArgs 
         __syncthreads();
         src ^= 1;
     }
+    QSA_STAMP(4);  // merged
     // 4. fold equal cells: a first occurrence gathers the bits of its run
     const uint32_t *M = s_buf[src];
     const int per = (E + kUnionNT - 1) / kUnionNT;
     const int e0 = min(E, tid * per), e1 = min(E, tid * per + per);
-    uint32_t cnt = 0;
-    for (int e = e0; e < e1; ++e) cnt += (e == 0 || (M[e] >> 3) != (M[e - 1] >> 3)) ? 1u : 0u;
-    uint32_t total;
-    uint32_t at = union_scan(cnt, s_w, total);
+    uint32_t n_first = 0;
+    for (int e = e0; e < e1; ++e) n_first += (e == 0 || (M[e] >> 3) != (M[e - 1] >> 3)) ? 1u : 0u;
+    uint32_t n_union;
+    uint32_t ui = union_scan(n_first, s_w, n_union);
     for (int e = e0; e < e1; ++e) {
         const uint32_t cell = M[e] >> 3;
         if (e > 0 && (M[e - 1] >> 3) == cell) continue;
         uint32_t bits = 0;
         for (int f = e; f < E && (M[f] >> 3) == cell; ++f) bits |= 1u << (M[f] & 7u);
-        urow[at] = (int32_t)((int64_t)s0 * a.g.cap_cells + cell);
-        umask[at] = (uint8_t)bits;
-        ++at;
+        urow[ui] = (int32_t)((int64_t)s0 * a.g.cap_cells + cell);
+        umask[ui] = (uint8_t)bits;
+        ++ui;
     }
-    if (tid == 0) u.n_union[gi] = (int32_t)total;
+    if (tid == 0) u.n_union[gi] = (int32_t)n_union;
+    QSA_STAMP(5);
 }
 
 // The union's rows as a cell source: handles are rows (-1 past the run); the
@@ -793,14 +825,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 }
 
-// grid (n_q * n_head), 256 threads: out[q][h] from the partial states of its
-// group's runs (every run below ceil(n_union / kURun) was written for every
-// token of the group: o = 0, m = -inf, l = 0 where the token saw no row).
+// grid (n_q * n_head * 4), 256 threads: workgroup (query q, head h, 64-dim
+// slice) merges the partial states of q's group's runs (every run below
+// ceil(n_union / kURun) was written for every token of the group: o = 0,
+// m = -inf, l = 0 where the token saw no row).  Wavefront w sums runs w,
+// w + 4, ... with lane = output dim; its first kUPre runs are loaded at once,
+// the rest 8 at a time; the wavefronts' sums are added in a fixed order.
+constexpr int kUPre = 17;
 __global__ __launch_bounds__(256) void k_union_combine(AttnArgs a, UnionArgs u) {
-    __shared__ float s_m[(kUnionCap + kURun - 1) / kURun];
+    __shared__ float s_w[(kUnionCap + kURun - 1) / kURun];  // m of run r, then its weight
     __shared__ float s_red[4];
-    const int q = blockIdx.x / a.n_head, h = blockIdx.x % a.n_head;
-    const int tid = threadIdx.x;
+    __shared__ float s_acc[4][kWave];
+    const int slice = blockIdx.x & 3, qh = blockIdx.x >> 2;
+    const int q = qh / a.n_head, h = qh % a.n_head;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int hpk = a.n_head / a.n_head_kv, g = h / hpk;
     const int gi = q / u.t_group, t = q % u.t_group;
     const int runs = (u.n_union[gi] + kURun - 1) / kURun;
@@ -808,38 +846,62 @@ __global__ __launch_bounds__(256) void k_union_combine(AttnArgs a, UnionArgs u) 
     const float *base = u.part + ((int64_t)gi * a.n_head_kv + g) * u.n_runs * rows * kUPartStride +
                         (int64_t)(t * hpk + h % hpk) * kUPartStride;
     const int64_t stride = (int64_t)rows * kUPartStride;
+    const int col = slice * kWave + lane;
+    if (runs == 0) {  // no row in the group: nothing was written to merge
+        if (wave == 0) a.out[((int64_t)q * a.n_head + h) * kHeadDim + col] = 0.f;
+        return;
+    }
+    const int last = runs - 1;
+    // (clamped, unconditional loads of written runs: a run past the end weighs 0)
+    float pre[kUPre];
+#pragma unroll
+    for (int k = 0; k < kUPre; ++k) pre[k] = base[min(wave + 4 * k, last) * stride + col];
     float mloc = -INFINITY;
     for (int r = tid; r < runs; r += 256) {
         const float m = base[r * stride + kHeadDim], l = base[r * stride + kHeadDim + 1];
         const float mm = l > 0.f ? m : -INFINITY;
-        s_m[r] = mm;
+        s_w[r] = mm;
         mloc = fmaxf(mloc, mm);
     }
     mloc = wave_max_f32(mloc);
-    if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+    if (lane == 0) s_red[wave] = mloc;
     __syncthreads();
     const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    // thread tid = output dim: sum over runs in order, 8 runs' loads at once
-    // (clamped to the last run; a run past the end, or one where the token
-    // saw no row, weighs 0)
-    float acc = 0.f, L = 0.f;
-    for (int r0 = 0; r0 < runs; r0 += 8) {
-        float v[8], lv[8], w[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int64_t rr = min(r0 + k, runs - 1);
-            v[k] = base[rr * stride + tid];
-            lv[k] = base[rr * stride + kHeadDim + 1];
-            const float m = r0 + k < runs ? s_m[r0 + k] : -INFINITY;
-            w[k] = m == -INFINITY ? 0.f : __expf(m - M);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            acc = fmaf(v[k], w[k], acc);
-            L = fmaf(lv[k], w[k], L);
-        }
+    float lw = 0.f;
+    for (int r = tid; r < runs; r += 256) {
+        const float m = s_w[r];
+        const float w = m == -INFINITY ? 0.f : __expf(m - M);
+        s_w[r] = w;
+        lw += w * base[r * stride + kHeadDim + 1];
     }
-    a.out[((int64_t)q * a.n_head + h) * kHeadDim + tid] = L > 0.f ? acc / L : 0.f;
+    lw = wave_sum_f32(lw);
+    __syncthreads();  // every M read before s_red is reused; every weight written
+    if (lane == 0) s_red[wave] = lw;
+    __syncthreads();
+    const float L = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kUPre; ++k) {
+        const int r = wave + 4 * k;
+        acc = fmaf(pre[k], r < runs ? s_w[r] : 0.f, acc);
+    }
+    for (int r0 = wave + 4 * kUPre; r0 < runs; r0 += 32) {
+        float v[8], w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = r0 + 4 * k;
+            v[k] = base[min(r, last) * stride + col];
+            w[k] = r < runs ? s_w[r] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = fmaf(v[k], w[k], acc);
+    }
+    s_acc[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        const float o = (s_acc[0][lane] + s_acc[1][lane]) + (s_acc[2][lane] + s_acc[3][lane]);
+        a.out[((int64_t)q * a.n_head + h) * kHeadDim + col] = L > 0.f ? o / L : 0.f;
+    }
 }
 
 // ---- the gather alone ----
@@ -962,6 +1024,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_rows(AttnArgs a) {
 
 size_t attn_prefill_ws_bytes(int, int, int) { return 0; }
 
+QSA_STAMP_READER(attnp)
+
 size_t union_ws_bytes(int n_q, int t_group, int n_head, int n_head_kv, int ld_cells) {
     return union_layout(nullptr, n_q, t_group, n_head, n_head_kv, ld_cells, nullptr);
 }
@@ -998,7 +1062,7 @@ hipError_t launch_attn_decode_union(const AttnArgs &a, int t_group, hipStream_t 
     const int n_slices = (t_group + kPWaves * tpw - 1) / (kPWaves * tpw);
     const int grid = u.n_groups * a.n_head_kv * u.n_runs * n_slices;
     hipLaunchKernelGGL(k_attn_union_q8, dim3(grid), dim3(256), 0, st, a, u);
-    hipLaunchKernelGGL(k_union_combine, dim3(a.n_q * a.n_head), dim3(256), 0, st, a, u);
+    hipLaunchKernelGGL(k_union_combine, dim3(a.n_q * a.n_head * 4), dim3(256), 0, st, a, u);
     return hipGetLastError();
 }
 

@@ -171,9 +171,13 @@ __device__ __forceinline__ uint64_t group_sort_by_block(uint64_t key, int n) {
     return (k << 32) | (k >> 32);
 }
 
-// 1-D grid: n_q * 4*n_wg scoring workgroups (one per query and 64-block
-// group), then ceil(n_dirty/4) update workgroups (one wavefront per dirty
-// entry).
+// Scoring workgroups: one per query and 64-block group, the groups padded
+// to a multiple of 8 (one round per XCD).
+__host__ __device__ inline int score_wgs(int n_grp, int n_q) { return (n_grp + 7) / 8 * 8 * n_q; }
+
+// 1-D grid: score_wgs(4*n_wg, n_q) scoring workgroups (one per query and
+// 64-block group, and the padding), then ceil(n_dirty/4) update workgroups
+// (one wavefront per dirty entry).
 //
 // Scoring: lane l of wavefront w owns block 64*g + l and the quads (4 dims)
 // q = w, w + 4, ..., w + 28 of it, so each load is 1 KiB contiguous and a
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
     const int64_t cap_blocks = a.g.cap_cells / a.r;
     const int n_grp = f.n_wg * 4;
-    const int n_score_wg = n_grp * a.n_q;
+    const int n_score_wg = score_wgs(n_grp, a.n_q);
 
     if ((int)blockIdx.x >= n_score_wg) {  // ---- update role ----
         const int e = ((int)blockIdx.x - n_score_wg) * 4 + wave;
@@ -213,9 +217,16 @@ __global__ __launch_bounds__(256) void k_score_cand(DecodeIdxArgs f) {
     // Loads are issued before anything waits: the query (no dependence),
     // the key tile (needs only the sequence), then the dirty list; the
     // causal count comes from scalar loads, which wait on their own counter.
-    // groups in reverse: the tail group, which usually holds the dirty block
-    // and recomputes it, is dispatched first instead of last
-    const int i = blockIdx.x / n_grp, gg = n_grp - 1 - (int)(blockIdx.x % n_grp);
+    // Ids are dealt to the 8 XCDs round robin (id mod 8): the k-th id of XCD x
+    // takes group position 8*(k / n_q) + x for query k % n_q, so the queries'
+    // workgroups of one key group run back to back on one XCD, and several
+    // tokens of one sequence read that tile from HBM once (their L2 serves the
+    // rest).  Positions count groups in reverse: the tail group, which usually
+    // holds the dirty block and recomputes it, is dispatched first.
+    const int xcd = (int)(blockIdx.x & 7), kth = (int)(blockIdx.x >> 3);
+    const int i = kth % a.n_q, gpos = 8 * (kth / a.n_q) + xcd;
+    if (gpos >= n_grp) return;  // padding of the last round of 8 groups
+    const int gg = n_grp - 1 - gpos;
     const int64_t b0 = (int64_t)gg * kTile;
     const int64_t b = b0 + lane;
     const float qxl = a.q_idx[(int64_t)i * kDIdx + lane];
@@ -502,7 +513,7 @@ size_t fused_select_ws_bytes(int n_q, int nb_max) { return cand_ws_bytes(n_q, nb
 
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st) {
     bind_candidates(f, ws);
-    const int grid = f.n_wg * 4 * f.s.n_q + (f.n_dirty + 3) / 4;
+    const int grid = score_wgs(f.n_wg * 4, f.s.n_q) + (f.n_dirty + 3) / 4;
     if (grid > 0) hipLaunchKernelGGL(k_score_cand, dim3(grid), dim3(256), 0, st, f);
     return hipGetLastError();
 }

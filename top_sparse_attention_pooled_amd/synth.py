@@ -125,6 +125,13 @@ WORKLOADS = {
                            note="1 seq, n_kv=248,278, q8_0 KV, 128 decode steps"),
     "decode5x250k": Workload("decode5x250k", 3, 5, 248278 - 1, n_new=1, steps=128,
                              note="5 independent seqs at n_kv=248,278, one token each"),
+    "verify5x250k": Workload("verify5x250k", 5, 1, 248278 - 5, n_new=5, steps=64,
+                             note="1 seq at n_kv=248,278, 5 query tokens per step (a "
+                                  "speculative verify step), i.i.d. indexer queries"),
+    "verify5x250k_ar1": Workload("verify5x250k_ar1", 5, 1, 248278 - 5, n_new=5, steps=64,
+                                 note="the verify step with AR(1) indexer queries (rho 0.9) "
+                                      "along its 5 tokens",
+                                 extra={"qidx_ar1": 0.9}),
     "prefill": Workload("prefill", 4, 1, 198628, n_new=512, steps=1,
                         note="512-token ubatch appended at depth 198,628"),
     "prefill_ar1": Workload("prefill_ar1", 4, 1, 198628, n_new=512, steps=1,
