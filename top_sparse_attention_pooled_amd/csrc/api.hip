@@ -395,20 +395,16 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const v
     if (need && (!ws_dev || ws_bytes < need || !aligned(ws_dev, 16)))
         return fail(QSA_EWS, "prefill indexer workspace needs %zu bytes, 16-byte aligned", need);
     const qsa::RopeTable rope = rope_table(dims->rope_theta);
-    hipError_t e = hipSuccess;
-    if (n_dirty > 0) {
-        qsa::UpdateArgs u{geom(seqs), kidx_ref(dims, kidx_dev), dirty_dev, n_dirty,
-                          pooled_dev, pooled_bf16_dev, dims->r,   dims->rms_eps,
-                          dims->idx_norm_w_dev, rope};
-        e = qsa::launch_update_pooled(u, (hipStream_t)stream);
-    }
-    if (e == hipSuccess && n_q > 0) {  // (nb_max 0: every query keeps its tail only)
-        qsa::ScoreArgs a{geom(seqs),      q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
-                         pooled_bf16_dev, nb_max,    nullptr,   0,         dims->r, rope};
-        e = qsa::launch_score_select_prefill(a, dims->idx_norm_w_dev, ws_dev, dims->top_k,
-                                             sel_blocks_dev, sel_cells_dev, n_sel_dev,
-                                             (hipStream_t)stream);
-    }
+    // the update shares the first launch of the indexer (alone when n_q is 0;
+    // nb_max 0: every query keeps its tail only)
+    const qsa::UpdateArgs u{geom(seqs), kidx_ref(dims, kidx_dev), dirty_dev,
+                            n_dirty > 0 ? n_dirty : 0, pooled_dev, pooled_bf16_dev, dims->r,
+                            dims->rms_eps, dims->idx_norm_w_dev, rope};
+    const qsa::ScoreArgs a{geom(seqs),      q_idx_dev, q_seq_dev, q_pos_dev, n_q, pooled_dev,
+                           pooled_bf16_dev, nb_max,    nullptr,   0,         dims->r, rope};
+    const hipError_t e = qsa::launch_score_select_prefill(
+        a, dims->idx_norm_w_dev, ws_dev, dims->top_k, sel_blocks_dev, sel_cells_dev, n_sel_dev, u,
+        (hipStream_t)stream);
     return launched(e, "score_select_prefill");
 }
 

@@ -55,12 +55,32 @@ __device__ __forceinline__ float bf16_value(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
 
-// One wavefront per query: the roped query rounded to bf16 (zeros if the
-// query is invalid) and Delta_i = 2^-15 * |q_i| * sqrt(d) * max(1, |gamma|)
-// * (1 + 2^-8), each factor rounded up.
+// One launch, two roles.  Workgroups 0 .. ceil(n_q/4)-1: one wavefront per
+// query, the roped query rounded to bf16 (zeros if the query is invalid) and
+// Delta_i = 2^-15 * |q_i| * sqrt(d) * max(1, |gamma|) * (1 + 2^-8), each
+// factor rounded up.  The rest: one wavefront per entry of the dirty list,
+// its pooled key recomputed (the pooled-key update of the ubatch, which the
+// scoring passes read; it shares the launch instead of taking one of its own).
 __global__ __launch_bounds__(256) void k_rope_queries_delta(ScoreArgs a, const float *gamma,
-                                                            PrefillWs w) {
+                                                            PrefillWs w, UpdateArgs upd) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int n_rope_wg = (a.n_q + 3) / 4;
+    if ((int)blockIdx.x >= n_rope_wg) {  // ---- update role ----
+        const int e = ((int)blockIdx.x - n_rope_wg) * 4 + (int)(threadIdx.x >> 6);
+        if (e >= upd.n_dirty) return;
+        const int s = upd.dirty[2 * e], b = upd.dirty[2 * e + 1];
+        if (s < 0 || s >= upd.g.n_seq || b < 0) return;
+        const int64_t cap_blocks = upd.g.cap_cells / upd.r;
+        if (b >= cap_blocks) return;
+        int64_t n = upd.g.n_cells[s];
+        if (n > upd.g.cap_cells) n = upd.g.cap_cells;
+        if ((int64_t)b * upd.r >= n) return;
+        float lo, hi;
+        pooled_key_lane(upd.kidx, upd.g, s, b, n, upd.r, upd.eps, upd.gamma, upd.rope, lane, lo,
+                        hi);
+        store_pooled_lane(upd.pooled, upd.pooled_bf16, cap_blocks, s, b, lane, lo, hi);
+        return;
+    }
     const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (i >= a.n_q) return;
     int s;
@@ -549,6 +569,44 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     QSA_STAMP(9);
 }
 
+// The kept entries of the band (ascending block order, exact keys) as the
+// outputs emit_from_bitmap writes: blocks ascending, their cells, then the
+// tail cells, -1 past them.  Thread tid takes a contiguous slice of the band.
+__device__ void emit_from_band(const uint64_t *band, int total, const Thresh &th, int B, int r,
+                               int64_t nc, int tail, int32_t *sel_blocks, int32_t *sel_cells,
+                               int ld_cells, int32_t *n_sel, TopkSmem<kSelPNT> &sm) {
+    const int per = (total + kSelPNT - 1) / kSelPNT;
+    const int x0 = threadIdx.x * per, x1 = min(total, x0 + per);
+    uint32_t local = 0;
+    for (int x = x0; x < x1; ++x) {
+        const uint64_t k = band[x];
+        local += th.keep((uint32_t)(k >> 32), (uint32_t)k) ? 1u : 0u;
+    }
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+    const uint32_t incl = wave_incl_scan_u32(local);
+    if (lane == kWave - 1) sm.red[wave] = incl;
+    __syncthreads();
+    uint32_t before, kept;
+    waves_prefix<kSelPNT / kWave>(sm.red, wave, before, kept);
+    uint32_t pos = before + incl - local;
+    const int n_keep = (int)(kept < (uint32_t)B ? kept : (uint32_t)B);
+    if (threadIdx.x == 0) *n_sel = n_keep * r + tail;
+    for (int x = x0; x < x1; ++x) {
+        const uint64_t k = band[x];
+        if (!th.keep((uint32_t)(k >> 32), (uint32_t)k)) continue;
+        if ((int)pos < B) {
+            const int32_t b = key_block(k);
+            sel_blocks[pos] = b;
+            for (int c = 0; c < r; ++c) sel_cells[pos * r + c] = b * r + c;
+        }
+        ++pos;
+    }
+    for (int j = n_keep + threadIdx.x; j < B; j += kSelPNT) sel_blocks[j] = -1;
+    const int n_full = n_keep * r;
+    for (int j = n_full + threadIdx.x; j < ld_cells; j += kSelPNT)
+        sel_cells[j] = (j < n_full + tail) ? (int32_t)(nc * r + (j - n_full)) : -1;
+}
+
 // grid (n_q), kSelPNT threads: the exact top-B of query i among its masked
 // blocks, rescored in order T.
 constexpr int kMaskPer = kPrefMaxBlocks / 64 / kSelPNT;  // group masks per thread
@@ -570,10 +628,13 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
     const uint16_t *keys = a.pooled_bf16 + (valid ? (int64_t)s * cap_blocks * kDIdx : 0);
     if (tid < kDIdx) sm.q[tid] = bf16_value(w.qr[(int64_t)i * kDIdx + tid]);
     const int n_words = (int)((limit + 31) / 32);
-    for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
     bool exact_all = limit > 0 && !delta_in_range(w.delta[i]);
+    const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
+    const int ld_cells = top_k + a.r - 1;
+    int32_t *out_blocks = sel_blocks + (int64_t)i * B;
+    int32_t *out_cells = sel_cells + (int64_t)i * ld_cells;
 
-    if (limit > 0 && !exact_all) {
+    if (!exact_all) {  // (limit 0: an empty band, the tail alone)
         // the masked blocks, listed by a prefix count over the masks
         const int n_g = (int)((limit + 63) / 64);
         uint64_t mk[kMaskPer];
@@ -604,9 +665,15 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
             }
             __syncthreads();
             QSA_STAMP(11);
-            for (int x = tid; x < (int)total; x += kSelPNT) {
-                const int64_t b = (int64_t)sm.band[x];
-                sm.band[x] = block_key(exact_score(keys + b * kDIdx, sm.q), b);
+            // two rows in flight per thread: their loads are issued together
+            for (int x = tid; x < (int)total; x += 2 * kSelPNT) {
+                const int y = x + kSelPNT;
+                const int64_t b0 = (int64_t)sm.band[x];
+                const int64_t b1 = y < (int)total ? (int64_t)sm.band[y] : b0;
+                const float s0 = exact_score(keys + b0 * kDIdx, sm.q);
+                const float s1 = exact_score(keys + b1 * kDIdx, sm.q);
+                sm.band[x] = block_key(s0, b0);
+                if (y < (int)total) sm.band[y] = block_key(s1, b1);
             }
             __syncthreads();
             QSA_STAMP(12);
@@ -618,12 +685,13 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
             }
             const Thresh th = topk_threshold<kSelPNT>(bk, (uint32_t)B, sm.tk);
             QSA_STAMP(13);
-            bk([&](uint32_t k, uint32_t u) {
-                if (th.keep(k, u)) mark(sm.bitmap, ~u);
-            });
+            emit_from_band(sm.band, (int)total, th, B, a.r, nc, tail, out_blocks, out_cells,
+                           ld_cells, n_sel + i, sm.tk);
         }
     }
     if (exact_all) {
+        for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
+        __syncthreads();
         ExactStream src;
         src.limit = limit;
         src.keys = keys;
@@ -632,13 +700,10 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
         src([&](uint32_t k, uint32_t u) {
             if (th.keep(k, u)) mark(sm.bitmap, ~u);
         });
+        __syncthreads();
+        emit_from_bitmap<kSelPNT>(sm.bitmap, n_words, B, a.r, nc, tail, out_blocks, out_cells,
+                                  ld_cells, n_sel + i, sm.tk);
     }
-    __syncthreads();
-    const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
-    const int ld_cells = top_k + a.r - 1;
-    emit_from_bitmap<kSelPNT>(sm.bitmap, n_words, B, a.r, nc, tail,
-                              sel_blocks + (int64_t)i * B, sel_cells + (int64_t)i * ld_cells,
-                              ld_cells, n_sel + i, sm.tk);
     QSA_STAMP(14);
 }
 
@@ -672,12 +737,13 @@ size_t prefill_ws_bytes(int n_q, int nb_max) {
 
 hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, void *ws,
                                        int top_k, int32_t *sel_blocks, int32_t *sel_cells,
-                                       int32_t *n_sel, hipStream_t st) {
-    if (a.n_q <= 0) return hipSuccess;
+                                       int32_t *n_sel, const UpdateArgs &upd, hipStream_t st) {
+    if (a.n_q <= 0) return launch_update_pooled(upd, st);
     PrefillWs w;
     prefill_layout(static_cast<char *>(ws), a.n_q, a.nb_max, &w);
-    hipLaunchKernelGGL(k_rope_queries_delta, dim3((a.n_q + 3) / 4), dim3(256), 0, st, a, gamma,
-                       w);
+    const int n_upd_wg = upd.n_dirty > 0 ? (upd.n_dirty + 3) / 4 : 0;
+    hipLaunchKernelGGL(k_rope_queries_delta, dim3((a.n_q + 3) / 4 + n_upd_wg), dim3(256), 0, st,
+                       a, gamma, w, upd);
     // per panel of 512 queries, workgroups for both halves of its sets of
     // groups, XCD-paired (one per CU, at most the chip's 256 CUs in all)
     const int n_panel = (a.n_q + kPanelQ - 1) / kPanelQ;

@@ -391,7 +391,7 @@ struct PrefillWs {
 size_t prefill_ws_bytes(int n_q, int nb_max);
 hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, void *ws,
                                        int top_k, int32_t *sel_blocks, int32_t *sel_cells,
-                                       int32_t *n_sel, hipStream_t st);
+                                       int32_t *n_sel, const UpdateArgs &upd, hipStream_t st);
 size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
 size_t attn_prefill_ws_bytes(int n_q, int n_head, int ld_cells);
