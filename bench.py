@@ -680,40 +680,58 @@ def cpu_baseline_prefill(w, host, budget):
 
 def run_probe(args, torch, dev):
     """Floors for the kernels' access patterns: qsa_probe_stream_read over 4
-    GiB (HBM, streaming loads), over 64 MiB re-read (resident in the 256 MB
-    last-level cache) and over 16 MiB re-read (each XCD re-reads the same 2
-    MiB, resident in its L2); then qsa_probe_gather_prefill -- the prefill
+    GiB (sustained HBM reads, streaming loads) and over 32 MiB from HBM once
+    per launch (a single pass like the 250k-cell scoring stream); then
+    qsa_probe_gather_prefill -- the prefill
     attention's K/V row gather without its arithmetic -- and
     qsa_sparse_attn_prefill itself on the 512-token ubatch's selections.
-    Each figure: events around n back-to-back launches on one stream."""
+    Each figure: events around a graph replay of n launches on one stream."""
     from top_sparse_attention_pooled_amd import qsa, runtime
     stream = torch.cuda.Stream()
-    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    n_sink = 8192  # a word per wavefront: no two wavefronts fold into one word
+    sink = torch.zeros(n_sink, dtype=torch.int32, device=dev)
 
     def timed(fn, n):
+        """us per launch: n launches captured in one HIP graph (no host gaps
+        between them), replayed once to warm up, then between two events."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                fn()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
-            fn()
-            fn()
+            g.replay()
             torch.cuda.synchronize()
             ev0.record(stream)
-            for _ in range(n):
-                fn()
+            g.replay()
             ev1.record(stream)
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) * 1000.0 / n  # us per launch
+        return ev0.elapsed_time(ev1) * 1000.0 / n
 
     out = {"probe": "memory-traffic floors", "unit": "GB/s and us per launch"}
-    for name, mib, nt, n in (("hbm_stream_read", 4096, True, 20),
-                             ("llc_reread", 64, False, 200), ("l2_reread", 16, False, 400)):
-        buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
-        nb = buf.numel()
-        us = timed(lambda: qsa.probe_stream_read(buf, nb, sink, 64, nontemporal=nt,
-                                                 stream=stream), n)
-        out[name] = {"bytes": nb, "us": round(us, 2), "GBps": round(nb / us / 1e3, 1)}
-        del buf
-        torch.cuda.empty_cache()
+    # sustained: one 4 GiB pass per launch
+    buf = torch.empty(4096 << 20, dtype=torch.uint8, device=dev)
+    nb = buf.numel()
+    us = timed(lambda: qsa.probe_stream_read(buf, nb, sink, n_sink, stream=stream), 20)
+    out["hbm_stream_read"] = {"bytes": nb, "us": round(us, 2), "GBps": round(nb / us / 1e3, 1)}
+    del buf
+    # one cold 32 MiB pass per launch (the size of the 250k-cell scoring
+    # stream): 16 buffers in turn, 512 MiB in all, more than the 256 MB
+    # last-level cache holds
+    bufs32 = [torch.empty(32 << 20, dtype=torch.uint8, device=dev) for _ in range(16)]
+    turn = [0]
+
+    def one_pass():
+        b = bufs32[turn[0] % 16]
+        turn[0] += 1
+        qsa.probe_stream_read(b, b.numel(), sink, n_sink, stream=stream)
+
+    us = timed(one_pass, 64)
+    out["hbm_32mib_cold_pass"] = {"bytes": 32 << 20, "us": round(us, 2),
+                                  "GBps": round((32 << 20) / us / 1e3, 1)}
+    del bufs32
+    torch.cuda.empty_cache()
     # the prefill ubatch's selections, then the gather alone and the kernel
     w, layers, inp, host = setup(torch, dev, "prefill", 1, 0, 1)
     layer = layers[0]
@@ -731,7 +749,7 @@ def run_probe(args, torch, dev):
     rows = int(np.sum(-(-n_sel // 32) * 32)) * w.Hk * 2
     gbytes = rows * 272
     g_us = timed(lambda: qsa.probe_gather_prefill(d, sq, inp["q_seq"][0], n_q, layer.k, layer.v,
-                                                  bf.sel_cells, bf.n_sel, sink, 64,
+                                                  bf.sel_cells, bf.n_sel, sink, n_sink,
                                                   stream=stream), 20)
     a_us = timed(lambda: qsa.sparse_attn_prefill(d, sq, inp["q"][0], inp["q_seq"][0], n_q,
                                                  layer.k, layer.v, bf.sel_cells, bf.n_sel,

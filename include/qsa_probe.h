@@ -6,9 +6,12 @@
  * Conventions are those of qsa.h (device pointers owned by the caller,
  * validation before any enqueue, QSA_* return codes, no allocation, no
  * synchronisation).  Each probe XOR-folds every 32-bit word it loads into
- * sink_dev[workgroup % n_sink] with atomic XORs, so the XOR of the n_sink
- * words after the call is the XOR of all words loaded (XOR'ed into what the
- * sink held).  Calls that share a sink must not overlap.
+ * sink_dev[wavefront % n_sink] (each wavefront into its own word when n_sink
+ * is at least the number of wavefronts -- at most 8192 for the stream read,
+ * ceil(n_q/8)*8*n_head_kv*4 for the gather -- atomically otherwise), so the
+ * XOR of the n_sink words after the call is the XOR of all words loaded
+ * (XOR'ed into what the sink held).  Calls that share a sink must not
+ * overlap.
  */
 #ifndef QSA_PROBE_H
 #define QSA_PROBE_H

@@ -27,21 +27,23 @@ def xor_words(a: np.ndarray) -> int:
                                      initial=np.uint32(0)))
 
 
+@pytest.mark.parametrize("n_sink", [7, 8192])  # shared words (atomic) / a word per wavefront
 @pytest.mark.parametrize("n_bytes,nontemporal", [(16, True), (4096 + 48, False),
                                                  (64 * 2**20 + 16 * 7, True)])
-def test_stream_read_loads_every_word_once(n_bytes, nontemporal):
-    say(f"probe stream read: {n_bytes} bytes, nontemporal {nontemporal}")
+def test_stream_read_loads_every_word_once(n_bytes, nontemporal, n_sink):
+    say(f"probe stream read: {n_bytes} bytes, nontemporal {nontemporal}, {n_sink} sink words")
     rng = np.random.default_rng(n_bytes)
     host = rng.integers(0, 2**32, n_bytes // 4, dtype=np.uint32)
     src = torch.from_numpy(host.view(np.uint8)).to(DEV)
-    sink = torch.zeros(7, dtype=torch.int32, device=DEV)
-    qsa.probe_stream_read(src, n_bytes, sink, 7, nontemporal=nontemporal)
+    sink = torch.zeros(n_sink, dtype=torch.int32, device=DEV)
+    qsa.probe_stream_read(src, n_bytes, sink, n_sink, nontemporal=nontemporal)
     torch.cuda.synchronize()
     got = xor_words(sink.cpu().numpy())
     assert got == xor_words(host)
 
 
-def test_gather_prefill_loads_the_attention_rows():
+@pytest.mark.parametrize("n_sink", [3, 8192])
+def test_gather_prefill_loads_the_attention_rows(n_sink):
     say("probe gather: 2 sequences, 9 queries, ragged lists")
     d = qsa.Dims()  # 2 KV heads, q8_0, lists of top_k + r - 1 = 2051 cells
     n_seq, cap = 2, 4096
@@ -58,9 +60,9 @@ def test_gather_prefill_loads_the_attention_rows():
         cells[i, :n] = np.sort(rng.choice(cap, size=n, replace=False))  # some past n_present
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     seqs = qsa.Seqs(n_seq, cap, t(n_present))
-    sink = torch.zeros(3, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(n_sink, dtype=torch.int32, device=DEV)
     qsa.probe_gather_prefill(d, seqs, t(q_seq), q_seq.size, t(k_host), t(v_host), t(cells),
-                             t(n_sel), sink, 3)
+                             t(n_sel), sink, n_sink)
     torch.cuda.synchronize()
     k_rows = k_host.reshape(-1, Q8_ROW)
     v_rows = v_host.reshape(-1, Q8_ROW)

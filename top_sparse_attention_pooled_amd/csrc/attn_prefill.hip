@@ -942,7 +942,7 @@ __global__ __launch_bounds__(256) void k_probe_gather_q8(AttnArgs a, uint32_t *s
     acc ^= xor_lane<8>(acc);
     acc ^= xor_lane<16>(acc);
     acc ^= xor_lane<32>(acc);
-    if (lane == 0) atomicXor(&sink[blockIdx.x % n_sink], acc);
+    if (lane == 0) fold_sink(sink, n_sink, acc);
 }
 
 // ---- rows gathered per lane: f32 and f16 caches, and q8_0 through a cell table ----

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kProbeNT) void k_probe_read(const u32x4 *src, uint6
     v ^= xor_lane<8>(v);
     v ^= xor_lane<16>(v);
     v ^= xor_lane<32>(v);
-    if ((threadIdx.x & (kWave - 1)) == 0) atomicXor(&sink[blockIdx.x % n_sink], v);
+    if ((threadIdx.x & (kWave - 1)) == 0) fold_sink(sink, n_sink, v);
 }
 
 }  // namespace

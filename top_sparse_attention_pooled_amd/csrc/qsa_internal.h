@@ -418,8 +418,20 @@ hipError_t launch_attn_decode_union(const AttnArgs &a, int t_group, hipStream_t 
 constexpr int kUnionMaxTokens = 8;
 constexpr int kUnionMaxEntries = 16448;  // 8 tokens of top_k + r - 1 = 2056 cells
 
-// Memory-traffic probes (probe.hip, attn_prefill.hip): loads only, folded
-// into sink[workgroup % n_sink] by XOR.
+// Memory-traffic probes (probe.hip, attn_prefill.hip): loads only, each
+// wavefront's XOR folded into sink[wavefront % n_sink] -- a plain
+// read-modify-write when the sink has a word per wavefront (the sole writer),
+// else an atomic (many wavefronts on a few words serialise at L2, which a
+// probe must not time).  Called by one lane per wavefront.
+__device__ __forceinline__ void fold_sink(uint32_t *sink, int n_sink, uint32_t v) {
+    const uint32_t wpg = blockDim.x / kWave;
+    const uint32_t n_waves = gridDim.x * gridDim.y * gridDim.z * wpg;
+    const uint32_t id = blockIdx.x * wpg + threadIdx.x / kWave;  // (1-D grids)
+    if ((uint32_t)n_sink >= n_waves)
+        sink[id] ^= v;
+    else
+        atomicXor(&sink[id % (uint32_t)n_sink], v);
+}
 hipError_t launch_probe_read(const void *src, size_t n_bytes, bool nontemporal, uint32_t *sink,
                              int n_sink, hipStream_t st);
 hipError_t launch_probe_gather_prefill(const AttnArgs &a, uint32_t *sink, int n_sink,
