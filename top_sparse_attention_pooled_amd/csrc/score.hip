@@ -372,12 +372,52 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
     const int B = f.top_k / a.r;
     CandKeys<kSelNT, MAXB> ck;
     Thresh th;
-    select_candidates<kSelNT, MAXB>(f, i, limit, B, sm, ck, th);
+    const bool fast = select_candidates<kSelNT, MAXB, true>(f, i, limit, B, sm, ck, th);
     const int n_words = (int)((limit + 31) / 32);
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = f.top_k + a.r - 1;
-    emit_from_bitmap<kSelNT>(sm.bitmap, n_words, B, a.r, nc, tail, f.sel_blocks + (int64_t)i * B,
-                             f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i, sm.tk);
+    int32_t *sel_blocks = f.sel_blocks + (int64_t)i * B;
+    int32_t *sel_cells = f.sel_cells + (int64_t)i * ld_cells;
+    if (!fast) {  // a group was re-admitted or the row streamed: the bitmap holds the set
+        emit_from_bitmap<kSelNT>(sm.bitmap, n_words, B, a.r, nc, tail, sel_blocks, sel_cells,
+                                 ld_cells, f.n_sel + i, sm.tk);
+        return;
+    }
+    // The kept set is the base candidates th keeps, and they ascend by block
+    // in the order (wavefront, slot, lane): a kept one's rank is the kept
+    // count of the earlier wavefronts, then of its wavefront's earlier slots,
+    // then of its slot's lower lanes (ballots) -- no bitmap to mark or scan.
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    uint32_t in_wave = 0;
+#pragma unroll
+    for (int x = 0; x < decltype(ck)::kBase; ++x)
+        if (x < ck.nb)
+            in_wave += __popcll(__ballot(th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x])));
+    if (lane == 0) sm.tk.red[wave] = in_wave;
+    __syncthreads();
+    uint32_t before, total;
+    waves_prefix<kSelNT / kWave>(sm.tk.red, wave, before, total);
+    const int n_keep = (int)(total < (uint32_t)B ? total : (uint32_t)B);
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t k0 = before;  // rank of this wavefront's next kept slot
+#pragma unroll
+    for (int x = 0; x < decltype(ck)::kBase; ++x) {
+        if (x >= ck.nb) continue;
+        const bool kp = th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]);
+        const uint64_t bal = __ballot(kp);
+        const int k = (int)(k0 + __popcll(bal & below));
+        if (kp && k < n_keep) {
+            const int32_t b = key_block(ck.k[x]);
+            sel_blocks[k] = b;
+            for (int c = 0; c < a.r; ++c) sel_cells[k * a.r + c] = b * a.r + c;
+        }
+        k0 += __popcll(bal);
+    }
+    if (threadIdx.x == 0) f.n_sel[i] = n_keep * a.r + tail;
+    for (int j = n_keep + (int)threadIdx.x; j < B; j += kSelNT) sel_blocks[j] = -1;
+    const int n_full = n_keep * a.r;
+    for (int j = n_full + (int)threadIdx.x; j < ld_cells; j += kSelNT)
+        sel_cells[j] = (j < n_full + tail) ? (int32_t)(nc * a.r + (j - n_full)) : -1;
 }
 
 // ---------------------------------------------------------------------------
