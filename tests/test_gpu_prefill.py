@@ -236,6 +236,30 @@ def test_prefill_ubatch_at_depth(name):
     assert worst <= 2e-3
 
 
+@pytest.mark.parametrize("depth", [100000, 520000])
+def test_prefill_selection_long_contexts(depth):
+    """Contexts of 25,000 and 130,000 blocks (the longest the indexer takes is
+    131,072): the threshold step holds 32 and 128 subgroup maxima per lane
+    (the 512-token ubatch at depth 198,628 takes 64, the small cases 16).
+    Queries at the end of the context and at early positions of it."""
+    w = synth.Workload("pfl", 96, 1, depth, n_new=6, steps=1, top_k=2048)
+    say(f"prefill select: depth {depth}, 6 new tokens and 6 earlier positions")
+    layer = runtime.Layer(w, DEV, k=np.zeros((1, 1, 1, 1), np.uint8),
+                          v=np.zeros((1, 1, 1, 1), np.uint8))
+    kidx = layer.kidx.cpu().numpy()
+    n = synth.n_cells_at(w, 0)
+    layer.rebuild(n)
+    q_idx, _, q_seq, q_pos = synth.make_queries(w, 0)
+    early = np.array([9000, 65535, 65536, depth // 2, depth - 3000, depth - 1], np.int32)
+    q_pos = np.concatenate([q_pos, early])
+    q_seq = np.zeros(q_pos.size, np.int32)
+    q_idx = np.concatenate([q_idx, synth.normal((early.size, w.d), 96, 0, synth.T_QIDX, 1)])
+    nb_max = w.nb_max(0)
+    bufs = run_prefill(w, layer, q_idx, q_seq, q_pos, nb_max)
+    ref_pooled = oracle_pooled(w, kidx, n)
+    check_against_oracle(w, bufs, ref_pooled, q_idx, q_seq, q_pos, nb_max, range(q_pos.size))
+
+
 def test_prefill_selection_extreme_query_norms():
     """Queries scaled far up and far down: their error bound Delta leaves the
     range where no partial sum can overflow or underflow, so every causal

@@ -41,8 +41,8 @@ namespace qsa {
 namespace {
 
 constexpr int kSelPNT = 256;      // selection workgroup (two share a CU)
-constexpr int kBandCap = 4096;    // masked blocks rescored from the LDS list (8 x B)
 constexpr int kTauNT = 256;       // threshold workgroup
+constexpr int kBandCap = 4096;    // masked blocks rescored from the LDS list (8 x B)
 constexpr int kPrefMaxBlocks = kFusedMaxBlocks;
 constexpr float kDeltaMin = 0x1p-100f, kDeltaMax = 0x1p100f;
 
@@ -506,10 +506,14 @@ __device__ __forceinline__ bool delta_in_range(float delta) {
 }
 
 // grid (n_q), kTauNT threads: w.thr[i] = tau_i - 2 Delta_i rounded down,
-// tau_i the B-th largest subgroup maximum of query i; -inf when fewer than B
+// tau_i the lower edge of the bin holding the B-th largest subgroup maximum
+// of query i after two radix rounds (2^11 bins over [lo, hi] at the smallest
+// power-of-two width, then within the chosen bin); -inf when fewer than B
 // subgroups hold a causal block or Delta_i is out of range (every causal
-// block then passes the filter).
-constexpr int kTauPer = kPrefMaxBlocks / 16 / kTauNT;  // subgroup maxima per thread
+// block then passes the filter).  PER (a power of two) maxima per thread
+// cover up to kTauNT * PER subgroups.
+constexpr int kTauMaxPer = kPrefMaxBlocks / 16 / kTauNT;
+template <int PER>
 __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w, int top_k) {
     QSA_STAMP(8);
     __shared__ TopkSmem<kTauNT> sm;
@@ -524,13 +528,19 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     const int B = top_k / a.r;
     const float delta = w.delta[i];
     const float *row = w.smax + (int64_t)i * 4 * w.n_grp;
-    RegKeys32<kTauPer, kTauNT> keys;
+    // every load issued before the first is used: indexes clamped to the
+    // row (n_sub <= 4 n_grp), entries past n_sub dropped afterwards
+    const int last = 4 * w.n_grp - 1;
+    float v[PER];
+#pragma unroll
+    for (int c = 0; c < PER; ++c) v[c] = last >= 0 ? row[min(c * kTauNT + tid, last)] : 0.0f;
+    RegKeys32<PER, kTauNT> keys;
     keys.tid = tid;
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
 #pragma unroll
-    for (int c = 0; c < kTauPer; ++c) {
+    for (int c = 0; c < PER; ++c) {
         const int x = c * kTauNT + tid;
-        const uint32_t k = x < n_sub ? approx_key(row[x]) : 0u;
+        const uint32_t k = x < n_sub ? approx_key(v[c]) : 0u;
         keys.k[c] = k;
         if (k) {
             ++cnt;
@@ -752,7 +762,18 @@ hipError_t launch_score_select_prefill(const ScoreArgs &a, const float *gamma, v
     if (w.n_grp > 0)
         hipLaunchKernelGGL(k_prefill_scores<kSubMax>, dim3(grid), dim3(kPanelNT), 0, st, a, w,
                            wg_per_panel);
-    hipLaunchKernelGGL(k_prefill_tau, dim3(a.n_q), dim3(kTauNT), 0, st, a, w, top_k);
+    {
+        const int64_t n_sub = (a.nb_max + 15) / 16;  // subgroups of the longest query, at most
+        if (n_sub <= 4 * kTauNT)
+            hipLaunchKernelGGL(k_prefill_tau<4>, dim3(a.n_q), dim3(kTauNT), 0, st, a, w, top_k);
+        else if (n_sub <= 8 * kTauNT)
+            hipLaunchKernelGGL(k_prefill_tau<8>, dim3(a.n_q), dim3(kTauNT), 0, st, a, w, top_k);
+        else if (n_sub <= 16 * kTauNT)
+            hipLaunchKernelGGL(k_prefill_tau<16>, dim3(a.n_q), dim3(kTauNT), 0, st, a, w, top_k);
+        else
+            hipLaunchKernelGGL(k_prefill_tau<kTauMaxPer>, dim3(a.n_q), dim3(kTauNT), 0, st, a, w,
+                               top_k);
+    }
     if (w.n_grp > 0)
         hipLaunchKernelGGL(k_prefill_scores<kMask>, dim3(grid), dim3(kPanelNT), 0, st, a, w,
                            wg_per_panel);
