@@ -25,11 +25,13 @@
 //      (-inf, every causal block, when there are fewer than B subgroups);
 //   4. k_prefill_scores<kMask>: per (query, 64-block group), a bit mask of
 //      the blocks whose MFMA score reaches the threshold;
-//   5. k_select_prefill: the masked blocks rescored in order T; their exact
-//      top-B is the exact top-B of all blocks, which lies among them.  If
-//      more blocks pass than the LDS list holds, or Delta is outside the
-//      range where no partial sum can overflow or underflow, every causal
-//      block is rescored instead.
+//   5. k_select_prefill: the exact top-B of all blocks lies among the masked
+//      ones.  Ranked by MFMA score, those more than 2 Delta above the B-th
+//      largest are in it and those more than 2 Delta below are not; the few
+//      between are rescored in order T and decide the rest.  If more blocks
+//      pass than the LDS list holds, or Delta is outside the range where no
+//      partial sum can overflow or underflow, every causal block is
+//      rescored instead.
 #include <type_traits>
 
 #include "mfma_tile.h"
@@ -462,12 +464,33 @@ __device__ __forceinline__ float exact_score(const uint16_t *krow, const float *
     return v[0];
 }
 
+constexpr int kUCap = kWave;  // rescored band blocks one wavefront ranks
+// Band histogram: 2^10 bins, lane l of one wavefront holding bins [16 l, 16
+// l + 16); bin b at word b + b / 16, so that the lanes' reads hit different
+// banks.
+constexpr int kSelBinBits = 10;
+constexpr int kSelBins = 1 << kSelBinBits;
+constexpr int kSelBinsPerLane = kSelBins / kWave;
+constexpr int kHistWords = kSelBins + kSelBins / kSelBinsPerLane;
+__device__ __forceinline__ int hist_word(uint32_t b) { return (int)(b + (b >> 4)); }
+__device__ __forceinline__ int sel_shift(uint32_t lo, uint32_t hi) {
+    const uint32_t span = hi - lo;
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    return bits > kSelBinBits ? bits - kSelBinBits : 0;
+}
+
 struct PrefSelSmem {
     TopkSmem<kSelPNT> tk;
     float q[kDIdx];
+    // every-block path: the kept blocks' bitmap; band path: the histogram
     uint32_t bitmap[kPrefMaxBlocks / 32];
-    uint64_t band[kBandCap];  // masked blocks, then their exact keys
+    uint64_t band[kBandCap];  // masked blocks, then their keys
+    uint16_t xlist[kBandCap];  // band entries to rescore
+    uint32_t n_unscored, kmin, kmax, n_in, n_u;
+    float in_edge, out_edge;  // the bin of the B-th largest band score
 };
+static_assert(kHistWords <= kPrefMaxBlocks / 32, "histogram shares the bitmap");
+static_assert(kSelBinsPerLane == 16, "bin padding assumes 16 bins per lane");
 
 __device__ __forceinline__ uint32_t approx_key(float v) {
     return finite_f32(v) ? score_key(v) : 0u;
@@ -582,7 +605,7 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
 // The kept entries of the band (ascending block order, exact keys) as the
 // outputs emit_from_bitmap writes: blocks ascending, their cells, then the
 // tail cells, -1 past them.  Thread tid takes a contiguous slice of the band.
-__device__ void emit_from_band(const uint64_t *band, int total, const Thresh &th, int B, int r,
+__device__ void emit_from_band(const uint64_t *band, int total, Thresh th, int B, int r,
                                int64_t nc, int tail, int32_t *sel_blocks, int32_t *sel_cells,
                                int ld_cells, int32_t *n_sel, TopkSmem<kSelPNT> &sm) {
     const int per = (total + kSelPNT - 1) / kSelPNT;
@@ -618,8 +641,17 @@ __device__ void emit_from_band(const uint64_t *band, int total, const Thresh &th
 }
 
 // grid (n_q), kSelPNT threads: the exact top-B of query i among its masked
-// blocks, rescored in order T.
-constexpr int kMaskPer = kPrefMaxBlocks / 64 / kSelPNT;  // group masks per thread
+// blocks.  A masked block alone in its 16-block subgroup is the subgroup's
+// maximum, so its MFMA score m_j is the stored maximum; a block sharing its
+// subgroup with another masked one is rescored in order T (m_j = s_j).
+// Either way |m_j - s_j| <= Delta.  With M the B-th largest m over the
+// band: a block with m_j > M + 2 Delta is in the top-B (only blocks with m
+// > M, fewer than B, can reach its score; blocks outside the band score
+// below thr + Delta <= M + Delta), one with m_j < M - 2 Delta is not (B
+// blocks score above it).  One histogram round brackets M; the blocks
+// within 2 Delta of the bracket are rescored in order T, and the best of
+// them by (s, lower block) fill the top-B up.
+constexpr int kMaskPer = kPrefMaxBlocks / 64 / kSelPNT;  // group masks per thread, at most
 __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, PrefillWs w, int top_k,
                                                             int32_t *sel_blocks,
                                                             int32_t *sel_cells, int32_t *n_sel) {
@@ -627,6 +659,25 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
     QSA_STAMP(10);
     const int i = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = wave_id();
+    // thread tid takes groups [tid * per, tid * per + per), per from nb_max
+    // (not from the query's own limit), so that the mask words and subgroup
+    // maxima are requested before anything else returns; indexes clamped
+    const int per = ((a.nb_max + 63) / 64 + kSelPNT - 1) / kSelPNT;
+    const int g0 = tid * per, last = w.n_grp - 1;
+    uint64_t mk[kMaskPer];
+    f32x4_t mx[kMaskPer];
+#pragma unroll
+    for (int c = 0; c < kMaskPer; ++c) {
+        if (c < per) {
+            const int64_t g = (int64_t)i * w.n_grp + min(g0 + c, last);
+            mk[c] = w.mask[g];
+            mx[c] = *reinterpret_cast<const f32x4_t *>(w.smax + g * 4);
+        } else {
+            mk[c] = 0ull;
+            mx[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const uint16_t qv = w.qr[(int64_t)i * kDIdx + (tid & (kDIdx - 1))];
     int s;
     int64_t p;
     bool valid;
@@ -636,70 +687,190 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
     const int B = top_k / a.r;
     const int64_t cap_blocks = a.g.cap_cells / a.r;
     const uint16_t *keys = a.pooled_bf16 + (valid ? (int64_t)s * cap_blocks * kDIdx : 0);
-    if (tid < kDIdx) sm.q[tid] = bf16_value(w.qr[(int64_t)i * kDIdx + tid]);
     const int n_words = (int)((limit + 31) / 32);
-    bool exact_all = limit > 0 && !delta_in_range(w.delta[i]);
+    const float delta = w.delta[i];
+    bool exact_all = limit > 0 && !delta_in_range(delta);
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = top_k + a.r - 1;
     int32_t *out_blocks = sel_blocks + (int64_t)i * B;
     int32_t *out_cells = sel_cells + (int64_t)i * ld_cells;
 
     if (!exact_all) {  // (limit 0: an empty band, the tail alone)
-        // the masked blocks, listed by a prefix count over the masks
         const int n_g = (int)((limit + 63) / 64);
-        uint64_t mk[kMaskPer];
+        for (int j = tid; j < kHistWords; j += kSelPNT) sm.bitmap[j] = 0u;
+        if (tid == 0) {
+            sm.n_unscored = 0u;
+            sm.kmin = ~0u;
+            sm.kmax = 0u;
+            sm.n_in = 0u;
+            sm.n_u = 0u;
+            sm.in_edge = INFINITY;    // no block certainly in
+            sm.out_edge = -INFINITY;  // none certainly out
+        }
         uint32_t cnt = 0;
 #pragma unroll
         for (int c = 0; c < kMaskPer; ++c) {
-            const int g = tid * kMaskPer + c;
-            mk[c] = g < n_g ? w.mask[(int64_t)i * w.n_grp + g] : 0ull;
+            if (g0 + c >= n_g) mk[c] = 0ull;
             cnt += (uint32_t)__popcll(mk[c]);
         }
         const uint32_t incl = wave_incl_scan_u32(cnt);
         if (lane == kWave - 1) sm.tk.red[wave] = incl;
+        if (tid < kDIdx) sm.q[tid] = bf16_value(qv);
         __syncthreads();
         uint32_t before, total;
         waves_prefix<kSelPNT / kWave>(sm.tk.red, wave, before, total);
         if (total > (uint32_t)kBandCap) {
             exact_all = true;
         } else {
+            // the masked blocks in ascending order, listed by the prefix
+            // count; entry: (MFMA score bits << 32) | block, NaN where the
+            // block shares its subgroup with another masked one
             uint32_t at = before + incl - cnt;
+            uint32_t kmn = ~0u, kmx = 0u;
 #pragma unroll
             for (int c = 0; c < kMaskPer; ++c) {
-                uint64_t bits = mk[c];
-                const int64_t g0 = (int64_t)(tid * kMaskPer + c) * 64;
+                const uint64_t M = mk[c];
+                const f32x4_t v = mx[c];
+                const int64_t gb = (int64_t)(g0 + c) * 64;
+                uint64_t bits = M;
                 while (bits) {
-                    sm.band[at++] = (uint64_t)(g0 + __builtin_ctzll(bits));
+                    const int bit = __builtin_ctzll(bits);
                     bits &= bits - 1;
+                    const int sub = bit >> 4;
+                    float m = __builtin_nanf("");
+                    if (__popc((uint32_t)(M >> (16 * sub)) & 0xffffu) == 1) {
+                        m = (sub & 2) ? ((sub & 1) ? v[3] : v[2]) : ((sub & 1) ? v[1] : v[0]);
+                        const uint32_t k = approx_key(m);
+                        kmn = min(kmn, k);
+                        kmx = max(kmx, k);
+                    } else {
+                        sm.xlist[atomicAdd(&sm.n_unscored, 1u)] = (uint16_t)at;
+                    }
+                    sm.band[at++] = ((uint64_t)__float_as_uint(m) << 32) | (uint64_t)(gb + bit);
                 }
             }
             __syncthreads();
             QSA_STAMP(11);
-            // two rows in flight per thread: their loads are issued together
-            for (int x = tid; x < (int)total; x += 2 * kSelPNT) {
-                const int y = x + kSelPNT;
-                const int64_t b0 = (int64_t)sm.band[x];
-                const int64_t b1 = y < (int)total ? (int64_t)sm.band[y] : b0;
-                const float s0 = exact_score(keys + b0 * kDIdx, sm.q);
-                const float s1 = exact_score(keys + b1 * kDIdx, sm.q);
-                sm.band[x] = block_key(s0, b0);
-                if (y < (int)total) sm.band[y] = block_key(s1, b1);
+            // the listed blocks without an MFMA score: the order-T score stands in
+            for (int j = tid; j < (int)sm.n_unscored; j += kSelPNT) {
+                const int x = sm.xlist[j];
+                const uint32_t b = (uint32_t)sm.band[x];
+                const float sc = exact_score(keys + (int64_t)b * kDIdx, sm.q);
+                const uint32_t k = approx_key(sc);
+                kmn = min(kmn, k);
+                kmx = max(kmx, k);
+                sm.band[x] = ((uint64_t)__float_as_uint(sc) << 32) | b;
+            }
+            kmn = wave_min_u32(kmn);
+            kmx = wave_max_u32(kmx);
+            if (lane == 0) {
+                atomicMin(&sm.kmin, kmn);
+                atomicMax(&sm.kmax, kmx);
             }
             __syncthreads();
-            QSA_STAMP(12);
-            BandKeys bk;
+            const uint32_t klo = sm.kmin, khi = sm.kmax;
+            const bool all_in = total <= (uint32_t)B;  // every masked block is kept
+            if (!all_in) {  // (block-uniform) the bin holding the B-th largest m
+                const int shift = sel_shift(klo, khi);
+                for (int x = tid; x < (int)total; x += kSelPNT) {
+                    const float m = __uint_as_float((uint32_t)(sm.band[x] >> 32));
+                    atomicAdd(&sm.bitmap[hist_word((approx_key(m) - klo) >> shift)], 1u);
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    uint32_t h[kSelBinsPerLane], local = 0;
 #pragma unroll
-            for (int c = 0; c < kBandCap / kSelPNT; ++c) {
-                const int x = c * kSelPNT + tid;
-                bk.k[c] = x < (int)total ? sm.band[x] : 0ull;
+                    for (int q = 0; q < kSelBinsPerLane; ++q) {
+                        h[q] = sm.bitmap[lane * (kSelBinsPerLane + 1) + q];
+                        local += h[q];
+                    }
+                    const uint32_t sc = wave_incl_scan_u32(local);
+                    uint32_t above = lane_value(sc, kWave - 1) - sc;
+                    uint32_t bin = 0;
+                    bool found = false;
+#pragma unroll
+                    for (int q = kSelBinsPerLane - 1; q >= 0; --q) {
+                        if (above < (uint32_t)B && above + h[q] >= (uint32_t)B) {
+                            found = true;
+                            bin = (uint32_t)(lane * kSelBinsPerLane + q);
+                        }
+                        above += h[q];
+                    }
+                    const uint64_t hit = __ballot(found);
+                    bin = lane_value(bin, __builtin_ctzll(hit));
+                    if (lane == 0) {
+                        const uint64_t e = (uint64_t)klo + ((uint64_t)(bin + 1) << shift) - 1;
+                        sm.in_edge = key_value(e < (uint64_t)khi ? (uint32_t)e : khi);
+                        sm.out_edge = key_value(klo + (bin << shift));
+                    }
+                }
+                __syncthreads();
             }
-            const Thresh th = topk_threshold<kSelPNT>(bk, (uint32_t)B, sm.tk);
+            QSA_STAMP(12);
+            // final keys: blocks certainly in above every order-T key, blocks
+            // certainly out 0; the rest listed, then rescored in order T
+            const double d2 = 2.0 * (double)delta;
+            const double in_above = (double)sm.in_edge + d2, out_below = (double)sm.out_edge - d2;
+            uint32_t my_in = 0;
+            for (int x = tid; x < (int)total; x += kSelPNT) {
+                const uint64_t e = sm.band[x];
+                const double m = (double)__uint_as_float((uint32_t)(e >> 32));
+                const uint32_t b = (uint32_t)e;
+                if (all_in || m > in_above) {
+                    sm.band[x] = (0xffffffffull << 32) | (uint64_t)(~b);
+                    ++my_in;
+                } else if (m < out_below) {
+                    sm.band[x] = 0ull;
+                } else {
+                    sm.xlist[atomicAdd(&sm.n_u, 1u)] = (uint16_t)x;
+                }
+            }
+            my_in = wave_sum_u32(my_in);
+            if (lane == 0 && my_in) atomicAdd(&sm.n_in, my_in);
+            __syncthreads();
+            const uint32_t n_u = sm.n_u, n_in = sm.n_in;
+            Thresh th{0u, 0u, false};  // every nonzero key kept
+            if (n_u > (uint32_t)kUCap) {
+                for (int j = tid; j < (int)n_u; j += kSelPNT) {
+                    const int x = sm.xlist[j];
+                    const uint32_t b = (uint32_t)sm.band[x];
+                    sm.band[x] = block_key(exact_score(keys + (int64_t)b * kDIdx, sm.q), b);
+                }
+                __syncthreads();
+                BandKeys bk;
+#pragma unroll
+                for (int c = 0; c < kBandCap / kSelPNT; ++c) {
+                    const int x = c * kSelPNT + tid;
+                    bk.k[c] = x < (int)total ? sm.band[x] : 0ull;
+                }
+                th = topk_threshold<kSelPNT>(bk, (uint32_t)B, sm.tk);
+            } else if (n_u > 0) {
+                if (wave == 0) {  // one block per lane; the best B - n_in stay
+                    const uint32_t need = (uint32_t)B > n_in ? (uint32_t)B - n_in : 0u;
+                    const bool mine_live = lane < (int)n_u;
+                    const int x = mine_live ? sm.xlist[lane] : 0;
+                    uint64_t mine = 0ull;
+                    if (mine_live) {
+                        const uint32_t b = (uint32_t)sm.band[x];
+                        mine = block_key(exact_score(keys + (int64_t)b * kDIdx, sm.q), b);
+                    }
+                    uint32_t rank = 0;
+                    for (int j = 0; j < (int)n_u; ++j) {
+                        const uint64_t o = ((uint64_t)lane_value((uint32_t)(mine >> 32), j) << 32) |
+                                           lane_value((uint32_t)mine, j);
+                        rank += o > mine ? 1u : 0u;
+                    }
+                    if (mine_live) sm.band[x] = rank < need ? mine : 0ull;
+                }
+                __syncthreads();
+            }
             QSA_STAMP(13);
             emit_from_band(sm.band, (int)total, th, B, a.r, nc, tail, out_blocks, out_cells,
                            ld_cells, n_sel + i, sm.tk);
         }
     }
     if (exact_all) {
+        if (tid < kDIdx) sm.q[tid] = bf16_value(w.qr[(int64_t)i * kDIdx + tid]);
         for (int x = tid; x < n_words; x += kSelPNT) sm.bitmap[x] = 0;
         __syncthreads();
         ExactStream src;

@@ -37,7 +37,7 @@ PREFILL_POINTS = {
     "k_prefill_scores (masks)": ("prefill", {4: "start", 5: "operands in",
                                              6: "first group", 7: "end"}),
     "k_prefill_tau": ("prefill", {8: "start", 9: "end"}),
-    "k_select_prefill": ("prefill", {10: "start", 11: "band listed", 12: "rescored",
+    "k_select_prefill": ("prefill", {10: "start", 11: "band listed", 12: "bracket",
                                      13: "threshold", 14: "end"}),
 }
 
