@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256) void k_rope_queries_delta(ScoreArgs a, const f
     int s;
     int64_t p;
     bool valid;
-    query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells, a.g.n_cells, a.r, s, p, valid);
+    const int64_t nc =
+        query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells, a.g.n_cells, a.r, s, p, valid);
+    if (lane == 0) w.qmeta[i] = make_int2(valid ? s : -1, (int)(nc < a.nb_max ? nc : a.nb_max));
     uint16_t lo16 = 0, hi16 = 0;
     if (valid) {
         float lo, hi;
@@ -279,53 +281,50 @@ __global__ __launch_bounds__(kPanelNT) void k_prefill_scores(ScoreArgs a, Prefil
     const int64_t cap_blocks = a.g.cap_cells / a.r;
     const int64_t n_sub = 4 * (int64_t)w.n_grp;
 
-    // the first unit's keys, requested before the query load so that the two
-    // overlap: the first sweep is almost always over the half's first row's
-    // sequence; a wrong guess is reloaded
-    bf16x8_t K[4][4];
-    int k_seq = -1, k_grp = set0 * kSetGroups + wave;
-    if (n_rows > 0) {
-        const int s0 = a.q_seq[qh0];
-        if (s0 >= 0 && s0 < a.g.n_seq && k_grp < w.n_grp) {
-            k_seq = s0;
-            load_key_tile(a.pooled_bf16 + (int64_t)s0 * cap_blocks * kDIdx, (int64_t)k_grp * 64,
-                          cap_blocks, true, K);
-        }
+    // every operand requested before the first wait: the rows' sequence and
+    // causal limit (and threshold), the half's queries, then the first
+    // unit's keys, for the sequence of the half's first row (the first sweep
+    // is almost always over it; a wrong guess is reloaded).  Query pieces are
+    // 16 bytes, row x / 16, part x % 16; rows past the last query repeat it:
+    // a column of the B operand only reaches its own column of results, and
+    // those are never stored.
+    const int s0 = n_rows > 0 ? a.q_seq[qh0] : -1;
+    int2 meta = make_int2(-1, 0);
+    float thr_row = 0.f;
+    if (tid < kHalfQ && tid < n_rows) {
+        meta = w.qmeta[qh0 + tid];
+        if constexpr (MODE == kMask) thr_row = w.thr[qh0 + tid];
     }
-    // the half's queries into LDS: 16-byte pieces, row x / 16, part x % 16,
-    // all of a thread's in flight at once.  Rows past the last query repeat
-    // it: a column of the B operand only reaches its own column of results,
-    // and those are never stored.
+    constexpr int kPer = kHalfQ * 16 / kPanelNT;
+    u32x4_t v[kPer];
     if (n_rows > 0) {
-        constexpr int kPer = kHalfQ * 16 / kPanelNT;
-        u32x4_t v[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int x = tid + i * kPanelNT, rr = min(x >> 4, n_rows - 1), part = x & 15;
             v[i] = *reinterpret_cast<const u32x4_t *>(w.qr + (int64_t)(qh0 + rr) * kDIdx +
                                                       part * 8);
         }
+    }
+    bf16x8_t K[4][4];
+    int k_seq = -1, k_grp = set0 * kSetGroups + wave;
+    if (s0 >= 0 && s0 < a.g.n_seq && k_grp < w.n_grp) {
+        k_seq = s0;
+        load_key_tile(a.pooled_bf16 + (int64_t)s0 * cap_blocks * kDIdx, (int64_t)k_grp * 64,
+                      cap_blocks, true, K);
+    }
+    // row tid of the half (wavefronts 0-3): sequence, causal limit, threshold
+    const int my_seq = meta.x, my_nc = meta.y;
+    if (tid < kHalfQ) {
+        s_seq[tid] = my_seq;
+        s_nc[tid] = my_nc;
+        if constexpr (MODE == kMask) s_thr[tid] = thr_row;
+    }
+    if (n_rows > 0) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int x = tid + i * kPanelNT, rr = x >> 4, part = x & 15;
             *reinterpret_cast<u32x4_t *>(&s_q[rr][part * 8]) = v[i];
         }
-    }
-    // row tid of the half (wavefronts 0-3): sequence, causal limit, threshold
-    int my_seq = -1, my_nc = 0;
-    if (tid < kHalfQ) {
-        const int qi = qh0 + tid;
-        if (tid < n_rows) {
-            int64_t p;
-            bool valid;
-            const int64_t nc = query_blocks(a.q_seq, a.q_pos, qi, a.g.n_seq, a.g.cap_cells,
-                                            a.g.n_cells, a.r, my_seq, p, valid);
-            if (!valid) my_seq = -1;
-            my_nc = (int)(nc < a.nb_max ? nc : a.nb_max);
-        }
-        s_seq[tid] = my_seq;
-        s_nc[tid] = my_nc;
-        if constexpr (MODE == kMask) s_thr[tid] = tid < n_rows ? w.thr[qi] : 0.f;
     }
 
     int sq = -1;  // the sequence being swept; rows of others are not stored
@@ -541,15 +540,6 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     QSA_STAMP(8);
     __shared__ TopkSmem<kTauNT> sm;
     const int i = blockIdx.x, tid = threadIdx.x;
-    int s;
-    int64_t p;
-    bool valid;
-    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells, a.g.n_cells,
-                                    a.r, s, p, valid);
-    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
-    const int n_sub = (int)((limit + 15) / 16);
-    const int B = top_k / a.r;
-    const float delta = w.delta[i];
     const float *row = w.smax + (int64_t)i * 4 * w.n_grp;
     // every load issued before the first is used: indexes clamped to the
     // row (n_sub <= 4 n_grp), entries past n_sub dropped afterwards
@@ -557,6 +547,9 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     float v[PER];
 #pragma unroll
     for (int c = 0; c < PER; ++c) v[c] = last >= 0 ? row[min(c * kTauNT + tid, last)] : 0.0f;
+    const int n_sub = (w.qmeta[i].y + 15) / 16;
+    const int B = top_k / a.r;
+    const float delta = w.delta[i];
     RegKeys32<PER, kTauNT> keys;
     keys.tid = tid;
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
@@ -906,6 +899,7 @@ static size_t prefill_layout(char *base, int n_q, int nb_max, PrefillWs *w) {
     d.mask = reinterpret_cast<uint64_t *>(take((size_t)n_q * d.n_grp * 8));
     d.qr = reinterpret_cast<uint16_t *>(take((size_t)n_q * kDIdx * 2));
     d.delta = reinterpret_cast<float *>(take((size_t)n_q * 4));
+    d.qmeta = reinterpret_cast<int2 *>(take((size_t)n_q * 8));
     if (w) *w = d;
     return off;
 }

@@ -386,6 +386,7 @@ struct PrefillWs {
     uint64_t *mask;   // [n_q][n_grp] blocks of each 64-block group with MFMA score >= thr
     uint16_t *qr;     // [n_q][128] roped queries, bf16
     float *delta;     // [n_q] bound on |MFMA score - T score|
+    int2 *qmeta;      // [n_q] (sequence, -1 if the query is invalid; causal blocks, at most nb_max)
     int32_t n_grp;
 };
 size_t prefill_ws_bytes(int n_q, int nb_max);
