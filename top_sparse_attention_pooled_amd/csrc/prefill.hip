@@ -527,19 +527,63 @@ __device__ __forceinline__ bool delta_in_range(float delta) {
     return delta >= kDeltaMin && delta <= kDeltaMax;  // false for NaN
 }
 
+// Bin q (of 2^11) held by lane q / 32 of one wavefront, at word q + q / 32:
+// the lanes' reads of their 32 consecutive bins hit different banks.
+constexpr int kTauHistWords = kBins + kBins / 32;
+__device__ __forceinline__ int tau_word(uint32_t q) { return (int)(q + (q >> 5)); }
+
+// One radix round's choice, by wavefront 0 alone: the bin of hist (over
+// [lo, hi], width 2^shift) holding the krem-th largest key; returns its
+// range [blo, bhi] and the keys above it (every lane gets them).
+__device__ __forceinline__ void tau_pick(const uint32_t *hist, uint32_t lo, uint32_t hi, int shift,
+                                         uint32_t krem, uint32_t &blo, uint32_t &bhi,
+                                         uint32_t &babove) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t h[32], local = 0;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        h[q] = hist[lane * 33 + q];
+        local += h[q];
+    }
+    const uint32_t incl = wave_incl_scan_u32(local);
+    uint32_t above = lane_value(incl, kWave - 1) - incl;  // keys in higher lanes' bins
+    uint32_t bin = 0, ab = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 31; q >= 0; --q) {
+        if (above < krem && above + h[q] >= krem) {
+            found = true;
+            bin = (uint32_t)(lane * 32 + q);
+            ab = above;
+        }
+        above += h[q];
+    }
+    const int src = __builtin_ctzll(__ballot(found));
+    bin = lane_value(bin, src);
+    babove = lane_value(ab, src);
+    blo = lo + (bin << shift);
+    bhi = blo + ((1u << shift) - 1u);
+    if (bhi > hi || bhi < blo) bhi = hi;
+}
+
 // grid (n_q), kTauNT threads: w.thr[i] = tau_i - 2 Delta_i rounded down,
 // tau_i the lower edge of the bin holding the B-th largest subgroup maximum
 // of query i after two radix rounds (2^11 bins over [lo, hi] at the smallest
 // power-of-two width, then within the chosen bin); -inf when fewer than B
 // subgroups hold a causal block or Delta_i is out of range (every causal
 // block then passes the filter).  PER (a power of two) maxima per thread
-// cover up to kTauNT * PER subgroups.
+// cover up to kTauNT * PER subgroups.  Four workgroup barriers: after the
+// count and range, after each round's histogram, after the first pick.
 constexpr int kTauMaxPer = kPrefMaxBlocks / 16 / kTauNT;
 template <int PER>
 __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w, int top_k) {
     QSA_STAMP(8);
-    __shared__ TopkSmem<kTauNT> sm;
+    constexpr int kW = kTauNT / kWave;
+    __shared__ uint32_t s_hist[2][kTauHistWords];
+    __shared__ uint32_t s_cnt[kW], s_mn[kW], s_mx[kW];
+    __shared__ uint32_t s_pick[3];
     const int i = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = wave_id();
     const float *row = w.smax + (int64_t)i * 4 * w.n_grp;
     // every load issued before the first is used: indexes clamped to the
     // row (n_sub <= 4 n_grp), entries past n_sub dropped afterwards
@@ -550,41 +594,69 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     const int n_sub = (w.qmeta[i].y + 15) / 16;
     const int B = top_k / a.r;
     const float delta = w.delta[i];
-    RegKeys32<PER, kTauNT> keys;
-    keys.tid = tid;
+    for (int j = tid; j < 2 * kTauHistWords; j += kTauNT) (&s_hist[0][0])[j] = 0u;
+    uint32_t key[PER];
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
         const int x = c * kTauNT + tid;
         const uint32_t k = x < n_sub ? approx_key(v[c]) : 0u;
-        keys.k[c] = k;
+        key[c] = k;
         if (k) {
             ++cnt;
             mn = min(mn, k);
             mx = max(mx, k);
         }
     }
-    const uint32_t n_valid = block_sum_u32<kTauNT>(cnt, sm);
+    cnt = wave_sum_u32(cnt);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        s_cnt[wave] = cnt;
+        s_mn[wave] = mn;
+        s_mx[wave] = mx;
+    }
+    __syncthreads();
+    uint32_t n_valid = 0, lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+        n_valid += s_cnt[u];
+        lo = min(lo, s_mn[u]);
+        hi = max(hi, s_mx[u]);
+    }
     float thr = -INFINITY;
-    if (n_valid >= (uint32_t)B && delta_in_range(delta)) {
-        block_minmax_u32<kTauNT>(mn, mx, sm);
-        // two rounds: the bin holding the B-th largest key, then the sub-bin
-        // within it; every key at or above the sub-bin's lower edge is >= it,
-        // and there are at least B of them
-        uint32_t lo = mn, hi = mx, krem = (uint32_t)B;
-        for (int round = 0; round < 2 && lo != hi; ++round) {
-            const int shift = range_shift(lo, hi);
-            for (int j = tid; j < kBins; j += kTauNT) sm.hist[j] = 0;
+    if (n_valid >= (uint32_t)B && delta_in_range(delta)) {  // (block-uniform)
+        uint32_t krem = (uint32_t)B;
+        if (lo != hi) {
+            int shift = range_shift(lo, hi);
+#pragma unroll
+            for (int c = 0; c < PER; ++c)
+                if (key[c]) atomicAdd(&s_hist[0][tau_word((key[c] - lo) >> shift)], 1u);
             __syncthreads();
-            keys([&](uint32_t k, uint32_t) {
-                if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> shift], 1u);
-            });
+            if (wave == 0) {
+                uint32_t blo, bhi, babove;
+                tau_pick(s_hist[0], lo, hi, shift, krem, blo, bhi, babove);
+                if (lane == 0) {
+                    s_pick[0] = blo;
+                    s_pick[1] = bhi;
+                    s_pick[2] = babove;
+                }
+            }
             __syncthreads();
-            pick_bin<kTauNT>(sm, lo, hi, shift, krem);
-            krem -= sm.b_above;
-            lo = sm.b_lo;
-            hi = sm.b_hi;
-            __syncthreads();
+            lo = s_pick[0];
+            hi = s_pick[1];
+            krem -= s_pick[2];
+            if (lo != hi) {
+                shift = range_shift(lo, hi);
+#pragma unroll
+                for (int c = 0; c < PER; ++c)
+                    if (key[c] >= lo && key[c] <= hi)
+                        atomicAdd(&s_hist[1][tau_word((key[c] - lo) >> shift)], 1u);
+                __syncthreads();
+                if (wave != 0) return;  // (no barrier follows)
+                uint32_t bhi, babove;
+                tau_pick(s_hist[1], lo, hi, shift, krem, lo, bhi, babove);
+            }
         }
         const float tau = key_value(lo);
         const double t = (double)tau - 2.0 * (double)delta;
