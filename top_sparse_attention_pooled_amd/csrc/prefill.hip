@@ -470,7 +470,7 @@ constexpr int kUCap = kWave;  // rescored band blocks one wavefront ranks
 constexpr int kSelBinBits = 10;
 constexpr int kSelBins = 1 << kSelBinBits;
 constexpr int kSelBinsPerLane = kSelBins / kWave;
-constexpr int kHistWords = kSelBins + kSelBins / kSelBinsPerLane;
+constexpr int kSelHistWords = kSelBins + kSelBins / kSelBinsPerLane;
 __device__ __forceinline__ int hist_word(uint32_t b) { return (int)(b + (b >> 4)); }
 __device__ __forceinline__ int sel_shift(uint32_t lo, uint32_t hi) {
     const uint32_t span = hi - lo;
@@ -488,7 +488,7 @@ struct PrefSelSmem {
     uint32_t n_unscored, kmin, kmax, n_in, n_u;
     float in_edge, out_edge;  // the bin of the B-th largest band score
 };
-static_assert(kHistWords <= kPrefMaxBlocks / 32, "histogram shares the bitmap");
+static_assert(kSelHistWords <= kPrefMaxBlocks / 32, "histogram shares the bitmap");
 static_assert(kSelBinsPerLane == 16, "bin padding assumes 16 bins per lane");
 
 __device__ __forceinline__ uint32_t approx_key(float v) {
@@ -527,45 +527,6 @@ __device__ __forceinline__ bool delta_in_range(float delta) {
     return delta >= kDeltaMin && delta <= kDeltaMax;  // false for NaN
 }
 
-// Bin q (of 2^11) held by lane q / 32 of one wavefront, at word q + q / 32:
-// the lanes' reads of their 32 consecutive bins hit different banks.
-constexpr int kTauHistWords = kBins + kBins / 32;
-__device__ __forceinline__ int tau_word(uint32_t q) { return (int)(q + (q >> 5)); }
-
-// One radix round's choice, by wavefront 0 alone: the bin of hist (over
-// [lo, hi], width 2^shift) holding the krem-th largest key; returns its
-// range [blo, bhi] and the keys above it (every lane gets them).
-__device__ __forceinline__ void tau_pick(const uint32_t *hist, uint32_t lo, uint32_t hi, int shift,
-                                         uint32_t krem, uint32_t &blo, uint32_t &bhi,
-                                         uint32_t &babove) {
-    const int lane = threadIdx.x & (kWave - 1);
-    uint32_t h[32], local = 0;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-        h[q] = hist[lane * 33 + q];
-        local += h[q];
-    }
-    const uint32_t incl = wave_incl_scan_u32(local);
-    uint32_t above = lane_value(incl, kWave - 1) - incl;  // keys in higher lanes' bins
-    uint32_t bin = 0, ab = 0;
-    bool found = false;
-#pragma unroll
-    for (int q = 31; q >= 0; --q) {
-        if (above < krem && above + h[q] >= krem) {
-            found = true;
-            bin = (uint32_t)(lane * 32 + q);
-            ab = above;
-        }
-        above += h[q];
-    }
-    const int src = __builtin_ctzll(__ballot(found));
-    bin = lane_value(bin, src);
-    babove = lane_value(ab, src);
-    blo = lo + (bin << shift);
-    bhi = blo + ((1u << shift) - 1u);
-    if (bhi > hi || bhi < blo) bhi = hi;
-}
-
 // grid (n_q), kTauNT threads: w.thr[i] = tau_i - 2 Delta_i rounded down,
 // tau_i the lower edge of the bin holding the B-th largest subgroup maximum
 // of query i after two radix rounds (2^11 bins over [lo, hi] at the smallest
@@ -579,7 +540,7 @@ template <int PER>
 __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w, int top_k) {
     QSA_STAMP(8);
     constexpr int kW = kTauNT / kWave;
-    __shared__ uint32_t s_hist[2][kTauHistWords];
+    __shared__ uint32_t s_hist[2][kHistWords];
     __shared__ uint32_t s_cnt[kW], s_mn[kW], s_mx[kW];
     __shared__ uint32_t s_pick[3];
     const int i = blockIdx.x, tid = threadIdx.x;
@@ -594,7 +555,7 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
     const int n_sub = (w.qmeta[i].y + 15) / 16;
     const int B = top_k / a.r;
     const float delta = w.delta[i];
-    for (int j = tid; j < 2 * kTauHistWords; j += kTauNT) (&s_hist[0][0])[j] = 0u;
+    for (int j = tid; j < 2 * kHistWords; j += kTauNT) (&s_hist[0][0])[j] = 0u;
     uint32_t key[PER];
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
 #pragma unroll
@@ -631,11 +592,11 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
             int shift = range_shift(lo, hi);
 #pragma unroll
             for (int c = 0; c < PER; ++c)
-                if (key[c]) atomicAdd(&s_hist[0][tau_word((key[c] - lo) >> shift)], 1u);
+                if (key[c]) atomicAdd(&s_hist[0][hist_slot((key[c] - lo) >> shift)], 1u);
             __syncthreads();
             if (wave == 0) {
-                uint32_t blo, bhi, babove;
-                tau_pick(s_hist[0], lo, hi, shift, krem, blo, bhi, babove);
+                uint32_t blo, bhi, babove, bcnt;
+                wave_pick_bin(s_hist[0], lo, hi, shift, krem, blo, bhi, babove, bcnt);
                 if (lane == 0) {
                     s_pick[0] = blo;
                     s_pick[1] = bhi;
@@ -651,11 +612,11 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
 #pragma unroll
                 for (int c = 0; c < PER; ++c)
                     if (key[c] >= lo && key[c] <= hi)
-                        atomicAdd(&s_hist[1][tau_word((key[c] - lo) >> shift)], 1u);
+                        atomicAdd(&s_hist[1][hist_slot((key[c] - lo) >> shift)], 1u);
                 __syncthreads();
                 if (wave != 0) return;  // (no barrier follows)
-                uint32_t bhi, babove;
-                tau_pick(s_hist[1], lo, hi, shift, krem, lo, bhi, babove);
+                uint32_t bhi, babove, bcnt;
+                wave_pick_bin(s_hist[1], lo, hi, shift, krem, lo, bhi, babove, bcnt);
             }
         }
         const float tau = key_value(lo);
@@ -762,7 +723,7 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
 
     if (!exact_all) {  // (limit 0: an empty band, the tail alone)
         const int n_g = (int)((limit + 63) / 64);
-        for (int j = tid; j < kHistWords; j += kSelPNT) sm.bitmap[j] = 0u;
+        for (int j = tid; j < kSelHistWords; j += kSelPNT) sm.bitmap[j] = 0u;
         if (tid == 0) {
             sm.n_unscored = 0u;
             sm.kmin = ~0u;

@@ -29,11 +29,18 @@ namespace qsa {
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;
 
+// A histogram of kBins bins, bin q at word q + q / 32: one wavefront reads
+// it with lane l holding bins [32 l, 32 l + 32), and those reads hit
+// different banks.
+constexpr int kHistWords = kBins + kBins / 32;
+__device__ __forceinline__ int hist_slot(uint32_t q) { return (int)(q + (q >> 5)); }
+
 template <int NT>
 struct TopkSmem {
-    uint32_t hist[kBins];
+    uint32_t hist[2][kHistWords];  // the radix rounds alternate between two
     uint32_t red[NT / 64];
     uint32_t red2[NT / 64];
+    uint32_t red3[NT / 64];
     uint32_t b_lo, b_hi, b_above, b_cnt;
 };
 
@@ -67,142 +74,106 @@ __device__ __forceinline__ void waves_prefix(const uint32_t *red, int wave, uint
     before = wave > 0 ? lane_value(incl, wave - 1) : 0u;
 }
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, TopkSmem<NT> &sm) {
-    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-    v = wave_sum_u32(v);
-    if (lane == 0) sm.red[wave] = v;
-    __syncthreads();
-    const uint32_t t = waves_sum<NT / 64>(sm.red);
-    __syncthreads();
-    return t;
-}
-
-// Block-wide (min, max) of per-thread values.
-template <int NT>
-__device__ __forceinline__ void block_minmax_u32(uint32_t &mn, uint32_t &mx, TopkSmem<NT> &sm) {
-    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-    mn = wave_min_u32(mn);
-    mx = wave_max_u32(mx);
-    if (lane == 0) {
-        sm.red[wave] = mn;
-        sm.red2[wave] = mx;
-    }
-    __syncthreads();
-    constexpr int NW = NT / 64;
-    mn = wave_min_u32(lane < NW ? sm.red[lane] : ~0u);
-    mx = wave_max_u32(lane < NW ? sm.red2[lane] : 0u);
-    __syncthreads();
-}
-
 __device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
     const uint32_t span = hi - lo;
     const int bits = span ? 32 - __builtin_clz(span) : 0;
     return bits > kBinBits ? bits - kBinBits : 0;
 }
 
-// Find the bin holding the krem-th largest value: sets b_lo/b_hi (the bin's
-// value range), b_above (values in higher bins) and b_cnt.
-template <int NT>
-__device__ __forceinline__ void pick_bin(TopkSmem<NT> &sm, uint32_t lo, uint32_t hi, int shift,
-                                         uint32_t krem) {
-    constexpr int PER = kBins / NT;  // consecutive bins per thread
-    const int t = threadIdx.x;
+// One radix round's choice, made by a single wavefront (every lane gets the
+// result): the bin of hist (kBins bins of width 2^shift over [lo, hi]) that
+// holds the krem-th largest value; its range [blo, bhi], the values in
+// higher bins (babove) and in it (bcnt).  Lane l sums bins [32 l, 32 l +
+// 32); a scan over the lanes finds the lane L whose bins hold the crossing,
+// then lane q < 32 reads bin 32 L + q and a second scan finds the bin (few
+// registers: the fused decode kernel keeps two workgroups per CU).
+__device__ __forceinline__ void wave_pick_bin(const uint32_t *hist, uint32_t lo, uint32_t hi,
+                                              int shift, uint32_t krem, uint32_t &blo,
+                                              uint32_t &bhi, uint32_t &babove, uint32_t &bcnt) {
+    const int lane = threadIdx.x & (kWave - 1);
     uint32_t local = 0;
-    uint32_t h[PER];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        h[q] = sm.hist[t * PER + q];
-        local += h[q];
-    }
-    // suffix sums: values in bins above this thread's bins
-    const int lane = t & (kWave - 1), wave = wave_id();
-    const uint32_t prefix = wave_incl_scan_u32(local);     // lanes <= this one
-    const uint32_t total = lane_value(prefix, kWave - 1);  // whole wave
-    if (lane == 0) sm.red[wave] = total;
-    __syncthreads();
-    uint32_t before, all;
-    waves_prefix<NT / 64>(sm.red, wave, before, all);
-    uint32_t above = all - before - prefix;  // higher lanes and higher wavefronts
-#pragma unroll
-    for (int q = PER - 1; q >= 0; --q) {
-        if (above < krem && above + h[q] >= krem) {
-            const uint32_t blo = lo + ((uint32_t)(t * PER + q) << shift);
-            uint32_t bhi = blo + ((1u << shift) - 1u);
-            if (bhi > hi || bhi < blo) bhi = hi;
-            sm.b_lo = blo;
-            sm.b_hi = bhi;
-            sm.b_above = above;
-            sm.b_cnt = h[q];
-        }
-        above += h[q];
-    }
-    __syncthreads();
+    for (int q = 0; q < 32; ++q) local += hist[lane * 33 + q];
+    const uint32_t incl = wave_incl_scan_u32(local);
+    const uint32_t above = lane_value(incl, kWave - 1) - incl;  // values in higher lanes' bins
+    const int L = __builtin_ctzll(__ballot(above < krem && above + local >= krem));
+    const uint32_t above_l = lane_value(above, L);
+    const uint32_t h = lane < 32 ? hist[L * 33 + lane] : 0u;
+    const uint32_t incl2 = wave_incl_scan_u32(h);
+    const uint32_t ab = above_l + (lane_value(incl2, 31) - incl2);  // values in higher bins
+    const int q = __builtin_ctzll(__ballot(lane < 32 && ab < krem && ab + h >= krem));
+    const uint32_t bin = (uint32_t)(L * 32 + q);
+    babove = lane_value(ab, q);
+    bcnt = lane_value(h, q);
+    blo = lo + (bin << shift);
+    bhi = blo + ((1u << shift) - 1u);
+    if (bhi > hi || bhi < blo) bhi = hi;
 }
 
 // Radix select of the krem-th largest of the values v = VAL(k, u) over the
-// elements with PRED(k, u), starting from their range [lo, hi].  Returns the
-// threshold value; n_above gets the count strictly above it; done tells
-// whether count(v >= threshold) == krem (no tie left at the threshold).
+// elements with PRED(k, u), in [lo, hi].  Histogram hist[buf] is clear on
+// entry; each round fills it, wavefront 0 picks the bin while the others
+// clear the other one for the next round (two barriers per round; every
+// thread has read the round's result when it returns, no barrier after).
+// Returns the threshold value; n_above gets the count strictly above it;
+// done tells whether count(v >= threshold) == krem (no tie left at the
+// threshold).  On return hist[buf] is clear again.
 template <int NT, typename ForEach, typename Pred, typename Val>
-__device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pred, Val val, uint32_t krem, uint32_t lo,
-                               uint32_t hi, TopkSmem<NT> &sm, uint32_t &n_above, bool &done) {
+__device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pred, Val val,
+                                               uint32_t krem, uint32_t lo, uint32_t hi,
+                                               TopkSmem<NT> &sm, int &buf, uint32_t &n_above,
+                                               bool &done) {
+    const int wave = wave_id();
     n_above = 0;
+    done = false;
     for (int round = 0; round < 4; ++round) {
         const int shift = range_shift(lo, hi);
-        for (int j = threadIdx.x; j < kBins; j += NT) sm.hist[j] = 0;
-        __syncthreads();
+        uint32_t *hist = sm.hist[buf];
         for_each([&](uint32_t k, uint32_t u) {
             if (!pred(k, u)) return;
             const uint32_t v = val(k, u);
-            if (v >= lo && v <= hi) atomicAdd(&sm.hist[(v - lo) >> shift], 1u);
+            if (v >= lo && v <= hi) atomicAdd(&hist[hist_slot((v - lo) >> shift)], 1u);
         });
         __syncthreads();
-        pick_bin<NT>(sm, lo, hi, shift, krem);
+        if (wave == 0) {
+            uint32_t blo, bhi, babove, bcnt;
+            wave_pick_bin(hist, lo, hi, shift, krem, blo, bhi, babove, bcnt);
+            if ((threadIdx.x & (kWave - 1)) == 0) {
+                sm.b_lo = blo;
+                sm.b_hi = bhi;
+                sm.b_above = babove;
+                sm.b_cnt = bcnt;
+            }
+        } else {
+            uint32_t *other = sm.hist[buf ^ 1];
+            for (int j = (int)threadIdx.x - kWave; j < kHistWords; j += NT - kWave) other[j] = 0u;
+        }
+        __syncthreads();
         const uint32_t above = sm.b_above, cnt = sm.b_cnt;
         lo = sm.b_lo;
         hi = sm.b_hi;
-        __syncthreads();
         n_above += above;
         krem -= above;
+        buf ^= 1;
         if (cnt == krem) {
             done = true;
-            return lo;
+            break;
         }
         if (lo == hi) break;  // a single value shared by more than krem elements
-    }
-    done = false;
-    return lo;
-}
-
-// The krem-th largest value among the keys k in [lo, hi] (k = 0 never
-// counts when lo > 0): the same binning, continued until the bin is a single
-// value (at most 3 rounds of 11 bits).  The caller guarantees that [lo, hi]
-// holds at least krem keys.
-template <int NT, typename ForEach>
-__device__ __forceinline__ uint32_t kth_largest_u32(const ForEach &for_each, uint32_t krem,
-                                                    uint32_t lo, uint32_t hi, TopkSmem<NT> &sm) {
-    while (lo != hi) {
-        const int shift = range_shift(lo, hi);
-        for (int j = threadIdx.x; j < kBins; j += NT) sm.hist[j] = 0;
-        __syncthreads();
-        for_each([&](uint32_t k, uint32_t) {
-            if (k >= lo && k <= hi) atomicAdd(&sm.hist[(k - lo) >> shift], 1u);
-        });
-        __syncthreads();
-        pick_bin<NT>(sm, lo, hi, shift, krem);
-        krem -= sm.b_above;
-        lo = sm.b_lo;
-        hi = sm.b_hi;
-        __syncthreads();
     }
     return lo;
 }
 
 // The exact kept set of the top B (or every valid element if there are at
-// most B).
+// most B).  Count and range of the valid keys in one reduction (both
+// histograms cleared meanwhile), then radix rounds over the score keys and,
+// for a tie at the threshold, over the block order.  When it returns, every
+// thread is past its reads of sm.red: the caller may reuse that.
 template <int NT, typename ForEach>
 __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32_t B, TopkSmem<NT> &sm) {
+    constexpr int NW = NT / 64;
+    static_assert(NW >= 2, "a wavefront picks while the others clear");
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     Thresh th{0u, 0u, false};
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
     for_each([&](uint32_t k, uint32_t) {
@@ -211,14 +182,29 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
         mn = min(mn, k);
         mx = max(mx, k);
     });
-    const uint32_t n_valid = block_sum_u32<NT>(cnt, sm);
-    if (n_valid <= B) return th;  // T = 0: every valid element
-    block_minmax_u32<NT>(mn, mx, sm);
+    cnt = wave_sum_u32(cnt);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        sm.red[wave] = cnt;
+        sm.red2[wave] = mn;
+        sm.red3[wave] = mx;
+    }
+    for (int j = threadIdx.x; j < 2 * kHistWords; j += NT) (&sm.hist[0][0])[j] = 0u;
+    __syncthreads();
+    const uint32_t n_valid = wave_sum_u32(lane < NW ? sm.red[lane] : 0u);
+    const uint32_t lo = wave_min_u32(lane < NW ? sm.red2[lane] : ~0u);
+    const uint32_t hi = wave_max_u32(lane < NW ? sm.red3[lane] : 0u);
+    if (n_valid <= B) {  // T = 0: every valid element
+        __syncthreads();
+        return th;
+    }
+    int buf = 0;
     uint32_t n_above;
     bool done;
     th.T = select_u32<NT>(
         for_each, [](uint32_t k, uint32_t) { return k != 0; },
-        [](uint32_t k, uint32_t) { return k; }, B, mn, mx, sm, n_above, done);
+        [](uint32_t k, uint32_t) { return k; }, B, lo, hi, sm, buf, n_above, done);
     if (done) return th;
     // ties at score key T: keep the lowest blocks (largest u) among them
     const uint32_t T = th.T;
@@ -228,10 +214,18 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
         umn = min(umn, u);
         umx = max(umx, u);
     });
-    block_minmax_u32<NT>(umn, umx, sm);
+    umn = wave_min_u32(umn);
+    umx = wave_max_u32(umx);
+    if (lane == 0) {
+        sm.red2[wave] = umn;
+        sm.red3[wave] = umx;
+    }
+    __syncthreads();
+    const uint32_t ulo = wave_min_u32(lane < NW ? sm.red2[lane] : ~0u);
+    const uint32_t uhi = wave_max_u32(lane < NW ? sm.red3[lane] : 0u);
     th.U = select_u32<NT>(
         for_each, [T](uint32_t k, uint32_t) { return k == T; },
-        [](uint32_t, uint32_t u) { return u; }, B - n_above, umn, umx, sm, n_above, done);
+        [](uint32_t, uint32_t u) { return u; }, B - n_above, ulo, uhi, sm, buf, n_above, done);
     th.tie = true;
     return th;
 }
