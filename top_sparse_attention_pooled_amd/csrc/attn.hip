@@ -377,24 +377,32 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int g = (hg * G) / hpk;
     const int h0 = hg * G;
     QSA_STAMP(0);
+    // requests in order: the query's sequence and position, the candidates,
+    // the query rows, then the sequence's cell count -- which the selection
+    // does not wait for (only the re-admission path and the tail need it)
+    const ScoreArgs &sa = f.s;
+    QueryFields qf{0, 0, 0, sa.g.n_seq, sa.g.cap_cells, sa.r, sa.nb_max};
+    const int s_first = sa.q_seq[i];
+    const int64_t p_first = sa.q_pos[i];
+    CandKeys<kSelAttnNT, kSelAttnMaxBlocks> ck;
+    uint64_t drop[kSelAttnMaxBlocks / kGroup / kSelAttnNT];
+    load_candidates(f, i, ck, drop);
     float qv[G][8];
     load_q<G>(a, i, h0, j, qv);
-
-    const ScoreArgs &sa = f.s;
-    int s;
-    int64_t p;
-    bool valid;
-    const int64_t nc = query_blocks(sa.q_seq, sa.q_pos, i, sa.g.n_seq, sa.g.cap_cells,
-                                    sa.g.n_cells, sa.r, s, p, valid);
-    const int64_t limit = nc < sa.nb_max ? nc : sa.nb_max;
+    qf.s = s_first;
+    qf.p = p_first;
+    qf.ncell = sa.g.n_cells[min(max(s_first, 0), sa.g.n_seq - 1)];
     const int r = sa.r;
     const int B = f.top_k / r;
-    const int tail = valid ? (int)(p + 1 - nc * r) : 0;
-    CandKeys<kSelAttnNT, kSelAttnMaxBlocks> ck;
     Thresh th;
-    const bool fast =
-        select_candidates<kSelAttnNT, kSelAttnMaxBlocks, true>(f, i, limit, B, ss, ck, th);
+    const bool fast = select_candidates<kSelAttnNT, kSelAttnMaxBlocks, true>(f, i, qf, B, ss,
+                                                                            ck, drop, th);
     QSA_STAMP(2);
+    bool valid;
+    const int64_t nc = qf.blocks(valid);
+    const int64_t limit = nc < sa.nb_max ? nc : sa.nb_max;
+    const int s = qf.s;
+    const int tail = valid ? (int)(qf.p + 1 - nc * r) : 0;
 
     // List positions [c_begin, c_begin + 32): the kept blocks of ascending
     // rank [k_lo, k_hi] (block k covers positions k*r .. k*r + r-1), then

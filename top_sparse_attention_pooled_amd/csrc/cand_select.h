@@ -99,25 +99,16 @@ struct CandSelSmem {
     int over[kMaxExpand];
 };
 
-// The exact top-B blocks among query i's scored blocks [0, limit): the
-// threshold th over the candidates ck (both returned).  Returns true when no
-// group was re-admitted and the score row was not streamed: the kept set is
-// then exactly the base slots of ck that th keeps.  The kept blocks are also
-// marked in sm.bitmap (words [0, ceil(limit/32)) all written), except in that
-// case when SKIP_FAST_MARK.  Needs nb_max <= MAXB.  Workgroup-uniform; ends
-// with a barrier.
-template <int NT, int MAXB, bool SKIP_FAST_MARK = false>
-__device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i, int64_t limit,
-                                                  int B, CandSelSmem<NT, MAXB> &sm,
-                                                  CandKeys<NT, MAXB> &ck, Thresh &th) {
-    const int tid = threadIdx.x;
+// Query i's candidate keys into ck and each group's largest dropped key into
+// drop: every load issued at once, none depending on another load, so a
+// kernel issues them first.
+template <int NT, int MAXB>
+__device__ __forceinline__ void load_candidates(const DecodeIdxArgs &f, int i,
+                                                CandKeys<NT, MAXB> &ck,
+                                                uint64_t (&drop)[MAXB / kGroup / NT]) {
+    using Keys = CandKeys<NT, MAXB>;
     const int n_grp = cand_groups(f.s.nb_max);
     const int64_t qbase = (int64_t)i * n_grp;
-    const float *srow = f.s.scores + (int64_t)i * f.s.ld;
-    const int n_words = (int)((limit + 31) / 32);
-    for (int w = tid; w < n_words; w += NT) sm.bitmap[w] = 0;
-
-    using Keys = CandKeys<NT, MAXB>;
     const int kc = f.n_cand;
     const int n_cand = n_grp * kc;
     ck.nb = (n_cand + NT - 1) / NT;
@@ -129,15 +120,54 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
     }
 #pragma unroll
     for (int s = 0; s < Keys::kExp; ++s) ck.k[Keys::kBase + s] = 0ull;
-    // largest dropped key of each group, fetched with the keys
-    constexpr int kDrop = MAXB / kGroup / NT;
-    static_assert(kDrop >= 1, "drop slots");
-    uint64_t drop[kDrop];
 #pragma unroll
-    for (int q = 0; q < kDrop; ++q) {
-        const int g = tid + NT * q;
+    for (int q = 0; q < MAXB / kGroup / NT; ++q) {
+        const int g = (int)threadIdx.x + NT * q;
         drop[q] = g < n_grp ? f.drop[qbase + g] : 0ull;
     }
+}
+
+// The exact top-B blocks among query i's scored blocks [0, limit), limit =
+// qf.limit(): the threshold th over the candidates ck (loaded by
+// load_candidates, with drop) (both returned).  Returns true when no group
+// was re-admitted and the score row was not streamed: the kept set is then
+// exactly the base slots of ck that th keeps, and the query's cell count
+// has not been needed.  The kept blocks are also marked in sm.bitmap (words
+// [0, ceil(limit/32)) all written), except in that case when
+// SKIP_FAST_MARK.  Needs nb_max <= MAXB.  Workgroup-uniform; ends with a
+// barrier.
+template <int NT, int MAXB, bool SKIP_FAST_MARK = false>
+__device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
+                                                  const QueryFields &qf, int B,
+                                                  CandSelSmem<NT, MAXB> &sm,
+                                                  CandKeys<NT, MAXB> &ck,
+                                                  const uint64_t (&drop)[MAXB / kGroup / NT],
+                                                  Thresh &th) {
+    const int tid = threadIdx.x;
+    const float *srow = f.s.scores + (int64_t)i * f.s.ld;
+    using Keys = CandKeys<NT, MAXB>;
+    constexpr int kDrop = MAXB / kGroup / NT;
+    static_assert(kDrop >= 1, "drop slots");
+    if (tid == 0) sm.n_over = 0;
+    th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
+
+#pragma unroll
+    for (int q = 0; q < kDrop; ++q) {
+        const uint64_t d = drop[q];
+        if (d != 0 && th.keep((uint32_t)(d >> 32), (uint32_t)d)) {
+            const int at = atomicAdd(&sm.n_over, 1);
+            if (at < kMaxExpand) sm.over[at] = tid + NT * q;
+        }
+    }
+    __syncthreads();
+    const int n_over = sm.n_over;
+    const bool fast = n_over == 0;
+    if (SKIP_FAST_MARK && fast) return true;
+
+    const int64_t limit = qf.limit();
+    const int n_words = (int)((limit + 31) / 32);
+    for (int w = tid; w < n_words; w += NT) sm.bitmap[w] = 0;
+    if (fast) __syncthreads();  // (otherwise a threshold pass orders the clearing and marking)
     auto from_memory = [&](auto &&fn) {
         constexpr int U = 16;
         for (int64_t base = 0; base < limit; base += (int64_t)NT * U) {
@@ -154,24 +184,12 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
             }
         }
     };
-    if (tid == 0) sm.n_over = 0;
-    th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
-
-#pragma unroll
-    for (int q = 0; q < kDrop; ++q) {
-        const uint64_t d = drop[q];
-        if (d != 0 && th.keep((uint32_t)(d >> 32), (uint32_t)d)) {
-            const int at = atomicAdd(&sm.n_over, 1);
-            if (at < kMaxExpand) sm.over[at] = tid + NT * q;
-        }
-    }
-    __syncthreads();
-    const int n_over = sm.n_over;
     const bool stream = n_over > kMaxExpand;
     if (stream) {
         th = topk_threshold<NT>(from_memory, (uint32_t)B, sm.tk);
     } else if (n_over > 0) {
         // replace the kept keys of the re-admitted groups by all of theirs
+        const int kc = f.n_cand;
 #pragma unroll
         for (int s = 0; s < Keys::kBase; ++s) {
             const int g = cand_index(ck.nb, s) / kc;
@@ -179,24 +197,25 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
                 if (sm.over[e] == g) ck.k[s] = 0ull;
         }
         ck.ne = (n_over * kGroup + NT - 1) / NT;
+        // every score requested before the first is used (indexes clamped)
+        float sc[Keys::kExp];
+        int64_t bbs[Keys::kExp];
 #pragma unroll
         for (int s = 0; s < Keys::kExp; ++s) {
             const int idx = s * NT + tid;
             const int x = idx / kGroup;
-            uint64_t key = 0ull;
-            if (x < n_over) {
-                const int64_t bb = (int64_t)sm.over[x] * kGroup + idx % kGroup;
-                if (bb < limit) {
-                    const float sc = srow[bb];
-                    if (finite_f32(sc)) key = block_key(sc, bb);
-                }
-            }
-            ck.k[Keys::kBase + s] = key;
+            const int64_t bb = x < n_over ? (int64_t)sm.over[x] * kGroup + idx % kGroup : -1;
+            bbs[s] = bb;
+            sc[s] = srow[bb >= 0 && bb < limit ? bb : 0];
+        }
+#pragma unroll
+        for (int s = 0; s < Keys::kExp; ++s) {
+            const int64_t bb = bbs[s];
+            ck.k[Keys::kBase + s] =
+                (bb >= 0 && bb < limit && finite_f32(sc[s])) ? block_key(sc[s], bb) : 0ull;
         }
         th = topk_threshold<NT>(ck, (uint32_t)B, sm.tk);
     }
-    const bool fast = n_over == 0;
-    if (SKIP_FAST_MARK && fast) return true;
 
     auto mark = [&](uint32_t k, uint32_t u) {
         if (th.keep(k, u)) {

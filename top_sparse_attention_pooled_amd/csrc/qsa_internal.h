@@ -121,6 +121,41 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
+// query_blocks in two steps, for kernels that request the query's fields
+// before their other loads and resolve them later: QueryFields::load reads
+// the sequence and position, then the sequence's cell count at a clamped
+// index (no check between the loads); blocks() gives what query_blocks
+// returns, limit() that capped at nb_max.
+struct QueryFields {
+    int s;
+    int64_t p;
+    int32_t ncell;
+    int n_seq;
+    int64_t cap_cells;
+    int r;
+    int64_t nb_max;
+    __device__ __forceinline__ void load(const int32_t *q_seq, const int32_t *q_pos,
+                                         const int32_t *n_cells, int i) {
+        s = q_seq[i];
+        p = q_pos[i];
+        ncell = n_cells[min(max(s, 0), n_seq - 1)];
+    }
+    __device__ __forceinline__ int64_t blocks(bool &valid) const {
+        valid = false;
+        if (s < 0 || s >= n_seq || p < 0) return 0;
+        int64_t n = ncell;
+        if (n > cap_cells) n = cap_cells;
+        if (p >= n) return 0;
+        valid = true;
+        return (p + 1) / r;
+    }
+    __device__ __forceinline__ int64_t limit() const {
+        bool v;
+        const int64_t nc = blocks(v);
+        return nc < nb_max ? nc : nb_max;
+    }
+};
+
 // Validity of query i; returns the number of complete visible blocks
 // (0 for an invalid query) and the sequence / position.
 __device__ __forceinline__ int64_t query_blocks(const int32_t *q_seq, const int32_t *q_pos,

@@ -363,16 +363,24 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
     __shared__ CandSelSmem<kSelNT, MAXB> sm;
     const ScoreArgs &a = f.s;
     const int i = blockIdx.x;
-    int s;
-    int64_t p;
-    bool valid;
-    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells,
-                                    a.g.n_cells, a.r, s, p, valid);
-    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
-    const int B = f.top_k / a.r;
+    // the query's sequence and position, then the candidates, then the
+    // sequence's cell count (the selection does not wait for it)
+    QueryFields qf{0, 0, 0, a.g.n_seq, a.g.cap_cells, a.r, a.nb_max};
+    const int s_first = a.q_seq[i];
+    const int64_t p_first = a.q_pos[i];
     CandKeys<kSelNT, MAXB> ck;
+    uint64_t drop[MAXB / kGroup / kSelNT];
+    load_candidates(f, i, ck, drop);
+    qf.s = s_first;
+    qf.p = p_first;
+    qf.ncell = a.g.n_cells[min(max(s_first, 0), a.g.n_seq - 1)];
+    const int B = f.top_k / a.r;
     Thresh th;
-    const bool fast = select_candidates<kSelNT, MAXB, true>(f, i, limit, B, sm, ck, th);
+    const bool fast = select_candidates<kSelNT, MAXB, true>(f, i, qf, B, sm, ck, drop, th);
+    bool valid;
+    const int64_t nc = qf.blocks(valid);
+    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
+    const int64_t p = qf.p;
     const int n_words = (int)((limit + 31) / 32);
     const int tail = valid ? (int)(p + 1 - nc * a.r) : 0;
     const int ld_cells = f.top_k + a.r - 1;
