@@ -638,25 +638,37 @@ hipError_t launch_g(const AttnArgs &a, int chunks_per_run, int n_runs, bool dire
 }
 
 // Heads per workgroup: 2 (enough workgroups to give every SIMD two
-// wavefronts on a single decode query, and a quarter of the registers of 8);
-// it must divide the query heads per KV head.
+// wavefronts on a single decode query, and a quarter of the registers of
+// 8); 4 (wide) when a call's queries fill the chip -- fewer, longer
+// workgroups, each K/V row loaded once for twice the heads; 8 heads cost
+// too many registers.  It must divide the query heads per KV head.
 template <int KVT>
 hipError_t launch_kvt(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct,
-                      hipStream_t st) {
+                      bool wide, hipStream_t st) {
     const int hpk = a.n_head / a.n_head_kv;
+    if (wide && hpk % 4 == 0) return launch_g<4, KVT>(a, chunks_per_run, n_runs, direct, st);
     if (hpk % 2 == 0) return launch_g<2, KVT>(a, chunks_per_run, n_runs, direct, st);
     return launch_g<1, KVT>(a, chunks_per_run, n_runs, direct, st);
 }
 
-hipError_t launch(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct,
+hipError_t launch(const AttnArgs &a, int chunks_per_run, int n_runs, bool direct, bool wide,
                   hipStream_t st) {
     if (a.n_q <= 0) return hipSuccess;
-    if (a.kv_type == QSA_KV_F32) return launch_kvt<QSA_KV_F32>(a, chunks_per_run, n_runs, direct, st);
-    if (a.kv_type == QSA_KV_F16) return launch_kvt<QSA_KV_F16>(a, chunks_per_run, n_runs, direct, st);
-    return launch_kvt<QSA_KV_Q8_0>(a, chunks_per_run, n_runs, direct, st);
+    if (a.kv_type == QSA_KV_F32)
+        return launch_kvt<QSA_KV_F32>(a, chunks_per_run, n_runs, direct, wide, st);
+    if (a.kv_type == QSA_KV_F16)
+        return launch_kvt<QSA_KV_F16>(a, chunks_per_run, n_runs, direct, wide, st);
+    return launch_kvt<QSA_KV_Q8_0>(a, chunks_per_run, n_runs, direct, wide, st);
 }
 
 int decode_runs(int ld_cells) { return (ld_cells + kChunk - 1) / kChunk; }
+
+// Chunks per run of the decode attention: one while a call fits the fused
+// grid (65 runs of a 2,051-cell list spread one query over the chip), two
+// past it (half the workgroups and partial states; measured on five
+// 250k-cell sessions, 4 heads x 2 chunks beat 2 x 1, 2 x 2, 4 x 1, 4 x 3,
+// 4 x 4 and 8 x 1).
+constexpr int kMultiChunks = 2;
 
 template <int G, int KVT>
 hipError_t launch_sel_g(const DecodeIdxArgs &f, const AttnArgs &a, hipStream_t st) {
@@ -688,8 +700,22 @@ size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells) {
     return (size_t)n_q * decode_runs(ld_cells) * n_head * (kHeadDim + 2) * sizeof(float);
 }
 
+// Whether the fused selection + attention grid of this call fits the chip
+// in one round (it then runs; otherwise selection and attention split).
+static bool fused_fits(const AttnArgs &a) {
+    const int hpk = a.n_head / a.n_head_kv;
+    const int n_set = (a.n_head / (hpk % 2 == 0 ? 2 : 1) + kParts - 1) / kParts;
+    return (int64_t)a.n_q * decode_runs(a.ld_cells) * n_set <= kSelAttnOnChip;
+}
+
+// The attention units are those of the fused kernel whenever that could
+// run (so the two paths give identical outputs); past it the units widen.
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st) {
-    return launch(a, 1, decode_runs(a.ld_cells), false, st);
+    if (!fused_fits(a)) {
+        const int span = kMultiChunks * kChunk;
+        return launch(a, kMultiChunks, (a.ld_cells + span - 1) / span, false, true, st);
+    }
+    return launch(a, 1, decode_runs(a.ld_cells), false, false, st);
 }
 
 hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnArgs &a,
@@ -699,9 +725,7 @@ hipError_t launch_select_attn_decode(DecodeIdxArgs f, void *ws_idx, const AttnAr
     // grid fits the chip in one round, wasteful beyond (several queries).
     // Then select once per query and attend over the lists instead; the
     // selection and the attention arithmetic are the same, so are the results.
-    const int hpk = a.n_head / a.n_head_kv;
-    const int n_set = (a.n_head / (hpk % 2 == 0 ? 2 : 1) + kParts - 1) / kParts;
-    if ((int64_t)a.n_q * decode_runs(a.ld_cells) * n_set > kSelAttnOnChip) {
+    if (!fused_fits(a)) {
         hipError_t e = launch_decode_select(f, ws_idx, st);
         if (e != hipSuccess) return e;
         return launch_attn_decode(a, st);
