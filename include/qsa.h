@@ -306,7 +306,10 @@ int qsa_score_select_prefill(const qsa_dims *dims, const qsa_seqs *seqs, const v
  *     block (a workgroup that holds a dirty block recomputes it in registers
  *     rather than reading it), keeping in the workspace the best keys of
  *     each group of 64 blocks (16 while nb_max <= 16384, 8 up to 32768, else
- *     4) and the largest key each group dropped;
+ *     4; when the call's queries overflow the fused selection + attention
+ *     grid of qsa_decode_select_attend -- n_q * ceil((top_k + r - 1) / 32)
+ *     * (4 for 16 heads over 2 KV heads) > 512 -- 16 up to 24576, 8 up to
+ *     49152, else 6) and the largest key each group dropped;
  *   qsa_decode_select_candidates selects from those, re-admitting all keys
  *     of any group whose dropped key could compete (or re-reading the score
  *     row if more than 32 groups could), so the selection is exact.

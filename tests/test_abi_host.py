@@ -45,8 +45,10 @@ def test_workspace_sizes():
     assert qsa.workspace_size(d, qsa.OP_SCORE_BF16, 512) == 512 * 128 * 2
     runs = -(-d.ld_cells // 32)  # 32-cell runs
     assert qsa.workspace_size(d, qsa.OP_ATTN_DECODE, 5) == 5 * runs * 16 * 258 * 4
-    n_grp = -(-62070 // 256) * 4  # decode score+select: per 64-block group, 4 kept + 1 dropped
-    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 5 * n_grp * 5 * 8
+    # decode score+select, sized for the calls whose queries overflow the fused
+    # grid: per 64-block group 6 kept + 1 dropped
+    n_grp = -(-62070 // 256) * 4
+    assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 5, 62070) == 5 * n_grp * 7 * 8
     # shorter contexts keep more keys per group: 16 for 196 groups (12,420 blocks)
     n_grp = -(-12420 // 256) * 4
     assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT, 1, 12420) == n_grp * 17 * 8
@@ -173,9 +175,10 @@ def test_prefill_indexer_workspace_and_limits():
     d = qsa.Dims()
     a256 = lambda x: -(-x // 256) * 256
     n_grp = -(-49785 // 256) * 4  # 64-block groups, 4 per 256 blocks
-    # subgroup maxima (4 per group), thresholds, group masks, roped queries, Delta
+    # subgroup maxima (4 per group), thresholds, group masks, roped queries,
+    # Delta, each query's (sequence, causal blocks)
     want = (a256(512 * n_grp * 4 * 4) + a256(512 * 4) + a256(512 * n_grp * 8)
-            + a256(512 * 128 * 2) + a256(512 * 4))
+            + a256(512 * 128 * 2) + a256(512 * 4) + a256(512 * 8))
     assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 512, 49785) == want
     assert qsa.workspace_size(d, qsa.OP_SCORE_SELECT_PREFILL, 0, 49785) == 0
     big = 131073  # blocks: above what the selection's bitmap holds

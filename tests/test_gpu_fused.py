@@ -161,18 +161,18 @@ def test_fused_fewer_blocks_than_budget(n_q):
 
 
 def test_fused_readmits_a_group_at_250k():
-    """248,278 cells (62,069 scored blocks): groups keep only their 4 best
-    keys at this length.  Six blocks of one group aligned with the query
+    """248,278 cells (62,069 scored blocks): groups keep only their 6 best
+    keys at this length.  Eight blocks of one group aligned with the query
     beat every other block, so that group's dropped key competes and its
     keys are re-admitted; one query runs the fused kernel (the bitmap path),
     three the per-query selection."""
     w = synth.Workload("fz250", 94, 1, 248278, n_new=1, steps=1, top_k=2048)
     kidx = synth.make_kidx(w)[0]
     q = synth.normal((w.d,), 94, 0, synth.T_QIDX)
-    planted = [40000 + 5 * j for j in range(6)]  # one 64-block group (block 40000 // 64 * 64 on)
+    planted = [40000 + 5 * j for j in range(8)]  # one 64-block group (block 40000 // 64 * 64 on)
     assert len({b // 64 for b in planted}) == 1
     aligned_cells(w, q, 248277, planted, kidx)
     for n_q in (1, 3):
-        s = run_case("one group with 6 winners at 250k", w, 248278, q, kidx, n_q)
+        s = run_case("one group with 8 winners at 250k", w, 248278, q, kidx, n_q)
         kept, _ = oracle.select(s, 248278 - n_q, w.r, w.top_k)
         assert np.isin(planted, kept).all()

@@ -360,6 +360,11 @@ static int decode_idx_args(const qsa_dims *dims, const qsa_seqs *seqs, const voi
     f->sel_blocks = sel_blocks_dev;
     f->sel_cells = sel_cells_dev;
     f->n_sel = n_sel_dev;
+    // the scoring call and the selection call of one step bind the same count
+    f->wide_cand = qsa::fused_decode_fits(n_q, dims->top_k + dims->r - 1, dims->n_head,
+                                          dims->n_head_kv)
+                       ? 0
+                       : 1;
     return QSA_OK;
 }
 

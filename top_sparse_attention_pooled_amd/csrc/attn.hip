@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     QueryFields qf{0, 0, 0, sa.g.n_seq, sa.g.cap_cells, sa.r, sa.nb_max};
     const int s_first = sa.q_seq[i];
     const int64_t p_first = sa.q_pos[i];
-    CandKeys<kSelAttnNT, kSelAttnMaxBlocks> ck;
+    CandKeys<kSelAttnNT, kSelAttnMaxBlocks, kCand> ck;
     uint64_t drop[kSelAttnMaxBlocks / kGroup / kSelAttnNT];
     load_candidates(f, i, ck, drop);
     float qv[G][8];
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int r = sa.r;
     const int B = f.top_k / r;
     Thresh th;
-    const bool fast = select_candidates<kSelAttnNT, kSelAttnMaxBlocks, true>(f, i, qf, B, ss,
+    const bool fast = select_candidates<kSelAttnNT, kSelAttnMaxBlocks, kCand, true>(f, i, qf, B, ss,
                                                                             ck, drop, th);
     QSA_STAMP(2);
     bool valid;
@@ -702,10 +702,10 @@ size_t attn_decode_ws_bytes(int n_q, int n_head, int ld_cells) {
 
 // Whether the fused selection + attention grid of this call fits the chip
 // in one round (it then runs; otherwise selection and attention split).
+static_assert(kSelAttnOnChip == 512 && kParts == 2 && kChunk == 32,
+              "fused_decode_fits assumes these");
 static bool fused_fits(const AttnArgs &a) {
-    const int hpk = a.n_head / a.n_head_kv;
-    const int n_set = (a.n_head / (hpk % 2 == 0 ? 2 : 1) + kParts - 1) / kParts;
-    return (int64_t)a.n_q * decode_runs(a.ld_cells) * n_set <= kSelAttnOnChip;
+    return fused_decode_fits(a.n_q, a.ld_cells, a.n_head, a.n_head_kv);
 }
 
 // The attention units are those of the fused kernel whenever that could

@@ -25,37 +25,48 @@
 namespace qsa {
 
 constexpr int kGroup = kTile;   // blocks per candidate group (one wavefront)
-constexpr int kCand = 4;        // fewest keys kept per group
-// candidates a selection workgroup holds in registers: 4 per group up to
-// nb_max 65536, 8 up to 32768, 16 up to 16384 blocks (more slots would cost
-// the fused decode kernel the registers that let two of its workgroups
-// share a CU)
+// Keys kept per group at the least, and the candidates a selection
+// workgroup holds in registers.  The fused decode kernel (512 threads,
+// every attention workgroup selecting): 4 per group up to nb_max 65536, 8
+// up to 32768, 16 up to 16384 blocks -- more slots would cost it the
+// registers that let two of its workgroups share a CU.  The per-query
+// selection (1024 threads, used when a call's queries overflow the fused
+// grid): 6 per group up to nb_max 65536 (per 65536), 8 up to 49152, 16 up
+// to 24576.
+constexpr int kCand = 4;
 constexpr int kCandSlots = 4096;
+constexpr int kCandWide = 6;
+constexpr int kCandSlotsWide = 6144;
 constexpr int kMaxExpand = 32;  // groups re-admitted whole before streaming
 
 // Workspace of the decode indexer: cand [n_q][groups][n_cand], then drop
 // [n_q][groups], groups = 4 per 256 blocks of nb_max.
 __host__ __device__ inline int cand_groups(int nb_max) { return (nb_max + 255) / 256 * 4; }
 
-// Keys kept per group: as many (16, 8, then 4) as the on-chip candidate
-// slots allow.  A group with more winners than it kept must be re-admitted
-// whole, which costs the selection a second pass: with B = 512 of ~62,000
-// blocks (250k cells) a group of 64 holds 0.53 winners on average, and with
-// 4 kept keys about one step in five has a group of 5 or more.  Winners
-// spread over fewer groups in a shorter context (512 of ~12,400 blocks at
-// 50k cells is 2.6 per group on average).
-__host__ __device__ inline int cand_per_group(int nb_max) {
+// Keys kept per group: as many (16, 8, then the least) as the on-chip
+// candidate slots allow.  A group with more winners than it kept must be
+// re-admitted whole, which costs the selection a second pass: with B = 512
+// of ~62,000 blocks (250k cells) a group of 64 holds 0.53 winners on
+// average; with 4 kept keys about one selection in five meets a group of 5
+// or more, with 6 about one in a thousand one of 7 or more (a step of five
+// sessions would otherwise re-admit in most steps).  Winners spread over
+// fewer groups in a shorter context (512 of ~12,400 blocks at 50k cells is
+// 2.6 per group on average).
+__host__ __device__ inline int cand_per_group(int nb_max, bool wide) {
     const int g = cand_groups(nb_max);
-    return g * 16 <= kCandSlots ? 16 : (g * 8 <= kCandSlots ? 8 : kCand);
+    const int slots = wide ? kCandSlotsWide : kCandSlots;
+    return g * 16 <= slots ? 16 : (g * 8 <= slots ? 8 : (wide ? kCandWide : kCand));
 }
 
+// Sized for the larger (wide) count, so one workspace serves every call.
 inline size_t cand_ws_bytes(int n_q, int nb_max) {
-    return (size_t)n_q * cand_groups(nb_max) * (cand_per_group(nb_max) + 1) * sizeof(uint64_t);
+    return (size_t)n_q * cand_groups(nb_max) * (cand_per_group(nb_max, true) + 1) *
+           sizeof(uint64_t);
 }
 
 inline void bind_candidates(DecodeIdxArgs &f, void *ws) {
     f.n_wg = (f.s.nb_max + 255) / 256;
-    f.n_cand = cand_per_group(f.s.nb_max);
+    f.n_cand = cand_per_group(f.s.nb_max, f.wide_cand != 0);
     f.cand = static_cast<uint64_t *>(ws);
     f.drop = f.cand + (size_t)f.s.n_q * cand_groups(f.s.nb_max) * f.n_cand;
 }
@@ -72,9 +83,9 @@ __device__ __forceinline__ int cand_index(int nb, int s) {
     return ((int)(threadIdx.x >> 6) * nb + s) * kWave + (int)(threadIdx.x & (kWave - 1));
 }
 
-template <int NT, int MAXB>
+template <int NT, int MAXB, int KC>
 struct CandKeys {
-    static constexpr int kBase = MAXB / kGroup * kCand / NT;
+    static constexpr int kBase = MAXB / kGroup * KC / NT;
     static constexpr int kExp = kMaxExpand * kGroup / NT;
     uint64_t k[kBase + kExp];
     int nb, ne;
@@ -102,11 +113,11 @@ struct CandSelSmem {
 // Query i's candidate keys into ck and each group's largest dropped key into
 // drop: every load issued at once, none depending on another load, so a
 // kernel issues them first.
-template <int NT, int MAXB>
+template <int NT, int MAXB, int KC>
 __device__ __forceinline__ void load_candidates(const DecodeIdxArgs &f, int i,
-                                                CandKeys<NT, MAXB> &ck,
+                                                CandKeys<NT, MAXB, KC> &ck,
                                                 uint64_t (&drop)[MAXB / kGroup / NT]) {
-    using Keys = CandKeys<NT, MAXB>;
+    using Keys = CandKeys<NT, MAXB, KC>;
     const int n_grp = cand_groups(f.s.nb_max);
     const int64_t qbase = (int64_t)i * n_grp;
     const int kc = f.n_cand;
@@ -136,16 +147,16 @@ __device__ __forceinline__ void load_candidates(const DecodeIdxArgs &f, int i,
 // [0, ceil(limit/32)) all written), except in that case when
 // SKIP_FAST_MARK.  Needs nb_max <= MAXB.  Workgroup-uniform; ends with a
 // barrier.
-template <int NT, int MAXB, bool SKIP_FAST_MARK = false>
+template <int NT, int MAXB, int KC, bool SKIP_FAST_MARK = false>
 __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
                                                   const QueryFields &qf, int B,
                                                   CandSelSmem<NT, MAXB> &sm,
-                                                  CandKeys<NT, MAXB> &ck,
+                                                  CandKeys<NT, MAXB, KC> &ck,
                                                   const uint64_t (&drop)[MAXB / kGroup / NT],
                                                   Thresh &th) {
     const int tid = threadIdx.x;
     const float *srow = f.s.scores + (int64_t)i * f.s.ld;
-    using Keys = CandKeys<NT, MAXB>;
+    using Keys = CandKeys<NT, MAXB, KC>;
     constexpr int kDrop = MAXB / kGroup / NT;
     static_assert(kDrop >= 1, "drop slots");
     if (tid == 0) sm.n_over = 0;

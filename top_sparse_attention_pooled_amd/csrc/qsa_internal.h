@@ -353,7 +353,8 @@ struct DecodeIdxArgs {
     uint64_t *cand;  // [n_q][4*n_wg][n_cand]: largest keys of each 64-block group
     uint64_t *drop;  // [n_q][4*n_wg]: largest key each group dropped
     int32_t n_wg;
-    int32_t n_cand;  // keys kept per group (16, 8 or 4: see cand_per_group)
+    int32_t n_cand;  // keys kept per group (see cand_per_group)
+    int32_t wide_cand;  // the call's queries overflow the fused grid: more keys per group
 };
 
 struct SelectArgs {
@@ -409,6 +410,20 @@ constexpr int kFusedMaxBlocks = 1 << 17;  // fused score+select handles nb_max u
 // decode selection fused into attention (256-thread workgroups holding the
 // candidates in registers) handles nb_max up to this: 262144-cell contexts
 constexpr int kSelAttnMaxBlocks = 1 << 16;
+
+// Whether the fused decode selection + attention grid of a call -- one
+// 512-thread workgroup per (query, run of 32 list cells, pair of 2-head
+// groups) -- fits the chip in one round (512 workgroups, two per CU).  It
+// then runs; otherwise the selection runs once per query and the attention
+// over the lists.  The indexer calls use the same rule to choose how many
+// candidates a group keeps.
+__host__ __device__ inline bool fused_decode_fits(int n_q, int ld_cells, int n_head,
+                                                  int n_head_kv) {
+    const int hpk = n_head / n_head_kv;
+    const int n_set = (n_head / (hpk % 2 == 0 ? 2 : 1) + 1) / 2;
+    const int n_runs = (ld_cells + 31) / 32;
+    return (int64_t)n_q * n_runs * n_set <= 512;
+}
 size_t fused_select_ws_bytes(int n_q, int nb_max);
 // part 1: update + scores + candidates; part 2: selection from candidates
 hipError_t launch_decode_candidates(DecodeIdxArgs f, void *ws, hipStream_t st);

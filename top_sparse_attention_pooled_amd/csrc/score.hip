@@ -146,18 +146,20 @@ __device__ __forceinline__ void bitonic_step(uint64_t &k, int lane) {
     k = take_max ? (o > k ? o : k) : (o < k ? o : k);
 }
 
-// Lanes [0, n) (n = 4, 8 or 16, wave-uniform) hold keys (score key << 32 |
-// ~block); on return they hold the same keys by descending ~block, that is
-// ascending block, with zero keys last.  A bitonic network over groups of n
-// lanes on the swapped halves; lanes from n on end up with other keys of
-// their own groups.
+// Lanes [0, n) (n = 4, 6, 8 or 16, wave-uniform) hold keys (score key <<
+// 32 | ~block); on return they hold the same keys by descending ~block,
+// that is ascending block, with zero keys last.  A bitonic network over
+// groups of 4, 8 or 16 lanes (n = 6: 8, lanes 6 and 7 emptied first) on the
+// swapped halves; lanes from n on end up with other keys of their own
+// groups.
 __device__ __forceinline__ uint64_t group_sort_by_block(uint64_t key, int n) {
     const int lane = threadIdx.x & (kWave - 1);
+    if (n == 6 && (lane & 7) >= 6) key = 0ull;
     uint64_t k = (key << 32) | (key >> 32);
     bitonic_step<2, 1>(k, lane);
     bitonic_step<4, 2>(k, lane);
     bitonic_step<4, 1>(k, lane);
-    if (n >= 8) {
+    if (n >= 6) {
         bitonic_step<8, 4>(k, lane);
         bitonic_step<8, 2>(k, lane);
         bitonic_step<8, 1>(k, lane);
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
     QueryFields qf{0, 0, 0, a.g.n_seq, a.g.cap_cells, a.r, a.nb_max};
     const int s_first = a.q_seq[i];
     const int64_t p_first = a.q_pos[i];
-    CandKeys<kSelNT, MAXB> ck;
+    CandKeys<kSelNT, MAXB, kCandWide> ck;
     uint64_t drop[MAXB / kGroup / kSelNT];
     load_candidates(f, i, ck, drop);
     qf.s = s_first;
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
     qf.ncell = a.g.n_cells[min(max(s_first, 0), a.g.n_seq - 1)];
     const int B = f.top_k / a.r;
     Thresh th;
-    const bool fast = select_candidates<kSelNT, MAXB, true>(f, i, qf, B, sm, ck, drop, th);
+    const bool fast = select_candidates<kSelNT, MAXB, kCandWide, true>(f, i, qf, B, sm, ck, drop, th);
     bool valid;
     const int64_t nc = qf.blocks(valid);
     const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
