@@ -376,7 +376,8 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int hpk = a.n_head / a.n_head_kv;
     const int g = (hg * G) / hpk;
     const int h0 = hg * G;
-    QSA_STAMP(0);
+    QSA_STAMP_HOLD(t_start);
+    QSA_STAMP_LDS_BEGIN();
     // requests in order: the query's sequence and position, the candidates,
     // the query rows, then the sequence's cell count -- which the selection
     // does not wait for (only the re-admission path and the tail need it)
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     Thresh th;
     const bool fast = select_candidates<kSelAttnNT, kSelAttnMaxBlocks, kCand, true>(f, i, qf, B, ss,
                                                                             ck, drop, th);
-    QSA_STAMP(2);
+    QSA_STAMP_HOLD(t_thresh);
     bool valid;
     const int64_t nc = qf.blocks(valid);
     const int64_t limit = nc < sa.nb_max ? nc : sa.nb_max;
@@ -411,13 +412,10 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     const int k_lo = c_begin / r, k_hi = (c_begin + kChunk - 1) / r;
     const int ld_cells = f.top_k + r - 1;
     int32_t *sel_blocks = f.sel_blocks + (int64_t)i * B;
-    auto place = [&](int k, int b) {
-        for (int c = 0; c < r; ++c) {
-            const int pos = k * r + c - c_begin;
-            if (pos >= 0 && pos < kChunk) s_cells[pos] = b * r + c;
-        }
-    };
-    uint32_t local = 0, incl;
+    // Each path leaves the kept blocks of ranks k_lo .. k_hi in s_blk; one
+    // wavefront then expands them (and the tail) into the run's cells.  (The
+    // expansion is one short loop-free step rather than a copy per kept key:
+    // this code runs once per workgroup, so its size is fetch time.)
     int n_keep_all;
     if (fast) {
         // the kept set is the base candidates th keeps; they ascend by block
@@ -448,29 +446,18 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
             const bool kp = th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]);
             const uint64_t bal = __ballot(kp);
             const int k = (int)(k0 + __popcll(bal & below));
-            if (kp && k >= k_lo && k <= k_hi && k < n_keep) {
-                const int b = key_block(ck.k[x]);
-                place(k, b);
-                s_blk[k - k_lo] = b;
-            }
+            if (kp && k >= k_lo && k <= k_hi && k < n_keep) s_blk[k - k_lo] = key_block(ck.k[x]);
             k0 += __popcll(bal);
         }
-        if (tid < kChunk) {
-            const int pos = c_begin + tid;
-            if (pos >= n_keep * r) {
-                const int n_sel = n_keep * r + tail;
-                s_cells[tid] = pos < n_sel ? (int)(nc * r + (pos - n_keep * r)) : -1;
-            }
-        }
-        __syncthreads();
         n_keep_all = n_keep;
     } else {
         // ranks of this thread's bitmap words
         const int n_words = (int)((limit + 31) / 32);
         const int per = (n_words + kSelAttnNT - 1) / kSelAttnNT;
         const int w0 = tid * per;
+        uint32_t local = 0;
         for (int w = w0; w < w0 + per && w < n_words; ++w) local += __popc(ss.bitmap[w]);
-        incl = wave_incl_scan_u32(local);
+        const uint32_t incl = wave_incl_scan_u32(local);
         if (lane == kWave - 1) ss.tk.red[wave] = incl;
         __syncthreads();
         uint32_t before, total;
@@ -485,23 +472,31 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
                     const int bit = __builtin_ctz(bits);
                     bits &= bits - 1;
                     if ((int)k >= k_lo && (int)k <= k_hi && (int)k < n_keep)
-                        place((int)k, w * 32 + bit);
+                        s_blk[k - k_lo] = w * 32 + bit;
                     ++k;
                 }
             }
         }
-        if (tid < kChunk) {
-            const int pos = c_begin + tid;
-            if (pos >= n_keep * r) {
-                const int n_sel = n_keep * r + tail;
-                s_cells[tid] = pos < n_sel ? (int)(nc * r + (pos - n_keep * r)) : -1;
-            }
-        }
-        __syncthreads();
         n_keep_all = n_keep;
     }
+    __syncthreads();
+    if (tid < kChunk) {
+        // position c_begin + tid: cell pos % r of the kept block of rank
+        // pos / r, else a tail cell, else -1
+        const int pos = c_begin + tid;
+        const int n_blk_cells = n_keep_all * r;
+        int cell;
+        if (pos < n_blk_cells) {
+            const int k = pos / r;
+            cell = s_blk[k - k_lo] * r + (pos - k * r);
+        } else {
+            cell = pos < n_blk_cells + tail ? (int)(nc * r + (pos - n_blk_cells)) : -1;
+        }
+        s_cells[tid] = cell;
+    }
+    __syncthreads();
     const int n_sel = n_keep_all * r + tail;
-    QSA_STAMP(3);
+    QSA_STAMP_HOLD(t_placed);
     int cell[kCPG];
 #pragma unroll
     for (int u = 0; u < kCPG; ++u) cell[u] = s_cells[grp * kCPG + u];
@@ -529,6 +524,10 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
                                      f.sel_cells + (int64_t)i * ld_cells, ld_cells, f.n_sel + i,
                                      ss.tk);
     }
+    QSA_STAMP_LDS_FLUSH();
+    QSA_STAMP_SAVE(0, t_start);
+    QSA_STAMP_SAVE(2, t_thresh);
+    QSA_STAMP_SAVE(3, t_placed);
     QSA_STAMP(4);
 }
 

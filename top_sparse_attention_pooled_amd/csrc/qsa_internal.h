@@ -55,6 +55,44 @@ __device__ __forceinline__ void stamp_at(int slot) {
     }
 }
 #define QSA_STAMP(slot) ::qsa::stamp_at(slot)
+// Held stamps: the clock read into a register now and stored by
+// QSA_STAMP_SAVE at the kernel's end, so that no stamp store is outstanding
+// at the kernel's barriers (a barrier waits for the workgroup's stores).
+__device__ __forceinline__ void stamp_save(int slot, uint64_t t) {
+    const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if (threadIdx.x == 0 && wg < (uint32_t)kStampWgs) {
+        g_stamps[wg][slot] = t;
+        if (slot == 0) {
+            uint32_t xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            g_stamps[wg][kStampSlots - 1] = xcc;
+        }
+    }
+}
+// LDS stamps: for points inside device functions; QSA_STAMP_LDS_FLUSH at the
+// kernel's end stores every slot written since QSA_STAMP_LDS_BEGIN.
+__device__ __forceinline__ uint64_t *stamp_lds_buf() {
+    __shared__ uint64_t buf[kStampSlots];
+    return buf;
+}
+__device__ __forceinline__ void stamp_lds_begin() {
+    if (threadIdx.x == 0)
+        for (int k = 0; k < kStampSlots; ++k) stamp_lds_buf()[k] = 0;
+}
+__device__ __forceinline__ void stamp_lds(int slot) {
+    if (threadIdx.x == 0) stamp_lds_buf()[slot] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void stamp_lds_flush() {
+    const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if (threadIdx.x == 0 && wg < (uint32_t)kStampWgs)
+        for (int k = 0; k < kStampSlots - 1; ++k)
+            if (stamp_lds_buf()[k]) g_stamps[wg][k] = stamp_lds_buf()[k];
+}
+#define QSA_STAMP_LDS_BEGIN() ::qsa::stamp_lds_begin()
+#define QSA_STAMP_LDS(slot) ::qsa::stamp_lds(slot)
+#define QSA_STAMP_LDS_FLUSH() ::qsa::stamp_lds_flush()
+#define QSA_STAMP_HOLD(name) const uint64_t name = __builtin_amdgcn_s_memrealtime()
+#define QSA_STAMP_SAVE(slot, name) ::qsa::stamp_save(slot, name)
 #define QSA_STAMP_READER(unit)                                                            \
     extern "C" int qsa_stamps_##unit(void *dst, int clear) {                              \
         hipError_t e = hipSuccess;                                                        \
@@ -69,6 +107,11 @@ __device__ __forceinline__ void stamp_at(int slot) {
     }
 #else
 #define QSA_STAMP(slot) ((void)0)
+#define QSA_STAMP_HOLD(name) ((void)0)
+#define QSA_STAMP_LDS_BEGIN() ((void)0)
+#define QSA_STAMP_LDS(slot) ((void)0)
+#define QSA_STAMP_LDS_FLUSH() ((void)0)
+#define QSA_STAMP_SAVE(slot, name) ((void)0)
 #define QSA_STAMP_READER(unit)
 #endif
 

@@ -126,6 +126,9 @@ __device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pre
     const int wave = wave_id();
     n_above = 0;
     done = false;
+    // not unrolled: a workgroup runs this once, and each copy of a round
+    // would be instructions fetched cold
+#pragma unroll 1
     for (int round = 0; round < 4; ++round) {
         const int shift = range_shift(lo, hi);
         uint32_t *hist = sm.hist[buf];
@@ -149,6 +152,7 @@ __device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pre
             for (int j = (int)threadIdx.x - kWave; j < kHistWords; j += NT - kWave) other[j] = 0u;
         }
         __syncthreads();
+        QSA_STAMP_LDS(8 + (round < 3 ? round : 3));
         const uint32_t above = sm.b_above, cnt = sm.b_cnt;
         lo = sm.b_lo;
         hi = sm.b_hi;
@@ -182,6 +186,7 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
         mn = min(mn, k);
         mx = max(mx, k);
     });
+    QSA_STAMP_LDS(1);
     cnt = wave_sum_u32(cnt);
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
@@ -195,6 +200,7 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
     const uint32_t n_valid = wave_sum_u32(lane < NW ? sm.red[lane] : 0u);
     const uint32_t lo = wave_min_u32(lane < NW ? sm.red2[lane] : ~0u);
     const uint32_t hi = wave_max_u32(lane < NW ? sm.red3[lane] : 0u);
+    QSA_STAMP_LDS(7);
     if (n_valid <= B) {  // T = 0: every valid element
         __syncthreads();
         return th;

@@ -28,7 +28,7 @@ STAMP_WGS = 4096
 # for the prefill indexer
 POINTS = {
     "k_score_cand": ("score", {0: "start", 2: "tile scored", 3: "end"}),
-    "k_sel_attn": ("attn", {0: "start", 2: "threshold", 3: "cells placed", 4: "end"}),
+    "k_sel_attn": ("attn", {0: "start", 1: "keys counted", 7: "range reduced", 8: "round 1", 9: "round 2", 10: "round 3", 11: "round 4+", 2: "threshold", 3: "cells placed", 4: "end"}),
     "k_attn_combine": ("attn", {5: "start", 6: "end"}),
 }
 PREFILL_POINTS = {
