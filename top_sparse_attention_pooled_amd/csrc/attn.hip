@@ -173,6 +173,7 @@ __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, i
 
     if (c_begin < c_end) {
         for (int c0 = c_begin; c0 < c_end; c0 += kChunk) {
+            QSA_STAMP_LDS(12);
             const int c1 = min(c_end, c0 + kChunk);
             if (c0 != c_begin) {
 #pragma unroll
@@ -220,6 +221,7 @@ __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, i
                     sm.p[head_of_lane<G>(j)][cc - c0] = ok ? sv[0] * a.scale : -INFINITY;
             }
             __syncthreads();
+            QSA_STAMP_LDS(13);
             // chunk statistics: 32 lanes per head, two heads per wavefront
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -263,6 +265,7 @@ __device__ __forceinline__ void attend_chunks(const AttnArgs &a, int i, int s, i
                 }
             }
             __syncthreads();
+            QSA_STAMP_LDS(14);
         }
     }
 
@@ -305,6 +308,8 @@ template <int G, int KVT>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, int n_runs,
                                               int direct) {
     __shared__ AttnSmem<G> sm;
+    QSA_STAMP_HOLD(t_start);
+    QSA_STAMP_LDS_BEGIN();
     const int n_hg = a.n_head / G;
     int i, run, hg;
     if (!unit_of(a.n_q, n_runs, n_hg, i, run, hg)) return;
@@ -332,6 +337,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunks_per_run, in
     attend_chunks<G, KVT>(a, i, s, g, h0, c_begin, c_end, cell, cells, qv, sm,
                           direct ? nullptr : partial_of<G>(a, i, hg, run, n_runs), direct != 0,
                           true);
+    QSA_STAMP_HOLD(t_end);
+    QSA_STAMP_LDS_FLUSH();
+    QSA_STAMP_SAVE(0, t_start);
+    QSA_STAMP_SAVE(4, t_end);
 }
 
 constexpr int kSelAttnNT = 512;

@@ -28,8 +28,14 @@ STAMP_WGS = 4096
 # for the prefill indexer
 POINTS = {
     "k_score_cand": ("score", {0: "start", 2: "tile scored", 3: "end"}),
-    "k_sel_attn": ("attn", {0: "start", 1: "keys counted", 7: "range reduced", 8: "round 1", 9: "round 2", 10: "round 3", 11: "round 4+", 2: "threshold", 3: "cells placed", 4: "end"}),
+    "k_sel_attn": ("attn", {0: "start", 1: "keys counted", 7: "range reduced", 8: "round 1",
+                            9: "round 2", 10: "round 3", 11: "round 4+", 2: "threshold",
+                            3: "cells placed", 12: "chunk start", 13: "chunk scored",
+                            14: "chunk done", 4: "end"}),
     "k_attn_combine": ("attn", {5: "start", 6: "end"}),
+    # the split path's attention (several queries): the same slots, its last chunk
+    "k_attn": ("attn", {0: "start", 12: "chunk start", 13: "chunk scored", 14: "chunk done",
+                        4: "end"}),
 }
 PREFILL_POINTS = {
     "k_prefill_scores (maxima)": ("prefill", {0: "start", 1: "operands in",
@@ -116,15 +122,22 @@ def main():
             rows = tab[tab[:, first] > 0]
             if name == "k_score_cand":
                 rows = sc[sc[:, 0] > 0]
+            # slots 0 and 4 are either kernel's: the fused kernel's rows have
+            # a threshold point, the split kernel's do not
+            if name == "k_sel_attn":
+                rows = rows[rows[:, 2] > 0]
+            elif name == "k_attn":
+                rows = rows[rows[:, 2] == 0]
             for slot, pname in pts.items():
                 vals = rows[:, slot]
                 vals = vals[vals > 0]
                 times[name][pname] += list((vals - t0) * 0.01)
             sl = list(pts)
-            for a_, b_ in zip(sl, sl[1:]):
-                ok = (rows[:, a_] > 0) & (rows[:, b_] > 0)
-                key = f"{name}: {pts[a_]} -> {pts[b_]}"
-                durs.setdefault(key, []).extend(list((rows[ok, b_] - rows[ok, a_]) * 0.01))
+            for row in rows:  # phases between consecutive recorded points
+                seen = [x for x in sl if row[x] > 0]
+                for a_, b_ in zip(seen, seen[1:]):
+                    key = f"{name}: {pts[a_]} -> {pts[b_]}"
+                    durs.setdefault(key, []).append((row[b_] - row[a_]) * 0.01)
     out = {"workload": args.workload, "steps": args.steps - args.skip,
            "unit": "us; quantiles p0 p10 p50 p90 p100 over workgroups and steps",
            "points_from_first_score_start": {}, "phases": {}}
