@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     // expansion is one short loop-free step rather than a copy per kept key:
     // this code runs once per workgroup, so its size is fetch time.)
     int n_keep_all;
-    if (fast) {
+    if (__builtin_expect(fast, 1)) {
         // the kept set is the base candidates th keeps; they ascend by block
         // in the order (wavefront, slot, lane), so a kept one's rank is the
         // kept count of the earlier wavefronts, then of the wavefront's
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
     // The selection outputs, after the attention: a barrier waits for every
     // store issued before it, so stores issued earlier would delay the
     // gather.  attend_chunks leaves s_cells, s_blk and ss untouched.
-    if (fast) {
+    if (__builtin_expect(fast, 1)) {
         // this run's share (set 0): its blocks, -1 past the kept blocks (the
         // runs' block ranks cover [0, B)), its list positions; the count
         // from run 0

@@ -165,7 +165,7 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
 #pragma unroll
     for (int q = 0; q < kDrop; ++q) {
         const uint64_t d = drop[q];
-        if (d != 0 && th.keep((uint32_t)(d >> 32), (uint32_t)d)) {
+        if (__builtin_expect(d != 0 && th.keep((uint32_t)(d >> 32), (uint32_t)d), 0)) {
             const int at = atomicAdd(&sm.n_over, 1);
             if (at < kMaxExpand) sm.over[at] = tid + NT * q;
         }
@@ -173,7 +173,8 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
     __syncthreads();
     const int n_over = sm.n_over;
     const bool fast = n_over == 0;
-    if (SKIP_FAST_MARK && fast) return true;
+    // (the common case: its code is laid out first, the rest out of line)
+    if (SKIP_FAST_MARK && __builtin_expect(fast, 1)) return true;
 
     const int64_t limit = qf.limit();
     const int n_words = (int)((limit + 31) / 32);

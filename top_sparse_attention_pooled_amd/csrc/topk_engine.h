@@ -45,12 +45,21 @@ struct TopkSmem {
 };
 
 // The kept set: valid (k != 0) and (k > T, or k == T and (!tie or u >= U)).
+// As one unsigned comparison of the 64-bit key k:u with the bound
+// T:(tie ? U : 0), raised to 1:0 so that k = 0 stays out (T is a valid key,
+// so T >= 1, whenever it is not 0 with no tie).  (The short-circuit form
+// compiles to three nested branches per key, several hundred cycles each
+// time a workgroup tests its keys.)
 struct Thresh {
     uint32_t T;
     uint32_t U;
     bool tie;
+    __device__ __forceinline__ uint64_t bound() const {
+        const uint64_t b = ((uint64_t)T << 32) | (tie ? U : 0u);
+        return b > (1ull << 32) ? b : (1ull << 32);
+    }
     __device__ __forceinline__ bool keep(uint32_t k, uint32_t u) const {
-        return k != 0 && (k > T || (k == T && (!tie || u >= U)));
+        return (((uint64_t)k << 32) | u) >= bound();
     }
 };
 
@@ -163,7 +172,7 @@ __device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pre
             done = true;
             break;
         }
-        if (lo == hi) break;  // a single value shared by more than krem elements
+        if (__builtin_expect(lo == hi, 0)) break;  // one value shared by more than krem elements
     }
     return lo;
 }
@@ -201,7 +210,7 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
     const uint32_t lo = wave_min_u32(lane < NW ? sm.red2[lane] : ~0u);
     const uint32_t hi = wave_max_u32(lane < NW ? sm.red3[lane] : 0u);
     QSA_STAMP_LDS(7);
-    if (n_valid <= B) {  // T = 0: every valid element
+    if (__builtin_expect(n_valid <= B, 0)) {  // T = 0: every valid element
         __syncthreads();
         return th;
     }
@@ -211,7 +220,7 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
     th.T = select_u32<NT>(
         for_each, [](uint32_t k, uint32_t) { return k != 0; },
         [](uint32_t k, uint32_t) { return k; }, B, lo, hi, sm, buf, n_above, done);
-    if (done) return th;
+    if (__builtin_expect(done, 1)) return th;
     // ties at score key T: keep the lowest blocks (largest u) among them
     const uint32_t T = th.T;
     uint32_t umn = ~0u, umx = 0u;
