@@ -165,7 +165,7 @@ __device__ __forceinline__ bool select_candidates(const DecodeIdxArgs &f, int i,
 #pragma unroll
     for (int q = 0; q < kDrop; ++q) {
         const uint64_t d = drop[q];
-        if (__builtin_expect(d != 0 && th.keep((uint32_t)(d >> 32), (uint32_t)d), 0)) {
+        if (__builtin_expect(th.keep((uint32_t)(d >> 32), (uint32_t)d), 0)) {  // (d = 0: never)
             const int at = atomicAdd(&sm.n_over, 1);
             if (at < kMaxExpand) sm.over[at] = tid + NT * q;
         }

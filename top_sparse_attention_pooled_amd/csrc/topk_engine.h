@@ -141,10 +141,12 @@ __device__ __forceinline__ uint32_t select_u32(const ForEach &for_each, Pred pre
     for (int round = 0; round < 4; ++round) {
         const int shift = range_shift(lo, hi);
         uint32_t *hist = sm.hist[buf];
+        // (one branch per element, around the atomic: v in [lo, hi] as one
+        // unsigned compare, the predicate combined without short circuit)
         for_each([&](uint32_t k, uint32_t u) {
-            if (!pred(k, u)) return;
             const uint32_t v = val(k, u);
-            if (v >= lo && v <= hi) atomicAdd(&hist[hist_slot((v - lo) >> shift)], 1u);
+            if (pred(k, u) & (v - lo <= hi - lo))
+                atomicAdd(&hist[hist_slot((v - lo) >> shift)], 1u);
         });
         __syncthreads();
         if (wave == 0) {
@@ -189,10 +191,9 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     Thresh th{0u, 0u, false};
     uint32_t cnt = 0, mn = ~0u, mx = 0u;
-    for_each([&](uint32_t k, uint32_t) {
-        if (!k) return;
-        ++cnt;
-        mn = min(mn, k);
+    for_each([&](uint32_t k, uint32_t) {  // (selects, no branches)
+        cnt += k != 0 ? 1u : 0u;
+        mn = min(mn, k != 0 ? k : ~0u);
         mx = max(mx, k);
     });
     QSA_STAMP_LDS(1);
@@ -225,9 +226,9 @@ __device__ __forceinline__ Thresh topk_threshold(const ForEach &for_each, uint32
     const uint32_t T = th.T;
     uint32_t umn = ~0u, umx = 0u;
     for_each([&](uint32_t k, uint32_t u) {
-        if (k != T) return;
-        umn = min(umn, u);
-        umx = max(umx, u);
+        const bool at_t = k == T;
+        umn = min(umn, at_t ? u : ~0u);
+        umx = max(umx, at_t ? u : 0u);
     });
     umn = wave_min_u32(umn);
     umx = wave_max_u32(umx);
