@@ -563,11 +563,9 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
         const int x = c * kTauNT + tid;
         const uint32_t k = x < n_sub ? approx_key(v[c]) : 0u;
         key[c] = k;
-        if (k) {
-            ++cnt;
-            mn = min(mn, k);
-            mx = max(mx, k);
-        }
+        cnt += k != 0 ? 1u : 0u;  // (selects: a branch per key costs far more)
+        mn = min(mn, k != 0 ? k : ~0u);
+        mx = max(mx, k);
     }
     cnt = wave_sum_u32(cnt);
     mn = wave_min_u32(mn);
@@ -611,7 +609,7 @@ __global__ __launch_bounds__(kTauNT) void k_prefill_tau(ScoreArgs a, PrefillWs w
                 shift = range_shift(lo, hi);
 #pragma unroll
                 for (int c = 0; c < PER; ++c)
-                    if (key[c] >= lo && key[c] <= hi)
+                    if (key[c] - lo <= hi - lo)  // key in [lo, hi]
                         atomicAdd(&s_hist[1][hist_slot((key[c] - lo) >> shift)], 1u);
                 __syncthreads();
                 if (wave != 0) return;  // (no barrier follows)
@@ -704,12 +702,14 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
         }
     }
     const uint16_t qv = w.qr[(int64_t)i * kDIdx + (tid & (kDIdx - 1))];
-    int s;
-    int64_t p;
-    bool valid;
-    const int64_t nc = query_blocks(a.q_seq, a.q_pos, i, a.g.n_seq, a.g.cap_cells, a.g.n_cells,
-                                    a.r, s, p, valid);
-    const int64_t limit = nc < a.nb_max ? nc : a.nb_max;
+    // the query's validity and sequence as the first launch resolved them
+    // (no dependent load of the sequence's cell count here)
+    const int2 meta = w.qmeta[i];
+    const int64_t p = a.q_pos[i];
+    const bool valid = meta.x >= 0;
+    const int s = valid ? meta.x : 0;
+    const int64_t nc = valid ? (p + 1) / a.r : 0;  // the complete visible blocks
+    const int64_t limit = meta.y;                   // nc capped at nb_max
     const int B = top_k / a.r;
     const int64_t cap_blocks = a.g.cap_cells / a.r;
     const uint16_t *keys = a.pooled_bf16 + (valid ? (int64_t)s * cap_blocks * kDIdx : 0);
