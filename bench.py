@@ -307,8 +307,12 @@ def run_decode(args, torch, dev, name):
     t_main = timer.run(W, T)
     parts, steps_us = {}, None
     if not args.eager:
-        for part in ("score", "select_attend"):
-            parts[part] = timer.part(W, T, K * L, part=part)
+        parts["score"] = timer.part(W, T, K * L, part="score")
+        # the selection reads the candidates its step's scoring left, so it is
+        # not replayed alone (stale candidates, or one step replayed K times,
+        # would send every replay down one step's path): its share is the
+        # step's time less the scoring launch's
+        parts["select_attend"] = t_main * 1e6 / (K * L) - parts["score"]
         if not args.profile:
             steps_us = timer.per_step(W, T) / L
 
@@ -332,7 +336,12 @@ def run_decode(args, torch, dev, name):
                         "bytes_per_launch": round(mean_b["score"] + mean_b["update"]),
                         "frac": round((mean_b["score"] + mean_b["update"]) /
                                       (parts["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
-        kernels.append({"kernel": "k_sel_attn + k_attn_combine (one call)",
+        d0 = layers[0].dims
+        hpk = d0.n_head // d0.n_head_kv
+        n_set = -(-(d0.n_head // (2 if hpk % 2 == 0 else 1)) // 2)
+        fused = n_q * -(-d0.ld_cells // 32) * n_set <= 512  # the library's fused-grid rule
+        kernels.append({"kernel": ("k_sel_attn + k_attn_combine (one call)" if fused else
+                                   "k_select_cand + k_attn + k_attn_combine (one call)"),
                         "avg_launch_us": round(parts["select_attend"], 3),
                         "bytes_per_launch": round(mean_b["attn"] + mean_b["select"]),
                         "frac": round((mean_b["attn"] + mean_b["select"]) /
@@ -366,7 +375,8 @@ def run_decode(args, torch, dev, name):
         "step_hbm_gbps": round(step_bytes / (us_per_step_layer * 1e-6) / 1e9, 1),
         "roofline": {
             "kernel": dom["kernel"] if dom else None,
-            "timing": "events around a graph of the K*L launches of that part alone",
+            "timing": ("scoring: events around a graph of its K*L launches alone; the "
+                       "selection + attention call: the step's time less the scoring's"),
             "bound": "hbm",
             "achieved": round(dom["bytes_per_launch"] / (dom["avg_launch_us"] * 1e-6) / 1e9, 1)
             if dom else None,
