@@ -335,7 +335,8 @@ def run_decode(args, torch, dev, name):
         kernels.append({"kernel": "k_score_cand", "avg_launch_us": round(parts["score"], 3),
                         "bytes_per_launch": round(mean_b["score"] + mean_b["update"]),
                         "frac": round((mean_b["score"] + mean_b["update"]) /
-                                      (parts["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                                      (parts["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": recorded_traffic(name, "k_score_cand")})
         d0 = layers[0].dims
         hpk = d0.n_head // d0.n_head_kv
         n_set = -(-(d0.n_head // (2 if hpk % 2 == 0 else 1)) // 2)
@@ -345,7 +346,9 @@ def run_decode(args, torch, dev, name):
                         "avg_launch_us": round(parts["select_attend"], 3),
                         "bytes_per_launch": round(mean_b["attn"] + mean_b["select"]),
                         "frac": round((mean_b["attn"] + mean_b["select"]) /
-                                      (parts["select_attend"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                                      (parts["select_attend"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": (recorded_call_traffic(name, ["k_sel_attn", "k_attn_combine"])
+                                    if fused else None)})
     dom = max(kernels, key=lambda k: k["avg_launch_us"]) if kernels else None
     step_frac = step_bytes / (us_per_step_layer * 1e-6) / 1e9 / HBM_PEAK_GBS
     result = {
@@ -383,7 +386,7 @@ def run_decode(args, torch, dev, name):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": dom["frac"] if dom else None,
-            "traffic": recorded_traffic(name) if dom and dom["kernel"] == "k_score_cand" else None,
+            "traffic": dom.get("traffic") if dom else None,
             "bytes_per_launch": dom["bytes_per_launch"] if dom else None,
             "avg_launch_us": dom["avg_launch_us"] if dom else None,
             "kernels": kernels,
@@ -589,19 +592,26 @@ def run_prefill(args, torch, dev, name, K, W):
 # counters and the CPU baseline
 # ---------------------------------------------------------------------------
 
-def recorded_traffic(workload):
-    """HBM-side bytes per scoring launch from the committed counter summary
-    (two rocprofv3 --pmc runs, scaled by a streaming kernel of known size),
-    or None if there is none or the kernel sources changed since."""
+def recorded_traffic(workload, kernel="k_score_cand"):
+    """HBM-side bytes per launch of `kernel` from the committed counter
+    summary (two rocprofv3 --pmc runs, scaled by a streaming kernel of known
+    size), or None if there is none or the kernel's sources changed since."""
     from top_sparse_attention_pooled_amd import profiling
-    path = os.path.join(ROOT, "profiles", f"k_score_cand_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != profiling.source_hash():
+    if rec.get("source_sha256") != profiling.source_hash(kernel):
         return None
     return round(rec["traffic_bytes"])
+
+
+def recorded_call_traffic(workload, kernels):
+    """The sum of recorded_traffic over the launches of one call, or None
+    if any of them has no current figure."""
+    parts = [recorded_traffic(workload, k) for k in kernels]
+    return None if any(p is None for p in parts) else sum(parts)
 
 
 def _decode_oracle_leg(w, host, W, K, budget, threads):

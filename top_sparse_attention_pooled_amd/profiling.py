@@ -42,7 +42,8 @@ CALIBRATION_KERNEL = "neg"
 
 
 # the source file that defines each profiled kernel
-KERNEL_SOURCE = {"k_score_cand": "score.hip"}
+KERNEL_SOURCE = {"k_score_cand": "score.hip", "k_sel_attn": "attn.hip",
+                 "k_attn_combine": "attn.hip"}
 
 
 def _sources_of(name: str) -> List[str]:
