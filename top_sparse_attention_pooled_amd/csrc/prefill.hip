@@ -751,6 +751,8 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
             // the masked blocks in ascending order, listed by the prefix
             // count; entry: (MFMA score bits << 32) | block, NaN where the
             // block shares its subgroup with another masked one
+            // (the walk has no branch or atomic per bit: a block that needs
+            // rescoring is marked by a NaN score and found by the pass below)
             uint32_t at = before + incl - cnt;
             uint32_t kmn = ~0u, kmx = 0u;
 #pragma unroll
@@ -763,22 +765,27 @@ __global__ __launch_bounds__(kSelPNT) void k_select_prefill(ScoreArgs a, Prefill
                     const int bit = __builtin_ctzll(bits);
                     bits &= bits - 1;
                     const int sub = bit >> 4;
-                    float m = __builtin_nanf("");
-                    if (__popc((uint32_t)(M >> (16 * sub)) & 0xffffu) == 1) {
-                        m = (sub & 2) ? ((sub & 1) ? v[3] : v[2]) : ((sub & 1) ? v[1] : v[0]);
-                        const uint32_t k = approx_key(m);
-                        kmn = min(kmn, k);
-                        kmx = max(kmx, k);
-                    } else {
-                        sm.xlist[atomicAdd(&sm.n_unscored, 1u)] = (uint16_t)at;
-                    }
+                    const bool alone = __popc((uint32_t)(M >> (16 * sub)) & 0xffffu) == 1;
+                    const float vs =
+                        (sub & 2) ? ((sub & 1) ? v[3] : v[2]) : ((sub & 1) ? v[1] : v[0]);
+                    const float m = alone ? vs : __builtin_nanf("");
+                    const uint32_t k = approx_key(vs);
+                    kmn = min(kmn, alone ? k : ~0u);
+                    kmx = max(kmx, alone ? k : 0u);
                     sm.band[at++] = ((uint64_t)__float_as_uint(m) << 32) | (uint64_t)(gb + bit);
                 }
             }
             __syncthreads();
             QSA_STAMP(11);
-            // the listed blocks without an MFMA score: the order-T score stands in
-            for (int j = tid; j < (int)sm.n_unscored; j += kSelPNT) {
+            // the listed blocks without an MFMA score (NaN), gathered into an
+            // index list (one short pass), then rescored in order T at once
+            for (int x = tid; x < (int)total; x += kSelPNT) {
+                const float m = __uint_as_float((uint32_t)(sm.band[x] >> 32));
+                if (m != m) sm.xlist[atomicAdd(&sm.n_unscored, 1u)] = (uint16_t)x;
+            }
+            __syncthreads();
+            const int n_unscored = (int)sm.n_unscored;
+            for (int j = tid; j < n_unscored; j += kSelPNT) {
                 const int x = sm.xlist[j];
                 const uint32_t b = (uint32_t)sm.band[x];
                 const float sc = exact_score(keys + (int64_t)b * kDIdx, sm.q);
