@@ -431,12 +431,15 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
         // in the order (wavefront, slot, lane), so a kept one's rank is the
         // kept count of the earlier wavefronts, then of the wavefront's
         // earlier slots, then of its slot's lower lanes (ballots)
+        // (each slot's ballot is kept for the ranks below)
+        uint64_t bal[decltype(ck)::kBase];
         uint32_t in_wave = 0;
 #pragma unroll
-        for (int x = 0; x < decltype(ck)::kBase; ++x)
-            if (x < ck.nb)
-                in_wave += __popcll(
-                    __ballot(th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x])));
+        for (int x = 0; x < decltype(ck)::kBase; ++x) {
+            bal[x] = x < ck.nb ? __ballot(th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]))
+                               : 0ull;
+            in_wave += __popcll(bal[x]);
+        }
         if (lane == 0) ss.tk.red[wave] = in_wave;
         __syncthreads();
         uint32_t before, total;
@@ -451,12 +454,10 @@ __global__ __launch_bounds__(kSelAttnNT) void k_sel_attn(DecodeIdxArgs f, AttnAr
         uint32_t k0 = before;  // rank of this wavefront's next kept slot
 #pragma unroll
         for (int x = 0; x < decltype(ck)::kBase; ++x) {
-            if (x >= ck.nb) continue;
-            const bool kp = th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]);
-            const uint64_t bal = __ballot(kp);
-            const int k = (int)(k0 + __popcll(bal & below));
+            const bool kp = (bal[x] >> lane) & 1ull;
+            const int k = (int)(k0 + __popcll(bal[x] & below));
             if (kp && k >= k_lo && k <= k_hi && k < n_keep) s_blk[k - k_lo] = key_block(ck.k[x]);
-            k0 += __popcll(bal);
+            k0 += __popcll(bal[x]);
         }
         n_keep_all = n_keep;
     } else {
