@@ -398,11 +398,14 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
     // count of the earlier wavefronts, then of its wavefront's earlier slots,
     // then of its slot's lower lanes (ballots) -- no bitmap to mark or scan.
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    uint64_t bal[decltype(ck)::kBase];  // each slot's ballot, kept for the ranks below
     uint32_t in_wave = 0;
 #pragma unroll
-    for (int x = 0; x < decltype(ck)::kBase; ++x)
-        if (x < ck.nb)
-            in_wave += __popcll(__ballot(th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x])));
+    for (int x = 0; x < decltype(ck)::kBase; ++x) {
+        bal[x] = x < ck.nb ? __ballot(th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]))
+                           : 0ull;
+        in_wave += __popcll(bal[x]);
+    }
     if (lane == 0) sm.tk.red[wave] = in_wave;
     __syncthreads();
     uint32_t before, total;
@@ -412,16 +415,14 @@ __global__ __launch_bounds__(kSelNT) void k_select_cand(DecodeIdxArgs f) {
     uint32_t k0 = before;  // rank of this wavefront's next kept slot
 #pragma unroll
     for (int x = 0; x < decltype(ck)::kBase; ++x) {
-        if (x >= ck.nb) continue;
-        const bool kp = th.keep((uint32_t)(ck.k[x] >> 32), (uint32_t)ck.k[x]);
-        const uint64_t bal = __ballot(kp);
-        const int k = (int)(k0 + __popcll(bal & below));
+        const bool kp = (bal[x] >> lane) & 1ull;
+        const int k = (int)(k0 + __popcll(bal[x] & below));
         if (kp && k < n_keep) {
             const int32_t b = key_block(ck.k[x]);
             sel_blocks[k] = b;
             for (int c = 0; c < a.r; ++c) sel_cells[k * a.r + c] = b * a.r + c;
         }
-        k0 += __popcll(bal);
+        k0 += __popcll(bal[x]);
     }
     if (threadIdx.x == 0) f.n_sel[i] = n_keep * a.r + tail;
     for (int j = n_keep + (int)threadIdx.x; j < B; j += kSelNT) sel_blocks[j] = -1;
