@@ -597,7 +597,8 @@ def recorded_traffic(workload, kernel="k_score_cand"):
     summary (two rocprofv3 --pmc runs, scaled by a streaming kernel of known
     size), or None if there is none or the kernel's sources changed since."""
     from top_sparse_attention_pooled_amd import profiling
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    stem = kernel.replace("<", "_").replace(">", "")  # k_prefill_scores<0> -> k_prefill_scores_0
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -605,6 +606,11 @@ def recorded_traffic(workload, kernel="k_score_cand"):
     if rec.get("source_sha256") != profiling.source_hash(kernel):
         return None
     return round(rec["traffic_bytes"])
+
+
+# the launches of one qsa_score_select_prefill call at the 512-token ubatch
+PREFILL_INDEXER_KERNELS = ["k_rope_queries_delta", "k_prefill_scores<0>", "k_prefill_tau<16>",
+                           "k_prefill_scores<1>", "k_select_prefill"]
 
 
 def recorded_call_traffic(workload, kernels):
@@ -828,7 +834,9 @@ def main():
                 "bound": "mfma",
                 "achieved": pf["indexer_mfma"]["achieved_tflops"],
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": pf["indexer_mfma"]["frac"], "traffic": None,
+                "frac": pf["indexer_mfma"]["frac"],
+                "traffic": (recorded_call_traffic(name, PREFILL_INDEXER_KERNELS)
+                            if name == "prefill" else None),
                 "flops_per_launch": pf["indexer_mfma"]["flops_per_launch"],
                 "avg_launch_us": pf["parts_us"].get("indexer"),
             },

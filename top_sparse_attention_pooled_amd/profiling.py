@@ -43,7 +43,9 @@ CALIBRATION_KERNEL = "neg"
 
 # the source file that defines each profiled kernel
 KERNEL_SOURCE = {"k_score_cand": "score.hip", "k_sel_attn": "attn.hip",
-                 "k_attn_combine": "attn.hip"}
+                 "k_attn_combine": "attn.hip", "k_rope_queries_delta": "prefill.hip",
+                 "k_prefill_scores<0>": "prefill.hip", "k_prefill_scores<1>": "prefill.hip",
+                 "k_prefill_tau<16>": "prefill.hip", "k_select_prefill": "prefill.hip"}
 
 
 def _sources_of(name: str) -> List[str]:
