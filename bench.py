@@ -566,7 +566,9 @@ def run_prefill(args, torch, dev, name, K, W):
         "indexer_mfma": {"flops_per_launch": flops,
                          "achieved_tflops": round(tflops, 2) if tflops else None,
                          "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if tflops else None},
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4) if tflops else None,
+                         "traffic": (recorded_call_traffic(name, PREFILL_INDEXER_KERNELS)
+                                     if name == "prefill" else None)},
         "attn_mfma": {"flops_per_launch": attn_flops,
                       "achieved_tflops": round(attn_tflops, 2) if attn_tflops else None,
                       "peak_tflops": MFMA_FP16_PEAK_TFLOPS,
