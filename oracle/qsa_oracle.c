@@ -20,7 +20,7 @@
  * in fp64.  Build with -ffp-contract=off and without fast-math: every fp32
  * multiply and add below must round separately.
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *   - RoPE is the split-half ("NeoX") form over all d dims, pairs (t, t+d/2),
  *     inverse frequency theta^(-2t/d), angle computed in fp64 and its cosine
  *     and sine rounded to fp32; a pooled block sits at position b*r.
